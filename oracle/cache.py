@@ -1,0 +1,132 @@
+"""State of the HBM expert cache: fixed slots, one global LRU over layers.
+
+Test infrastructure (see the package docstring).
+
+The pages describe one global LRU cache across the MoE layers, used during
+decode instead of pinning chosen experts at start-up (jansverre.net FreeToken
+article, section "Hvorfor er båndbredden viktigere enn antall kjerner?"), that
+exploits expert overlap between adjacent tokens (aipolix.com FreeToken
+article, fifth paragraph), whose size can change without restarting or
+reloading the host-resident expert pool (same article, sixth paragraph).
+They give no algorithm; the readings below are this implementation's.
+
+State: ``key[C]`` (layer*E + expert, -1 = empty), ``stamp[C]`` (0 = empty,
+otherwise a unique recency number), ``clock``.
+
+lookup(layer, U) for the ascending unique experts U of one call:
+  1. start = clock;
+  2. hits, in ascending expert: clock += 1, stamp the slot with clock;
+  3. victims = empty slots in ascending index, then occupied slots whose
+     stamp <= start in ascending stamp (this call's hits are pinned);
+  4. the i-th miss (ascending expert) takes victims[i] when it exists
+     (evicting its key; clock += 1; stamp; a fill of that slot is issued);
+     otherwise it bypasses the cache through staging slot b (the b-th
+     bypass), encoded -1-b, and the state is unchanged.
+resize(C'): grow appends empty slots; shrink evicts occupied slots in
+  ascending stamp while occupancy > C', then moves every survivor in a slot
+  >= C' (ascending) to the lowest empty slot < C' (ascending), keeping key
+  and stamp.  clock is unchanged.
+"""
+
+
+class SlotCache:
+    def __init__(self, capacity: int, n_experts: int):
+        self.E = n_experts
+        self.key = [-1] * capacity
+        self.stamp = [0] * capacity
+        self.clock = 0
+        self.hits = self.fills = self.bypasses = self.evictions = 0
+
+    @property
+    def capacity(self):
+        return len(self.key)
+
+    def slot_of(self, key):
+        for s, k in enumerate(self.key):
+            if k == key:
+                return s
+        return None
+
+    def lookup(self, layer: int, experts):
+        """Returns (slots, fills, bypass).
+
+        slots[i] >= 0: the cache slot of experts[i]; < 0: -1 - staging index.
+        fills: [(slot, layer, expert)] in issue order; bypass: [(staging,
+        layer, expert)].
+        """
+        experts = [int(e) for e in experts]
+        assert experts == sorted(set(experts)), "experts must be ascending unique"
+        start = self.clock
+        keys = [layer * self.E + e for e in experts]
+        slots = [None] * len(keys)
+        misses = []
+        for i, kk in enumerate(keys):
+            s = self.slot_of(kk)
+            if s is None:
+                misses.append(i)
+            else:
+                self.clock += 1
+                self.stamp[s] = self.clock
+                slots[i] = s
+                self.hits += 1
+        empty = [s for s in range(self.capacity) if self.key[s] < 0]
+        old = sorted((self.stamp[s], s) for s in range(self.capacity)
+                     if self.key[s] >= 0 and self.stamp[s] <= start)
+        victims = empty + [s for _, s in old]
+        fills, bypass = [], []
+        for r, i in enumerate(misses):
+            e = experts[i]
+            if r < len(victims):
+                s = victims[r]
+                if self.key[s] >= 0:
+                    self.evictions += 1
+                self.key[s] = keys[i]
+                self.clock += 1
+                self.stamp[s] = self.clock
+                slots[i] = s
+                fills.append((s, layer, e))
+                self.fills += 1
+            else:
+                b = r - len(victims)
+                slots[i] = -1 - b
+                bypass.append((b, layer, e))
+                self.bypasses += 1
+        return slots, fills, bypass
+
+    def fill(self, layer: int, experts):
+        """Explicit preload: the same rule as a lookup."""
+        return self.lookup(layer, experts)
+
+    def resize(self, new_capacity: int):
+        """Returns (moves [(src, dst)], evicted keys)."""
+        assert new_capacity >= 0
+        C = self.capacity
+        if new_capacity >= C:
+            self.key += [-1] * (new_capacity - C)
+            self.stamp += [0] * (new_capacity - C)
+            return [], []
+        evicted = []
+        occupied = sorted((self.stamp[s], s) for s in range(C) if self.key[s] >= 0)
+        n_occ = len(occupied)
+        for _, s in occupied:
+            if n_occ <= new_capacity:
+                break
+            evicted.append(self.key[s])
+            self.key[s] = -1
+            self.stamp[s] = 0
+            n_occ -= 1
+            self.evictions += 1
+        moves = []
+        free = [s for s in range(new_capacity) if self.key[s] < 0]
+        for s in range(new_capacity, C):
+            if self.key[s] >= 0:
+                d = free.pop(0)
+                self.key[d], self.stamp[d] = self.key[s], self.stamp[s]
+                self.key[s], self.stamp[s] = -1, 0
+                moves.append((s, d))
+        del self.key[new_capacity:]
+        del self.stamp[new_capacity:]
+        return moves, evicted
+
+    def snapshot(self):
+        return list(self.key), list(self.stamp), self.clock

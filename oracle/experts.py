@@ -1,0 +1,56 @@
+"""Expert SwiGLU FFN and the weighted combine, per token, per chosen expert.
+
+Test infrastructure (see the package docstring).
+
+The pages fix only that partial expert results are summed at the end with no
+approximation (jansverre.net FreeToken article, section "Hva er
+FreeToken?") and that DeepSeek-V4-Flash runs MXFP4 experts (same article,
+section "Hvor raskt kjører modellene?").  Readings where they are silent:
+
+* FFN: o = W_d (silu(W_g x) * (W_u x)), silu(z) = z / (1 + exp(-z)), no
+  biases; W_g, W_u are [I][H], W_d is [H][I];
+* combine: y_t = sum_j g[t, j] * o_{t,j} (+ o_{t,shared}); the shared expert
+  is added with weight 1 and takes no part in top-k or renormalisation;
+* all arithmetic here is fp64 on exactly dequantised weights.
+"""
+import numpy as np
+
+from .mxfp4 import dequant
+
+
+def dequant_expert(w):
+    """Canonical packed expert -> (W_g, W_u, W_d) fp32, exact."""
+    return dequant(w.qg, w.sg), dequant(w.qu, w.su), dequant(w.qd, w.sd)
+
+
+def expert_ffn(x_t: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray):
+    """One token through one expert, fp64.  x_t: [H]."""
+    x = np.asarray(x_t, dtype=np.float64)
+    a = wg.astype(np.float64) @ x
+    b = wu.astype(np.float64) @ x
+    h = a / (1.0 + np.exp(-a)) * b
+    return wd.astype(np.float64) @ h
+
+
+def moe_layer(x: np.ndarray, ids: np.ndarray, g: np.ndarray, get_expert,
+              shared=None, tokens=None):
+    """y[t] = sum_j g[t,j] * FFN_{ids[t,j]}(x[t]) (+ FFN_shared(x[t])), fp64.
+
+    x: [T][H] activation values; ids, g: [T][k]; get_expert(e) returns the
+    dequantised (W_g, W_u, W_d) of routed expert e; shared: the same triple
+    or None.  tokens: optional subset of token rows to evaluate (others are
+    left as NaN) so that large batches can be sampled.
+    """
+    T, k = ids.shape
+    H = x.shape[1]
+    y = np.full((T, H), np.nan, dtype=np.float64)
+    rows = range(T) if tokens is None else tokens
+    for t in rows:
+        acc = np.zeros(H, dtype=np.float64)
+        for j in range(k):
+            wg, wu, wd = get_expert(int(ids[t, j]))
+            acc += float(g[t, j]) * expert_ffn(x[t], wg, wu, wd)
+        if shared is not None:
+            acc += expert_ffn(x[t], *shared)
+        y[t] = acc
+    return y

@@ -1,0 +1,202 @@
+"""Seeded synthetic inputs for the routed MoE expert-layer forward.
+
+This module draws inputs only: token activations, router weights, MXFP4
+expert weights in their canonical packed form, and the Zipf routing traces
+that bias the router.  It holds none of the layer's arithmetic (no
+dequantisation, no routing, no expert math), so both the CPU oracle and the
+HIP path may consume what it produces.
+
+Workload shapes follow the synthetic stand-ins for the models the FreeToken
+pages measure (Qwen3.6-35B-A3B, DeepSeek-V4-Flash, GLM-5.2; jansverre.net
+page, sections "Hvor raskt kjører modellene?" and "Hvorfor er båndbredden
+viktigere enn antall kjerner?").  No trained weights or real prompts are used.
+
+Randomness: every array has its own PCG64 stream keyed by
+(seed, purpose, layer, index, ...) through ``numpy.random.SeedSequence``'s
+``spawn_key``, so any expert, step or layer can be regenerated on its own.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+import numpy as np
+
+# purpose tags for the SeedSequence spawn keys
+_ROUTER, _EXPERT, _SHARED, _X, _TRACE, _PERM = 1, 2, 3, 4, 5, 6
+
+#: additive router bias that forces a drawn expert set into the top-k
+BIAS_STRENGTH = 32.0
+
+
+@dataclass(frozen=True)
+class Shape:
+    """Shape of one MoE layer stack."""
+
+    H: int          # hidden size
+    I: int          # expert intermediate size
+    E: int          # routed experts
+    k: int          # experts per token
+    layers: int = 1
+    shared: bool = False      # one always-on shared expert per layer
+    renormalize: bool = True  # renormalise the top-k gates to sum to 1
+
+    def expert_bytes(self) -> int:
+        """MXFP4 bytes of one expert: 3 matrices, 4 bits + 8 bits per 32."""
+        return 3 * self.H * self.I * 17 // 32
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    shape: Shape
+    Ts: Sequence[int]                 # token batch sizes run on this shape
+    steps: int = 1
+    cache_slots: int = 0              # HBM LRU slots (global across layers)
+    staging_slots: int = 0
+    zipf_s: Optional[float] = None    # None: no router bias
+    overlap: float = 0.0              # expected fraction kept step to step
+    resize: tuple = ()                # ((before_step, new_slots), ...)
+    preload_all: bool = False         # every expert resident before step 0
+    prefill: bool = False
+    notes: str = ""
+
+
+WORKLOADS = {
+    "tiny": Workload(
+        "tiny", Shape(H=256, I=512, E=8, k=2), Ts=(4,), steps=1,
+        cache_slots=8, staging_slots=8, preload_all=True,
+        notes="T=4 tokens, all 8 experts resident, no router bias"),
+    "a3b_decode": Workload(
+        "a3b_decode", Shape(H=2048, I=512, E=256, k=8), Ts=(1, 4, 16),
+        steps=512, cache_slots=64, staging_slots=128, zipf_s=1.1, overlap=0.6,
+        notes="35B-A3B-shaped decode layer, 64-slot LRU, cold start"),
+    "dsv4_decode": Workload(
+        "dsv4_decode", Shape(H=4096, I=2048, E=256, k=6, layers=4, shared=True),
+        Ts=(1, 32), steps=512, cache_slots=256, staging_slots=192,
+        zipf_s=1.1, overlap=0.5,
+        notes="DeepSeek-V4-Flash-shaped decode, 4 layers, global LRU of "
+              "25% of experts per layer"),
+    "dsv4_prefill": Workload(
+        "dsv4_prefill", Shape(H=4096, I=2048, E=256, k=6, layers=4, shared=True),
+        Ts=(4096,), steps=1, prefill=True,
+        notes="T=4096 prefill, near-uniform routing, double-buffered layer "
+              "uploads"),
+    "glm_decode": Workload(
+        "glm_decode", Shape(H=6144, I=2048, E=256, k=8, layers=8, shared=True),
+        Ts=(1,), steps=1024, cache_slots=1228, staging_slots=8,
+        zipf_s=1.2, overlap=0.55, resize=((512, 614),),
+        notes="GLM-5.2-shaped decode, 8 layers, cache resized 60% -> 30% of "
+              "experts before step 512"),
+}
+
+
+def _rng(seed: int, *key: int) -> np.random.Generator:
+    ss = np.random.SeedSequence(entropy=seed, spawn_key=tuple(int(k) for k in key))
+    return np.random.Generator(np.random.PCG64(ss))
+
+
+# ----------------------------------------------------------------- bf16 bits
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (nearest, ties to even); returns uint16 bits.
+
+    Inputs are finite.  This is how synthetic activations are stored.
+    """
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# -------------------------------------------------------------------- draws
+def tokens(shape: Shape, layer: int, step: int, T: int, seed: int = 0) -> np.ndarray:
+    """Activations x ~ N(0, 1) rounded to bf16; uint16 bits [T][H]."""
+    g = _rng(seed, _X, layer, step, T)
+    return f32_to_bf16_bits(g.standard_normal((T, shape.H), dtype=np.float32))
+
+
+def router_weights(shape: Shape, layer: int, seed: int = 0) -> np.ndarray:
+    """Router matrix W_r ~ N(0, 0.02^2), fp32 [H][E] (E contiguous)."""
+    g = _rng(seed, _ROUTER, layer)
+    return (g.standard_normal((shape.H, shape.E), dtype=np.float32) * np.float32(0.02))
+
+
+@dataclass
+class ExpertWeights:
+    """Canonical MXFP4 expert: rows are output features, K contiguous.
+
+    q*: packed E2M1 codes, element 2i in the low nibble of byte i.
+    s*: E8M0 scale bytes, one per 32 consecutive K elements of a row.
+    gate/up: [I][H/2] and [I][H/32]; down: [H][I/2] and [H][I/32].
+    """
+
+    qg: np.ndarray
+    qu: np.ndarray
+    qd: np.ndarray
+    sg: np.ndarray
+    su: np.ndarray
+    sd: np.ndarray
+
+
+def expert_weights(shape: Shape, layer: int, expert: int, seed: int = 0,
+                   scale_lo: int = 119, scale_hi: int = 123) -> ExpertWeights:
+    """Uniform 4-bit codes; scale exponents uniform over integers [-8, -4].
+
+    ``expert = -1`` draws the layer's shared expert.
+    """
+    H, I = shape.H, shape.I
+    g = _rng(seed, _SHARED if expert < 0 else _EXPERT, layer, max(expert, 0))
+    q = g.integers(0, 256, size=3 * H * I // 2, dtype=np.uint8)
+    s = g.integers(scale_lo, scale_hi + 1, size=3 * H * I // 32, dtype=np.uint8)
+    n2, n32 = H * I // 2, H * I // 32
+    return ExpertWeights(
+        qg=q[:n2].reshape(I, H // 2), qu=q[n2:2 * n2].reshape(I, H // 2),
+        qd=q[2 * n2:].reshape(H, I // 2),
+        sg=s[:n32].reshape(I, H // 32), su=s[n32:2 * n32].reshape(I, H // 32),
+        sd=s[2 * n32:].reshape(H, I // 32))
+
+
+def zipf_sets(shape: Shape, layer: int, T: int, steps: int, s: float,
+              overlap: float, seed: int = 0) -> np.ndarray:
+    """Expert sets S[step][row] of size k drawn for one layer.
+
+    Popularity: a per-layer random ranking pi of the experts, with
+    p(pi[r]) proportional to (r+1)^-s.  Step 0 draws k experts without
+    replacement from p.  Each later step keeps m ~ Binomial(k, overlap) of the
+    row's previous set (a uniform subset) and draws the other k-m from p
+    restricted to experts outside the previous set.  Returns int32
+    [steps][T][k], each row sorted ascending.
+    """
+    E, k = shape.E, shape.k
+    perm = _rng(seed, _PERM, layer).permutation(E)
+    p = np.empty(E, dtype=np.float64)
+    p[perm] = (np.arange(E, dtype=np.float64) + 1.0) ** (-s)
+    p /= p.sum()
+    out = np.empty((steps, T, k), dtype=np.int32)
+    for r in range(T):
+        g = _rng(seed, _TRACE, layer, T, r)
+        prev = np.sort(g.choice(E, size=k, replace=False, p=p))
+        out[0, r] = prev
+        for st in range(1, steps):
+            m = int(g.binomial(k, overlap))
+            keep = g.choice(prev, size=m, replace=False) if m else np.empty(0, np.int64)
+            mask = np.ones(E, dtype=bool)
+            mask[prev] = False
+            q = np.where(mask, p, 0.0)
+            q /= q.sum()
+            new = g.choice(E, size=k - m, replace=False, p=q)
+            prev = np.sort(np.concatenate([keep, new]).astype(np.int64))
+            out[st, r] = prev
+    return out
+
+
+def bias_from_sets(sets_step: np.ndarray, E: int) -> np.ndarray:
+    """Router bias [T][E] fp32: BIAS_STRENGTH on each row's drawn set."""
+    T = sets_step.shape[0]
+    b = np.zeros((T, E), dtype=np.float32)
+    b[np.arange(T)[:, None], sets_step] = BIAS_STRENGTH
+    return b

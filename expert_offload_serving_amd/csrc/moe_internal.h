@@ -1,0 +1,196 @@
+// Internal declarations of libmoe: context, device layouts, kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// MXFP4 expert record in the library's tiled layout.
+//
+// A matrix W [N rows][K] (rows = output features) is cut into atoms of
+// 16 rows x 128 K.  One atom is 1088 contiguous bytes:
+//   bytes [0, 1024): 64 lanes x 16 bytes.  Lane l holds row (l % 16); its
+//     4-byte word j (j = 0..3) holds the 8 E2M1 codes of K range
+//     [32 j + 8 (l / 16), +8) of the chunk, low nibble first.  This is the
+//     B-operand layout of v_mfma_f32_16x16x32_bf16 for four K=32 steps, so a
+//     wave loads an atom with one 16-byte load per lane.
+//   bytes [1024, 1088): E8M0 scales, [row 0..15][block j 0..3].
+// Gate and up are fused: row groups alternate 16 gate rows, 16 up rows
+// (group 2p = gate rows 16p..16p+15, 2p+1 = up rows of the same indices).
+// Record = [gate/up atoms: group-major, K-chunk minor] [down atoms: same].
+// Total = 3*H*I*17/32 bytes, the MXFP4 size.
+// ---------------------------------------------------------------------------
+constexpr int kAtomRows = 16;
+constexpr int kAtomK = 128;
+constexpr int kAtomData = 1024;
+constexpr int kAtomBytes = 1088;
+
+inline size_t expert_record_bytes(int H, int I) { return (size_t)3 * H * I * 17 / 32; }
+inline size_t gateup_section_bytes(int H, int I) { return (size_t)2 * I * H * 17 / 32; }
+
+// Host-side repack of one canonical MXFP4 matrix [N][K] into atoms.
+// fuse_pair: the matrix is gate (even groups) / up (odd groups) pair; pass
+// both sources.  Out must hold N*K*17/32 (or twice that for fused) bytes.
+void repack_gateup(const uint8_t* qg, const uint8_t* sg, const uint8_t* qu,
+                   const uint8_t* su, int I, int H, uint8_t* out);
+void repack_down(const uint8_t* qd, const uint8_t* sd, int H, int I, uint8_t* out);
+
+// ---------------------------------------------------------------------------
+// Device-side work descriptors written by the routing kernels.
+// ---------------------------------------------------------------------------
+struct WorkItem {          // one expert's share of a decode call
+  const uint8_t* w;        // expert record (cache slot, staging or shared)
+  int32_t pos0;            // first row in the permuted order
+  int32_t cnt;             // rows (tokens) routed to it
+};
+
+struct FillEntry {         // one host-pool -> HBM expert copy
+  const uint8_t* src;      // pinned host record (device-mapped)
+  uint8_t* dst;            // cache or staging slot
+};
+
+// Small per-call counters kept on the device.
+struct DevMeta {
+  int32_t T;
+  int32_t n_unique;
+  int32_t n_items;
+  int32_t n_fill;
+  int32_t n_hit;
+  int32_t n_bypass;
+  int32_t pad[2];
+};
+
+// Cache state and statistics on the device.
+struct DevCache {
+  uint64_t clock;
+  uint64_t lookups, hits, fills, bypasses, evictions;
+};
+
+// Arguments of the block-wide LRU lookup.
+struct LookupArgs {
+  int32_t layer, E, C, staging;
+  int32_t* key;            // [C]
+  uint64_t* stamp;         // [C]
+  int32_t* order;          // [C] slots from least to most recent
+  int32_t* order_tmp;      // [C]
+  int32_t* map;            // [L*E] slot of each key or -1
+  uint8_t* hitflag;        // [C]
+  int32_t* victim;         // [max unique]
+  DevCache* cache;
+  const uint8_t* pool;     // pinned host pool (device-mapped)
+  uint8_t* slots;          // [C] records
+  uint8_t* staging_buf;    // [S] records
+  size_t stride;           // bytes between records
+  FillEntry* fills;        // [max unique]
+  DevMeta* meta;
+};
+
+// ---------------------------------------------------------------------------
+// Context
+// ---------------------------------------------------------------------------
+struct Ctx {
+  moe_config cfg{};
+  int device = 0;
+  size_t rec_bytes = 0;     // 3*H*I*17/32
+  size_t stride = 0;        // record stride (256-byte multiple)
+  int max_unique = 0;       // min(T_max*k, E)
+  int max_items = 0;        // max_unique + has_shared
+  int rows_max = 0;         // T_max*k + T_max (shared rows)
+  int n_chunks_max = 0;     // router H chunks
+
+  // host pool and HBM weights
+  uint8_t* pool = nullptr;          // pinned, [L][E] records
+  float* d_router = nullptr;        // [L][H][E]
+  uint8_t* d_shared = nullptr;      // [L] records
+  std::vector<uint8_t> router_set;  // per layer
+  std::vector<uint8_t> shared_set;
+
+  // cache
+  int C = 0;
+  uint8_t* d_slots = nullptr;       // [C] records
+  uint8_t* d_staging = nullptr;     // [S] records
+  int32_t* d_key = nullptr;
+  uint64_t* d_stamp = nullptr;
+  int32_t* d_order = nullptr;
+  int32_t* d_order_tmp = nullptr;
+  uint8_t* d_hitflag = nullptr;
+  int32_t* d_map = nullptr;         // [L*E]
+  int32_t* d_victim = nullptr;
+  DevCache* d_cache = nullptr;
+
+  // decode scratch
+  double* d_partials = nullptr;     // [n_chunks][T_max][E]
+  float* d_logits = nullptr;        // [T_max][E]
+  int32_t* d_ids = nullptr;         // [T_max*k]
+  float* d_gates = nullptr;         // [T_max*k]
+  int32_t* d_counts = nullptr;      // [E]
+  int32_t* d_offsets = nullptr;     // [E+1]
+  int32_t* d_sorted = nullptr;      // [T_max*k]
+  int32_t* d_inv = nullptr;         // [T_max*k]
+  int32_t* d_unique = nullptr;      // [E]
+  int32_t* d_slotcode = nullptr;    // [E]
+  int32_t* d_tok = nullptr;         // [rows_max] token of each permuted row
+  WorkItem* d_items = nullptr;      // [max_items]
+  FillEntry* d_fills = nullptr;     // [max_unique]
+  DevMeta* d_meta = nullptr;
+  uint16_t* d_h = nullptr;          // bf16 [rows_max][I]
+  float* d_yperm = nullptr;         // [rows_max][H]
+  int32_t* d_lookup_ids = nullptr;  // [E] for expert_cache_fill
+
+  // prefill (allocated on first use)
+  int Tp_max = 0;
+  uint8_t* d_layerbuf[2] = {nullptr, nullptr};
+  hipStream_t copy_stream = nullptr;
+  hipEvent_t ev_upload[2] = {nullptr, nullptr};
+  hipEvent_t ev_compute[2] = {nullptr, nullptr};
+  struct Prefill* pf = nullptr;
+
+  // timing
+  bool timing = false;
+  std::vector<hipEvent_t> ev_pool;  // pairs, reused
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> t_decode, t_prefill;
+  size_t ev_next = 0;
+
+  // host-side counters not tracked on the device
+  moe_stats host_stats{};
+};
+
+// ---------------------------------------------------------------------------
+// Launchers (each enqueues on `st` and returns hipGetLastError()).
+// ---------------------------------------------------------------------------
+int router_chunk_rows(int H);
+hipError_t launch_router_partial(const uint16_t* x, int T, int H, int E,
+                                 const float* w_router, double* partials,
+                                 hipStream_t st);
+hipError_t launch_route_finalize(Ctx* c, int layer, int T, const float* bias,
+                                 int32_t* user_ids, float* user_gates,
+                                 hipStream_t st);
+hipError_t launch_cache_lookup(Ctx* c, int layer, const int32_t* d_experts,
+                               const int32_t* d_n, int n_max, int32_t* d_slot,
+                               hipStream_t st);
+hipError_t launch_fill(const FillEntry* fills, const DevMeta* meta, int max_fill,
+                       size_t bytes, hipStream_t st);
+hipError_t launch_copy_pairs(const FillEntry* pairs, int n, size_t bytes,
+                             hipStream_t st);
+hipError_t launch_probe_copy(const void* src, void* dst, size_t n_bytes,
+                             hipStream_t st);
+hipError_t launch_expert_gateup(const Ctx* c, const uint16_t* x, int T,
+                                hipStream_t st);
+hipError_t launch_expert_down(const Ctx* c, int T, hipStream_t st);
+hipError_t launch_combine(const Ctx* c, int T, uint16_t* y, float* y32, hipStream_t st);
+
+// prefill
+hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* x, int T,
+                           const float* const* bias, void* const* y, float* const* y32,
+                           hipStream_t st);
+void prefill_free(Ctx* c);
+
+}  // namespace moe

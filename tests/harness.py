@@ -1,0 +1,173 @@
+"""Drive the HIP library (through its C ABI) and the CPU oracle on the same
+seeded synthetic inputs.  Used by the GPU tests, smoke and bench."""
+from __future__ import annotations
+
+from collections import OrderedDict
+from dataclasses import replace
+from typing import Optional
+
+import numpy as np
+
+import oracle
+from oracle import experts as oexp
+from workload import gen
+
+RTOL_Y = 2e-2     # max |y - y_ref| <= RTOL_Y * rms(y_ref), per call
+ATOL_G = 1e-6     # gates
+TOL_SUM = 1e-6    # |sum(g) - 1| with renormalisation
+
+
+def bf16_dev(bits: np.ndarray, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device)
+
+
+def bf16_host(t) -> np.ndarray:
+    return gen.bf16_bits_to_f32(t.cpu().numpy().view(np.uint16))
+
+
+class Model:
+    """Weights of a workload's layer stack: uploaded to an engine, and
+    dequantised on demand for the oracle (bounded cache)."""
+
+    def __init__(self, shape: gen.Shape, seed: int = 0, cache_entries: int = 32):
+        self.shape = shape
+        self.seed = seed
+        self.routers = [gen.router_weights(shape, l, seed) for l in range(shape.layers)]
+        self._mats = OrderedDict()
+        self._cap = cache_entries
+
+    def expert(self, layer: int, e: int):
+        return gen.expert_weights(self.shape, layer, e, self.seed)
+
+    def mats(self, layer: int, e: int):
+        key = (layer, e)
+        if key in self._mats:
+            self._mats.move_to_end(key)
+            return self._mats[key]
+        m = oexp.dequant_expert(self.expert(layer, e))
+        self._mats[key] = m
+        if len(self._mats) > self._cap:
+            self._mats.popitem(last=False)
+        return m
+
+    def load(self, eng):
+        for l in range(self.shape.layers):
+            eng.set_router(l, self.routers[l])
+            for e in range(self.shape.E):
+                eng.set_expert(l, e, self.expert(l, e))
+            if self.shape.shared:
+                eng.set_expert(l, -1, self.expert(l, -1))
+
+    # oracle
+    def route(self, layer, x, bias):
+        return oracle.route(x, self.routers[layer], self.shape.k, bias, self.shape.renormalize)
+
+    def layer_out(self, layer, x, ids, g, tokens=None):
+        sh = self.mats(layer, -1) if self.shape.shared else None
+        return oracle.moe_layer(x, ids, g, lambda e: self.mats(layer, e), shared=sh, tokens=tokens)
+
+
+def make_engine(shape: gen.Shape, max_tokens: int, cache_slots: int, staging_slots: int,
+                max_prefill_tokens: int = 0):
+    from expert_offload_serving_amd import MoEEngine
+    return MoEEngine(shape.H, shape.I, shape.E, shape.k, n_layers=shape.layers,
+                     has_shared=shape.shared, renormalize=shape.renormalize,
+                     max_tokens=max_tokens, cache_slots=cache_slots,
+                     staging_slots=staging_slots, max_prefill_tokens=max_prefill_tokens)
+
+
+def check_rounding(y_bf16, y32, what=""):
+    """The bf16 output must be the fp32 result rounded to nearest even."""
+    bits = y_bf16.cpu().numpy().view(np.uint16)
+    want = gen.f32_to_bf16_bits(y32.cpu().numpy())
+    assert np.array_equal(bits, want), f"{what}: bf16 output is not RNE of the fp32 result"
+
+
+def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, rows=None, what=""):
+    """max |y - y_ref| <= RTOL_Y * rms(y_ref) over the checked rows; y_gpu is
+    the fp32 combine result (before the bf16 rounding, checked separately)."""
+    if rows is not None:
+        y_gpu, y_ref = y_gpu[rows], y_ref[rows]
+    rms = float(np.sqrt(np.mean(y_ref.astype(np.float64) ** 2)))
+    err = float(np.max(np.abs(y_gpu.astype(np.float64) - y_ref)))
+    assert err <= RTOL_Y * rms, f"{what}: max|dy| = {err:.4g} > {RTOL_Y} x rms {rms:.4g}"
+    return err / rms
+
+
+class DecodeRun:
+    """Runs decode steps of one workload on the GPU and the oracle side by side."""
+
+    def __init__(self, wl: gen.Workload, model: Model, T: int, cache_slots: Optional[int] = None,
+                 staging_slots: Optional[int] = None, max_tokens: Optional[int] = None,
+                 steps: Optional[int] = None):
+        import torch
+        self.wl, self.model, self.T = wl, model, T
+        sh = wl.shape
+        self.C = wl.cache_slots if cache_slots is None else cache_slots
+        S = wl.staging_slots if staging_slots is None else staging_slots
+        self.eng = make_engine(sh, max_tokens or T, self.C, S)
+        model.load(self.eng)
+        self.cache = oracle.SlotCache(self.C, sh.E)
+        self.steps = wl.steps if steps is None else steps
+        self.sets = ([gen.zipf_sets(sh, l, T, self.steps, wl.zipf_s, wl.overlap, model.seed)
+                      for l in range(sh.layers)] if wl.zipf_s else None)
+        self.dev = torch.device("cuda")
+        self.ids = torch.empty((T, sh.k), dtype=torch.int32, device=self.dev)
+        self.gates = torch.empty((T, sh.k), dtype=torch.float32, device=self.dev)
+        self.y32 = torch.empty((T, sh.H), dtype=torch.float32, device=self.dev)
+        if wl.preload_all:
+            for l in range(sh.layers):
+                self.preload(l, list(range(sh.E)))
+
+    def preload(self, layer, experts):
+        self.eng.cache_fill(layer, experts)
+        self.cache.fill(layer, experts)
+
+    def inputs(self, layer, step):
+        sh = self.wl.shape
+        xb = gen.tokens(sh, layer, step, self.T, self.model.seed)
+        bias = gen.bias_from_sets(self.sets[layer][step], sh.E) if self.sets else None
+        return xb, bias
+
+    def step(self, layer, step, check_out=False, check_state=True, out_tokens=None):
+        import torch
+        sh = self.wl.shape
+        xb, bias = self.inputs(layer, step)
+        x = bf16_dev(xb)
+        bdev = torch.from_numpy(bias).to(self.dev) if bias is not None else None
+        y = self.eng.forward(layer, x, bias=bdev, ids=self.ids, gates=self.gates, y32=self.y32)
+        xf = gen.bf16_bits_to_f32(xb)
+        lg, ids_ref, g_ref = self.model.route(layer, xf, bias)
+        ids = self.ids.cpu().numpy()
+        assert np.array_equal(ids, ids_ref), f"ids differ at layer {layer} step {step}"
+        g = self.gates.cpu().numpy()
+        assert np.max(np.abs(g - g_ref)) <= ATOL_G, f"gates differ at layer {layer} step {step}"
+        if sh.renormalize:
+            assert np.max(np.abs(g.astype(np.float64).sum(1) - 1)) <= TOL_SUM
+        perm = oracle.permutation(ids_ref, sh.E)
+        slots_ref, fills, bypass = self.cache.lookup(layer, perm["unique"])
+        if check_state:
+            d = self.eng.inspect_dispatch()
+            for k in ("counts", "offsets", "sorted", "inv", "unique"):
+                assert np.array_equal(d[k], perm[k]), f"{k} differs at layer {layer} step {step}"
+            assert d["slot"].tolist() == slots_ref, f"slots differ at layer {layer} step {step}"
+            key, stamp, clock = self.eng.cache_snapshot()
+            k_ref, s_ref, c_ref = self.cache.snapshot()
+            assert key.tolist() == k_ref and stamp.tolist() == s_ref and clock == c_ref, \
+                f"cache state differs at layer {layer} step {step}"
+        err = None
+        if check_out:
+            what = f"layer {layer} step {step}"
+            check_rounding(y, self.y32, what)
+            y_ref = self.model.layer_out(layer, xf, ids_ref, g_ref, tokens=out_tokens)
+            err = check_y(self.y32.cpu().numpy(), y_ref, rows=out_tokens, what=what)
+        return y, err
+
+    def close(self):
+        self.eng.close()
+
+
+def small_shape(**kw) -> gen.Shape:
+    base = gen.Shape(H=256, I=512, E=8, k=2)
+    return replace(base, **kw)

@@ -57,7 +57,7 @@ void destroy_all(Ctx* c) {
   dfree(c->d_router); dfree(c->d_shared); dfree(c->d_slots); dfree(c->d_staging);
   dfree(c->d_key); dfree(c->d_stamp); dfree(c->d_order); dfree(c->d_order_tmp);
   dfree(c->d_hitflag); dfree(c->d_map); dfree(c->d_victim); dfree(c->d_cache);
-  dfree(c->d_partials); dfree(c->d_logits); dfree(c->d_ids); dfree(c->d_gates);
+  dfree(c->d_logits); dfree(c->d_ids); dfree(c->d_gates);
   dfree(c->d_counts); dfree(c->d_offsets); dfree(c->d_sorted); dfree(c->d_inv);
   dfree(c->d_unique); dfree(c->d_slotcode); dfree(c->d_tok); dfree(c->d_items);
   dfree(c->d_fills); dfree(c->d_meta); dfree(c->d_h); dfree(c->d_yperm);
@@ -124,19 +124,15 @@ namespace moe {
 
 // --------------------------------------------------------------- repacking
 // Canonical row r of a [N][K] MXFP4 matrix: codes q[r][K/2], scales s[r][K/32].
+// Lane l of the atom takes row row0 + l % 16, MX block 4 c + l / 16.
 static void write_atom(const uint8_t* q, const uint8_t* s, int K, int row0, int c,
                        uint8_t* atom) {
   const int kc = K / 2, sc = K / 32;
   for (int l = 0; l < 64; l++) {
-    const int r = row0 + (l % 16), g = l / 16;
-    for (int j = 0; j < 4; j++) {
-      const int k0 = c * kAtomK + 32 * j + 8 * g;   // even: 4 whole bytes
-      std::memcpy(atom + l * 16 + j * 4, q + (size_t)r * kc + k0 / 2, 4);
-    }
+    const int r = row0 + (l % 16), blk = c * 4 + l / 16;
+    std::memcpy(atom + l * 16, q + (size_t)r * kc + (size_t)blk * 16, 16);
+    atom[kAtomData + l] = s[(size_t)r * sc + blk];
   }
-  for (int r = 0; r < 16; r++)
-    for (int j = 0; j < 4; j++)
-      atom[kAtomData + r * 4 + j] = s[(size_t)(row0 + r) * sc + c * 4 + j];
 }
 
 void repack_gateup(const uint8_t* qg, const uint8_t* sg, const uint8_t* qu,
@@ -182,8 +178,12 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     return fail(MOE_ERR_INVALID_ARG, "moe_config field out of range");
   if ((int64_t)f.cache_slots > (int64_t)f.n_layers * f.n_experts)
     return fail(MOE_ERR_INVALID_ARG, "cache_slots exceeds n_layers*n_experts");
-  if (f.hidden % 128 || f.inter % 128)
-    return fail(MOE_ERR_UNSUPPORTED, "hidden and inter must be multiples of 128");
+  if ((int64_t)f.n_layers * f.n_experts >= (1 << (31 - kOrderKeyShift)))
+    return fail(MOE_ERR_UNSUPPORTED, "n_layers*n_experts too large");
+  if (f.hidden % 128 || f.inter % 128 || f.hidden > kMaxH || f.inter > kMaxH)
+    return fail(MOE_ERR_UNSUPPORTED, "hidden and inter must be multiples of 128, at most 6144");
+  if (f.cache_slots > kMaxCacheSlots)
+    return fail(MOE_ERR_UNSUPPORTED, "cache_slots above 4096");
   if (f.max_prefill_tokens > (1 << 20))
     return fail(MOE_ERR_INVALID_ARG, "max_prefill_tokens too large");
 
@@ -198,7 +198,6 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   c->max_unique = std::min(Tm * k, E);
   c->max_items = c->max_unique + f.has_shared;
   c->rows_max = Tm * k + Tm;
-  c->n_chunks_max = (H + router_chunk_rows(H) - 1) / router_chunk_rows(H);
   c->C = f.cache_slots;
   c->router_set.assign(L, 0);
   c->shared_set.assign(L, 0);
@@ -224,7 +223,6 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   ALLOC(c->d_map, (size_t)L * E * 4);
   ALLOC(c->d_victim, (size_t)c->max_unique * 4);
   ALLOC(c->d_cache, sizeof(DevCache));
-  ALLOC(c->d_partials, (size_t)c->n_chunks_max * Tm * E * sizeof(double));
   ALLOC(c->d_logits, (size_t)Tm * E * 4);
   ALLOC(c->d_ids, (size_t)Tm * k * 4);
   ALLOC(c->d_gates, (size_t)Tm * k * 4);
@@ -238,12 +236,12 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   ALLOC(c->d_items, (size_t)c->max_items * sizeof(WorkItem));
   ALLOC(c->d_fills, (size_t)c->max_unique * sizeof(FillEntry));
   ALLOC(c->d_meta, sizeof(DevMeta));
-  ALLOC(c->d_h, (size_t)c->rows_max * I * 2);
+  ALLOC(c->d_h, (size_t)c->rows_max * I * 2 * 2);  // hi and lo bf16 planes
   ALLOC(c->d_yperm, (size_t)c->rows_max * H * 4);
   ALLOC(c->d_lookup_ids, (size_t)(E + 1) * 4);
 
   std::vector<int32_t> key(std::max(c->C, 1), -1), order(std::max(c->C, 1)), map((size_t)L * E, -1);
-  std::iota(order.begin(), order.end(), 0);
+  std::iota(order.begin(), order.end(), 0);  // all empty: slot | (0 << kOrderKeyShift)
   std::vector<uint64_t> stamp(std::max(c->C, 1), 0);
   std::vector<uint8_t> zero(sizeof(DevCache) > sizeof(DevMeta) ? sizeof(DevCache) : sizeof(DevMeta), 0);
   if (upload(c->d_key, key) != hipSuccess || upload(c->d_order, order) != hipSuccess ||
@@ -273,8 +271,12 @@ moe_status moe_set_router(moe_ctx* ctx, int32_t layer, const float* h_router) {
   Ctx* c = C_(ctx);
   if (layer < 0 || layer >= c->cfg.n_layers || !h_router)
     return fail(MOE_ERR_INVALID_ARG, "bad layer or NULL router");
-  const size_t n = (size_t)c->cfg.hidden * c->cfg.n_experts;
-  HIPCHK(hipMemcpy(c->d_router + (size_t)layer * n, h_router, n * 4, hipMemcpyHostToDevice));
+  const size_t H = c->cfg.hidden, E = c->cfg.n_experts;
+  std::vector<float> t(H * E);  // [E][H]: one expert's column contiguous
+  for (size_t h = 0; h < H; h++)
+    for (size_t e = 0; e < E; e++) t[e * H + h] = h_router[h * E + e];
+  HIPCHK(hipMemcpy(c->d_router + (size_t)layer * H * E, t.data(), H * E * 4,
+                   hipMemcpyHostToDevice));
   c->router_set[layer] = 1;
   return MOE_OK;
 }
@@ -353,9 +355,9 @@ moe_status moe_layer_forward(moe_ctx* ctx, int32_t layer, const void* d_x, int32
                                       std::to_string(worst_bypass));
   hipStream_t st = (hipStream_t)stream;
   const float* wr = c->d_router + (size_t)layer * f.hidden * f.n_experts;
-  HIPCHK(launch_router_partial((const uint16_t*)d_x, T, f.hidden, f.n_experts, wr,
-                               c->d_partials, st));
-  HIPCHK(launch_route_finalize(c, layer, T, d_bias, d_ids, d_gates, st));
+  HIPCHK(launch_router((const uint16_t*)d_x, T, f.hidden, f.n_experts, wr, d_bias, c->d_logits,
+                       st));
+  HIPCHK(launch_route_finalize(c, layer, T, d_ids, d_gates, st));
   HIPCHK(launch_fill(c->d_fills, c->d_meta, c->max_unique, c->rec_bytes, st));
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (c->timing && c->t_decode.size() < kMaxTimingPairs) {
@@ -445,6 +447,7 @@ moe_status expert_cache_resize(moe_ctx* ctx, int32_t new_slots, void* stream) {
   const int L = c->cfg.n_layers, E = c->cfg.n_experts;
   if (new_slots < 0 || (int64_t)new_slots > (int64_t)L * E)
     return fail(MOE_ERR_INVALID_ARG, "new_slots outside [0, n_layers*n_experts]");
+  if (new_slots > kMaxCacheSlots) return fail(MOE_ERR_UNSUPPORTED, "cache_slots above 4096");
   hipStream_t st = (hipStream_t)stream;
   HIPCHK(hipStreamSynchronize(st));
   HIPCHK(hipDeviceSynchronize());
@@ -510,6 +513,7 @@ moe_status expert_cache_resize(moe_ctx* ctx, int32_t new_slots, void* stream) {
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
     return (key2[a] < 0 ? 0 : stamp2[a]) < (key2[b] < 0 ? 0 : stamp2[b]);
   });
+  for (auto& o : order) o |= (key2[o] + 1) << kOrderKeyShift;
   std::vector<int32_t> map((size_t)L * E, -1);
   for (int s = 0; s < C2; s++) if (key2[s] >= 0) map[key2[s]] = s;
   dfree(c->d_key); dfree(c->d_stamp); dfree(c->d_order); dfree(c->d_order_tmp); dfree(c->d_hitflag);

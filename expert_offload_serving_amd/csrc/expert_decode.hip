@@ -1,14 +1,25 @@
 // Decode expert FFN: grouped skinny GEMMs over the experts of one call.
 //
 // Each expert of the call has 1..T tokens.  Its weights are streamed once
-// from HBM in 1088-byte MXFP4 atoms (one 16-byte load per lane), dequantised
-// in registers with the gfx950 scaled FP4 -> bf16 convert, and multiplied on
-// v_mfma_f32_16x16x32_bf16 with the tokens as the 16-row A operand.  The
-// kernels are HBM-bound: MFMA replaces the per-lane dot products and wave
-// reductions a VALU GEMV would need, keeping VALU work per weight byte flat
-// in the token count.  FFN: o = W_d (silu(W_g x) * (W_u x)); the pages name
-// MXFP4 experts (jansverre.net FreeToken article, section "Hvor raskt kjører
-// modellene?") but not the FFN form, which is SwiGLU here.
+// from HBM in 1088-byte MXFP4 atoms (one 16-byte load per lane, one lane per
+// MX block), dequantised in registers with the gfx950 scaled FP4 -> bf16
+// convert, and multiplied on v_mfma_f32_16x16x32_bf16 with up to 16 tokens as
+// the A operand.  The kernels are HBM-bound, so the design is about bytes in
+// flight: a workgroup owns one 16-row output tile (a gate/up pair, or a down
+// row group) of one expert and splits K over up to 16 waves; every wave
+// issues all of its weight and activation loads before its first MFMA, and
+// the waves' partial tiles are summed through LDS in a fixed order (results
+// do not depend on where an expert's weights live).  MFMA replaces the
+// per-lane dot products and wave reductions of a VALU GEMV, keeping VALU work
+// per weight byte flat in the token count.
+//
+// FFN: o = W_d (silu(W_g x) * (W_u x)); the pages name MXFP4 experts
+// (jansverre.net FreeToken article, section "Hvor raskt kjører modellene?")
+// but not the FFN form, which is SwiGLU here.  h passes between the two
+// kernels as a hi/lo pair of bf16 values (two MFMAs per weight fragment in
+// the down kernel, free while HBM-bound), so it keeps ~16 significant bits.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -18,12 +29,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMT = 4;  // 16-token M tiles per pass
+constexpr int kMaxWaves = 16;
 
-// 8 E2M1 codes (one dword, low nibble first) times 2^(s-127) -> 8 bf16.
+__device__ __forceinline__ float scale_of(uint32_t sbyte) { return __uint_as_float(sbyte << 23); }
+
+// 8 E2M1 codes (one dword, low nibble first) times 2^(sbyte-127) -> 8 bf16.
 // The convert reads only the exponent field of its fp32 scale operand.
 __device__ __forceinline__ bf16x8 dequant8(uint32_t q, uint32_t sbyte) {
-  const float s = __uint_as_float(sbyte << 23);
+  const float s = scale_of(sbyte);
   u32x4 r;
   r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 0));
   r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 1));
@@ -38,146 +51,221 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
 
-__device__ __forceinline__ bf16x8 load_a(const uint16_t* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
+typedef __attribute__((address_space(1))) const u32x4 gu32x4;
+typedef __attribute__((address_space(1))) const uint8_t gu8;
+
+// Global-address-space loads (global_load rather than flat_load).
+__device__ __forceinline__ u32x4 load_atom_data(const uint8_t* atom, int lane) {
+  return *(gu32x4*)(atom + lane * 16);
+}
+__device__ __forceinline__ uint32_t load_scale(const uint8_t* atom, int lane) {
+  return *(gu8*)(atom + kAtomData + lane);
 }
 
-// Gate/up + SwiGLU.  Block (p, item): row pair p (16 gate + 16 up rows) of
-// one expert; the 4 waves split K and are reduced through LDS in fixed order.
-__global__ __launch_bounds__(256) void gateup_decode_kernel(
+// Activation loads go through a bounds-checked buffer resource: a lane whose
+// row does not exist passes an out-of-range offset and reads zeros without
+// touching memory (no branch, no wait at a branch join).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ bf16x8 bload8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// Gate/up + SwiGLU.  Block (pair p, item): 16 gate and 16 up rows of one
+// expert; wave w takes K chunks [w*CPW, w*CPW+CPW).  M tiles of 16 tokens
+// are processed one after another (weights re-read from L2 after the first).
+// Small workgroups that finish independently keep a CU's memory pipeline
+// full better than large ones that must be resident as a whole.
+template <int CPW>
+__global__ __launch_bounds__(1024) void gateup_decode_kernel(
     const WorkItem* __restrict__ items, const DevMeta* __restrict__ meta,
-    const int32_t* __restrict__ tok, const uint16_t* __restrict__ x, int H, int I,
-    uint16_t* __restrict__ h) {
+    const int32_t* __restrict__ tok, const uint16_t* __restrict__ x, uint32_t x_bytes, int H,
+    int I, uint16_t* __restrict__ h, size_t lo_plane) {
   const int item = blockIdx.y;
   if (item >= meta->n_items) return;
   const WorkItem it = items[item];
   const int p = blockIdx.x;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int KC = H / kAtomK;
   const uint8_t* gbase = it.w + (size_t)(2 * p) * KC * kAtomBytes;
   const uint8_t* ubase = gbase + (size_t)KC * kAtomBytes;
-  __shared__ f32x4 red[4][2][kMT][64];
-  const bf16x8 zero = {};
+  __shared__ f32x4 red[kMaxWaves][2][64];
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, x_bytes);
 
-  for (int m0 = 0; m0 < it.cnt; m0 += 16 * kMT) {
-    const int mt_n = min(kMT, (it.cnt - m0 + 15) / 16);
-    const uint16_t* xrow[kMT];
+  // Token row of this lane in the first M tile.
+  const int trow = (lane & 15) < it.cnt ? tok[it.pos0 + (lane & 15)] : 0;
+  // Weight loads are unconditional: a chunk past K (only when waves do not
+  // divide K) reads chunk 0, whose finite values meet zero activations.
+  // A guarded load would wait at its branch instead of staying in flight.
+  u32x4 wg[CPW], wu[CPW];
+  uint32_t sg[CPW], su[CPW];
 #pragma unroll
-    for (int mt = 0; mt < kMT; mt++) {
-      const int m = m0 + mt * 16 + (lane & 15);
-      xrow[mt] = (mt < mt_n && m < it.cnt)
-                     ? x + (size_t)tok[it.pos0 + m] * H + 8 * (lane >> 4)
-                     : nullptr;
+  for (int cc = 0; cc < CPW; cc++) {
+    const int c = w * CPW + cc;
+    const uint8_t* ga = gbase + (size_t)(c < KC ? c : 0) * kAtomBytes;
+    const uint8_t* ua = ubase + (size_t)(c < KC ? c : 0) * kAtomBytes;
+    wg[cc] = load_atom_data(ga, lane);
+    wu[cc] = load_atom_data(ua, lane);
+    sg[cc] = load_scale(ga, lane);
+    su[cc] = load_scale(ua, lane);
+  }
+
+  // One M tile of 16 tokens.  The first tile is peeled out of the loop so
+  // that its loads are scheduled against the weight loads precisely.
+  auto tile = [&](int m0, int trow) {
+    const int m = m0 + (lane & 15);
+    const bool mok = m < it.cnt;
+    // byte offset of this lane's 32 activations in chunk c, or out of range
+    const uint32_t xrow = (uint32_t)(trow * H + 32 * (lane >> 4)) * 2u;
+    auto xoff = [&](int c) { return (mok && c < KC) ? xrow + (uint32_t)c * kAtomK * 2u : kOutOfRange; };
+    // activation fragments (L2-resident) are fetched one chunk ahead
+    bf16x8 xa[2][4];
+    {
+      const uint32_t o = xoff(w * CPW);
+#pragma unroll
+      for (int j = 0; j < 4; j++) xa[0][j] = bload8(rx, o + 16u * j);
     }
-    f32x4 accg[kMT], accu[kMT];
+    f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mt = 0; mt < kMT; mt++) accg[mt] = accu[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int c = w; c < KC; c += 4) {
-      const uint8_t* ga = gbase + (size_t)c * kAtomBytes;
-      const uint8_t* ua = ubase + (size_t)c * kAtomBytes;
-      const u32x4 dg = *reinterpret_cast<const u32x4*>(ga + lane * 16);
-      const u32x4 du = *reinterpret_cast<const u32x4*>(ua + lane * 16);
-      const uint32_t sg = *reinterpret_cast<const uint32_t*>(ga + kAtomData + (lane & 15) * 4);
-      const uint32_t su = *reinterpret_cast<const uint32_t*>(ua + kAtomData + (lane & 15) * 4);
+    for (int cc = 0; cc < CPW; cc++) {
+      const int c = w * CPW + cc;
+      if (cc + 1 < CPW) {
+        const uint32_t o = xoff(c + 1);
+#pragma unroll
+        for (int j = 0; j < 4; j++) xa[(cc + 1) & 1][j] = bload8(rx, o + 16u * j);
+      }
+      if (cc == 0) {
+        // The packed weights stay in registers across M tiles; hiding them
+        // from loop-invariant motion keeps the (4x larger) dequantised
+        // fragments from being hoisted out of the tile loop and held live.
+#pragma unroll
+        for (int q = 0; q < CPW; q++)
+          asm volatile("" : "+v"(wg[q]), "+v"(wu[q]), "+v"(sg[q]), "+v"(su[q]));
+      }
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        const bf16x8 bg = dequant8(dg[j], (sg >> (8 * j)) & 0xFFu);
-        const bf16x8 bu = dequant8(du[j], (su >> (8 * j)) & 0xFFu);
-#pragma unroll
-        for (int mt = 0; mt < kMT; mt++) {
-          if (mt < mt_n) {
-            const bf16x8 a = xrow[mt] ? load_a(xrow[mt] + c * kAtomK + 32 * j) : zero;
-            accg[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bg, accg[mt], 0, 0, 0);
-            accu[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bu, accu[mt], 0, 0, 0);
-          }
-        }
+        ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[cc & 1][j], dequant8(wg[cc][j], sg[cc]), ag, 0, 0, 0);
+        au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[cc & 1][j], dequant8(wu[cc][j], su[cc]), au, 0, 0, 0);
+        // keep each fragment's dequant next to its MFMAs (bounds live registers)
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-#pragma unroll
-    for (int mt = 0; mt < kMT; mt++) {
-      if (mt < mt_n) {
-        red[w][0][mt][lane] = accg[mt];
-        red[w][1][mt][lane] = accu[mt];
+    red[w][0][lane] = ag;
+    red[w][1][lane] = au;
+    __syncthreads();
+    for (int v0 = threadIdx.x; v0 < 256; v0 += blockDim.x) {  // 64 lanes x 4 values
+      const int L = v0 >> 2, i = v0 & 3;
+      float gs = 0.f, us = 0.f;
+      for (int v = 0; v < nw; v++) {
+        gs += red[v][0][L][i];
+        us += red[v][1][L][i];
+      }
+      const int mm = m0 + 4 * (L >> 4) + i;
+      if (mm < it.cnt) {
+        const float hv = silu(gs) * us;
+        const uint16_t hi = f32_to_bf16_rne(hv);
+        const size_t o = (size_t)(it.pos0 + mm) * I + p * 16 + (L & 15);
+        h[o] = hi;
+        h[lo_plane + o] = f32_to_bf16_rne(hv - bf16_to_f32(hi));
       }
     }
     __syncthreads();
-    if (w < mt_n) {
-      const int mt = w;
-      const f32x4 g = ((red[0][0][mt][lane] + red[1][0][mt][lane]) + red[2][0][mt][lane]) +
-                      red[3][0][mt][lane];
-      const f32x4 u = ((red[0][1][mt][lane] + red[1][1][mt][lane]) + red[2][1][mt][lane]) +
-                      red[3][1][mt][lane];
-      const int col = p * 16 + (lane & 15);
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int m = m0 + mt * 16 + 4 * (lane >> 4) + i;
-        if (m < it.cnt)
-          h[(size_t)(it.pos0 + m) * I + col] = f32_to_bf16_rne(silu(g[i]) * u[i]);
-      }
-    }
-    __syncthreads();
+  };
+  tile(0, trow);
+  for (int m0 = 16; m0 < it.cnt; m0 += 16) {
+    const int m = m0 + (lane & 15);
+    tile(m0, m < it.cnt ? tok[it.pos0 + m] : 0);
   }
 }
 
-// Down projection.  Block (rb, item): 4 row groups (64 rows of H), one per
-// wave, over the full K = I.
-__global__ __launch_bounds__(256) void down_decode_kernel(
+// Down projection.  Block (row group rg, item): 16 rows of H of one expert;
+// waves split K = I; each weight fragment meets both h planes.
+template <int CPW>
+__global__ __launch_bounds__(1024) void down_decode_kernel(
     const WorkItem* __restrict__ items, const DevMeta* __restrict__ meta,
-    const uint16_t* __restrict__ h, int H, int I, size_t gateup_bytes,
+    const uint16_t* __restrict__ h, size_t lo_plane, int H, int I, size_t gateup_bytes,
     float* __restrict__ yperm) {
   const int item = blockIdx.y;
   if (item >= meta->n_items) return;
   const WorkItem it = items[item];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int rg = blockIdx.x * 4 + w;
-  if (rg >= H / kAtomRows) return;
+  const int rg = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int KC = I / kAtomK;
   const uint8_t* dbase = it.w + gateup_bytes + (size_t)rg * KC * kAtomBytes;
-  const bf16x8 zero = {};
+  __shared__ f32x4 red[kMaxWaves][64];
+  const uint32_t lo_bytes = (uint32_t)(lo_plane * 2);
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(h, 2 * lo_bytes);
 
-  for (int m0 = 0; m0 < it.cnt; m0 += 16 * kMT) {
-    const int mt_n = min(kMT, (it.cnt - m0 + 15) / 16);
-    const uint16_t* hrow[kMT];
+  // Unconditional weight loads, as in the gate/up kernel.
+  u32x4 wd[CPW];
+  uint32_t sd[CPW];
 #pragma unroll
-    for (int mt = 0; mt < kMT; mt++) {
-      const int m = m0 + mt * 16 + (lane & 15);
-      hrow[mt] = (mt < mt_n && m < it.cnt) ? h + (size_t)(it.pos0 + m) * I + 8 * (lane >> 4)
-                                           : nullptr;
-    }
-    f32x4 acc[kMT];
-#pragma unroll
-    for (int mt = 0; mt < kMT; mt++) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < KC; c++) {
-      const uint8_t* da = dbase + (size_t)c * kAtomBytes;
-      const u32x4 d = *reinterpret_cast<const u32x4*>(da + lane * 16);
-      const uint32_t s = *reinterpret_cast<const uint32_t*>(da + kAtomData + (lane & 15) * 4);
+  for (int cc = 0; cc < CPW; cc++) {
+    const int c = w * CPW + cc;
+    const uint8_t* da = dbase + (size_t)(c < KC ? c : 0) * kAtomBytes;
+    wd[cc] = load_atom_data(da, lane);
+    sd[cc] = load_scale(da, lane);
+  }
+
+  // One M tile of 16 tokens (first tile peeled, as in the gate/up kernel).
+  auto tile = [&](int m0) {
+    const int m = m0 + (lane & 15);
+    const bool mok = m < it.cnt;
+    const uint32_t hrow = (uint32_t)((it.pos0 + m) * I + 32 * (lane >> 4)) * 2u;
+    auto hoff = [&](int c) { return (mok && c < KC) ? hrow + (uint32_t)c * kAtomK * 2u : kOutOfRange; };
+    // h fragments (L2-resident, hi and lo planes) are fetched one chunk ahead
+    bf16x8 ahi[2][4], alo[2][4];
+    {
+      const uint32_t o = hoff(w * CPW);
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        const bf16x8 b = dequant8(d[j], (s >> (8 * j)) & 0xFFu);
-#pragma unroll
-        for (int mt = 0; mt < kMT; mt++) {
-          if (mt < mt_n) {
-            const bf16x8 a = hrow[mt] ? load_a(hrow[mt] + c * kAtomK + 32 * j) : zero;
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[mt], 0, 0, 0);
-          }
-        }
+        ahi[0][j] = bload8(rh, o + 16u * j);
+        alo[0][j] = bload8(rh, o == kOutOfRange ? o : o + lo_bytes + 16u * j);
       }
     }
-    const int col = rg * 16 + (lane & 15);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mt = 0; mt < kMT; mt++) {
-      if (mt < mt_n) {
+    for (int cc = 0; cc < CPW; cc++) {
+      const int c = w * CPW + cc;
+      if (cc + 1 < CPW) {
+        const uint32_t o = hoff(c + 1);
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const int m = m0 + mt * 16 + 4 * (lane >> 4) + i;
-          if (m < it.cnt) yperm[(size_t)(it.pos0 + m) * H + col] = acc[mt][i];
+        for (int j = 0; j < 4; j++) {
+          ahi[(cc + 1) & 1][j] = bload8(rh, o + 16u * j);
+          alo[(cc + 1) & 1][j] = bload8(rh, o == kOutOfRange ? o : o + lo_bytes + 16u * j);
         }
       }
+      if (cc == 0) {
+#pragma unroll
+        for (int q = 0; q < CPW; q++) asm volatile("" : "+v"(wd[q]), "+v"(sd[q]));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const bf16x8 b = dequant8(wd[cc][j], sd[cc]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[cc & 1][j], b, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[cc & 1][j], b, acc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-  }
+    red[w][lane] = acc;
+    __syncthreads();
+    for (int v0 = threadIdx.x; v0 < 256; v0 += blockDim.x) {  // 64 lanes x 4 values
+      const int L = v0 >> 2, i = v0 & 3;
+      float s = 0.f;
+      for (int v = 0; v < nw; v++) s += red[v][L][i];
+      const int mm = m0 + 4 * (L >> 4) + i;
+      if (mm < it.cnt) yperm[(size_t)(it.pos0 + mm) * H + rg * 16 + (L & 15)] = s;
+    }
+    __syncthreads();
+  };
+  tile(0);
+  for (int m0 = 16; m0 < it.cnt; m0 += 16) tile(m0);
 }
 
 // y[t] = sum_j g[t,j] * o[inv(t,j)] (+ shared row), fp32 in rank order, bf16 out.
@@ -196,6 +284,21 @@ __global__ __launch_bounds__(256) void combine_kernel(
   if (y32) y32[(size_t)t * H + col] = acc;
 }
 
+// Waves per workgroup (the split of K) and chunks per wave, for K of KC
+// chunks and `tiles` output tiles: split until the launch has about 4096
+// waves (fills 256 CUs at 16 waves), but never give a wave more than
+// max_cpw chunks (its loads are all issued at once).
+struct Split {
+  int waves, cpw;
+};
+Split split_k(int KC, int tiles, int max_cpw) {
+  int s = 1;
+  while (s < kMaxWaves && s * tiles < 4096) s *= 2;
+  s = std::max(s, (KC + max_cpw - 1) / max_cpw);
+  s = std::min(s, std::min(kMaxWaves, KC));
+  return {s, (KC + s - 1) / s};
+}
+
 }  // namespace
 
 static int items_for(const Ctx* c, int T) {
@@ -204,17 +307,36 @@ static int items_for(const Ctx* c, int T) {
 
 hipError_t launch_expert_gateup(const Ctx* c, const uint16_t* x, int T, hipStream_t st) {
   dim3 grid(c->cfg.inter / kAtomRows, items_for(c, T));
-  gateup_decode_kernel<<<grid, 256, 0, st>>>(c->d_items, c->d_meta, c->d_tok, x, c->cfg.hidden,
-                                             c->cfg.inter, c->d_h);
+  const Split s = split_k(c->cfg.hidden / kAtomK, grid.x * grid.y, 4);
+  const size_t lo = (size_t)c->rows_max * c->cfg.inter;
+#define GATEUP(N)                                                                       \
+  gateup_decode_kernel<N><<<grid, s.waves * 64, 0, st>>>(                             \
+      c->d_items, c->d_meta, c->d_tok, x, (uint32_t)T * c->cfg.hidden * 2, c->cfg.hidden, \
+      c->cfg.inter, c->d_h, lo)
+  switch (s.cpw) {
+    case 1: GATEUP(1); break;
+    case 2: GATEUP(2); break;
+    case 3: GATEUP(3); break;
+    default: GATEUP(4); break;
+  }
+#undef GATEUP
   return hipGetLastError();
 }
 
 hipError_t launch_expert_down(const Ctx* c, int T, hipStream_t st) {
-  dim3 grid((c->cfg.hidden / kAtomRows + 3) / 4, items_for(c, T));
-  down_decode_kernel<<<grid, 256, 0, st>>>(c->d_items, c->d_meta, c->d_h, c->cfg.hidden,
-                                           c->cfg.inter,
-                                           gateup_section_bytes(c->cfg.hidden, c->cfg.inter),
-                                           c->d_yperm);
+  dim3 grid(c->cfg.hidden / kAtomRows, items_for(c, T));
+  const Split s = split_k(c->cfg.inter / kAtomK, grid.x * grid.y, 2);
+  const size_t lo = (size_t)c->rows_max * c->cfg.inter;
+  const size_t gub = gateup_section_bytes(c->cfg.hidden, c->cfg.inter);
+#define DOWN(N)                                                                       \
+  down_decode_kernel<N><<<grid, s.waves * 64, 0, st>>>(                             \
+      c->d_items, c->d_meta, c->d_h, lo, c->cfg.hidden, c->cfg.inter, gub,           \
+      c->d_yperm)
+  switch (s.cpw) {
+    case 1: DOWN(1); break;
+    default: DOWN(2); break;
+  }
+#undef DOWN
   return hipGetLastError();
 }
 

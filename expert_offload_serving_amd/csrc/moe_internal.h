@@ -16,18 +16,23 @@ namespace moe {
 // MXFP4 expert record in the library's tiled layout.
 //
 // A matrix W [N rows][K] (rows = output features) is cut into atoms of
-// 16 rows x 128 K.  One atom is 1088 contiguous bytes:
-//   bytes [0, 1024): 64 lanes x 16 bytes.  Lane l holds row (l % 16); its
-//     4-byte word j (j = 0..3) holds the 8 E2M1 codes of K range
-//     [32 j + 8 (l / 16), +8) of the chunk, low nibble first.  This is the
-//     B-operand layout of v_mfma_f32_16x16x32_bf16 for four K=32 steps, so a
-//     wave loads an atom with one 16-byte load per lane.
-//   bytes [1024, 1088): E8M0 scales, [row 0..15][block j 0..3].
+// 16 rows x 128 K (four MX blocks per row).  One atom is 1088 contiguous
+// bytes, one lane of a wave per MX block:
+//   bytes [16 l, 16 l + 16), l = 0..63: the 32 E2M1 codes (low nibble
+//     first) of row (l % 16), block (l / 16) of the chunk, i.e. K range
+//     [32 (l / 16), +32);
+//   byte 1024 + l: that block's E8M0 scale.
+// A wave loads an atom with one 16-byte and one 1-byte load per lane.  Word
+// j of a lane's 16 bytes feeds MFMA step j of v_mfma_f32_16x16x32_bf16 as the
+// B operand (hardware k = 8 (l / 16) + i stands for K = 32 (l / 16) + 8 j + i;
+// the A operand uses the same correspondence, so the sum over K is exact).
 // Gate and up are fused: row groups alternate 16 gate rows, 16 up rows
 // (group 2p = gate rows 16p..16p+15, 2p+1 = up rows of the same indices).
 // Record = [gate/up atoms: group-major, K-chunk minor] [down atoms: same].
 // Total = 3*H*I*17/32 bytes, the MXFP4 size.
 // ---------------------------------------------------------------------------
+constexpr int kMaxH = 6144;            // largest hidden / inter size
+constexpr int kMaxCacheSlots = 4096;   // the lookup keeps the LRU order in LDS
 constexpr int kAtomRows = 16;
 constexpr int kAtomK = 128;
 constexpr int kAtomData = 1024;
@@ -75,11 +80,14 @@ struct DevCache {
 };
 
 // Arguments of the block-wide LRU lookup.
+// Recency-order entry: slot | (key + 1) << kOrderKeyShift (key + 1 = 0: empty).
+constexpr int kOrderKeyShift = 12;   // slots < 4096
+
 struct LookupArgs {
   int32_t layer, E, C, staging;
   int32_t* key;            // [C]
   uint64_t* stamp;         // [C]
-  int32_t* order;          // [C] slots from least to most recent
+  int32_t* order;          // [C] packed entries, least recent first
   int32_t* order_tmp;      // [C]
   int32_t* map;            // [L*E] slot of each key or -1
   uint8_t* hitflag;        // [C]
@@ -104,11 +112,10 @@ struct Ctx {
   int max_unique = 0;       // min(T_max*k, E)
   int max_items = 0;        // max_unique + has_shared
   int rows_max = 0;         // T_max*k + T_max (shared rows)
-  int n_chunks_max = 0;     // router H chunks
 
   // host pool and HBM weights
   uint8_t* pool = nullptr;          // pinned, [L][E] records
-  float* d_router = nullptr;        // [L][H][E]
+  float* d_router = nullptr;        // [L][E][H]: router matrices, transposed
   uint8_t* d_shared = nullptr;      // [L] records
   std::vector<uint8_t> router_set;  // per layer
   std::vector<uint8_t> shared_set;
@@ -127,7 +134,6 @@ struct Ctx {
   DevCache* d_cache = nullptr;
 
   // decode scratch
-  double* d_partials = nullptr;     // [n_chunks][T_max][E]
   float* d_logits = nullptr;        // [T_max][E]
   int32_t* d_ids = nullptr;         // [T_max*k]
   float* d_gates = nullptr;         // [T_max*k]
@@ -141,7 +147,7 @@ struct Ctx {
   WorkItem* d_items = nullptr;      // [max_items]
   FillEntry* d_fills = nullptr;     // [max_unique]
   DevMeta* d_meta = nullptr;
-  uint16_t* d_h = nullptr;          // bf16 [rows_max][I]
+  uint16_t* d_h = nullptr;          // bf16 [2][rows_max][I]: hi, lo planes
   float* d_yperm = nullptr;         // [rows_max][H]
   int32_t* d_lookup_ids = nullptr;  // [E] for expert_cache_fill
 
@@ -166,13 +172,10 @@ struct Ctx {
 // ---------------------------------------------------------------------------
 // Launchers (each enqueues on `st` and returns hipGetLastError()).
 // ---------------------------------------------------------------------------
-int router_chunk_rows(int H);
-hipError_t launch_router_partial(const uint16_t* x, int T, int H, int E,
-                                 const float* w_router, double* partials,
-                                 hipStream_t st);
-hipError_t launch_route_finalize(Ctx* c, int layer, int T, const float* bias,
-                                 int32_t* user_ids, float* user_gates,
-                                 hipStream_t st);
+hipError_t launch_router(const uint16_t* x, int T, int H, int E, const float* w_router_t,
+                         const float* bias, float* logits, hipStream_t st);
+hipError_t launch_route_finalize(Ctx* c, int layer, int T, int32_t* user_ids,
+                                 float* user_gates, hipStream_t st);
 hipError_t launch_cache_lookup(Ctx* c, int layer, const int32_t* d_experts,
                                const int32_t* d_n, int n_max, int32_t* d_slot,
                                hipStream_t st);

@@ -11,56 +11,151 @@
 namespace moe {
 namespace {
 
-constexpr int kRouterRows = 32;   // H rows per router workgroup
+constexpr int kRouterWaves = 4;       // waves per expert in the router
+constexpr int kRouterTG = 8;          // tokens per pass
 constexpr int kFinalizeThreads = 1024;
 
-__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
-  return __uint_as_float((uint32_t)b << 16);
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Wave-wide reductions on DPP (row shifts, then row broadcasts 15 and 31);
+// the full result lands in lane 63.  The combination order is fixed.
+template <int CTRL, int ROWS = 0xF, int BANKS = 0xF>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return __builtin_amdgcn_update_dpp(0u, v, CTRL, ROWS, BANKS, false);
+}
+template <int CTRL, int ROWS = 0xF, int BANKS = 0xF>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint64_t r = ((uint64_t)dpp<CTRL, ROWS, BANKS>((uint32_t)(u >> 32)) << 32) |
+                     dpp<CTRL, ROWS, BANKS>((uint32_t)u);
+  return __builtin_bit_cast(double, r);
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64<0x111>(v);          // row_shr:1
+  v += dpp_f64<0x112>(v);          // row_shr:2
+  v += dpp_f64<0x114>(v);          // row_shr:4
+  v += dpp_f64<0x118>(v);          // row_shr:8
+  v += dpp_f64<0x142, 0xA>(v);     // row_bcast:15
+  v += dpp_f64<0x143, 0xC>(v);     // row_bcast:31
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint64_t r = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(u >> 32), 63) << 32) |
+                     (uint32_t)__builtin_amdgcn_readlane((uint32_t)u, 63);
+  return __builtin_bit_cast(double, r);
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint64_t max_step(uint64_t v) {
+  const uint64_t o = ((uint64_t)dpp<CTRL, ROWS>((uint32_t)(v >> 32)) << 32) |
+                     dpp<CTRL, ROWS>((uint32_t)v);
+  return o > v ? o : v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = max_step<0x111>(v);
+  v = max_step<0x112>(v);
+  v = max_step<0x114>(v);
+  v = max_step<0x118>(v);
+  v = max_step<0x142, 0xA>(v);
+  v = max_step<0x143, 0xC>(v);
+  return ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(v >> 32), 63) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((uint32_t)v, 63);
 }
 
-// partials[chunk][t][e] = sum over the chunk's H rows of x[t][h] * W_r[h][e],
-// in fp64.  bf16 x fp32 products are exact in fp64.
+// logits[t][e] = fp32(sum_h x[t][h] W_r[h][e] + bias[t][e]), sums in fp64
+// (bf16 x fp32 products are exact in fp64).  W_r is held transposed,
+// [E][H], so an expert's column is contiguous.  One workgroup per expert:
+// its 4 waves split H into quarters, lane l of a wave takes the 8-element
+// pieces l, l+64, ... of its quarter (all loads issued before the first
+// FMA), each wave reduces in a fixed DPP order and the quarters are added
+// in order through LDS.
+constexpr int kRouterMaxPieces = 3;   // pieces per lane: H <= 4 * 64 * 8 * 3
+
 template <int TG>
-__global__ __launch_bounds__(256) void router_partial_kernel(
-    const uint16_t* __restrict__ x, int T, int H, int E,
-    const float* __restrict__ wr, double* __restrict__ partials) {
-  const int chunk = blockIdx.x;
-  const int h0 = chunk * kRouterRows;
-  const int hn = min(kRouterRows, H - h0);
-  __shared__ float xs[TG][kRouterRows];
-  for (int tg = 0; tg < T; tg += TG) {
-    const int tn = min(TG, T - tg);
-    __syncthreads();
-    for (int i = threadIdx.x; i < TG * kRouterRows; i += blockDim.x) {
-      const int t = i / kRouterRows, hh = i % kRouterRows;
-      xs[t][hh] = (t < tn && hh < hn) ? bf16_bits_to_f32(x[(size_t)(tg + t) * H + h0 + hh]) : 0.f;
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-      double acc[TG];
+__global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(
+    const uint16_t* __restrict__ x, int T, int H, int E, const float* __restrict__ wrt,
+    const float* __restrict__ bias, float* __restrict__ logits) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int e = blockIdx.x;
+  const int per_wave = H / 8 / kRouterWaves;   // pieces in this wave's quarter
+  const int q0 = w * per_wave;
+  const float* wrow = wrt + (size_t)e * H;
+  __shared__ double red[kRouterWaves][TG];
+  f32x4 w0[kRouterMaxPieces], w1[kRouterMaxPieces];
 #pragma unroll
-      for (int t = 0; t < TG; t++) acc[t] = 0.0;
-      for (int hh = 0; hh < hn; hh++) {
-        const double wv = (double)wr[(size_t)(h0 + hh) * E + e];
-#pragma unroll
-        for (int t = 0; t < TG; t++) acc[t] = fma((double)xs[t][hh], wv, acc[t]);
-      }
-#pragma unroll
-      for (int t = 0; t < TG; t++)
-        if (t < tn) partials[((size_t)chunk * T + tg + t) * E + e] = acc[t];
+  for (int i = 0; i < kRouterMaxPieces; i++) {
+    const int q = lane + 64 * i;
+    if (q < per_wave) {
+      w0[i] = *reinterpret_cast<const f32x4*>(wrow + 8 * (q0 + q));
+      w1[i] = *reinterpret_cast<const f32x4*>(wrow + 8 * (q0 + q) + 4);
+    } else {
+      w0[i] = w1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
+  for (int tg = 0; tg < T; tg += TG) {
+    const int tn = min(TG, T - tg);
+    u32x4 xv[kRouterMaxPieces][TG];
+#pragma unroll
+    for (int i = 0; i < kRouterMaxPieces; i++) {
+      const int q = lane + 64 * i;
+#pragma unroll
+      for (int t = 0; t < TG; t++)
+        xv[i][t] = (q < per_wave && t < tn)
+                       ? *reinterpret_cast<const u32x4*>(x + (size_t)(tg + t) * H + 8 * (q0 + q))
+                       : u32x4{0u, 0u, 0u, 0u};
+    }
+    double acc[TG];
+#pragma unroll
+    for (int t = 0; t < TG; t++) acc[t] = 0.0;
+#pragma unroll
+    for (int i = 0; i < kRouterMaxPieces; i++) {
+      double wd[8];
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        wd[j] = (double)w0[i][j];
+        wd[4 + j] = (double)w1[i][j];
+      }
+#pragma unroll
+      for (int t = 0; t < TG; t++) {
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          const uint32_t word = xv[i][t][j >> 1];
+          const float xf = __uint_as_float((j & 1) ? (word & 0xFFFF0000u) : (word << 16));
+          acc[t] = fma((double)xf, wd[j], acc[t]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TG; t++) {
+      const double s = wave_sum_f64(acc[t]);
+      if (lane == 0) red[w][t] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x < tn) {
+      const int t = threadIdx.x;
+      double s = 0.0;
+#pragma unroll
+      for (int v = 0; v < kRouterWaves; v++) s += red[v][t];
+      const size_t o = (size_t)(tg + t) * E + e;
+      logits[o] = (float)(bias ? s + (double)bias[o] : s);
+    }
+    __syncthreads();
+  }
+}
+
+// Inclusive scan of one int per lane (DPP, fixed order).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += (int)dpp<0x111>((uint32_t)v);
+  v += (int)dpp<0x112>((uint32_t)v);
+  v += (int)dpp<0x114>((uint32_t)v);
+  v += (int)dpp<0x118>((uint32_t)v);
+  v += (int)dpp<0x142, 0xA>((uint32_t)v);
+  v += (int)dpp<0x143, 0xC>((uint32_t)v);
+  return v;
 }
 
 // Exclusive scan of one int per thread over the block; *total gets the sum.
 __device__ int block_excl_scan(int v, int* s_tmp, int* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) s_tmp[w] = x;
   __syncthreads();
   int base = 0, tot = 0;
@@ -83,85 +178,89 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, d, 64);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d, 64);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+// LDS working set of a lookup: the packed recency order, per-slot hit
+// flags, the victims, and this layer's expert -> slot map.
+struct LookupShared {
+  int order[kMaxCacheSlots];
+  uint8_t hit[kMaxCacheSlots];
+  int victim[1024];
+  int map[1024];
+  int tmp[16];
+  int evict;
+};
+
+// Copy the recency order and this layer's map into LDS (issued first, so
+// the loads overlap the work before the lookup).
+__device__ __forceinline__ void prefetch_lookup(const LookupArgs& a, LookupShared& ls) {
+  for (int p = threadIdx.x; p < a.C; p += blockDim.x) ls.order[p] = a.order[p];
+  for (int e = threadIdx.x; e < a.E; e += blockDim.x) ls.map[e] = a.map[a.layer * a.E + e];
 }
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-  return v;
-}
-
-// Block-wide LRU lookup of the n unique experts in s_U (ascending).
-// Slot codes go to s_slot[u]; fills (cache and staging copies) to a.fills.
-// See the rule in moe.h (moe_layer_forward).
-__device__ void block_lookup(const LookupArgs& a, const int* s_U, int n, int* s_slot,
-                             int* s_tmp, int* s_evict) {
+// Block-wide LRU lookup of the n unique experts in s_U (ascending).  Slot
+// codes go to s_slot[u]; fills (cache and staging copies) to a.fills.  The
+// rule is the one stated in moe.h (moe_layer_forward).  prefetch_lookup
+// must have run (and a barrier passed) before.
+__device__ void block_lookup(const LookupArgs& a, LookupShared& ls, const int* s_U, int n,
+                             int* s_slot) {
   const int tid = threadIdx.x, nt = blockDim.x;
   const int C = a.C;
   const uint64_t clock0 = a.cache->clock;
-  if (tid == 0) *s_evict = 0;
-  for (int s = tid; s < C; s += nt) a.hitflag[s] = 0;
-  __syncthreads();
+  if (tid == 0) ls.evict = 0;
+  for (int s = tid; s < C; s += nt) ls.hit[s] = 0;
 
   const int u = tid;
   const int e = u < n ? s_U[u] : -1;
   const bool valid = e >= 0 && e < a.E;
   const int key = valid ? a.layer * a.E + e : -1;
-  const int slot = valid ? a.map[key] : -1;
+  const int slot = valid ? ls.map[e] : -1;
   const bool hit = valid && slot >= 0;
   const bool miss = valid && !hit;
   int n_hit, n_miss;
-  const int hrank = block_excl_scan(hit ? 1 : 0, s_tmp, &n_hit);
-  const int mrank = block_excl_scan(miss ? 1 : 0, s_tmp, &n_miss);
+  const int hrank = block_excl_scan(hit ? 1 : 0, ls.tmp, &n_hit);   // barrier: hit[] cleared
+  const int mrank = block_excl_scan(miss ? 1 : 0, ls.tmp, &n_miss);
   const int n_fill = min(n_miss, C - n_hit);
   if (hit) {
-    a.hitflag[slot] = 1;
+    ls.hit[slot] = 1;
     a.stamp[slot] = clock0 + 1 + (uint64_t)hrank;
     s_slot[u] = slot;
   }
   __syncthreads();
 
-  // Victims: non-hit slots in recency order; untouched ones keep their order.
+  // Victims: non-hit slots in recency order.  Untouched slots are compacted
+  // to the front in place (a slot only moves to a lower position, and every
+  // position of a chunk is read before the chunk's first write).
+  constexpr int kSlotMask = (1 << kOrderKeyShift) - 1;
   int carry = 0, carry_keep = 0;
   for (int p0 = 0; p0 < C; p0 += nt) {
     const int p = p0 + tid;
-    const int s = p < C ? a.order[p] : -1;
-    const bool nonhit = p < C && !a.hitflag[s];
+    const int ent = p < C ? ls.order[p] : 0;
+    const bool nonhit = p < C && !ls.hit[ent & kSlotMask];
     int tot, ktot;
-    const int r = block_excl_scan(nonhit ? 1 : 0, s_tmp, &tot) + carry;
+    const int r = block_excl_scan(nonhit ? 1 : 0, ls.tmp, &tot) + carry;
     const bool victim = nonhit && r < n_fill;
-    if (victim) a.victim[r] = s;
+    if (victim) ls.victim[r] = ent;
     const bool keep = nonhit && !victim;
-    const int kr = block_excl_scan(keep ? 1 : 0, s_tmp, &ktot) + carry_keep;
-    if (keep) a.order_tmp[kr] = s;
+    const int kr = block_excl_scan(keep ? 1 : 0, ls.tmp, &ktot) + carry_keep;
+    if (keep) ls.order[kr] = ent;
     carry += tot;
     carry_keep += ktot;
   }
   __syncthreads();
   const int n_keep = C - n_hit - n_fill;
-  if (hit) a.order_tmp[n_keep + hrank] = slot;
+  if (hit) ls.order[n_keep + hrank] = slot | ((key + 1) << kOrderKeyShift);
   if (miss) {
     const uint8_t* src = a.pool + (size_t)key * a.stride;
     if (mrank < n_fill) {
-      const int s = a.victim[mrank];
-      const int old = a.key[s];
+      const int ent = ls.victim[mrank];
+      const int s = ent & kSlotMask, old = (ent >> kOrderKeyShift) - 1;
       if (old >= 0) {
         a.map[old] = -1;
-        atomicAdd(s_evict, 1);
+        atomicAdd(&ls.evict, 1);
       }
       a.key[s] = key;
       a.map[key] = s;
       a.stamp[s] = clock0 + (uint64_t)n_hit + 1 + (uint64_t)mrank;
-      a.order_tmp[n_keep + n_hit + mrank] = s;
+      ls.order[n_keep + n_hit + mrank] = s | ((key + 1) << kOrderKeyShift);
       a.fills[mrank] = FillEntry{src, a.slots + (size_t)s * a.stride};
       s_slot[u] = s;
     } else {
@@ -172,7 +271,7 @@ __device__ void block_lookup(const LookupArgs& a, const int* s_U, int n, int* s_
   }
   if (u < n && !valid) s_slot[u] = INT_MIN;
   __syncthreads();
-  for (int p = tid; p < C; p += nt) a.order[p] = a.order_tmp[p];
+  for (int p = tid; p < C; p += nt) a.order[p] = ls.order[p];
   if (tid == 0) {
     DevCache* dc = a.cache;
     dc->clock = clock0 + (uint64_t)n_hit + (uint64_t)n_fill;
@@ -180,7 +279,7 @@ __device__ void block_lookup(const LookupArgs& a, const int* s_U, int n, int* s_
     dc->hits += (uint64_t)n_hit;
     dc->fills += (uint64_t)n_fill;
     dc->bypasses += (uint64_t)(n_miss - n_fill);
-    dc->evictions += (uint64_t)*s_evict;
+    dc->evictions += (uint64_t)ls.evict;
     a.meta->n_fill = n_miss;
     a.meta->n_hit = n_hit;
     a.meta->n_bypass = n_miss - n_fill;
@@ -189,10 +288,8 @@ __device__ void block_lookup(const LookupArgs& a, const int* s_U, int n, int* s_
 }
 
 struct FinalizeArgs {
-  int T, H, E, k, renorm, n_chunks, has_shared;
-  const double* partials;
-  const float* bias;
-  float* logits;
+  int T, H, E, k, renorm, has_shared;
+  const float* logits;
   int32_t* ids;
   float* gates;
   int32_t* user_ids;
@@ -209,85 +306,93 @@ struct FinalizeArgs {
   LookupArgs la;
 };
 
+// Top-k of one token in one wave.  Lane l holds the keys of experts
+// l, l+64, ... (NK of them) as (ordered logit << 32 | ~expert): the largest
+// key is the largest logit, ties to the lower expert.  Each round takes the
+// wave maximum of the lanes' current maxima; only the winner lane clears
+// that key and recomputes its maximum.
+template <int NK>
+__device__ void topk_token(const FinalizeArgs& a, int t, int* s_ids) {
+  const int lane = threadIdx.x & 63;
+  const int E = a.E, k = a.k;
+  uint64_t keys[NK];
+#pragma unroll
+  for (int i = 0; i < NK; i++) {
+    const int e = lane + 64 * i;
+    keys[i] = e < E ? ((uint64_t)ordered_bits(a.logits[(size_t)t * E + e]) << 32) |
+                          (uint64_t)(0xFFFFFFFFu - (uint32_t)e)
+                    : 0ull;
+  }
+  uint64_t lmax = 0;
+#pragma unroll
+  for (int i = 0; i < NK; i++) lmax = keys[i] > lmax ? keys[i] : lmax;
+  float my_l = 0.f, l0 = 0.f;
+  for (int j = 0; j < k; j++) {
+    const uint64_t best = wave_max_u64(lmax);
+    const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
+    const float l = from_ordered_bits((uint32_t)(best >> 32));
+    if (lmax == best) {  // the winner lane (keys are unique)
+      lmax = 0;
+#pragma unroll
+      for (int i = 0; i < NK; i++) {
+        if (keys[i] == best) keys[i] = 0ull;
+        lmax = keys[i] > lmax ? keys[i] : lmax;
+      }
+    }
+    if (lane == j) my_l = l;
+    if (j == 0) l0 = l;
+    if (lane == 0) {
+      a.ids[t * k + j] = e;
+      s_ids[t * k + j] = e;
+      if (a.user_ids) a.user_ids[t * k + j] = e;
+    }
+  }
+  double z = 0.0, denom;
+  if (a.renorm) {
+    z = lane < k ? exp((double)my_l - (double)l0) : 0.0;
+    denom = wave_sum_f64(z);
+  } else {
+    double part = 0.0;
+#pragma unroll
+    for (int i = 0; i < NK; i++) {
+      const int e = lane + 64 * i;
+      if (e < E) part += exp((double)a.logits[(size_t)t * E + e] - (double)l0);
+    }
+    denom = wave_sum_f64(part);
+    z = lane < k ? exp((double)my_l - (double)l0) : 0.0;
+  }
+  if (lane < k) {
+    const float g = (float)(z / denom);
+    a.gates[t * k + lane] = g;
+    if (a.user_gates) a.user_gates[t * k + lane] = g;
+  }
+}
+
+template <int NK>
 __global__ __launch_bounds__(kFinalizeThreads) void route_finalize_kernel(FinalizeArgs a) {
   __shared__ int s_counts[1024];
   __shared__ unsigned long long s_mask[1024];
   __shared__ int s_offsets[1025];
-  __shared__ int s_ids[1024];
+  __shared__ int s_ids[1024];      // (t, j) -> expert; reused for slot codes
   __shared__ int s_U[1024];
-  __shared__ int s_slot[1024];
-  __shared__ int s_tmp[16];
-  __shared__ int s_evict;
+  __shared__ LookupShared ls;
+  int* s_slot = s_ids;
   const int tid = threadIdx.x, nt = blockDim.x;
-  const int lane = tid & 63, w = tid >> 6, nw = nt >> 6;
+  const int w = tid >> 6, nw = nt >> 6;
   const int T = a.T, E = a.E, k = a.k;
 
-  // 1. logits = fp32(sum of chunk partials in order + bias), fp64 inside
-  for (int i = tid; i < T * E; i += nt) {
-    const int t = i / E, e = i % E;
-    double s = 0.0;
-    for (int c = 0; c < a.n_chunks; c++) s += a.partials[((size_t)c * T + t) * E + e];
-    if (a.bias) s += (double)a.bias[i];
-    a.logits[i] = (float)s;
-  }
+  prefetch_lookup(a.la, ls);
   for (int e = tid; e < 1024; e += nt) {
     s_counts[e] = 0;
     s_mask[e] = 0ull;
   }
   __syncthreads();
 
-  // 2. top-k per token (one wave per token): key = (ordered logit, ~expert)
-  for (int t = w; t < T; t += nw) {
-    uint64_t keys[16];
-#pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const int e = lane + 64 * i;
-      keys[i] = e < E ? ((uint64_t)ordered_bits(a.logits[(size_t)t * E + e]) << 32) |
-                            (uint64_t)(0xFFFFFFFFu - (uint32_t)e)
-                      : 0ull;
-    }
-    float my_l = 0.f;
-    float l0 = 0.f;
-    for (int j = 0; j < k; j++) {
-      uint64_t best = 0;
-#pragma unroll
-      for (int i = 0; i < 16; i++) best = keys[i] > best ? keys[i] : best;
-      best = wave_max_u64(best);
-      const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-      const float l = from_ordered_bits((uint32_t)(best >> 32));
-#pragma unroll
-      for (int i = 0; i < 16; i++)
-        if (lane + 64 * i == e) keys[i] = 0ull;
-      if (lane == j) my_l = l;
-      if (j == 0) l0 = l;
-      if (lane == 0) {
-        a.ids[t * k + j] = e;
-        s_ids[t * k + j] = e;
-        if (a.user_ids) a.user_ids[t * k + j] = e;
-      }
-    }
-    double z = 0.0, denom;
-    if (a.renorm) {
-      z = lane < k ? exp((double)my_l - (double)l0) : 0.0;
-      denom = wave_sum_f64(z);
-    } else {
-      double part = 0.0;
-      for (int i = 0; i < 16; i++) {
-        const int e = lane + 64 * i;
-        if (e < E) part += exp((double)a.logits[(size_t)t * E + e] - (double)l0);
-      }
-      denom = wave_sum_f64(part);
-      z = lane < k ? exp((double)my_l - (double)l0) : 0.0;
-    }
-    if (lane < k) {
-      const float g = (float)(z / denom);
-      a.gates[t * k + lane] = g;
-      if (a.user_gates) a.user_gates[t * k + lane] = g;
-    }
-  }
+  // top-k and gates, one wave per token
+  for (int t = w; t < T; t += nw) topk_token<NK>(a, t, s_ids);
   __syncthreads();
 
-  // 3. dispatch: counts, offsets, stable permutation, unique experts
+  // dispatch: counts, offsets, stable permutation, unique experts
   const int nk = T * k;
   int n_unique;
   for (int f = tid; f < nk; f += nt) {
@@ -300,8 +405,8 @@ __global__ __launch_bounds__(kFinalizeThreads) void route_finalize_kernel(Finali
     const int e = tid;
     const int cnt = e < E ? s_counts[e] : 0;
     int total;
-    const int off = block_excl_scan(cnt, s_tmp, &total);
-    const int ur = block_excl_scan(cnt > 0 ? 1 : 0, s_tmp, &n_unique);
+    const int off = block_excl_scan(cnt, ls.tmp, &total);
+    const int ur = block_excl_scan(cnt > 0 ? 1 : 0, ls.tmp, &n_unique);
     if (e < E) {
       s_offsets[e] = off;
       a.counts[e] = cnt;
@@ -327,12 +432,12 @@ __global__ __launch_bounds__(kFinalizeThreads) void route_finalize_kernel(Finali
     a.inv[f] = pos;
     a.tok[pos] = t;
   }
-  __syncthreads();
 
-  // 4. cache lookup of the unique experts
-  block_lookup(a.la, s_U, n_unique, s_slot, s_tmp, &s_evict);
+  // cache lookup of the unique experts (its first barrier orders the
+  // reads of s_ids above before the slot codes overwrite them)
+  block_lookup(a.la, ls, s_U, n_unique, s_slot);
 
-  // 5. work list for the expert kernels
+  // work list for the expert kernels
   for (int u = tid; u < n_unique; u += nt) {
     const int code = s_slot[u];
     const uint8_t* wptr = code >= 0 ? a.la.slots + (size_t)code * a.la.stride
@@ -353,13 +458,13 @@ __global__ __launch_bounds__(kFinalizeThreads) void cache_lookup_kernel(
     LookupArgs la, const int32_t* experts, const int32_t* d_n, int n_max, int32_t* out_slot) {
   __shared__ int s_U[1024];
   __shared__ int s_slot[1024];
-  __shared__ int s_tmp[16];
-  __shared__ int s_evict;
+  __shared__ LookupShared ls;
+  prefetch_lookup(la, ls);
   int n = *d_n;
   n = n < 0 ? 0 : (n > n_max ? n_max : n);
   for (int u = threadIdx.x; u < n; u += blockDim.x) s_U[u] = experts[u];
   __syncthreads();
-  block_lookup(la, s_U, n, s_slot, s_tmp, &s_evict);
+  block_lookup(la, ls, s_U, n, s_slot);
   for (int u = threadIdx.x; u < n; u += blockDim.x) out_slot[u] = s_slot[u];
 }
 
@@ -388,32 +493,26 @@ LookupArgs make_lookup_args(Ctx* c, int layer) {
 
 }  // namespace
 
-int router_chunk_rows(int) { return kRouterRows; }
-
-hipError_t launch_router_partial(const uint16_t* x, int T, int H, int E, const float* wr,
-                                 double* partials, hipStream_t st) {
-  const int chunks = (H + kRouterRows - 1) / kRouterRows;
+hipError_t launch_router(const uint16_t* x, int T, int H, int E, const float* wrt,
+                         const float* bias, float* logits, hipStream_t st) {
   if (T <= 1)
-    router_partial_kernel<1><<<chunks, 256, 0, st>>>(x, T, H, E, wr, partials);
+    router_kernel<1><<<E, kRouterWaves * 64, 0, st>>>(x, T, H, E, wrt, bias, logits);
   else if (T <= 4)
-    router_partial_kernel<4><<<chunks, 256, 0, st>>>(x, T, H, E, wr, partials);
+    router_kernel<4><<<E, kRouterWaves * 64, 0, st>>>(x, T, H, E, wrt, bias, logits);
   else
-    router_partial_kernel<16><<<chunks, 256, 0, st>>>(x, T, H, E, wr, partials);
+    router_kernel<kRouterTG><<<E, kRouterWaves * 64, 0, st>>>(x, T, H, E, wrt, bias, logits);
   return hipGetLastError();
 }
 
-hipError_t launch_route_finalize(Ctx* c, int layer, int T, const float* bias,
-                                 int32_t* user_ids, float* user_gates, hipStream_t st) {
+hipError_t launch_route_finalize(Ctx* c, int layer, int T, int32_t* user_ids,
+                                 float* user_gates, hipStream_t st) {
   FinalizeArgs a;
   a.T = T;
   a.H = c->cfg.hidden;
   a.E = c->cfg.n_experts;
   a.k = c->cfg.top_k;
   a.renorm = c->cfg.renormalize;
-  a.n_chunks = (a.H + kRouterRows - 1) / kRouterRows;
   a.has_shared = c->cfg.has_shared;
-  a.partials = c->d_partials;
-  a.bias = bias;
   a.logits = c->d_logits;
   a.ids = c->d_ids;
   a.gates = c->d_gates;
@@ -429,7 +528,17 @@ hipError_t launch_route_finalize(Ctx* c, int layer, int T, const float* bias,
   a.items = c->d_items;
   a.shared_w = c->cfg.has_shared ? c->d_shared + (size_t)layer * c->stride : nullptr;
   a.la = make_lookup_args(c, layer);
-  route_finalize_kernel<<<1, kFinalizeThreads, 0, st>>>(a);
+  const int nk = (a.E + 63) / 64;
+  if (nk <= 1)
+    route_finalize_kernel<1><<<1, kFinalizeThreads, 0, st>>>(a);
+  else if (nk <= 2)
+    route_finalize_kernel<2><<<1, kFinalizeThreads, 0, st>>>(a);
+  else if (nk <= 4)
+    route_finalize_kernel<4><<<1, kFinalizeThreads, 0, st>>>(a);
+  else if (nk <= 8)
+    route_finalize_kernel<8><<<1, kFinalizeThreads, 0, st>>>(a);
+  else
+    route_finalize_kernel<16><<<1, kFinalizeThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

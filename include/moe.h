@@ -65,15 +65,17 @@ typedef struct moe_ctx moe_ctx;
 
 /* Layer-stack shape and capacities, fixed at moe_create. */
 typedef struct moe_config {
-  int32_t hidden;          /* H: multiple of 128, >= 128                     */
-  int32_t inter;           /* I: expert intermediate size, multiple of 128   */
+  int32_t hidden;          /* H: multiple of 128, 128..6144                  */
+  int32_t inter;           /* I: expert intermediate size, multiple of 128,
+                              128..6144                                      */
   int32_t n_experts;       /* E: routed experts, top_k <= E <= 1024          */
   int32_t top_k;           /* k: 1..16                                       */
   int32_t n_layers;        /* L >= 1                                         */
   int32_t has_shared;      /* 1: each layer has one always-on shared expert  */
   int32_t renormalize;     /* 1: top-k gates renormalised to sum to 1        */
   int32_t max_tokens;      /* T_max of moe_layer_forward, 1..64              */
-  int32_t cache_slots;     /* C: HBM LRU slots, 0..n_layers*n_experts        */
+  int32_t cache_slots;     /* C: HBM LRU slots, 0..min(n_layers*n_experts,
+                              4096)                                          */
   int32_t staging_slots;   /* S: HBM slots for misses that bypass the cache  */
   int32_t max_prefill_tokens; /* 0 disables moe_prefill_forward              */
 } moe_config;
@@ -104,7 +106,8 @@ size_t moe_expert_bytes(int32_t hidden, int32_t inter);
  * matrices, shared experts, cache slots, staging slots and scratch, and
  * the device-resident cache state (all slots empty, clock 0).
  * Errors: INVALID_ARG (NULL or field out of range), UNSUPPORTED (H or I not
- * a multiple of 128), OOM, HIP.  *out is set only on success.
+ * a multiple of 128 or above 6144, cache_slots above 4096), OOM, HIP.  *out
+ * is set only on success.
  */
 moe_status moe_create(const moe_config* cfg, moe_ctx** out);
 
@@ -218,7 +221,8 @@ moe_status expert_cache_fill(moe_ctx* ctx, int32_t layer,
  * occupied slots in ascending recency while more than new_slots are
  * occupied, moves the survivors held in slots >= new_slots (ascending) into
  * the lowest empty slots < new_slots (ascending) keeping their recency,
- * then releases the tail of the slot memory.  Errors: INVALID_ARG, OOM, HIP.
+ * then releases the tail of the slot memory.  Errors: INVALID_ARG,
+ * UNSUPPORTED (above 4096 slots), OOM, HIP.
  */
 moe_status expert_cache_resize(moe_ctx* ctx, int32_t new_slots, void* stream);
 

@@ -46,6 +46,7 @@ GOOD = dict(hidden=256, inter=512, n_experts=8, top_k=2, n_layers=1, has_shared=
 
 @pytest.mark.parametrize("field,value,status", [
     ("hidden", 0, "INVALID_ARG"), ("hidden", 200, "UNSUPPORTED"), ("inter", 96, "UNSUPPORTED"),
+    ("hidden", 6272, "UNSUPPORTED"), ("inter", 8192, "UNSUPPORTED"),
     ("top_k", 0, "INVALID_ARG"), ("top_k", 17, "INVALID_ARG"), ("n_experts", 1, "INVALID_ARG"),
     ("n_experts", 1025, "INVALID_ARG"), ("max_tokens", 0, "INVALID_ARG"),
     ("max_tokens", 65, "INVALID_ARG"), ("cache_slots", 9, "INVALID_ARG"),

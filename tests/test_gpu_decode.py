@@ -98,7 +98,8 @@ def test_ragged_token_counts(T):
 
 
 @pytest.mark.parametrize("kw", [dict(k=1), dict(E=64, k=16), dict(E=200, k=6), dict(renormalize=False),
-                                dict(shared=True), dict(H=384, I=128), dict(layers=3, E=16, k=3)])
+                                dict(shared=True), dict(H=384, I=128), dict(H=128, I=128, E=4, k=2),
+                                dict(layers=3, E=16, k=3)])
 def test_shape_variants(kw):
     sh = H.small_shape(**kw)
     T = 9

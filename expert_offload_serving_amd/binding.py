@@ -60,6 +60,7 @@ _SIGS = {
     "expert_cache_resize": (_I32, [_P, _I32, _P]),
     "expert_cache_snapshot": (_I32, [_P, _I32, _P, _P, _P, _P]),
     "moe_inspect_dispatch": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_inspect_prefill": (_I32, [_P, _P, _P, _P]),
     "moe_get_stats": (_I32, [_P, ctypes.POINTER(moe_stats)]),
     "moe_reset_stats": (_I32, [_P]),
     "moe_set_timing": (_I32, [_P, _I32]),
@@ -200,6 +201,16 @@ def moe_inspect_dispatch(ctx, E: int, k: int, T_max: int):
     n = T.value * k
     return dict(T=T.value, counts=counts, offsets=offsets, sorted=sorted_[:n], inv=inv[:n],
                 unique=unique[:nu.value], slot=slot[:nu.value])
+
+
+def moe_inspect_prefill(ctx, k: int, T_max: int):
+    T = ctypes.c_int32()
+    ids = np.zeros(T_max * k, np.int32)
+    gates = np.zeros(T_max * k, np.float32)
+    _check(lib.moe_inspect_prefill(ctx, ctypes.byref(T), _ptr(ids), _ptr(gates)),
+           "moe_inspect_prefill")
+    n = T.value
+    return ids[:n * k].reshape(n, k), gates[:n * k].reshape(n, k)
 
 
 def moe_get_stats(ctx) -> dict:

@@ -107,7 +107,14 @@ moe_status check_ctx(moe_ctx* ctx) {
 
 Ctx* C_(moe_ctx* ctx) { return reinterpret_cast<Ctx*>(ctx); }
 
-hipEvent_t next_event(Ctx* c) {
+
+constexpr size_t kMaxTimingPairs = 65536;
+
+}  // namespace
+
+namespace moe {
+
+hipEvent_t timing_event(Ctx* c) {
   if (c->ev_next == c->ev_pool.size()) {
     hipEvent_t e;
     if (hipEventCreate(&e) != hipSuccess) return nullptr;
@@ -115,12 +122,6 @@ hipEvent_t next_event(Ctx* c) {
   }
   return c->ev_pool[c->ev_next++];
 }
-
-constexpr size_t kMaxTimingPairs = 65536;
-
-}  // namespace
-
-namespace moe {
 
 // --------------------------------------------------------------- repacking
 // Canonical row r of a [N][K] MXFP4 matrix: codes q[r][K/2], scales s[r][K/32].
@@ -361,8 +362,8 @@ moe_status moe_layer_forward(moe_ctx* ctx, int32_t layer, const void* d_x, int32
   HIPCHK(launch_fill(c->d_fills, c->d_meta, c->max_unique, c->rec_bytes, st));
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (c->timing && c->t_decode.size() < kMaxTimingPairs) {
-    e0 = next_event(c);
-    e1 = next_event(c);
+    e0 = timing_event(c);
+    e1 = timing_event(c);
     if (e0 && e1) HIPCHK(hipEventRecord(e0, st));
   }
   HIPCHK(launch_expert_gateup(c, (const uint16_t*)d_x, T, st));
@@ -575,6 +576,13 @@ moe_status moe_inspect_dispatch(moe_ctx* ctx, int32_t* h_T, int32_t* h_counts,
     HIPCHK(hipMemcpy(h_unique, c->d_unique, (size_t)m.n_unique * 4, hipMemcpyDeviceToHost));
   if (h_slot && m.n_unique)
     HIPCHK(hipMemcpy(h_slot, c->d_slotcode, (size_t)m.n_unique * 4, hipMemcpyDeviceToHost));
+  return MOE_OK;
+}
+
+moe_status moe_inspect_prefill(moe_ctx* ctx, int32_t* h_T, int32_t* h_ids, float* h_gates) {
+  if (moe_status s = check_ctx(ctx)) return s;
+  if (!h_T) return fail(MOE_ERR_INVALID_ARG, "h_T is NULL");
+  HIPCHK(prefill_inspect(C_(ctx), h_T, h_ids, h_gates));
   return MOE_OK;
 }
 

@@ -340,11 +340,17 @@ hipError_t launch_expert_down(const Ctx* c, int T, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const Ctx* c, int T, uint16_t* y, float* y32, hipStream_t st) {
-  dim3 grid((c->cfg.hidden + 255) / 256, T);
-  combine_kernel<<<grid, 256, 0, st>>>(c->d_yperm, c->d_inv, c->d_gates, T, c->cfg.top_k,
-                                       c->cfg.hidden, c->cfg.has_shared, y, y32);
+hipError_t launch_combine_rows(const float* yperm, const int32_t* inv, const float* gates, int T,
+                               int k, int H, int has_shared, uint16_t* y, float* y32,
+                               hipStream_t st) {
+  dim3 grid((H + 255) / 256, T);
+  combine_kernel<<<grid, 256, 0, st>>>(yperm, inv, gates, T, k, H, has_shared, y, y32);
   return hipGetLastError();
+}
+
+hipError_t launch_combine(const Ctx* c, int T, uint16_t* y, float* y32, hipStream_t st) {
+  return launch_combine_rows(c->d_yperm, c->d_inv, c->d_gates, T, c->cfg.top_k, c->cfg.hidden,
+                             c->cfg.has_shared, y, y32, st);
 }
 
 }  // namespace moe

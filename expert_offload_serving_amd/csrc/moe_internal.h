@@ -189,8 +189,15 @@ hipError_t launch_expert_gateup(const Ctx* c, const uint16_t* x, int T,
                                 hipStream_t st);
 hipError_t launch_expert_down(const Ctx* c, int T, hipStream_t st);
 hipError_t launch_combine(const Ctx* c, int T, uint16_t* y, float* y32, hipStream_t st);
+hipError_t launch_combine_rows(const float* yperm, const int32_t* inv, const float* gates, int T,
+                               int k, int H, int has_shared, uint16_t* y, float* y32,
+                               hipStream_t st);
+
+// Next event of the context's timing pool (created on demand; NULL on failure).
+hipEvent_t timing_event(Ctx* c);
 
 // prefill
+hipError_t prefill_inspect(Ctx* c, int32_t* T, int32_t* ids, float* gates);
 hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* x, int T,
                            const float* const* bias, void* const* y, float* const* y32,
                            hipStream_t st);

@@ -1,13 +1,595 @@
-// Prefill forward (grouped MFMA GEMMs, double-buffered layer uploads).
+// Prefill forward: whole layers of experts streamed from the pinned pool into
+// two HBM layer buffers (layer l+1 uploads on a copy stream while layer l
+// computes: aipolix.com FreeToken article, fourth paragraph; jansverre.net
+// FreeToken article, section "Hvorfor er båndbredden viktigere enn antall
+// kjerner?"), an fp64 router GEMM on MFMA, multi-workgroup top-k and
+// counting-sort dispatch, and the expert FFN as grouped bf16 MFMA GEMMs over
+// every expert with fused MXFP4 dequantisation.
+#include <algorithm>
+
 #include "moe_internal.h"
+#include "route_common.h"
 
 namespace moe {
 
-hipError_t prefill_forward(Ctx*, int, const void* const*, int, const float* const*, void* const*,
-                           float* const*, hipStream_t) {
-  return hipErrorNotSupported;
+struct Prefill {
+  int Tmax = 0;
+  int last_T = 0;
+  int nchunk_max = 0;
+  int max_tiles = 0;
+  float* logits = nullptr;     // [Tmax][E]
+  int32_t* ids = nullptr;      // [Tmax*k]
+  float* gates = nullptr;      // [Tmax*k]
+  int32_t* chunk_cnt = nullptr;  // [nchunk][E]
+  int32_t* counts = nullptr;   // [E+1]: rows per group (group E: shared expert)
+  int32_t* offsets = nullptr;  // [E+1]: first permuted row per group
+  int32_t* sorted = nullptr;   // [Tmax*k]
+  int32_t* inv = nullptr;      // [Tmax*k]
+  int32_t* tok = nullptr;      // [Tmax*k + Tmax]
+  int2* tiles = nullptr;       // [max_tiles]: (group, first row)
+  int32_t* n_tiles = nullptr;  // [1]
+  uint16_t* h = nullptr;       // bf16 [rows][I]
+  float* yperm = nullptr;      // [rows][H]
+};
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunkTokens = 64;   // tokens per dispatch chunk (one wave)
+constexpr int kBM = 128;           // tokens per GEMM tile
+constexpr int kFragsPerWave = 4;   // 16-row weight fragments per wave
+constexpr int kLdsRow = kAtomK * 2 + 16;  // bytes per staged A row (padded)
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ bf16x8 dequant8(uint32_t q, uint32_t sbyte) {
+  const float s = __uint_as_float(sbyte << 23);
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 3));
+  return __builtin_bit_cast(bf16x8, r);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
+
+// ---------------------------------------------------------------- router
+// logits[t][e] = fp32(sum_h x[t][h] W_r[h][e] + bias), fp64 products and
+// sums on v_mfma_f64_16x16x4_f64.  Block: 64 tokens x 64 experts, K staged
+// through LDS in chunks of 64 as fp32 (bf16 x and fp32 W_r are exact in
+// fp64); each wave owns a 32 x 32 sub-tile (2 x 2 fragments).  Operands:
+// lane l holds A[l % 16][l / 16] and B[l / 16][l % 16] of a K=4 step.
+__global__ __launch_bounds__(256) void router_prefill_kernel(
+    const uint16_t* __restrict__ x, int T, int H, int E, const float* __restrict__ wrt,
+    const float* __restrict__ bias, float* __restrict__ logits) {
+  __shared__ float xs[64][65];
+  __shared__ float ws[64][65];
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w & 1, wn = w >> 1;
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int k0 = 0; k0 < H; k0 += 64) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 8; i += 256) {  // 64 rows x 8 pieces of 8
+      const int r = i >> 3, q = i & 7;
+      const int t = t0 + r, e = e0 + r;
+      u32x4 xv = {0u, 0u, 0u, 0u};
+      if (t < T) xv = *reinterpret_cast<const u32x4*>(x + (size_t)t * H + k0 + 8 * q);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        xs[r][8 * q + 2 * j] = __uint_as_float(xv[j] << 16);
+        xs[r][8 * q + 2 * j + 1] = __uint_as_float(xv[j] & 0xFFFF0000u);
+      }
+      f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = {0.f, 0.f, 0.f, 0.f};
+      if (e < E) {
+        w0 = *reinterpret_cast<const f32x4*>(wrt + (size_t)e * H + k0 + 8 * q);
+        w1 = *reinterpret_cast<const f32x4*>(wrt + (size_t)e * H + k0 + 8 * q + 4);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        ws[r][8 * q + j] = w0[j];
+        ws[r][8 * q + 4 + j] = w1[j];
+      }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < 64; kk += 4) {
+      double a[2], b[2];
+#pragma unroll
+      for (int f = 0; f < 2; f++) {
+        a[f] = (double)xs[wm * 32 + f * 16 + (lane & 15)][kk + (lane >> 4)];
+        b[f] = (double)ws[wn * 32 + f * 16 + (lane & 15)][kk + (lane >> 4)];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        // f64 16x16x4 output: lane l, register r holds row (l / 16) + 4 r
+        const int t = t0 + wm * 32 + i * 16 + (lane >> 4) + 4 * r;
+        const int e = e0 + wn * 32 + j * 16 + (lane & 15);
+        if (t < T && e < E) {
+          const size_t o = (size_t)t * E + e;
+          const double s = acc[i][j][r];
+          logits[o] = (float)(bias ? s + (double)bias[o] : s);
+        }
+      }
 }
 
-void prefill_free(Ctx*) {}
+// ------------------------------------------------------------------ top-k
+template <int NK>
+__global__ __launch_bounds__(1024) void topk_prefill_kernel(TopkArgs a, int T) {
+  const int t = blockIdx.x * 16 + (threadIdx.x >> 6);
+  if (t < T) topk_token<NK>(a, t, nullptr);
+}
+
+// --------------------------------------------------------------- dispatch
+// Per chunk of 64 tokens: a bit matrix [token][expert] in LDS, then for each
+// expert a ballot over the chunk's tokens gives the count (and, in the place
+// kernel, each token's rank among the chunk's tokens of that expert).
+__device__ void chunk_bits(const int32_t* ids, int T, int k, int chunk, uint32_t (*bits)[33]) {
+  for (int i = threadIdx.x; i < kChunkTokens * 32; i += blockDim.x) bits[i >> 5][i & 31] = 0u;
+  __syncthreads();
+  for (int i = threadIdx.x; i < kChunkTokens * k; i += blockDim.x) {
+    const int r = i / k, t = chunk * kChunkTokens + r;
+    if (t < T) {
+      const int e = ids[t * k + i % k];
+      atomicOr(&bits[r][e >> 5], 1u << (e & 31));
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ ids,
+                                                             int T, int k, int E,
+                                                             int32_t* __restrict__ chunk_cnt) {
+  __shared__ uint32_t bits[kChunkTokens][33];
+  const int c = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  chunk_bits(ids, T, k, c, bits);
+  for (int e = w; e < E; e += blockDim.x >> 6) {
+    const bool has = (bits[lane][e >> 5] >> (e & 31)) & 1u;
+    const uint64_t b = __ballot(has);
+    if (lane == 0) chunk_cnt[(size_t)c * E + e] = __popcll(b);
+  }
+}
+
+__global__ __launch_bounds__(1024) void dispatch_place_kernel(
+    const int32_t* __restrict__ ids, int T, int k, int E, int has_shared, int nchunk,
+    const int32_t* __restrict__ chunk_cnt, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted, int32_t* __restrict__ inv,
+    int32_t* __restrict__ tok, int2* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+  __shared__ uint32_t bits[kChunkTokens][33];
+  __shared__ int s_base[1024];
+  __shared__ int s_tmp[16];
+  const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  chunk_bits(ids, T, k, c, bits);
+  const int e = tid;
+  int tot = 0, pre = 0;
+  if (e < E) {
+    for (int cc = 0; cc < nchunk; cc++) {
+      const int v = chunk_cnt[(size_t)cc * E + e];
+      tot += v;
+      if (cc < c) pre += v;
+    }
+  }
+  int total;
+  const int off = block_excl_scan(tot, s_tmp, &total);
+  if (e < E) s_base[e] = off + pre;
+  if (c == 0) {
+    if (e < E) {
+      counts[e] = tot;
+      offsets[e] = off;
+    }
+    if (tid == 0) {
+      counts[E] = has_shared ? T : 0;
+      offsets[E] = T * k;
+    }
+    // GEMM tiles of kBM rows: routed groups 0..E-1, then the shared group E
+    const int nt = e < E ? (tot + kBM - 1) / kBM : 0;
+    int ntot;
+    const int tfirst = block_excl_scan(nt, s_tmp, &ntot);
+    for (int i = 0; i < nt; i++) tiles[tfirst + i] = int2{e, i * kBM};
+    const int nts = has_shared ? (T + kBM - 1) / kBM : 0;
+    for (int i = tid; i < nts; i += blockDim.x) tiles[ntot + i] = int2{E, i * kBM};
+    if (tid == 0) *n_tiles = ntot + nts;
+    if (has_shared)
+      for (int t = tid; t < T; t += blockDim.x) tok[T * k + t] = t;
+  }
+  __syncthreads();
+  const int t = c * kChunkTokens + lane;
+  for (int ee = w; ee < E; ee += blockDim.x >> 6) {
+    const bool has = (bits[lane][ee >> 5] >> (ee & 31)) & 1u;
+    const uint64_t b = __ballot(has);
+    if (has) {
+      const int pos = s_base[ee] + __popcll(b & ((1ull << lane) - 1ull));
+      int j = 0;
+      while (ids[t * k + j] != ee) j++;
+      const int f = t * k + j;
+      sorted[pos] = f;
+      inv[f] = pos;
+      tok[pos] = t;
+    }
+  }
+}
+
+// -------------------------------------------------------------- grouped GEMM
+// Tile t of the tile list and n-block nb, with the workgroups of one tile
+// kept on one XCD (workgroup ids are dealt round-robin over the 8 XCDs), so
+// that the tile's gathered token rows stay in that XCD's L2.
+__device__ __forceinline__ void tile_of_block(int nbn, int* ti, int* nb) {
+  const int L = blockIdx.x, xcd = L & 7, j = L >> 3;
+  *ti = (j / nbn) * 8 + xcd;
+  *nb = j % nbn;
+}
+
+// One GEMM: C[tile rows][4 waves x 4 fragments x 16 columns] over K in
+// chunks of 128.  A rows (bf16, gathered through `arow`) are staged in LDS
+// with the next chunk prefetched in registers; each wave streams its 4
+// weight fragments (MXFP4 atoms, dequantised in registers) with the next
+// chunk prefetched.  `frag_row_group(f)` gives the atom row group of the
+// wave's fragment f.
+struct GemmTile {
+  const uint8_t* wbase;  // expert record (section start)
+  int KC;                // K chunks
+  int rg[kFragsPerWave]; // atom row group per fragment (this wave)
+  int rows;              // valid rows in this tile (<= kBM)
+};
+
+__device__ __forceinline__ void gemm_tile(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
+                                          const uint32_t* arow_off, uint8_t* As,
+                                          f32x4 (&acc)[kBM / 16][kFragsPerWave]) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int mfrags = (gt.rows + 15) >> 4;
+  // A staging: 128 rows x 16 pieces of 16 bytes, 8 pieces per thread
+  u32x4 areg[8];
+  auto load_a = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int q = (tid + 256 * i) & 15;
+      const uint32_t o = arow_off[i];
+      areg[i] = bload16(ra, o == kOOB ? kOOB : o + (uint32_t)(c * kAtomK + 8 * q) * 2u);
+    }
+  };
+  auto store_a = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int p = tid + 256 * i, r = p >> 4, q = p & 15;
+      *reinterpret_cast<u32x4*>(As + r * kLdsRow + q * 16) = areg[i];
+    }
+  };
+  u32x4 wd[2][kFragsPerWave];
+  uint32_t sd[2][kFragsPerWave];
+  auto load_w = [&](int c, int buf) {
+#pragma unroll
+    for (int f = 0; f < kFragsPerWave; f++) {
+      const uint8_t* atom = gt.wbase + ((size_t)gt.rg[f] * gt.KC + c) * kAtomBytes;
+      wd[buf][f] = *reinterpret_cast<const u32x4*>(atom + lane * 16);
+      sd[buf][f] = atom[kAtomData + lane];
+    }
+  };
+  load_a(0);
+  load_w(0, 0);
+  __syncthreads();  // the previous tile's readers of As are done
+  store_a();
+  __syncthreads();
+  for (int c = 0; c < gt.KC; c++) {
+    const int cur = c & 1;
+    if (c + 1 < gt.KC) {
+      load_a(c + 1);
+      load_w(c + 1, cur ^ 1);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      bf16x8 b[kFragsPerWave];
+#pragma unroll
+      for (int f = 0; f < kFragsPerWave; f++) b[f] = dequant8(wd[cur][f][j], sd[cur][f]);
+#pragma unroll
+      for (int mf = 0; mf < kBM / 16; mf++) {
+        if (mf < mfrags) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+              As + (mf * 16 + (lane & 15)) * kLdsRow + 64 * (lane >> 4) + 16 * j);
+#pragma unroll
+          for (int f = 0; f < kFragsPerWave; f++)
+            acc[mf][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[f], acc[mf][f], 0, 0, 0);
+        }
+      }
+    }
+    if (c + 1 < gt.KC) {
+      __syncthreads();
+      store_a();
+      __syncthreads();
+    }
+  }
+}
+
+struct GroupArgs {
+  const int2* tiles;
+  const int32_t* n_tiles;
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* tok;
+  const uint8_t* layerbuf;
+  size_t stride;
+  const uint8_t* shared_w;
+  int E;
+};
+
+// Gate/up + SwiGLU.  N-block nb covers 8 row pairs (gate, up): wave w takes
+// pairs nb*8 + 2w and +1 (fragments g0, u0, g1, u1).
+__global__ __launch_bounds__(256) void gateup_prefill_kernel(GroupArgs g, const uint16_t* x,
+                                                             uint32_t x_bytes, int H, int I,
+                                                             int nbn, uint16_t* __restrict__ h) {
+  int ti, nb;
+  tile_of_block(nbn, &ti, &nb);
+  if (ti >= *g.n_tiles) return;
+  __shared__ __attribute__((aligned(16))) uint8_t As[kBM * kLdsRow];
+  const int2 td = g.tiles[ti];
+  const int grp = td.x, m0 = td.y;
+  const int cnt = g.counts[grp], pos0 = g.offsets[grp];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  GemmTile gt;
+  gt.wbase = grp < g.E ? g.layerbuf + (size_t)grp * g.stride : g.shared_w;
+  gt.KC = H / kAtomK;
+  gt.rows = min(kBM, cnt - m0);
+  const int p0 = nb * 8 + 2 * w;
+  gt.rg[0] = 2 * p0;
+  gt.rg[1] = 2 * p0 + 1;
+  gt.rg[2] = 2 * p0 + 2;
+  gt.rg[3] = 2 * p0 + 3;
+  uint32_t arow[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int r = (tid + 256 * i) >> 4;
+    arow[i] = r < gt.rows ? (uint32_t)g.tok[pos0 + m0 + r] * (uint32_t)H * 2u : kOOB;
+  }
+  f32x4 acc[kBM / 16][kFragsPerWave];
+#pragma unroll
+  for (int i = 0; i < kBM / 16; i++)
+#pragma unroll
+    for (int f = 0; f < kFragsPerWave; f++) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  gemm_tile(gt, rsrc(x, x_bytes), arow, As, acc);
+#pragma unroll
+  for (int mf = 0; mf < kBM / 16; mf++) {
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int m = mf * 16 + 4 * (lane >> 4) + i;
+        if (m < gt.rows) {
+          const float hv = silu(acc[mf][2 * q][i]) * acc[mf][2 * q + 1][i];
+          h[(size_t)(pos0 + m0 + m) * I + (p0 + q) * 16 + (lane & 15)] = f32_to_bf16_rne(hv);
+        }
+      }
+    }
+  }
+}
+
+// Down.  N-block nb covers 16 row groups of H (256 columns): wave w takes
+// row groups nb*16 + 4w .. +3.
+__global__ __launch_bounds__(256) void down_prefill_kernel(GroupArgs g, const uint16_t* h,
+                                                           uint32_t h_bytes, int H, int I, int nbn,
+                                                           size_t gateup_bytes,
+                                                           float* __restrict__ yperm) {
+  int ti, nb;
+  tile_of_block(nbn, &ti, &nb);
+  if (ti >= *g.n_tiles) return;
+  __shared__ __attribute__((aligned(16))) uint8_t As[kBM * kLdsRow];
+  const int2 td = g.tiles[ti];
+  const int grp = td.x, m0 = td.y;
+  const int cnt = g.counts[grp], pos0 = g.offsets[grp];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  GemmTile gt;
+  gt.wbase = (grp < g.E ? g.layerbuf + (size_t)grp * g.stride : g.shared_w) + gateup_bytes;
+  gt.KC = I / kAtomK;
+  gt.rows = min(kBM, cnt - m0);
+  const int rg0 = nb * 16 + 4 * w;
+  const int ngroups = H / kAtomRows;  // a multiple of 8; the last n-block may be partial
+#pragma unroll
+  for (int f = 0; f < kFragsPerWave; f++) gt.rg[f] = rg0 + f < ngroups ? rg0 + f : 0;
+  uint32_t arow[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int r = (tid + 256 * i) >> 4;
+    arow[i] = r < gt.rows ? (uint32_t)(pos0 + m0 + r) * (uint32_t)I * 2u : kOOB;
+  }
+  f32x4 acc[kBM / 16][kFragsPerWave];
+#pragma unroll
+  for (int i = 0; i < kBM / 16; i++)
+#pragma unroll
+    for (int f = 0; f < kFragsPerWave; f++) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  gemm_tile(gt, rsrc(h, h_bytes), arow, As, acc);
+#pragma unroll
+  for (int mf = 0; mf < kBM / 16; mf++)
+#pragma unroll
+    for (int f = 0; f < kFragsPerWave; f++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int m = mf * 16 + 4 * (lane >> 4) + i;
+        if (m < gt.rows && rg0 + f < ngroups)
+          yperm[(size_t)(pos0 + m0 + m) * H + (rg0 + f) * 16 + (lane & 15)] = acc[mf][f][i];
+      }
+}
+
+template <class T>
+hipError_t dalloc(T** p, size_t n) {
+  return hipMalloc((void**)p, std::max<size_t>(n, 1) * sizeof(T));
+}
+
+hipError_t prefill_alloc(Ctx* c) {
+  if (c->pf) return hipSuccess;
+  const moe_config& f = c->cfg;
+  Prefill* p = new Prefill();
+  c->pf = p;
+  const int T = f.max_prefill_tokens, E = f.n_experts, k = f.top_k;
+  p->Tmax = T;
+  p->nchunk_max = (T + kChunkTokens - 1) / kChunkTokens;
+  p->max_tiles = ((T * k + T + kBM - 1) / kBM + E + 1 + 7) / 8 * 8;
+  const size_t rows = (size_t)T * k + T;
+  hipError_t e;
+#define PA(ptr, n) \
+  if ((e = dalloc(&p->ptr, (n))) != hipSuccess) return e
+  PA(logits, (size_t)T * E);
+  PA(ids, (size_t)T * k);
+  PA(gates, (size_t)T * k);
+  PA(chunk_cnt, (size_t)p->nchunk_max * E);
+  PA(counts, (size_t)E + 1);
+  PA(offsets, (size_t)E + 1);
+  PA(sorted, (size_t)T * k);
+  PA(inv, (size_t)T * k);
+  PA(tok, rows);
+  PA(tiles, (size_t)p->max_tiles);
+  PA(n_tiles, 1);
+  PA(h, rows * f.inter);
+  PA(yperm, rows * f.hidden);
+#undef PA
+  const size_t layer_bytes = (size_t)E * c->stride;
+  for (int b = 0; b < 2; b++)
+    if ((e = hipMalloc((void**)&c->d_layerbuf[b], layer_bytes)) != hipSuccess) return e;
+  if ((e = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking)) != hipSuccess) return e;
+  for (int b = 0; b < 2; b++) {
+    if ((e = hipEventCreateWithFlags(&c->ev_upload[b], hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&c->ev_compute[b], hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+void prefill_free(Ctx* c) {
+  if (c->copy_stream) (void)hipStreamSynchronize(c->copy_stream);
+  if (Prefill* p = c->pf) {
+    void* ptrs[] = {p->logits, p->ids, p->gates, p->chunk_cnt, p->counts, p->offsets, p->sorted,
+                    p->inv, p->tok, p->tiles, p->n_tiles, p->h, p->yperm};
+    for (void* q : ptrs)
+      if (q) (void)hipFree(q);
+    delete p;
+    c->pf = nullptr;
+  }
+  for (int b = 0; b < 2; b++) {
+    if (c->d_layerbuf[b]) (void)hipFree(c->d_layerbuf[b]);
+    c->d_layerbuf[b] = nullptr;
+    if (c->ev_upload[b]) (void)hipEventDestroy(c->ev_upload[b]);
+    if (c->ev_compute[b]) (void)hipEventDestroy(c->ev_compute[b]);
+    c->ev_upload[b] = c->ev_compute[b] = nullptr;
+  }
+  if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
+  c->copy_stream = nullptr;
+}
+
+hipError_t prefill_inspect(Ctx* c, int32_t* T, int32_t* ids, float* gates) {
+  *T = c->pf ? c->pf->last_T : 0;
+  if (!c->pf || !*T) return hipSuccess;
+  hipError_t e = hipDeviceSynchronize();
+  const size_t n = (size_t)*T * c->cfg.top_k;
+  if (e == hipSuccess && ids) e = hipMemcpy(ids, c->pf->ids, n * 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && gates) e = hipMemcpy(gates, c->pf->gates, n * 4, hipMemcpyDeviceToHost);
+  return e;
+}
+
+hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
+                           const float* const* biases, void* const* ys, float* const* y32s,
+                           hipStream_t st) {
+  hipError_t e = prefill_alloc(c);
+  if (e != hipSuccess) {
+    prefill_free(c);
+    return e;
+  }
+  Prefill* p = c->pf;
+  p->last_T = T;
+  const moe_config& f = c->cfg;
+  const int H = f.hidden, I = f.inter, E = f.n_experts, k = f.top_k;
+  const size_t layer_bytes = (size_t)E * c->stride;
+  const int nchunk = (T + kChunkTokens - 1) / kChunkTokens;
+  const size_t rows = (size_t)T * k + (f.has_shared ? T : 0);
+
+  // Uploads wait for everything already on the caller's stream (an earlier
+  // call may still read the layer buffers).
+  hipEvent_t entry = c->ev_compute[0];
+  if ((e = hipEventRecord(entry, st)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(c->copy_stream, entry, 0)) != hipSuccess) return e;
+  if ((e = hipMemcpyAsync(c->d_layerbuf[0], c->pool, layer_bytes, hipMemcpyHostToDevice,
+                          c->copy_stream)) != hipSuccess)
+    return e;
+  if ((e = hipEventRecord(c->ev_upload[0], c->copy_stream)) != hipSuccess) return e;
+
+  for (int l = 0; l < n_layers; l++) {
+    const int b = l & 1;
+    if (l + 1 < n_layers) {
+      // buffer b^1 was last read by layer l-1
+      if (l >= 1 && (e = hipStreamWaitEvent(c->copy_stream, c->ev_compute[b ^ 1], 0)) != hipSuccess)
+        return e;
+      if ((e = hipMemcpyAsync(c->d_layerbuf[b ^ 1], c->pool + (size_t)(l + 1) * layer_bytes,
+                              layer_bytes, hipMemcpyHostToDevice, c->copy_stream)) != hipSuccess)
+        return e;
+      if ((e = hipEventRecord(c->ev_upload[b ^ 1], c->copy_stream)) != hipSuccess) return e;
+    }
+    if ((e = hipStreamWaitEvent(st, c->ev_upload[b], 0)) != hipSuccess) return e;
+
+    const uint16_t* x = (const uint16_t*)xs[l];
+    const float* bias = biases ? biases[l] : nullptr;
+    const float* wrt = c->d_router + (size_t)l * H * E;
+    router_prefill_kernel<<<dim3((T + 63) / 64, (E + 63) / 64), 256, 0, st>>>(x, T, H, E, wrt,
+                                                                              bias, p->logits);
+    const TopkArgs ta{E, k, f.renormalize, p->logits, p->ids, p->gates, nullptr, nullptr};
+    const int nk = (E + 63) / 64, tb = (T + 15) / 16;
+    if (nk <= 1) topk_prefill_kernel<1><<<tb, 1024, 0, st>>>(ta, T);
+    else if (nk <= 2) topk_prefill_kernel<2><<<tb, 1024, 0, st>>>(ta, T);
+    else if (nk <= 4) topk_prefill_kernel<4><<<tb, 1024, 0, st>>>(ta, T);
+    else if (nk <= 8) topk_prefill_kernel<8><<<tb, 1024, 0, st>>>(ta, T);
+    else topk_prefill_kernel<16><<<tb, 1024, 0, st>>>(ta, T);
+    dispatch_count_kernel<<<nchunk, 256, 0, st>>>(p->ids, T, k, E, p->chunk_cnt);
+    dispatch_place_kernel<<<nchunk, 1024, 0, st>>>(p->ids, T, k, E, f.has_shared, nchunk,
+                                                   p->chunk_cnt, p->counts, p->offsets, p->sorted,
+                                                   p->inv, p->tok, p->tiles, p->n_tiles);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    GroupArgs ga{p->tiles, p->n_tiles, p->counts, p->offsets, p->tok, c->d_layerbuf[b],
+                 c->stride, f.has_shared ? c->d_shared + (size_t)l * c->stride : nullptr, E};
+    hipEvent_t t0 = nullptr, t1 = nullptr;
+    if (c->timing && c->t_prefill.size() < 65536) {
+      t0 = timing_event(c);
+      t1 = timing_event(c);
+      if (t0 && t1) (void)hipEventRecord(t0, st);
+    }
+    const int nbn_gu = I / (16 * 8), nbn_dn = (H + 255) / 256;
+    gateup_prefill_kernel<<<p->max_tiles * nbn_gu, 256, 0, st>>>(ga, x, (uint32_t)T * H * 2, H, I,
+                                                                nbn_gu, p->h);
+    down_prefill_kernel<<<p->max_tiles * nbn_dn, 256, 0, st>>>(
+        ga, p->h, (uint32_t)(rows * I * 2), H, I, nbn_dn, gateup_section_bytes(H, I), p->yperm);
+    if (t0 && t1) {
+      (void)hipEventRecord(t1, st);
+      c->t_prefill.emplace_back(t0, t1);
+    }
+    if ((e = launch_combine_rows(p->yperm, p->inv, p->gates, T, k, H, f.has_shared,
+                                 (uint16_t*)ys[l], y32s ? y32s[l] : nullptr, st)) != hipSuccess)
+      return e;
+    if ((e = hipEventRecord(c->ev_compute[b], st)) != hipSuccess) return e;
+  }
+  return hipGetLastError();
+}
 
 }  // namespace moe

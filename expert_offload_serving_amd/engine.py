@@ -17,6 +17,7 @@ class MoEEngine:
         self.H, self.I, self.E, self.k, self.L = H, I, E, k, n_layers
         self.has_shared = bool(has_shared)
         self.max_tokens = max_tokens
+        self.max_prefill_tokens = max_prefill_tokens
         self.ctx = b.moe_create(hidden=H, inter=I, n_experts=E, top_k=k, n_layers=n_layers,
                                 has_shared=int(has_shared), renormalize=int(renormalize),
                                 max_tokens=max_tokens, cache_slots=cache_slots,
@@ -64,6 +65,10 @@ class MoEEngine:
 
     def inspect_dispatch(self):
         return b.moe_inspect_dispatch(self.ctx, self.E, self.k, self.max_tokens)
+
+    def inspect_prefill(self):
+        """(ids, gates) of the last layer of the last prefill call."""
+        return b.moe_inspect_prefill(self.ctx, self.k, self.max_prefill_tokens)
 
     def stats(self) -> dict:
         return b.moe_get_stats(self.ctx)

@@ -248,6 +248,13 @@ moe_status moe_inspect_dispatch(moe_ctx* ctx, int32_t* h_T, int32_t* h_counts,
                                 int32_t* h_inv, int32_t* h_unique,
                                 int32_t* h_n_unique, int32_t* h_slot);
 
+/*
+ * (sync) Copy the routing of the last layer run by moe_prefill_forward:
+ * h_ids int32 [T][k], h_gates fp32 [T][k] (either may be NULL); *h_T
+ * receives that call's T (0 if none ran).
+ */
+moe_status moe_inspect_prefill(moe_ctx* ctx, int32_t* h_T, int32_t* h_ids, float* h_gates);
+
 /* (sync) Read / clear the counters. */
 moe_status moe_get_stats(moe_ctx* ctx, moe_stats* out);
 moe_status moe_reset_stats(moe_ctx* ctx);

@@ -178,3 +178,53 @@ class DecodeRun:
 def small_shape(**kw) -> gen.Shape:
     base = gen.Shape(H=256, I=512, E=8, k=2)
     return replace(base, **kw)
+
+
+class PrefillRun:
+    """Prefill of a layer stack: every layer gets its own seeded x [T][H]."""
+
+    def __init__(self, shape: gen.Shape, T: int, seed: int = 0, model: Optional[Model] = None,
+                 bias_sets=None):
+        import torch
+        self.shape, self.T = shape, T
+        self.model = model or Model(shape, seed)
+        self.eng = make_engine(shape, max_tokens=1, cache_slots=0, staging_slots=shape.k,
+                               max_prefill_tokens=T)
+        self.model.load(self.eng)
+        L = shape.layers
+        self.xb = [gen.tokens(shape, l, 0, T, self.model.seed) for l in range(L)]
+        self.xs = [bf16_dev(b) for b in self.xb]
+        self.bias = bias_sets
+        self.bias_dev = (None if bias_sets is None else
+                         [torch.from_numpy(b).to("cuda") for b in bias_sets])
+        self.ys = [torch.empty((T, shape.H), dtype=torch.int16, device="cuda") for _ in range(L)]
+        self.y32 = [torch.empty((T, shape.H), dtype=torch.float32, device="cuda") for _ in range(L)]
+
+    def run(self):
+        import torch
+        self.eng.prefill(self.xs, self.ys, biases=self.bias_dev, y32s=self.y32)
+        torch.cuda.synchronize()
+
+    def route(self, layer):
+        xf = gen.bf16_bits_to_f32(self.xb[layer])
+        b = None if self.bias is None else self.bias[layer]
+        return xf, self.model.route(layer, xf, b)
+
+    def reference_rows(self, layer, tokens, ids, g):
+        """Oracle outputs of the sampled tokens, evaluated expert by expert
+        (each expert dequantised once) with oracle.expert_ffn."""
+        xf = gen.bf16_bits_to_f32(self.xb[layer])
+        y = {t: np.zeros(self.shape.H) for t in tokens}
+        need = sorted({int(ids[t, j]) for t in tokens for j in range(self.shape.k)})
+        for e in need + ([-1] if self.shape.shared else []):
+            wg, wu, wd = oexp.dequant_expert(self.model.expert(layer, e))
+            for t in tokens:
+                if e < 0:
+                    y[t] += oracle.expert_ffn(xf[t], wg, wu, wd)
+                elif e in ids[t]:
+                    j = list(ids[t]).index(e)
+                    y[t] += float(g[t, j]) * oracle.expert_ffn(xf[t], wg, wu, wd)
+        return np.stack([y[t] for t in tokens])
+
+    def close(self):
+        self.eng.close()

@@ -1,0 +1,74 @@
+"""Prefill-path parity: the HIP library against the CPU oracle (GPU)."""
+import numpy as np
+import pytest
+
+from workload import gen
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_layer(run, layer, tokens, check_ids):
+    import torch
+    xf, (lg, ids_ref, g_ref) = run.route(layer)
+    if check_ids:
+        ids, g = run.eng.inspect_prefill()
+        assert np.array_equal(ids, ids_ref), f"prefill ids differ at layer {layer}"
+        assert np.max(np.abs(g - g_ref)) <= H.ATOL_G
+        if run.shape.renormalize:
+            assert np.max(np.abs(g.astype(np.float64).sum(1) - 1)) <= H.TOL_SUM
+    H.check_rounding(run.ys[layer], run.y32[layer], f"prefill layer {layer}")
+    y_ref = run.reference_rows(layer, tokens, ids_ref, g_ref)
+    y32 = run.y32[layer].cpu().numpy()[tokens]
+    return H.check_y(y32, y_ref, what=f"prefill layer {layer}")
+
+
+@pytest.mark.parametrize("T,kw", [(300, dict(E=32, k=4, shared=True, layers=3)),
+                                  (129, dict(E=16, k=2, layers=2)),
+                                  (64, dict(E=64, k=8, shared=True, renormalize=False)),
+                                  (1000, dict(H=384, I=256, E=40, k=6, layers=2))])
+def test_prefill_small_all_tokens(T, kw):
+    """Ragged token counts (not multiples of the 64/128-row tiles), every
+    layer, every token."""
+    sh = H.small_shape(**kw)
+    print(f"case: prefill T={T} {kw}", flush=True)
+    run = H.PrefillRun(sh, T, seed=4)
+    run.run()
+    for l in range(sh.layers):
+        _check_layer(run, l, list(range(T)), check_ids=(l == sh.layers - 1))
+    run.close()
+
+
+def test_prefill_single_token_and_bias():
+    sh = H.small_shape(E=16, k=4, shared=True, layers=2)
+    T = 1
+    sets = [gen.zipf_sets(sh, l, T, 1, 1.1, 0.5, 0)[0] for l in range(2)]
+    bias = [gen.bias_from_sets(s, sh.E) for s in sets]
+    run = H.PrefillRun(sh, T, seed=7, bias_sets=bias)
+    run.run()
+    for l in range(2):
+        _check_layer(run, l, [0], check_ids=(l == 1))
+    ids, _ = run.eng.inspect_prefill()
+    assert sorted(ids[0].tolist()) == sorted(sets[1][0].tolist())
+    run.close()
+
+
+def test_prefill_dsv4_full_size():
+    """DeepSeek-V4-Flash-shaped prefill, T=4096, 4 layers, double-buffered
+    uploads: last layer's routing of all 4096 tokens bit-exact; outputs of
+    sampled tokens (first, last, and spread) on layers 0 and 3."""
+    wl = gen.WORKLOADS["dsv4_prefill"]
+    sh = wl.shape
+    T = wl.Ts[0]
+    print("case: dsv4_prefill T=4096 (loading 13.7 GB expert pool)", flush=True)
+    run = H.PrefillRun(sh, T, seed=0, model=H.Model(sh, cache_entries=4))
+    run.run()
+    e0 = _check_layer(run, 3, [0, 1, 777, 2048, 4095], check_ids=True)
+    e1 = _check_layer(run, 0, [5, 1500, 4094], check_ids=False)
+    print(f"dsv4 prefill max err/rms {max(e0, e1):.3e}", flush=True)
+    # a second call reuses the layer buffers: same outputs bit for bit
+    import torch
+    first = run.ys[3].clone()
+    run.run()
+    assert torch.equal(first, run.ys[3])
+    run.close()

@@ -1,12 +1,16 @@
 """Benchmark of the routed MoE expert-layer forward on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--T T]
+                [--prefill-steps P]
 
 A step is one decode call per layer of the workload (router, top-k, dispatch,
 cache lookup, miss fills, expert FFN, combine) for a batch of T tokens, with
 all inputs already resident in HBM.  Default workload: the 35B-A3B-shaped
 decode layer (H=2048, E=256, top-8, I=512, MXFP4 experts, bf16 activations,
 64-slot LRU from a cold start, Zipf(1.1) routing with 60% step overlap), T=16.
+The line also carries the prefill leg: the DeepSeek-V4-Flash-shaped stack
+(4 layers, H=4096, I=2048, E=256, top-6 + shared, T=4096) with whole-layer
+uploads from the pinned pool, its grouped-GEMM time and MFMA utilisation.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -36,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--extra-T", default="1,4", help="also time these T (decode)")
+    ap.add_argument("--prefill-steps", type=int, default=3,
+                    help="prefill passes of the DeepSeek-V4-Flash-shaped stack (0: skip)")
     return ap.parse_args()
 
 
@@ -126,6 +132,49 @@ def run_decode(wl, T, steps, warmup, seed=0):
                 h2d_gbs=st["bytes_h2d"] / (elapsed * 1e9))
 
 
+def run_prefill(wl, steps, warmup, seed=0):
+    """Prefill of the whole layer stack per step (layer uploads included)."""
+    import torch
+    from workload import gen
+    sh = wl.shape
+    T = wl.Ts[0]
+    eng = make_engine(sh, 1, 0, sh.k, prefill_tokens=T)
+    load_weights(eng, sh, seed)
+    xs = [bf16_dev(gen.tokens(sh, l, 0, T, seed)) for l in range(sh.layers)]
+    ys = [torch.empty((T, sh.H), dtype=torch.int16, device="cuda") for _ in range(sh.layers)]
+    for _ in range(warmup):
+        eng.prefill(xs, ys)
+    torch.cuda.synchronize()
+    eng.reset_stats()
+    eng.set_timing(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        eng.prefill(xs, ys)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    tm = eng.get_timing()
+    eng.close()
+    el = t1 - t0
+    layers = steps * sh.layers
+    # algorithmic flops per layer: 3 matrices of H x I per (token, expert),
+    # k routed experts plus the shared one, 2 flops per multiply-add
+    flops_layer = 2 * 3 * sh.H * sh.I * T * (sh.k + (1 if sh.shared else 0))
+    gemm_ms = tm["ms_prefill"] / max(tm["n_prefill"], 1)
+    tflops = flops_layer / (gemm_ms * 1e9)
+    upload = sh.E * sh.expert_bytes() * layers
+    return {"workload": wl.name, "T": T, "layers": sh.layers, "steps": steps,
+            "tokens_per_s_end_to_end": round(T * steps / el, 1),
+            "ms_per_step": round(1e3 * el / steps, 2),
+            "gemm_ms_per_layer": round(gemm_ms, 4),
+            "gemm_launches": tm["n_prefill"],
+            "tokens_per_s_gemm_only": round(T / (gemm_ms * 1e-3) / sh.layers, 1),
+            "flops_per_layer": flops_layer,
+            "mfma_tflops": round(tflops, 1),
+            "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+            "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "pcie_h2d_gbs": round(upload / (el * 1e9), 2)}
+
+
 def cpu_baseline(wl, T, seconds):
     """The oracle as it stands, on a bounded sample of the same workload."""
     import oracle
@@ -213,6 +262,8 @@ def main():
         "pcie_h2d_gbs": round(res["h2d_gbs"], 2),
         "other_T": extra,
     }
+    if a.prefill_steps > 0:
+        line["prefill"] = run_prefill(gen.WORKLOADS["dsv4_prefill"], a.prefill_steps, 1)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, T, a.cpu_seconds)
     print(json.dumps(line), flush=True)

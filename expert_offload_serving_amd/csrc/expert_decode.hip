@@ -95,7 +95,7 @@ __global__ __launch_bounds__(1024) void gateup_decode_kernel(
   const int KC = H / kAtomK;
   const uint8_t* gbase = it.w + (size_t)(2 * p) * KC * kAtomBytes;
   const uint8_t* ubase = gbase + (size_t)KC * kAtomBytes;
-  __shared__ f32x4 red[kMaxWaves][2][64];
+  extern __shared__ f32x4 red[];  // [waves][2][64], sized by the launch
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, x_bytes);
 
   // Token row of this lane in the first M tile.
@@ -156,15 +156,15 @@ __global__ __launch_bounds__(1024) void gateup_decode_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    red[w][0][lane] = ag;
-    red[w][1][lane] = au;
+    red[(2 * w) * 64 + lane] = ag;
+    red[(2 * w + 1) * 64 + lane] = au;
     __syncthreads();
     for (int v0 = threadIdx.x; v0 < 256; v0 += blockDim.x) {  // 64 lanes x 4 values
       const int L = v0 >> 2, i = v0 & 3;
       float gs = 0.f, us = 0.f;
       for (int v = 0; v < nw; v++) {
-        gs += red[v][0][L][i];
-        us += red[v][1][L][i];
+        gs += red[(2 * v) * 64 + L][i];
+        us += red[(2 * v + 1) * 64 + L][i];
       }
       const int mm = m0 + 4 * (L >> 4) + i;
       if (mm < it.cnt) {
@@ -184,8 +184,9 @@ __global__ __launch_bounds__(1024) void gateup_decode_kernel(
   }
 }
 
-// Down projection.  Block (row group rg, item): 16 rows of H of one expert;
-// waves split K = I; each weight fragment meets both h planes.
+// Down projection.  Block (row-group pair q, item): rows [32q, 32q+32) of H
+// of one expert, as two 16-row groups that share every h fragment; waves
+// split K = I; each weight fragment meets both h planes.
 template <int CPW>
 __global__ __launch_bounds__(1024) void down_decode_kernel(
     const WorkItem* __restrict__ items, const DevMeta* __restrict__ meta,
@@ -194,23 +195,26 @@ __global__ __launch_bounds__(1024) void down_decode_kernel(
   const int item = blockIdx.y;
   if (item >= meta->n_items) return;
   const WorkItem it = items[item];
-  const int rg = blockIdx.x;
+  const int q = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int KC = I / kAtomK;
-  const uint8_t* dbase = it.w + gateup_bytes + (size_t)rg * KC * kAtomBytes;
-  __shared__ f32x4 red[kMaxWaves][64];
+  const uint8_t* abase = it.w + gateup_bytes + (size_t)(2 * q) * KC * kAtomBytes;
+  const uint8_t* bbase = abase + (size_t)KC * kAtomBytes;
+  extern __shared__ f32x4 red[];  // [waves][2][64], sized by the launch
   const uint32_t lo_bytes = (uint32_t)(lo_plane * 2);
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(h, 2 * lo_bytes);
 
   // Unconditional weight loads, as in the gate/up kernel.
-  u32x4 wd[CPW];
-  uint32_t sd[CPW];
+  u32x4 wa[CPW], wb[CPW];
+  uint32_t sa[CPW], sb[CPW];
 #pragma unroll
   for (int cc = 0; cc < CPW; cc++) {
     const int c = w * CPW + cc;
-    const uint8_t* da = dbase + (size_t)(c < KC ? c : 0) * kAtomBytes;
-    wd[cc] = load_atom_data(da, lane);
-    sd[cc] = load_scale(da, lane);
+    const size_t o = (size_t)(c < KC ? c : 0) * kAtomBytes;
+    wa[cc] = load_atom_data(abase + o, lane);
+    wb[cc] = load_atom_data(bbase + o, lane);
+    sa[cc] = load_scale(abase + o, lane);
+    sb[cc] = load_scale(bbase + o, lane);
   }
 
   // One M tile of 16 tokens (first tile peeled, as in the gate/up kernel).
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(1024) void down_decode_kernel(
         alo[0][j] = bload8(rh, o == kOutOfRange ? o : o + lo_bytes + 16u * j);
       }
     }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cc = 0; cc < CPW; cc++) {
       const int c = w * CPW + cc;
@@ -243,24 +247,28 @@ __global__ __launch_bounds__(1024) void down_decode_kernel(
       }
       if (cc == 0) {
 #pragma unroll
-        for (int q = 0; q < CPW; q++) asm volatile("" : "+v"(wd[q]), "+v"(sd[q]));
+        for (int r = 0; r < CPW; r++) asm volatile("" : "+v"(wa[r]), "+v"(wb[r]), "+v"(sa[r]), "+v"(sb[r]));
       }
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        const bf16x8 b = dequant8(wd[cc][j], sd[cc]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[cc & 1][j], b, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[cc & 1][j], b, acc, 0, 0, 0);
+        const bf16x8 b0 = dequant8(wa[cc][j], sa[cc]);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[cc & 1][j], b0, acc0, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[cc & 1][j], b0, acc0, 0, 0, 0);
+        const bf16x8 b1 = dequant8(wb[cc][j], sb[cc]);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[cc & 1][j], b1, acc1, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[cc & 1][j], b1, acc1, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    red[w][lane] = acc;
+    red[(2 * w) * 64 + lane] = acc0;
+    red[(2 * w + 1) * 64 + lane] = acc1;
     __syncthreads();
-    for (int v0 = threadIdx.x; v0 < 256; v0 += blockDim.x) {  // 64 lanes x 4 values
-      const int L = v0 >> 2, i = v0 & 3;
+    for (int v0 = threadIdx.x; v0 < 512; v0 += blockDim.x) {  // 2 groups x 64 lanes x 4 values
+      const int g = v0 >> 8, L = (v0 >> 2) & 63, i = v0 & 3;
       float s = 0.f;
-      for (int v = 0; v < nw; v++) s += red[v][L][i];
+      for (int v = 0; v < nw; v++) s += red[(2 * v + g) * 64 + L][i];
       const int mm = m0 + 4 * (L >> 4) + i;
-      if (mm < it.cnt) yperm[(size_t)(it.pos0 + mm) * H + rg * 16 + (L & 15)] = s;
+      if (mm < it.cnt) yperm[(size_t)(it.pos0 + mm) * H + (2 * q + g) * 16 + (L & 15)] = s;
     }
     __syncthreads();
   };
@@ -310,7 +318,7 @@ hipError_t launch_expert_gateup(const Ctx* c, const uint16_t* x, int T, hipStrea
   const Split s = split_k(c->cfg.hidden / kAtomK, grid.x * grid.y, 4);
   const size_t lo = (size_t)c->rows_max * c->cfg.inter;
 #define GATEUP(N)                                                                       \
-  gateup_decode_kernel<N><<<grid, s.waves * 64, 0, st>>>(                             \
+  gateup_decode_kernel<N><<<grid, s.waves * 64, s.waves * 2 * 64 * 16, st>>>(        \
       c->d_items, c->d_meta, c->d_tok, x, (uint32_t)T * c->cfg.hidden * 2, c->cfg.hidden, \
       c->cfg.inter, c->d_h, lo)
   switch (s.cpw) {
@@ -324,17 +332,19 @@ hipError_t launch_expert_gateup(const Ctx* c, const uint16_t* x, int T, hipStrea
 }
 
 hipError_t launch_expert_down(const Ctx* c, int T, hipStream_t st) {
-  dim3 grid(c->cfg.hidden / kAtomRows, items_for(c, T));
-  const Split s = split_k(c->cfg.inter / kAtomK, grid.x * grid.y, 2);
+  dim3 grid(c->cfg.hidden / (2 * kAtomRows), items_for(c, T));
+  const Split s = split_k(c->cfg.inter / kAtomK, grid.x * grid.y, 4);
   const size_t lo = (size_t)c->rows_max * c->cfg.inter;
   const size_t gub = gateup_section_bytes(c->cfg.hidden, c->cfg.inter);
 #define DOWN(N)                                                                       \
-  down_decode_kernel<N><<<grid, s.waves * 64, 0, st>>>(                             \
+  down_decode_kernel<N><<<grid, s.waves * 64, s.waves * 2 * 64 * 16, st>>>(        \
       c->d_items, c->d_meta, c->d_h, lo, c->cfg.hidden, c->cfg.inter, gub,           \
       c->d_yperm)
   switch (s.cpw) {
     case 1: DOWN(1); break;
-    default: DOWN(2); break;
+    case 2: DOWN(2); break;
+    case 3: DOWN(3); break;
+    default: DOWN(4); break;
   }
 #undef DOWN
   return hipGetLastError();

@@ -74,6 +74,11 @@ def _load() -> ctypes.CDLL:
         raise ImportError(
             f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`"
             " (there is no fallback implementation)")
+    # torch first: its bundled HIP runtime then satisfies libmoe's dependency
+    # on libamdhip64, so the process holds one HIP runtime whichever module
+    # the caller imports first (two runtimes of one soname leave torch
+    # without devices).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in _SIGS.items():
         fn = getattr(lib, name)

@@ -40,14 +40,10 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 constexpr int kChunkTokens = 64;   // tokens per dispatch chunk (one wave)
 constexpr int kBM = 128;           // tokens per GEMM tile
 constexpr int kFragsPerWave = 4;   // 16-row weight fragments per wave
-constexpr int kLdsRow = kAtomK * 2 + 16;  // bytes per staged A row (padded)
 constexpr uint32_t kOOB = 0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 __device__ __forceinline__ bf16x8 dequant8(uint32_t q, uint32_t sbyte) {
   const float s = __uint_as_float(sbyte << 23);
@@ -246,84 +242,147 @@ __device__ __forceinline__ void tile_of_block(int nbn, int* ti, int* nb) {
   *nb = j % nbn;
 }
 
-// One GEMM: C[tile rows][4 waves x 4 fragments x 16 columns] over K in
-// chunks of 128.  A rows (bf16, gathered through `arow`) are staged in LDS
-// with the next chunk prefetched in registers; each wave streams its 4
-// weight fragments (MXFP4 atoms, dequantised in registers) with the next
-// chunk prefetched.  `frag_row_group(f)` gives the atom row group of the
-// wave's fragment f.
+// Grouped GEMM tile: C[128 token rows][256 columns] over K in chunks of 128,
+// on 8 waves (two per SIMD): wave w owns rows 64(w/4).. and columns
+// 64(w%4).. as 4 x 4 fragments of the 16x16x32 bf16 MFMA.  Both operands go
+// straight from global memory into LDS with buffer-to-LDS loads, so nothing
+// but the accumulators lives across chunks:
+//  - A (bf16 token rows, gathered): block (mf, q) is 1 KB, lane l's 16 bytes
+//    at 16l holding row 16mf + l%16, chunk elements 32q + 8(l/16) .. +8, so
+//    each load instruction reads 64 contiguous bytes of 16 rows.  At K step
+//    j a lane needs the elements its weight fragment covers, 32(l/16) + 8j
+//    (MX block l/16, sub-block j): it reads block (mf, l/16) at
+//    256j + 16(l%16), 256 contiguous bytes per 16 lanes;
+//  - B (the tile's 16 MXFP4 weight atoms of the chunk, 4 per column
+//    quarter): the 1 KB of codes of atom t at block t (lane order, as
+//    stored), then its 64 scale bytes, one per 4-byte LDS slot (a byte-sized
+//    buffer-to-LDS load still writes one dword slot per lane); dequantised in
+//    registers after the read.
+// Each wave issues kVmemPerChunk loads per chunk (A fragment block w, atoms
+// 2w and 2w+1).  kStages chunks are in flight: past the last chunk a wave
+// re-issues the last one into a stage no one reads any more, so "this
+// wave's loads of chunk c landed" is always vmcnt <= (kStages - 2) chunks'
+// worth; then one barrier makes every wave's loads visible and frees the
+// stage read at chunk c-1, chunk c + kStages - 1 is issued and chunk c is
+// computed.  The barrier is a bare s_barrier with a compiler memory clobber:
+// a workgroup fence there would make the compiler drain every buffer-to-LDS
+// load in flight, including the prefetched ones.
+constexpr int kGemmWaves = 8;
+constexpr int kStages = 3;
+constexpr int kAtomsPerTile = 16;                               // 256 columns
+constexpr int kLdsA = kBM * kAtomK * 2;                         // 32 KB
+constexpr int kLdsB = kAtomsPerTile * kAtomData;                // 16 KB
+constexpr int kLdsS = kAtomsPerTile * 64 * 4;                   // 4 KB
+constexpr int kStageBytes = kLdsA + kLdsB + kLdsS;              // 52 KB
+constexpr int kVmemPerChunk = 8;  // per wave: 4 A, 2 code and 2 scale loads
+
+typedef __attribute__((address_space(3))) void lds_void;
+
 struct GemmTile {
-  const uint8_t* wbase;  // expert record (section start)
+  const uint8_t* wbase;  // expert section start (gate/up or down)
+  uint32_t wbytes;       // section bytes
   int KC;                // K chunks
-  int rg[kFragsPerWave]; // atom row group per fragment (this wave)
   int rows;              // valid rows in this tile (<= kBM)
+  int rg[2];             // atom row groups of this wave's atoms 2w, 2w+1
+  uint32_t aoff;         // this lane's A row offset for row block w (+16(l/16)), or kOOB
 };
 
-__device__ __forceinline__ void gemm_tile(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
-                                          const uint32_t* arow_off, uint8_t* As,
-                                          f32x4 (&acc)[kBM / 16][kFragsPerWave]) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int mfrags = (gt.rows + 15) >> 4;
-  // A staging: 128 rows x 16 pieces of 16 bytes, 8 pieces per thread
-  u32x4 areg[8];
-  auto load_a = [&](int c) {
+struct Stages {
+  uint8_t* buf[kStages];
+};
+
+// Wait until at most N of this wave's vector-memory instructions are
+// outstanding, then barrier the workgroup.
+template <int N>
+__device__ __forceinline__ void wait_vmem_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+// MF: this wave's 16-row fragments that hold rows (0..4).
+template <int MF>
+__device__ __forceinline__ void gemm_tile_mf(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
+                                             const Stages& st,
+                                             f32x4 (&acc)[MF > 0 ? MF : 1][kFragsPerWave]) {
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int mh = w >> 2, nq = w & 3;
+  const int KC = gt.KC;
+  const __amdgpu_buffer_rsrc_t rw = rsrc(gt.wbase, gt.wbytes);
+  const uint32_t woff0 = (uint32_t)gt.rg[0] * KC * kAtomBytes;
+  const uint32_t woff1 = (uint32_t)gt.rg[1] * KC * kAtomBytes;
+  // Issue chunk min(c, KC - 1) into stage r.
+  auto issue = [&](int c, int r) {
+    c = c < KC ? c : KC - 1;
+    uint8_t* buf = st.buf[r];
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const int q = (tid + 256 * i) & 15;
-      const uint32_t o = arow_off[i];
-      areg[i] = bload16(ra, o == kOOB ? kOOB : o + (uint32_t)(c * kAtomK + 8 * q) * 2u);
+    for (int j = 0; j < 4; j++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(buf + (w * 4 + j) * 1024), 16,
+                                               gt.aoff + (uint32_t)c * (kAtomK * 2) + 64u * j, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      const uint32_t o = (t ? woff1 : woff0) + (uint32_t)c * kAtomBytes;
+      const int atom = 2 * w + t;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(buf + kLdsA + atom * kAtomData), 16,
+                                               o + 16u * lane, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(buf + kLdsA + kLdsB + atom * 256), 1,
+                                               o + kAtomData + lane, 0, 0, 0);
     }
   };
-  auto store_a = [&]() {
+  // One chunk: the A fragments and dequantised weights of K step j+1 are
+  // fetched while the MFMAs of step j run.
+  auto compute = [&](int r) {
+    if constexpr (MF > 0) {
+      const uint8_t* buf = st.buf[r];
+      u32x4 wd[kFragsPerWave];
+      uint32_t sd[kFragsPerWave];
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const int p = tid + 256 * i, r = p >> 4, q = p & 15;
-      *reinterpret_cast<u32x4*>(As + r * kLdsRow + q * 16) = areg[i];
-    }
-  };
-  u32x4 wd[2][kFragsPerWave];
-  uint32_t sd[2][kFragsPerWave];
-  auto load_w = [&](int c, int buf) {
+      for (int f = 0; f < kFragsPerWave; f++) {
+        const int atom = nq * kFragsPerWave + f;
+        wd[f] = *reinterpret_cast<const u32x4*>(buf + kLdsA + atom * kAtomData + 16 * lane);
+        sd[f] = *reinterpret_cast<const uint32_t*>(buf + kLdsA + kLdsB + atom * 256 + 4 * lane) & 0xFFu;
+      }
+      bf16x8 a[2][MF], b[2][kFragsPerWave];
+      auto fetch = [&](int j, int q) {
 #pragma unroll
-    for (int f = 0; f < kFragsPerWave; f++) {
-      const uint8_t* atom = gt.wbase + ((size_t)gt.rg[f] * gt.KC + c) * kAtomBytes;
-      wd[buf][f] = *reinterpret_cast<const u32x4*>(atom + lane * 16);
-      sd[buf][f] = atom[kAtomData + lane];
-    }
-  };
-  load_a(0);
-  load_w(0, 0);
-  __syncthreads();  // the previous tile's readers of As are done
-  store_a();
-  __syncthreads();
-  for (int c = 0; c < gt.KC; c++) {
-    const int cur = c & 1;
-    if (c + 1 < gt.KC) {
-      load_a(c + 1);
-      load_w(c + 1, cur ^ 1);
-    }
+        for (int i = 0; i < MF; i++)
+          a[q][i] = *reinterpret_cast<const bf16x8*>(buf + ((4 * mh + i) * 4 + (lane >> 4)) * 1024 +
+                                                     256 * j + 16 * (lane & 15));
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      bf16x8 b[kFragsPerWave];
+        for (int f = 0; f < kFragsPerWave; f++) b[q][f] = dequant8(wd[f][j], sd[f]);
+      };
+      fetch(0, 0);
 #pragma unroll
-      for (int f = 0; f < kFragsPerWave; f++) b[f] = dequant8(wd[cur][f][j], sd[cur][f]);
+      for (int j = 0; j < 4; j++) {
+        if (j + 1 < 4) fetch(j + 1, (j + 1) & 1);
 #pragma unroll
-      for (int mf = 0; mf < kBM / 16; mf++) {
-        if (mf < mfrags) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              As + (mf * 16 + (lane & 15)) * kLdsRow + 64 * (lane >> 4) + 16 * j);
+        for (int i = 0; i < MF; i++)
 #pragma unroll
           for (int f = 0; f < kFragsPerWave; f++)
-            acc[mf][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[f], acc[mf][f], 0, 0, 0);
-        }
+            acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j & 1][i], b[j & 1][f], acc[i][f], 0, 0, 0);
       }
     }
-    if (c + 1 < gt.KC) {
-      __syncthreads();
-      store_a();
-      __syncthreads();
+  };
+#pragma unroll
+  for (int s = 0; s < kStages - 1; s++) {
+    issue(s, s);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int c0 = 0; c0 < KC; c0 += kStages) {
+#pragma unroll
+    for (int u = 0; u < kStages; u++) {
+      if (c0 + u >= KC) break;
+      wait_vmem_barrier<kVmemPerChunk * (kStages - 2)>();
+      issue(c0 + u + kStages - 1, (u + kStages - 1) % kStages);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(u);
     }
   }
+  // No buffer-to-LDS write may land after the workgroup has ended.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 struct GroupArgs {
@@ -338,101 +397,148 @@ struct GroupArgs {
   int E;
 };
 
-// Gate/up + SwiGLU.  N-block nb covers 8 row pairs (gate, up): wave w takes
-// pairs nb*8 + 2w and +1 (fragments g0, u0, g1, u1).
-__global__ __launch_bounds__(256) void gateup_prefill_kernel(GroupArgs g, const uint16_t* x,
-                                                             uint32_t x_bytes, int H, int I,
-                                                             int nbn, uint16_t* __restrict__ h) {
-  int ti, nb;
-  tile_of_block(nbn, &ti, &nb);
-  if (ti >= *g.n_tiles) return;
-  __shared__ __attribute__((aligned(16))) uint8_t As[kBM * kLdsRow];
-  const int2 td = g.tiles[ti];
-  const int grp = td.x, m0 = td.y;
-  const int cnt = g.counts[grp], pos0 = g.offsets[grp];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  GemmTile gt;
-  gt.wbase = grp < g.E ? g.layerbuf + (size_t)grp * g.stride : g.shared_w;
-  gt.KC = H / kAtomK;
-  gt.rows = min(kBM, cnt - m0);
-  const int p0 = nb * 8 + 2 * w;
-  gt.rg[0] = 2 * p0;
-  gt.rg[1] = 2 * p0 + 1;
-  gt.rg[2] = 2 * p0 + 2;
-  gt.rg[3] = 2 * p0 + 3;
-  uint32_t arow[8];
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int r = (tid + 256 * i) >> 4;
-    arow[i] = r < gt.rows ? (uint32_t)g.tok[pos0 + m0 + r] * (uint32_t)H * 2u : kOOB;
+// This wave's fragment count: rows of the tile in its 64-row half, in 16s.
+#define MOE_MF_SWITCH(mf, CALL)  \
+  switch (mf) {                  \
+    case 0: CALL(0); break;      \
+    case 1: CALL(1); break;      \
+    case 2: CALL(2); break;      \
+    case 3: CALL(3); break;      \
+    default: CALL(4); break;     \
   }
-  f32x4 acc[kBM / 16][kFragsPerWave];
+
+__device__ __forceinline__ int wave_mfrags(int rows) {
+  const int mh = wave_id() >> 2;
+  return max(0, min(4, ((rows + 15) >> 4) - 4 * mh));
+}
+
+template <int MF>
+__device__ __forceinline__ void gateup_tile(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
+                                            const Stages& st, uint16_t* __restrict__ h, int I,
+                                            size_t row0, int p0) {
+  const int lane = threadIdx.x & 63, mh = wave_id() >> 2;
+  f32x4 acc[MF > 0 ? MF : 1][kFragsPerWave];
 #pragma unroll
-  for (int i = 0; i < kBM / 16; i++)
+  for (int i = 0; i < (MF > 0 ? MF : 1); i++)
 #pragma unroll
     for (int f = 0; f < kFragsPerWave; f++) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gemm_tile(gt, rsrc(x, x_bytes), arow, As, acc);
+  gemm_tile_mf<MF>(gt, ra, st, acc);
 #pragma unroll
-  for (int mf = 0; mf < kBM / 16; mf++) {
+  for (int i = 0; i < MF; i++) {
 #pragma unroll
     for (int q = 0; q < 2; q++) {
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int m = mf * 16 + 4 * (lane >> 4) + i;
+      for (int r = 0; r < 4; r++) {
+        const int m = 64 * mh + i * 16 + 4 * (lane >> 4) + r;
         if (m < gt.rows) {
-          const float hv = silu(acc[mf][2 * q][i]) * acc[mf][2 * q + 1][i];
-          h[(size_t)(pos0 + m0 + m) * I + (p0 + q) * 16 + (lane & 15)] = f32_to_bf16_rne(hv);
+          const float hv = silu(acc[i][2 * q][r]) * acc[i][2 * q + 1][r];
+          h[(row0 + m) * I + (p0 + q) * 16 + (lane & 15)] = f32_to_bf16_rne(hv);
         }
       }
     }
   }
 }
 
-// Down.  N-block nb covers 16 row groups of H (256 columns): wave w takes
-// row groups nb*16 + 4w .. +3.
-__global__ __launch_bounds__(256) void down_prefill_kernel(GroupArgs g, const uint16_t* h,
-                                                           uint32_t h_bytes, int H, int I, int nbn,
-                                                           size_t gateup_bytes,
-                                                           float* __restrict__ yperm) {
-  int ti, nb;
-  tile_of_block(nbn, &ti, &nb);
-  if (ti >= *g.n_tiles) return;
-  __shared__ __attribute__((aligned(16))) uint8_t As[kBM * kLdsRow];
-  const int2 td = g.tiles[ti];
-  const int grp = td.x, m0 = td.y;
-  const int cnt = g.counts[grp], pos0 = g.offsets[grp];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  GemmTile gt;
-  gt.wbase = (grp < g.E ? g.layerbuf + (size_t)grp * g.stride : g.shared_w) + gateup_bytes;
-  gt.KC = I / kAtomK;
-  gt.rows = min(kBM, cnt - m0);
-  const int rg0 = nb * 16 + 4 * w;
-  const int ngroups = H / kAtomRows;  // a multiple of 8; the last n-block may be partial
+template <int MF>
+__device__ __forceinline__ void down_tile(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
+                                          const Stages& st, float* __restrict__ yperm, int H,
+                                          size_t row0, int rg0, int ngroups) {
+  const int lane = threadIdx.x & 63, mh = wave_id() >> 2;
+  f32x4 acc[MF > 0 ? MF : 1][kFragsPerWave];
 #pragma unroll
-  for (int f = 0; f < kFragsPerWave; f++) gt.rg[f] = rg0 + f < ngroups ? rg0 + f : 0;
-  uint32_t arow[8];
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int r = (tid + 256 * i) >> 4;
-    arow[i] = r < gt.rows ? (uint32_t)(pos0 + m0 + r) * (uint32_t)I * 2u : kOOB;
-  }
-  f32x4 acc[kBM / 16][kFragsPerWave];
-#pragma unroll
-  for (int i = 0; i < kBM / 16; i++)
+  for (int i = 0; i < (MF > 0 ? MF : 1); i++)
 #pragma unroll
     for (int f = 0; f < kFragsPerWave; f++) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gemm_tile(gt, rsrc(h, h_bytes), arow, As, acc);
+  gemm_tile_mf<MF>(gt, ra, st, acc);
 #pragma unroll
-  for (int mf = 0; mf < kBM / 16; mf++)
+  for (int i = 0; i < MF; i++)
 #pragma unroll
     for (int f = 0; f < kFragsPerWave; f++)
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int m = mf * 16 + 4 * (lane >> 4) + i;
+      for (int r = 0; r < 4; r++) {
+        const int m = 64 * mh + i * 16 + 4 * (lane >> 4) + r;
         if (m < gt.rows && rg0 + f < ngroups)
-          yperm[(size_t)(pos0 + m0 + m) * H + (rg0 + f) * 16 + (lane & 15)] = acc[mf][f][i];
+          yperm[(row0 + m) * H + (rg0 + f) * 16 + (lane & 15)] = acc[i][f][r];
       }
 }
+
+// Gate/up + SwiGLU.  N-block nb covers row pairs nb*8 .. nb*8+7 (gate, up);
+// column quarter nq takes pairs nb*8 + 2nq and +1 (atoms g0, u0, g1, u1).
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void gateup_prefill_kernel(
+    GroupArgs g, const uint16_t* x, uint32_t x_bytes, int H, int I, int nbn,
+    uint16_t* __restrict__ h) {
+  int ti, nb;
+  tile_of_block(nbn, &ti, &nb);
+  if (ti >= *g.n_tiles) return;
+  __shared__ __attribute__((aligned(1024))) uint8_t S0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t S1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t S2[kStageBytes];
+  static_assert(kStages == 3, "one LDS array per stage");
+  const Stages st{{S0, S1, S2}};
+  const int2 td = g.tiles[ti];
+  const int grp = td.x, m0 = td.y;
+  const int cnt = g.counts[grp], pos0 = g.offsets[grp];
+  const int lane = threadIdx.x & 63, w = wave_id(), nq = w & 3;
+  GemmTile gt;
+  gt.wbase = grp < g.E ? g.layerbuf + (size_t)grp * g.stride : g.shared_w;
+  gt.KC = H / kAtomK;
+  gt.wbytes = (uint32_t)(2 * I / kAtomRows) * (uint32_t)gt.KC * kAtomBytes;
+  gt.rows = min(kBM, cnt - m0);
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+    const int atom = 2 * w + t;  // column quarter atom >> 2, fragment atom & 3
+    gt.rg[t] = 2 * (nb * 8 + 2 * (atom >> 2)) + (atom & 3);
+  }
+  const int r = w * 16 + (lane & 15);
+  gt.aoff = r < gt.rows ? (uint32_t)g.tok[pos0 + m0 + r] * (uint32_t)H * 2u + 16u * (lane >> 4) : kOOB;
+  const __amdgpu_buffer_rsrc_t ra = rsrc(x, x_bytes);
+  const size_t row0 = (size_t)(pos0 + m0);
+  const int p0 = nb * 8 + 2 * nq;
+#define GU(N) gateup_tile<N>(gt, ra, st, h, I, row0, p0)
+  MOE_MF_SWITCH(wave_mfrags(gt.rows), GU)
+#undef GU
+}
+
+// Down.  N-block nb covers row groups nb*16 .. nb*16+15 of H (256 columns);
+// column quarter nq takes row groups nb*16 + 4nq .. +3.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void down_prefill_kernel(
+    GroupArgs g, const uint16_t* h, uint32_t h_bytes, int H, int I, int nbn, size_t gateup_bytes,
+    float* __restrict__ yperm) {
+  int ti, nb;
+  tile_of_block(nbn, &ti, &nb);
+  if (ti >= *g.n_tiles) return;
+  __shared__ __attribute__((aligned(1024))) uint8_t S0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t S1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t S2[kStageBytes];
+  static_assert(kStages == 3, "one LDS array per stage");
+  const Stages st{{S0, S1, S2}};
+  const int2 td = g.tiles[ti];
+  const int grp = td.x, m0 = td.y;
+  const int cnt = g.counts[grp], pos0 = g.offsets[grp];
+  const int lane = threadIdx.x & 63, w = wave_id(), nq = w & 3;
+  const int ngroups = H / kAtomRows;  // a multiple of 8; the last n-block may be partial
+  GemmTile gt;
+  gt.wbase = (grp < g.E ? g.layerbuf + (size_t)grp * g.stride : g.shared_w) + gateup_bytes;
+  gt.KC = I / kAtomK;
+  gt.wbytes = (uint32_t)ngroups * (uint32_t)gt.KC * kAtomBytes;
+  gt.rows = min(kBM, cnt - m0);
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+    const int atom = 2 * w + t;
+    const int rg = nb * 16 + atom;  // = nb*16 + 4*(atom>>2) + (atom&3)
+    gt.rg[t] = rg < ngroups ? rg : 0;
+  }
+  const int r = w * 16 + (lane & 15);
+  gt.aoff = r < gt.rows ? (uint32_t)(pos0 + m0 + r) * (uint32_t)I * 2u + 16u * (lane >> 4) : kOOB;
+  const __amdgpu_buffer_rsrc_t ra = rsrc(h, h_bytes);
+  const size_t row0 = (size_t)(pos0 + m0);
+  const int rg0 = nb * 16 + 4 * nq;
+#define DN(N) down_tile<N>(gt, ra, st, yperm, H, row0, rg0, ngroups)
+  MOE_MF_SWITCH(wave_mfrags(gt.rows), DN)
+#undef DN
+}
+
+#undef MOE_MF_SWITCH
 
 template <class T>
 hipError_t dalloc(T** p, size_t n) {
@@ -576,9 +682,9 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
       if (t0 && t1) (void)hipEventRecord(t0, st);
     }
     const int nbn_gu = I / (16 * 8), nbn_dn = (H + 255) / 256;
-    gateup_prefill_kernel<<<p->max_tiles * nbn_gu, 256, 0, st>>>(ga, x, (uint32_t)T * H * 2, H, I,
+    gateup_prefill_kernel<<<p->max_tiles * nbn_gu, 64 * kGemmWaves, 0, st>>>(ga, x, (uint32_t)T * H * 2, H, I,
                                                                 nbn_gu, p->h);
-    down_prefill_kernel<<<p->max_tiles * nbn_dn, 256, 0, st>>>(
+    down_prefill_kernel<<<p->max_tiles * nbn_dn, 64 * kGemmWaves, 0, st>>>(
         ga, p->h, (uint32_t)(rows * I * 2), H, I, nbn_dn, gateup_section_bytes(H, I), p->yperm);
     if (t0 && t1) {
       (void)hipEventRecord(t1, st);

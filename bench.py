@@ -1,16 +1,20 @@
 """Benchmark of the routed MoE expert-layer forward on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--T T]
-                [--prefill-steps P]
+                [--prefill-steps P] [--dsv4-decode-steps D] [--calibrate-copy-mb M]
 
 A step is one decode call per layer of the workload (router, top-k, dispatch,
 cache lookup, miss fills, expert FFN, combine) for a batch of T tokens, with
 all inputs already resident in HBM.  Default workload: the 35B-A3B-shaped
 decode layer (H=2048, E=256, top-8, I=512, MXFP4 experts, bf16 activations,
 64-slot LRU from a cold start, Zipf(1.1) routing with 60% step overlap), T=16.
-The line also carries the prefill leg: the DeepSeek-V4-Flash-shaped stack
-(4 layers, H=4096, I=2048, E=256, top-6 + shared, T=4096) with whole-layer
-uploads from the pinned pool, its grouped-GEMM time and MFMA utilisation.
+The roofline object is the gate/up expert kernel's (the dominant HBM-bound
+kernel; the miss-fill kernel is bound by PCIe and reported as pcie_h2d_gbs),
+from per-kernel HIP events taken in a second pass queued behind a spin
+kernel.  The line also carries the DeepSeek-V4-Flash-shaped stack (4 layers,
+H=4096, I=2048, E=256, top-6 + shared): prefill of T=4096 with whole-layer
+uploads from the pinned pool (grouped-GEMM time and MFMA utilisation), and
+T=1 decode through its global LRU.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -42,20 +46,25 @@ def parse():
     ap.add_argument("--extra-T", default="1,4", help="also time these T (decode)")
     ap.add_argument("--prefill-steps", type=int, default=3,
                     help="prefill passes of the DeepSeek-V4-Flash-shaped stack (0: skip)")
+    ap.add_argument("--dsv4-decode-steps", type=int, default=256,
+                    help="T=1 decode steps of the DeepSeek-V4-Flash-shaped stack (0: skip)")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="also run one plain copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
-def ffn_bytes(sh, lookups, calls, pairs, T_total):
-    """Algorithmic bytes of the expert FFN kernels over `calls` calls:
-    every looked-up expert's MXFP4 weights once (plus the shared expert per
-    call), the token rows read, the h rows written and read (bf16), and the
-    expert output rows written (fp32)."""
-    from workload import gen  # noqa: F401
+def kernel_bytes(sh, lookups, calls, pairs, T_total):
+    """Algorithmic HBM bytes of the two decode expert kernels over `calls`
+    calls, as (gate/up, down).  Weights: every looked-up expert once, plus
+    the shared expert once per call; gate/up is 2/3 of an MXFP4 expert, down
+    1/3.  Activations: gate/up reads each token row once and writes h as two
+    bf16 planes; down reads those planes and writes fp32 expert outputs."""
     b_e = sh.expert_bytes()
+    experts = lookups + (calls if sh.shared else 0)
     rows = pairs + (T_total if sh.shared else 0)
-    weights = (lookups + (calls if sh.shared else 0)) * b_e
-    acts = T_total * sh.H * 2 + rows * sh.I * 2 * 2 + rows * sh.H * 4
-    return weights + acts
+    gateup = experts * (2 * b_e // 3) + T_total * sh.H * 2 + rows * sh.I * 2 * 2
+    down = experts * (b_e // 3) + rows * sh.I * 2 * 2 + rows * sh.H * 4
+    return gateup, down
 
 
 def make_engine(sh, T, cache_slots, staging_slots, prefill_tokens=0):
@@ -80,14 +89,10 @@ def bf16_dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda")
 
 
-def run_decode(wl, T, steps, warmup, seed=0):
+def decode_inputs(wl, T, n, seed=0):
     import torch
     from workload import gen
-
     sh = wl.shape
-    eng = make_engine(sh, T, wl.cache_slots, wl.staging_slots)
-    load_weights(eng, sh, seed)
-    n = min(wl.steps, steps + warmup)
     dev = torch.device("cuda")
     xs, bs = [], []
     for l in range(sh.layers):
@@ -95,7 +100,24 @@ def run_decode(wl, T, steps, warmup, seed=0):
         xs.append(torch.stack([bf16_dev(gen.tokens(sh, l, s, T, seed)) for s in range(n)]))
         bs.append(torch.from_numpy(np.stack([gen.bias_from_sets(sets[s], sh.E) for s in range(n)])).to(dev)
                   if sets is not None else None)
-    y = torch.empty((T, sh.H), dtype=torch.int16, device=dev)
+    return xs, bs
+
+
+def run_decode(wl, T, steps, warmup, seed=0, eng=None):
+    """Decode throughput (wall clock over `steps` steps, host submission
+    included), then a kernel-timing pass: the same number of steps queued
+    behind a spin kernel so that the per-kernel HIP events measure the
+    kernels back to back, not the host's submission gaps."""
+    import torch
+
+    sh = wl.shape
+    own = eng is None
+    if own:
+        eng = make_engine(sh, T, wl.cache_slots, wl.staging_slots)
+        load_weights(eng, sh, seed)
+    n = min(wl.steps, steps + warmup)
+    xs, bs = decode_inputs(wl, T, n, seed)
+    y = torch.empty((T, sh.H), dtype=torch.int16, device="cuda")
     resize = dict(wl.resize)
 
     def do_step(s):
@@ -108,71 +130,114 @@ def run_decode(wl, T, steps, warmup, seed=0):
         do_step(s)
     torch.cuda.synchronize()
     eng.reset_stats()
-    eng.set_timing(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(warmup, warmup + steps):
         do_step(s)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    tm = eng.get_timing()
     st = eng.stats()
-    eng.close()
     elapsed = t1 - t0
     calls = steps * sh.layers
     pairs = calls * T * sh.k
-    fb = ffn_bytes(sh, st["lookups"], calls, pairs, calls * T)
-    ms_ffn = tm["ms_decode"]
+    gb, db = kernel_bytes(sh, st["lookups"], calls, pairs, calls * T)
+    # kernel-timing pass over the same step range (the cache state differs:
+    # it continues from the first pass, so the byte count is recomputed)
+    eng.reset_stats()
+    eng.set_timing(True)
+    torch.cuda._sleep(int(2e8))  # ~0.1 s spin: the host queues the steps meanwhile
+    for s in range(warmup, warmup + steps):
+        do_step(s)
+    torch.cuda.synchronize()
+    tm = eng.get_timing()
+    eng.set_timing(False)
+    st2 = eng.stats()
+    gb2, db2 = kernel_bytes(sh, st2["lookups"], calls, pairs, calls * T)
+    if own:
+        eng.close()
+    nl = max(tm["n_decode"], 1)
     return dict(T=T, steps=steps, elapsed_s=elapsed, tokens_per_s=T * steps / elapsed,
                 ms_per_step=1e3 * elapsed / steps, stats=st,
                 hit_rate=st["hits"] / max(st["lookups"], 1),
-                ffn_launches=tm["n_decode"], ffn_ms_total=ms_ffn,
-                ffn_bytes_total=fb,
-                ffn_gbs=fb / (ms_ffn * 1e6) if ms_ffn > 0 else None,
+                launches=tm["n_decode"],
+                gateup_us=1e3 * tm["ms_decode_gateup"] / nl, down_us=1e3 * tm["ms_decode_down"] / nl,
+                gateup_bytes=gb2 / nl, down_bytes=db2 / nl,
+                gateup_gbs=gb2 / (tm["ms_decode_gateup"] * 1e6) if tm["ms_decode_gateup"] > 0 else None,
+                down_gbs=db2 / (tm["ms_decode_down"] * 1e6) if tm["ms_decode_down"] > 0 else None,
+                ffn_gbs=(gb2 + db2) / (tm["ms_decode"] * 1e6) if tm["ms_decode"] > 0 else None,
                 h2d_gbs=st["bytes_h2d"] / (elapsed * 1e9))
 
 
-def run_prefill(wl, steps, warmup, seed=0):
-    """Prefill of the whole layer stack per step (layer uploads included)."""
+def roofline_entry(name, gbs, us, nbytes, launches):
+    return {"kernel": name, "bound": "hbm",
+            "achieved": None if gbs is None else round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": None if gbs is None else round(gbs / HBM_PEAK_GBS, 4),
+            "launches": launches, "avg_launch_us": round(us, 3), "bytes_per_launch": round(nbytes)}
+
+
+def run_dsv4(prefill_steps, decode_steps, decode_warmup, seed=0):
+    """The DeepSeek-V4-Flash-shaped stack on one engine: prefill of all
+    layers per step (layer uploads included), then T=1 decode through the
+    global LRU (13.4 MB experts: HBM-bound, not cache-resident)."""
     import torch
     from workload import gen
-    sh = wl.shape
-    T = wl.Ts[0]
-    eng = make_engine(sh, 1, 0, sh.k, prefill_tokens=T)
+    wp, wd = gen.WORKLOADS["dsv4_prefill"], gen.WORKLOADS["dsv4_decode"]
+    sh = wp.shape
+    T = wp.Ts[0]
+    eng = make_engine(sh, max(wd.Ts), wd.cache_slots, wd.staging_slots, prefill_tokens=T)
     load_weights(eng, sh, seed)
-    xs = [bf16_dev(gen.tokens(sh, l, 0, T, seed)) for l in range(sh.layers)]
-    ys = [torch.empty((T, sh.H), dtype=torch.int16, device="cuda") for _ in range(sh.layers)]
-    for _ in range(warmup):
+    out = {}
+    if prefill_steps > 0:
+        xs = [bf16_dev(gen.tokens(sh, l, 0, T, seed)) for l in range(sh.layers)]
+        ys = [torch.empty((T, sh.H), dtype=torch.int16, device="cuda") for _ in range(sh.layers)]
         eng.prefill(xs, ys)
-    torch.cuda.synchronize()
-    eng.reset_stats()
-    eng.set_timing(True)
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        eng.prefill(xs, ys)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    tm = eng.get_timing()
-    eng.close()
-    el = t1 - t0
-    layers = steps * sh.layers
-    # algorithmic flops per layer: 3 matrices of H x I per (token, expert),
-    # k routed experts plus the shared one, 2 flops per multiply-add
-    flops_layer = 2 * 3 * sh.H * sh.I * T * (sh.k + (1 if sh.shared else 0))
-    gemm_ms = tm["ms_prefill"] / max(tm["n_prefill"], 1)
-    tflops = flops_layer / (gemm_ms * 1e9)
-    upload = sh.E * sh.expert_bytes() * layers
-    return {"workload": wl.name, "T": T, "layers": sh.layers, "steps": steps,
-            "tokens_per_s_end_to_end": round(T * steps / el, 1),
-            "ms_per_step": round(1e3 * el / steps, 2),
+        torch.cuda.synchronize()
+        eng.reset_stats()
+        eng.set_timing(True)
+        t0 = time.perf_counter()
+        for _ in range(prefill_steps):
+            eng.prefill(xs, ys)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        tm = eng.get_timing()
+        eng.set_timing(False)
+        el = t1 - t0
+        layers = prefill_steps * sh.layers
+        # algorithmic flops per layer: 3 matrices of H x I per (token, expert),
+        # k routed experts plus the shared one, 2 flops per multiply-add
+        flops_layer = 2 * 3 * sh.H * sh.I * T * (sh.k + (1 if sh.shared else 0))
+        nl = max(tm["n_prefill"], 1)
+        gemm_ms = tm["ms_prefill"] / nl
+        gu_ms, dn_ms = tm["ms_prefill_gateup"] / nl, tm["ms_prefill_down"] / nl
+        tflops = flops_layer / (gemm_ms * 1e9)
+        upload = sh.E * sh.expert_bytes() * layers
+        out["prefill"] = {
+            "workload": wp.name, "T": T, "layers": sh.layers, "steps": prefill_steps,
+            "tokens_per_s_end_to_end": round(T * prefill_steps / el, 1),
+            "ms_per_step": round(1e3 * el / prefill_steps, 2),
             "gemm_ms_per_layer": round(gemm_ms, 4),
-            "gemm_launches": tm["n_prefill"],
+            "gemm_launches": 2 * tm["n_prefill"],
             "tokens_per_s_gemm_only": round(T / (gemm_ms * 1e-3) / sh.layers, 1),
             "flops_per_layer": flops_layer,
             "mfma_tflops": round(tflops, 1),
             "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
             "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "gateup_prefill_kernel": {"avg_us": round(1e3 * gu_ms, 1),
+                                      "tflops": round(2 * flops_layer / 3 / (gu_ms * 1e9), 1)},
+            "down_prefill_kernel": {"avg_us": round(1e3 * dn_ms, 1),
+                                    "tflops": round(flops_layer / 3 / (dn_ms * 1e9), 1)},
             "pcie_h2d_gbs": round(upload / (el * 1e9), 2)}
+    if decode_steps > 0:
+        r = run_decode(wd, 1, decode_steps, decode_warmup, seed, eng=eng)
+        out["dsv4_decode_T1"] = {
+            "tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 4),
+            "hit_rate": round(r["hit_rate"], 4), "h2d_gbs": round(r["h2d_gbs"], 2),
+            "roofline": [roofline_entry("gateup_decode_kernel", r["gateup_gbs"], r["gateup_us"],
+                                        r["gateup_bytes"], r["launches"]),
+                         roofline_entry("down_decode_kernel", r["down_gbs"], r["down_us"],
+                                        r["down_bytes"], r["launches"])]}
+    eng.close()
+    return out
 
 
 def cpu_baseline(wl, T, seconds):
@@ -207,6 +272,42 @@ def cpu_baseline(wl, T, seconds):
                       f"fp64 expert loops) in {el:.1f}s"}
 
 
+def traffic_from_profile(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/traffic_<kernel>_<workload>.md), if it was taken on the current
+    source of the kernel's file; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].strip().split(": ", 1)
+            fields[k.strip("`")] = v.strip().strip("`")
+    src = os.path.join(ROOT, fields.get("source", ""))
+    if not os.path.isfile(src):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != fields.get("source_sha256"):
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(mb):
+    """One plain device-to-device copy of `mb` MiB through the library's copy
+    kernel, for scaling traffic counters to bytes."""
+    import torch
+    from expert_offload_serving_amd import binding
+    n = mb << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    binding.moe_probe_copy(src.data_ptr(), dst.data_ptr(), n)
+    torch.cuda.synchronize()
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -223,10 +324,19 @@ def main():
     for t in [int(v) for v in a.extra_T.split(",") if v.strip()]:
         if t != T and t in wl.Ts:
             r = run_decode(wl, t, a.steps, a.warmup)
-            extra[f"T={t}"] = {k: r[k] for k in ("tokens_per_s", "ms_per_step", "hit_rate", "ffn_gbs",
-                                                 "h2d_gbs")}
+            extra[f"T={t}"] = {"tokens_per_s": round(r["tokens_per_s"], 1),
+                               "ms_per_step": round(r["ms_per_step"], 4),
+                               "hit_rate": round(r["hit_rate"], 4),
+                               "gateup_gbs": r["gateup_gbs"] and round(r["gateup_gbs"], 1),
+                               "down_gbs": r["down_gbs"] and round(r["down_gbs"], 1),
+                               "h2d_gbs": round(r["h2d_gbs"], 2)}
     sh = wl.shape
-    achieved = res["ffn_gbs"]
+    roof = roofline_entry("gateup_decode_kernel", res["gateup_gbs"], res["gateup_us"],
+                          res["gateup_bytes"], res["launches"])
+    roof["traffic"] = traffic_from_profile("gateup_decode_kernel", f"{wl.name}_T{T}")
+    roof["other_kernels"] = [roofline_entry("down_decode_kernel", res["down_gbs"], res["down_us"],
+                                            res["down_bytes"], res["launches"])]
+    roof["expert_ffn_pair_gbs"] = res["ffn_gbs"] and round(res["ffn_gbs"], 1)
     line = {
         "metric": "MoE-layer decode tokens/s",
         "value": round(res["tokens_per_s"], 2),
@@ -245,25 +355,16 @@ def main():
                    "cache_slots": wl.cache_slots, "staging_slots": wl.staging_slots,
                    "weights": "MXFP4 (E2M1 + E8M0/32)", "zipf_s": wl.zipf_s,
                    "overlap": wl.overlap},
-        "roofline": {
-            "kernel": "expert FFN (gate/up+SwiGLU and down kernels)",
-            "bound": "hbm",
-            "achieved": None if achieved is None else round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": None if achieved is None else round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "launches": res["ffn_launches"],
-            "avg_launch_us": round(1e3 * res["ffn_ms_total"] / max(res["ffn_launches"], 1), 3),
-            "bytes_per_launch": round(res["ffn_bytes_total"] / max(res["ffn_launches"], 1)),
-        },
+        "roofline": roof,
         "cache": {"hit_rate": round(res["hit_rate"], 4), **{k: res["stats"][k] for k in
                   ("lookups", "hits", "fills", "bypasses", "evictions")}},
         "pcie_h2d_gbs": round(res["h2d_gbs"], 2),
         "other_T": extra,
     }
-    if a.prefill_steps > 0:
-        line["prefill"] = run_prefill(gen.WORKLOADS["dsv4_prefill"], a.prefill_steps, 1)
+    if a.prefill_steps > 0 or a.dsv4_decode_steps > 0:
+        line.update(run_dsv4(a.prefill_steps, a.dsv4_decode_steps, max(a.dsv4_decode_steps // 4, 1)))
+    if a.calibrate_copy_mb > 0:
+        calibrate_copy(a.calibrate_copy_mb)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, T, a.cpu_seconds)
     print(json.dumps(line), flush=True)

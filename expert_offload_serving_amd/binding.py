@@ -65,6 +65,7 @@ _SIGS = {
     "moe_reset_stats": (_I32, [_P]),
     "moe_set_timing": (_I32, [_P, _I32]),
     "moe_get_timing": (_I32, [_P, _P, _P, _P, _P]),
+    "moe_get_timing_split": (_I32, [_P, _P, _P]),
     "moe_probe_copy": (_I32, [_P, _P, ctypes.c_size_t, _P]),
 }
 
@@ -238,6 +239,14 @@ def moe_get_timing(ctx):
     _check(lib.moe_get_timing(ctx, ctypes.byref(nd), ctypes.byref(md), ctypes.byref(np_),
                               ctypes.byref(mp)), "moe_get_timing")
     return dict(n_decode=nd.value, ms_decode=md.value, n_prefill=np_.value, ms_prefill=mp.value)
+
+
+def moe_get_timing_split(ctx):
+    n = (ctypes.c_int32 * 2)()
+    ms = (ctypes.c_double * 6)()
+    _check(lib.moe_get_timing_split(ctx, n, ms), "moe_get_timing_split")
+    return dict(n_decode=n[0], ms_decode=ms[0], ms_decode_gateup=ms[1], ms_decode_down=ms[2],
+                n_prefill=n[1], ms_prefill=ms[3], ms_prefill_gateup=ms[4], ms_prefill_down=ms[5])
 
 
 def moe_probe_copy(d_src, d_dst, n_bytes: int, stream=None):

@@ -117,7 +117,9 @@ namespace moe {
 hipEvent_t timing_event(Ctx* c) {
   if (c->ev_next == c->ev_pool.size()) {
     hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    // Timing only: no system-scope fences (they flush caches and add
+    // microseconds between the event and the kernel it brackets).
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     c->ev_pool.push_back(e);
   }
   return c->ev_pool[c->ev_next++];
@@ -360,17 +362,20 @@ moe_status moe_layer_forward(moe_ctx* ctx, int32_t layer, const void* d_x, int32
                        st));
   HIPCHK(launch_route_finalize(c, layer, T, d_ids, d_gates, st));
   HIPCHK(launch_fill(c->d_fills, c->d_meta, c->max_unique, c->rec_bytes, st));
-  hipEvent_t e0 = nullptr, e1 = nullptr;
+  Ctx::TimingRec tr{nullptr, nullptr, nullptr};
   if (c->timing && c->t_decode.size() < kMaxTimingPairs) {
-    e0 = timing_event(c);
-    e1 = timing_event(c);
-    if (e0 && e1) HIPCHK(hipEventRecord(e0, st));
+    tr = {timing_event(c), timing_event(c), timing_event(c)};
+    if (tr.before_gateup && tr.before_down && tr.after_down)
+      HIPCHK(hipEventRecord(tr.before_gateup, st));
+    else
+      tr = {nullptr, nullptr, nullptr};
   }
   HIPCHK(launch_expert_gateup(c, (const uint16_t*)d_x, T, st));
+  if (tr.before_down) HIPCHK(hipEventRecord(tr.before_down, st));
   HIPCHK(launch_expert_down(c, T, st));
-  if (e0 && e1) {
-    HIPCHK(hipEventRecord(e1, st));
-    c->t_decode.emplace_back(e0, e1);
+  if (tr.after_down) {
+    HIPCHK(hipEventRecord(tr.after_down, st));
+    c->t_decode.push_back(tr);
   }
   HIPCHK(launch_combine(c, T, (uint16_t*)d_y, d_y32, st));
   c->host_stats.forward_calls++;
@@ -623,30 +628,50 @@ moe_status moe_set_timing(moe_ctx* ctx, int32_t enable) {
   return MOE_OK;
 }
 
-moe_status moe_get_timing(moe_ctx* ctx, int32_t* h_n_decode, double* h_ms_decode,
-                          int32_t* h_n_prefill, double* h_ms_prefill) {
-  if (moe_status s = check_ctx(ctx)) return s;
-  Ctx* c = C_(ctx);
+static hipError_t sum_timing(const std::vector<Ctx::TimingRec>& v, double* ms3) {
+  double s[3] = {0, 0, 0};
+  for (const auto& r : v) {
+    float a = 0, b = 0;
+    hipError_t e = hipEventElapsedTime(&a, r.before_gateup, r.before_down);
+    if (e == hipSuccess) e = hipEventElapsedTime(&b, r.before_down, r.after_down);
+    if (e != hipSuccess) return e;
+    s[0] += (double)a + b;
+    s[1] += a;
+    s[2] += b;
+  }
+  for (int i = 0; i < 3; i++) ms3[i] = s[i];
+  return hipSuccess;
+}
+
+static moe_status take_timing(Ctx* c, int32_t* n2, double* ms6) {
   HIPCHK(hipDeviceSynchronize());
-  auto total = [&](std::vector<std::pair<hipEvent_t, hipEvent_t>>& v, double* ms) -> hipError_t {
-    double sum = 0;
-    for (auto& p : v) {
-      float m = 0;
-      hipError_t e = hipEventElapsedTime(&m, p.first, p.second);
-      if (e != hipSuccess) return e;
-      sum += m;
-    }
-    if (ms) *ms = sum;
-    return hipSuccess;
-  };
-  if (h_n_decode) *h_n_decode = (int32_t)c->t_decode.size();
-  if (h_n_prefill) *h_n_prefill = (int32_t)c->t_prefill.size();
-  HIPCHK(total(c->t_decode, h_ms_decode));
-  HIPCHK(total(c->t_prefill, h_ms_prefill));
+  n2[0] = (int32_t)c->t_decode.size();
+  n2[1] = (int32_t)c->t_prefill.size();
+  HIPCHK(sum_timing(c->t_decode, ms6));
+  HIPCHK(sum_timing(c->t_prefill, ms6 + 3));
   c->t_decode.clear();
   c->t_prefill.clear();
   c->ev_next = 0;
   return MOE_OK;
+}
+
+moe_status moe_get_timing(moe_ctx* ctx, int32_t* h_n_decode, double* h_ms_decode,
+                          int32_t* h_n_prefill, double* h_ms_prefill) {
+  if (moe_status s = check_ctx(ctx)) return s;
+  int32_t n[2];
+  double ms[6];
+  if (moe_status s = take_timing(C_(ctx), n, ms)) return s;
+  if (h_n_decode) *h_n_decode = n[0];
+  if (h_n_prefill) *h_n_prefill = n[1];
+  if (h_ms_decode) *h_ms_decode = ms[0];
+  if (h_ms_prefill) *h_ms_prefill = ms[3];
+  return MOE_OK;
+}
+
+moe_status moe_get_timing_split(moe_ctx* ctx, int32_t* h_n, double* h_ms) {
+  if (moe_status s = check_ctx(ctx)) return s;
+  if (!h_n || !h_ms) return fail(MOE_ERR_INVALID_ARG, "NULL output array");
+  return take_timing(C_(ctx), h_n, h_ms);
 }
 
 moe_status moe_probe_copy(const void* d_src, void* d_dst, size_t n_bytes, void* stream) {

@@ -161,8 +161,11 @@ struct Ctx {
 
   // timing
   bool timing = false;
-  std::vector<hipEvent_t> ev_pool;  // pairs, reused
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> t_decode, t_prefill;
+  std::vector<hipEvent_t> ev_pool;  // reused
+  struct TimingRec {
+    hipEvent_t before_gateup, before_down, after_down;
+  };
+  std::vector<TimingRec> t_decode, t_prefill;
   size_t ev_next = 0;
 
   // host-side counters not tracked on the device

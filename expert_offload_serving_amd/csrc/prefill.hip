@@ -675,20 +675,23 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
 
     GroupArgs ga{p->tiles, p->n_tiles, p->counts, p->offsets, p->tok, c->d_layerbuf[b],
                  c->stride, f.has_shared ? c->d_shared + (size_t)l * c->stride : nullptr, E};
-    hipEvent_t t0 = nullptr, t1 = nullptr;
+    Ctx::TimingRec tr{nullptr, nullptr, nullptr};
     if (c->timing && c->t_prefill.size() < 65536) {
-      t0 = timing_event(c);
-      t1 = timing_event(c);
-      if (t0 && t1) (void)hipEventRecord(t0, st);
+      tr = {timing_event(c), timing_event(c), timing_event(c)};
+      if (tr.before_gateup && tr.before_down && tr.after_down)
+        (void)hipEventRecord(tr.before_gateup, st);
+      else
+        tr = {nullptr, nullptr, nullptr};
     }
     const int nbn_gu = I / (16 * 8), nbn_dn = (H + 255) / 256;
-    gateup_prefill_kernel<<<p->max_tiles * nbn_gu, 64 * kGemmWaves, 0, st>>>(ga, x, (uint32_t)T * H * 2, H, I,
-                                                                nbn_gu, p->h);
+    gateup_prefill_kernel<<<p->max_tiles * nbn_gu, 64 * kGemmWaves, 0, st>>>(
+        ga, x, (uint32_t)T * H * 2, H, I, nbn_gu, p->h);
+    if (tr.before_down) (void)hipEventRecord(tr.before_down, st);
     down_prefill_kernel<<<p->max_tiles * nbn_dn, 64 * kGemmWaves, 0, st>>>(
         ga, p->h, (uint32_t)(rows * I * 2), H, I, nbn_dn, gateup_section_bytes(H, I), p->yperm);
-    if (t0 && t1) {
-      (void)hipEventRecord(t1, st);
-      c->t_prefill.emplace_back(t0, t1);
+    if (tr.after_down) {
+      (void)hipEventRecord(tr.after_down, st);
+      c->t_prefill.push_back(tr);
     }
     if ((e = launch_combine_rows(p->yperm, p->inv, p->gates, T, k, H, f.has_shared,
                                  (uint16_t*)ys[l], y32s ? y32s[l] : nullptr, st)) != hipSuccess)

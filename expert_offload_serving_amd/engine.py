@@ -80,7 +80,9 @@ class MoEEngine:
         b.moe_set_timing(self.ctx, enable)
 
     def get_timing(self) -> dict:
-        return b.moe_get_timing(self.ctx)
+        """Summed event times (ms) since the last call, in total and per
+        expert kernel (gate/up, down), for decode calls and prefill layers."""
+        return b.moe_get_timing_split(self.ctx)
 
     def close(self):
         if self.ctx:

@@ -260,15 +260,26 @@ moe_status moe_get_stats(moe_ctx* ctx, moe_stats* out);
 moe_status moe_reset_stats(moe_ctx* ctx);
 
 /*
- * Kernel timing for measurement: when enabled, moe_layer_forward records a
- * HIP event pair on the caller's stream around its expert FFN kernels and
- * moe_prefill_forward around each layer's grouped GEMMs (up to 65536 pairs,
- * then recording stops).  moe_get_timing (sync) returns the number of pairs
- * and the summed milliseconds for each of the two paths, and clears them.
+ * Kernel timing for measurement: when enabled, moe_layer_forward records HIP
+ * events on the caller's stream around its expert FFN kernels and
+ * moe_prefill_forward around each layer's grouped GEMMs (up to 65536
+ * records, then recording stops).  moe_get_timing (sync) returns the number
+ * of records and the summed milliseconds for each of the two paths, and
+ * clears them.
  */
 moe_status moe_set_timing(moe_ctx* ctx, int32_t enable);
 moe_status moe_get_timing(moe_ctx* ctx, int32_t* h_n_decode, double* h_ms_decode,
                           int32_t* h_n_prefill, double* h_ms_prefill);
+
+/*
+ * (sync) As moe_get_timing, split per kernel: each record holds an event
+ * before the gate/up kernel, one between it and the down kernel and one
+ * after the down kernel.  h_n[2] = {decode records, prefill layer records};
+ * h_ms[6] = {decode total, decode gate/up, decode down, prefill total,
+ * prefill gate/up, prefill down}, summed milliseconds.  Clears the records.
+ * Errors: INVALID_ARG (NULL context or arrays), HIP.
+ */
+moe_status moe_get_timing_split(moe_ctx* ctx, int32_t* h_n, double* h_ms);
 
 /*
  * Bandwidth probe: copy n_bytes (multiple of 16) from d_src to d_dst with a

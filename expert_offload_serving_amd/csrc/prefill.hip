@@ -243,8 +243,10 @@ __device__ __forceinline__ void tile_of_block(int nbn, int* ti, int* nb) {
 }
 
 // Grouped GEMM tile: C[128 token rows][256 columns] over K in chunks of 128,
-// on 8 waves (two per SIMD): wave w owns rows 64(w/4).. and columns
-// 64(w%4).. as 4 x 4 fragments of the 16x16x32 bf16 MFMA.  Both operands go
+// on 8 waves (two per SIMD): wave w owns columns 64(w%4).. and the 16-row
+// fragments 2i + w/4 (i < 4) -- interleaved, so that the two waves sharing
+// a SIMD hold nearly equal row counts in a partly filled tile -- as 4 x 4
+// fragments of the 16x16x32 bf16 MFMA.  Both operands go
 // straight from global memory into LDS with buffer-to-LDS loads, so nothing
 // but the accumulators lives across chunks:
 //  - A (bf16 token rows, gathered): block (mf, q) is 1 KB, lane l's 16 bytes
@@ -291,6 +293,24 @@ struct Stages {
   uint8_t* buf[kStages];
 };
 
+// Buffer-to-LDS loads: `bytes` per lane from rsrc + voffset into LDS at
+// lds + lane * slot (16 bytes for the 16-byte form, a 4-byte slot for one
+// byte).  Written as asm so that the compiler, which cannot tell the stage
+// buffers apart, adds no waits of its own before the LDS reads: every wait
+// on these loads is the explicit one in wait_vmem_barrier.  No output
+// registers: the data goes to LDS.  The s_nop is the wait state an M0 write
+// needs before a load that reads M0 (the compiler emits M0 right before).
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, void* lds) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(r),
+               "{m0}"((uint32_t)(uintptr_t)(lds_void*)lds)
+               : "memory");
+}
+__device__ __forceinline__ void lds_load1(__amdgpu_buffer_rsrc_t r, uint32_t voffset, void* lds) {
+  asm volatile("s_nop 0\n\tbuffer_load_ubyte %0, %1, 0 offen lds" ::"v"(voffset), "s"(r),
+               "{m0}"((uint32_t)(uintptr_t)(lds_void*)lds)
+               : "memory");
+}
+
 // Wait until at most N of this wave's vector-memory instructions are
 // outstanding, then barrier the workgroup.
 template <int N>
@@ -320,16 +340,13 @@ __device__ __forceinline__ void gemm_tile_mf(const GemmTile& gt, __amdgpu_buffer
     uint8_t* buf = st.buf[r];
 #pragma unroll
     for (int j = 0; j < 4; j++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(buf + (w * 4 + j) * 1024), 16,
-                                               gt.aoff + (uint32_t)c * (kAtomK * 2) + 64u * j, 0, 0, 0);
+      lds_load16(ra, gt.aoff + (uint32_t)c * (kAtomK * 2) + 64u * j, buf + (w * 4 + j) * 1024);
 #pragma unroll
     for (int t = 0; t < 2; t++) {
       const uint32_t o = (t ? woff1 : woff0) + (uint32_t)c * kAtomBytes;
       const int atom = 2 * w + t;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(buf + kLdsA + atom * kAtomData), 16,
-                                               o + 16u * lane, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(buf + kLdsA + kLdsB + atom * 256), 1,
-                                               o + kAtomData + lane, 0, 0, 0);
+      lds_load16(rw, o + 16u * lane, buf + kLdsA + atom * kAtomData);
+      lds_load1(rw, o + kAtomData + lane, buf + kLdsA + kLdsB + atom * 256);
     }
   };
   // One chunk: the A fragments and dequantised weights of K step j+1 are
@@ -349,7 +366,7 @@ __device__ __forceinline__ void gemm_tile_mf(const GemmTile& gt, __amdgpu_buffer
       auto fetch = [&](int j, int q) {
 #pragma unroll
         for (int i = 0; i < MF; i++)
-          a[q][i] = *reinterpret_cast<const bf16x8*>(buf + ((4 * mh + i) * 4 + (lane >> 4)) * 1024 +
+          a[q][i] = *reinterpret_cast<const bf16x8*>(buf + ((2 * i + mh) * 4 + (lane >> 4)) * 1024 +
                                                      256 * j + 16 * (lane & 15));
 #pragma unroll
         for (int f = 0; f < kFragsPerWave; f++) b[q][f] = dequant8(wd[f][j], sd[f]);
@@ -397,7 +414,8 @@ struct GroupArgs {
   int E;
 };
 
-// This wave's fragment count: rows of the tile in its 64-row half, in 16s.
+// This wave's fragment count: of the tile's ceil(rows/16) fragments, those
+// with index parity w/4.
 #define MOE_MF_SWITCH(mf, CALL)  \
   switch (mf) {                  \
     case 0: CALL(0); break;      \
@@ -409,7 +427,7 @@ struct GroupArgs {
 
 __device__ __forceinline__ int wave_mfrags(int rows) {
   const int mh = wave_id() >> 2;
-  return max(0, min(4, ((rows + 15) >> 4) - 4 * mh));
+  return (((rows + 15) >> 4) - mh + 1) >> 1;
 }
 
 template <int MF>
@@ -429,7 +447,7 @@ __device__ __forceinline__ void gateup_tile(const GemmTile& gt, __amdgpu_buffer_
     for (int q = 0; q < 2; q++) {
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        const int m = 64 * mh + i * 16 + 4 * (lane >> 4) + r;
+        const int m = (2 * i + mh) * 16 + 4 * (lane >> 4) + r;
         if (m < gt.rows) {
           const float hv = silu(acc[i][2 * q][r]) * acc[i][2 * q + 1][r];
           h[(row0 + m) * I + (p0 + q) * 16 + (lane & 15)] = f32_to_bf16_rne(hv);
@@ -456,7 +474,7 @@ __device__ __forceinline__ void down_tile(const GemmTile& gt, __amdgpu_buffer_rs
     for (int f = 0; f < kFragsPerWave; f++)
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        const int m = 64 * mh + i * 16 + 4 * (lane >> 4) + r;
+        const int m = (2 * i + mh) * 16 + 4 * (lane >> 4) + r;
         if (m < gt.rows && rg0 + f < ngroups)
           yperm[(row0 + m) * H + (rg0 + f) * 16 + (lane & 15)] = acc[i][f][r];
       }

@@ -283,7 +283,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 struct GemmTile {
   const uint8_t* wbase;  // expert section start (gate/up or down)
   uint32_t wbytes;       // section bytes
-  int KC;                // K chunks
+  int KC;                // K chunks of the weights
+  int plane_shift;       // 0: one A plane; 1: A has two planes (hi, lo), each
+                         // weight chunk is used for both (step s: chunk s >> 1,
+                         // plane s & 1)
+  uint32_t a_plane;      // bytes from one A plane to the next
   int rows;              // valid rows in this tile (<= kBM)
   int rg[2];             // atom row groups of this wave's atoms 2w, 2w+1
   uint32_t aoff;         // this lane's A row offset for row block w (+16(l/16)), or kOOB
@@ -331,16 +335,19 @@ __device__ __forceinline__ void gemm_tile_mf(const GemmTile& gt, __amdgpu_buffer
   const int lane = threadIdx.x & 63, w = wave_id();
   const int mh = w >> 2, nq = w & 3;
   const int KC = gt.KC;
+  const int steps = KC << gt.plane_shift;
   const __amdgpu_buffer_rsrc_t rw = rsrc(gt.wbase, gt.wbytes);
   const uint32_t woff0 = (uint32_t)gt.rg[0] * KC * kAtomBytes;
   const uint32_t woff1 = (uint32_t)gt.rg[1] * KC * kAtomBytes;
-  // Issue chunk min(c, KC - 1) into stage r.
-  auto issue = [&](int c, int r) {
-    c = c < KC ? c : KC - 1;
+  // Issue step min(s, steps - 1) into stage r.
+  auto issue = [&](int s, int r) {
+    s = s < steps ? s : steps - 1;
+    const int c = s >> gt.plane_shift;
+    const uint32_t plane = (uint32_t)(s & gt.plane_shift) * gt.a_plane;
     uint8_t* buf = st.buf[r];
 #pragma unroll
     for (int j = 0; j < 4; j++)
-      lds_load16(ra, gt.aoff + (uint32_t)c * (kAtomK * 2) + 64u * j, buf + (w * 4 + j) * 1024);
+      lds_load16(ra, gt.aoff + plane + (uint32_t)c * (kAtomK * 2) + 64u * j, buf + (w * 4 + j) * 1024);
 #pragma unroll
     for (int t = 0; t < 2; t++) {
       const uint32_t o = (t ? woff1 : woff0) + (uint32_t)c * kAtomBytes;
@@ -388,10 +395,10 @@ __device__ __forceinline__ void gemm_tile_mf(const GemmTile& gt, __amdgpu_buffer
     issue(s, s);
     __builtin_amdgcn_sched_barrier(0);
   }
-  for (int c0 = 0; c0 < KC; c0 += kStages) {
+  for (int c0 = 0; c0 < steps; c0 += kStages) {
 #pragma unroll
     for (int u = 0; u < kStages; u++) {
-      if (c0 + u >= KC) break;
+      if (c0 + u >= steps) break;
       wait_vmem_barrier<kVmemPerChunk * (kStages - 2)>();
       issue(c0 + u + kStages - 1, (u + kStages - 1) % kStages);
       __builtin_amdgcn_sched_barrier(0);
@@ -432,8 +439,8 @@ __device__ __forceinline__ int wave_mfrags(int rows) {
 
 template <int MF>
 __device__ __forceinline__ void gateup_tile(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
-                                            const Stages& st, uint16_t* __restrict__ h, int I,
-                                            size_t row0, int p0) {
+                                            const Stages& st, uint16_t* __restrict__ h,
+                                            size_t lo_plane, int I, size_t row0, int p0) {
   const int lane = threadIdx.x & 63, mh = wave_id() >> 2;
   f32x4 acc[MF > 0 ? MF : 1][kFragsPerWave];
 #pragma unroll
@@ -450,7 +457,10 @@ __device__ __forceinline__ void gateup_tile(const GemmTile& gt, __amdgpu_buffer_
         const int m = (2 * i + mh) * 16 + 4 * (lane >> 4) + r;
         if (m < gt.rows) {
           const float hv = silu(acc[i][2 * q][r]) * acc[i][2 * q + 1][r];
-          h[(row0 + m) * I + (p0 + q) * 16 + (lane & 15)] = f32_to_bf16_rne(hv);
+          const uint16_t hi = f32_to_bf16_rne(hv);
+          const size_t o = (row0 + m) * I + (p0 + q) * 16 + (lane & 15);
+          h[o] = hi;
+          h[lo_plane + o] = f32_to_bf16_rne(hv - __uint_as_float((uint32_t)hi << 16));
         }
       }
     }
@@ -482,9 +492,11 @@ __device__ __forceinline__ void down_tile(const GemmTile& gt, __amdgpu_buffer_rs
 
 // Gate/up + SwiGLU.  N-block nb covers row pairs nb*8 .. nb*8+7 (gate, up);
 // column quarter nq takes pairs nb*8 + 2nq and +1 (atoms g0, u0, g1, u1).
+// h leaves as two bf16 planes, hi = RNE(h) and lo = RNE(h - hi) (about 16
+// significant bits), both of which the down GEMM contracts.
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void gateup_prefill_kernel(
     GroupArgs g, const uint16_t* x, uint32_t x_bytes, int H, int I, int nbn,
-    uint16_t* __restrict__ h) {
+    uint16_t* __restrict__ h, size_t lo_plane) {
   int ti, nb;
   tile_of_block(nbn, &ti, &nb);
   if (ti >= *g.n_tiles) return;
@@ -501,6 +513,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   gt.wbase = grp < g.E ? g.layerbuf + (size_t)grp * g.stride : g.shared_w;
   gt.KC = H / kAtomK;
   gt.wbytes = (uint32_t)(2 * I / kAtomRows) * (uint32_t)gt.KC * kAtomBytes;
+  gt.plane_shift = 0;
+  gt.a_plane = 0;
   gt.rows = min(kBM, cnt - m0);
 #pragma unroll
   for (int t = 0; t < 2; t++) {
@@ -512,7 +526,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   const __amdgpu_buffer_rsrc_t ra = rsrc(x, x_bytes);
   const size_t row0 = (size_t)(pos0 + m0);
   const int p0 = nb * 8 + 2 * nq;
-#define GU(N) gateup_tile<N>(gt, ra, st, h, I, row0, p0)
+#define GU(N) gateup_tile<N>(gt, ra, st, h, lo_plane, I, row0, p0)
   MOE_MF_SWITCH(wave_mfrags(gt.rows), GU)
 #undef GU
 }
@@ -520,8 +534,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
 // Down.  N-block nb covers row groups nb*16 .. nb*16+15 of H (256 columns);
 // column quarter nq takes row groups nb*16 + 4nq .. +3.
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void down_prefill_kernel(
-    GroupArgs g, const uint16_t* h, uint32_t h_bytes, int H, int I, int nbn, size_t gateup_bytes,
-    float* __restrict__ yperm) {
+    GroupArgs g, const uint16_t* h, uint32_t h_bytes, uint32_t lo_plane_bytes, int H, int I,
+    int nbn, size_t gateup_bytes, float* __restrict__ yperm) {
   int ti, nb;
   tile_of_block(nbn, &ti, &nb);
   if (ti >= *g.n_tiles) return;
@@ -539,6 +553,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
   gt.wbase = (grp < g.E ? g.layerbuf + (size_t)grp * g.stride : g.shared_w) + gateup_bytes;
   gt.KC = I / kAtomK;
   gt.wbytes = (uint32_t)ngroups * (uint32_t)gt.KC * kAtomBytes;
+  gt.plane_shift = 1;
+  gt.a_plane = lo_plane_bytes;
   gt.rows = min(kBM, cnt - m0);
 #pragma unroll
   for (int t = 0; t < 2; t++) {
@@ -587,7 +603,7 @@ hipError_t prefill_alloc(Ctx* c) {
   PA(tok, rows);
   PA(tiles, (size_t)p->max_tiles);
   PA(n_tiles, 1);
-  PA(h, rows * f.inter);
+  PA(h, 2 * rows * f.inter);  // hi and lo planes
   PA(yperm, rows * f.hidden);
 #undef PA
   const size_t layer_bytes = (size_t)E * c->stride;
@@ -648,7 +664,6 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
   const int H = f.hidden, I = f.inter, E = f.n_experts, k = f.top_k;
   const size_t layer_bytes = (size_t)E * c->stride;
   const int nchunk = (T + kChunkTokens - 1) / kChunkTokens;
-  const size_t rows = (size_t)T * k + (f.has_shared ? T : 0);
 
   // Uploads wait for everything already on the caller's stream (an earlier
   // call may still read the layer buffers).
@@ -702,11 +717,13 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
         tr = {nullptr, nullptr, nullptr};
     }
     const int nbn_gu = I / (16 * 8), nbn_dn = (H + 255) / 256;
+    const size_t lo_plane = (size_t)p->Tmax * (k + 1) * I;  // elements
     gateup_prefill_kernel<<<p->max_tiles * nbn_gu, 64 * kGemmWaves, 0, st>>>(
-        ga, x, (uint32_t)T * H * 2, H, I, nbn_gu, p->h);
+        ga, x, (uint32_t)T * H * 2, H, I, nbn_gu, p->h, lo_plane);
     if (tr.before_down) (void)hipEventRecord(tr.before_down, st);
     down_prefill_kernel<<<p->max_tiles * nbn_dn, 64 * kGemmWaves, 0, st>>>(
-        ga, p->h, (uint32_t)(rows * I * 2), H, I, nbn_dn, gateup_section_bytes(H, I), p->yperm);
+        ga, p->h, (uint32_t)(4 * lo_plane), (uint32_t)(2 * lo_plane), H, I, nbn_dn,
+        gateup_section_bytes(H, I), p->yperm);
     if (tr.after_down) {
       (void)hipEventRecord(tr.after_down, st);
       c->t_prefill.push_back(tr);

@@ -77,7 +77,9 @@ typedef struct moe_config {
   int32_t cache_slots;     /* C: HBM LRU slots, 0..min(n_layers*n_experts,
                               4096)                                          */
   int32_t staging_slots;   /* S: HBM slots for misses that bypass the cache  */
-  int32_t max_prefill_tokens; /* 0 disables moe_prefill_forward              */
+  int32_t max_prefill_tokens; /* 0 disables moe_prefill_forward; at most
+                              what keeps T*H*2 and T*(k+1)*I*4 bytes below
+                              2 GiB (else UNSUPPORTED)                      */
 } moe_config;
 
 /* Counters since creation or the last moe_reset_stats. */

@@ -246,37 +246,48 @@ __device__ __forceinline__ void tile_of_block(int nbn, int* ti, int* nb) {
 // on 8 waves (two per SIMD): wave w owns columns 64(w%4).. and the 16-row
 // fragments 2i + w/4 (i < 4) -- interleaved, so that the two waves sharing
 // a SIMD hold nearly equal row counts in a partly filled tile -- as 4 x 4
-// fragments of the 16x16x32 bf16 MFMA.  Both operands go
-// straight from global memory into LDS with buffer-to-LDS loads, so nothing
-// but the accumulators lives across chunks:
-//  - A (bf16 token rows, gathered): block (mf, q) is 1 KB, lane l's 16 bytes
-//    at 16l holding row 16mf + l%16, chunk elements 32q + 8(l/16) .. +8, so
-//    each load instruction reads 64 contiguous bytes of 16 rows.  At K step
-//    j a lane needs the elements its weight fragment covers, 32(l/16) + 8j
-//    (MX block l/16, sub-block j): it reads block (mf, l/16) at
-//    256j + 16(l%16), 256 contiguous bytes per 16 lanes;
+// fragments of the 16x16x32 bf16 MFMA.  Both operands go straight from
+// global memory into LDS with buffer-to-LDS loads, so nothing but the
+// accumulators lives across chunks:
+//  - A (bf16 token rows, gathered): fragment mf is 4 KB, one 256-byte chunk
+//    row per token row, its sixteen 16-byte pieces stored XOR-swizzled by
+//    the row (piece p of row r at slot p ^ r).  Each load instruction fills
+//    1 KB, four whole rows (so every 128-byte line it touches is read in
+//    full: half-line reads measured at half the rate).  At K step j a lane
+//    needs the elements its weight fragment covers, 32(l/16) + 8j (MX block
+//    l/16, sub-block j), i.e. piece 4(l/16) + j of row l%16; the swizzle
+//    puts the 16 rows' pieces in 16 different bank groups;
 //  - B (the tile's 16 MXFP4 weight atoms of the chunk, 4 per column
 //    quarter): the 1 KB of codes of atom t at block t (lane order, as
-//    stored), then its 64 scale bytes, one per 4-byte LDS slot (a byte-sized
-//    buffer-to-LDS load still writes one dword slot per lane); dequantised in
+//    stored), then every atom's 64 scale bytes packed at 64t (one 4-byte
+//    load per lane fetches the scales of four atoms); dequantised in
 //    registers after the read.
-// Each wave issues kVmemPerChunk loads per chunk (A fragment block w, atoms
-// 2w and 2w+1).  kStages chunks are in flight: past the last chunk a wave
-// re-issues the last one into a stage no one reads any more, so "this
-// wave's loads of chunk c landed" is always vmcnt <= (kStages - 2) chunks'
-// worth; then one barrier makes every wave's loads visible and frees the
-// stage read at chunk c-1, chunk c + kStages - 1 is issued and chunk c is
-// computed.  The barrier is a bare s_barrier with a compiler memory clobber:
-// a workgroup fence there would make the compiler drain every buffer-to-LDS
-// load in flight, including the prefetched ones.
+// The loads are split by source.  Waves 0-3 fetch A (rows 32w .. 32w+31:
+// 8 loads per step); those are mostly L2 hits, since the column
+// blocks of a token tile run together on one XCD, and one step of lead is
+// enough.  Waves 4-7 fetch B (atoms 4(w-4) .. +3: 5 loads per chunk), which
+// streams from HBM and is fetched kStagesB - 1 chunks ahead.  vmcnt counts
+// only the wave's own loads, so the deep weight prefetch never lengthens the
+// short A wait.  Per step every wave waits for its own loads of the step,
+// one barrier makes them visible and frees the stages the previous step
+// read, the next loads are issued and the step is computed.  Loads past the
+// end go to an out-of-range offset (zeros, no memory traffic) into a stage
+// no one reads any more, so the wait counts never change.  The barrier is a
+// bare s_barrier with a compiler memory clobber: a workgroup fence there
+// would make the compiler drain every buffer-to-LDS load in flight,
+// including the prefetched ones.
 constexpr int kGemmWaves = 8;
-constexpr int kStages = 3;
-constexpr int kAtomsPerTile = 16;                               // 256 columns
-constexpr int kLdsA = kBM * kAtomK * 2;                         // 32 KB
-constexpr int kLdsB = kAtomsPerTile * kAtomData;                // 16 KB
-constexpr int kLdsS = kAtomsPerTile * 64 * 4;                   // 4 KB
-constexpr int kStageBytes = kLdsA + kLdsB + kLdsS;              // 52 KB
-constexpr int kVmemPerChunk = 8;  // per wave: 4 A, 2 code and 2 scale loads
+constexpr int kStagesA = 2;
+constexpr int kStagesB = 4;
+constexpr int kAtomsPerTile = 16;                                   // 256 columns
+constexpr int kLdsA = kBM * kAtomK * 2;                             // 32 KB per A stage
+constexpr int kLdsBc = kAtomsPerTile * kAtomData;                   // 16 KB of codes
+constexpr int kLdsBStage = kLdsBc + kAtomsPerTile * 64;             // + 1 KB of scales
+constexpr int kLdsGemm = kStagesA * kLdsA + kStagesB * kLdsBStage;  // 132 KB
+constexpr int kVmemA = 8;  // per A wave and step: 2 row blocks x 4 pieces
+constexpr int kVmemB = 5;  // per B wave and chunk: 4 code loads, 1 scale load
+static_assert(kLdsGemm <= 160 * 1024, "LDS per CU");
+static_assert(kStagesA >= 2 && kStagesB >= 2, "one stage in flight at least");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -288,40 +299,42 @@ struct GemmTile {
                          // weight chunk is used for both (step s: chunk s >> 1,
                          // plane s & 1)
   uint32_t a_plane;      // bytes from one A plane to the next
+  int k0;                // first K chunk: the walk is k0 .. KC-1, 0 .. k0-1
   int rows;              // valid rows in this tile (<= kBM)
-  int rg[2];             // atom row groups of this wave's atoms 2w, 2w+1
-  uint32_t aoff;         // this lane's A row offset for row block w (+16(l/16)), or kOOB
-};
-
-struct Stages {
-  uint8_t* buf[kStages];
+  uint32_t aoff[8];      // A waves: this lane's piece of row 32w + 4i + l/16 for
+                         // load i (row start + swizzled piece), or kOOB past
+                         // the valid rows
+  uint32_t woff[4];      // B waves: atom 4(w-4) + t, chunk 0
+  uint32_t soff;         // B waves: this lane's scale dword (atom 4(w-4) + l/16,
+                         // bytes 4(l%16) ..), chunk 0
 };
 
 // Buffer-to-LDS loads: `bytes` per lane from rsrc + voffset into LDS at
 // lds + lane * slot (16 bytes for the 16-byte form, a 4-byte slot for one
-// byte).  Written as asm so that the compiler, which cannot tell the stage
+// dword).  Written as asm so that the compiler, which cannot tell the stage
 // buffers apart, adds no waits of its own before the LDS reads: every wait
-// on these loads is the explicit one in wait_vmem_barrier.  No output
-// registers: the data goes to LDS.  The s_nop is the wait state an M0 write
-// needs before a load that reads M0 (the compiler emits M0 right before).
+// on these loads is an explicit one.  No output registers: the data goes to
+// LDS.  The s_nop is the wait state an M0 write needs before a load that
+// reads M0 (the compiler emits M0 right before).
 __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, void* lds) {
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(r),
                "{m0}"((uint32_t)(uintptr_t)(lds_void*)lds)
                : "memory");
 }
-__device__ __forceinline__ void lds_load1(__amdgpu_buffer_rsrc_t r, uint32_t voffset, void* lds) {
-  asm volatile("s_nop 0\n\tbuffer_load_ubyte %0, %1, 0 offen lds" ::"v"(voffset), "s"(r),
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, uint32_t voffset, void* lds) {
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voffset), "s"(r),
                "{m0}"((uint32_t)(uintptr_t)(lds_void*)lds)
                : "memory");
 }
 
 // Wait until at most N of this wave's vector-memory instructions are
-// outstanding, then barrier the workgroup.
+// outstanding.
 template <int N>
-__device__ __forceinline__ void wait_vmem_barrier() {
+__device__ __forceinline__ void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -330,51 +343,57 @@ __device__ __forceinline__ int wave_id() {
 // MF: this wave's 16-row fragments that hold rows (0..4).
 template <int MF>
 __device__ __forceinline__ void gemm_tile_mf(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
-                                             const Stages& st,
+                                             uint8_t* lds,
                                              f32x4 (&acc)[MF > 0 ? MF : 1][kFragsPerWave]) {
   const int lane = threadIdx.x & 63, w = wave_id();
   const int mh = w >> 2, nq = w & 3;
-  const int KC = gt.KC;
-  const int steps = KC << gt.plane_shift;
+  const bool a_wave = w < 4;
+  const int KC = gt.KC, ps = gt.plane_shift;
+  const int steps = KC << ps;
   const __amdgpu_buffer_rsrc_t rw = rsrc(gt.wbase, gt.wbytes);
-  const uint32_t woff0 = (uint32_t)gt.rg[0] * KC * kAtomBytes;
-  const uint32_t woff1 = (uint32_t)gt.rg[1] * KC * kAtomBytes;
-  // Issue step min(s, steps - 1) into stage r.
-  auto issue = [&](int s, int r) {
-    s = s < steps ? s : steps - 1;
-    const int c = s >> gt.plane_shift;
-    const uint32_t plane = (uint32_t)(s & gt.plane_shift) * gt.a_plane;
-    uint8_t* buf = st.buf[r];
+  uint8_t* const bstages = lds + kStagesA * kLdsA;
+  // Chunk of the weights (and of A) that walk position c covers.
+  auto chunk = [&](int c) { return c + gt.k0 < KC ? c + gt.k0 : c + gt.k0 - KC; };
+  // A waves: step s into stage s % kStagesA.
+  auto issue_a = [&](int s) {
+    uint8_t* buf = lds + (s % kStagesA) * kLdsA;
+    const bool in = s < steps;
+    const uint32_t k = (uint32_t)chunk(s >> ps) * (kAtomK * 2) + (uint32_t)(s & ps) * gt.a_plane;
 #pragma unroll
-    for (int j = 0; j < 4; j++)
-      lds_load16(ra, gt.aoff + plane + (uint32_t)c * (kAtomK * 2) + 64u * j, buf + (w * 4 + j) * 1024);
-#pragma unroll
-    for (int t = 0; t < 2; t++) {
-      const uint32_t o = (t ? woff1 : woff0) + (uint32_t)c * kAtomBytes;
-      const int atom = 2 * w + t;
-      lds_load16(rw, o + 16u * lane, buf + kLdsA + atom * kAtomData);
-      lds_load1(rw, o + kAtomData + lane, buf + kLdsA + kLdsB + atom * 256);
-    }
+    for (int i = 0; i < 8; i++) lds_load16(ra, in ? gt.aoff[i] + k : kOOB, buf + (8 * w + i) * 1024);
   };
-  // One chunk: the A fragments and dequantised weights of K step j+1 are
+  // B waves: chunk c into stage c % kStagesB.
+  auto issue_b = [&](int c) {
+    uint8_t* buf = bstages + (c % kStagesB) * kLdsBStage;
+    const int u = w - 4;
+    const bool in = c < KC;
+    const uint32_t k = (uint32_t)chunk(c) * kAtomBytes;
+#pragma unroll
+    for (int t = 0; t < 4; t++)
+      lds_load16(rw, in ? gt.woff[t] + k + 16u * lane : kOOB, buf + (4 * u + t) * kAtomData);
+    lds_load4(rw, in ? gt.soff + k : kOOB, buf + kLdsBc + 4 * u * 64);
+  };
+  // One step: the A fragments and dequantised weights of K step j+1 are
   // fetched while the MFMAs of step j run.
-  auto compute = [&](int r) {
+  auto compute = [&](int s) {
     if constexpr (MF > 0) {
-      const uint8_t* buf = st.buf[r];
+      const uint8_t* abuf = lds + (s % kStagesA) * kLdsA;
+      const uint8_t* bbuf = bstages + ((s >> ps) % kStagesB) * kLdsBStage;
       u32x4 wd[kFragsPerWave];
       uint32_t sd[kFragsPerWave];
 #pragma unroll
       for (int f = 0; f < kFragsPerWave; f++) {
         const int atom = nq * kFragsPerWave + f;
-        wd[f] = *reinterpret_cast<const u32x4*>(buf + kLdsA + atom * kAtomData + 16 * lane);
-        sd[f] = *reinterpret_cast<const uint32_t*>(buf + kLdsA + kLdsB + atom * 256 + 4 * lane) & 0xFFu;
+        wd[f] = *reinterpret_cast<const u32x4*>(bbuf + atom * kAtomData + 16 * lane);
+        sd[f] = bbuf[kLdsBc + atom * 64 + lane];
       }
       bf16x8 a[2][MF], b[2][kFragsPerWave];
       auto fetch = [&](int j, int q) {
+        const int r = lane & 15;
+        const int slot = ((4 * (lane >> 4) + j) ^ r) & 15;
 #pragma unroll
         for (int i = 0; i < MF; i++)
-          a[q][i] = *reinterpret_cast<const bf16x8*>(buf + ((2 * i + mh) * 4 + (lane >> 4)) * 1024 +
-                                                     256 * j + 16 * (lane & 15));
+          a[q][i] = *reinterpret_cast<const bf16x8*>(abuf + (2 * i + mh) * 4096 + 256 * r + 16 * slot);
 #pragma unroll
         for (int f = 0; f < kFragsPerWave; f++) b[q][f] = dequant8(wd[f][j], sd[f]);
       };
@@ -390,23 +409,55 @@ __device__ __forceinline__ void gemm_tile_mf(const GemmTile& gt, __amdgpu_buffer
       }
     }
   };
+  if (a_wave) {
 #pragma unroll
-  for (int s = 0; s < kStages - 1; s++) {
-    issue(s, s);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int s = 0; s < kStagesA - 1; s++) issue_a(s);
+  } else {
+#pragma unroll
+    for (int c = 0; c < kStagesB - 1; c++) issue_b(c);
   }
-  for (int c0 = 0; c0 < steps; c0 += kStages) {
-#pragma unroll
-    for (int u = 0; u < kStages; u++) {
-      if (c0 + u >= steps) break;
-      wait_vmem_barrier<kVmemPerChunk * (kStages - 2)>();
-      issue(c0 + u + kStages - 1, (u + kStages - 1) % kStages);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(u);
-    }
+  __builtin_amdgcn_sched_barrier(0);
+  for (int s = 0; s < steps; s++) {
+    const bool new_chunk = (s & ps) == 0;
+    if (a_wave)
+      wait_vmem<kVmemA * (kStagesA - 2)>();
+    else if (new_chunk)
+      wait_vmem<kVmemB * (kStagesB - 2)>();
+    lds_barrier();
+    if (a_wave)
+      issue_a(s + kStagesA - 1);
+    else if (new_chunk)
+      issue_b((s >> ps) + kStagesB - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s);
   }
   // No buffer-to-LDS write may land after the workgroup has ended.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  wait_vmem<0>();
+}
+
+// A wave w loads rows 32w .. 32w+31 (offsets set by the kernel); B wave
+// w loads tile atoms 4(w-4) .. +3, which are weight row groups rg0 .. rg0+3.
+// Row groups at or past ngroups (the last, partial column block of the down
+// GEMM) read group 0 instead: their columns are never stored.
+__device__ __forceinline__ void clear_loads(GemmTile& gt) {
+#pragma unroll
+  for (int i = 0; i < 8; i++) gt.aoff[i] = kOOB;
+#pragma unroll
+  for (int t = 0; t < 4; t++) gt.woff[t] = 0;
+  gt.soff = 0;
+}
+// Byte offset, within a 256-byte chunk row, of the piece that lane l loads
+// for tile row r: it lands in LDS slot l % 16 of that row, which holds
+// piece (l % 16) ^ (r % 16).
+__device__ __forceinline__ uint32_t a_piece(int r, int lane) {
+  return 16u * (uint32_t)(((lane & 15) ^ r) & 15);
+}
+__device__ __forceinline__ void set_weight_loads(GemmTile& gt, int rg0, int lane, int ngroups) {
+  const uint32_t group_bytes = (uint32_t)gt.KC * kAtomBytes;
+#pragma unroll
+  for (int t = 0; t < 4; t++) gt.woff[t] = (uint32_t)(rg0 + t < ngroups ? rg0 + t : 0) * group_bytes;
+  const int rl = rg0 + (lane >> 4);
+  gt.soff = (uint32_t)(rl < ngroups ? rl : 0) * group_bytes + kAtomData + 4u * (lane & 15);
 }
 
 struct GroupArgs {
@@ -439,7 +490,7 @@ __device__ __forceinline__ int wave_mfrags(int rows) {
 
 template <int MF>
 __device__ __forceinline__ void gateup_tile(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
-                                            const Stages& st, uint16_t* __restrict__ h,
+                                            uint8_t* lds, uint16_t* __restrict__ h,
                                             size_t lo_plane, int I, size_t row0, int p0) {
   const int lane = threadIdx.x & 63, mh = wave_id() >> 2;
   f32x4 acc[MF > 0 ? MF : 1][kFragsPerWave];
@@ -447,7 +498,7 @@ __device__ __forceinline__ void gateup_tile(const GemmTile& gt, __amdgpu_buffer_
   for (int i = 0; i < (MF > 0 ? MF : 1); i++)
 #pragma unroll
     for (int f = 0; f < kFragsPerWave; f++) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gemm_tile_mf<MF>(gt, ra, st, acc);
+  gemm_tile_mf<MF>(gt, ra, lds, acc);
 #pragma unroll
   for (int i = 0; i < MF; i++) {
 #pragma unroll
@@ -469,7 +520,7 @@ __device__ __forceinline__ void gateup_tile(const GemmTile& gt, __amdgpu_buffer_
 
 template <int MF>
 __device__ __forceinline__ void down_tile(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
-                                          const Stages& st, float* __restrict__ yperm, int H,
+                                          uint8_t* lds, float* __restrict__ yperm, int H,
                                           size_t row0, int rg0, int ngroups) {
   const int lane = threadIdx.x & 63, mh = wave_id() >> 2;
   f32x4 acc[MF > 0 ? MF : 1][kFragsPerWave];
@@ -477,7 +528,7 @@ __device__ __forceinline__ void down_tile(const GemmTile& gt, __amdgpu_buffer_rs
   for (int i = 0; i < (MF > 0 ? MF : 1); i++)
 #pragma unroll
     for (int f = 0; f < kFragsPerWave; f++) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gemm_tile_mf<MF>(gt, ra, st, acc);
+  gemm_tile_mf<MF>(gt, ra, lds, acc);
 #pragma unroll
   for (int i = 0; i < MF; i++)
 #pragma unroll
@@ -500,11 +551,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   int ti, nb;
   tile_of_block(nbn, &ti, &nb);
   if (ti >= *g.n_tiles) return;
-  __shared__ __attribute__((aligned(1024))) uint8_t S0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t S1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t S2[kStageBytes];
-  static_assert(kStages == 3, "one LDS array per stage");
-  const Stages st{{S0, S1, S2}};
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsGemm];
   const int2 td = g.tiles[ti];
   const int grp = td.x, m0 = td.y;
   const int cnt = g.counts[grp], pos0 = g.offsets[grp];
@@ -515,18 +562,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   gt.wbytes = (uint32_t)(2 * I / kAtomRows) * (uint32_t)gt.KC * kAtomBytes;
   gt.plane_shift = 0;
   gt.a_plane = 0;
+  gt.k0 = nb * gt.KC / nbn;
   gt.rows = min(kBM, cnt - m0);
+  clear_loads(gt);
+  if (w < 4) {
 #pragma unroll
-  for (int t = 0; t < 2; t++) {
-    const int atom = 2 * w + t;  // column quarter atom >> 2, fragment atom & 3
-    gt.rg[t] = 2 * (nb * 8 + 2 * (atom >> 2)) + (atom & 3);
+    for (int i = 0; i < 8; i++) {
+      const int r = 32 * w + 4 * i + (lane >> 4);
+      if (r < gt.rows) gt.aoff[i] = (uint32_t)g.tok[pos0 + m0 + r] * (uint32_t)H * 2u + a_piece(r, lane);
+    }
+  } else {
+    // Tile atom a (column quarter a/4, fragment a%4) is row group 16nb + a:
+    // pair nb*8 + 2(a/4) + (a%4)/2, gate if a is even, up if odd.
+    set_weight_loads(gt, nb * 16 + 4 * (w - 4), lane, 2 * I / kAtomRows);
   }
-  const int r = w * 16 + (lane & 15);
-  gt.aoff = r < gt.rows ? (uint32_t)g.tok[pos0 + m0 + r] * (uint32_t)H * 2u + 16u * (lane >> 4) : kOOB;
   const __amdgpu_buffer_rsrc_t ra = rsrc(x, x_bytes);
   const size_t row0 = (size_t)(pos0 + m0);
   const int p0 = nb * 8 + 2 * nq;
-#define GU(N) gateup_tile<N>(gt, ra, st, h, lo_plane, I, row0, p0)
+#define GU(N) gateup_tile<N>(gt, ra, lds, h, lo_plane, I, row0, p0)
   MOE_MF_SWITCH(wave_mfrags(gt.rows), GU)
 #undef GU
 }
@@ -539,11 +592,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
   int ti, nb;
   tile_of_block(nbn, &ti, &nb);
   if (ti >= *g.n_tiles) return;
-  __shared__ __attribute__((aligned(1024))) uint8_t S0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t S1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t S2[kStageBytes];
-  static_assert(kStages == 3, "one LDS array per stage");
-  const Stages st{{S0, S1, S2}};
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsGemm];
   const int2 td = g.tiles[ti];
   const int grp = td.x, m0 = td.y;
   const int cnt = g.counts[grp], pos0 = g.offsets[grp];
@@ -555,19 +604,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
   gt.wbytes = (uint32_t)ngroups * (uint32_t)gt.KC * kAtomBytes;
   gt.plane_shift = 1;
   gt.a_plane = lo_plane_bytes;
+  gt.k0 = nb * gt.KC / nbn;
   gt.rows = min(kBM, cnt - m0);
+  clear_loads(gt);
+  if (w < 4) {
 #pragma unroll
-  for (int t = 0; t < 2; t++) {
-    const int atom = 2 * w + t;
-    const int rg = nb * 16 + atom;  // = nb*16 + 4*(atom>>2) + (atom&3)
-    gt.rg[t] = rg < ngroups ? rg : 0;
+    for (int i = 0; i < 8; i++) {
+      const int r = 32 * w + 4 * i + (lane >> 4);
+      if (r < gt.rows) gt.aoff[i] = (uint32_t)(pos0 + m0 + r) * (uint32_t)I * 2u + a_piece(r, lane);
+    }
+  } else {
+    set_weight_loads(gt, nb * 16 + 4 * (w - 4), lane, ngroups);  // tile atom a: row group 16nb + a
   }
-  const int r = w * 16 + (lane & 15);
-  gt.aoff = r < gt.rows ? (uint32_t)(pos0 + m0 + r) * (uint32_t)I * 2u + 16u * (lane >> 4) : kOOB;
   const __amdgpu_buffer_rsrc_t ra = rsrc(h, h_bytes);
   const size_t row0 = (size_t)(pos0 + m0);
   const int rg0 = nb * 16 + 4 * nq;
-#define DN(N) down_tile<N>(gt, ra, st, yperm, H, row0, rg0, ngroups)
+#define DN(N) down_tile<N>(gt, ra, lds, yperm, H, row0, rg0, ngroups)
   MOE_MF_SWITCH(wave_mfrags(gt.rows), DN)
 #undef DN
 }

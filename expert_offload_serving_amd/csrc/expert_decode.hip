@@ -55,6 +55,13 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
 
+// Workgroup barrier for the LDS reduction: waits for LDS operations only, so
+// the output stores of one M tile stay in flight across it (__syncthreads()
+// would drain them first).  No thread reads another's global stores.
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 typedef __attribute__((address_space(1))) const u32x4 gu32x4;
 typedef __attribute__((address_space(1))) const uint8_t gu8;
 
@@ -158,7 +165,7 @@ __global__ __launch_bounds__(1024) void gateup_decode_kernel(
     }
     red[(2 * w) * 64 + lane] = ag;
     red[(2 * w + 1) * 64 + lane] = au;
-    __syncthreads();
+    lds_sync();
     for (int v0 = threadIdx.x; v0 < 256; v0 += blockDim.x) {  // 64 lanes x 4 values
       const int L = v0 >> 2, i = v0 & 3;
       float gs = 0.f, us = 0.f;
@@ -175,7 +182,7 @@ __global__ __launch_bounds__(1024) void gateup_decode_kernel(
         h[lo_plane + o] = f32_to_bf16_rne(hv - bf16_to_f32(hi));
       }
     }
-    __syncthreads();
+    lds_sync();
   };
   tile(0, trow);
   for (int m0 = 16; m0 < it.cnt; m0 += 16) {
@@ -262,7 +269,7 @@ __global__ __launch_bounds__(1024) void down_decode_kernel(
     }
     red[(2 * w) * 64 + lane] = acc0;
     red[(2 * w + 1) * 64 + lane] = acc1;
-    __syncthreads();
+    lds_sync();
     for (int v0 = threadIdx.x; v0 < 512; v0 += blockDim.x) {  // 2 groups x 64 lanes x 4 values
       const int g = v0 >> 8, L = (v0 >> 2) & 63, i = v0 & 3;
       float s = 0.f;
@@ -270,7 +277,7 @@ __global__ __launch_bounds__(1024) void down_decode_kernel(
       const int mm = m0 + 4 * (L >> 4) + i;
       if (mm < it.cnt) yperm[(size_t)(it.pos0 + mm) * H + (2 * q + g) * 16 + (L & 15)] = s;
     }
-    __syncthreads();
+    lds_sync();
   };
   tile(0);
   for (int m0 = 16; m0 < it.cnt; m0 += 16) tile(m0);

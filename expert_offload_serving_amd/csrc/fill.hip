@@ -50,13 +50,17 @@ __global__ __launch_bounds__(256) void probe_copy_kernel(const u32x4* __restrict
 }
 
 constexpr int kCopyBlocks = 1024;
+// Fills read mapped host memory at PCIe rate: a workgroup per CU keeps far
+// more than enough in flight, and a launch with nothing to copy (every
+// expert a hit) costs less to dispatch.
+constexpr int kFillBlocks = 256;
 
 }  // namespace
 
 hipError_t launch_fill(const FillEntry* fills, const DevMeta* meta, int max_fill, size_t bytes,
                        hipStream_t st) {
   if (max_fill <= 0) return hipSuccess;
-  fill_kernel<<<kCopyBlocks, 256, 0, st>>>(fills, meta, max_fill, bytes / 16);
+  fill_kernel<<<kFillBlocks, 256, 0, st>>>(fills, meta, max_fill, bytes / 16);
   return hipGetLastError();
 }
 

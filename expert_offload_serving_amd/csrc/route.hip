@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(
       const double s = wave_sum_f64(acc[t]);
       if (lane == 0) red[w][t] = s;
     }
-    __syncthreads();
+    lds_sync();
     if (threadIdx.x < tn) {
       const int t = threadIdx.x;
       double s = 0.0;
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(
       const size_t o = (size_t)(tg + t) * E + e;
       logits[o] = (float)(bias ? s + (double)bias[o] : s);
     }
-    __syncthreads();
+    lds_sync();
   }
 }
 
@@ -106,11 +106,13 @@ struct LookupShared {
   int map[1024];
   int tmp[16];
   int evict;
+  uint64_t clock0;
 };
 
 // Copy the recency order and this layer's map into LDS (issued first, so
 // the loads overlap the work before the lookup).
 __device__ __forceinline__ void prefetch_lookup(const LookupArgs& a, LookupShared& ls) {
+  if (threadIdx.x == 0) ls.clock0 = a.cache->clock;
   for (int p = threadIdx.x; p < a.C; p += blockDim.x) ls.order[p] = a.order[p];
   for (int e = threadIdx.x; e < a.E; e += blockDim.x) ls.map[e] = a.map[a.layer * a.E + e];
 }
@@ -123,7 +125,7 @@ __device__ void block_lookup(const LookupArgs& a, LookupShared& ls, const int* s
                              int* s_slot) {
   const int tid = threadIdx.x, nt = blockDim.x;
   const int C = a.C;
-  const uint64_t clock0 = a.cache->clock;
+  const uint64_t clock0 = ls.clock0;
   if (tid == 0) ls.evict = 0;
   for (int s = tid; s < C; s += nt) ls.hit[s] = 0;
 
@@ -134,37 +136,40 @@ __device__ void block_lookup(const LookupArgs& a, LookupShared& ls, const int* s
   const int slot = valid ? ls.map[e] : -1;
   const bool hit = valid && slot >= 0;
   const bool miss = valid && !hit;
-  int n_hit, n_miss;
-  const int hrank = block_excl_scan(hit ? 1 : 0, ls.tmp, &n_hit);   // barrier: hit[] cleared
-  const int mrank = block_excl_scan(miss ? 1 : 0, ls.tmp, &n_miss);
+  // One scan ranks hits (low 16 bits) and misses (high 16 bits): n <= 1024.
+  int both;
+  const int ranks = block_excl_scan((hit ? 1 : 0) | (miss ? 1 << 16 : 0), ls.tmp, &both);  // barrier: hit[] cleared
+  const int hrank = ranks & 0xFFFF, mrank = ranks >> 16;
+  const int n_hit = both & 0xFFFF, n_miss = both >> 16;
   const int n_fill = min(n_miss, C - n_hit);
   if (hit) {
     ls.hit[slot] = 1;
     a.stamp[slot] = clock0 + 1 + (uint64_t)hrank;
     s_slot[u] = slot;
   }
-  __syncthreads();
+  lds_sync();
 
-  // Victims: non-hit slots in recency order.  Untouched slots are compacted
-  // to the front in place (a slot only moves to a lower position, and every
+  // Victims: the first n_fill non-hit slots in recency order; the other
+  // non-hit slots are kept, compacted to the front in place (non-hit number
+  // r goes to position r - n_fill, never above its own position, and every
   // position of a chunk is read before the chunk's first write).
   constexpr int kSlotMask = (1 << kOrderKeyShift) - 1;
-  int carry = 0, carry_keep = 0;
+  int carry = 0;
   for (int p0 = 0; p0 < C; p0 += nt) {
     const int p = p0 + tid;
     const int ent = p < C ? ls.order[p] : 0;
     const bool nonhit = p < C && !ls.hit[ent & kSlotMask];
-    int tot, ktot;
+    int tot;
     const int r = block_excl_scan(nonhit ? 1 : 0, ls.tmp, &tot) + carry;
-    const bool victim = nonhit && r < n_fill;
-    if (victim) ls.victim[r] = ent;
-    const bool keep = nonhit && !victim;
-    const int kr = block_excl_scan(keep ? 1 : 0, ls.tmp, &ktot) + carry_keep;
-    if (keep) ls.order[kr] = ent;
+    if (nonhit) {
+      if (r < n_fill)
+        ls.victim[r] = ent;
+      else
+        ls.order[r - n_fill] = ent;
+    }
     carry += tot;
-    carry_keep += ktot;
   }
-  __syncthreads();
+  lds_sync();
   const int n_keep = C - n_hit - n_fill;
   if (hit) ls.order[n_keep + hrank] = slot | ((key + 1) << kOrderKeyShift);
   if (miss) {
@@ -189,7 +194,7 @@ __device__ void block_lookup(const LookupArgs& a, LookupShared& ls, const int* s
     }
   }
   if (u < n && !valid) s_slot[u] = INT_MIN;
-  __syncthreads();
+  lds_sync();
   for (int p = tid; p < C; p += nt) a.order[p] = ls.order[p];
   if (tid == 0) {
     DevCache* dc = a.cache;
@@ -203,7 +208,7 @@ __device__ void block_lookup(const LookupArgs& a, LookupShared& ls, const int* s
     a.meta->n_hit = n_hit;
     a.meta->n_bypass = n_miss - n_fill;
   }
-  __syncthreads();
+  lds_sync();
 }
 
 struct FinalizeArgs {
@@ -238,17 +243,24 @@ __global__ __launch_bounds__(kFinalizeThreads) void route_finalize_kernel(Finali
   const int w = tid >> 6, nw = nt >> 6;
   const int T = a.T, E = a.E, k = a.k;
 
+  // Every global load the kernel needs first is issued before the first
+  // barrier: the wave's first token's logits and the cache state.
+  const TopkArgs ta{a.E, a.k, a.renorm, a.logits, a.ids, a.gates, a.user_ids, a.user_gates};
+  uint32_t keys[NK];
+  if (w < T) topk_load<NK>(ta, w, keys);
   prefetch_lookup(a.la, ls);
   for (int e = tid; e < 1024; e += nt) {
     s_counts[e] = 0;
     s_mask[e] = 0ull;
   }
-  __syncthreads();
+  lds_sync();
 
   // top-k and gates, one wave per token
-  const TopkArgs ta{a.E, a.k, a.renorm, a.logits, a.ids, a.gates, a.user_ids, a.user_gates};
-  for (int t = w; t < T; t += nw) topk_token<NK>(ta, t, s_ids);
-  __syncthreads();
+  for (int t = w; t < T; t += nw) {
+    if (t != w) topk_load<NK>(ta, t, keys);
+    topk_select<NK>(ta, t, keys, s_ids);
+  }
+  lds_sync();
 
   // dispatch: counts, offsets, stable permutation, unique experts
   const int nk = T * k;
@@ -258,13 +270,16 @@ __global__ __launch_bounds__(kFinalizeThreads) void route_finalize_kernel(Finali
     atomicAdd(&s_counts[e], 1);
     atomicOr(&s_mask[e], 1ull << (f / k));
   }
-  __syncthreads();
+  lds_sync();
   {
     const int e = tid;
     const int cnt = e < E ? s_counts[e] : 0;
-    int total;
-    const int off = block_excl_scan(cnt, ls.tmp, &total);
-    const int ur = block_excl_scan(cnt > 0 ? 1 : 0, ls.tmp, &n_unique);
+    // one scan: offsets in the low 16 bits (T*k <= 1024), unique ranks above
+    int both;
+    const int ranks = block_excl_scan(cnt | (cnt > 0 ? 1 << 16 : 0), ls.tmp, &both);
+    const int off = ranks & 0xFFFF, ur = ranks >> 16;
+    const int total = both & 0xFFFF;
+    n_unique = both >> 16;
     if (e < E) {
       s_offsets[e] = off;
       a.counts[e] = cnt;
@@ -281,7 +296,7 @@ __global__ __launch_bounds__(kFinalizeThreads) void route_finalize_kernel(Finali
       a.la.meta->T = T;
     }
   }
-  __syncthreads();
+  lds_sync();
   for (int f = tid; f < nk; f += nt) {
     const int t = f / k, e = s_ids[f];
     const int rank = __popcll(s_mask[e] & ((1ull << t) - 1ull));
@@ -321,7 +336,7 @@ __global__ __launch_bounds__(kFinalizeThreads) void cache_lookup_kernel(
   int n = *d_n;
   n = n < 0 ? 0 : (n > n_max ? n_max : n);
   for (int u = threadIdx.x; u < n; u += blockDim.x) s_U[u] = experts[u];
-  __syncthreads();
+  lds_sync();
   block_lookup(la, ls, s_U, n, s_slot);
   for (int u = threadIdx.x; u < n; u += blockDim.x) out_slot[u] = s_slot[u];
 }

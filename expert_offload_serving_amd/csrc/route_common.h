@@ -34,23 +34,6 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
                      (uint32_t)__builtin_amdgcn_readlane((uint32_t)u, 63);
   return __builtin_bit_cast(double, r);
 }
-template <int CTRL, int ROWS = 0xF>
-__device__ __forceinline__ uint64_t max_step(uint64_t v) {
-  const uint64_t o = ((uint64_t)dpp<CTRL, ROWS>((uint32_t)(v >> 32)) << 32) |
-                     dpp<CTRL, ROWS>((uint32_t)v);
-  return o > v ? o : v;
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = max_step<0x111>(v);
-  v = max_step<0x112>(v);
-  v = max_step<0x114>(v);
-  v = max_step<0x118>(v);
-  v = max_step<0x142, 0xA>(v);
-  v = max_step<0x143, 0xC>(v);
-  return ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(v >> 32), 63) << 32) |
-         (uint32_t)__builtin_amdgcn_readlane((uint32_t)v, 63);
-}
-
 // Inclusive scan of one int per lane (DPP, fixed order).
 __device__ __forceinline__ int wave_incl_scan(int v) {
   v += (int)dpp<0x111>((uint32_t)v);
@@ -62,20 +45,31 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Exclusive scan of one int per thread over the block; *total gets the sum.
+// Workgroup barrier for LDS traffic only: it waits for the wave's LDS (and
+// scalar) operations but not for its global stores, which stay in flight.
+// __syncthreads() would also drain every store before the barrier, about a
+// microsecond per barrier after a store.  Only for code in which no thread
+// reads global memory that another thread of the workgroup wrote during the
+// same launch.
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Exclusive scan of one int per thread over the block (at most 64 waves);
+// *total gets the sum.  The wave totals go through LDS once and are scanned
+// by every wave with the same DPP scan (lane i holds wave i's total), so
+// the cost does not grow with the wave count.  Synchronises through LDS only
+// (lds_sync).
 __device__ int block_excl_scan(int v, int* s_tmp, int* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int x = wave_incl_scan(v);
   if (lane == 63) s_tmp[w] = x;
-  __syncthreads();
-  int base = 0, tot = 0;
-  for (int i = 0; i < nw; i++) {
-    const int s = s_tmp[i];
-    if (i < w) base += s;
-    tot += s;
-  }
-  __syncthreads();
-  *total = tot;
+  lds_sync();
+  const int wsum = wave_incl_scan(lane < nw ? s_tmp[lane] : 0);
+  lds_sync();  // s_tmp may be rewritten by the next scan
+  *total = __builtin_amdgcn_readlane(wsum, 63);
+  const int base = w > 0 ? __builtin_amdgcn_readlane(wsum, w - 1) : 0;
   return base + x - v;
 }
 
@@ -97,39 +91,78 @@ struct TopkArgs {
   float* user_gates;
 };
 
-// Top-k of one token in one wave.  Lane l holds the keys of experts
-// l, l+64, ... (NK of them) as (ordered logit << 32 | ~expert): the largest
-// key is the largest logit, ties to the lower expert.  Each round takes the
-// wave maximum of the lanes' current maxima; only the winner lane clears
-// that key and recomputes its maximum.
+// Top-k of one token in one wave.  Lane l holds the ordered-logit keys of
+// experts l, l+64, ... (NK of them; 0 for experts past E, below every finite
+// logit) and its best one (the first maximum, so the lowest expert among
+// equal logits).  Each round reduces the lanes' best keys to the wave
+// maximum on 32-bit DPP steps; a ballot finds the lanes that hold it, and
+// when more than one does (equal logits in several lanes) the lowest expert
+// among them wins, as in the (logit descending, expert ascending) order.  The
+// winner lane clears that key and recomputes its best.  topk_load issues the
+// logit loads (so a caller can start them early), topk_select does the rest.
 template <int NK>
-__device__ void topk_token(const TopkArgs& a, int t, int* s_ids) {
+__device__ __forceinline__ void topk_load(const TopkArgs& a, int t, uint32_t (&keys)[NK]) {
   const int lane = threadIdx.x & 63;
-  const int E = a.E, k = a.k;
-  uint64_t keys[NK];
 #pragma unroll
   for (int i = 0; i < NK; i++) {
     const int e = lane + 64 * i;
-    keys[i] = e < E ? ((uint64_t)ordered_bits(a.logits[(size_t)t * E + e]) << 32) |
-                          (uint64_t)(0xFFFFFFFFu - (uint32_t)e)
-                    : 0ull;
+    keys[i] = e < a.E ? ordered_bits(a.logits[(size_t)t * a.E + e]) : 0u;
   }
-  uint64_t lmax = 0;
+}
+
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t max_step_u32(uint32_t v) {
+  const uint32_t o = dpp<CTRL, ROWS>(v);
+  return o > v ? o : v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max_step_u32<0x111>(v);
+  v = max_step_u32<0x112>(v);
+  v = max_step_u32<0x114>(v);
+  v = max_step_u32<0x118>(v);
+  v = max_step_u32<0x142, 0xA>(v);
+  v = max_step_u32<0x143, 0xC>(v);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+// Wave minimum through the maximum of the complements.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
+
+template <int NK>
+__device__ __forceinline__ void best_key(const uint32_t (&keys)[NK], uint32_t& bv, int& bi) {
+  bv = keys[0];
+  bi = 0;
 #pragma unroll
-  for (int i = 0; i < NK; i++) lmax = keys[i] > lmax ? keys[i] : lmax;
+  for (int i = 1; i < NK; i++)
+    if (keys[i] > bv) {
+      bv = keys[i];
+      bi = i;
+    }
+}
+
+template <int NK>
+__device__ void topk_select(const TopkArgs& a, int t, uint32_t (&keys)[NK], int* s_ids) {
+  const int lane = threadIdx.x & 63;
+  const int E = a.E, k = a.k;
+  uint32_t bv;
+  int bi;
+  best_key<NK>(keys, bv, bi);
   float my_l = 0.f, l0 = 0.f;
   for (int j = 0; j < k; j++) {
-    const uint64_t best = wave_max_u64(lmax);
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-    const float l = from_ordered_bits((uint32_t)(best >> 32));
-    if (lmax == best) {  // the winner lane (keys are unique)
-      lmax = 0;
-#pragma unroll
-      for (int i = 0; i < NK; i++) {
-        if (keys[i] == best) keys[i] = 0ull;
-        lmax = keys[i] > lmax ? keys[i] : lmax;
-      }
+    const uint32_t m = wave_max_u32(bv);
+    const uint64_t holders = __ballot(bv == m);
+    int e;
+    if (__popcll(holders) == 1) {
+      e = __builtin_amdgcn_readlane(lane + 64 * bi, (int)__builtin_ctzll(holders));
+    } else {
+      e = (int)wave_min_u32(bv == m ? (uint32_t)(lane + 64 * bi) : 0xFFFFFFFFu);
     }
+    if (lane == (e & 63)) {  // the winner lane
+#pragma unroll
+      for (int i = 0; i < NK; i++)
+        if (i == (e >> 6)) keys[i] = 0u;
+      best_key<NK>(keys, bv, bi);
+    }
+    const float l = from_ordered_bits(m);
     if (lane == j) my_l = l;
     if (j == 0) l0 = l;
     if (lane == 0) {
@@ -157,6 +190,13 @@ __device__ void topk_token(const TopkArgs& a, int t, int* s_ids) {
     a.gates[t * k + lane] = g;
     if (a.user_gates) a.user_gates[t * k + lane] = g;
   }
+}
+
+template <int NK>
+__device__ void topk_token(const TopkArgs& a, int t, int* s_ids) {
+  uint32_t keys[NK];
+  topk_load<NK>(a, t, keys);
+  topk_select<NK>(a, t, keys, s_ids);
 }
 
 }  // namespace moe

@@ -199,7 +199,13 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   Ctx* c = new (std::nothrow) Ctx();
   if (!c) return fail(MOE_ERR_OOM, "context allocation");
   c->cfg = f;
-  HIPCHK(hipGetDevice(&c->device));
+  {
+    const hipError_t e0 = hipGetDevice(&c->device);
+    if (e0 != hipSuccess) {
+      delete c;
+      return fail(MOE_ERR_HIP, std::string("device query: ") + hipGetErrorString(e0));
+    }
+  }
   const int H = f.hidden, I = f.inter, E = f.n_experts, k = f.top_k, L = f.n_layers;
   const int Tm = f.max_tokens;
   c->rec_bytes = expert_record_bytes(H, I);

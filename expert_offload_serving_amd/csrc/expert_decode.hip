@@ -84,6 +84,44 @@ __device__ __forceinline__ bf16x8 bload8(__amdgpu_buffer_rsrc_t r, uint32_t byte
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+// Epilogues shared by the kernels below: the waves' partial 16x16 tiles in
+// red[wave][tile][lane] are summed in wave order (a fixed order, so results
+// do not depend on scheduling).
+//
+// Gate/up: h for tokens m0 .. m0+15 of the item, columns 16p .. 16p+15, as
+// hi = RNE(h) and lo = RNE(h - hi).
+__device__ __forceinline__ void gateup_epilogue(const f32x4* red, int nw, const WorkItem& it,
+                                                int m0, int p, int I, uint16_t* __restrict__ h,
+                                                size_t lo_plane) {
+  for (int v0 = threadIdx.x; v0 < 256; v0 += blockDim.x) {  // 64 lanes x 4 values
+    const int L = v0 >> 2, i = v0 & 3;
+    float gs = 0.f, us = 0.f;
+    for (int v = 0; v < nw; v++) {
+      gs += red[(2 * v) * 64 + L][i];
+      us += red[(2 * v + 1) * 64 + L][i];
+    }
+    const int mm = m0 + 4 * (L >> 4) + i;
+    if (mm < it.cnt) {
+      const float hv = silu(gs) * us;
+      const uint16_t hi = f32_to_bf16_rne(hv);
+      const size_t o = (size_t)(it.pos0 + mm) * I + p * 16 + (L & 15);
+      h[o] = hi;
+      h[lo_plane + o] = f32_to_bf16_rne(hv - bf16_to_f32(hi));
+    }
+  }
+}
+// Down: rows 32q .. 32q+31 of H (tiles g = 0, 1) for tokens m0 .. m0+15.
+__device__ __forceinline__ void down_epilogue(const f32x4* red, int nw, const WorkItem& it, int m0,
+                                              int q, int H, float* __restrict__ yperm) {
+  for (int v0 = threadIdx.x; v0 < 512; v0 += blockDim.x) {  // 2 tiles x 64 lanes x 4 values
+    const int g = v0 >> 8, L = (v0 >> 2) & 63, i = v0 & 3;
+    float s = 0.f;
+    for (int v = 0; v < nw; v++) s += red[(2 * v + g) * 64 + L][i];
+    const int mm = m0 + 4 * (L >> 4) + i;
+    if (mm < it.cnt) yperm[(size_t)(it.pos0 + mm) * H + (2 * q + g) * 16 + (L & 15)] = s;
+  }
+}
+
 // Gate/up + SwiGLU.  Block (pair p, item): 16 gate and 16 up rows of one
 // expert; wave w takes K chunks [w*CPW, w*CPW+CPW).  M tiles of 16 tokens
 // are processed one after another (weights re-read from L2 after the first).
@@ -166,22 +204,7 @@ __global__ __launch_bounds__(1024) void gateup_decode_kernel(
     red[(2 * w) * 64 + lane] = ag;
     red[(2 * w + 1) * 64 + lane] = au;
     lds_sync();
-    for (int v0 = threadIdx.x; v0 < 256; v0 += blockDim.x) {  // 64 lanes x 4 values
-      const int L = v0 >> 2, i = v0 & 3;
-      float gs = 0.f, us = 0.f;
-      for (int v = 0; v < nw; v++) {
-        gs += red[(2 * v) * 64 + L][i];
-        us += red[(2 * v + 1) * 64 + L][i];
-      }
-      const int mm = m0 + 4 * (L >> 4) + i;
-      if (mm < it.cnt) {
-        const float hv = silu(gs) * us;
-        const uint16_t hi = f32_to_bf16_rne(hv);
-        const size_t o = (size_t)(it.pos0 + mm) * I + p * 16 + (L & 15);
-        h[o] = hi;
-        h[lo_plane + o] = f32_to_bf16_rne(hv - bf16_to_f32(hi));
-      }
-    }
+    gateup_epilogue(red, nw, it, m0, p, I, h, lo_plane);
     lds_sync();
   };
   tile(0, trow);
@@ -270,17 +293,182 @@ __global__ __launch_bounds__(1024) void down_decode_kernel(
     red[(2 * w) * 64 + lane] = acc0;
     red[(2 * w + 1) * 64 + lane] = acc1;
     lds_sync();
-    for (int v0 = threadIdx.x; v0 < 512; v0 += blockDim.x) {  // 2 groups x 64 lanes x 4 values
-      const int g = v0 >> 8, L = (v0 >> 2) & 63, i = v0 & 3;
-      float s = 0.f;
-      for (int v = 0; v < nw; v++) s += red[(2 * v + g) * 64 + L][i];
-      const int mm = m0 + 4 * (L >> 4) + i;
-      if (mm < it.cnt) yperm[(size_t)(it.pos0 + mm) * H + (2 * q + g) * 16 + (L & 15)] = s;
-    }
+    down_epilogue(red, nw, it, m0, q, H, yperm);
     lds_sync();
   };
   tile(0);
   for (int m0 = 16; m0 < it.cnt; m0 += 16) tile(m0);
+}
+
+// Streaming variants for calls of at most 16 tokens (one M tile).  A wave
+// covers CPW consecutive K chunks in steps of two chunks with two steps of
+// weight loads in flight (double-buffered registers), so a wave can cover
+// more of K than it can hold.  The launch then needs fewer waves, and with
+// CPW chosen from the kernels' occupancy every workgroup of the call is
+// resident at once: a second round of workgroups would wait out the memory
+// latency a second time.  Same data layout, reduction order and epilogues
+// as above.
+template <int CPW>
+__global__ __launch_bounds__(1024) void gateup_stream_kernel(
+    const WorkItem* __restrict__ items, const DevMeta* __restrict__ meta,
+    const int32_t* __restrict__ tok, const uint16_t* __restrict__ x, uint32_t x_bytes, int H,
+    int I, uint16_t* __restrict__ h, size_t lo_plane) {
+  constexpr int S = CPW < 2 ? CPW : 2;  // chunks per step
+  constexpr int NS = CPW / S;           // steps
+  const int item = blockIdx.y;
+  if (item >= meta->n_items) return;
+  const WorkItem it = items[item];
+  const int p = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int KC = H / kAtomK;
+  const int c0 = w * CPW;
+  const uint8_t* gbase = it.w + (size_t)(2 * p) * KC * kAtomBytes;
+  const uint8_t* ubase = gbase + (size_t)KC * kAtomBytes;
+  extern __shared__ f32x4 red[];  // [waves][2][64], sized by the launch
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, x_bytes);
+
+  // The token row first: loads return in order, so a token index loaded
+  // after the weights would hold the activation loads back until every
+  // weight load had landed.
+  const int m = lane & 15;
+  const bool mok = m < it.cnt;
+  const int trow = mok ? tok[it.pos0 + m] : 0;
+
+  // Weight loads of step st into buffer b; a chunk past K reads chunk 0
+  // (finite values that meet zero activations), as in the kernels above.
+  u32x4 wg[2][S], wu[2][S];
+  uint32_t sg[2][S], su[2][S];
+  auto load_step = [&](int st, int b) {
+#pragma unroll
+    for (int cc = 0; cc < S; cc++) {
+      const int c = c0 + st * S + cc;
+      const size_t o = (size_t)(c < KC ? c : 0) * kAtomBytes;
+      wg[b][cc] = load_atom_data(gbase + o, lane);
+      wu[b][cc] = load_atom_data(ubase + o, lane);
+      sg[b][cc] = load_scale(gbase + o, lane);
+      su[b][cc] = load_scale(ubase + o, lane);
+    }
+  };
+  load_step(0, 0);
+  if (NS > 1) load_step(1, 1);
+
+  const uint32_t xrow = (uint32_t)(trow * H + 32 * (lane >> 4)) * 2u;
+  auto xoff = [&](int c) { return (mok && c < KC) ? xrow + (uint32_t)c * kAtomK * 2u : kOutOfRange; };
+  bf16x8 xa[2][4];  // activation fragments, fetched one chunk ahead
+  {
+    const uint32_t o = xoff(c0);
+#pragma unroll
+    for (int j = 0; j < 4; j++) xa[0][j] = bload8(rx, o + 16u * j);
+  }
+  f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < NS; st++) {
+    const int b = st & 1;
+#pragma unroll
+    for (int cc = 0; cc < S; cc++) {
+      const int q = st * S + cc;
+      if (q + 1 < CPW) {
+        const uint32_t o = xoff(c0 + q + 1);
+#pragma unroll
+        for (int j = 0; j < 4; j++) xa[(q + 1) & 1][j] = bload8(rx, o + 16u * j);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[q & 1][j], dequant8(wg[b][cc][j], sg[b][cc]), ag, 0, 0, 0);
+        au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[q & 1][j], dequant8(wu[b][cc][j], su[b][cc]), au, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // refill the buffer this step consumed
+    if (st + 2 < NS) load_step(st + 2, b);
+  }
+  red[(2 * w) * 64 + lane] = ag;
+  red[(2 * w + 1) * 64 + lane] = au;
+  lds_sync();
+  gateup_epilogue(red, nw, it, 0, p, I, h, lo_plane);
+}
+
+template <int CPW>
+__global__ __launch_bounds__(1024) void down_stream_kernel(
+    const WorkItem* __restrict__ items, const DevMeta* __restrict__ meta,
+    const uint16_t* __restrict__ h, size_t lo_plane, int H, int I, size_t gateup_bytes,
+    float* __restrict__ yperm) {
+  constexpr int S = CPW < 2 ? CPW : 2;
+  constexpr int NS = CPW / S;
+  const int item = blockIdx.y;
+  if (item >= meta->n_items) return;
+  const WorkItem it = items[item];
+  const int q = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int KC = I / kAtomK;
+  const int c0 = w * CPW;
+  const uint8_t* abase = it.w + gateup_bytes + (size_t)(2 * q) * KC * kAtomBytes;
+  const uint8_t* bbase = abase + (size_t)KC * kAtomBytes;
+  extern __shared__ f32x4 red[];  // [waves][2][64], sized by the launch
+  const uint32_t lo_bytes = (uint32_t)(lo_plane * 2);
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(h, 2 * lo_bytes);
+
+  u32x4 wa[2][S], wb[2][S];
+  uint32_t sa[2][S], sb[2][S];
+  auto load_step = [&](int st, int b) {
+#pragma unroll
+    for (int cc = 0; cc < S; cc++) {
+      const int c = c0 + st * S + cc;
+      const size_t o = (size_t)(c < KC ? c : 0) * kAtomBytes;
+      wa[b][cc] = load_atom_data(abase + o, lane);
+      wb[b][cc] = load_atom_data(bbase + o, lane);
+      sa[b][cc] = load_scale(abase + o, lane);
+      sb[b][cc] = load_scale(bbase + o, lane);
+    }
+  };
+  load_step(0, 0);
+  if (NS > 1) load_step(1, 1);
+
+  const int m = lane & 15;
+  const bool mok = m < it.cnt;
+  const uint32_t hrow = (uint32_t)((it.pos0 + m) * I + 32 * (lane >> 4)) * 2u;
+  auto hoff = [&](int c) { return (mok && c < KC) ? hrow + (uint32_t)c * kAtomK * 2u : kOutOfRange; };
+  bf16x8 ahi[2][4], alo[2][4];  // h fragments (both planes), fetched one chunk ahead
+  {
+    const uint32_t o = hoff(c0);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      ahi[0][j] = bload8(rh, o + 16u * j);
+      alo[0][j] = bload8(rh, o == kOutOfRange ? o : o + lo_bytes + 16u * j);
+    }
+  }
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < NS; st++) {
+    const int b = st & 1;
+#pragma unroll
+    for (int cc = 0; cc < S; cc++) {
+      const int k = st * S + cc;
+      if (k + 1 < CPW) {
+        const uint32_t o = hoff(c0 + k + 1);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          ahi[(k + 1) & 1][j] = bload8(rh, o + 16u * j);
+          alo[(k + 1) & 1][j] = bload8(rh, o == kOutOfRange ? o : o + lo_bytes + 16u * j);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const bf16x8 b0 = dequant8(wa[b][cc][j], sa[b][cc]);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[k & 1][j], b0, acc0, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[k & 1][j], b0, acc0, 0, 0, 0);
+        const bf16x8 b1 = dequant8(wb[b][cc][j], sb[b][cc]);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[k & 1][j], b1, acc1, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[k & 1][j], b1, acc1, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (st + 2 < NS) load_step(st + 2, b);
+  }
+  red[(2 * w) * 64 + lane] = acc0;
+  red[(2 * w + 1) * 64 + lane] = acc1;
+  lds_sync();
+  down_epilogue(red, nw, it, 0, q, H, yperm);
 }
 
 // y[t] = sum_j g[t,j] * o[inv(t,j)] (+ shared row), fp32 in rank order, bf16 out.
@@ -314,6 +502,26 @@ Split split_k(int KC, int tiles, int max_cpw) {
   return {s, (KC + s - 1) / s};
 }
 
+// Chunks per wave of the streaming launches (1, 2, 4, 8 or 16), from timings
+// of every variant on the 35B-A3B, DSV4 and GLM decode shapes (K of 16, 32
+// and 48 chunks for gate/up, 4 and 16 for down):
+//  - gate/up: two chunks per wave while K needs at most 16 such waves (the
+//    whole K of a workgroup in flight at once), else 16 chunks per wave;
+//  - down: the fewest chunks per wave that keep a workgroup at <= 8 waves.
+constexpr int kMaxStreamTokens = 16;
+
+int stream_waves(int KC, int cpw) { return (KC + cpw - 1) / cpw; }
+
+int gateup_stream_cpw(int KC) {
+  if (KC <= 1) return 1;
+  return stream_waves(KC, 2) <= kMaxWaves ? 2 : 16;
+}
+int down_stream_cpw(int KC) {
+  int cpw = 1;
+  while (cpw < 16 && (cpw < KC ? stream_waves(KC, cpw) : 1) > 8) cpw *= 2;
+  return cpw;
+}
+
 }  // namespace
 
 static int items_for(const Ctx* c, int T) {
@@ -322,8 +530,25 @@ static int items_for(const Ctx* c, int T) {
 
 hipError_t launch_expert_gateup(const Ctx* c, const uint16_t* x, int T, hipStream_t st) {
   dim3 grid(c->cfg.inter / kAtomRows, items_for(c, T));
-  const Split s = split_k(c->cfg.hidden / kAtomK, grid.x * grid.y, 4);
   const size_t lo = (size_t)c->rows_max * c->cfg.inter;
+  const int KC = c->cfg.hidden / kAtomK;
+  if (T <= kMaxStreamTokens) {
+    const int cpw = gateup_stream_cpw(KC), waves = stream_waves(KC, cpw);
+#define GATEUP_S(N)                                                                      \
+  gateup_stream_kernel<N><<<grid, waves * 64, waves * 2 * 64 * 16, st>>>(              \
+      c->d_items, c->d_meta, c->d_tok, x, (uint32_t)T * c->cfg.hidden * 2, c->cfg.hidden, \
+      c->cfg.inter, c->d_h, lo)
+    switch (cpw) {
+      case 1: GATEUP_S(1); break;
+      case 2: GATEUP_S(2); break;
+      case 4: GATEUP_S(4); break;
+      case 8: GATEUP_S(8); break;
+      default: GATEUP_S(16); break;
+    }
+#undef GATEUP_S
+    return hipGetLastError();
+  }
+  const Split s = split_k(KC, grid.x * grid.y, 4);
 #define GATEUP(N)                                                                       \
   gateup_decode_kernel<N><<<grid, s.waves * 64, s.waves * 2 * 64 * 16, st>>>(        \
       c->d_items, c->d_meta, c->d_tok, x, (uint32_t)T * c->cfg.hidden * 2, c->cfg.hidden, \
@@ -340,9 +565,25 @@ hipError_t launch_expert_gateup(const Ctx* c, const uint16_t* x, int T, hipStrea
 
 hipError_t launch_expert_down(const Ctx* c, int T, hipStream_t st) {
   dim3 grid(c->cfg.hidden / (2 * kAtomRows), items_for(c, T));
-  const Split s = split_k(c->cfg.inter / kAtomK, grid.x * grid.y, 4);
   const size_t lo = (size_t)c->rows_max * c->cfg.inter;
   const size_t gub = gateup_section_bytes(c->cfg.hidden, c->cfg.inter);
+  const int KC = c->cfg.inter / kAtomK;
+  if (T <= kMaxStreamTokens) {
+    const int cpw = down_stream_cpw(KC), waves = stream_waves(KC, cpw);
+#define DOWN_S(N)                                                                  \
+  down_stream_kernel<N><<<grid, waves * 64, waves * 2 * 64 * 16, st>>>(          \
+      c->d_items, c->d_meta, c->d_h, lo, c->cfg.hidden, c->cfg.inter, gub, c->d_yperm)
+    switch (cpw) {
+      case 1: DOWN_S(1); break;
+      case 2: DOWN_S(2); break;
+      case 4: DOWN_S(4); break;
+      case 8: DOWN_S(8); break;
+      default: DOWN_S(16); break;
+    }
+#undef DOWN_S
+    return hipGetLastError();
+  }
+  const Split s = split_k(KC, grid.x * grid.y, 4);
 #define DOWN(N)                                                                       \
   down_decode_kernel<N><<<grid, s.waves * 64, s.waves * 2 * 64 * 16, st>>>(        \
       c->d_items, c->d_meta, c->d_h, lo, c->cfg.hidden, c->cfg.inter, gub,           \

@@ -39,7 +39,7 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kChunkTokens = 64;   // tokens per dispatch chunk (one wave)
 constexpr int kBM = 128;           // tokens per GEMM tile
-constexpr int kFragsPerWave = 4;   // 16-row weight fragments per wave
+constexpr int kFragsPerWave = 8;   // weight atoms (16 columns each) per wave
 constexpr uint32_t kOOB = 0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
@@ -242,11 +242,14 @@ __device__ __forceinline__ void tile_of_block(int nbn, int* ti, int* nb) {
   *nb = j % nbn;
 }
 
-// Grouped GEMM tile: C[128 token rows][256 columns] over K in chunks of 128,
-// on 8 waves (two per SIMD): wave w owns columns 64(w%4).. and the 16-row
+// Grouped GEMM tile: C[128 token rows][512 columns] over K in chunks of 128,
+// on 8 waves (two per SIMD): wave w owns columns 128(w%4).. and the 16-row
 // fragments 2i + w/4 (i < 4) -- interleaved, so that the two waves sharing
-// a SIMD hold nearly equal row counts in a partly filled tile -- as 4 x 4
-// fragments of the 16x16x32 bf16 MFMA.  Both operands go straight from
+// a SIMD hold nearly equal row counts in a partly filled tile -- as 4 x 8
+// fragments of the 16x16x32 bf16 MFMA.  512 columns read each gathered
+// token row once per 512 output columns: the token rows are the larger
+// operand (bf16 against 4-bit weights) and, re-read from L2 by every column
+// block, dominate what the loads move.  Both operands go straight from
 // global memory into LDS with buffer-to-LDS loads, so nothing but the
 // accumulators lives across chunks:
 //  - A (bf16 token rows, gathered): fragment mf is 4 KB, one 256-byte chunk
@@ -257,18 +260,17 @@ __device__ __forceinline__ void tile_of_block(int nbn, int* ti, int* nb) {
 //    needs the elements its weight fragment covers, 32(l/16) + 8j (MX block
 //    l/16, sub-block j), i.e. piece 4(l/16) + j of row l%16; the swizzle
 //    puts the 16 rows' pieces in 16 different bank groups;
-//  - B (the tile's 16 MXFP4 weight atoms of the chunk, 4 per column
+//  - B (the tile's 32 MXFP4 weight atoms of the chunk, 8 per column
 //    quarter): the 1 KB of codes of atom t at block t (lane order, as
 //    stored), then every atom's 64 scale bytes packed at 64t (one 4-byte
 //    load per lane fetches the scales of four atoms); dequantised in
-//    registers after the read.
+//    registers right before its MFMAs.
 // The loads are split by source.  Waves 0-3 fetch A (rows 32w .. 32w+31:
-// 8 loads per step); those are mostly L2 hits, since the column
-// blocks of a token tile run together on one XCD, and one step of lead is
-// enough.  Waves 4-7 fetch B (atoms 4(w-4) .. +3: 5 loads per chunk), which
-// streams from HBM and is fetched kStagesB - 1 chunks ahead.  vmcnt counts
-// only the wave's own loads, so the deep weight prefetch never lengthens the
-// short A wait.  Per step every wave waits for its own loads of the step,
+// 8 loads per step), mostly L2 hits since the column blocks of a token tile
+// run together on one XCD; waves 4-7 fetch B (atoms 8(w-4) .. +7: 10 loads
+// per chunk), which streams from HBM.  Both are fetched one step ahead (a
+// step of 128 x 512 x 128 is long enough to cover HBM latency), and vmcnt
+// counts only the wave's own loads.  Per step every wave waits for its own loads of the step,
 // one barrier makes them visible and frees the stages the previous step
 // read, the next loads are issued and the step is computed.  Loads past the
 // end go to an out-of-range offset (zeros, no memory traffic) into a stage
@@ -278,14 +280,14 @@ __device__ __forceinline__ void tile_of_block(int nbn, int* ti, int* nb) {
 // including the prefetched ones.
 constexpr int kGemmWaves = 8;
 constexpr int kStagesA = 2;
-constexpr int kStagesB = 4;
-constexpr int kAtomsPerTile = 16;                                   // 256 columns
+constexpr int kStagesB = 2;
+constexpr int kAtomsPerTile = 32;                                   // 512 columns
 constexpr int kLdsA = kBM * kAtomK * 2;                             // 32 KB per A stage
-constexpr int kLdsBc = kAtomsPerTile * kAtomData;                   // 16 KB of codes
-constexpr int kLdsBStage = kLdsBc + kAtomsPerTile * 64;             // + 1 KB of scales
+constexpr int kLdsBc = kAtomsPerTile * kAtomData;                   // 32 KB of codes
+constexpr int kLdsBStage = kLdsBc + kAtomsPerTile * 64;             // + 2 KB of scales
 constexpr int kLdsGemm = kStagesA * kLdsA + kStagesB * kLdsBStage;  // 132 KB
-constexpr int kVmemA = 8;  // per A wave and step: 2 row blocks x 4 pieces
-constexpr int kVmemB = 5;  // per B wave and chunk: 4 code loads, 1 scale load
+constexpr int kVmemA = 8;   // per A wave and step: 8 loads of 4 rows
+constexpr int kVmemB = 10;  // per B wave and chunk: 8 code loads, 2 scale loads
 static_assert(kLdsGemm <= 160 * 1024, "LDS per CU");
 static_assert(kStagesA >= 2 && kStagesB >= 2, "one stage in flight at least");
 
@@ -304,9 +306,9 @@ struct GemmTile {
   uint32_t aoff[8];      // A waves: this lane's piece of row 32w + 4i + l/16 for
                          // load i (row start + swizzled piece), or kOOB past
                          // the valid rows
-  uint32_t woff[4];      // B waves: atom 4(w-4) + t, chunk 0
-  uint32_t soff;         // B waves: this lane's scale dword (atom 4(w-4) + l/16,
-                         // bytes 4(l%16) ..), chunk 0
+  uint32_t woff[8];      // B waves: atom 8(w-4) + t, chunk 0
+  uint32_t soff[2];      // B waves: this lane's scale dwords (atoms
+                         // 8(w-4) + 4h + l/16, bytes 4(l%16) ..), chunk 0
 };
 
 // Buffer-to-LDS loads: `bytes` per lane from rsrc + voffset into LDS at
@@ -369,9 +371,11 @@ __device__ __forceinline__ void gemm_tile_mf(const GemmTile& gt, __amdgpu_buffer
     const bool in = c < KC;
     const uint32_t k = (uint32_t)chunk(c) * kAtomBytes;
 #pragma unroll
-    for (int t = 0; t < 4; t++)
-      lds_load16(rw, in ? gt.woff[t] + k + 16u * lane : kOOB, buf + (4 * u + t) * kAtomData);
-    lds_load4(rw, in ? gt.soff + k : kOOB, buf + kLdsBc + 4 * u * 64);
+    for (int t = 0; t < 8; t++)
+      lds_load16(rw, in ? gt.woff[t] + k + 16u * lane : kOOB, buf + (8 * u + t) * kAtomData);
+#pragma unroll
+    for (int hh = 0; hh < 2; hh++)
+      lds_load4(rw, in ? gt.soff[hh] + k : kOOB, buf + kLdsBc + (8 * u + 4 * hh) * 64);
   };
   // One step: the A fragments and dequantised weights of K step j+1 are
   // fetched while the MFMAs of step j run.
@@ -387,25 +391,26 @@ __device__ __forceinline__ void gemm_tile_mf(const GemmTile& gt, __amdgpu_buffer
         wd[f] = *reinterpret_cast<const u32x4*>(bbuf + atom * kAtomData + 16 * lane);
         sd[f] = bbuf[kLdsBc + atom * 64 + lane];
       }
-      bf16x8 a[2][MF], b[2][kFragsPerWave];
+      bf16x8 a[2][MF];
       auto fetch = [&](int j, int q) {
         const int r = lane & 15;
         const int slot = ((4 * (lane >> 4) + j) ^ r) & 15;
 #pragma unroll
         for (int i = 0; i < MF; i++)
           a[q][i] = *reinterpret_cast<const bf16x8*>(abuf + (2 * i + mh) * 4096 + 256 * r + 16 * slot);
-#pragma unroll
-        for (int f = 0; f < kFragsPerWave; f++) b[q][f] = dequant8(wd[f][j], sd[f]);
       };
       fetch(0, 0);
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         if (j + 1 < 4) fetch(j + 1, (j + 1) & 1);
+        // each atom's weights are dequantised right before its MFMAs
 #pragma unroll
-        for (int i = 0; i < MF; i++)
+        for (int f = 0; f < kFragsPerWave; f++) {
+          const bf16x8 b = dequant8(wd[f][j], sd[f]);
 #pragma unroll
-          for (int f = 0; f < kFragsPerWave; f++)
-            acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j & 1][i], b[j & 1][f], acc[i][f], 0, 0, 0);
+          for (int i = 0; i < MF; i++)
+            acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j & 1][i], b, acc[i][f], 0, 0, 0);
+        }
       }
     }
   };
@@ -436,15 +441,15 @@ __device__ __forceinline__ void gemm_tile_mf(const GemmTile& gt, __amdgpu_buffer
 }
 
 // A wave w loads rows 32w .. 32w+31 (offsets set by the kernel); B wave
-// w loads tile atoms 4(w-4) .. +3, which are weight row groups rg0 .. rg0+3.
-// Row groups at or past ngroups (the last, partial column block of the down
-// GEMM) read group 0 instead: their columns are never stored.
+// w loads tile atoms 8(w-4) .. +7, which are weight row groups rg0 .. rg0+7.
+// Row groups at or past ngroups (the last, partial column block) read group
+// 0 instead: their columns are never stored.
 __device__ __forceinline__ void clear_loads(GemmTile& gt) {
 #pragma unroll
   for (int i = 0; i < 8; i++) gt.aoff[i] = kOOB;
 #pragma unroll
-  for (int t = 0; t < 4; t++) gt.woff[t] = 0;
-  gt.soff = 0;
+  for (int t = 0; t < 8; t++) gt.woff[t] = 0;
+  gt.soff[0] = gt.soff[1] = 0;
 }
 // Byte offset, within a 256-byte chunk row, of the piece that lane l loads
 // for tile row r: it lands in LDS slot l % 16 of that row, which holds
@@ -455,9 +460,12 @@ __device__ __forceinline__ uint32_t a_piece(int r, int lane) {
 __device__ __forceinline__ void set_weight_loads(GemmTile& gt, int rg0, int lane, int ngroups) {
   const uint32_t group_bytes = (uint32_t)gt.KC * kAtomBytes;
 #pragma unroll
-  for (int t = 0; t < 4; t++) gt.woff[t] = (uint32_t)(rg0 + t < ngroups ? rg0 + t : 0) * group_bytes;
-  const int rl = rg0 + (lane >> 4);
-  gt.soff = (uint32_t)(rl < ngroups ? rl : 0) * group_bytes + kAtomData + 4u * (lane & 15);
+  for (int t = 0; t < 8; t++) gt.woff[t] = (uint32_t)(rg0 + t < ngroups ? rg0 + t : 0) * group_bytes;
+#pragma unroll
+  for (int hh = 0; hh < 2; hh++) {
+    const int rl = rg0 + 4 * hh + (lane >> 4);
+    gt.soff[hh] = (uint32_t)(rl < ngroups ? rl : 0) * group_bytes + kAtomData + 4u * (lane & 15);
+  }
 }
 
 struct GroupArgs {
@@ -492,6 +500,7 @@ template <int MF>
 __device__ __forceinline__ void gateup_tile(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
                                             uint8_t* lds, uint16_t* __restrict__ h,
                                             size_t lo_plane, int I, size_t row0, int p0) {
+  const int npairs = I / kAtomRows;
   const int lane = threadIdx.x & 63, mh = wave_id() >> 2;
   f32x4 acc[MF > 0 ? MF : 1][kFragsPerWave];
 #pragma unroll
@@ -502,11 +511,11 @@ __device__ __forceinline__ void gateup_tile(const GemmTile& gt, __amdgpu_buffer_
 #pragma unroll
   for (int i = 0; i < MF; i++) {
 #pragma unroll
-    for (int q = 0; q < 2; q++) {
+    for (int q = 0; q < kFragsPerWave / 2; q++) {
 #pragma unroll
       for (int r = 0; r < 4; r++) {
         const int m = (2 * i + mh) * 16 + 4 * (lane >> 4) + r;
-        if (m < gt.rows) {
+        if (m < gt.rows && p0 + q < npairs) {
           const float hv = silu(acc[i][2 * q][r]) * acc[i][2 * q + 1][r];
           const uint16_t hi = f32_to_bf16_rne(hv);
           const size_t o = (row0 + m) * I + (p0 + q) * 16 + (lane & 15);
@@ -541,8 +550,10 @@ __device__ __forceinline__ void down_tile(const GemmTile& gt, __amdgpu_buffer_rs
       }
 }
 
-// Gate/up + SwiGLU.  N-block nb covers row pairs nb*8 .. nb*8+7 (gate, up);
-// column quarter nq takes pairs nb*8 + 2nq and +1 (atoms g0, u0, g1, u1).
+// Gate/up + SwiGLU.  N-block nb covers row pairs nb*16 .. nb*16+15 (gate,
+// up; pairs past I/16 in the last block are computed on group 0 and not
+// stored); column quarter nq takes pairs nb*16 + 4nq .. +3 (atoms g0, u0,
+// g1, u1, ...).
 // h leaves as two bf16 planes, hi = RNE(h) and lo = RNE(h - hi) (about 16
 // significant bits), both of which the down GEMM contracts.
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void gateup_prefill_kernel(
@@ -572,20 +583,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
       if (r < gt.rows) gt.aoff[i] = (uint32_t)g.tok[pos0 + m0 + r] * (uint32_t)H * 2u + a_piece(r, lane);
     }
   } else {
-    // Tile atom a (column quarter a/4, fragment a%4) is row group 16nb + a:
-    // pair nb*8 + 2(a/4) + (a%4)/2, gate if a is even, up if odd.
-    set_weight_loads(gt, nb * 16 + 4 * (w - 4), lane, 2 * I / kAtomRows);
+    // Tile atom a (column quarter a/8, atom a%8 of it) is row group 32nb + a:
+    // pair 16nb + a/2, gate if a is even, up if odd.
+    set_weight_loads(gt, nb * 32 + 8 * (w - 4), lane, 2 * I / kAtomRows);
   }
   const __amdgpu_buffer_rsrc_t ra = rsrc(x, x_bytes);
   const size_t row0 = (size_t)(pos0 + m0);
-  const int p0 = nb * 8 + 2 * nq;
+  const int p0 = nb * 16 + 4 * nq;
 #define GU(N) gateup_tile<N>(gt, ra, lds, h, lo_plane, I, row0, p0)
   MOE_MF_SWITCH(wave_mfrags(gt.rows), GU)
 #undef GU
 }
 
-// Down.  N-block nb covers row groups nb*16 .. nb*16+15 of H (256 columns);
-// column quarter nq takes row groups nb*16 + 4nq .. +3.
+// Down.  N-block nb covers row groups nb*32 .. nb*32+31 of H (512 columns;
+// the last block may be partial); column quarter nq takes row groups
+// nb*32 + 8nq .. +7.
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void down_prefill_kernel(
     GroupArgs g, const uint16_t* h, uint32_t h_bytes, uint32_t lo_plane_bytes, int H, int I,
     int nbn, size_t gateup_bytes, float* __restrict__ yperm) {
@@ -614,11 +626,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
       if (r < gt.rows) gt.aoff[i] = (uint32_t)(pos0 + m0 + r) * (uint32_t)I * 2u + a_piece(r, lane);
     }
   } else {
-    set_weight_loads(gt, nb * 16 + 4 * (w - 4), lane, ngroups);  // tile atom a: row group 16nb + a
+    set_weight_loads(gt, nb * 32 + 8 * (w - 4), lane, ngroups);  // tile atom a: row group 32nb + a
   }
   const __amdgpu_buffer_rsrc_t ra = rsrc(h, h_bytes);
   const size_t row0 = (size_t)(pos0 + m0);
-  const int rg0 = nb * 16 + 4 * nq;
+  const int rg0 = nb * 32 + 8 * nq;
 #define DN(N) down_tile<N>(gt, ra, lds, yperm, H, row0, rg0, ngroups)
   MOE_MF_SWITCH(wave_mfrags(gt.rows), DN)
 #undef DN
@@ -768,7 +780,7 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
       else
         tr = {nullptr, nullptr, nullptr};
     }
-    const int nbn_gu = I / (16 * 8), nbn_dn = (H + 255) / 256;
+    const int nbn_gu = (2 * I + 511) / 512, nbn_dn = (H + 511) / 512;
     const size_t lo_plane = (size_t)p->Tmax * (k + 1) * I;  // elements
     gateup_prefill_kernel<<<p->max_tiles * nbn_gu, 64 * kGemmWaves, 0, st>>>(
         ga, x, (uint32_t)T * H * 2, H, I, nbn_gu, p->h, lo_plane);

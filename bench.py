@@ -168,6 +168,14 @@ def run_decode(wl, T, steps, warmup, seed=0, eng=None):
                 h2d_gbs=st["bytes_h2d"] / (elapsed * 1e9))
 
 
+def decode_kernels(T):
+    """Names of the decode expert kernels the library launches for T tokens:
+    the streaming variants up to 16 tokens per call, else the others."""
+    if T <= 16:
+        return "gateup_stream_kernel", "down_stream_kernel"
+    return "gateup_decode_kernel", "down_decode_kernel"
+
+
 def roofline_entry(name, gbs, us, nbytes, launches):
     return {"kernel": name, "bound": "hbm",
             "achieved": None if gbs is None else round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -232,9 +240,9 @@ def run_dsv4(prefill_steps, decode_steps, decode_warmup, seed=0):
         out["dsv4_decode_T1"] = {
             "tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 4),
             "hit_rate": round(r["hit_rate"], 4), "h2d_gbs": round(r["h2d_gbs"], 2),
-            "roofline": [roofline_entry("gateup_decode_kernel", r["gateup_gbs"], r["gateup_us"],
+            "roofline": [roofline_entry(decode_kernels(1)[0], r["gateup_gbs"], r["gateup_us"],
                                         r["gateup_bytes"], r["launches"]),
-                         roofline_entry("down_decode_kernel", r["down_gbs"], r["down_us"],
+                         roofline_entry(decode_kernels(1)[1], r["down_gbs"], r["down_us"],
                                         r["down_bytes"], r["launches"])]}
     eng.close()
     return out
@@ -331,10 +339,11 @@ def main():
                                "down_gbs": r["down_gbs"] and round(r["down_gbs"], 1),
                                "h2d_gbs": round(r["h2d_gbs"], 2)}
     sh = wl.shape
-    roof = roofline_entry("gateup_decode_kernel", res["gateup_gbs"], res["gateup_us"],
-                          res["gateup_bytes"], res["launches"])
-    roof["traffic"] = traffic_from_profile("gateup_decode_kernel", f"{wl.name}_T{T}")
-    roof["other_kernels"] = [roofline_entry("down_decode_kernel", res["down_gbs"], res["down_us"],
+    kgu, kdn = decode_kernels(T)
+    roof = roofline_entry(kgu, res["gateup_gbs"], res["gateup_us"], res["gateup_bytes"],
+                          res["launches"])
+    roof["traffic"] = traffic_from_profile(kgu, f"{wl.name}_T{T}")
+    roof["other_kernels"] = [roofline_entry(kdn, res["down_gbs"], res["down_us"],
                                             res["down_bytes"], res["launches"])]
     roof["expert_ffn_pair_gbs"] = res["ffn_gbs"] and round(res["ffn_gbs"], 1)
     line = {

@@ -133,8 +133,14 @@ __global__ __launch_bounds__(1024) void gateup_decode_kernel(
     const int32_t* __restrict__ tok, const uint16_t* __restrict__ x, uint32_t x_bytes, int H,
     int I, uint16_t* __restrict__ h, size_t lo_plane) {
   const int item = blockIdx.y;
-  if (item >= meta->n_items) return;
+  // Both loads at once (the grid covers the largest possible item count and
+  // items[] has that many entries): one memory latency before the weight
+  // loads instead of two.  The exit test reads the whole item (a real item
+  // has cnt >= 1 and a weight pointer) so the compiler cannot sink the item
+  // load below it.
+  const int n_items = meta->n_items;
   const WorkItem it = items[item];
+  if ((item >= n_items) | (it.cnt < 1) | (it.w == nullptr)) return;
   const int p = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int KC = H / kAtomK;
@@ -223,8 +229,14 @@ __global__ __launch_bounds__(1024) void down_decode_kernel(
     const uint16_t* __restrict__ h, size_t lo_plane, int H, int I, size_t gateup_bytes,
     float* __restrict__ yperm) {
   const int item = blockIdx.y;
-  if (item >= meta->n_items) return;
+  // Both loads at once (the grid covers the largest possible item count and
+  // items[] has that many entries): one memory latency before the weight
+  // loads instead of two.  The exit test reads the whole item (a real item
+  // has cnt >= 1 and a weight pointer) so the compiler cannot sink the item
+  // load below it.
+  const int n_items = meta->n_items;
   const WorkItem it = items[item];
+  if ((item >= n_items) | (it.cnt < 1) | (it.w == nullptr)) return;
   const int q = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int KC = I / kAtomK;
@@ -316,8 +328,14 @@ __global__ __launch_bounds__(1024) void gateup_stream_kernel(
   constexpr int S = CPW < 2 ? CPW : 2;  // chunks per step
   constexpr int NS = CPW / S;           // steps
   const int item = blockIdx.y;
-  if (item >= meta->n_items) return;
+  // Both loads at once (the grid covers the largest possible item count and
+  // items[] has that many entries): one memory latency before the weight
+  // loads instead of two.  The exit test reads the whole item (a real item
+  // has cnt >= 1 and a weight pointer) so the compiler cannot sink the item
+  // load below it.
+  const int n_items = meta->n_items;
   const WorkItem it = items[item];
+  if ((item >= n_items) | (it.cnt < 1) | (it.w == nullptr)) return;
   const int p = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int KC = H / kAtomK;
@@ -396,8 +414,14 @@ __global__ __launch_bounds__(1024) void down_stream_kernel(
   constexpr int S = CPW < 2 ? CPW : 2;
   constexpr int NS = CPW / S;
   const int item = blockIdx.y;
-  if (item >= meta->n_items) return;
+  // Both loads at once (the grid covers the largest possible item count and
+  // items[] has that many entries): one memory latency before the weight
+  // loads instead of two.  The exit test reads the whole item (a real item
+  // has cnt >= 1 and a weight pointer) so the compiler cannot sink the item
+  // load below it.
+  const int n_items = meta->n_items;
   const WorkItem it = items[item];
+  if ((item >= n_items) | (it.cnt < 1) | (it.w == nullptr)) return;
   const int q = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int KC = I / kAtomK;

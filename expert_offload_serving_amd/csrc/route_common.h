@@ -146,30 +146,33 @@ __device__ void topk_select(const TopkArgs& a, int t, uint32_t (&keys)[NK], int*
   uint32_t bv;
   int bi;
   best_key<NK>(keys, bv, bi);
+  // Round j's expert and logit stay in lane j; no branch on the winner lane,
+  // one store per output at the end.
+  int my_e = 0;
   float my_l = 0.f, l0 = 0.f;
   for (int j = 0; j < k; j++) {
     const uint32_t m = wave_max_u32(bv);
     const uint64_t holders = __ballot(bv == m);
     int e;
-    if (__popcll(holders) == 1) {
+    if (__popcll(holders) == 1)
       e = __builtin_amdgcn_readlane(lane + 64 * bi, (int)__builtin_ctzll(holders));
-    } else {
+    else  // equal logits in several lanes: the lowest expert
       e = (int)wave_min_u32(bv == m ? (uint32_t)(lane + 64 * bi) : 0xFFFFFFFFu);
-    }
-    if (lane == (e & 63)) {  // the winner lane
+    const bool winner = lane == (e & 63);
 #pragma unroll
-      for (int i = 0; i < NK; i++)
-        if (i == (e >> 6)) keys[i] = 0u;
-      best_key<NK>(keys, bv, bi);
-    }
+    for (int i = 0; i < NK; i++) keys[i] = (winner && i == (e >> 6)) ? 0u : keys[i];
+    best_key<NK>(keys, bv, bi);
     const float l = from_ordered_bits(m);
-    if (lane == j) my_l = l;
-    if (j == 0) l0 = l;
-    if (lane == 0) {
-      a.ids[t * k + j] = e;
-      if (s_ids) s_ids[t * k + j] = e;
-      if (a.user_ids) a.user_ids[t * k + j] = e;
+    if (lane == j) {
+      my_e = e;
+      my_l = l;
     }
+    if (j == 0) l0 = l;
+  }
+  if (lane < k) {
+    a.ids[t * k + lane] = my_e;
+    if (s_ids) s_ids[t * k + lane] = my_e;
+    if (a.user_ids) a.user_ids[t * k + lane] = my_e;
   }
   double z = 0.0, denom;
   if (a.renorm) {

@@ -99,7 +99,12 @@ def test_ragged_token_counts(T):
 
 @pytest.mark.parametrize("kw", [dict(k=1), dict(E=64, k=16), dict(E=200, k=6), dict(renormalize=False),
                                 dict(shared=True), dict(H=384, I=128), dict(H=128, I=128, E=4, k=2),
-                                dict(layers=3, E=16, k=3)])
+                                dict(layers=3, E=16, k=3),
+                                # split of K in the expert kernels: down with 4 chunks per
+                                # wave (K = 24 chunks), gate/up with 16 chunks per wave and
+                                # a last wave past K (36 chunks), odd chunk counts (9 and 5)
+                                dict(H=256, I=3072, E=4, k=2), dict(H=4608, I=128, E=4, k=2),
+                                dict(H=1152, I=640, E=8, k=2)])
 def test_shape_variants(kw):
     sh = H.small_shape(**kw)
     T = 9

@@ -404,12 +404,16 @@ __device__ __forceinline__ void gemm_tile_mf(const GemmTile& gt, __amdgpu_buffer
       for (int j = 0; j < 4; j++) {
         if (j + 1 < 4) fetch(j + 1, (j + 1) & 1);
         // each atom's weights are dequantised right before its MFMAs
+        // two operand registers in turn: the convert for atom f+1 never
+        // waits for the MFMAs still reading atom f's operand
+        bf16x8 bb[2];
+        bb[0] = dequant8(wd[0][j], sd[0]);
 #pragma unroll
         for (int f = 0; f < kFragsPerWave; f++) {
-          const bf16x8 b = dequant8(wd[f][j], sd[f]);
+          if (f + 1 < kFragsPerWave) bb[(f + 1) & 1] = dequant8(wd[f + 1][j], sd[f + 1]);
 #pragma unroll
           for (int i = 0; i < MF; i++)
-            acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j & 1][i], b, acc[i][f], 0, 0, 0);
+            acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j & 1][i], bb[f & 1], acc[i][f], 0, 0, 0);
         }
       }
     }

@@ -5,13 +5,16 @@
 // MX block), dequantised in registers with the gfx950 scaled FP4 -> bf16
 // convert, and multiplied on v_mfma_f32_16x16x32_bf16 with up to 16 tokens as
 // the A operand.  The kernels are HBM-bound, so the design is about bytes in
-// flight: a workgroup owns one 16-row output tile (a gate/up pair, or a down
-// row group) of one expert and splits K over up to 16 waves; every wave
-// issues all of its weight and activation loads before its first MFMA, and
-// the waves' partial tiles are summed through LDS in a fixed order (results
-// do not depend on where an expert's weights live).  MFMA replaces the
-// per-lane dot products and wave reductions of a VALU GEMV, keeping VALU work
-// per weight byte flat in the token count.
+// flight: a workgroup owns one output tile (a 16-row gate/up pair, or two
+// 16-row down row groups) of one expert and splits K over up to 16 waves,
+// and the waves' partial tiles are summed through LDS in a fixed order
+// (results do not depend on where an expert's weights live).  Calls of up
+// to 16 tokens use the streaming kernels (a wave walks its K range in steps
+// of two chunks with two steps of loads in flight; chunks per wave set per
+// shape by the launcher); larger calls use the kernels that issue all of a
+// wave's loads before its first MFMA and loop over 16-token M tiles.  MFMA
+// replaces the per-lane dot products and wave reductions of a VALU GEMV,
+// keeping VALU work per weight byte flat in the token count.
 //
 // FFN: o = W_d (silu(W_g x) * (W_u x)); the pages name MXFP4 experts
 // (jansverre.net FreeToken article, section "Hvor raskt kjører modellene?")
@@ -122,11 +125,11 @@ __device__ __forceinline__ void down_epilogue(const f32x4* red, int nw, const Wo
   }
 }
 
-// Gate/up + SwiGLU.  Block (pair p, item): 16 gate and 16 up rows of one
-// expert; wave w takes K chunks [w*CPW, w*CPW+CPW).  M tiles of 16 tokens
-// are processed one after another (weights re-read from L2 after the first).
-// Small workgroups that finish independently keep a CU's memory pipeline
-// full better than large ones that must be resident as a whole.
+// Gate/up + SwiGLU for calls of more than 16 tokens.  Block (pair p, item):
+// 16 gate and 16 up rows of one expert; wave w takes K chunks
+// [w*CPW, w*CPW+CPW), all loaded before its first MFMA.  M tiles of 16
+// tokens are processed one after another with the weights held in
+// registers.
 template <int CPW>
 __global__ __launch_bounds__(1024) void gateup_decode_kernel(
     const WorkItem* __restrict__ items, const DevMeta* __restrict__ meta,
@@ -220,9 +223,10 @@ __global__ __launch_bounds__(1024) void gateup_decode_kernel(
   }
 }
 
-// Down projection.  Block (row-group pair q, item): rows [32q, 32q+32) of H
-// of one expert, as two 16-row groups that share every h fragment; waves
-// split K = I; each weight fragment meets both h planes.
+// Down projection for calls of more than 16 tokens.  Block (row-group pair
+// q, item): rows [32q, 32q+32) of H of one expert, as two 16-row groups that
+// share every h fragment; waves split K = I; each weight fragment meets both
+// h planes.
 template <int CPW>
 __global__ __launch_bounds__(1024) void down_decode_kernel(
     const WorkItem* __restrict__ items, const DevMeta* __restrict__ meta,

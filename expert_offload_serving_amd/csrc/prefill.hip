@@ -59,7 +59,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
-__device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
+// silu(a) = a / (1 + e^-a) on the hardware exp2 and reciprocal (about 1 ulp
+// each; the GEMM epilogue evaluates it for every h element, and the IEEE
+// divide and library exp cost about 30 instructions per value).  Very
+// negative a gives e^-a = inf and a * rcp(inf) = -0; the inputs are finite.
+__device__ __forceinline__ float silu(float a) {
+  const float e = __builtin_amdgcn_exp2f(-a * 1.4426950408889634f);
+  return a * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // ---------------------------------------------------------------- router
 // logits[t][e] = fp32(sum_h x[t][h] W_r[h][e] + bias), fp64 products and

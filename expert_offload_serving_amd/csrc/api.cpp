@@ -189,12 +189,14 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     return fail(MOE_ERR_UNSUPPORTED, "cache_slots above 4096");
   if (f.max_prefill_tokens > (1 << 20))
     return fail(MOE_ERR_INVALID_ARG, "max_prefill_tokens too large");
-  // The prefill kernels address x (T x H bf16) and h (two bf16 planes of
-  // T*(k+1) x I) through 32-bit buffer offsets.
+  // The prefill kernels address x (T x H bf16), h (a bf16 plane of
+  // T*(k+1) x I) and h's low-order records through 32-bit buffer offsets.
   if ((int64_t)f.max_prefill_tokens * f.hidden * 2 >= (int64_t(1) << 31) ||
-      (int64_t)f.max_prefill_tokens * (f.top_k + 1) * f.inter * 4 >= (int64_t(1) << 31))
+      (int64_t)f.max_prefill_tokens * (f.top_k + 1) * f.inter * 2 >= (int64_t(1) << 31) ||
+      (int64_t)prefill_lo_bytes(f.max_prefill_tokens, f.top_k, f.n_experts, f.inter) >=
+          (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED,
-                "max_prefill_tokens too large for this shape (x or the h planes reach 2 GiB)");
+                "max_prefill_tokens too large for this shape (x or h reach 2 GiB)");
 
   Ctx* c = new (std::nothrow) Ctx();
   if (!c) return fail(MOE_ERR_OOM, "context allocation");

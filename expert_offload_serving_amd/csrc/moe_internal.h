@@ -200,6 +200,8 @@ hipError_t launch_combine_rows(const float* yperm, const int32_t* inv, const flo
 hipEvent_t timing_event(Ctx* c);
 
 // prefill
+int prefill_max_tiles(int T, int k, int E);
+size_t prefill_lo_bytes(int T, int k, int E, int I);
 hipError_t prefill_inspect(Ctx* c, int32_t* T, int32_t* ids, float* gates);
 hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* x, int T,
                            const float* const* bias, void* const* y, float* const* y32,

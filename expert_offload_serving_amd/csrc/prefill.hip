@@ -28,9 +28,20 @@ struct Prefill {
   int32_t* tok = nullptr;      // [Tmax*k + Tmax]
   int2* tiles = nullptr;       // [max_tiles]: (group, first row)
   int32_t* n_tiles = nullptr;  // [1]
-  uint16_t* h = nullptr;       // bf16 [rows][I]
+  uint16_t* h = nullptr;       // bf16 [rows][I]: h rounded to bf16
+  uint8_t* hlo = nullptr;      // low-order records of h: [max_tiles][I/128][8][1664]
   float* yperm = nullptr;      // [rows][H]
 };
+
+// Tiles of 128 rows: every group's partial tile plus the whole rows, rounded
+// up to a multiple of 8 (the launch deals tiles to the 8 XCDs).
+int prefill_max_tiles(int T, int k, int E) {
+  return ((T * k + T + 127) / 128 + E + 1 + 7) / 8 * 8;
+}
+// Bytes of the low-order records of h: 13 KB per tile and K chunk of 128.
+size_t prefill_lo_bytes(int T, int k, int E, int I) {
+  return (size_t)prefill_max_tiles(T, k, E) * (size_t)(I / 128) * (8 * 1664);
+}
 
 namespace {
 
@@ -271,20 +282,40 @@ __device__ __forceinline__ void tile_of_block(int nbn, int* ti, int* nb) {
 //    quarter): the 1 KB of codes of atom t at block t (lane order, as
 //    stored), then every atom's 64 scale bytes packed at 64t (one 4-byte
 //    load per lane fetches the scales of four atoms); dequantised in
-//    registers right before its MFMAs.
+//    registers right before its MFMAs;
+//  - in the down GEMM, the low-order piece of h (see below): the tile's 13 KB
+//    record of the chunk, contracted once per chunk with the scaled
+//    fp6 x fp4 MFMA on the weight codes as they are stored.
 // The loads are split by source.  Waves 0-3 fetch A (rows 32w .. 32w+31:
-// 8 loads per step), mostly L2 hits since the column blocks of a token tile
-// run together on one XCD; waves 4-7 fetch B (atoms 8(w-4) .. +7: 10 loads
-// per chunk), which streams from HBM.  Both are fetched one step ahead (a
-// step of 128 x 512 x 128 is long enough to cover HBM latency), and vmcnt
-// counts only the wave's own loads.  Per step every wave waits for its own loads of the step,
-// one barrier makes them visible and frees the stages the previous step
-// read, the next loads are issued and the step is computed.  Loads past the
-// end go to an out-of-range offset (zeros, no memory traffic) into a stage
-// no one reads any more, so the wait counts never change.  The barrier is a
-// bare s_barrier with a compiler memory clobber: a workgroup fence there
-// would make the compiler drain every buffer-to-LDS load in flight,
-// including the prefetched ones.
+// 8 loads per step, plus 3-4 loads of the low-order record in the down
+// GEMM), mostly L2 hits since the column blocks of a token tile run together
+// on one XCD; waves 4-7 fetch B (atoms 8(w-4) .. +7: 10 loads per chunk),
+// which streams from HBM.  Both are fetched one step ahead.  The address
+// unit takes a 1 KB buffer-to-LDS load about every 25 cycles and a wave
+// that issues while it is busy stalls, so the two kinds are issued apart:
+// the A waves right after the step's barrier, the B waves after the MFMAs of
+// their first K step (their loads then no longer queue behind the A loads,
+// and the A wave on the same SIMD computes meanwhile).  Per step every wave
+// waits for its own loads of the step, one barrier makes them visible and
+// frees the stages the previous step read.  Loads past the end go to an
+// out-of-range offset (zeros, no memory traffic) into a stage no one reads
+// any more, so the wait counts never change.  The barrier is a bare
+// s_barrier with a compiler memory clobber: a workgroup fence there would
+// make the compiler drain every buffer-to-LDS load in flight, including the
+// prefetched ones.
+//
+// h between the two GEMMs: hi = RNE_bf16(h) as a bf16 plane [rows][I], and
+// the remainder h - hi (at most 2^-9 |h|) as a block-scaled fp6 (E2M3)
+// piece: per row and block of 32 columns one power-of-two scale 2^E with
+// the block's largest remainder at most 7.5 * 2^E, each element RNE to the
+// E2M3 grid.  The remainder piece errs by at most 2^-5 of its block's
+// largest remainder, so h is carried to about 2^-14 of its block's largest
+// value; the scaled MFMA contracts it at a quarter of the cost of a second
+// bf16 plane.  Records: per (tile, K chunk of the down GEMM, 16-row
+// fragment) 1664 bytes laid out as the MFMA operand wants them: lane L
+// (row L%16, block L/16 of the chunk) has its 24 code bytes (element i at
+// bits 6i) at 16L (bytes 0-15) and 1024 + 8L (bytes 16-23), its scale byte
+// (E + 127) at 1536 + L; 64 bytes of padding.
 constexpr int kGemmWaves = 8;
 constexpr int kStagesA = 2;
 constexpr int kStagesB = 2;
@@ -292,24 +323,29 @@ constexpr int kAtomsPerTile = 32;                                   // 512 colum
 constexpr int kLdsA = kBM * kAtomK * 2;                             // 32 KB per A stage
 constexpr int kLdsBc = kAtomsPerTile * kAtomData;                   // 32 KB of codes
 constexpr int kLdsBStage = kLdsBc + kAtomsPerTile * 64;             // + 2 KB of scales
-constexpr int kLdsGemm = kStagesA * kLdsA + kStagesB * kLdsBStage;  // 132 KB
-constexpr int kVmemA = 8;   // per A wave and step: 8 loads of 4 rows
-constexpr int kVmemB = 10;  // per B wave and chunk: 8 code loads, 2 scale loads
-static_assert(kLdsGemm <= 160 * 1024, "LDS per CU");
-static_assert(kStagesA >= 2 && kStagesB >= 2, "one stage in flight at least");
+constexpr int kLoFrag = 1664;                                       // one 16-row fragment
+constexpr int kLoChunk = 8 * kLoFrag;                               // 13 KB per tile and chunk
+constexpr int kLdsMain = kStagesA * kLdsA + kStagesB * kLdsBStage;  // 132 KB
+constexpr int kEpiStride = 68;  // floats per row in the epilogue's transpose: rows 4 apart
+                                // land 16 banks apart
+constexpr int kEpiWave = 4 * 16 * kEpiStride * 4;                   // 17 KB per wave
+constexpr int kLdsGateUp = kLdsMain > 8 * kEpiWave ? kLdsMain : 8 * kEpiWave;  // 136 KB
+constexpr int kLdsDown = kLdsMain + kStagesA * kLoChunk;            // 158 KB
+static_assert(kLdsGateUp <= 160 * 1024 && kLdsDown <= 160 * 1024, "LDS per CU");
+static_assert(kStagesA == 2 && kStagesB == 2, "the waits below assume one step in flight");
+static_assert(kLoChunk % 1024 == 0, "low-order records load in whole kilobytes");
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct GemmTile {
   const uint8_t* wbase;  // expert section start (gate/up or down)
   uint32_t wbytes;       // section bytes
   int KC;                // K chunks of the weights
-  int plane_shift;       // 0: one A plane; 1: A has two planes (hi, lo), each
-                         // weight chunk is used for both (step s: chunk s >> 1,
-                         // plane s & 1)
-  uint32_t a_plane;      // bytes from one A plane to the next
   int k0;                // first K chunk: the walk is k0 .. KC-1, 0 .. k0-1
   int rows;              // valid rows in this tile (<= kBM)
+  uint32_t lo0;          // down: byte offset of this tile's low-order records
   uint32_t aoff[8];      // A waves: this lane's piece of row 32w + 4i + l/16 for
                          // load i (row start + swizzled piece), or kOOB past
                          // the valid rows
@@ -336,42 +372,49 @@ __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, uint32_t vof
                : "memory");
 }
 
-// Wait until at most N of this wave's vector-memory instructions are
-// outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
+// Wait until none of this wave's vector-memory instructions is outstanding.
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
-// MF: this wave's 16-row fragments that hold rows (0..4).
-template <int MF>
+// MF: this wave's 16-row fragments that hold rows (0..4).  LO: the down GEMM,
+// which also contracts the low-order piece of h (records through rl).
+template <int MF, bool LO>
 __device__ __forceinline__ void gemm_tile_mf(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
-                                             uint8_t* lds,
+                                             __amdgpu_buffer_rsrc_t rl, uint8_t* lds,
                                              f32x4 (&acc)[MF > 0 ? MF : 1][kFragsPerWave]) {
   const int lane = threadIdx.x & 63, w = wave_id();
   const int mh = w >> 2, nq = w & 3;
   const bool a_wave = w < 4;
-  const int KC = gt.KC, ps = gt.plane_shift;
-  const int steps = KC << ps;
+  const int KC = gt.KC;
   const __amdgpu_buffer_rsrc_t rw = rsrc(gt.wbase, gt.wbytes);
-  uint8_t* const bstages = lds + kStagesA * kLdsA;
+  uint8_t* const lostages = lds + kStagesA * kLdsA;
+  uint8_t* const bstages = lostages + (LO ? kStagesA * kLoChunk : 0);
   // Chunk of the weights (and of A) that walk position c covers.
   auto chunk = [&](int c) { return c + gt.k0 < KC ? c + gt.k0 : c + gt.k0 - KC; };
-  // A waves: step s into stage s % kStagesA.
+  // A waves: step s into stage s % 2; in the down GEMM also kilobytes
+  // q0 .. q0+n-1 of the step's low-order record (4, 3, 3, 3 of its 13).
   auto issue_a = [&](int s) {
-    uint8_t* buf = lds + (s % kStagesA) * kLdsA;
-    const bool in = s < steps;
-    const uint32_t k = (uint32_t)chunk(s >> ps) * (kAtomK * 2) + (uint32_t)(s & ps) * gt.a_plane;
+    const int st = s % kStagesA;
+    uint8_t* buf = lds + st * kLdsA;
+    const bool in = s < KC;
+    const uint32_t k = (uint32_t)chunk(s) * (kAtomK * 2);
 #pragma unroll
     for (int i = 0; i < 8; i++) lds_load16(ra, in ? gt.aoff[i] + k : kOOB, buf + (8 * w + i) * 1024);
+    if constexpr (LO) {
+      const int q0 = w == 0 ? 0 : 1 + 3 * w, n = w == 0 ? 4 : 3;
+      const uint32_t lk = gt.lo0 + (uint32_t)chunk(s) * kLoChunk + 16u * (uint32_t)lane;
+#pragma unroll
+      for (int t = 0; t < 4; t++)
+        if (t < n)
+          lds_load16(rl, in ? lk + (uint32_t)(q0 + t) * 1024u : kOOB,
+                     lostages + st * kLoChunk + (q0 + t) * 1024);
+    }
   };
-  // B waves: chunk c into stage c % kStagesB.
+  // B waves: chunk c into stage c % 2.
   auto issue_b = [&](int c) {
     uint8_t* buf = bstages + (c % kStagesB) * kLdsBStage;
     const int u = w - 4;
@@ -387,9 +430,11 @@ __device__ __forceinline__ void gemm_tile_mf(const GemmTile& gt, __amdgpu_buffer
   // One step: the A fragments and dequantised weights of K step j+1 are
   // fetched while the MFMAs of step j run.
   auto compute = [&](int s) {
-    if constexpr (MF > 0) {
+    if constexpr (MF == 0) {
+      if (!a_wave) issue_b(s + 1);
+    } else {
       const uint8_t* abuf = lds + (s % kStagesA) * kLdsA;
-      const uint8_t* bbuf = bstages + ((s >> ps) % kStagesB) * kLdsBStage;
+      const uint8_t* bbuf = bstages + (s % kStagesB) * kLdsBStage;
       u32x4 wd[kFragsPerWave];
       uint32_t sd[kFragsPerWave];
 #pragma unroll
@@ -406,10 +451,24 @@ __device__ __forceinline__ void gemm_tile_mf(const GemmTile& gt, __amdgpu_buffer
         for (int i = 0; i < MF; i++)
           a[q][i] = *reinterpret_cast<const bf16x8*>(abuf + (2 * i + mh) * 4096 + 256 * r + 16 * slot);
       };
+      // low-order operand: 24 code bytes and the scale of (row l%16, block l/16)
+      u32x4 lq[MF];
+      u32x2 lr[MF];
+      uint32_t ls[MF];
       fetch(0, 0);
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         if (j + 1 < 4) fetch(j + 1, (j + 1) & 1);
+        if (LO && j == 3) {
+          const uint8_t* lbuf = lostages + (s % kStagesA) * kLoChunk;
+#pragma unroll
+          for (int i = 0; i < MF; i++) {
+            const uint8_t* fr = lbuf + (2 * i + mh) * kLoFrag;
+            lq[i] = *reinterpret_cast<const u32x4*>(fr + 16 * lane);
+            lr[i] = *reinterpret_cast<const u32x2*>(fr + 1024 + 8 * lane);
+            ls[i] = fr[1536 + lane];
+          }
+        }
         // each atom's weights are dequantised right before its MFMAs
         // two operand registers in turn: the convert for atom f+1 never
         // waits for the MFMAs still reading atom f's operand
@@ -422,33 +481,44 @@ __device__ __forceinline__ void gemm_tile_mf(const GemmTile& gt, __amdgpu_buffer
           for (int i = 0; i < MF; i++)
             acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j & 1][i], bb[f & 1], acc[i][f], 0, 0, 0);
         }
+        if (j == 0 && !a_wave) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_b(s + 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if constexpr (LO) {
+        // fp6 (E2M3) remainder x fp4 (E2M1) weights, both block-scaled:
+        // one MFMA covers the chunk's 128 K for a fragment and an atom
+#pragma unroll
+        for (int f = 0; f < kFragsPerWave; f++) {
+          const i32x8 b8 = {(int)wd[f][0], (int)wd[f][1], (int)wd[f][2], (int)wd[f][3], 0, 0, 0, 0};
+#pragma unroll
+          for (int i = 0; i < MF; i++) {
+            const i32x8 a8 = {(int)lq[i][0], (int)lq[i][1], (int)lq[i][2], (int)lq[i][3],
+                              (int)lr[i][0], (int)lr[i][1], 0,            0};
+            acc[i][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                a8, b8, acc[i][f], 2 /* A: fp6 E2M3 */, 4 /* B: fp4 E2M1 */, 0, (int)ls[i], 0,
+                (int)sd[f]);
+          }
+        }
       }
     }
   };
-  if (a_wave) {
-#pragma unroll
-    for (int s = 0; s < kStagesA - 1; s++) issue_a(s);
-  } else {
-#pragma unroll
-    for (int c = 0; c < kStagesB - 1; c++) issue_b(c);
-  }
+  if (a_wave)
+    issue_a(0);
+  else
+    issue_b(0);
   __builtin_amdgcn_sched_barrier(0);
-  for (int s = 0; s < steps; s++) {
-    const bool new_chunk = (s & ps) == 0;
-    if (a_wave)
-      wait_vmem<kVmemA * (kStagesA - 2)>();
-    else if (new_chunk)
-      wait_vmem<kVmemB * (kStagesB - 2)>();
+  for (int s = 0; s < KC; s++) {
+    wait_vmem_all();
     lds_barrier();
-    if (a_wave)
-      issue_a(s + kStagesA - 1);
-    else if (new_chunk)
-      issue_b((s >> ps) + kStagesB - 1);
+    if (a_wave) issue_a(s + 1);
     __builtin_amdgcn_sched_barrier(0);
-    compute(s);
+    compute(s);  // the B waves issue step s+1 inside
   }
   // No buffer-to-LDS write may land after the workgroup has ended.
-  wait_vmem<0>();
+  wait_vmem_all();
 }
 
 // A wave w loads rows 32w .. 32w+31 (offsets set by the kernel); B wave
@@ -461,6 +531,7 @@ __device__ __forceinline__ void clear_loads(GemmTile& gt) {
 #pragma unroll
   for (int t = 0; t < 8; t++) gt.woff[t] = 0;
   gt.soff[0] = gt.soff[1] = 0;
+  gt.lo0 = 0;
 }
 // Byte offset, within a 256-byte chunk row, of the piece that lane l loads
 // for tile row r: it lands in LDS slot l % 16 of that row, which holds
@@ -507,48 +578,115 @@ __device__ __forceinline__ int wave_mfrags(int rows) {
   return (((rows + 15) >> 4) - mh + 1) >> 1;
 }
 
+// E2M3 code of t = lo * 2^-E (|t| <= 7.5), rounded to nearest even: for
+// |t| in [2^e, 2^(e+1)) (e = 0, 1, 2; e = 0 also below 1, the subnormals)
+// the grid step is 2^(e-3), and 8e + RNE(|t| * 2^(3-e)) is the magnitude
+// code (a carry into the next binade gives the right code as well).
+__device__ __forceinline__ uint32_t e2m3_code(float lo, float inv_scale) {
+  const float t = lo * inv_scale;
+  const float a = fabsf(t);
+  const int ex = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;
+  const int e = ex < 0 ? 0 : (ex > 2 ? 2 : ex);
+  const float q = __builtin_rintf(a * __uint_as_float((uint32_t)(130 - e) << 23));
+  return (uint32_t)(8 * e + (int)q) | (t < 0.0f ? 32u : 0u);
+}
+
 template <int MF>
 __device__ __forceinline__ void gateup_tile(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
-                                            uint8_t* lds, uint16_t* __restrict__ h,
-                                            size_t lo_plane, int I, size_t row0, int p0) {
+                                            uint8_t* lds, uint16_t* __restrict__ hhi,
+                                            uint8_t* __restrict__ hlo, int I, size_t row0,
+                                            int p0) {
   const int npairs = I / kAtomRows;
-  const int lane = threadIdx.x & 63, mh = wave_id() >> 2;
+  const int lane = threadIdx.x & 63, w = wave_id(), mh = w >> 2;
   f32x4 acc[MF > 0 ? MF : 1][kFragsPerWave];
 #pragma unroll
   for (int i = 0; i < (MF > 0 ? MF : 1); i++)
 #pragma unroll
     for (int f = 0; f < kFragsPerWave; f++) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gemm_tile_mf<MF>(gt, ra, lds, acc);
+  gemm_tile_mf<MF, false>(gt, ra, ra, lds, acc);
+  // Every wave's loads have landed (each ended with vmcnt(0)); after this
+  // barrier no wave reads a stage any more and the LDS holds the transpose:
+  // wave w's h at w * kEpiWave as [fragment i][row][64 columns] floats.
+  lds_barrier();
+  float* ep = reinterpret_cast<float*>(lds + w * kEpiWave);
 #pragma unroll
-  for (int i = 0; i < MF; i++) {
+  for (int i = 0; i < MF; i++)
 #pragma unroll
-    for (int q = 0; q < kFragsPerWave / 2; q++) {
+    for (int q = 0; q < kFragsPerWave / 2; q++)
 #pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int m = (2 * i + mh) * 16 + 4 * (lane >> 4) + r;
-        if (m < gt.rows && p0 + q < npairs) {
-          const float hv = silu(acc[i][2 * q][r]) * acc[i][2 * q + 1][r];
-          const uint16_t hi = f32_to_bf16_rne(hv);
-          const size_t o = (row0 + m) * I + (p0 + q) * 16 + (lane & 15);
-          h[o] = hi;
-          h[lo_plane + o] = f32_to_bf16_rne(hv - __uint_as_float((uint32_t)hi << 16));
-        }
+      for (int r = 0; r < 4; r++)
+        ep[(i * 16 + 4 * (lane >> 4) + r) * kEpiStride + 16 * q + (lane & 15)] =
+            silu(acc[i][2 * q][r]) * acc[i][2 * q + 1][r];
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave reads its own writes
+  // Lane L: row L%16 of fragment 2it + L/32, block (L/16)%2 of the wave's
+  // 64 columns (h columns 16 p0 + 32 b ..), i.e. block kb = (p0/2 + b) % 4 of
+  // the down GEMM's chunk p0/8.
+  const int row = lane & 15, b = (lane >> 4) & 1;
+  const bool col_ok = p0 + 2 * b < npairs;
+  const int kb = ((p0 >> 1) + b) & 3, LL = row + 16 * kb;
+  uint8_t* const rec_chunk = hlo + (size_t)(p0 >> 3) * kLoChunk;
+#pragma unroll
+  for (int it = 0; it < (MF + 1) / 2; it++) {
+    const int i = 2 * it + (lane >> 5);
+    if (i < MF && col_ok) {
+      const float* src = ep + (i * 16 + row) * kEpiStride + 32 * b;
+      float v[32];
+#pragma unroll
+      for (int t = 0; t < 8; t++) {
+        const f32x4 x4 = *reinterpret_cast<const f32x4*>(src + 4 * t);
+        v[4 * t] = x4[0], v[4 * t + 1] = x4[1], v[4 * t + 2] = x4[2], v[4 * t + 3] = x4[3];
       }
+      uint32_t hp[16];
+      float mx = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 32; t++) {
+        const uint32_t hb = f32_to_bf16_rne(v[t]);
+        hp[t >> 1] = (t & 1) ? (hp[t >> 1] | (hb << 16)) : hb;
+        v[t] -= __uint_as_float(hb << 16);  // the remainder, exact in fp32
+        mx = fmaxf(mx, fabsf(v[t]));
+      }
+      // block exponent: the largest remainder at most 7.5 * 2^E
+      int E = -127;
+      if (mx > 0.0f) {
+        E = (int)((__float_as_uint(mx) >> 23) & 0xffu) - 127 - 2;
+        E = E < -126 ? -126 : E;  // 2^E stays a normal float
+        if (mx > 7.5f * __uint_as_float((uint32_t)(E + 127) << 23)) E += 1;
+      }
+      const float inv = __uint_as_float((uint32_t)(127 - E) << 23);
+      uint32_t d[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int t = 0; t < 32; t++) {
+        const uint32_t c = e2m3_code(v[t], inv);
+        const int bit = 6 * t, dw = bit >> 5, sh = bit & 31;
+        d[dw] |= c << sh;
+        if (sh > 26) d[dw + 1] |= c >> (32 - sh);
+      }
+      const int g = 2 * i + mh, m = g * 16 + row;
+      if (m < gt.rows) {
+        u32x4* dst = reinterpret_cast<u32x4*>(hhi + (row0 + m) * I + 16 * p0 + 32 * b);
+#pragma unroll
+        for (int t = 0; t < 4; t++) dst[t] = u32x4{hp[4 * t], hp[4 * t + 1], hp[4 * t + 2], hp[4 * t + 3]};
+      }
+      uint8_t* rec = rec_chunk + g * kLoFrag;
+      *reinterpret_cast<u32x4*>(rec + 16 * LL) = u32x4{d[0], d[1], d[2], d[3]};
+      *reinterpret_cast<u32x2*>(rec + 1024 + 8 * LL) = u32x2{d[4], d[5]};
+      rec[1536 + LL] = (uint8_t)(E + 127);
     }
   }
 }
 
 template <int MF>
 __device__ __forceinline__ void down_tile(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
-                                          uint8_t* lds, float* __restrict__ yperm, int H,
-                                          size_t row0, int rg0, int ngroups) {
+                                          __amdgpu_buffer_rsrc_t rl, uint8_t* lds,
+                                          float* __restrict__ yperm, int H, size_t row0, int rg0,
+                                          int ngroups) {
   const int lane = threadIdx.x & 63, mh = wave_id() >> 2;
   f32x4 acc[MF > 0 ? MF : 1][kFragsPerWave];
 #pragma unroll
   for (int i = 0; i < (MF > 0 ? MF : 1); i++)
 #pragma unroll
     for (int f = 0; f < kFragsPerWave; f++) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gemm_tile_mf<MF>(gt, ra, lds, acc);
+  gemm_tile_mf<MF, true>(gt, ra, rl, lds, acc);
 #pragma unroll
   for (int i = 0; i < MF; i++)
 #pragma unroll
@@ -564,16 +702,15 @@ __device__ __forceinline__ void down_tile(const GemmTile& gt, __amdgpu_buffer_rs
 // Gate/up + SwiGLU.  N-block nb covers row pairs nb*16 .. nb*16+15 (gate,
 // up; pairs past I/16 in the last block are computed on group 0 and not
 // stored); column quarter nq takes pairs nb*16 + 4nq .. +3 (atoms g0, u0,
-// g1, u1, ...).
-// h leaves as two bf16 planes, hi = RNE(h) and lo = RNE(h - hi) (about 16
-// significant bits), both of which the down GEMM contracts.
+// g1, u1, ...).  h leaves as the bf16 plane hi and the tile's low-order
+// records (their layout is described above the GEMM constants).
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void gateup_prefill_kernel(
     GroupArgs g, const uint16_t* x, uint32_t x_bytes, int H, int I, int nbn,
-    uint16_t* __restrict__ h, size_t lo_plane) {
+    uint16_t* __restrict__ hhi, uint8_t* __restrict__ hlo) {
   int ti, nb;
   tile_of_block(nbn, &ti, &nb);
   if (ti >= *g.n_tiles) return;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsGemm];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsGateUp];
   const int2 td = g.tiles[ti];
   const int grp = td.x, m0 = td.y;
   const int cnt = g.counts[grp], pos0 = g.offsets[grp];
@@ -582,8 +719,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   gt.wbase = grp < g.E ? g.layerbuf + (size_t)grp * g.stride : g.shared_w;
   gt.KC = H / kAtomK;
   gt.wbytes = (uint32_t)(2 * I / kAtomRows) * (uint32_t)gt.KC * kAtomBytes;
-  gt.plane_shift = 0;
-  gt.a_plane = 0;
   gt.k0 = nb * gt.KC / nbn;
   gt.rows = min(kBM, cnt - m0);
   clear_loads(gt);
@@ -601,21 +736,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
   const __amdgpu_buffer_rsrc_t ra = rsrc(x, x_bytes);
   const size_t row0 = (size_t)(pos0 + m0);
   const int p0 = nb * 16 + 4 * nq;
-#define GU(N) gateup_tile<N>(gt, ra, lds, h, lo_plane, I, row0, p0)
+  uint8_t* const tile_lo = hlo + (size_t)ti * (size_t)(I / kAtomK) * kLoChunk;
+#define GU(N) gateup_tile<N>(gt, ra, lds, hhi, tile_lo, I, row0, p0)
   MOE_MF_SWITCH(wave_mfrags(gt.rows), GU)
 #undef GU
 }
 
 // Down.  N-block nb covers row groups nb*32 .. nb*32+31 of H (512 columns;
 // the last block may be partial); column quarter nq takes row groups
-// nb*32 + 8nq .. +7.
+// nb*32 + 8nq .. +7.  A is the bf16 plane hi; the low-order records of h
+// come through their own stage.
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void down_prefill_kernel(
-    GroupArgs g, const uint16_t* h, uint32_t h_bytes, uint32_t lo_plane_bytes, int H, int I,
-    int nbn, size_t gateup_bytes, float* __restrict__ yperm) {
+    GroupArgs g, const uint16_t* hhi, uint32_t hhi_bytes, const uint8_t* hlo, uint32_t hlo_bytes,
+    int H, int I, int nbn, size_t gateup_bytes, float* __restrict__ yperm) {
   int ti, nb;
   tile_of_block(nbn, &ti, &nb);
   if (ti >= *g.n_tiles) return;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsGemm];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsDown];
   const int2 td = g.tiles[ti];
   const int grp = td.x, m0 = td.y;
   const int cnt = g.counts[grp], pos0 = g.offsets[grp];
@@ -625,11 +762,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
   gt.wbase = (grp < g.E ? g.layerbuf + (size_t)grp * g.stride : g.shared_w) + gateup_bytes;
   gt.KC = I / kAtomK;
   gt.wbytes = (uint32_t)ngroups * (uint32_t)gt.KC * kAtomBytes;
-  gt.plane_shift = 1;
-  gt.a_plane = lo_plane_bytes;
   gt.k0 = nb * gt.KC / nbn;
   gt.rows = min(kBM, cnt - m0);
   clear_loads(gt);
+  gt.lo0 = (uint32_t)ti * (uint32_t)gt.KC * (uint32_t)kLoChunk;
   if (w < 4) {
 #pragma unroll
     for (int i = 0; i < 8; i++) {
@@ -639,10 +775,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
   } else {
     set_weight_loads(gt, nb * 32 + 8 * (w - 4), lane, ngroups);  // tile atom a: row group 32nb + a
   }
-  const __amdgpu_buffer_rsrc_t ra = rsrc(h, h_bytes);
+  const __amdgpu_buffer_rsrc_t ra = rsrc(hhi, hhi_bytes), rl = rsrc(hlo, hlo_bytes);
   const size_t row0 = (size_t)(pos0 + m0);
   const int rg0 = nb * 32 + 8 * nq;
-#define DN(N) down_tile<N>(gt, ra, lds, yperm, H, row0, rg0, ngroups)
+#define DN(N) down_tile<N>(gt, ra, rl, lds, yperm, H, row0, rg0, ngroups)
   MOE_MF_SWITCH(wave_mfrags(gt.rows), DN)
 #undef DN
 }
@@ -662,7 +798,7 @@ hipError_t prefill_alloc(Ctx* c) {
   const int T = f.max_prefill_tokens, E = f.n_experts, k = f.top_k;
   p->Tmax = T;
   p->nchunk_max = (T + kChunkTokens - 1) / kChunkTokens;
-  p->max_tiles = ((T * k + T + kBM - 1) / kBM + E + 1 + 7) / 8 * 8;
+  p->max_tiles = prefill_max_tiles(T, k, E);
   const size_t rows = (size_t)T * k + T;
   hipError_t e;
 #define PA(ptr, n) \
@@ -678,7 +814,8 @@ hipError_t prefill_alloc(Ctx* c) {
   PA(tok, rows);
   PA(tiles, (size_t)p->max_tiles);
   PA(n_tiles, 1);
-  PA(h, 2 * rows * f.inter);  // hi and lo planes
+  PA(h, rows * f.inter);
+  PA(hlo, prefill_lo_bytes(T, k, E, f.inter));
   PA(yperm, rows * f.hidden);
 #undef PA
   const size_t layer_bytes = (size_t)E * c->stride;
@@ -698,7 +835,7 @@ void prefill_free(Ctx* c) {
   if (c->copy_stream) (void)hipStreamSynchronize(c->copy_stream);
   if (Prefill* p = c->pf) {
     void* ptrs[] = {p->logits, p->ids, p->gates, p->chunk_cnt, p->counts, p->offsets, p->sorted,
-                    p->inv, p->tok, p->tiles, p->n_tiles, p->h, p->yperm};
+                    p->inv, p->tok, p->tiles, p->n_tiles, p->h, p->hlo, p->yperm};
     for (void* q : ptrs)
       if (q) (void)hipFree(q);
     delete p;
@@ -792,12 +929,13 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
         tr = {nullptr, nullptr, nullptr};
     }
     const int nbn_gu = (2 * I + 511) / 512, nbn_dn = (H + 511) / 512;
-    const size_t lo_plane = (size_t)p->Tmax * (k + 1) * I;  // elements
+    const size_t hhi_bytes = (size_t)p->Tmax * (k + 1) * I * 2;
+    const size_t hlo_bytes = prefill_lo_bytes(p->Tmax, k, E, I);
     gateup_prefill_kernel<<<p->max_tiles * nbn_gu, 64 * kGemmWaves, 0, st>>>(
-        ga, x, (uint32_t)T * H * 2, H, I, nbn_gu, p->h, lo_plane);
+        ga, x, (uint32_t)T * H * 2, H, I, nbn_gu, p->h, p->hlo);
     if (tr.before_down) (void)hipEventRecord(tr.before_down, st);
     down_prefill_kernel<<<p->max_tiles * nbn_dn, 64 * kGemmWaves, 0, st>>>(
-        ga, p->h, (uint32_t)(4 * lo_plane), (uint32_t)(2 * lo_plane), H, I, nbn_dn,
+        ga, p->h, (uint32_t)hhi_bytes, p->hlo, (uint32_t)hlo_bytes, H, I, nbn_dn,
         gateup_section_bytes(H, I), p->yperm);
     if (tr.after_down) {
       (void)hipEventRecord(tr.after_down, st);

@@ -18,6 +18,13 @@ RTOL_Y = 2e-2     # max |y - y_ref| <= RTOL_Y * rms(y_ref), per call
 # oracle; this tighter bar catches small indexing or scaling mistakes that
 # the 2e-2 bar would hide.
 RTOL_Y_DECODE = 1e-3
+# Prefill carries h as bf16 plus a block-scaled fp6 remainder (about 2^-14 of
+# each 32-column block's largest value).  A CPU emulation of that rounding
+# gives 1.06e-3 at the E = 1024, top-16, H = I = 256 shape (the worst one the
+# tests run) and 3e-4 at wide I; this bar sits above those with room to spare
+# and still far below the 2e-2 contract, so a mis-scaled or misplaced piece
+# of h fails it.
+RTOL_Y_PREFILL = 4e-3
 ATOL_G = 1e-6     # gates
 TOL_SUM = 1e-6    # |sum(g) - 1| with renormalisation
 

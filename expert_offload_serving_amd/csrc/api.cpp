@@ -376,21 +376,14 @@ moe_status moe_layer_forward(moe_ctx* ctx, int32_t layer, const void* d_x, int32
                        st));
   HIPCHK(launch_route_finalize(c, layer, T, d_ids, d_gates, st));
   HIPCHK(launch_fill(c->d_fills, c->d_meta, c->max_unique, c->rec_bytes, st));
-  Ctx::TimingRec tr{nullptr, nullptr, nullptr};
+  Ctx::TimingRec tr{nullptr, nullptr, nullptr, nullptr};
   if (c->timing && c->t_decode.size() < kMaxTimingPairs) {
-    tr = {timing_event(c), timing_event(c), timing_event(c)};
-    if (tr.before_gateup && tr.before_down && tr.after_down)
-      HIPCHK(hipEventRecord(tr.before_gateup, st));
-    else
-      tr = {nullptr, nullptr, nullptr};
+    tr = {timing_event(c), timing_event(c), timing_event(c), timing_event(c)};
+    if (!(tr.gu0 && tr.gu1 && tr.dn0 && tr.dn1)) tr = {nullptr, nullptr, nullptr, nullptr};
   }
-  HIPCHK(launch_expert_gateup(c, (const uint16_t*)d_x, T, st));
-  if (tr.before_down) HIPCHK(hipEventRecord(tr.before_down, st));
-  HIPCHK(launch_expert_down(c, T, st));
-  if (tr.after_down) {
-    HIPCHK(hipEventRecord(tr.after_down, st));
-    c->t_decode.push_back(tr);
-  }
+  HIPCHK(launch_expert_gateup(c, (const uint16_t*)d_x, T, st, tr.gu0, tr.gu1));
+  HIPCHK(launch_expert_down(c, T, st, tr.dn0, tr.dn1));
+  if (tr.gu0) c->t_decode.push_back(tr);
   HIPCHK(launch_combine(c, T, (uint16_t*)d_y, d_y32, st));
   c->host_stats.forward_calls++;
   return MOE_OK;
@@ -646,8 +639,8 @@ static hipError_t sum_timing(const std::vector<Ctx::TimingRec>& v, double* ms3) 
   double s[3] = {0, 0, 0};
   for (const auto& r : v) {
     float a = 0, b = 0;
-    hipError_t e = hipEventElapsedTime(&a, r.before_gateup, r.before_down);
-    if (e == hipSuccess) e = hipEventElapsedTime(&b, r.before_down, r.after_down);
+    hipError_t e = hipEventElapsedTime(&a, r.gu0, r.gu1);
+    if (e == hipSuccess) e = hipEventElapsedTime(&b, r.dn0, r.dn1);
     if (e != hipSuccess) return e;
     s[0] += (double)a + b;
     s[1] += a;

@@ -556,16 +556,17 @@ static int items_for(const Ctx* c, int T) {
   return std::min(T * c->cfg.top_k, c->cfg.n_experts) + c->cfg.has_shared;
 }
 
-hipError_t launch_expert_gateup(const Ctx* c, const uint16_t* x, int T, hipStream_t st) {
+hipError_t launch_expert_gateup(const Ctx* c, const uint16_t* x, int T, hipStream_t st,
+                                hipEvent_t ev0, hipEvent_t ev1) {
   dim3 grid(c->cfg.inter / kAtomRows, items_for(c, T));
   const size_t lo = (size_t)c->rows_max * c->cfg.inter;
   const int KC = c->cfg.hidden / kAtomK;
   if (T <= kMaxStreamTokens) {
     const int cpw = gateup_stream_cpw(KC), waves = stream_waves(KC, cpw);
-#define GATEUP_S(N)                                                                      \
-  gateup_stream_kernel<N><<<grid, waves * 64, waves * 2 * 64 * 16, st>>>(              \
-      c->d_items, c->d_meta, c->d_tok, x, (uint32_t)T * c->cfg.hidden * 2, c->cfg.hidden, \
-      c->cfg.inter, c->d_h, lo)
+#define GATEUP_S(N)                                                                       \
+  MOE_LAUNCH(gateup_stream_kernel<N>, grid, waves * 64, waves * 2 * 64 * 16, st, ev0, ev1, \
+             c->d_items, c->d_meta, c->d_tok, x, (uint32_t)T * c->cfg.hidden * 2,          \
+             c->cfg.hidden, c->cfg.inter, c->d_h, lo)
     switch (cpw) {
       case 1: GATEUP_S(1); break;
       case 2: GATEUP_S(2); break;
@@ -577,10 +578,10 @@ hipError_t launch_expert_gateup(const Ctx* c, const uint16_t* x, int T, hipStrea
     return hipGetLastError();
   }
   const Split s = split_k(KC, grid.x * grid.y, 4);
-#define GATEUP(N)                                                                       \
-  gateup_decode_kernel<N><<<grid, s.waves * 64, s.waves * 2 * 64 * 16, st>>>(        \
-      c->d_items, c->d_meta, c->d_tok, x, (uint32_t)T * c->cfg.hidden * 2, c->cfg.hidden, \
-      c->cfg.inter, c->d_h, lo)
+#define GATEUP(N)                                                                           \
+  MOE_LAUNCH(gateup_decode_kernel<N>, grid, s.waves * 64, s.waves * 2 * 64 * 16, st, ev0, ev1, \
+             c->d_items, c->d_meta, c->d_tok, x, (uint32_t)T * c->cfg.hidden * 2,            \
+             c->cfg.hidden, c->cfg.inter, c->d_h, lo)
   switch (s.cpw) {
     case 1: GATEUP(1); break;
     case 2: GATEUP(2); break;
@@ -591,16 +592,17 @@ hipError_t launch_expert_gateup(const Ctx* c, const uint16_t* x, int T, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_expert_down(const Ctx* c, int T, hipStream_t st) {
+hipError_t launch_expert_down(const Ctx* c, int T, hipStream_t st, hipEvent_t ev0,
+                              hipEvent_t ev1) {
   dim3 grid(c->cfg.hidden / (2 * kAtomRows), items_for(c, T));
   const size_t lo = (size_t)c->rows_max * c->cfg.inter;
   const size_t gub = gateup_section_bytes(c->cfg.hidden, c->cfg.inter);
   const int KC = c->cfg.inter / kAtomK;
   if (T <= kMaxStreamTokens) {
     const int cpw = down_stream_cpw(KC), waves = stream_waves(KC, cpw);
-#define DOWN_S(N)                                                                  \
-  down_stream_kernel<N><<<grid, waves * 64, waves * 2 * 64 * 16, st>>>(          \
-      c->d_items, c->d_meta, c->d_h, lo, c->cfg.hidden, c->cfg.inter, gub, c->d_yperm)
+#define DOWN_S(N)                                                                       \
+  MOE_LAUNCH(down_stream_kernel<N>, grid, waves * 64, waves * 2 * 64 * 16, st, ev0, ev1, \
+             c->d_items, c->d_meta, c->d_h, lo, c->cfg.hidden, c->cfg.inter, gub, c->d_yperm)
     switch (cpw) {
       case 1: DOWN_S(1); break;
       case 2: DOWN_S(2); break;
@@ -612,10 +614,9 @@ hipError_t launch_expert_down(const Ctx* c, int T, hipStream_t st) {
     return hipGetLastError();
   }
   const Split s = split_k(KC, grid.x * grid.y, 4);
-#define DOWN(N)                                                                       \
-  down_decode_kernel<N><<<grid, s.waves * 64, s.waves * 2 * 64 * 16, st>>>(        \
-      c->d_items, c->d_meta, c->d_h, lo, c->cfg.hidden, c->cfg.inter, gub,           \
-      c->d_yperm)
+#define DOWN(N)                                                                           \
+  MOE_LAUNCH(down_decode_kernel<N>, grid, s.waves * 64, s.waves * 2 * 64 * 16, st, ev0, ev1, \
+             c->d_items, c->d_meta, c->d_h, lo, c->cfg.hidden, c->cfg.inter, gub, c->d_yperm)
   switch (s.cpw) {
     case 1: DOWN(1); break;
     case 2: DOWN(2); break;

@@ -1,6 +1,7 @@
 // Internal declarations of libmoe: context, device layouts, kernel launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -162,8 +163,10 @@ struct Ctx {
   // timing
   bool timing = false;
   std::vector<hipEvent_t> ev_pool;  // reused
+  // start and stop of the gate/up and the down kernel, recorded by the
+  // dispatches themselves
   struct TimingRec {
-    hipEvent_t before_gateup, before_down, after_down;
+    hipEvent_t gu0, gu1, dn0, dn1;
   };
   std::vector<TimingRec> t_decode, t_prefill;
   size_t ev_next = 0;
@@ -188,9 +191,13 @@ hipError_t launch_copy_pairs(const FillEntry* pairs, int n, size_t bytes,
                              hipStream_t st);
 hipError_t launch_probe_copy(const void* src, void* dst, size_t n_bytes,
                              hipStream_t st);
-hipError_t launch_expert_gateup(const Ctx* c, const uint16_t* x, int T,
-                                hipStream_t st);
-hipError_t launch_expert_down(const Ctx* c, int T, hipStream_t st);
+// The expert launchers take optional start and stop events: when given, the
+// kernel is launched with hipExtLaunchKernel, which records them as part of
+// the dispatch, so that their interval is the kernel's own duration.
+hipError_t launch_expert_gateup(const Ctx* c, const uint16_t* x, int T, hipStream_t st,
+                                hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+hipError_t launch_expert_down(const Ctx* c, int T, hipStream_t st, hipEvent_t ev0 = nullptr,
+                              hipEvent_t ev1 = nullptr);
 hipError_t launch_combine(const Ctx* c, int T, uint16_t* y, float* y32, hipStream_t st);
 hipError_t launch_combine_rows(const float* yperm, const int32_t* inv, const float* gates, int T,
                                int k, int H, int has_shared, uint16_t* y, float* y32,
@@ -198,6 +205,17 @@ hipError_t launch_combine_rows(const float* yperm, const int32_t* inv, const flo
 
 // Next event of the context's timing pool (created on demand; NULL on failure).
 hipEvent_t timing_event(Ctx* c);
+
+// kernel<<<grid, block, shm, st>>>(args...), or with start and stop events
+// recorded by the dispatch itself when ev0 is given.
+#define MOE_LAUNCH(KERNEL, GRID, BLOCK, SHM, ST, EV0, EV1, ...)                          \
+  do {                                                                                  \
+    if (EV0)                                                                            \
+      hipExtLaunchKernelGGL(KERNEL, dim3(GRID), dim3(BLOCK), (uint32_t)(SHM), ST, EV0, EV1, \
+                            0u, __VA_ARGS__);                                           \
+    else                                                                                \
+      KERNEL<<<GRID, BLOCK, SHM, ST>>>(__VA_ARGS__);                                    \
+  } while (0)
 
 // prefill
 int prefill_max_tiles(int T, int k, int E);

@@ -920,27 +920,20 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
 
     GroupArgs ga{p->tiles, p->n_tiles, p->counts, p->offsets, p->tok, c->d_layerbuf[b],
                  c->stride, f.has_shared ? c->d_shared + (size_t)l * c->stride : nullptr, E};
-    Ctx::TimingRec tr{nullptr, nullptr, nullptr};
+    Ctx::TimingRec tr{nullptr, nullptr, nullptr, nullptr};
     if (c->timing && c->t_prefill.size() < 65536) {
-      tr = {timing_event(c), timing_event(c), timing_event(c)};
-      if (tr.before_gateup && tr.before_down && tr.after_down)
-        (void)hipEventRecord(tr.before_gateup, st);
-      else
-        tr = {nullptr, nullptr, nullptr};
+      tr = {timing_event(c), timing_event(c), timing_event(c), timing_event(c)};
+      if (!(tr.gu0 && tr.gu1 && tr.dn0 && tr.dn1)) tr = {nullptr, nullptr, nullptr, nullptr};
     }
     const int nbn_gu = (2 * I + 511) / 512, nbn_dn = (H + 511) / 512;
     const size_t hhi_bytes = (size_t)p->Tmax * (k + 1) * I * 2;
     const size_t hlo_bytes = prefill_lo_bytes(p->Tmax, k, E, I);
-    gateup_prefill_kernel<<<p->max_tiles * nbn_gu, 64 * kGemmWaves, 0, st>>>(
-        ga, x, (uint32_t)T * H * 2, H, I, nbn_gu, p->h, p->hlo);
-    if (tr.before_down) (void)hipEventRecord(tr.before_down, st);
-    down_prefill_kernel<<<p->max_tiles * nbn_dn, 64 * kGemmWaves, 0, st>>>(
-        ga, p->h, (uint32_t)hhi_bytes, p->hlo, (uint32_t)hlo_bytes, H, I, nbn_dn,
-        gateup_section_bytes(H, I), p->yperm);
-    if (tr.after_down) {
-      (void)hipEventRecord(tr.after_down, st);
-      c->t_prefill.push_back(tr);
-    }
+    MOE_LAUNCH(gateup_prefill_kernel, p->max_tiles * nbn_gu, 64 * kGemmWaves, 0, st, tr.gu0,
+               tr.gu1, ga, x, (uint32_t)T * H * 2, H, I, nbn_gu, p->h, p->hlo);
+    MOE_LAUNCH(down_prefill_kernel, p->max_tiles * nbn_dn, 64 * kGemmWaves, 0, st, tr.dn0,
+               tr.dn1, ga, p->h, (uint32_t)hhi_bytes, p->hlo, (uint32_t)hlo_bytes, H, I,
+               nbn_dn, gateup_section_bytes(H, I), p->yperm);
+    if (tr.gu0) c->t_prefill.push_back(tr);
     if ((e = launch_combine_rows(p->yperm, p->inv, p->gates, T, k, H, f.has_shared,
                                  (uint16_t*)ys[l], y32s ? y32s[l] : nullptr, st)) != hipSuccess)
       return e;

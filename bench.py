@@ -10,8 +10,9 @@ decode layer (H=2048, E=256, top-8, I=512, MXFP4 experts, bf16 activations,
 64-slot LRU from a cold start, Zipf(1.1) routing with 60% step overlap), T=16.
 The roofline object is the gate/up expert kernel's (the dominant HBM-bound
 kernel; the miss-fill kernel is bound by PCIe and reported as pcie_h2d_gbs),
-from per-kernel HIP events taken in a second pass queued behind a spin
-kernel.  The line also carries the DeepSeek-V4-Flash-shaped stack (4 layers,
+from per-kernel HIP events taken in a second pass: the library launches
+each expert kernel with start and stop events recorded by the dispatch
+itself, so an interval is the kernel's own duration.  The line also carries the DeepSeek-V4-Flash-shaped stack (4 layers,
 H=4096, I=2048, E=256, top-6 + shared): prefill of T=4096 with whole-layer
 uploads from the pinned pool (grouped-GEMM time and MFMA utilisation), and
 T=1 decode through its global LRU.
@@ -105,9 +106,10 @@ def decode_inputs(wl, T, n, seed=0):
 
 def run_decode(wl, T, steps, warmup, seed=0, eng=None):
     """Decode throughput (wall clock over `steps` steps, host submission
-    included), then a kernel-timing pass: the same number of steps queued
-    behind a spin kernel so that the per-kernel HIP events measure the
-    kernels back to back, not the host's submission gaps."""
+    included), then a kernel-timing pass over the same number of steps, in
+    which each expert kernel carries HIP start and stop events recorded by
+    its dispatch (queued behind a spin kernel, so that the kernels also run
+    back to back as in the timed pass and not at the host's pace)."""
     import torch
 
     sh = wl.shape

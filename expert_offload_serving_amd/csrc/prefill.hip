@@ -84,12 +84,16 @@ __device__ __forceinline__ float silu(float a) {
 // sums on v_mfma_f64_16x16x4_f64.  Block: 64 tokens x 64 experts, K staged
 // through LDS in chunks of 64 as fp32 (bf16 x and fp32 W_r are exact in
 // fp64); each wave owns a 32 x 32 sub-tile (2 x 2 fragments).  Operands:
-// lane l holds A[l % 16][l / 16] and B[l / 16][l % 16] of a K=4 step.
+// lane l holds A[l % 16][l / 16] and B[l / 16][l % 16] of a K=4 step.  The
+// LDS is double-buffered: a chunk's global loads go to registers before the
+// MFMAs of the previous chunk and into the other buffer after them, one
+// barrier per chunk (a DSV4 layer has exactly one block per CU, one wave per
+// SIMD, so nothing else would hide the loads).
 __global__ __launch_bounds__(256) void router_prefill_kernel(
     const uint16_t* __restrict__ x, int T, int H, int E, const float* __restrict__ wrt,
     const float* __restrict__ bias, float* __restrict__ logits) {
-  __shared__ float xs[64][65];
-  __shared__ float ws[64][65];
+  __shared__ float xs[2][64][65];
+  __shared__ float ws[2][64][65];
   const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w & 1, wn = w >> 1;
@@ -98,44 +102,59 @@ __global__ __launch_bounds__(256) void router_prefill_kernel(
   for (int i = 0; i < 2; i++)
 #pragma unroll
     for (int j = 0; j < 2; j++) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
-  for (int k0 = 0; k0 < H; k0 += 64) {
-    __syncthreads();
-    for (int i = threadIdx.x; i < 64 * 8; i += 256) {  // 64 rows x 8 pieces of 8
-      const int r = i >> 3, q = i & 7;
+  // thread's two pieces per chunk: row r = i >> 3, 8 columns from 8 (i & 7)
+  u32x4 xv[2];
+  f32x4 wv[2][2];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int i = threadIdx.x + 256 * u, r = i >> 3, q = i & 7;
       const int t = t0 + r, e = e0 + r;
-      u32x4 xv = {0u, 0u, 0u, 0u};
-      if (t < T) xv = *reinterpret_cast<const u32x4*>(x + (size_t)t * H + k0 + 8 * q);
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        xs[r][8 * q + 2 * j] = __uint_as_float(xv[j] << 16);
-        xs[r][8 * q + 2 * j + 1] = __uint_as_float(xv[j] & 0xFFFF0000u);
-      }
-      f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = {0.f, 0.f, 0.f, 0.f};
+      xv[u] = u32x4{0u, 0u, 0u, 0u};
+      wv[u][0] = wv[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (t < T) xv[u] = *reinterpret_cast<const u32x4*>(x + (size_t)t * H + k0 + 8 * q);
       if (e < E) {
-        w0 = *reinterpret_cast<const f32x4*>(wrt + (size_t)e * H + k0 + 8 * q);
-        w1 = *reinterpret_cast<const f32x4*>(wrt + (size_t)e * H + k0 + 8 * q + 4);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        ws[r][8 * q + j] = w0[j];
-        ws[r][8 * q + 4 + j] = w1[j];
+        wv[u][0] = *reinterpret_cast<const f32x4*>(wrt + (size_t)e * H + k0 + 8 * q);
+        wv[u][1] = *reinterpret_cast<const f32x4*>(wrt + (size_t)e * H + k0 + 8 * q + 4);
       }
     }
-    __syncthreads();
+  };
+  auto store = [&](int b) {
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int i = threadIdx.x + 256 * u, r = i >> 3, q = i & 7;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        xs[b][r][8 * q + 2 * j] = __uint_as_float(xv[u][j] << 16);
+        xs[b][r][8 * q + 2 * j + 1] = __uint_as_float(xv[u][j] & 0xFFFF0000u);
+        ws[b][r][8 * q + j] = wv[u][0][j];
+        ws[b][r][8 * q + 4 + j] = wv[u][1][j];
+      }
+    }
+  };
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int k0 = 0, b = 0; k0 < H; k0 += 64, b ^= 1) {
+    const bool more = k0 + 64 < H;
+    if (more) load(k0 + 64);
 #pragma unroll 4
     for (int kk = 0; kk < 64; kk += 4) {
-      double a[2], b[2];
+      double a[2], bb[2];
 #pragma unroll
       for (int f = 0; f < 2; f++) {
-        a[f] = (double)xs[wm * 32 + f * 16 + (lane & 15)][kk + (lane >> 4)];
-        b[f] = (double)ws[wn * 32 + f * 16 + (lane & 15)][kk + (lane >> 4)];
+        a[f] = (double)xs[b][wm * 32 + f * 16 + (lane & 15)][kk + (lane >> 4)];
+        bb[f] = (double)ws[b][wn * 32 + f * 16 + (lane & 15)][kk + (lane >> 4)];
       }
 #pragma unroll
       for (int i = 0; i < 2; i++)
 #pragma unroll
         for (int j = 0; j < 2; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], bb[j], acc[i][j], 0, 0, 0);
     }
+    // buffer b^1 was last read before the previous barrier
+    if (more) store(b ^ 1);
+    __syncthreads();
   }
 #pragma unroll
   for (int i = 0; i < 2; i++)

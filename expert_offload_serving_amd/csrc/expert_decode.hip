@@ -500,19 +500,37 @@ __global__ __launch_bounds__(1024) void down_stream_kernel(
 }
 
 // y[t] = sum_j g[t,j] * o[inv(t,j)] (+ shared row), fp32 in rank order, bf16 out.
+// A thread takes 4 consecutive columns (H is a multiple of 128); the k rows
+// (at most 16) are all loaded before the fmas, which keep rank order.
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ yperm, const int32_t* __restrict__ inv,
     const float* __restrict__ gates, int T, int k, int H, int has_shared,
     uint16_t* __restrict__ y, float* __restrict__ y32) {
   const int t = blockIdx.y;
-  const int col = blockIdx.x * 256 + threadIdx.x;
+  const int col = 4 * (blockIdx.x * 256 + threadIdx.x);
   if (col >= H) return;
-  float acc = 0.f;
-  for (int j = 0; j < k; j++)
-    acc = fmaf(gates[t * k + j], yperm[(size_t)inv[t * k + j] * H + col], acc);
-  if (has_shared) acc += yperm[(size_t)(T * k + t) * H + col];
-  y[(size_t)t * H + col] = f32_to_bf16_rne(acc);
-  if (y32) y32[(size_t)t * H + col] = acc;
+  f32x4 v[17];
+#pragma unroll
+  for (int j = 0; j < 16; j++)
+    if (j < k) v[j] = *reinterpret_cast<const f32x4*>(yperm + (size_t)inv[t * k + j] * H + col);
+  if (has_shared) v[16] = *reinterpret_cast<const f32x4*>(yperm + (size_t)(T * k + t) * H + col);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 16; j++)
+    if (j < k) {
+      const float g = gates[t * k + j];
+#pragma unroll
+      for (int c = 0; c < 4; c++) acc[c] = fmaf(g, v[j][c], acc[c]);
+    }
+  if (has_shared) {
+#pragma unroll
+    for (int c = 0; c < 4; c++) acc[c] += v[16][c];
+  }
+  const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
+  const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  *reinterpret_cast<u32x2_t*>(y + (size_t)t * H + col) = u32x2_t{lo, hi};
+  if (y32) *reinterpret_cast<f32x4*>(y32 + (size_t)t * H + col) = acc;
 }
 
 // Waves per workgroup (the split of K) and chunks per wave, for K of KC
@@ -630,7 +648,7 @@ hipError_t launch_expert_down(const Ctx* c, int T, hipStream_t st, hipEvent_t ev
 hipError_t launch_combine_rows(const float* yperm, const int32_t* inv, const float* gates, int T,
                                int k, int H, int has_shared, uint16_t* y, float* y32,
                                hipStream_t st) {
-  dim3 grid((H + 255) / 256, T);
+  dim3 grid((H / 4 + 255) / 256, T);
   combine_kernel<<<grid, 256, 0, st>>>(yperm, inv, gates, T, k, H, has_shared, y, y32);
   return hipGetLastError();
 }

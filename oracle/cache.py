@@ -26,12 +26,32 @@ resize(C'): grow appends empty slots; shrink evicts occupied slots in
   ascending stamp while occupancy > C', then moves every survivor in a slot
   >= C' (ascending) to the lowest empty slot < C' (ascending), keeping key
   and stamp.  clock is unchanged.
+
+Placement policies.  The pages set the global LRU against placements that
+lock chosen experts into GPU memory at start-up, and quote the miss rates of
+the global cache and of two other engines at equal capacity (jansverre.net
+FreeToken article, section "Hvorfor er båndbredden viktigere enn antall
+kjerner?").  Two alternatives to the global LRU are modelled with the same
+rule, for that comparison:
+  - "per_layer": layer l owns the slots floor(l C / L) .. floor((l+1) C / L) - 1
+    and a lookup of layer l takes its victims from those slots only (empty
+    ones ascending, then its occupied ones whose stamp <= start, ascending);
+  - "static": lookups never insert, so every miss bypasses; only fill()
+    places experts (with the global rule), e.g. a set chosen beforehand.
+Hits, stamps and the clock follow the same rule under every policy.  resize
+is defined for the global policy only.
 """
 
 
+POLICIES = ("global", "per_layer", "static")
+
+
 class SlotCache:
-    def __init__(self, capacity: int, n_experts: int):
+    def __init__(self, capacity: int, n_experts: int, n_layers: int = 1, policy: str = "global"):
+        assert policy in POLICIES
         self.E = n_experts
+        self.L = n_layers
+        self.policy = policy
         self.key = [-1] * capacity
         self.stamp = [0] * capacity
         self.clock = 0
@@ -47,13 +67,23 @@ class SlotCache:
                 return s
         return None
 
-    def lookup(self, layer: int, experts):
+    def victim_range(self, layer: int):
+        """The slots a lookup of `layer` may fill."""
+        if self.policy == "per_layer":
+            C, L = self.capacity, self.L
+            return range(layer * C // L, (layer + 1) * C // L)
+        return range(self.capacity)
+
+    def lookup(self, layer: int, experts, insert=None):
         """Returns (slots, fills, bypass).
 
         slots[i] >= 0: the cache slot of experts[i]; < 0: -1 - staging index.
         fills: [(slot, layer, expert)] in issue order; bypass: [(staging,
-        layer, expert)].
+        layer, expert)].  insert (default: every policy but "static") lets
+        misses take victims.
         """
+        if insert is None:
+            insert = self.policy != "static"
         experts = [int(e) for e in experts]
         assert experts == sorted(set(experts)), "experts must be ascending unique"
         start = self.clock
@@ -69,10 +99,11 @@ class SlotCache:
                 self.stamp[s] = self.clock
                 slots[i] = s
                 self.hits += 1
-        empty = [s for s in range(self.capacity) if self.key[s] < 0]
-        old = sorted((self.stamp[s], s) for s in range(self.capacity)
+        rng = self.victim_range(layer)
+        empty = [s for s in rng if self.key[s] < 0]
+        old = sorted((self.stamp[s], s) for s in rng
                      if self.key[s] >= 0 and self.stamp[s] <= start)
-        victims = empty + [s for _, s in old]
+        victims = empty + [s for _, s in old] if insert else []
         fills, bypass = [], []
         for r, i in enumerate(misses):
             e = experts[i]
@@ -94,12 +125,14 @@ class SlotCache:
         return slots, fills, bypass
 
     def fill(self, layer: int, experts):
-        """Explicit preload: the same rule as a lookup."""
-        return self.lookup(layer, experts)
+        """Explicit preload: the same rule as a lookup, inserting under every
+        policy (it is how the "static" set is placed)."""
+        return self.lookup(layer, experts, insert=True)
 
     def resize(self, new_capacity: int):
         """Returns (moves [(src, dst)], evicted keys)."""
         assert new_capacity >= 0
+        assert self.policy == "global", "resize is defined for the global policy only"
         C = self.capacity
         if new_capacity >= C:
             self.key += [-1] * (new_capacity - C)

@@ -194,6 +194,12 @@ def zipf_sets(shape: Shape, layer: int, T: int, steps: int, s: float,
     return out
 
 
+def popularity_order(shape: Shape, layer: int, seed: int = 0) -> np.ndarray:
+    """The layer's experts from most to least popular under zipf_sets's
+    ranking pi (the same permutation)."""
+    return _rng(seed, _PERM, layer).permutation(shape.E).astype(np.int32)
+
+
 def bias_from_sets(sets_step: np.ndarray, E: int) -> np.ndarray:
     """Router bias [T][E] fp32: BIAS_STRENGTH on each row's drawn set."""
     T = sets_step.shape[0]

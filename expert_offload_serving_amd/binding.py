@@ -31,7 +31,7 @@ class MoEError(RuntimeError):
 class moe_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "hidden", "inter", "n_experts", "top_k", "n_layers", "has_shared", "renormalize",
-        "max_tokens", "cache_slots", "staging_slots", "max_prefill_tokens")]
+        "max_tokens", "cache_slots", "staging_slots", "max_prefill_tokens", "cache_policy")]
 
 
 class moe_stats(ctypes.Structure):
@@ -122,6 +122,10 @@ def _stream(stream) -> Optional[int]:
 # ------------------------------------------------------------------ calls
 def moe_expert_bytes(hidden: int, inter: int) -> int:
     return int(lib.moe_expert_bytes(hidden, inter))
+
+
+# moe_config.cache_policy values, in enum order (MOE_CACHE_GLOBAL, ...)
+CACHE_POLICIES = ("global", "per_layer", "static")
 
 
 def moe_create(**fields) -> int:

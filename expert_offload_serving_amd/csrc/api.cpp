@@ -114,6 +114,19 @@ constexpr size_t kMaxTimingPairs = 65536;
 
 namespace moe {
 
+int fillable_slots(const Ctx* c, int layer, bool insert, int* slot0) {
+  int first = 0, n = c->C;
+  if (c->cfg.cache_policy == MOE_CACHE_PER_LAYER) {
+    const int64_t L = c->cfg.n_layers;
+    first = (int)(layer * (int64_t)c->C / L);
+    n = (int)((layer + 1) * (int64_t)c->C / L) - first;
+  } else if (c->cfg.cache_policy == MOE_CACHE_STATIC && !insert) {
+    n = 0;
+  }
+  if (slot0) *slot0 = first;
+  return n;
+}
+
 hipEvent_t timing_event(Ctx* c) {
   if (c->ev_next == c->ev_pool.size()) {
     hipEvent_t e;
@@ -177,6 +190,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       f.n_experts < f.top_k || f.n_experts > 1024 || f.max_tokens < 1 ||
       f.max_tokens > 64 || f.cache_slots < 0 || f.staging_slots < 0 ||
       f.max_prefill_tokens < 0 || (f.has_shared != 0 && f.has_shared != 1) ||
+      f.cache_policy < MOE_CACHE_GLOBAL || f.cache_policy > MOE_CACHE_STATIC ||
       (f.renormalize != 0 && f.renormalize != 1))
     return fail(MOE_ERR_INVALID_ARG, "moe_config field out of range");
   if ((int64_t)f.cache_slots > (int64_t)f.n_layers * f.n_experts)
@@ -365,7 +379,8 @@ moe_status moe_layer_forward(moe_ctx* ctx, int32_t layer, const void* d_x, int32
   if (!c->router_set[layer]) return fail(MOE_ERR_STATE, "router of this layer not set");
   if (f.has_shared && !c->shared_set[layer])
     return fail(MOE_ERR_STATE, "shared expert of this layer not set");
-  const int worst_bypass = std::max(0, std::min(T * f.top_k, f.n_experts) - c->C);
+  const int worst_bypass =
+      std::max(0, std::min(T * f.top_k, f.n_experts) - fillable_slots(c, layer, false, nullptr));
   if (worst_bypass > f.staging_slots)
     return fail(MOE_ERR_CAPACITY, "staging_slots (" + std::to_string(f.staging_slots) +
                                       ") below worst-case bypass count " +
@@ -418,11 +433,11 @@ moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer, const int32_t* d_exp
   Ctx* c = C_(ctx);
   if (layer < 0 || layer >= c->cfg.n_layers || !d_experts || !d_n || !d_slot)
     return fail(MOE_ERR_INVALID_ARG, "bad layer or NULL pointer");
-  const int worst_bypass = std::max(0, c->max_unique - c->C);
+  const int worst_bypass = std::max(0, c->max_unique - fillable_slots(c, layer, false, nullptr));
   if (worst_bypass > c->cfg.staging_slots)
     return fail(MOE_ERR_CAPACITY, "staging_slots below worst-case bypass count");
   hipStream_t st = (hipStream_t)stream;
-  HIPCHK(launch_cache_lookup(c, layer, d_experts, d_n, c->max_unique, d_slot, st));
+  HIPCHK(launch_cache_lookup(c, layer, d_experts, d_n, c->max_unique, d_slot, false, st));
   HIPCHK(launch_fill(c->d_fills, c->d_meta, c->max_unique, c->rec_bytes, st));
   return MOE_OK;
 }
@@ -441,14 +456,15 @@ moe_status expert_cache_fill(moe_ctx* ctx, int32_t layer, const int32_t* h_exper
       return fail(MOE_ERR_INVALID_ARG, "expert ids must be ascending and unique");
   }
   if (n == 0) return MOE_OK;
-  if (std::max(0, n - c->C) > c->cfg.staging_slots)
+  if (std::max(0, n - fillable_slots(c, layer, true, nullptr)) > c->cfg.staging_slots)
     return fail(MOE_ERR_CAPACITY, "fill would bypass more experts than staging_slots");
   hipStream_t st = (hipStream_t)stream;
   std::vector<int32_t> buf(h_experts, h_experts + n);
   buf.push_back(n);
   HIPCHK(hipStreamSynchronize(st));
   HIPCHK(hipMemcpy(c->d_lookup_ids, buf.data(), buf.size() * 4, hipMemcpyHostToDevice));
-  HIPCHK(launch_cache_lookup(c, layer, c->d_lookup_ids, c->d_lookup_ids + n, n, c->d_slotcode, st));
+  HIPCHK(launch_cache_lookup(c, layer, c->d_lookup_ids, c->d_lookup_ids + n, n, c->d_slotcode, true,
+                             st));
   HIPCHK(launch_fill(c->d_fills, c->d_meta, n, c->rec_bytes, st));
   HIPCHK(hipStreamSynchronize(st));
   return MOE_OK;
@@ -461,6 +477,8 @@ moe_status expert_cache_resize(moe_ctx* ctx, int32_t new_slots, void* stream) {
   if (new_slots < 0 || (int64_t)new_slots > (int64_t)L * E)
     return fail(MOE_ERR_INVALID_ARG, "new_slots outside [0, n_layers*n_experts]");
   if (new_slots > kMaxCacheSlots) return fail(MOE_ERR_UNSUPPORTED, "cache_slots above 4096");
+  if (c->cfg.cache_policy != MOE_CACHE_GLOBAL)
+    return fail(MOE_ERR_UNSUPPORTED, "resize is supported for the global cache policy only");
   hipStream_t st = (hipStream_t)stream;
   HIPCHK(hipStreamSynchronize(st));
   HIPCHK(hipDeviceSynchronize());

@@ -86,9 +86,12 @@ constexpr int kOrderKeyShift = 12;   // slots < 4096
 
 struct LookupArgs {
   int32_t layer, E, C, staging;
+  int32_t slot0;           // first slot this lookup may fill (C slots from it)
+  int32_t insert;          // 0: misses bypass (the static policy's lookups)
   int32_t* key;            // [C]
   uint64_t* stamp;         // [C]
-  int32_t* order;          // [C] packed entries, least recent first
+  int32_t* order;          // [C] packed entries, least recent first (the
+                           // sub-array of the slots slot0 .. slot0+C-1)
   int32_t* order_tmp;      // [C]
   int32_t* map;            // [L*E] slot of each key or -1
   uint8_t* hitflag;        // [C]
@@ -183,7 +186,7 @@ hipError_t launch_router(const uint16_t* x, int T, int H, int E, const float* w_
 hipError_t launch_route_finalize(Ctx* c, int layer, int T, int32_t* user_ids,
                                  float* user_gates, hipStream_t st);
 hipError_t launch_cache_lookup(Ctx* c, int layer, const int32_t* d_experts,
-                               const int32_t* d_n, int n_max, int32_t* d_slot,
+                               const int32_t* d_n, int n_max, int32_t* d_slot, bool insert,
                                hipStream_t st);
 hipError_t launch_fill(const FillEntry* fills, const DevMeta* meta, int max_fill,
                        size_t bytes, hipStream_t st);
@@ -216,6 +219,11 @@ hipEvent_t timing_event(Ctx* c);
     else                                                                                \
       KERNEL<<<GRID, BLOCK, SHM, ST>>>(__VA_ARGS__);                                    \
   } while (0)
+
+// Slots a lookup of `layer` may fill under the context's cache policy: the
+// first one in *slot0 (may be NULL), the count returned.  insert = false for
+// lookups that place nothing under the static policy (forward, lookup).
+int fillable_slots(const Ctx* c, int layer, bool insert, int* slot0);
 
 // prefill
 int prefill_max_tiles(int T, int k, int E);

@@ -127,7 +127,7 @@ __device__ void block_lookup(const LookupArgs& a, LookupShared& ls, const int* s
   const int C = a.C;
   const uint64_t clock0 = ls.clock0;
   if (tid == 0) ls.evict = 0;
-  for (int s = tid; s < C; s += nt) ls.hit[s] = 0;
+  for (int s = tid; s < C; s += nt) ls.hit[a.slot0 + s] = 0;
 
   const int u = tid;
   const int e = u < n ? s_U[u] : -1;
@@ -141,7 +141,7 @@ __device__ void block_lookup(const LookupArgs& a, LookupShared& ls, const int* s
   const int ranks = block_excl_scan((hit ? 1 : 0) | (miss ? 1 << 16 : 0), ls.tmp, &both);  // barrier: hit[] cleared
   const int hrank = ranks & 0xFFFF, mrank = ranks >> 16;
   const int n_hit = both & 0xFFFF, n_miss = both >> 16;
-  const int n_fill = min(n_miss, C - n_hit);
+  const int n_fill = a.insert ? min(n_miss, C - n_hit) : 0;
   if (hit) {
     ls.hit[slot] = 1;
     a.stamp[slot] = clock0 + 1 + (uint64_t)hrank;
@@ -341,15 +341,19 @@ __global__ __launch_bounds__(kFinalizeThreads) void cache_lookup_kernel(
   for (int u = threadIdx.x; u < n; u += blockDim.x) out_slot[u] = s_slot[u];
 }
 
-LookupArgs make_lookup_args(Ctx* c, int layer) {
+LookupArgs make_lookup_args(Ctx* c, int layer, bool insert) {
   LookupArgs la;
   la.layer = layer;
   la.E = c->cfg.n_experts;
-  la.C = c->C;
+  // the lookup runs the same rule on the recency order of the slots the
+  // policy lets this layer fill (a layer's share is a contiguous range, and
+  // the order of an unresized cache keeps each share's slots in its range)
+  la.C = fillable_slots(c, layer, true, &la.slot0);
+  la.insert = c->cfg.cache_policy == MOE_CACHE_STATIC ? insert : true;
   la.staging = c->cfg.staging_slots;
   la.key = c->d_key;
   la.stamp = c->d_stamp;
-  la.order = c->d_order;
+  la.order = c->d_order + la.slot0;
   la.order_tmp = c->d_order_tmp;
   la.map = c->d_map;
   la.hitflag = c->d_hitflag;
@@ -400,7 +404,7 @@ hipError_t launch_route_finalize(Ctx* c, int layer, int T, int32_t* user_ids,
   a.tok = c->d_tok;
   a.items = c->d_items;
   a.shared_w = c->cfg.has_shared ? c->d_shared + (size_t)layer * c->stride : nullptr;
-  a.la = make_lookup_args(c, layer);
+  a.la = make_lookup_args(c, layer, false);
   const int nk = (a.E + 63) / 64;
   if (nk <= 1)
     route_finalize_kernel<1><<<1, kFinalizeThreads, 0, st>>>(a);
@@ -416,9 +420,9 @@ hipError_t launch_route_finalize(Ctx* c, int layer, int T, int32_t* user_ids,
 }
 
 hipError_t launch_cache_lookup(Ctx* c, int layer, const int32_t* d_experts, const int32_t* d_n,
-                               int n_max, int32_t* d_slot, hipStream_t st) {
-  cache_lookup_kernel<<<1, kFinalizeThreads, 0, st>>>(make_lookup_args(c, layer), d_experts, d_n,
-                                                      n_max, d_slot);
+                               int n_max, int32_t* d_slot, bool insert, hipStream_t st) {
+  cache_lookup_kernel<<<1, kFinalizeThreads, 0, st>>>(make_lookup_args(c, layer, insert),
+                                                      d_experts, d_n, n_max, d_slot);
   return hipGetLastError();
 }
 

@@ -13,16 +13,19 @@ class MoEEngine:
 
     def __init__(self, H: int, I: int, E: int, k: int, n_layers: int = 1,
                  has_shared: bool = False, renormalize: bool = True, max_tokens: int = 16,
-                 cache_slots: int = 0, staging_slots: int = 0, max_prefill_tokens: int = 0):
+                 cache_slots: int = 0, staging_slots: int = 0, max_prefill_tokens: int = 0,
+                 cache_policy: str = "global"):
         self.H, self.I, self.E, self.k, self.L = H, I, E, k, n_layers
         self.has_shared = bool(has_shared)
         self.max_tokens = max_tokens
         self.max_prefill_tokens = max_prefill_tokens
+        self.cache_policy = cache_policy
         self.ctx = b.moe_create(hidden=H, inter=I, n_experts=E, top_k=k, n_layers=n_layers,
                                 has_shared=int(has_shared), renormalize=int(renormalize),
                                 max_tokens=max_tokens, cache_slots=cache_slots,
                                 staging_slots=staging_slots,
-                                max_prefill_tokens=max_prefill_tokens)
+                                max_prefill_tokens=max_prefill_tokens,
+                                cache_policy=b.CACHE_POLICIES.index(cache_policy))
 
     # ---------------------------------------------------------------- weights
     def set_router(self, layer: int, w_router: np.ndarray):

@@ -63,6 +63,27 @@ enum {
 
 typedef struct moe_ctx moe_ctx;
 
+/*
+ * Placement policy of the decode expert cache (moe_config.cache_policy).
+ * The pages use one global LRU across the MoE layers instead of locking
+ * chosen experts into GPU memory at start-up, and compare its miss rate with
+ * other placements at equal capacity (jansverre.net FreeToken article,
+ * section "Hvorfor er båndbredden viktigere enn antall kjerner?").  The two
+ * alternatives exist for that comparison; every policy uses the lookup rule
+ * of moe_layer_forward:
+ *  - GLOBAL: all C slots are one LRU over (layer, expert) keys;
+ *  - PER_LAYER: layer l owns slots floor(l*C/L) .. floor((l+1)*C/L) - 1, and
+ *    a lookup of layer l takes victims only from them;
+ *  - STATIC: lookups never insert (every miss bypasses through staging);
+ *    only expert_cache_fill places experts, with the GLOBAL rule.
+ * expert_cache_resize is supported under GLOBAL only.
+ */
+enum {
+  MOE_CACHE_GLOBAL = 0,
+  MOE_CACHE_PER_LAYER = 1,
+  MOE_CACHE_STATIC = 2
+};
+
 /* Layer-stack shape and capacities, fixed at moe_create. */
 typedef struct moe_config {
   int32_t hidden;          /* H: multiple of 128, 128..6144                  */
@@ -78,8 +99,10 @@ typedef struct moe_config {
                               4096)                                          */
   int32_t staging_slots;   /* S: HBM slots for misses that bypass the cache  */
   int32_t max_prefill_tokens; /* 0 disables moe_prefill_forward; at most
-                              what keeps T*H*2 and T*(k+1)*I*4 bytes below
-                              2 GiB (else UNSUPPORTED)                      */
+                              what keeps T*H*2 and T*(k+1)*I*2 bytes (and
+                              the prefill h records) below 2 GiB (else
+                              UNSUPPORTED)                                  */
+  int32_t cache_policy;    /* MOE_CACHE_GLOBAL (0), _PER_LAYER or _STATIC  */
 } moe_config;
 
 /* Counters since creation or the last moe_reset_stats. */
@@ -157,10 +180,11 @@ moe_status moe_set_layer(moe_ctx* ctx, int32_t layer, const float* h_router,
  *   (logit descending, expert ascending); gates = softmax over the chosen
  *   logits (renormalize = 1) or the full-softmax probabilities of the chosen
  *   experts (renormalize = 0); pairs (t, j) permuted stably by expert;
- *   the unique experts looked up in the global LRU cache (hits stamped in
+ *   the unique experts looked up in the LRU cache (hits stamped in
  *   ascending expert order, then misses take the empty slots in ascending
- *   index and then the least recently used slots not hit in this call; misses
- *   beyond those bypass through staging slots without changing the state),
+ *   index and then the least recently used slots not hit in this call, among
+ *   the slots the cache policy lets this layer fill; misses beyond those
+ *   bypass through staging slots without changing the state),
  *   misses copied from the pinned pool by a device kernel; the SwiGLU FFN of
  *   every (token, expert) pair on MXFP4 weights dequantised to bf16 inside
  *   the MFMA loads, h rounded to bf16, expert outputs in fp32;
@@ -171,7 +195,8 @@ moe_status moe_set_layer(moe_ctx* ctx, int32_t layer, const float* h_router,
  * rounding.  d_ids (int32 [T][k]) and d_gates (fp32 [T][k]) receive the
  * routing when not NULL.  Errors: INVALID_ARG (T out of range, NULL x/y, bad layer), STATE
  * (router not set), CAPACITY (staging_slots cannot cover the worst-case
- * bypass count max(0, min(T*k, E) - C)), HIP.
+ * bypass count max(0, min(T*k, E) - C'), C' the slots this layer may fill:
+ * C, its share under PER_LAYER, 0 under STATIC), HIP.
  */
 moe_status moe_layer_forward(moe_ctx* ctx, int32_t layer, const void* d_x,
                              int32_t T, const float* d_bias, void* d_y,
@@ -201,7 +226,9 @@ moe_status moe_prefill_forward(moe_ctx* ctx, int32_t n_layers,
  * with the moe_layer_forward rule and fill the misses.  d_experts: int32
  * [>= *d_n]; d_n: int32 on the device, 0 <= *d_n <= min(E, max_tokens*k)
  * (larger values are clamped); d_slot: int32 [*d_n] receives the slot
- * (>= 0) or -1-b for staging slot b.  Errors: INVALID_ARG, HIP.
+ * (>= 0) or -1-b for staging slot b.  Errors: INVALID_ARG, CAPACITY
+ * (staging_slots below the worst-case bypass count, as for
+ * moe_layer_forward), HIP.
  */
 moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer,
                                const int32_t* d_experts, const int32_t* d_n,
@@ -209,7 +236,8 @@ moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer,
 
 /*
  * Preload experts of one layer: the same rule as a lookup of h_experts
- * (ascending unique, 0 <= n <= min(E, max_tokens*k)), without compute.
+ * (ascending unique, 0 <= n <= min(E, max_tokens*k)), without compute.  It
+ * inserts under every policy (it is how the STATIC set is placed).
  * Errors: INVALID_ARG (unsorted, duplicate or out-of-range ids), CAPACITY
  * (bypass would exceed staging_slots), HIP.
  */
@@ -224,7 +252,7 @@ moe_status expert_cache_fill(moe_ctx* ctx, int32_t layer,
  * occupied, moves the survivors held in slots >= new_slots (ascending) into
  * the lowest empty slots < new_slots (ascending) keeping their recency,
  * then releases the tail of the slot memory.  Errors: INVALID_ARG,
- * UNSUPPORTED (above 4096 slots), OOM, HIP.
+ * UNSUPPORTED (above 4096 slots, or a policy other than GLOBAL), OOM, HIP.
  */
 moe_status expert_cache_resize(moe_ctx* ctx, int32_t new_slots, void* stream);
 

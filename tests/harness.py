@@ -81,12 +81,13 @@ class Model:
 
 
 def make_engine(shape: gen.Shape, max_tokens: int, cache_slots: int, staging_slots: int,
-                max_prefill_tokens: int = 0):
+                max_prefill_tokens: int = 0, cache_policy: str = "global"):
     from expert_offload_serving_amd import MoEEngine
     return MoEEngine(shape.H, shape.I, shape.E, shape.k, n_layers=shape.layers,
                      has_shared=shape.shared, renormalize=shape.renormalize,
                      max_tokens=max_tokens, cache_slots=cache_slots,
-                     staging_slots=staging_slots, max_prefill_tokens=max_prefill_tokens)
+                     staging_slots=staging_slots, max_prefill_tokens=max_prefill_tokens,
+                     cache_policy=cache_policy)
 
 
 def check_rounding(y_bf16, y32, what=""):
@@ -112,15 +113,15 @@ class DecodeRun:
 
     def __init__(self, wl: gen.Workload, model: Model, T: int, cache_slots: Optional[int] = None,
                  staging_slots: Optional[int] = None, max_tokens: Optional[int] = None,
-                 steps: Optional[int] = None):
+                 steps: Optional[int] = None, cache_policy: str = "global"):
         import torch
         self.wl, self.model, self.T = wl, model, T
         sh = wl.shape
         self.C = wl.cache_slots if cache_slots is None else cache_slots
         S = wl.staging_slots if staging_slots is None else staging_slots
-        self.eng = make_engine(sh, max_tokens or T, self.C, S)
+        self.eng = make_engine(sh, max_tokens or T, self.C, S, cache_policy=cache_policy)
         model.load(self.eng)
-        self.cache = oracle.SlotCache(self.C, sh.E)
+        self.cache = oracle.SlotCache(self.C, sh.E, sh.layers, cache_policy)
         self.steps = wl.steps if steps is None else steps
         self.sets = ([gen.zipf_sets(sh, l, T, self.steps, wl.zipf_s, wl.overlap, model.seed)
                       for l in range(sh.layers)] if wl.zipf_s else None)

@@ -51,6 +51,9 @@ def parse():
                     help="T=1 decode steps of the DeepSeek-V4-Flash-shaped stack (0: skip)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="also run one plain copy of this many MiB (counter calibration)")
+    ap.add_argument("--policy-study", type=int, default=0, metavar="STEPS",
+                    help="instead of the benchmark line: DeepSeek-V4-Flash-shaped decode under "
+                         "each cache placement policy (STEPS timed steps per run)")
     return ap.parse_args()
 
 
@@ -68,21 +71,69 @@ def kernel_bytes(sh, lookups, calls, pairs, T_total):
     return gateup, down
 
 
-def make_engine(sh, T, cache_slots, staging_slots, prefill_tokens=0):
+def make_engine(sh, T, cache_slots, staging_slots, prefill_tokens=0, cache_policy="global"):
     from expert_offload_serving_amd import MoEEngine
     return MoEEngine(sh.H, sh.I, sh.E, sh.k, n_layers=sh.layers, has_shared=sh.shared,
                      renormalize=sh.renormalize, max_tokens=T, cache_slots=cache_slots,
-                     staging_slots=staging_slots, max_prefill_tokens=prefill_tokens)
+                     staging_slots=staging_slots, max_prefill_tokens=prefill_tokens,
+                     cache_policy=cache_policy)
 
 
-def load_weights(eng, sh, seed=0):
+def load_weights(eng, sh, seed=0, distinct=None):
+    """Router and expert weights of every layer.  distinct = n reuses n
+    generated expert records per layer (same sizes and bytes moved, less
+    set-up time) where the expert values do not matter."""
     from workload import gen
     for l in range(sh.layers):
         eng.set_router(l, gen.router_weights(sh, l, seed))
+        recs = {}
         for e in range(sh.E):
-            eng.set_expert(l, e, gen.expert_weights(sh, l, e, seed))
+            src = e if distinct is None else e % distinct
+            if src not in recs:
+                recs[src] = gen.expert_weights(sh, l, src, seed)
+            eng.set_expert(l, e, recs[src])
+            if distinct is None:
+                recs.clear()
         if sh.shared:
             eng.set_expert(l, -1, gen.expert_weights(sh, l, -1, seed))
+
+
+def policy_study(steps, warmup, seed=0):
+    """Decode of the DeepSeek-V4-Flash-shaped stack (4 layers, 256 experts of
+    13.4 MB, 256 slots = a quarter of each layer's experts) under each cache
+    placement policy at equal capacity, T = 1 and 32, each run from a fresh
+    engine: the global LRU, per-layer shares of 64 slots, and a static set
+    (each layer's 64 most popular experts under the trace's ranking, placed
+    before the run; every other expert bypasses through staging)."""
+    from workload import gen
+    wl = gen.WORKLOADS["dsv4_decode"]
+    sh = wl.shape
+    rows = []
+    for policy in ("global", "per_layer", "static"):
+        for T in wl.Ts:
+            eng = make_engine(sh, T, wl.cache_slots, wl.staging_slots, cache_policy=policy)
+            load_weights(eng, sh, seed, distinct=8)
+            if policy == "static":
+                per = wl.cache_slots // sh.layers
+                for l in range(sh.layers):
+                    top = sorted(gen.popularity_order(sh, l, seed)[:per].tolist())
+                    for i in range(0, per, T * sh.k):
+                        eng.cache_fill(l, top[i:i + T * sh.k])
+            eng.reset_stats()
+            r = run_decode(wl, T, steps, warmup, seed, eng=eng)
+            st = r["stats"]
+            n = max(st["lookups"], 1)
+            rows.append({"policy": policy, "T": T, "hit_rate": round(st["hits"] / n, 4),
+                         "fill_rate": round(st["fills"] / n, 4),
+                         "bypass_rate": round(st["bypasses"] / n, 4),
+                         "tokens_per_s": round(r["tokens_per_s"], 1),
+                         "ms_per_step": round(r["ms_per_step"], 3),
+                         "h2d_gbs": round(r["h2d_gbs"], 2)})
+            print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+            eng.close()
+    return {"policy_study": rows, "config": {"workload": wl.name, "layers": sh.layers, "E": sh.E,
+            "k": sh.k, "cache_slots": wl.cache_slots, "staging_slots": wl.staging_slots,
+            "steps": steps, "warmup": warmup, "zipf_s": wl.zipf_s, "overlap": wl.overlap}}
 
 
 def bf16_dev(bits):
@@ -327,6 +378,9 @@ def main():
     import torch
     from workload import gen
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if a.policy_study > 0:
+        print(json.dumps(policy_study(a.policy_study, min(a.warmup, a.policy_study))), flush=True)
+        return
     wl = gen.WORKLOADS[a.workload]
     T = a.T or max(wl.Ts)
     res = run_decode(wl, T, a.steps, a.warmup)

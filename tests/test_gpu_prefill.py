@@ -28,7 +28,11 @@ def _check_layer(run, layer, tokens, check_ids):
 @pytest.mark.parametrize("T,kw", [(300, dict(E=32, k=4, shared=True, layers=3)),
                                   (129, dict(E=16, k=2, layers=2)),
                                   (64, dict(E=64, k=8, shared=True, renormalize=False)),
-                                  (1000, dict(H=384, I=256, E=40, k=6, layers=2))])
+                                  (1000, dict(H=384, I=256, E=40, k=6, layers=2)),
+                                  # I = 3 chunks of 128 (h's last remainder records come from
+                                  # a half-filled gate/up column block), H = 640 (the last down
+                                  # column block is partial)
+                                  (200, dict(H=640, I=384, E=12, k=3, shared=True))])
 def test_prefill_small_all_tokens(T, kw):
     """Ragged token counts (not multiples of the 64/128-row tiles), every
     layer, every token."""

@@ -597,18 +597,8 @@ __device__ __forceinline__ int wave_mfrags(int rows) {
   return (((rows + 15) >> 4) - mh + 1) >> 1;
 }
 
-// E2M3 code of t = lo * 2^-E (|t| <= 7.5), rounded to nearest even: for
-// |t| in [2^e, 2^(e+1)) (e = 0, 1, 2; e = 0 also below 1, the subnormals)
-// the grid step is 2^(e-3), and 8e + RNE(|t| * 2^(3-e)) is the magnitude
-// code (a carry into the next binade gives the right code as well).
-__device__ __forceinline__ uint32_t e2m3_code(float lo, float inv_scale) {
-  const float t = lo * inv_scale;
-  const float a = fabsf(t);
-  const int ex = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;
-  const int e = ex < 0 ? 0 : (ex > 2 ? 2 : ex);
-  const float q = __builtin_rintf(a * __uint_as_float((uint32_t)(130 - e) << 23));
-  return (uint32_t)(8 * e + (int)q) | (t < 0.0f ? 32u : 0u);
-}
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int32_t i32x6 __attribute__((ext_vector_type(6)));
 
 template <int MF>
 __device__ __forceinline__ void gateup_tile(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
@@ -655,13 +645,15 @@ __device__ __forceinline__ void gateup_tile(const GemmTile& gt, __amdgpu_buffer_
         const f32x4 x4 = *reinterpret_cast<const f32x4*>(src + 4 * t);
         v[4 * t] = x4[0], v[4 * t + 1] = x4[1], v[4 * t + 2] = x4[2], v[4 * t + 3] = x4[3];
       }
+      // bf16 of each value (v_cvt_pk_bf16_f32: nearest, ties to even) and
+      // the remainder, exact in fp32
       uint32_t hp[16];
       float mx = 0.0f;
 #pragma unroll
       for (int t = 0; t < 32; t++) {
-        const uint32_t hb = f32_to_bf16_rne(v[t]);
+        const uint32_t hb = __builtin_bit_cast(uint16_t, (__bf16)v[t]);
         hp[t >> 1] = (t & 1) ? (hp[t >> 1] | (hb << 16)) : hb;
-        v[t] -= __uint_as_float(hb << 16);  // the remainder, exact in fp32
+        v[t] -= __uint_as_float(hb << 16);
         mx = fmaxf(mx, fabsf(v[t]));
       }
       // block exponent: the largest remainder at most 7.5 * 2^E
@@ -671,15 +663,19 @@ __device__ __forceinline__ void gateup_tile(const GemmTile& gt, __amdgpu_buffer_
         E = E < -126 ? -126 : E;  // 2^E stays a normal float
         if (mx > 7.5f * __uint_as_float((uint32_t)(E + 127) << 23)) E += 1;
       }
-      const float inv = __uint_as_float((uint32_t)(127 - E) << 23);
-      uint32_t d[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+      // E2M3 codes of remainder / 2^E, nearest with ties to even (|.| <= 7.5 by
+      // the choice of E), packed 6 bits each: v_cvt_scalef32_2xpk16_fp6_f32
+      // writes its first operand's element j at position 2j and its second's
+      // at 2j + 1, so it takes the even and the odd elements.  An all-zero
+      // block gives zero codes with any scale.
+      f32x16 ev, od;
 #pragma unroll
-      for (int t = 0; t < 32; t++) {
-        const uint32_t c = e2m3_code(v[t], inv);
-        const int bit = 6 * t, dw = bit >> 5, sh = bit & 31;
-        d[dw] |= c << sh;
-        if (sh > 26) d[dw + 1] |= c >> (32 - sh);
-      }
+      for (int j = 0; j < 16; j++) ev[j] = v[2 * j], od[j] = v[2 * j + 1];
+      const float scale = mx > 0.0f ? __uint_as_float((uint32_t)(E + 127) << 23) : 1.0f;
+      const i32x6 d6 = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, scale);
+      uint32_t d[6];
+#pragma unroll
+      for (int j = 0; j < 6; j++) d[j] = (uint32_t)d6[j];
       const int g = 2 * i + mh, m = g * 16 + row;
       if (m < gt.rows) {
         u32x4* dst = reinterpret_cast<u32x4*>(hhi + (row0 + m) * I + 16 * p0 + 32 * b);

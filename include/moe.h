@@ -187,7 +187,9 @@ moe_status moe_set_layer(moe_ctx* ctx, int32_t layer, const float* h_router,
  *   bypass through staging slots without changing the state),
  *   misses copied from the pinned pool by a device kernel; the SwiGLU FFN of
  *   every (token, expert) pair on MXFP4 weights dequantised to bf16 inside
- *   the MFMA loads, h rounded to bf16, expert outputs in fp32;
+ *   the MFMA loads, fp32 accumulation, h carried between the two matrices as
+ *   bf16 plus a second bf16 plane of its remainder (about 16 significant
+ *   bits), expert outputs in fp32;
  *   y[t] = sum_j g[t,j] o[t,j] (+ shared expert output), fp32, rounded to
  *   bf16 (nearest, ties to even).  Nothing is synchronised with the host.
  * d_x: bf16 [T][H].  d_bias: fp32 [T][E] or NULL.  d_y: bf16 [T][H].
@@ -210,7 +212,9 @@ moe_status moe_layer_forward(moe_ctx* ctx, int32_t layer, const void* d_x,
  * stream; the upload of layer l+1 overlaps the compute of layer l and waits
  * for layer l-1 (the previous reader of that buffer).  Expert FFNs run as
  * grouped MFMA GEMMs.  The cache state is not used or changed.  Math as in
- * moe_layer_forward.  h_x, h_bias, h_y are host arrays of n_layers device
+ * moe_layer_forward, except that h's remainder travels as fp6 (E2M3) with one
+ * power-of-two scale per 32 values, which keeps h to about 2^-14 of each
+ * block's largest value.  h_x, h_bias, h_y are host arrays of n_layers device
  * pointers (bf16 [T][H] in, fp32 [T][E] bias or NULL entries / NULL array,
  * bf16 [T][H] out, and optionally fp32 [T][H] pre-rounding outputs in h_y32,
  * a NULL array or NULL entries when not wanted).  Errors: INVALID_ARG, STATE

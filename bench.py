@@ -283,6 +283,8 @@ def run_dsv4(prefill_steps, decode_steps, decode_warmup, seed=0):
             "mfma_tflops": round(tflops, 1),
             "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
             "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            # matrix-core busy share by counters (profiles/mfma_busy_*.md)
+            "mfma_busy_counters": mfma_busy_from_profile(),
             "gateup_prefill_kernel": {"avg_us": round(1e3 * gu_ms, 1),
                                       "tflops": round(2 * flops_layer / 3 / (gu_ms * 1e9), 1)},
             "down_prefill_kernel": {"avg_us": round(1e3 * dn_ms, 1),
@@ -333,12 +335,12 @@ def cpu_baseline(wl, T, seconds):
                       f"fp64 expert loops) in {el:.1f}s"}
 
 
-def traffic_from_profile(kernel, workload):
-    """HBM bytes per launch of `kernel` from the committed counter summary
-    (profiles/traffic_<kernel>_<workload>.md), if it was taken on the current
-    source of the kernel's file; else None."""
+def profile_fields(name):
+    """The `- key: value` fields of a committed counter summary in profiles/,
+    or None when the file is missing or was taken on another version of the
+    source file it names (its source_sha256)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -351,11 +353,31 @@ def traffic_from_profile(kernel, workload):
         return None
     if hashlib.sha256(open(src, "rb").read()).hexdigest() != fields.get("source_sha256"):
         return None
+    return fields
+
+
+def mfma_busy_from_profile():
+    """Matrix-core busy share (SQ_VALU_MFMA_BUSY_CYCLES per SIMD over
+    GRBM_GUI_ACTIVE per XCD) of the two prefill GEMMs from the committed
+    counter summary, or None."""
+    f = profile_fields("mfma_busy_prefill_dsv4_T4096.md")
+    if f is None:
+        return None
     try:
-        return int(fields["hbm_bytes_per_launch"])
+        return {k: float(f["busy_" + k]) for k in ("gateup_prefill_kernel", "down_prefill_kernel")}
     except (KeyError, ValueError):
         return None
 
+
+def traffic_from_profile(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/traffic_<kernel>_<workload>.md), if it was taken on the current
+    source of the kernel's file; else None."""
+    f = profile_fields(f"traffic_{kernel}_{workload}.md")
+    try:
+        return int(f["hbm_bytes_per_launch"]) if f else None
+    except (KeyError, ValueError):
+        return None
 
 def calibrate_copy(mb):
     """One plain device-to-device copy of `mb` MiB through the library's copy

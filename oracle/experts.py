@@ -12,14 +12,28 @@ section "Hvor raskt kjører modellene?").  Readings where they are silent:
 * combine: y_t = sum_j g[t, j] * o_{t,j} (+ o_{t,shared}); the shared expert
   is added with weight 1 and takes no part in top-k or renormalisation;
 * all arithmetic here is fp64 on exactly dequantised weights.
+
+Experts come as MXFP4 (codes and scales, decoded by ``mxfp4.dequant``) or as
+bf16 matrices, the format the pages run the 35B-A3B model in (jansverre.net
+FreeToken article, section "Hvor raskt kjører modellene?"); a bf16 value is
+the fp32 number whose upper 16 bits are its bit pattern and whose lower 16
+are zero.
 """
 import numpy as np
 
 from .mxfp4 import dequant
 
 
+def bf16_values(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> their values as fp32."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
 def dequant_expert(w):
-    """Canonical packed expert -> (W_g, W_u, W_d) fp32, exact."""
+    """Canonical expert (MXFP4 codes and scales, or bf16 matrices) ->
+    (W_g, W_u, W_d) fp32, exact."""
+    if hasattr(w, "wg"):
+        return bf16_values(w.wg), bf16_values(w.wu), bf16_values(w.wd)
     return dequant(w.qg, w.sg), dequant(w.qu, w.su), dequant(w.qd, w.sd)
 
 

@@ -50,7 +50,7 @@ class Model:
         self._cap = cache_entries
 
     def expert(self, layer: int, e: int):
-        return gen.expert_weights(self.shape, layer, e, self.seed)
+        return gen.expert_weights_of(self.shape, layer, e, self.seed)
 
     def mats(self, layer: int, e: int):
         key = (layer, e)

@@ -40,9 +40,13 @@ class Shape:
     layers: int = 1
     shared: bool = False      # one always-on shared expert per layer
     renormalize: bool = True  # renormalise the top-k gates to sum to 1
+    weights: str = "mxfp4"    # expert format: "mxfp4" or "bf16"
 
     def expert_bytes(self) -> int:
-        """MXFP4 bytes of one expert: 3 matrices, 4 bits + 8 bits per 32."""
+        """Bytes of one expert: 3 matrices, MXFP4 (4 bits + 8 bits per 32)
+        or bf16 (16 bits)."""
+        if self.weights == "bf16":
+            return 3 * self.H * self.I * 2
         return 3 * self.H * self.I * 17 // 32
 
 
@@ -192,6 +196,34 @@ def zipf_sets(shape: Shape, layer: int, T: int, steps: int, s: float,
             prev = np.sort(np.concatenate([keep, new]).astype(np.int64))
             out[st, r] = prev
     return out
+
+
+@dataclass
+class ExpertWeightsBF16:
+    """Canonical bf16 expert (bit patterns): rows are output features, K
+    contiguous.  wg, wu: [I][H]; wd: [H][I]."""
+    wg: np.ndarray
+    wu: np.ndarray
+    wd: np.ndarray
+
+
+def expert_weights_bf16(shape: Shape, layer: int, expert: int, seed: int = 0,
+                        sigma: float = 2.0 ** -5) -> ExpertWeightsBF16:
+    """Normal weights N(0, sigma^2) rounded to bf16 (sigma near the typical
+    magnitude of the MXFP4 draws).  ``expert = -1`` draws the shared expert."""
+    H, I = shape.H, shape.I
+    g = _rng(seed, _SHARED if expert < 0 else _EXPERT, layer, max(expert, 0), 16)
+    w = f32_to_bf16_bits((g.standard_normal(3 * H * I) * sigma).astype(np.float32))
+    n = H * I
+    return ExpertWeightsBF16(wg=w[:n].reshape(I, H), wu=w[n:2 * n].reshape(I, H),
+                             wd=w[2 * n:].reshape(H, I))
+
+
+def expert_weights_of(shape: Shape, layer: int, expert: int, seed: int = 0):
+    """The expert in the shape's weight format."""
+    if shape.weights == "bf16":
+        return expert_weights_bf16(shape, layer, expert, seed)
+    return expert_weights(shape, layer, expert, seed)
 
 
 def popularity_order(shape: Shape, layer: int, seed: int = 0) -> np.ndarray:

@@ -51,6 +51,9 @@ def parse():
                     help="T=1 decode steps of the DeepSeek-V4-Flash-shaped stack (0: skip)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="also run one plain copy of this many MiB (counter calibration)")
+    ap.add_argument("--weights", choices=("mxfp4", "bf16"), default="mxfp4",
+                    help="expert format of the decode workload (bf16: decode only, no "
+                         "DeepSeek-V4-Flash legs)")
     ap.add_argument("--policy-study", type=int, default=0, metavar="STEPS",
                     help="instead of the benchmark line: DeepSeek-V4-Flash-shaped decode under "
                          "each cache placement policy (STEPS timed steps per run)")
@@ -76,7 +79,7 @@ def make_engine(sh, T, cache_slots, staging_slots, prefill_tokens=0, cache_polic
     return MoEEngine(sh.H, sh.I, sh.E, sh.k, n_layers=sh.layers, has_shared=sh.shared,
                      renormalize=sh.renormalize, max_tokens=T, cache_slots=cache_slots,
                      staging_slots=staging_slots, max_prefill_tokens=prefill_tokens,
-                     cache_policy=cache_policy)
+                     cache_policy=cache_policy, weight_format=sh.weights)
 
 
 def load_weights(eng, sh, seed=0, distinct=None):
@@ -90,12 +93,12 @@ def load_weights(eng, sh, seed=0, distinct=None):
         for e in range(sh.E):
             src = e if distinct is None else e % distinct
             if src not in recs:
-                recs[src] = gen.expert_weights(sh, l, src, seed)
+                recs[src] = gen.expert_weights_of(sh, l, src, seed)
             eng.set_expert(l, e, recs[src])
             if distinct is None:
                 recs.clear()
         if sh.shared:
-            eng.set_expert(l, -1, gen.expert_weights(sh, l, -1, seed))
+            eng.set_expert(l, -1, gen.expert_weights_of(sh, l, -1, seed))
 
 
 def policy_study(steps, warmup, seed=0):
@@ -404,6 +407,9 @@ def main():
         print(json.dumps(policy_study(a.policy_study, min(a.warmup, a.policy_study))), flush=True)
         return
     wl = gen.WORKLOADS[a.workload]
+    if a.weights != "mxfp4":
+        from dataclasses import replace
+        wl = replace(wl, name=f"{wl.name}_{a.weights}", shape=replace(wl.shape, weights=a.weights))
     T = a.T or max(wl.Ts)
     res = run_decode(wl, T, a.steps, a.warmup)
     extra = {}
@@ -440,7 +446,8 @@ def main():
         "config": {"workload": wl.name, "T": T, "H": sh.H, "I": sh.I, "E": sh.E, "k": sh.k,
                    "layers": sh.layers, "shared_expert": sh.shared,
                    "cache_slots": wl.cache_slots, "staging_slots": wl.staging_slots,
-                   "weights": "MXFP4 (E2M1 + E8M0/32)", "zipf_s": wl.zipf_s,
+                   "weights": ("MXFP4 (E2M1 + E8M0/32)" if sh.weights == "mxfp4" else sh.weights),
+                   "zipf_s": wl.zipf_s,
                    "overlap": wl.overlap},
         "roofline": roof,
         "cache": {"hit_rate": round(res["hit_rate"], 4), **{k: res["stats"][k] for k in
@@ -448,7 +455,7 @@ def main():
         "pcie_h2d_gbs": round(res["h2d_gbs"], 2),
         "other_T": extra,
     }
-    if a.prefill_steps > 0 or a.dsv4_decode_steps > 0:
+    if a.weights == "mxfp4" and (a.prefill_steps > 0 or a.dsv4_decode_steps > 0):
         line.update(run_dsv4(a.prefill_steps, a.dsv4_decode_steps, max(a.dsv4_decode_steps // 4, 1)))
     if a.calibrate_copy_mb > 0:
         calibrate_copy(a.calibrate_copy_mb)

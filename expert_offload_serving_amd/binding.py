@@ -31,7 +31,8 @@ class MoEError(RuntimeError):
 class moe_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "hidden", "inter", "n_experts", "top_k", "n_layers", "has_shared", "renormalize",
-        "max_tokens", "cache_slots", "staging_slots", "max_prefill_tokens", "cache_policy")]
+        "max_tokens", "cache_slots", "staging_slots", "max_prefill_tokens", "cache_policy",
+        "weight_format")]
 
 
 class moe_stats(ctypes.Structure):
@@ -126,6 +127,8 @@ def moe_expert_bytes(hidden: int, inter: int) -> int:
 
 # moe_config.cache_policy values, in enum order (MOE_CACHE_GLOBAL, ...)
 CACHE_POLICIES = ("global", "per_layer", "static")
+# moe_config.weight_format values, in enum order (MOE_WEIGHTS_MXFP4, ...)
+WEIGHT_FORMATS = ("mxfp4", "bf16")
 
 
 def moe_create(**fields) -> int:

@@ -171,6 +171,46 @@ void repack_down(const uint8_t* qd, const uint8_t* sd, int H, int I, uint8_t* ou
   });
 }
 
+// bf16 [N][K] matrix: lane l of the atom takes row row0 + l % 16, values
+// K = 32 (4 c + l / 16) .. +31, as 4 pieces of 8 at 1024 p + 16 l (piece p is
+// what the lane feeds the MFMA at K step p).
+static void write_atom_bf16(const uint16_t* w, int K, int row0, int c, uint8_t* atom) {
+  for (int l = 0; l < 64; l++) {
+    const uint16_t* src = w + (size_t)(row0 + l % 16) * K + (size_t)(c * 4 + l / 16) * 32;
+    for (int p = 0; p < 4; p++) std::memcpy(atom + 1024 * p + 16 * l, src + 8 * p, 16);
+  }
+}
+
+void repack_gateup_bf16(const uint16_t* wg, const uint16_t* wu, int I, int H, uint8_t* out) {
+  const int KC = H / kAtomK, groups = 2 * I / kAtomRows;
+  parallel_for(groups, (size_t)I * H > (1 << 22) ? host_threads() : 1, [&](int rg) {
+    for (int c = 0; c < KC; c++)
+      write_atom_bf16((rg & 1) ? wu : wg, H, (rg / 2) * kAtomRows, c,
+                      out + ((size_t)rg * KC + c) * kAtomBytesBF16);
+  });
+}
+
+void repack_down_bf16(const uint16_t* wd, int H, int I, uint8_t* out) {
+  const int KC = I / kAtomK, groups = H / kAtomRows;
+  parallel_for(groups, (size_t)I * H > (1 << 22) ? host_threads() : 1, [&](int rg) {
+    for (int c = 0; c < KC; c++)
+      write_atom_bf16(wd, I, rg * kAtomRows, c, out + ((size_t)rg * KC + c) * kAtomBytesBF16);
+  });
+}
+
+// Repack one expert into `rec` in the context's format.
+static void repack_expert(const Ctx* c, const uint8_t* qg, const uint8_t* qu, const uint8_t* qd,
+                          const uint8_t* sg, const uint8_t* su, const uint8_t* sd, uint8_t* rec) {
+  const int H = c->cfg.hidden, I = c->cfg.inter, fmt = c->cfg.weight_format;
+  if (fmt == MOE_WEIGHTS_BF16) {
+    repack_gateup_bf16((const uint16_t*)qg, (const uint16_t*)qu, I, H, rec);
+    repack_down_bf16((const uint16_t*)qd, H, I, rec + gateup_section_bytes(H, I, fmt));
+  } else {
+    repack_gateup(qg, sg, qu, su, I, H, rec);
+    repack_down(qd, sd, H, I, rec + gateup_section_bytes(H, I, fmt));
+  }
+}
+
 }  // namespace moe
 
 // =========================================================================
@@ -191,6 +231,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       f.max_tokens > 64 || f.cache_slots < 0 || f.staging_slots < 0 ||
       f.max_prefill_tokens < 0 || (f.has_shared != 0 && f.has_shared != 1) ||
       f.cache_policy < MOE_CACHE_GLOBAL || f.cache_policy > MOE_CACHE_STATIC ||
+      f.weight_format < MOE_WEIGHTS_MXFP4 || f.weight_format > MOE_WEIGHTS_BF16 ||
       (f.renormalize != 0 && f.renormalize != 1))
     return fail(MOE_ERR_INVALID_ARG, "moe_config field out of range");
   if ((int64_t)f.cache_slots > (int64_t)f.n_layers * f.n_experts)
@@ -199,6 +240,9 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     return fail(MOE_ERR_UNSUPPORTED, "n_layers*n_experts too large");
   if (f.hidden % 128 || f.inter % 128 || f.hidden > kMaxH || f.inter > kMaxH)
     return fail(MOE_ERR_UNSUPPORTED, "hidden and inter must be multiples of 128, at most 6144");
+  if (f.weight_format == MOE_WEIGHTS_BF16 && (f.max_tokens > 16 || f.max_prefill_tokens > 0))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "bf16 experts run the decode path for at most 16 tokens per call (no prefill)");
   if (f.cache_slots > kMaxCacheSlots)
     return fail(MOE_ERR_UNSUPPORTED, "cache_slots above 4096");
   if (f.max_prefill_tokens > (1 << 20))
@@ -224,7 +268,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   }
   const int H = f.hidden, I = f.inter, E = f.n_experts, k = f.top_k, L = f.n_layers;
   const int Tm = f.max_tokens;
-  c->rec_bytes = expert_record_bytes(H, I);
+  c->rec_bytes = expert_record_bytes(H, I, f.weight_format);
   c->stride = (c->rec_bytes + 255) / 256 * 256;
   c->max_unique = std::min(Tm * k, E);
   c->max_items = c->max_unique + f.has_shared;
@@ -320,22 +364,23 @@ moe_status moe_set_expert(moe_ctx* ctx, int32_t layer, int32_t expert,
   const int H = c->cfg.hidden, I = c->cfg.inter;
   if (layer < 0 || layer >= c->cfg.n_layers || expert < -1 || expert >= c->cfg.n_experts)
     return fail(MOE_ERR_INVALID_ARG, "bad layer or expert index");
-  if (!qg || !qu || !qd || !sg || !su || !sd)
+  const bool bf16 = c->cfg.weight_format == MOE_WEIGHTS_BF16;
+  if (!qg || !qu || !qd || (!bf16 && (!sg || !su || !sd)))
     return fail(MOE_ERR_INVALID_ARG, "NULL weight pointer");
+  if (bf16 && (sg || su || sd))
+    return fail(MOE_ERR_INVALID_ARG, "bf16 experts take no scale arrays");
   if (expert == -1 && !c->cfg.has_shared)
     return fail(MOE_ERR_STATE, "context has no shared expert");
   const size_t ns = (size_t)H * I / 32;
-  if (!scales_valid(sg, ns) || !scales_valid(su, ns) || !scales_valid(sd, ns))
+  if (!bf16 && (!scales_valid(sg, ns) || !scales_valid(su, ns) || !scales_valid(sd, ns)))
     return fail(MOE_ERR_INVALID_ARG, "E8M0 scale byte 255 (NaN)");
   if (expert >= 0) {
     uint8_t* rec = c->pool + ((size_t)layer * c->cfg.n_experts + expert) * c->stride;
-    repack_gateup(qg, sg, qu, su, I, H, rec);
-    repack_down(qd, sd, H, I, rec + gateup_section_bytes(H, I));
+    repack_expert(c, qg, qu, qd, sg, su, sd, rec);
     return MOE_OK;
   }
   std::vector<uint8_t> rec(c->stride, 0);
-  repack_gateup(qg, sg, qu, su, I, H, rec.data());
-  repack_down(qd, sd, H, I, rec.data() + gateup_section_bytes(H, I));
+  repack_expert(c, qg, qu, qd, sg, su, sd, rec.data());
   HIPCHK(hipMemcpy(c->d_shared + (size_t)layer * c->stride, rec.data(), c->stride,
                    hipMemcpyHostToDevice));
   c->shared_set[layer] = 1;
@@ -347,22 +392,26 @@ moe_status moe_set_layer(moe_ctx* ctx, int32_t layer, const float* h_router,
                          const uint8_t* h_shared_q, const uint8_t* h_shared_s) {
   if (moe_status s = check_ctx(ctx)) return s;
   Ctx* c = C_(ctx);
-  if (layer < 0 || layer >= c->cfg.n_layers || !h_router || !h_q || !h_s)
+  const bool bf16 = c->cfg.weight_format == MOE_WEIGHTS_BF16;
+  if (layer < 0 || layer >= c->cfg.n_layers || !h_router || !h_q || (!bf16 && !h_s))
     return fail(MOE_ERR_INVALID_ARG, "bad layer or NULL pointer");
-  if (c->cfg.has_shared && (!h_shared_q || !h_shared_s))
+  if (bf16 && (h_s || h_shared_s)) return fail(MOE_ERR_INVALID_ARG, "bf16 experts take no scales");
+  if (c->cfg.has_shared && (!h_shared_q || (!bf16 && !h_shared_s)))
     return fail(MOE_ERR_INVALID_ARG, "shared expert weights required");
   const size_t H = c->cfg.hidden, I = c->cfg.inter;
-  const size_t q1 = H * I / 2, s1 = H * I / 32;
+  const size_t q1 = bf16 ? H * I * 2 : H * I / 2, s1 = bf16 ? 0 : H * I / 32;
+  auto sp = [&](const uint8_t* base, size_t off) { return base ? base + off : nullptr; };
   if (moe_status s = moe_set_router(ctx, layer, h_router)) return s;
   for (int e = 0; e < c->cfg.n_experts; e++) {
     const uint8_t* q = h_q + (size_t)e * 3 * q1;
-    const uint8_t* s = h_s + (size_t)e * 3 * s1;
-    if (moe_status st = moe_set_expert(ctx, layer, e, q, q + q1, q + 2 * q1, s, s + s1, s + 2 * s1))
+    const uint8_t* s = sp(h_s, (size_t)e * 3 * s1);
+    if (moe_status st = moe_set_expert(ctx, layer, e, q, q + q1, q + 2 * q1, s, sp(s, s1),
+                                       sp(s, 2 * s1)))
       return st;
   }
   if (c->cfg.has_shared)
     return moe_set_expert(ctx, layer, -1, h_shared_q, h_shared_q + q1, h_shared_q + 2 * q1,
-                          h_shared_s, h_shared_s + s1, h_shared_s + 2 * s1);
+                          h_shared_s, sp(h_shared_s, s1), sp(h_shared_s, 2 * s1));
   return MOE_OK;
 }
 

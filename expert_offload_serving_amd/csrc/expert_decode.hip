@@ -316,6 +316,44 @@ __global__ __launch_bounds__(1024) void down_decode_kernel(
   for (int m0 = 16; m0 < it.cnt; m0 += 16) tile(m0);
 }
 
+// Weight formats of the streaming kernels.  A lane holds its part of an atom
+// (row l % 16, K block l / 16 of a 16-row x 128-K tile) in registers and
+// turns K step j into the MFMA's bf16x8 operand: MXFP4 as one 16-byte load
+// of codes plus the scale byte, dequantised per step; bf16 as four 16-byte
+// pieces used as they are.  kStep: chunks per load step (a bf16 chunk holds
+// four times the bytes); kMaxThreads: workgroup size limit (bf16 keeps 8
+// waves, which leaves its larger operands 256 registers a lane).
+struct WMxfp4 {
+  static constexpr int kAtom = kAtomBytes;
+  static constexpr int kStep = 2;
+  static constexpr int kMaxThreads = 1024;
+  struct Reg {
+    u32x4 q;
+    uint32_t s;
+  };
+  __device__ static void load_data(Reg& r, const uint8_t* atom, int lane) {
+    r.q = load_atom_data(atom, lane);
+  }
+  __device__ static void load_aux(Reg& r, const uint8_t* atom, int lane) {
+    r.s = load_scale(atom, lane);
+  }
+  __device__ static bf16x8 op(const Reg& r, int j) { return dequant8(r.q[j], r.s); }
+};
+struct WBf16 {
+  static constexpr int kAtom = kAtomBytesBF16;
+  static constexpr int kStep = 1;
+  static constexpr int kMaxThreads = 512;
+  struct Reg {
+    u32x4 v[4];
+  };
+  __device__ static void load_data(Reg& r, const uint8_t* atom, int lane) {
+#pragma unroll
+    for (int p = 0; p < 4; p++) r.v[p] = *(gu32x4*)(atom + 1024 * p + lane * 16);
+  }
+  __device__ static void load_aux(Reg&, const uint8_t*, int) {}
+  __device__ static bf16x8 op(const Reg& r, int j) { return __builtin_bit_cast(bf16x8, r.v[j]); }
+};
+
 // Streaming variants for calls of at most 16 tokens (one M tile).  A wave
 // covers CPW consecutive K chunks in steps of two chunks with two steps of
 // weight loads in flight (double-buffered registers), so a wave can cover
@@ -324,12 +362,12 @@ __global__ __launch_bounds__(1024) void down_decode_kernel(
 // resident at once: a second round of workgroups would wait out the memory
 // latency a second time.  Same data layout, reduction order and epilogues
 // as above.
-template <int CPW>
-__global__ __launch_bounds__(1024) void gateup_stream_kernel(
+template <int CPW, class W>
+__global__ __launch_bounds__(W::kMaxThreads) void gateup_stream_kernel(
     const WorkItem* __restrict__ items, const DevMeta* __restrict__ meta,
     const int32_t* __restrict__ tok, const uint16_t* __restrict__ x, uint32_t x_bytes, int H,
     int I, uint16_t* __restrict__ h, size_t lo_plane) {
-  constexpr int S = CPW < 2 ? CPW : 2;  // chunks per step
+  constexpr int S = CPW < W::kStep ? CPW : W::kStep;  // chunks per step
   constexpr int NS = CPW / S;           // steps
   const int item = blockIdx.y;
   // Both loads at once (the grid covers the largest possible item count and
@@ -344,8 +382,8 @@ __global__ __launch_bounds__(1024) void gateup_stream_kernel(
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int KC = H / kAtomK;
   const int c0 = w * CPW;
-  const uint8_t* gbase = it.w + (size_t)(2 * p) * KC * kAtomBytes;
-  const uint8_t* ubase = gbase + (size_t)KC * kAtomBytes;
+  const uint8_t* gbase = it.w + (size_t)(2 * p) * KC * W::kAtom;
+  const uint8_t* ubase = gbase + (size_t)KC * W::kAtom;
   extern __shared__ f32x4 red[];  // [waves][2][64], sized by the launch
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, x_bytes);
 
@@ -358,17 +396,16 @@ __global__ __launch_bounds__(1024) void gateup_stream_kernel(
 
   // Weight loads of step st into buffer b; a chunk past K reads chunk 0
   // (finite values that meet zero activations), as in the kernels above.
-  u32x4 wg[2][S], wu[2][S];
-  uint32_t sg[2][S], su[2][S];
+  typename W::Reg wg[2][S], wu[2][S];
   auto load_step = [&](int st, int b) {
 #pragma unroll
     for (int cc = 0; cc < S; cc++) {
       const int c = c0 + st * S + cc;
-      const size_t o = (size_t)(c < KC ? c : 0) * kAtomBytes;
-      wg[b][cc] = load_atom_data(gbase + o, lane);
-      wu[b][cc] = load_atom_data(ubase + o, lane);
-      sg[b][cc] = load_scale(gbase + o, lane);
-      su[b][cc] = load_scale(ubase + o, lane);
+      const size_t o = (size_t)(c < KC ? c : 0) * W::kAtom;
+      W::load_data(wg[b][cc], gbase + o, lane);
+      W::load_data(wu[b][cc], ubase + o, lane);
+      W::load_aux(wg[b][cc], gbase + o, lane);
+      W::load_aux(wu[b][cc], ubase + o, lane);
     }
   };
   load_step(0, 0);
@@ -396,8 +433,8 @@ __global__ __launch_bounds__(1024) void gateup_stream_kernel(
       }
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[q & 1][j], dequant8(wg[b][cc][j], sg[b][cc]), ag, 0, 0, 0);
-        au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[q & 1][j], dequant8(wu[b][cc][j], su[b][cc]), au, 0, 0, 0);
+        ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[q & 1][j], W::op(wg[b][cc], j), ag, 0, 0, 0);
+        au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[q & 1][j], W::op(wu[b][cc], j), au, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -410,12 +447,12 @@ __global__ __launch_bounds__(1024) void gateup_stream_kernel(
   gateup_epilogue(red, nw, it, 0, p, I, h, lo_plane);
 }
 
-template <int CPW>
-__global__ __launch_bounds__(1024) void down_stream_kernel(
+template <int CPW, class W>
+__global__ __launch_bounds__(W::kMaxThreads) void down_stream_kernel(
     const WorkItem* __restrict__ items, const DevMeta* __restrict__ meta,
     const uint16_t* __restrict__ h, size_t lo_plane, int H, int I, size_t gateup_bytes,
     float* __restrict__ yperm) {
-  constexpr int S = CPW < 2 ? CPW : 2;
+  constexpr int S = CPW < W::kStep ? CPW : W::kStep;
   constexpr int NS = CPW / S;
   const int item = blockIdx.y;
   // Both loads at once (the grid covers the largest possible item count and
@@ -430,23 +467,22 @@ __global__ __launch_bounds__(1024) void down_stream_kernel(
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int KC = I / kAtomK;
   const int c0 = w * CPW;
-  const uint8_t* abase = it.w + gateup_bytes + (size_t)(2 * q) * KC * kAtomBytes;
-  const uint8_t* bbase = abase + (size_t)KC * kAtomBytes;
+  const uint8_t* abase = it.w + gateup_bytes + (size_t)(2 * q) * KC * W::kAtom;
+  const uint8_t* bbase = abase + (size_t)KC * W::kAtom;
   extern __shared__ f32x4 red[];  // [waves][2][64], sized by the launch
   const uint32_t lo_bytes = (uint32_t)(lo_plane * 2);
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(h, 2 * lo_bytes);
 
-  u32x4 wa[2][S], wb[2][S];
-  uint32_t sa[2][S], sb[2][S];
+  typename W::Reg wa[2][S], wb[2][S];
   auto load_step = [&](int st, int b) {
 #pragma unroll
     for (int cc = 0; cc < S; cc++) {
       const int c = c0 + st * S + cc;
-      const size_t o = (size_t)(c < KC ? c : 0) * kAtomBytes;
-      wa[b][cc] = load_atom_data(abase + o, lane);
-      wb[b][cc] = load_atom_data(bbase + o, lane);
-      sa[b][cc] = load_scale(abase + o, lane);
-      sb[b][cc] = load_scale(bbase + o, lane);
+      const size_t o = (size_t)(c < KC ? c : 0) * W::kAtom;
+      W::load_data(wa[b][cc], abase + o, lane);
+      W::load_data(wb[b][cc], bbase + o, lane);
+      W::load_aux(wa[b][cc], abase + o, lane);
+      W::load_aux(wb[b][cc], bbase + o, lane);
     }
   };
   load_step(0, 0);
@@ -482,10 +518,10 @@ __global__ __launch_bounds__(1024) void down_stream_kernel(
       }
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        const bf16x8 b0 = dequant8(wa[b][cc][j], sa[b][cc]);
+        const bf16x8 b0 = W::op(wa[b][cc], j);
         acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[k & 1][j], b0, acc0, 0, 0, 0);
         acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[k & 1][j], b0, acc0, 0, 0, 0);
-        const bf16x8 b1 = dequant8(wb[b][cc][j], sb[b][cc]);
+        const bf16x8 b1 = W::op(wb[b][cc], j);
         acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[k & 1][j], b1, acc1, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[k & 1][j], b1, acc1, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
@@ -562,6 +598,13 @@ int gateup_stream_cpw(int KC) {
   if (KC <= 1) return 1;
   return stream_waves(KC, 2) <= kMaxWaves ? 2 : 16;
 }
+// bf16 streaming launches: the MXFP4 choice `cpw`, with fewer, longer waves
+// where it would need more than the 8 a bf16 workgroup may have.  Where the
+// two formats launch alike, their partial sums meet in the same order.
+int bf16_stream_cpw(int KC, int cpw) {
+  while (cpw < 16 && stream_waves(KC, cpw) > 8) cpw *= 2;
+  return cpw;
+}
 int down_stream_cpw(int KC) {
   int cpw = 1;
   while (cpw < 16 && (cpw < KC ? stream_waves(KC, cpw) : 1) > 8) cpw *= 2;
@@ -579,22 +622,28 @@ hipError_t launch_expert_gateup(const Ctx* c, const uint16_t* x, int T, hipStrea
   dim3 grid(c->cfg.inter / kAtomRows, items_for(c, T));
   const size_t lo = (size_t)c->rows_max * c->cfg.inter;
   const int KC = c->cfg.hidden / kAtomK;
+  const bool bf16 = c->cfg.weight_format == MOE_WEIGHTS_BF16;
   if (T <= kMaxStreamTokens) {
-    const int cpw = gateup_stream_cpw(KC), waves = stream_waves(KC, cpw);
-#define GATEUP_S(N)                                                                       \
-  MOE_LAUNCH(gateup_stream_kernel<N>, grid, waves * 64, waves * 2 * 64 * 16, st, ev0, ev1, \
-             c->d_items, c->d_meta, c->d_tok, x, (uint32_t)T * c->cfg.hidden * 2,          \
+    const int cpw = bf16 ? bf16_stream_cpw(KC, gateup_stream_cpw(KC)) : gateup_stream_cpw(KC);
+    const int waves = stream_waves(KC, cpw);
+#define GATEUP_S(N, F)                                                                     \
+  MOE_LAUNCH((gateup_stream_kernel<N, F>), grid, waves * 64, waves * 2 * 64 * 16, st, ev0, \
+             ev1, c->d_items, c->d_meta, c->d_tok, x, (uint32_t)T * c->cfg.hidden * 2,      \
              c->cfg.hidden, c->cfg.inter, c->d_h, lo)
+#define GATEUP_F(N) \
+  if (bf16) GATEUP_S(N, WBf16); else GATEUP_S(N, WMxfp4);
     switch (cpw) {
-      case 1: GATEUP_S(1); break;
-      case 2: GATEUP_S(2); break;
-      case 4: GATEUP_S(4); break;
-      case 8: GATEUP_S(8); break;
-      default: GATEUP_S(16); break;
+      case 1: GATEUP_F(1); break;
+      case 2: GATEUP_F(2); break;
+      case 4: GATEUP_F(4); break;
+      case 8: GATEUP_F(8); break;
+      default: GATEUP_F(16); break;
     }
+#undef GATEUP_F
 #undef GATEUP_S
     return hipGetLastError();
   }
+  if (bf16) return hipErrorNotSupported;  // bf16 contexts have max_tokens <= 16
   const Split s = split_k(KC, grid.x * grid.y, 4);
 #define GATEUP(N)                                                                           \
   MOE_LAUNCH(gateup_decode_kernel<N>, grid, s.waves * 64, s.waves * 2 * 64 * 16, st, ev0, ev1, \
@@ -614,23 +663,29 @@ hipError_t launch_expert_down(const Ctx* c, int T, hipStream_t st, hipEvent_t ev
                               hipEvent_t ev1) {
   dim3 grid(c->cfg.hidden / (2 * kAtomRows), items_for(c, T));
   const size_t lo = (size_t)c->rows_max * c->cfg.inter;
-  const size_t gub = gateup_section_bytes(c->cfg.hidden, c->cfg.inter);
+  const bool bf16 = c->cfg.weight_format == MOE_WEIGHTS_BF16;
+  const size_t gub = gateup_section_bytes(c->cfg.hidden, c->cfg.inter, c->cfg.weight_format);
   const int KC = c->cfg.inter / kAtomK;
   if (T <= kMaxStreamTokens) {
-    const int cpw = down_stream_cpw(KC), waves = stream_waves(KC, cpw);
-#define DOWN_S(N)                                                                       \
-  MOE_LAUNCH(down_stream_kernel<N>, grid, waves * 64, waves * 2 * 64 * 16, st, ev0, ev1, \
+    const int cpw = bf16 ? bf16_stream_cpw(KC, down_stream_cpw(KC)) : down_stream_cpw(KC);
+    const int waves = stream_waves(KC, cpw);
+#define DOWN_S(N, F)                                                                         \
+  MOE_LAUNCH((down_stream_kernel<N, F>), grid, waves * 64, waves * 2 * 64 * 16, st, ev0, ev1, \
              c->d_items, c->d_meta, c->d_h, lo, c->cfg.hidden, c->cfg.inter, gub, c->d_yperm)
+#define DOWN_F(N) \
+  if (bf16) DOWN_S(N, WBf16); else DOWN_S(N, WMxfp4);
     switch (cpw) {
-      case 1: DOWN_S(1); break;
-      case 2: DOWN_S(2); break;
-      case 4: DOWN_S(4); break;
-      case 8: DOWN_S(8); break;
-      default: DOWN_S(16); break;
+      case 1: DOWN_F(1); break;
+      case 2: DOWN_F(2); break;
+      case 4: DOWN_F(4); break;
+      case 8: DOWN_F(8); break;
+      default: DOWN_F(16); break;
     }
+#undef DOWN_F
 #undef DOWN_S
     return hipGetLastError();
   }
+  if (bf16) return hipErrorNotSupported;  // bf16 contexts have max_tokens <= 16
   const Split s = split_k(KC, grid.x * grid.y, 4);
 #define DOWN(N)                                                                           \
   MOE_LAUNCH(down_decode_kernel<N>, grid, s.waves * 64, s.waves * 2 * 64 * 16, st, ev0, ev1, \

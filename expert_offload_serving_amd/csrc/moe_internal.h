@@ -39,8 +39,15 @@ constexpr int kAtomK = 128;
 constexpr int kAtomData = 1024;
 constexpr int kAtomBytes = 1088;
 
-inline size_t expert_record_bytes(int H, int I) { return (size_t)3 * H * I * 17 / 32; }
-inline size_t gateup_section_bytes(int H, int I) { return (size_t)2 * I * H * 17 / 32; }
+// bf16 atom: the same 16 rows x 128 K tile as an MXFP4 atom, lane l's 32
+// values (row l % 16, K block l / 16) as 4 pieces of 8 at 1024 p + 16 l.
+constexpr int kAtomBytesBF16 = 4096;
+inline size_t expert_record_bytes(int H, int I, int fmt = MOE_WEIGHTS_MXFP4) {
+  return fmt == MOE_WEIGHTS_BF16 ? (size_t)3 * H * I * 2 : (size_t)3 * H * I * 17 / 32;
+}
+inline size_t gateup_section_bytes(int H, int I, int fmt = MOE_WEIGHTS_MXFP4) {
+  return fmt == MOE_WEIGHTS_BF16 ? (size_t)2 * I * H * 2 : (size_t)2 * I * H * 17 / 32;
+}
 
 // Host-side repack of one canonical MXFP4 matrix [N][K] into atoms.
 // fuse_pair: the matrix is gate (even groups) / up (odd groups) pair; pass

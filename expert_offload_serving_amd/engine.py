@@ -14,25 +14,32 @@ class MoEEngine:
     def __init__(self, H: int, I: int, E: int, k: int, n_layers: int = 1,
                  has_shared: bool = False, renormalize: bool = True, max_tokens: int = 16,
                  cache_slots: int = 0, staging_slots: int = 0, max_prefill_tokens: int = 0,
-                 cache_policy: str = "global"):
+                 cache_policy: str = "global", weight_format: str = "mxfp4"):
         self.H, self.I, self.E, self.k, self.L = H, I, E, k, n_layers
         self.has_shared = bool(has_shared)
         self.max_tokens = max_tokens
         self.max_prefill_tokens = max_prefill_tokens
         self.cache_policy = cache_policy
+        self.weight_format = weight_format
         self.ctx = b.moe_create(hidden=H, inter=I, n_experts=E, top_k=k, n_layers=n_layers,
                                 has_shared=int(has_shared), renormalize=int(renormalize),
                                 max_tokens=max_tokens, cache_slots=cache_slots,
                                 staging_slots=staging_slots,
                                 max_prefill_tokens=max_prefill_tokens,
-                                cache_policy=b.CACHE_POLICIES.index(cache_policy))
+                                cache_policy=b.CACHE_POLICIES.index(cache_policy),
+                                weight_format=b.WEIGHT_FORMATS.index(weight_format))
 
     # ---------------------------------------------------------------- weights
     def set_router(self, layer: int, w_router: np.ndarray):
         b.moe_set_router(self.ctx, layer, np.ascontiguousarray(w_router, dtype=np.float32))
 
     def set_expert(self, layer: int, expert: int, w):
-        """w has canonical MXFP4 arrays qg, qu, qd, sg, su, sd (uint8)."""
+        """w has canonical MXFP4 arrays qg, qu, qd, sg, su, sd (uint8), or
+        bf16 matrices wg, wu, wd (uint16 bit patterns) for a bf16 context."""
+        if self.weight_format == "bf16":
+            arrs = [np.ascontiguousarray(getattr(w, n), dtype=np.uint16) for n in ("wg", "wu", "wd")]
+            b.moe_set_expert(self.ctx, layer, expert, *arrs, None, None, None)
+            return
         arrs = [np.ascontiguousarray(getattr(w, n), dtype=np.uint8)
                 for n in ("qg", "qu", "qd", "sg", "su", "sd")]
         b.moe_set_expert(self.ctx, layer, expert, *arrs)

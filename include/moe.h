@@ -84,6 +84,20 @@ enum {
   MOE_CACHE_STATIC = 2
 };
 
+/*
+ * Expert weight format (moe_config.weight_format).  MXFP4: E2M1 codes with
+ * one E8M0 scale per 32 along K, DeepSeek-V4-Flash's format on the pages.
+ * BF16: plain bf16 matrices, the format the pages run their 35B-A3B model
+ * in (jansverre.net FreeToken article, section "Hvor raskt kjører
+ * modellene?").  BF16 experts run the decode path for up to 16 tokens per
+ * call: moe_create requires max_tokens <= 16 and max_prefill_tokens = 0
+ * with them (else UNSUPPORTED).
+ */
+enum {
+  MOE_WEIGHTS_MXFP4 = 0,
+  MOE_WEIGHTS_BF16 = 1
+};
+
 /* Layer-stack shape and capacities, fixed at moe_create. */
 typedef struct moe_config {
   int32_t hidden;          /* H: multiple of 128, 128..6144                  */
@@ -103,6 +117,7 @@ typedef struct moe_config {
                               the prefill h records) below 2 GiB (else
                               UNSUPPORTED)                                  */
   int32_t cache_policy;    /* MOE_CACHE_GLOBAL (0), _PER_LAYER or _STATIC  */
+  int32_t weight_format;   /* MOE_WEIGHTS_MXFP4 (0) or MOE_WEIGHTS_BF16     */
 } moe_config;
 
 /* Counters since creation or the last moe_reset_stats. */
@@ -155,8 +170,11 @@ moe_status moe_set_router(moe_ctx* ctx, int32_t layer, const float* h_router);
  * record into the pinned host pool (an existing cached copy is NOT
  * refreshed: set weights before the first forward); expert = -1 sets the
  * layer's shared expert, held in HBM.  The library repacks into its own
- * MFMA-tiled layout.  Errors: INVALID_ARG (NULL, bad index, scale byte 255
- * which is NaN), STATE (expert = -1 without has_shared), HIP.
+ * MFMA-tiled layout.  With weight_format = MOE_WEIGHTS_BF16 the three
+ * matrices are bf16 instead: h_qg and h_qu [I][H], h_qd [H][I] (2 bytes per
+ * element, same row order), and h_sg, h_su, h_sd must be NULL.  Errors:
+ * INVALID_ARG (NULL, bad index, scale byte 255 which is NaN, scale pointers
+ * given with bf16 weights), STATE (expert = -1 without has_shared), HIP.
  */
 moe_status moe_set_expert(moe_ctx* ctx, int32_t layer, int32_t expert,
                           const uint8_t* h_qg, const uint8_t* h_qu,
@@ -168,7 +186,9 @@ moe_status moe_set_expert(moe_ctx* ctx, int32_t layer, int32_t expert,
  * expert.  h_q holds E consecutive records of [qg | qu | qd] (3*H*I/2
  * bytes each) and h_s E consecutive records of [sg | su | sd] (3*H*I/32
  * bytes each), each part laid out as in moe_set_expert; h_shared_q /
- * h_shared_s hold one such record, or are NULL when has_shared is 0.
+ * h_shared_s hold one such record, or are NULL when has_shared is 0.  With
+ * bf16 weights a record of h_q is [wg | wu | wd] (3*H*I*2 bytes) and h_s
+ * and h_shared_s are NULL.
  */
 moe_status moe_set_layer(moe_ctx* ctx, int32_t layer, const float* h_router,
                          const uint8_t* h_q, const uint8_t* h_s,

@@ -87,7 +87,7 @@ def make_engine(shape: gen.Shape, max_tokens: int, cache_slots: int, staging_slo
                      has_shared=shape.shared, renormalize=shape.renormalize,
                      max_tokens=max_tokens, cache_slots=cache_slots,
                      staging_slots=staging_slots, max_prefill_tokens=max_prefill_tokens,
-                     cache_policy=cache_policy)
+                     cache_policy=cache_policy, weight_format=shape.weights)
 
 
 def check_rounding(y_bf16, y32, what=""):

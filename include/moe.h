@@ -21,8 +21,9 @@
  *    the host-resident pool (aipolix.com article, sixth paragraph).
  * The pages give no formulas; the readings used (softmax router, top-k by
  * logit then lower id, renormalised gates, SwiGLU experts, MXFP4 weights
- * with E2M1 elements and one E8M0 scale per 32 along K) are stated at each
- * call.
+ * with E2M1 elements and one E8M0 scale per 32 along K, or bf16 weights) are
+ * stated at each call.  Two other cache placements (per-layer shares, a
+ * static set) exist for comparing the global LRU with them.
  *
  * Conventions
  *  - Every call returns a moe_status (int32_t); MOE_OK is 0, errors are

@@ -65,11 +65,6 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t q, uint32_t sbyte) {
   r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 3));
   return __builtin_bit_cast(bf16x8, r);
 }
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
 // silu(a) = a / (1 + e^-a) on the hardware exp2 and reciprocal (about 1 ulp
 // each; the GEMM epilogue evaluates it for every h element, and the IEEE
 // divide and library exp cost about 30 instructions per value).  Very

@@ -411,19 +411,27 @@ __device__ __forceinline__ void gemm_tile_mf(const GemmTile& gt, __amdgpu_buffer
   auto chunk = [&](int c) { return c + gt.k0 < KC ? c + gt.k0 : c + gt.k0 - KC; };
   // A waves: step s into stage s % 2; in the down GEMM also kilobytes
   // q0 .. q0+n-1 of the step's low-order record (4, 3, 3, 3 of its 13).
+  // Loads that would fetch only rows at or past gt.rows are not issued: the
+  // LDS rows they would fill feed only output rows that are never stored
+  // (an MFMA output row depends on its own A row alone), so stale values
+  // there are harmless.  The same holds for the kilobytes of a low-order
+  // record past the tile's last 16-row fragment.
   auto issue_a = [&](int s) {
     const int st = s % kStagesA;
     uint8_t* buf = lds + st * kLdsA;
     const bool in = s < KC;
     const uint32_t k = (uint32_t)chunk(s) * (kAtomK * 2);
 #pragma unroll
-    for (int i = 0; i < 8; i++) lds_load16(ra, in ? gt.aoff[i] + k : kOOB, buf + (8 * w + i) * 1024);
+    for (int i = 0; i < 8; i++)
+      if (32 * w + 4 * i < gt.rows)
+        lds_load16(ra, in ? gt.aoff[i] + k : kOOB, buf + (8 * w + i) * 1024);
     if constexpr (LO) {
       const int q0 = w == 0 ? 0 : 1 + 3 * w, n = w == 0 ? 4 : 3;
+      const int lo_end = ((gt.rows + 15) >> 4) * kLoFrag;  // bytes of the valid fragments
       const uint32_t lk = gt.lo0 + (uint32_t)chunk(s) * kLoChunk + 16u * (uint32_t)lane;
 #pragma unroll
       for (int t = 0; t < 4; t++)
-        if (t < n)
+        if (t < n && (q0 + t) * 1024 < lo_end)
           lds_load16(rl, in ? lk + (uint32_t)(q0 + t) * 1024u : kOOB,
                      lostages + st * kLoChunk + (q0 + t) * 1024);
     }

@@ -78,3 +78,29 @@ def test_prefill_dsv4_full_size():
     run.run()
     assert torch.equal(first, run.ys[3])
     run.close()
+
+
+def test_prefill_outputs_ignore_earlier_calls():
+    """Row loads past a tile's valid rows are not issued, so those LDS rows
+    hold whatever an earlier workgroup left there.  Valid outputs must not
+    depend on it: after a call whose activations are scaled by 2^124 (gate/up
+    overflows, h becomes inf/NaN in the epilogue's LDS), the original call
+    gives the same bits as before.  Both calls use ragged tiles (T=300,
+    32 experts, top-4)."""
+    import torch
+    sh = H.small_shape(E=32, k=4, shared=True, layers=1)
+    T = 300
+    print("case: prefill after an overflowing call", flush=True)
+    run = H.PrefillRun(sh, T, seed=4)
+    run.run()
+    ref32, refb = run.y32[0].clone(), run.ys[0].clone()
+    big = gen.f32_to_bf16_bits(gen.bf16_bits_to_f32(run.xb[0]) * np.float32(2.0 ** 124))
+    assert np.all(np.isfinite(gen.bf16_bits_to_f32(big)))
+    good = run.xs[0]
+    run.xs = [H.bf16_dev(big)]
+    run.run()
+    assert not torch.isfinite(run.y32[0]).all()  # the poisoning call did overflow
+    run.xs = [good]
+    run.run()
+    assert torch.equal(run.y32[0], ref32) and torch.equal(run.ys[0], refb)
+    run.close()

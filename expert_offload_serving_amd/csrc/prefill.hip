@@ -212,6 +212,7 @@ __global__ __launch_bounds__(1024) void dispatch_place_kernel(
     int32_t* __restrict__ tok, int2* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
   __shared__ uint32_t bits[kChunkTokens][33];
   __shared__ int s_base[1024];
+  __shared__ __attribute__((aligned(16))) int s_rem[1024];
   __shared__ int s_tmp[16];
   const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   chunk_bits(ids, T, k, c, bits);
@@ -236,14 +237,46 @@ __global__ __launch_bounds__(1024) void dispatch_place_kernel(
       counts[E] = has_shared ? T : 0;
       offsets[E] = T * k;
     }
-    // GEMM tiles of kBM rows: routed groups 0..E-1, then the shared group E
-    const int nt = e < E ? (tot + kBM - 1) / kBM : 0;
-    int ntot;
-    const int tfirst = block_excl_scan(nt, s_tmp, &ntot);
-    for (int i = 0; i < nt; i++) tiles[tfirst + i] = int2{e, i * kBM};
-    const int nts = has_shared ? (T + kBM - 1) / kBM : 0;
-    for (int i = tid; i < nts; i += blockDim.x) tiles[ntot + i] = int2{E, i * kBM};
-    if (tid == 0) *n_tiles = ntot + nts;
+    // GEMM tiles of kBM rows.  Every full tile first (routed groups 0..E-1,
+    // then the shared group E), then each group's partial tile by descending
+    // row count (ties: lower group first).  Workgroups start in tile order,
+    // so the last round of the GEMM launches holds the smallest tiles, which
+    // issue the fewest loads and MFMAs, instead of full ones.
+    const int nfull = e < E ? tot / kBM : 0;
+    const int nfs = has_shared ? T / kBM : 0;
+    int nfull_tot;
+    const int ffirst = block_excl_scan(nfull, s_tmp, &nfull_tot);
+    for (int i = 0; i < nfull; i++) tiles[ffirst + i] = int2{e, i * kBM};
+    for (int i = tid; i < nfs; i += blockDim.x) tiles[nfull_tot + i] = int2{E, i * kBM};
+    const int full_end = nfull_tot + nfs;
+    // Partial tiles: group g has s_rem[g] rows left over (0: none; entries
+    // past E stay 0).  One scan counts the routed partial tiles (low 16
+    // bits) and the routed groups that rank before the shared group's
+    // partial tile, s_rem >= rs (high 16 bits).
+    const int rs = has_shared ? T % kBM : 0;
+    const int mine = e < E ? tot % kBM : 0;
+    s_rem[tid] = mine;
+    int counts2;
+    block_excl_scan((mine > 0 ? 1 : 0) | (rs > 0 && mine >= rs ? 1 << 16 : 0), s_tmp,
+                    &counts2);  // its barriers also publish s_rem
+    if (mine > 0) {
+      int rank = rs > mine ? 1 : 0;  // the shared group ranks after equal routed ones
+      const int4* r4 = reinterpret_cast<const int4*>(s_rem);
+      for (int g4 = 0; g4 < (E + 3) / 4; g4++) {
+        const int4 r = r4[g4];
+        const int g = 4 * g4;
+        rank += (r.x > mine) | ((r.x == mine) & (g < e));
+        rank += (r.y > mine) | ((r.y == mine) & (g + 1 < e));
+        rank += (r.z > mine) | ((r.z == mine) & (g + 2 < e));
+        rank += (r.w > mine) | ((r.w == mine) & (g + 3 < e));
+      }
+      tiles[full_end + rank] = int2{e, nfull * kBM};
+    }
+    if (tid == 0) {
+      const int npart = (counts2 & 0xFFFF) + (rs > 0 ? 1 : 0);
+      if (rs > 0) tiles[full_end + (counts2 >> 16)] = int2{E, nfs * kBM};
+      *n_tiles = full_end + npart;
+    }
     if (has_shared)
       for (int t = tid; t < T; t += blockDim.x) tok[T * k + t] = t;
   }

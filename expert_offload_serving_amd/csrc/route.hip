@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(
       if (lane == 0) red[w][t] = s;
     }
     lds_sync();
-    if (threadIdx.x < tn) {
+    if ((int)threadIdx.x < tn) {
       const int t = threadIdx.x;
       double s = 0.0;
 #pragma unroll

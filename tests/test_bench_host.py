@@ -5,6 +5,7 @@ import hashlib
 import os
 import subprocess
 import sys
+
 import pytest
 
 import bench

@@ -16,6 +16,9 @@ itself, so an interval is the kernel's own duration.  The line also carries the 
 H=4096, I=2048, E=256, top-6 + shared): prefill of T=4096 with whole-layer
 uploads from the pinned pool (grouped-GEMM time and MFMA utilisation), and
 T=1 decode through its global LRU.
+With --graph-T, `graph_replay` repeats the decode workload at those T with
+each timed step replayed from its own HIP graph; `value` is always the
+eager, host-submitted rate.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -45,6 +48,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--extra-T", default="1,4", help="also time these T (decode)")
+    ap.add_argument("--graph-T", default="",
+                    help="also time these T with every step replayed from a HIP graph "
+                         "(e.g. 1,4,16; default: none)")
     ap.add_argument("--prefill-steps", type=int, default=3,
                     help="prefill passes of the DeepSeek-V4-Flash-shaped stack (0: skip)")
     ap.add_argument("--dsv4-decode-steps", type=int, default=256,
@@ -156,6 +162,48 @@ def decode_inputs(wl, T, n, seed=0):
         bs.append(torch.from_numpy(np.stack([gen.bias_from_sets(sets[s], sh.E) for s in range(n)])).to(dev)
                   if sets is not None else None)
     return xs, bs
+
+
+def run_decode_graph(wl, T, steps, warmup, seed=0):
+    """Decode throughput with every timed step replayed from its own HIP
+    graph (captured after the eager warm-up; capture runs nothing), so the
+    host's launch work is out of the timed region.  Same inputs, cache and
+    kernels as run_decode; the steps run in the same order."""
+    import torch
+
+    sh = wl.shape
+    assert not wl.resize, "a cache resize cannot be captured"
+    eng = make_engine(sh, T, wl.cache_slots, wl.staging_slots)
+    load_weights(eng, sh, seed)
+    n = min(wl.steps, steps + warmup)
+    xs, bs = decode_inputs(wl, T, n, seed)
+    y = torch.empty((T, sh.H), dtype=torch.int16, device="cuda")
+
+    def do_step(s):
+        for l in range(sh.layers):
+            eng.forward(l, xs[l][s % n], bias=None if bs[l] is None else bs[l][s % n], y=y)
+
+    for s in range(warmup):
+        do_step(s)
+    torch.cuda.synchronize()
+    graphs = []
+    for s in range(warmup, warmup + steps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            do_step(s)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    eng.reset_stats()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st = eng.stats()
+    eng.close()
+    return dict(T=T, steps=steps, tokens_per_s=T * steps / elapsed, ms_per_step=1e3 * elapsed / steps,
+                hit_rate=st["hits"] / max(st["lookups"], 1))
 
 
 def run_decode(wl, T, steps, warmup, seed=0, eng=None):
@@ -422,6 +470,14 @@ def main():
                                "gateup_gbs": r["gateup_gbs"] and round(r["gateup_gbs"], 1),
                                "down_gbs": r["down_gbs"] and round(r["down_gbs"], 1),
                                "h2d_gbs": round(r["h2d_gbs"], 2)}
+    graph = {}
+    if not wl.resize:
+        for t in [int(v) for v in a.graph_T.split(",") if v.strip()]:
+            if t in wl.Ts:
+                r = run_decode_graph(wl, t, a.steps, a.warmup)
+                graph[f"T={t}"] = {"tokens_per_s": round(r["tokens_per_s"], 1),
+                                   "ms_per_step": round(r["ms_per_step"], 4),
+                                   "hit_rate": round(r["hit_rate"], 4)}
     sh = wl.shape
     kgu, kdn = decode_kernels(T)
     roof = roofline_entry(kgu, res["gateup_gbs"], res["gateup_us"], res["gateup_bytes"],
@@ -455,6 +511,8 @@ def main():
         "pcie_h2d_gbs": round(res["h2d_gbs"], 2),
         "other_T": extra,
     }
+    if graph:
+        line["graph_replay"] = graph
     if a.weights == "mxfp4" and (a.prefill_steps > 0 or a.dsv4_decode_steps > 0):
         line.update(run_dsv4(a.prefill_steps, a.dsv4_decode_steps, max(a.dsv4_decode_steps // 4, 1)))
     if a.calibrate_copy_mb > 0:

@@ -163,3 +163,74 @@ def test_resize_to_zero_empties():
     assert c.capacity == 0 and sorted(evicted) == [1, 2, 3] and not moves
     slots, fills, byp = c.lookup(0, [4])
     assert slots == [-1] and not fills
+
+
+def _with_state(C, E, key, stamp, clock):
+    c = SlotCache(C, E)
+    c.key, c.stamp, c.clock = list(key), list(stamp), clock
+    return c
+
+
+def test_resize_hand_computed_slot_numbering():
+    """Six slots holding keys in slots 1, 3, 4, 5 (stamps 4, 2, 9, 7), shrunk
+    to three: the least recent key (13, stamp 2) is evicted, the survivors
+    in slots 4 and 5 move to the free slots 0 and 2 in that order, and slot
+    1 keeps its key.  Worked out by hand from the rule."""
+    c = _with_state(6, 10, [-1, 11, -1, 13, 14, 15], [0, 4, 0, 2, 9, 7], 9)
+    moves, evicted = c.resize(3)
+    assert c.key == [14, 11, 15] and c.stamp == [9, 4, 7] and c.clock == 9
+    assert moves == [(4, 0), (5, 2)] and evicted == [13]
+    # no eviction, survivors fill the holes in ascending order
+    c = _with_state(5, 10, [7, -1, -1, 8, 9], [3, 0, 0, 1, 2], 3)
+    moves, evicted = c.resize(3)
+    assert c.key == [7, 8, 9] and c.stamp == [3, 1, 2] and not evicted
+    assert moves == [(3, 1), (4, 2)]
+    # several evictions, all among the tail; the head is left alone
+    c = _with_state(6, 10, [1, 2, 3, 4, 5, 6], [6, 5, 4, 3, 2, 1], 6)
+    moves, evicted = c.resize(2)
+    assert c.key == [1, 2] and c.stamp == [6, 5] and not moves
+    assert evicted == [6, 5, 4, 3]
+
+
+def _resize_by_ranks(key, stamp, new_C):
+    """A second resize model: rank the occupied slots by recency, keep the
+    new_C most recent, then pair the kept slots at or past new_C (ascending)
+    with the empty slots below new_C (ascending) by position."""
+    occupied = [s for s in range(len(key)) if key[s] >= 0]
+    keep = set(sorted(occupied, key=lambda s: -stamp[s])[:new_C])
+    out_key = [key[s] if s in keep else -1 for s in range(new_C)]
+    out_stamp = [stamp[s] if s in keep else 0 for s in range(new_C)]
+    movers = sorted(s for s in keep if s >= new_C)
+    holes = [d for d in range(new_C) if out_key[d] < 0]
+    for s, d in zip(movers, holes):
+        out_key[d], out_stamp[d] = key[s], stamp[s]
+    return out_key, out_stamp, list(zip(movers, holes))
+
+
+@pytest.mark.parametrize("E,C,calls", [(4, 3, 3), (3, 4, 3), (5, 4, 2)])
+def test_resize_brute_force_against_rank_model(E, C, calls):
+    """Every trace of lookups over all subsets, then every shrink and grow
+    target: the oracle's resize equals the rank model, and later lookups
+    keep agreeing with the recency-list simulator (recency is preserved)."""
+    subsets = [s for r in range(1, E + 1) for s in itertools.combinations(range(E), r)]
+    for trace in itertools.product(subsets, repeat=calls):
+        base = SlotCache(C, E)
+        for U in trace:
+            base.lookup(0, list(U))
+        for new_C in range(0, C + 2):
+            c = _with_state(C, E, base.key, base.stamp, base.clock)
+            want_key, want_stamp, want_moves = _resize_by_ranks(base.key, base.stamp, new_C)
+            moves, evicted = c.resize(new_C)
+            if new_C >= C:
+                want_key = base.key + [-1] * (new_C - C)
+                want_stamp = base.stamp + [0] * (new_C - C)
+                want_moves = []
+            assert c.key == want_key and c.stamp == want_stamp, (trace, new_C)
+            assert moves == want_moves and c.clock == base.clock
+            # a lookup after the resize: the recency-list model rebuilt from
+            # the resized state (empty slots by index, then by stamp) agrees
+            r = RecencyListCache(new_C, E)
+            r.owner = [k if k >= 0 else None for k in c.key]
+            r.order = sorted(range(new_C), key=lambda s: (c.key[s] >= 0, c.stamp[s], s))
+            for U in subsets[:: max(1, len(subsets) // 4)]:
+                assert c.lookup(0, list(U))[0] == r.lookup(0, list(U))

@@ -25,9 +25,12 @@ def _dense_masked_reference(x, gate_matrix, mats, shared=None):
     return Y
 
 
-@pytest.mark.parametrize("seed,shared", [(0, False), (1, False), (2, True), (3, True)])
-def test_tiny_layer_equals_dense_masked_reference(seed, shared):
-    shape = gen.Shape(H=256, I=512, E=8, k=2, shared=shared)
+@pytest.mark.parametrize("seed,shared,I", [(0, False, 512), (1, False, 512), (2, True, 512),
+                                           (3, True, 512), (4, True, 256)])
+def test_tiny_layer_equals_dense_masked_reference(seed, shared, I):
+    """I = H = 256 is the square case, where a transposed operand would not
+    change the shapes."""
+    shape = gen.Shape(H=256, I=I, E=8, k=2, shared=shared)
     x = gen.bf16_bits_to_f32(gen.tokens(shape, 0, 0, 4, seed))
     wr = gen.router_weights(shape, 0, seed)
     _, ids, g = router.route(x, wr, shape.k)

@@ -658,10 +658,16 @@ moe_status moe_inspect_dispatch(moe_ctx* ctx, int32_t* h_T, int32_t* h_counts,
   return MOE_OK;
 }
 
-moe_status moe_inspect_prefill(moe_ctx* ctx, int32_t* h_T, int32_t* h_ids, float* h_gates) {
+moe_status moe_inspect_prefill(moe_ctx* ctx, int32_t layer, int32_t* h_T, int32_t* h_ids,
+                               float* h_gates, int32_t* h_counts, int32_t* h_offsets,
+                               int32_t* h_sorted, int32_t* h_inv) {
   if (moe_status s = check_ctx(ctx)) return s;
   if (!h_T) return fail(MOE_ERR_INVALID_ARG, "h_T is NULL");
-  HIPCHK(prefill_inspect(C_(ctx), h_T, h_ids, h_gates));
+  Ctx* c = C_(ctx);
+  const int run = prefill_layers_run(c);
+  if (run > 0 && (layer < 0 || layer >= run))
+    return fail(MOE_ERR_INVALID_ARG, "layer outside the layers of the last prefill call");
+  HIPCHK(prefill_inspect(c, layer, h_T, h_ids, h_gates, h_counts, h_offsets, h_sorted, h_inv));
   return MOE_OK;
 }
 

@@ -235,7 +235,9 @@ int fillable_slots(const Ctx* c, int layer, bool insert, int* slot0);
 // prefill
 int prefill_max_tiles(int T, int k, int E);
 size_t prefill_lo_bytes(int T, int k, int E, int I);
-hipError_t prefill_inspect(Ctx* c, int32_t* T, int32_t* ids, float* gates);
+int prefill_layers_run(const Ctx* c);
+hipError_t prefill_inspect(Ctx* c, int layer, int32_t* T, int32_t* ids, float* gates,
+                           int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* inv);
 hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* x, int T,
                            const float* const* bias, void* const* y, float* const* y32,
                            hipStream_t st);

@@ -12,19 +12,22 @@
 
 namespace moe {
 
+// Routing arrays are kept per layer ([L][...]) so that every layer of the
+// last call can be inspected; the GEMM scratch is shared by the layers.
 struct Prefill {
   int Tmax = 0;
   int last_T = 0;
+  int last_layers = 0;
   int nchunk_max = 0;
   int max_tiles = 0;
   float* logits = nullptr;     // [Tmax][E]
-  int32_t* ids = nullptr;      // [Tmax*k]
-  float* gates = nullptr;      // [Tmax*k]
+  int32_t* ids = nullptr;      // [L][Tmax*k]
+  float* gates = nullptr;      // [L][Tmax*k]
   int32_t* chunk_cnt = nullptr;  // [nchunk][E]
-  int32_t* counts = nullptr;   // [E+1]: rows per group (group E: shared expert)
-  int32_t* offsets = nullptr;  // [E+1]: first permuted row per group
-  int32_t* sorted = nullptr;   // [Tmax*k]
-  int32_t* inv = nullptr;      // [Tmax*k]
+  int32_t* counts = nullptr;   // [L][E+1]: rows per group (group E: shared expert)
+  int32_t* offsets = nullptr;  // [L][E+1]: first permuted row per group
+  int32_t* sorted = nullptr;   // [L][Tmax*k]
+  int32_t* inv = nullptr;      // [L][Tmax*k]
   int32_t* tok = nullptr;      // [Tmax*k + Tmax]
   int2* tiles = nullptr;       // [max_tiles]: (group, first row)
   int32_t* n_tiles = nullptr;  // [1]
@@ -854,14 +857,15 @@ hipError_t prefill_alloc(Ctx* c) {
   hipError_t e;
 #define PA(ptr, n) \
   if ((e = dalloc(&p->ptr, (n))) != hipSuccess) return e
+  const size_t L = f.n_layers;
   PA(logits, (size_t)T * E);
-  PA(ids, (size_t)T * k);
-  PA(gates, (size_t)T * k);
+  PA(ids, L * T * k);
+  PA(gates, L * T * k);
   PA(chunk_cnt, (size_t)p->nchunk_max * E);
-  PA(counts, (size_t)E + 1);
-  PA(offsets, (size_t)E + 1);
-  PA(sorted, (size_t)T * k);
-  PA(inv, (size_t)T * k);
+  PA(counts, L * (E + 1));
+  PA(offsets, L * (E + 1));
+  PA(sorted, L * T * k);
+  PA(inv, L * T * k);
   PA(tok, rows);
   PA(tiles, (size_t)p->max_tiles);
   PA(n_tiles, 1);
@@ -903,13 +907,26 @@ void prefill_free(Ctx* c) {
   c->copy_stream = nullptr;
 }
 
-hipError_t prefill_inspect(Ctx* c, int32_t* T, int32_t* ids, float* gates) {
+int prefill_layers_run(const Ctx* c) { return c->pf ? c->pf->last_layers : 0; }
+
+hipError_t prefill_inspect(Ctx* c, int layer, int32_t* T, int32_t* ids, float* gates,
+                           int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* inv) {
   *T = c->pf ? c->pf->last_T : 0;
   if (!c->pf || !*T) return hipSuccess;
+  Prefill* p = c->pf;
   hipError_t e = hipDeviceSynchronize();
-  const size_t n = (size_t)*T * c->cfg.top_k;
-  if (e == hipSuccess && ids) e = hipMemcpy(ids, c->pf->ids, n * 4, hipMemcpyDeviceToHost);
-  if (e == hipSuccess && gates) e = hipMemcpy(gates, c->pf->gates, n * 4, hipMemcpyDeviceToHost);
+  const int E = c->cfg.n_experts;
+  const size_t n = (size_t)*T * c->cfg.top_k, per = (size_t)p->Tmax * c->cfg.top_k;
+  const size_t lo = (size_t)layer * per, lg = (size_t)layer * (E + 1);
+  auto get = [&](void* dst, const void* src, size_t bytes) {
+    if (e == hipSuccess && dst && bytes) e = hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost);
+  };
+  get(ids, p->ids + lo, n * 4);
+  get(gates, p->gates + lo, n * 4);
+  get(counts, p->counts + lg, (size_t)E * 4);
+  get(offsets, p->offsets + lg, (size_t)(E + 1) * 4);
+  get(sorted, p->sorted + lo, n * 4);
+  get(inv, p->inv + lo, n * 4);
   return e;
 }
 
@@ -923,6 +940,7 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
   }
   Prefill* p = c->pf;
   p->last_T = T;
+  p->last_layers = n_layers;
   const moe_config& f = c->cfg;
   const int H = f.hidden, I = f.inter, E = f.n_experts, k = f.top_k;
   const size_t layer_bytes = (size_t)E * c->stride;
@@ -954,22 +972,30 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
     const uint16_t* x = (const uint16_t*)xs[l];
     const float* bias = biases ? biases[l] : nullptr;
     const float* wrt = c->d_router + (size_t)l * H * E;
+    // this layer's routing arrays
+    const size_t per = (size_t)p->Tmax * k;
+    int32_t* ids = p->ids + l * per;
+    float* gates = p->gates + l * per;
+    int32_t* sorted = p->sorted + l * per;
+    int32_t* inv = p->inv + l * per;
+    int32_t* counts = p->counts + (size_t)l * (E + 1);
+    int32_t* offsets = p->offsets + (size_t)l * (E + 1);
     router_prefill_kernel<<<dim3((T + 63) / 64, (E + 63) / 64), 256, 0, st>>>(x, T, H, E, wrt,
                                                                               bias, p->logits);
-    const TopkArgs ta{E, k, f.renormalize, p->logits, p->ids, p->gates, nullptr, nullptr};
+    const TopkArgs ta{E, k, f.renormalize, p->logits, ids, gates, nullptr, nullptr};
     const int nk = (E + 63) / 64, tb = (T + 15) / 16;
     if (nk <= 1) topk_prefill_kernel<1><<<tb, 1024, 0, st>>>(ta, T);
     else if (nk <= 2) topk_prefill_kernel<2><<<tb, 1024, 0, st>>>(ta, T);
     else if (nk <= 4) topk_prefill_kernel<4><<<tb, 1024, 0, st>>>(ta, T);
     else if (nk <= 8) topk_prefill_kernel<8><<<tb, 1024, 0, st>>>(ta, T);
     else topk_prefill_kernel<16><<<tb, 1024, 0, st>>>(ta, T);
-    dispatch_count_kernel<<<nchunk, 256, 0, st>>>(p->ids, T, k, E, p->chunk_cnt);
-    dispatch_place_kernel<<<nchunk, 1024, 0, st>>>(p->ids, T, k, E, f.has_shared, nchunk,
-                                                   p->chunk_cnt, p->counts, p->offsets, p->sorted,
-                                                   p->inv, p->tok, p->tiles, p->n_tiles);
+    dispatch_count_kernel<<<nchunk, 256, 0, st>>>(ids, T, k, E, p->chunk_cnt);
+    dispatch_place_kernel<<<nchunk, 1024, 0, st>>>(ids, T, k, E, f.has_shared, nchunk,
+                                                   p->chunk_cnt, counts, offsets, sorted, inv,
+                                                   p->tok, p->tiles, p->n_tiles);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    GroupArgs ga{p->tiles, p->n_tiles, p->counts, p->offsets, p->tok, c->d_layerbuf[b],
+    GroupArgs ga{p->tiles, p->n_tiles, counts, offsets, p->tok, c->d_layerbuf[b],
                  c->stride, f.has_shared ? c->d_shared + (size_t)l * c->stride : nullptr, E};
     Ctx::TimingRec tr{nullptr, nullptr, nullptr, nullptr};
     if (c->timing && c->t_prefill.size() < 65536) {
@@ -985,7 +1011,7 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
                tr.dn1, ga, p->h, (uint32_t)hhi_bytes, p->hlo, (uint32_t)hlo_bytes, H, I,
                nbn_dn, gateup_section_bytes(H, I), p->yperm);
     if (tr.gu0) c->t_prefill.push_back(tr);
-    if ((e = launch_combine_rows(p->yperm, p->inv, p->gates, T, k, H, f.has_shared,
+    if ((e = launch_combine_rows(p->yperm, inv, gates, T, k, H, f.has_shared,
                                  (uint16_t*)ys[l], y32s ? y32s[l] : nullptr, st)) != hipSuccess)
       return e;
     if ((e = hipEventRecord(c->ev_compute[b], st)) != hipSuccess) return e;

@@ -326,16 +326,28 @@ __global__ __launch_bounds__(kFinalizeThreads) void route_finalize_kernel(Finali
   if (tid == 0) a.la.meta->n_items = n_unique + a.has_shared;
 }
 
-// Standalone lookup for expert_cache_lookup / expert_cache_fill.
+// Standalone lookup for expert_cache_lookup / expert_cache_fill.  The list
+// must be ascending and unique: from the first entry that is not above its
+// predecessor on, every entry is passed on as invalid (slot code INT_MIN,
+// no state change), so a duplicate can never claim two slots or two
+// recency positions.
 __global__ __launch_bounds__(kFinalizeThreads) void cache_lookup_kernel(
     LookupArgs la, const int32_t* experts, const int32_t* d_n, int n_max, int32_t* out_slot) {
   __shared__ int s_U[1024];
   __shared__ int s_slot[1024];
+  __shared__ int s_first_bad;
   __shared__ LookupShared ls;
   prefetch_lookup(la, ls);
   int n = *d_n;
   n = n < 0 ? 0 : (n > n_max ? n_max : n);
+  if (threadIdx.x == 0) s_first_bad = n;
   for (int u = threadIdx.x; u < n; u += blockDim.x) s_U[u] = experts[u];
+  lds_sync();
+  for (int u = threadIdx.x; u < n; u += blockDim.x)
+    if (u > 0 && s_U[u] <= s_U[u - 1]) atomicMin(&s_first_bad, u);
+  lds_sync();
+  for (int u = threadIdx.x; u < n; u += blockDim.x)
+    if (u >= s_first_bad) s_U[u] = -1;
   lds_sync();
   block_lookup(la, ls, s_U, n, s_slot);
   for (int u = threadIdx.x; u < n; u += blockDim.x) out_slot[u] = s_slot[u];

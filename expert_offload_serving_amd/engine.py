@@ -1,4 +1,12 @@
-"""A Python handle on one libmoe context (argument marshalling only)."""
+"""A Python handle on one libmoe context (argument marshalling only).
+
+The library takes raw device addresses, so a wrong tensor (host memory, a
+transposed view, the wrong element size, too few rows) would reach the GPU
+unchecked.  Every tensor and array is therefore checked here first and
+rejected with ValueError: device tensors must be CUDA, contiguous, of the
+element type and shape the call documents; host weight arrays must have the
+canonical shapes.
+"""
 from __future__ import annotations
 
 from typing import Optional, Sequence
@@ -6,6 +14,78 @@ from typing import Optional, Sequence
 import numpy as np
 
 from . import binding as b
+
+_BF16_TYPES = ("bfloat16", "int16", "uint16", "float16")
+
+
+def check_device(name: str, t, dtypes: Sequence[str], shape: tuple, device=None):
+    """t must be a contiguous CUDA tensor of one of `dtypes` (torch dtype
+    names) with exactly `shape`, on `device` when given."""
+    if t is None or not hasattr(t, "data_ptr") or not hasattr(t, "is_cuda"):
+        raise ValueError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a CUDA tensor (got device {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, the other tensors are on {device}")
+    dt = str(t.dtype).replace("torch.", "")
+    if dt not in dtypes:
+        raise ValueError(f"{name}: dtype {dt}, expected one of {tuple(dtypes)}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def check_host(name: str, a, shape: tuple):
+    """a must be a host array with exactly `shape` (it is converted to the
+    element type the library reads)."""
+    if hasattr(a, "is_cuda") and a.is_cuda:
+        raise ValueError(f"{name}: expected a host array, got a CUDA tensor")
+    if tuple(np.shape(a)) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(np.shape(a))}, expected {tuple(shape)}")
+
+
+def check_forward(H: int, E: int, k: int, max_tokens: int, x, bias, y, ids, gates, y32):
+    """Arguments of one decode forward (moe_layer_forward)."""
+    check_device("x", x, _BF16_TYPES, (x.shape[0] if hasattr(x, "shape") and len(x.shape) else -1, H))
+    T = int(x.shape[0])
+    if not 0 <= T <= max_tokens:
+        raise ValueError(f"x: {T} tokens, the context takes at most {max_tokens}")
+    dev = x.device
+    check_device("y", y, _BF16_TYPES, (T, H), dev)
+    if bias is not None:
+        check_device("bias", bias, ("float32",), (T, E), dev)
+    if ids is not None:
+        check_device("ids", ids, ("int32",), (T, k), dev)
+    if gates is not None:
+        check_device("gates", gates, ("float32",), (T, k), dev)
+    if y32 is not None:
+        check_device("y32", y32, ("float32",), (T, H), dev)
+    return T
+
+
+def check_prefill(H: int, E: int, n_layers: int, max_prefill_tokens: int, xs, ys, biases, y32s):
+    """Arguments of one prefill call (moe_prefill_forward)."""
+    L = len(xs)
+    if not 1 <= L <= n_layers:
+        raise ValueError(f"{L} layers given, the context has {n_layers}")
+    check_device("xs[0]", xs[0], _BF16_TYPES,
+                 (xs[0].shape[0] if hasattr(xs[0], "shape") and len(xs[0].shape) else -1, H))
+    T = int(xs[0].shape[0])
+    if not 1 <= T <= max_prefill_tokens:
+        raise ValueError(f"prefill of {T} tokens, the context takes 1..{max_prefill_tokens}")
+    dev = xs[0].device
+    for name, seq, dts, cols in (("xs", xs, _BF16_TYPES, H), ("ys", ys, _BF16_TYPES, H),
+                                 ("biases", biases, ("float32",), E),
+                                 ("y32s", y32s, ("float32",), H)):
+        if seq is None:
+            continue
+        if len(seq) != L:
+            raise ValueError(f"{name}: {len(seq)} entries for {L} layers")
+        for l, t in enumerate(seq):
+            if t is not None or name in ("xs", "ys"):
+                check_device(f"{name}[{l}]", t, dts, (T, cols), dev)
+    return T
 
 
 class MoEEngine:
@@ -31,32 +111,40 @@ class MoEEngine:
 
     # ---------------------------------------------------------------- weights
     def set_router(self, layer: int, w_router: np.ndarray):
+        check_host("w_router", w_router, (self.H, self.E))
         b.moe_set_router(self.ctx, layer, np.ascontiguousarray(w_router, dtype=np.float32))
 
     def set_expert(self, layer: int, expert: int, w):
         """w has canonical MXFP4 arrays qg, qu, qd, sg, su, sd (uint8), or
         bf16 matrices wg, wu, wd (uint16 bit patterns) for a bf16 context."""
+        H, I = self.H, self.I
         if self.weight_format == "bf16":
-            arrs = [np.ascontiguousarray(getattr(w, n), dtype=np.uint16) for n in ("wg", "wu", "wd")]
+            shapes = {"wg": (I, H), "wu": (I, H), "wd": (H, I)}
+            for n, shp in shapes.items():
+                check_host(n, getattr(w, n), shp)
+            arrs = [np.ascontiguousarray(getattr(w, n), dtype=np.uint16) for n in shapes]
             b.moe_set_expert(self.ctx, layer, expert, *arrs, None, None, None)
             return
-        arrs = [np.ascontiguousarray(getattr(w, n), dtype=np.uint8)
-                for n in ("qg", "qu", "qd", "sg", "su", "sd")]
+        shapes = {"qg": (I, H // 2), "qu": (I, H // 2), "qd": (H, I // 2),
+                  "sg": (I, H // 32), "su": (I, H // 32), "sd": (H, I // 32)}
+        for n, shp in shapes.items():
+            check_host(n, getattr(w, n), shp)
+        arrs = [np.ascontiguousarray(getattr(w, n), dtype=np.uint8) for n in shapes]
         b.moe_set_expert(self.ctx, layer, expert, *arrs)
 
     # ---------------------------------------------------------------- forward
     def forward(self, layer: int, x, bias=None, y=None, ids=None, gates=None, y32=None,
                 stream=None):
         import torch
-        T = int(x.shape[0])
-        if y is None:
-            y = torch.empty((T, self.H), dtype=x.dtype, device=x.device)
+        if y is None and hasattr(x, "shape") and hasattr(x, "is_cuda"):
+            y = torch.empty((int(x.shape[0]), self.H), dtype=x.dtype, device=x.device)
+        T = check_forward(self.H, self.E, self.k, self.max_tokens, x, bias, y, ids, gates, y32)
         b.moe_layer_forward(self.ctx, layer, x, T, bias, y, y32, ids, gates, stream)
         return y
 
     def prefill(self, xs: Sequence, ys: Sequence, biases: Optional[Sequence] = None,
                 y32s: Optional[Sequence] = None, stream=None):
-        T = int(xs[0].shape[0])
+        T = check_prefill(self.H, self.E, self.L, self.max_prefill_tokens, xs, ys, biases, y32s)
         b.moe_prefill_forward(self.ctx, len(xs), xs, T, biases, ys, y32s, stream)
         return ys
 
@@ -76,9 +164,10 @@ class MoEEngine:
     def inspect_dispatch(self):
         return b.moe_inspect_dispatch(self.ctx, self.E, self.k, self.max_tokens)
 
-    def inspect_prefill(self):
-        """(ids, gates) of the last layer of the last prefill call."""
-        return b.moe_inspect_prefill(self.ctx, self.k, self.max_prefill_tokens)
+    def inspect_prefill(self, layer: int):
+        """Routing (ids, gates) and dispatch (counts, offsets, sorted, inv) of
+        one layer of the last prefill call."""
+        return b.moe_inspect_prefill(self.ctx, layer, self.E, self.k, self.max_prefill_tokens)
 
     def stats(self) -> dict:
         return b.moe_get_stats(self.ctx)

@@ -248,12 +248,18 @@ moe_status moe_prefill_forward(moe_ctx* ctx, int32_t n_layers,
 
 /*
  * Look up n unique experts (ascending, in [0, E)) of one layer in the cache
- * with the moe_layer_forward rule and fill the misses.  d_experts: int32
- * [>= *d_n]; d_n: int32 on the device, 0 <= *d_n <= min(E, max_tokens*k)
- * (larger values are clamped); d_slot: int32 [*d_n] receives the slot
- * (>= 0) or -1-b for staging slot b.  Errors: INVALID_ARG, CAPACITY
- * (staging_slots below the worst-case bypass count, as for
- * moe_layer_forward), HIP.
+ * with the moe_layer_forward rule and fill the misses: the cache step of the
+ * decode path on its own, for custom pipelines (one global LRU across
+ * layers, misses fetched from the host pool on demand: jansverre.net
+ * FreeToken article, section "Hvorfor er båndbredden viktigere enn antall
+ * kjerner?").  d_experts: int32 [>= *d_n]; d_n: int32 on the device,
+ * 0 <= *d_n <= min(E, max_tokens*k) (larger values are clamped); d_slot:
+ * int32 [*d_n] receives the slot (>= 0) or -1-b for staging slot b.  The
+ * list is read on the device, so it is checked there: an entry outside
+ * [0, E), and every entry from the first one that is not above its
+ * predecessor on, receives INT_MIN and changes no state.  Errors:
+ * INVALID_ARG, CAPACITY (staging_slots below the worst-case bypass count,
+ * as for moe_layer_forward), HIP.
  */
 moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer,
                                const int32_t* d_experts, const int32_t* d_n,
@@ -304,11 +310,17 @@ moe_status moe_inspect_dispatch(moe_ctx* ctx, int32_t* h_T, int32_t* h_counts,
                                 int32_t* h_n_unique, int32_t* h_slot);
 
 /*
- * (sync) Copy the routing of the last layer run by moe_prefill_forward:
- * h_ids int32 [T][k], h_gates fp32 [T][k] (either may be NULL); *h_T
- * receives that call's T (0 if none ran).
+ * (sync) Copy the routing and dispatch of one layer of the last
+ * moe_prefill_forward call: h_ids int32 [T][k], h_gates fp32 [T][k],
+ * h_counts [E], h_offsets [E+1] (h_offsets[E] = T*k), h_sorted [T*k] (pair
+ * f = t*k+j at each permuted position, stable by f within an expert), h_inv
+ * [T*k].  Any of them may be NULL.  *h_T receives that call's T (0 if none
+ * ran; nothing else is written then).  Errors: INVALID_ARG (NULL h_T, layer
+ * outside [0, n_layers of that call)), HIP.
  */
-moe_status moe_inspect_prefill(moe_ctx* ctx, int32_t* h_T, int32_t* h_ids, float* h_gates);
+moe_status moe_inspect_prefill(moe_ctx* ctx, int32_t layer, int32_t* h_T, int32_t* h_ids,
+                               float* h_gates, int32_t* h_counts, int32_t* h_offsets,
+                               int32_t* h_sorted, int32_t* h_inv);
 
 /* (sync) Read / clear the counters. */
 moe_status moe_get_stats(moe_ctx* ctx, moe_stats* out);

@@ -2,6 +2,7 @@
 seeded synthetic inputs.  Used by the GPU tests, smoke and bench."""
 from __future__ import annotations
 
+import os
 from collections import OrderedDict
 from dataclasses import replace
 from typing import Optional
@@ -27,6 +28,39 @@ RTOL_Y_DECODE = 1e-3
 RTOL_Y_PREFILL = 4e-3
 ATOL_G = 1e-6     # gates
 TOL_SUM = 1e-6    # |sum(g) - 1| with renormalisation
+
+
+def oracle_rows(model: "Model", layer: int, xf: np.ndarray, ids: np.ndarray, g: np.ndarray,
+                tokens, workers: Optional[int] = None) -> np.ndarray:
+    """Oracle outputs of the listed token rows of one layer, through
+    oracle.moe_layer.  Every expert those rows use is dequantised once, and
+    the rows are split over worker threads (numpy releases the GIL in the
+    dequantisation and in the products; each thread's BLAS keeps to one
+    thread), so that a few hundred rows of a 256-expert layer take seconds
+    instead of many minutes.  Returns [len(tokens)][H] in the order given."""
+    import concurrent.futures
+    from threadpoolctl import threadpool_limits
+    tokens = list(tokens)
+    sh = model.shape
+    workers = workers or max(1, min(16, len(os.sched_getaffinity(0))))
+    need = sorted({int(ids[t, j]) for t in tokens for j in range(sh.k)})
+    if sh.shared:
+        need.append(-1)
+    with threadpool_limits(1), concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        mats = dict(zip(need, ex.map(lambda e: oexp.dequant_expert(model.expert(layer, e)),
+                                     need)))
+        shared = mats.pop(-1, None)
+        chunks = [tokens[i::workers] for i in range(workers) if tokens[i::workers]]
+
+        def run(rows):
+            return oracle.moe_layer(xf[rows], ids[rows], g[rows], mats.__getitem__,
+                                    shared=shared)
+        outs = list(ex.map(run, chunks))
+    y = {}
+    for rows, out in zip(chunks, outs):
+        for i, t in enumerate(rows):
+            y[t] = out[i]
+    return np.stack([y[t] for t in tokens])
 
 
 def bf16_dev(bits: np.ndarray, device="cuda"):
@@ -218,21 +252,22 @@ class PrefillRun:
         b = None if self.bias is None else self.bias[layer]
         return xf, self.model.route(layer, xf, b)
 
-    def reference_rows(self, layer, tokens, ids, g):
-        """Oracle outputs of the sampled tokens, evaluated expert by expert
-        (each expert dequantised once) with oracle.expert_ffn."""
-        xf = gen.bf16_bits_to_f32(self.xb[layer])
-        y = {t: np.zeros(self.shape.H) for t in tokens}
-        need = sorted({int(ids[t, j]) for t in tokens for j in range(self.shape.k)})
-        for e in need + ([-1] if self.shape.shared else []):
-            wg, wu, wd = oexp.dequant_expert(self.model.expert(layer, e))
-            for t in tokens:
-                if e < 0:
-                    y[t] += oracle.expert_ffn(xf[t], wg, wu, wd)
-                elif e in ids[t]:
-                    j = list(ids[t]).index(e)
-                    y[t] += float(g[t, j]) * oracle.expert_ffn(xf[t], wg, wu, wd)
-        return np.stack([y[t] for t in tokens])
+    def check_routing(self, layer):
+        """Routing and dispatch of one layer, read back from the library,
+        against oracle.route and oracle.permutation: ids, counts, offsets,
+        sorted and inv bit for bit, gates within ATOL_G.  Returns the oracle
+        (x, ids, gates)."""
+        xf, (lg, ids_ref, g_ref) = self.route(layer)
+        d = self.eng.inspect_prefill(layer)
+        assert d["T"] == self.T
+        assert np.array_equal(d["ids"], ids_ref), f"prefill ids differ at layer {layer}"
+        assert np.max(np.abs(d["gates"] - g_ref)) <= ATOL_G, f"prefill gates at layer {layer}"
+        if self.shape.renormalize:
+            assert np.max(np.abs(d["gates"].astype(np.float64).sum(1) - 1)) <= TOL_SUM
+        perm = oracle.permutation(ids_ref, self.shape.E)
+        for k in ("counts", "offsets", "sorted", "inv"):
+            assert np.array_equal(d[k], perm[k]), f"prefill {k} differs at layer {layer}"
+        return xf, ids_ref, g_ref
 
     def close(self):
         self.eng.close()

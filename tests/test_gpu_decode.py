@@ -175,4 +175,23 @@ def test_cache_lookup_and_fill_api():
     for bad in ([3, 2], [1, 1], [16], [-1]):
         with pytest.raises(MoEError):
             eng.cache_fill(0, bad)
+    # a device-side list that breaks the order: the ascending prefix is
+    # looked up, every entry from the first break on is rejected (INT_MIN)
+    # and changes nothing
+    int_min = -2 ** 31
+    for U in ([4, 4, 9], [7, 2, 11], [1, 5, 5, 6], [3, 16, 2], [0, 17, 18]):
+        d_ids = torch.tensor(U, dtype=torch.int32, device="cuda")
+        d_n = torch.tensor([len(U)], dtype=torch.int32, device="cuda")
+        d_slot = torch.full((len(U),), 12345, dtype=torch.int32, device="cuda")
+        eng.cache_lookup(1, d_ids, d_n, d_slot)
+        first_bad = next((u for u in range(1, len(U)) if U[u] <= U[u - 1]), len(U))
+        ok = [u for u in range(first_bad) if 0 <= U[u] < sh.E]
+        slots, _, _ = ref.lookup(1, [U[u] for u in ok])
+        want = [int_min] * len(U)
+        for u, sl in zip(ok, slots):
+            want[u] = sl
+        assert d_slot.cpu().tolist() == want, (U, d_slot.cpu().tolist(), want)
+        key, stamp, clock = eng.cache_snapshot()
+        k_ref, s_ref, c_ref = ref.snapshot()
+        assert key.tolist() == k_ref and stamp.tolist() == s_ref and clock == c_ref, U
     eng.close()

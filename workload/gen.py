@@ -238,3 +238,43 @@ def bias_from_sets(sets_step: np.ndarray, E: int) -> np.ndarray:
     b = np.zeros((T, E), dtype=np.float32)
     b[np.arange(T)[:, None], sets_step] = BIAS_STRENGTH
     return b
+
+
+# ------------------------------------------------- wide scale-exponent inputs
+def expert_weights_scaled(shape: Shape, layer: int, expert: int, seed: int = 0,
+                          gu_block_exp: Optional[np.ndarray] = None,
+                          dn_row_exp: Optional[np.ndarray] = None,
+                          jitter: int = 2) -> ExpertWeights:
+    """MXFP4 expert whose E8M0 scale bytes span a wide range of exponents.
+
+    Codes are uniform over the 16 values.  Gate and up: the scale byte of
+    (row r, K block b) is gu_block_exp[b] + j; down: the scale byte of (row
+    r, any K block) is dn_row_exp[r] + j; j uniform over [-jitter, jitter],
+    the result clipped to [0, 250].  A part given as None keeps the usual
+    bytes 119..123.  ``expert = -1`` draws the shared expert.
+    """
+    H, I = shape.H, shape.I
+    base = expert_weights(shape, layer, expert, seed)
+    g = _rng(seed, _SHARED if expert < 0 else _EXPERT, layer, max(expert, 0), 250)
+
+    def spread(centre_of_block, rows, blocks):
+        j = g.integers(-jitter, jitter + 1, size=(rows, blocks))
+        return np.clip(centre_of_block + j, 0, 250).astype(np.uint8)
+
+    sg, su, sd = base.sg, base.su, base.sd
+    if gu_block_exp is not None:
+        c = np.asarray(gu_block_exp, dtype=np.int64)[None, :]
+        sg, su = spread(c, I, H // 32), spread(c, I, H // 32)
+    if dn_row_exp is not None:
+        sd = spread(np.asarray(dn_row_exp, dtype=np.int64)[:, None], H, I // 32)
+    return ExpertWeights(qg=base.qg, qu=base.qu, qd=base.qd, sg=sg, su=su, sd=sd)
+
+
+def tokens_block_scaled(shape: Shape, layer: int, step: int, T: int,
+                        block_shift: np.ndarray, seed: int = 0) -> np.ndarray:
+    """Activations x[t, 32 b + i] = N(0, 1) * 2^block_shift[b], rounded to
+    bf16 (values below 2^-126 land on bf16's subnormal grid); uint16 [T][H]."""
+    g = _rng(seed, _X, layer, step, T, 250)
+    z = g.standard_normal((T, shape.H)).astype(np.float64)
+    z *= np.exp2(np.repeat(np.asarray(block_shift, dtype=np.float64), 32))[None, :]
+    return f32_to_bf16_bits(z.astype(np.float32))

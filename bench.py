@@ -1,24 +1,34 @@
 """Benchmark of the routed MoE expert-layer forward on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--T T]
-                [--prefill-steps P] [--dsv4-decode-steps D] [--calibrate-copy-mb M]
+                [--prefill-steps P] [--dsv4-decode-steps D] [--no-context] ...
 
-A step is one decode call per layer of the workload (router, top-k, dispatch,
-cache lookup, miss fills, expert FFN, combine) for a batch of T tokens, with
-all inputs already resident in HBM.  Default workload: the 35B-A3B-shaped
-decode layer (H=2048, E=256, top-8, I=512, MXFP4 experts, bf16 activations,
-64-slot LRU from a cold start, Zipf(1.1) routing with 60% step overlap), T=16.
-The roofline object is the gate/up expert kernel's (the dominant HBM-bound
-kernel; the miss-fill kernel is bound by PCIe and reported as pcie_h2d_gbs),
-from per-kernel HIP events taken in a second pass: the library launches
-each expert kernel with start and stop events recorded by the dispatch
-itself, so an interval is the kernel's own duration.  The line also carries the DeepSeek-V4-Flash-shaped stack (4 layers,
-H=4096, I=2048, E=256, top-6 + shared): prefill of T=4096 with whole-layer
-uploads from the pinned pool (grouped-GEMM time and MFMA utilisation), and
-T=1 decode through its global LRU.
-With --graph-T, `graph_replay` repeats the decode workload at those T with
-each timed step replayed from its own HIP graph; `value` is always the
-eager, host-submitted rate.
+A step is one decode call per MoE layer of the workload (router, top-k,
+dispatch, cache lookup, miss copies, expert FFN, combine) for a batch of T
+tokens, with every step's activations and router bias already resident in
+HBM.  The headline workload is the GLM-5.2-shaped decode: 8 MoE layers,
+H=6144, E=256 routed experts top-8 plus one shared expert, I=2048, MXFP4
+experts (a 41 GB pool in pinned host memory), T=1, Zipf(1.2) routing with
+55% step-to-step overlap, through one global HBM expert cache of 1228
+slots (60% of the experts) from a cold start; the cache is resized to 614
+slots (30%) without a restart before the middle timed step.  W untimed
+steps run first, then K timed ones.
+
+`value` is tokens/s of whole forwards, miss copies over PCIe included (the
+expert pool lives in host memory by design).  The roofline object is the
+gate/up expert kernel's, the dominant HBM-bound kernel of a layer (the miss
+copies are bound by PCIe and reported as pcie_h2d_gbs), with the down kernel
+and the layer as a whole (router, finalize, gate/up, down, combine) beside
+it; kernel durations come from a second pass over the timed steps in which
+every kernel carries HIP start and stop events recorded by its own dispatch.
+A check pass then runs sampled (step, layer) pairs again with their routing
+and fp32 outputs read back, and the CPU oracle evaluates the same pairs:
+that comparison is `parity`, and its timing `cpu_baseline`.
+
+Context legs (skipped with --no-context): the 35B-A3B-shaped layer at T=16
+(its 107 MB cache stays in the 256 MB Infinity Cache, so its kernel rates
+are MALL rates), and the DeepSeek-V4-Flash-shaped stack: prefill of T=4096
+(grouped MFMA GEMMs, layer uploads double-buffered) and T=1 decode.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -37,20 +47,32 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
+# decode steps of the kernel-timing pass
+TIMING_STEPS = 128
+# (warmup, timed steps) when --warmup / --steps are not given
+DEFAULT_STEPS = {"glm_decode": (0, 1024), "a3b_decode": (32, 512), "dsv4_decode": (16, 256)}
 
-def parse():
+
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=512)
-    ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--workload", default="a3b_decode")
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="glm_decode")
     ap.add_argument("--T", type=int, default=None, help="tokens per step (default: largest of the workload)")
+    ap.add_argument("--distinct", type=int, default=8,
+                    help="generated expert records per layer of the headline workload (expert e "
+                         "holds record e mod N; the same bytes move, set-up is faster; 0: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--extra-T", default="1,4", help="also time these T (decode)")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--check-pairs", type=int, default=4,
+                    help="(step, layer) pairs read back and compared with the oracle")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the 35B-A3B and DeepSeek-V4-Flash context legs")
+    ap.add_argument("--extra-T", default="1,4", help="35B-A3B context leg: also time these T")
     ap.add_argument("--graph-T", default="",
-                    help="also time these T with every step replayed from a HIP graph "
-                         "(e.g. 1,4,16; default: none)")
+                    help="35B-A3B context leg: also time these T with every step replayed from a "
+                         "HIP graph (e.g. 1,4,16; default: none)")
     ap.add_argument("--prefill-steps", type=int, default=3,
                     help="prefill passes of the DeepSeek-V4-Flash-shaped stack (0: skip)")
     ap.add_argument("--dsv4-decode-steps", type=int, default=256,
@@ -58,14 +80,15 @@ def parse():
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="also run one plain copy of this many MiB (counter calibration)")
     ap.add_argument("--weights", choices=("mxfp4", "bf16"), default="mxfp4",
-                    help="expert format of the decode workload (bf16: decode only, no "
-                         "DeepSeek-V4-Flash legs)")
+                    help="expert format of the headline workload (bf16: decode of up to 16 "
+                         "tokens; no context legs)")
     ap.add_argument("--policy-study", type=int, default=0, metavar="STEPS",
                     help="instead of the benchmark line: DeepSeek-V4-Flash-shaped decode under "
                          "each cache placement policy (STEPS timed steps per run)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
+# ------------------------------------------------------------ byte accounting
 def kernel_bytes(sh, lookups, calls, pairs, T_total):
     """Algorithmic HBM bytes of the two decode expert kernels over `calls`
     calls, as (gate/up, down).  Weights: every looked-up expert once, plus
@@ -80,12 +103,31 @@ def kernel_bytes(sh, lookups, calls, pairs, T_total):
     return gateup, down
 
 
+def layer_bytes(sh, lookups, calls, pairs, T_total, bias=True):
+    """Algorithmic HBM bytes of a layer's compute kernels over `calls` calls
+    (the miss copies move host-pool bytes over PCIe and are counted apart):
+    the router reads W_r (fp32 H x E) once per call, the token rows and the
+    bias, and writes the logits; the expert kernels as in kernel_bytes; the
+    combine reads every fp32 expert output row once and writes y in bf16."""
+    gu, dn = kernel_bytes(sh, lookups, calls, pairs, T_total)
+    rows = pairs + (T_total if sh.shared else 0)
+    router = calls * sh.H * sh.E * 4 + T_total * (sh.H * 2 + sh.E * 4 * (2 if bias else 1))
+    combine = rows * sh.H * 4 + T_total * sh.H * 2
+    return router + gu + dn + combine
+
+
+# --------------------------------------------------------------- set-up
 def make_engine(sh, T, cache_slots, staging_slots, prefill_tokens=0, cache_policy="global"):
     from expert_offload_serving_amd import MoEEngine
     return MoEEngine(sh.H, sh.I, sh.E, sh.k, n_layers=sh.layers, has_shared=sh.shared,
                      renormalize=sh.renormalize, max_tokens=T, cache_slots=cache_slots,
                      staging_slots=staging_slots, max_prefill_tokens=prefill_tokens,
                      cache_policy=cache_policy, weight_format=sh.weights)
+
+
+def record_of(e, distinct):
+    """The generated record expert e holds (all distinct when distinct is 0)."""
+    return e if not distinct or e < 0 else e % distinct
 
 
 def load_weights(eng, sh, seed=0, distinct=None):
@@ -97,14 +139,299 @@ def load_weights(eng, sh, seed=0, distinct=None):
         eng.set_router(l, gen.router_weights(sh, l, seed))
         recs = {}
         for e in range(sh.E):
-            src = e if distinct is None else e % distinct
+            src = record_of(e, distinct)
             if src not in recs:
                 recs[src] = gen.expert_weights_of(sh, l, src, seed)
             eng.set_expert(l, e, recs[src])
-            if distinct is None:
+            if not distinct:
                 recs.clear()
         if sh.shared:
             eng.set_expert(l, -1, gen.expert_weights_of(sh, l, -1, seed))
+
+
+def bf16_dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda")
+
+
+def decode_inputs(wl, T, n, seed=0):
+    """Per layer: activations [n][T][H] (bf16 bits) and router bias [n][T][E]
+    on the device, and the same on the host."""
+    import torch
+    from workload import gen
+    sh = wl.shape
+    dev = torch.device("cuda")
+    xs, bs, hx, hb = [], [], [], []
+    for l in range(sh.layers):
+        sets = gen.zipf_sets(sh, l, T, n, wl.zipf_s, wl.overlap, seed) if wl.zipf_s else None
+        x = np.stack([gen.tokens(sh, l, s, T, seed) for s in range(n)])
+        b = np.stack([gen.bias_from_sets(sets[s], sh.E) for s in range(n)]) if sets is not None else None
+        hx.append(x)
+        hb.append(b)
+        xs.append(torch.from_numpy(x.view(np.int16)).to(dev))
+        bs.append(torch.from_numpy(b).to(dev) if b is not None else None)
+    return xs, bs, hx, hb
+
+
+# ------------------------------------------------------------ decode runs
+def run_decode(wl, T, steps, warmup, seed=0, eng=None, distinct=None, resize_at=None,
+               check_pairs=()):
+    """Decode throughput: W untimed steps, then K timed steps by wall clock
+    (host submission included; a cache resize placed at step `resize_at` is
+    inside the timed region).  Then a kernel-timing pass over the same K
+    steps, queued behind a spin kernel so that the kernels run back to back
+    as in the timed pass, in which every kernel carries start and stop
+    events recorded by its own dispatch.  Then a check pass: the listed
+    (step, layer) pairs again with routing and fp32 outputs read back (the
+    outputs do not depend on the cache state)."""
+    import torch
+
+    sh = wl.shape
+    own = eng is None
+    if own:
+        eng = make_engine(sh, T, wl.cache_slots, wl.staging_slots)
+        load_weights(eng, sh, seed, distinct)
+    n = warmup + steps
+    xs, bs, hx, hb = decode_inputs(wl, T, n, seed)
+    y = torch.empty((T, sh.H), dtype=torch.int16, device="cuda")
+    resize_to = wl.resize[0][1] if wl.resize else None
+    resize_info = {}
+
+    def do_step(s, allow_resize=True):
+        if allow_resize and resize_to is not None and s == resize_at:
+            t0 = time.perf_counter()
+            before = eng.stats()
+            eng.cache_resize(resize_to)
+            after = eng.stats()
+            resize_info.update(before_step=s, slots=[wl.cache_slots, resize_to],
+                               wall_ms=round(1e3 * (time.perf_counter() - t0), 3),
+                               evicted=after["evictions"] - before["evictions"],
+                               bytes_d2d=after["bytes_d2d"] - before["bytes_d2d"])
+        for l in range(sh.layers):
+            eng.forward(l, xs[l][s], bias=None if bs[l] is None else bs[l][s], y=y)
+
+    for s in range(warmup):
+        do_step(s)
+    torch.cuda.synchronize()
+    eng.reset_stats()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(warmup, warmup + steps):
+        do_step(s)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    st = eng.stats()
+    elapsed = t1 - t0
+    # kernel-timing pass over the first timed steps, at most TIMING_STEPS of
+    # them (every call records 16 events); the cache state continues from
+    # the first pass, so the byte counts come from this pass's stats
+    n_t = min(steps, TIMING_STEPS)
+    eng.reset_stats()
+    eng.set_timing(True)
+    torch.cuda._sleep(int(2e8))  # ~0.1 s spin: the host queues the steps meanwhile
+    for s in range(warmup, warmup + n_t):
+        do_step(s, allow_resize=False)
+    torch.cuda.synchronize()
+    tm = eng.get_timing()
+    eng.set_timing(False)
+    st2 = eng.stats()
+    calls_t = n_t * sh.layers
+    pairs_t = calls_t * T * sh.k
+    gb, db = kernel_bytes(sh, st2["lookups"], calls_t, pairs_t, calls_t * T)
+    lb = layer_bytes(sh, st2["lookups"], calls_t, pairs_t, calls_t * T, bias=wl.zipf_s is not None)
+    checked = []
+    if check_pairs:
+        ids = torch.empty((T, sh.k), dtype=torch.int32, device="cuda")
+        gates = torch.empty((T, sh.k), dtype=torch.float32, device="cuda")
+        y32 = torch.empty((T, sh.H), dtype=torch.float32, device="cuda")
+        for (s, l) in check_pairs:
+            eng.forward(l, xs[l][s], bias=None if bs[l] is None else bs[l][s], y=y, ids=ids,
+                        gates=gates, y32=y32)
+            torch.cuda.synchronize()
+            checked.append(dict(step=s, layer=l, x=hx[l][s], bias=None if hb[l] is None else hb[l][s],
+                                ids=ids.cpu().numpy(), gates=gates.cpu().numpy(),
+                                y32=y32.cpu().numpy(), y=y.cpu().numpy().view(np.uint16)))
+    if own:
+        eng.close()
+    nl = max(tm["n_decode"], 1)
+    ms = tm["decode_ms"]
+    layer_ms = ms["router"] + ms["finalize"] + ms["gateup"] + ms["down"] + ms["combine"]
+
+    def gbs(nbytes, t_ms):
+        return nbytes / (t_ms * 1e6) if t_ms > 0 else None
+    return dict(T=T, steps=steps, elapsed_s=elapsed, tokens_per_s=T * steps / elapsed,
+                ms_per_step=1e3 * elapsed / steps, stats=st,
+                hit_rate=st["hits"] / max(st["lookups"], 1),
+                launches=tm["n_decode"],
+                kernel_us={k: round(1e3 * v / nl, 3) for k, v in ms.items()},
+                gateup_us=1e3 * ms["gateup"] / nl, down_us=1e3 * ms["down"] / nl,
+                gateup_bytes=gb / nl, down_bytes=db / nl, layer_bytes=lb / nl,
+                layer_us=1e3 * layer_ms / nl,
+                gateup_gbs=gbs(gb, ms["gateup"]), down_gbs=gbs(db, ms["down"]),
+                layer_gbs=gbs(lb, layer_ms),
+                h2d_gbs=st["bytes_h2d"] / (elapsed * 1e9), resize=resize_info, checked=checked)
+
+
+def run_decode_graph(wl, T, steps, warmup, seed=0):
+    """Decode throughput with every timed step replayed from its own HIP
+    graph (captured after the eager warm-up; capture runs nothing), so the
+    host's launch work is out of the timed region.  Same inputs, cache and
+    kernels as run_decode; the steps run in the same order."""
+    import torch
+
+    sh = wl.shape
+    assert not wl.resize, "a cache resize cannot be captured"
+    eng = make_engine(sh, T, wl.cache_slots, wl.staging_slots)
+    load_weights(eng, sh, seed)
+    n = warmup + steps
+    xs, bs, _, _ = decode_inputs(wl, T, n, seed)
+    y = torch.empty((T, sh.H), dtype=torch.int16, device="cuda")
+
+    def do_step(s):
+        for l in range(sh.layers):
+            eng.forward(l, xs[l][s], bias=None if bs[l] is None else bs[l][s], y=y)
+
+    for s in range(warmup):
+        do_step(s)
+    torch.cuda.synchronize()
+    graphs = []
+    for s in range(warmup, warmup + steps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            do_step(s)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    eng.reset_stats()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st = eng.stats()
+    eng.close()
+    return dict(T=T, steps=steps, tokens_per_s=T * steps / elapsed, ms_per_step=1e3 * elapsed / steps,
+                hit_rate=st["hits"] / max(st["lookups"], 1))
+
+
+def decode_kernels(T):
+    """Names of the decode expert kernels the library launches for T tokens:
+    the streaming variants up to 16 tokens per call, else the others."""
+    if T <= 16:
+        return "gateup_stream_kernel", "down_stream_kernel"
+    return "gateup_decode_kernel", "down_decode_kernel"
+
+
+def roofline_entry(name, gbs, us, nbytes, launches, bound="hbm"):
+    return {"kernel": name, "bound": bound,
+            "achieved": None if gbs is None else round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": None if gbs is None else round(gbs / HBM_PEAK_GBS, 4),
+            "launches": launches, "avg_launch_us": round(us, 3), "bytes_per_launch": round(nbytes)}
+
+
+def layer_entry(r, bound="hbm"):
+    """The layer as a whole: algorithmic bytes of its compute kernels over
+    the sum of their durations (router, finalize, gate/up, down, combine)."""
+    gbs = r["layer_gbs"]
+    return {"bound": bound, "achieved": None if gbs is None else round(gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": None if gbs is None else round(gbs / HBM_PEAK_GBS, 4),
+            "bytes_per_layer": round(r["layer_bytes"]), "us_per_layer": round(r["layer_us"], 3)}
+
+
+def decode_summary(r, bound="hbm"):
+    kgu, kdn = decode_kernels(r["T"])
+    return {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 4),
+            "hit_rate": round(r["hit_rate"], 4), "h2d_gbs": round(r["h2d_gbs"], 2),
+            "kernel_us": r["kernel_us"],
+            "roofline": [roofline_entry(kgu, r["gateup_gbs"], r["gateup_us"], r["gateup_bytes"],
+                                        r["launches"], bound),
+                         roofline_entry(kdn, r["down_gbs"], r["down_us"], r["down_bytes"],
+                                        r["launches"], bound)],
+            "layer": layer_entry(r, bound)}
+
+
+# ------------------------------------------------------------ context legs
+def run_dsv4(prefill_steps, decode_steps, decode_warmup, seed=0):
+    """The DeepSeek-V4-Flash-shaped stack on one engine: prefill of all
+    layers per step (layer uploads included), then T=1 decode through the
+    global LRU (13.4 MB experts: HBM-bound, not cache-resident)."""
+    import torch
+    from workload import gen
+    wp, wd = gen.WORKLOADS["dsv4_prefill"], gen.WORKLOADS["dsv4_decode"]
+    sh = wp.shape
+    T = wp.Ts[0]
+    eng = make_engine(sh, max(wd.Ts), wd.cache_slots, wd.staging_slots, prefill_tokens=T)
+    load_weights(eng, sh, seed)
+    out = {}
+    if prefill_steps > 0:
+        xs = [bf16_dev(gen.tokens(sh, l, 0, T, seed)) for l in range(sh.layers)]
+        ys = [torch.empty((T, sh.H), dtype=torch.int16, device="cuda") for _ in range(sh.layers)]
+        eng.prefill(xs, ys)
+        torch.cuda.synchronize()
+        eng.reset_stats()
+        eng.set_timing(True)
+        t0 = time.perf_counter()
+        for _ in range(prefill_steps):
+            eng.prefill(xs, ys)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        tm = eng.get_timing()
+        eng.set_timing(False)
+        el = t1 - t0
+        layers = prefill_steps * sh.layers
+        # algorithmic flops per layer: 3 matrices of H x I per (token, expert),
+        # k routed experts plus the shared one, 2 flops per multiply-add
+        flops_layer = 2 * 3 * sh.H * sh.I * T * (sh.k + (1 if sh.shared else 0))
+        nl = max(tm["n_prefill"], 1)
+        pm = tm["prefill_ms"]
+        gu_ms, dn_ms = pm["gateup"] / nl, pm["down"] / nl
+        gemm_ms = gu_ms + dn_ms
+        tflops = flops_layer / (gemm_ms * 1e9)
+        upload = sh.E * sh.expert_bytes() * layers
+        out["prefill"] = {
+            "workload": wp.name, "T": T, "layers": sh.layers, "steps": prefill_steps,
+            "tokens_per_s_end_to_end": round(T * prefill_steps / el, 1),
+            "ms_per_step": round(1e3 * el / prefill_steps, 2),
+            "gemm_ms_per_layer": round(gemm_ms, 4),
+            "stage_us_per_layer": {k: round(1e3 * v / nl, 1) for k, v in pm.items()},
+            "gemm_launches": 2 * tm["n_prefill"],
+            "tokens_per_s_gemm_only": round(T / (gemm_ms * 1e-3) / sh.layers, 1),
+            "flops_per_layer": flops_layer,
+            "mfma_tflops": round(tflops, 1),
+            "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+            "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            # matrix-core busy share by counters (profiles/mfma_busy_*.md)
+            "mfma_busy_counters": mfma_busy_from_profile(),
+            "gateup_prefill_kernel": {"avg_us": round(1e3 * gu_ms, 1),
+                                      "tflops": round(2 * flops_layer / 3 / (gu_ms * 1e9), 1)},
+            "down_prefill_kernel": {"avg_us": round(1e3 * dn_ms, 1),
+                                    "tflops": round(flops_layer / 3 / (dn_ms * 1e9), 1)},
+            "pcie_h2d_gbs": round(upload / (el * 1e9), 2)}
+    if decode_steps > 0:
+        r = run_decode(wd, 1, decode_steps, decode_warmup, seed, eng=eng)
+        out["dsv4_decode_T1"] = decode_summary(r)
+    eng.close()
+    return out
+
+
+def run_a3b(steps, warmup, extra_T, graph_T, seed=0):
+    """The 35B-A3B-shaped layer from a cold 64-slot cache: T=16 and the
+    extra T.  Its 107 MB cache fits the 256 MB Infinity Cache, so the kernel
+    rates are labelled as MALL rates."""
+    from workload import gen
+    wl = gen.WORKLOADS["a3b_decode"]
+    out = {}
+    for T in [16] + [t for t in extra_T if t != 16 and t in wl.Ts]:
+        r = run_decode(wl, T, steps, warmup, seed)
+        out[f"T={T}"] = decode_summary(r, bound="mall")
+    for T in graph_T:
+        if T in wl.Ts:
+            r = run_decode_graph(wl, T, steps, warmup, seed)
+            out[f"graph_T={T}"] = {"tokens_per_s": round(r["tokens_per_s"], 1),
+                                   "ms_per_step": round(r["ms_per_step"], 4),
+                                   "hit_rate": round(r["hit_rate"], 4)}
+    return out
 
 
 def policy_study(steps, warmup, seed=0):
@@ -145,247 +472,93 @@ def policy_study(steps, warmup, seed=0):
             "steps": steps, "warmup": warmup, "zipf_s": wl.zipf_s, "overlap": wl.overlap}}
 
 
-def bf16_dev(bits):
-    import torch
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda")
+# ------------------------------------------------------ oracle on the sample
+def check_pairs_of(wl, warmup, steps, n_pairs):
+    """(step, layer) pairs spread over the timed steps and the layers (the
+    last timed step is always one of them)."""
+    L = wl.shape.layers
+    if n_pairs <= 0 or steps <= 0:
+        return []
+    out = []
+    for i in range(n_pairs):
+        s = warmup + steps - 1 - (i * steps) // n_pairs
+        out.append((s, (L - 1 - (i * max(L - 1, 1)) // max(n_pairs - 1, 1)) % L))
+    return sorted(set(out))
 
 
-def decode_inputs(wl, T, n, seed=0):
-    import torch
-    from workload import gen
-    sh = wl.shape
-    dev = torch.device("cuda")
-    xs, bs = [], []
-    for l in range(sh.layers):
-        sets = gen.zipf_sets(sh, l, T, n, wl.zipf_s, wl.overlap, seed) if wl.zipf_s else None
-        xs.append(torch.stack([bf16_dev(gen.tokens(sh, l, s, T, seed)) for s in range(n)]))
-        bs.append(torch.from_numpy(np.stack([gen.bias_from_sets(sets[s], sh.E) for s in range(n)])).to(dev)
-                  if sets is not None else None)
-    return xs, bs
-
-
-def run_decode_graph(wl, T, steps, warmup, seed=0):
-    """Decode throughput with every timed step replayed from its own HIP
-    graph (captured after the eager warm-up; capture runs nothing), so the
-    host's launch work is out of the timed region.  Same inputs, cache and
-    kernels as run_decode; the steps run in the same order."""
-    import torch
-
-    sh = wl.shape
-    assert not wl.resize, "a cache resize cannot be captured"
-    eng = make_engine(sh, T, wl.cache_slots, wl.staging_slots)
-    load_weights(eng, sh, seed)
-    n = min(wl.steps, steps + warmup)
-    xs, bs = decode_inputs(wl, T, n, seed)
-    y = torch.empty((T, sh.H), dtype=torch.int16, device="cuda")
-
-    def do_step(s):
-        for l in range(sh.layers):
-            eng.forward(l, xs[l][s % n], bias=None if bs[l] is None else bs[l][s % n], y=y)
-
-    for s in range(warmup):
-        do_step(s)
-    torch.cuda.synchronize()
-    graphs = []
-    for s in range(warmup, warmup + steps):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            do_step(s)
-        graphs.append(g)
-    torch.cuda.synchronize()
-    eng.reset_stats()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for g in graphs:
-        g.replay()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    st = eng.stats()
-    eng.close()
-    return dict(T=T, steps=steps, tokens_per_s=T * steps / elapsed, ms_per_step=1e3 * elapsed / steps,
-                hit_rate=st["hits"] / max(st["lookups"], 1))
-
-
-def run_decode(wl, T, steps, warmup, seed=0, eng=None):
-    """Decode throughput (wall clock over `steps` steps, host submission
-    included), then a kernel-timing pass over the same number of steps, in
-    which each expert kernel carries HIP start and stop events recorded by
-    its dispatch (queued behind a spin kernel, so that the kernels also run
-    back to back as in the timed pass and not at the host's pace)."""
-    import torch
-
-    sh = wl.shape
-    own = eng is None
-    if own:
-        eng = make_engine(sh, T, wl.cache_slots, wl.staging_slots)
-        load_weights(eng, sh, seed)
-    n = min(wl.steps, steps + warmup)
-    xs, bs = decode_inputs(wl, T, n, seed)
-    y = torch.empty((T, sh.H), dtype=torch.int16, device="cuda")
-    resize = dict(wl.resize)
-
-    def do_step(s):
-        if s in resize:
-            eng.cache_resize(resize[s])
-        for l in range(sh.layers):
-            eng.forward(l, xs[l][s % n], bias=None if bs[l] is None else bs[l][s % n], y=y)
-
-    for s in range(warmup):
-        do_step(s)
-    torch.cuda.synchronize()
-    eng.reset_stats()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(warmup, warmup + steps):
-        do_step(s)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    st = eng.stats()
-    elapsed = t1 - t0
-    calls = steps * sh.layers
-    pairs = calls * T * sh.k
-    gb, db = kernel_bytes(sh, st["lookups"], calls, pairs, calls * T)
-    # kernel-timing pass over the same step range (the cache state differs:
-    # it continues from the first pass, so the byte count is recomputed)
-    eng.reset_stats()
-    eng.set_timing(True)
-    torch.cuda._sleep(int(2e8))  # ~0.1 s spin: the host queues the steps meanwhile
-    for s in range(warmup, warmup + steps):
-        do_step(s)
-    torch.cuda.synchronize()
-    tm = eng.get_timing()
-    eng.set_timing(False)
-    st2 = eng.stats()
-    gb2, db2 = kernel_bytes(sh, st2["lookups"], calls, pairs, calls * T)
-    if own:
-        eng.close()
-    nl = max(tm["n_decode"], 1)
-    return dict(T=T, steps=steps, elapsed_s=elapsed, tokens_per_s=T * steps / elapsed,
-                ms_per_step=1e3 * elapsed / steps, stats=st,
-                hit_rate=st["hits"] / max(st["lookups"], 1),
-                launches=tm["n_decode"],
-                gateup_us=1e3 * tm["ms_decode_gateup"] / nl, down_us=1e3 * tm["ms_decode_down"] / nl,
-                gateup_bytes=gb2 / nl, down_bytes=db2 / nl,
-                gateup_gbs=gb2 / (tm["ms_decode_gateup"] * 1e6) if tm["ms_decode_gateup"] > 0 else None,
-                down_gbs=db2 / (tm["ms_decode_down"] * 1e6) if tm["ms_decode_down"] > 0 else None,
-                ffn_gbs=(gb2 + db2) / (tm["ms_decode"] * 1e6) if tm["ms_decode"] > 0 else None,
-                h2d_gbs=st["bytes_h2d"] / (elapsed * 1e9))
-
-
-def decode_kernels(T):
-    """Names of the decode expert kernels the library launches for T tokens:
-    the streaming variants up to 16 tokens per call, else the others."""
-    if T <= 16:
-        return "gateup_stream_kernel", "down_stream_kernel"
-    return "gateup_decode_kernel", "down_decode_kernel"
-
-
-def roofline_entry(name, gbs, us, nbytes, launches):
-    return {"kernel": name, "bound": "hbm",
-            "achieved": None if gbs is None else round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": None if gbs is None else round(gbs / HBM_PEAK_GBS, 4),
-            "launches": launches, "avg_launch_us": round(us, 3), "bytes_per_launch": round(nbytes)}
-
-
-def run_dsv4(prefill_steps, decode_steps, decode_warmup, seed=0):
-    """The DeepSeek-V4-Flash-shaped stack on one engine: prefill of all
-    layers per step (layer uploads included), then T=1 decode through the
-    global LRU (13.4 MB experts: HBM-bound, not cache-resident)."""
-    import torch
-    from workload import gen
-    wp, wd = gen.WORKLOADS["dsv4_prefill"], gen.WORKLOADS["dsv4_decode"]
-    sh = wp.shape
-    T = wp.Ts[0]
-    eng = make_engine(sh, max(wd.Ts), wd.cache_slots, wd.staging_slots, prefill_tokens=T)
-    load_weights(eng, sh, seed)
-    out = {}
-    if prefill_steps > 0:
-        xs = [bf16_dev(gen.tokens(sh, l, 0, T, seed)) for l in range(sh.layers)]
-        ys = [torch.empty((T, sh.H), dtype=torch.int16, device="cuda") for _ in range(sh.layers)]
-        eng.prefill(xs, ys)
-        torch.cuda.synchronize()
-        eng.reset_stats()
-        eng.set_timing(True)
-        t0 = time.perf_counter()
-        for _ in range(prefill_steps):
-            eng.prefill(xs, ys)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        tm = eng.get_timing()
-        eng.set_timing(False)
-        el = t1 - t0
-        layers = prefill_steps * sh.layers
-        # algorithmic flops per layer: 3 matrices of H x I per (token, expert),
-        # k routed experts plus the shared one, 2 flops per multiply-add
-        flops_layer = 2 * 3 * sh.H * sh.I * T * (sh.k + (1 if sh.shared else 0))
-        nl = max(tm["n_prefill"], 1)
-        gemm_ms = tm["ms_prefill"] / nl
-        gu_ms, dn_ms = tm["ms_prefill_gateup"] / nl, tm["ms_prefill_down"] / nl
-        tflops = flops_layer / (gemm_ms * 1e9)
-        upload = sh.E * sh.expert_bytes() * layers
-        out["prefill"] = {
-            "workload": wp.name, "T": T, "layers": sh.layers, "steps": prefill_steps,
-            "tokens_per_s_end_to_end": round(T * prefill_steps / el, 1),
-            "ms_per_step": round(1e3 * el / prefill_steps, 2),
-            "gemm_ms_per_layer": round(gemm_ms, 4),
-            "gemm_launches": 2 * tm["n_prefill"],
-            "tokens_per_s_gemm_only": round(T / (gemm_ms * 1e-3) / sh.layers, 1),
-            "flops_per_layer": flops_layer,
-            "mfma_tflops": round(tflops, 1),
-            "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
-            "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            # matrix-core busy share by counters (profiles/mfma_busy_*.md)
-            "mfma_busy_counters": mfma_busy_from_profile(),
-            "gateup_prefill_kernel": {"avg_us": round(1e3 * gu_ms, 1),
-                                      "tflops": round(2 * flops_layer / 3 / (gu_ms * 1e9), 1)},
-            "down_prefill_kernel": {"avg_us": round(1e3 * dn_ms, 1),
-                                    "tflops": round(flops_layer / 3 / (dn_ms * 1e9), 1)},
-            "pcie_h2d_gbs": round(upload / (el * 1e9), 2)}
-    if decode_steps > 0:
-        r = run_decode(wd, 1, decode_steps, decode_warmup, seed, eng=eng)
-        out["dsv4_decode_T1"] = {
-            "tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 4),
-            "hit_rate": round(r["hit_rate"], 4), "h2d_gbs": round(r["h2d_gbs"], 2),
-            "roofline": [roofline_entry(decode_kernels(1)[0], r["gateup_gbs"], r["gateup_us"],
-                                        r["gateup_bytes"], r["launches"]),
-                         roofline_entry(decode_kernels(1)[1], r["down_gbs"], r["down_us"],
-                                        r["down_bytes"], r["launches"])]}
-    eng.close()
-    return out
-
-
-def cpu_baseline(wl, T, seconds):
-    """The oracle as it stands, on a bounded sample of the same workload."""
+def oracle_pair(sh, pair, routers, records, shared_recs):
+    """The CPU oracle on one (step, layer) pair: routing, dispatch and the
+    per-token expert loops, each expert dequantised where it is used."""
     import oracle
-    from tests import harness as hz
+    from oracle import experts as oexp
+    from workload import gen
+    l = pair["layer"]
+    x = gen.bf16_bits_to_f32(pair["x"])
+    lg, ids, g = oracle.route(x, routers[l], sh.k, pair["bias"], sh.renormalize)
+    oracle.permutation(ids, sh.E)
+    shared = oexp.dequant_expert(shared_recs[l]) if sh.shared else None
+    y = oracle.moe_layer(x, ids, g, lambda e: oexp.dequant_expert(records[l][e]), shared=shared)
+    return ids, g, y
+
+
+def cpu_baseline(wl, checked, seconds, distinct, seed=0):
+    """The oracle as it stands on the check pass's sample: timed on all the
+    threads numpy may use, plus one pair on one thread; and compared with the
+    GPU's results for the same pairs (routing bit for bit, gates, fp32
+    outputs against 2e-2 x rms)."""
     from workload import gen
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
+        threadpool_limits = None
         threads = len(os.sched_getaffinity(0))
     sh = wl.shape
-    model = hz.Model(sh)
-    sets = [gen.zipf_sets(sh, l, T, 64, wl.zipf_s, wl.overlap, 0) if wl.zipf_s else None
-            for l in range(sh.layers)]
-    cache = oracle.SlotCache(wl.cache_slots, sh.E)
+    routers = {p["layer"]: gen.router_weights(sh, p["layer"], seed) for p in checked}
+    records = {}
+    for p in checked:
+        l = p["layer"]
+        recs = records.setdefault(l, {})
+        for e in range(sh.E):
+            if record_of(e, distinct) not in recs:
+                recs[record_of(e, distinct)] = gen.expert_weights_of(sh, l, record_of(e, distinct), seed)
+    by_expert = {l: {e: records[l][record_of(e, distinct)] for e in range(sh.E)} for l in records}
+    shared = {l: gen.expert_weights_of(sh, l, -1, seed) for l in records} if sh.shared else {}
+    done, worst, ids_ok, gates_ok = 0, 0.0, True, True
     t0 = time.perf_counter()
-    done = 0
-    while time.perf_counter() - t0 < seconds and done < 64:
-        for l in range(sh.layers):
-            x = gen.bf16_bits_to_f32(gen.tokens(sh, l, done, T, 0))
-            bias = gen.bias_from_sets(sets[l][done], sh.E) if sets[l] is not None else None
-            _, ids, g = model.route(l, x, bias)
-            cache.lookup(l, oracle.permutation(ids, sh.E)["unique"])
-            model.layer_out(l, x, ids, g)
+    for p in checked:
+        if done and time.perf_counter() - t0 > seconds:
+            break
+        ids, g, y = oracle_pair(sh, p, routers, by_expert, shared)
+        ids_ok &= bool(np.array_equal(ids, p["ids"]))
+        gates_ok &= bool(np.max(np.abs(g - p["gates"])) <= 1e-6)
+        rms = float(np.sqrt(np.mean(y ** 2)))
+        worst = max(worst, float(np.max(np.abs(p["y32"].astype(np.float64) - y))) / rms)
         done += 1
     el = time.perf_counter() - t0
-    return {"value": round(T * done / el, 3), "unit": "tokens/s", "cores": int(threads),
+    T = p["x"].shape[0]
+    one = None
+    if threadpool_limits is not None and checked:
+        with threadpool_limits(limits=1):
+            t1 = time.perf_counter()
+            oracle_pair(sh, checked[0], routers, by_expert, shared)
+            one = time.perf_counter() - t1
+    L = sh.layers
+    base = {"value": round(T * done / L / el, 4), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{done} steps x T={T} of {wl.name} (routing, LRU simulation, per-token "
-                      f"fp64 expert loops) in {el:.1f}s"}
+            "sample": f"{done} (step, layer) pairs of {wl.name} at T={T} (routing, dispatch, "
+                      f"per-token fp64 expert loops with each expert dequantised where used) in "
+                      f"{el:.1f}s; a token is {L} layer-steps",
+            "one_thread": None if one is None else {"value": round(T / L / one, 4),
+                                                    "unit": "tokens/s", "cores": 1,
+                                                    "sample": "the first pair on one thread"}}
+    parity = {"pairs": [(p["step"], p["layer"]) for p in checked[:done]], "ids_exact": ids_ok,
+              "gates_within_1e-6": gates_ok, "max_err_over_rms": round(worst, 8),
+              "tolerance": 2e-2, "ok": bool(ids_ok and gates_ok and worst <= 2e-2)}
+    return base, parity
 
 
+# ---------------------------------------------------------------- profiles
 def profile_fields(name):
     """The `- key: value` fields of a committed counter summary in profiles/,
     or None when the file is missing or was taken on another version of the
@@ -430,6 +603,7 @@ def traffic_from_profile(kernel, workload):
     except (KeyError, ValueError):
         return None
 
+
 def calibrate_copy(mb):
     """One plain device-to-device copy of `mb` MiB through the library's copy
     kernel, for scaling traffic counters to bytes."""
@@ -442,6 +616,10 @@ def calibrate_copy(mb):
     torch.cuda.synchronize()
 
 
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -449,76 +627,80 @@ def main():
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
     import torch
+    from dataclasses import replace
     from workload import gen
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if a.policy_study > 0:
-        print(json.dumps(policy_study(a.policy_study, min(a.warmup, a.policy_study))), flush=True)
+        print(json.dumps(policy_study(a.policy_study, min(a.warmup or 16, a.policy_study))),
+              flush=True)
         return
     wl = gen.WORKLOADS[a.workload]
     if a.weights != "mxfp4":
-        from dataclasses import replace
         wl = replace(wl, name=f"{wl.name}_{a.weights}", shape=replace(wl.shape, weights=a.weights))
+    W0, K0 = DEFAULT_STEPS.get(a.workload, (32, 512))
+    W = W0 if a.warmup is None else a.warmup
+    K = K0 if a.steps is None else a.steps
     T = a.T or max(wl.Ts)
-    res = run_decode(wl, T, a.steps, a.warmup)
-    extra = {}
-    for t in [int(v) for v in a.extra_T.split(",") if v.strip()]:
-        if t != T and t in wl.Ts:
-            r = run_decode(wl, t, a.steps, a.warmup)
-            extra[f"T={t}"] = {"tokens_per_s": round(r["tokens_per_s"], 1),
-                               "ms_per_step": round(r["ms_per_step"], 4),
-                               "hit_rate": round(r["hit_rate"], 4),
-                               "gateup_gbs": r["gateup_gbs"] and round(r["gateup_gbs"], 1),
-                               "down_gbs": r["down_gbs"] and round(r["down_gbs"], 1),
-                               "h2d_gbs": round(r["h2d_gbs"], 2)}
-    graph = {}
-    if not wl.resize:
-        for t in [int(v) for v in a.graph_T.split(",") if v.strip()]:
-            if t in wl.Ts:
-                r = run_decode_graph(wl, t, a.steps, a.warmup)
-                graph[f"T={t}"] = {"tokens_per_s": round(r["tokens_per_s"], 1),
-                                   "ms_per_step": round(r["ms_per_step"], 4),
-                                   "hit_rate": round(r["hit_rate"], 4)}
     sh = wl.shape
+    resize_at = W + K // 2 if wl.resize else None
+    pairs = check_pairs_of(wl, W, K, 0 if a.no_cpu_baseline else a.check_pairs)
+    log(f"headline {wl.name} T={T}: {W} warm-up + {K} timed steps (loading the expert pool)")
+    res = run_decode(wl, T, K, W, distinct=a.distinct, resize_at=resize_at, check_pairs=pairs)
+    log(f"headline done: {res['tokens_per_s']:.1f} tokens/s")
     kgu, kdn = decode_kernels(T)
     roof = roofline_entry(kgu, res["gateup_gbs"], res["gateup_us"], res["gateup_bytes"],
                           res["launches"])
     roof["traffic"] = traffic_from_profile(kgu, f"{wl.name}_T{T}")
     roof["other_kernels"] = [roofline_entry(kdn, res["down_gbs"], res["down_us"],
                                             res["down_bytes"], res["launches"])]
-    roof["expert_ffn_pair_gbs"] = res["ffn_gbs"] and round(res["ffn_gbs"], 1)
+    roof["layer"] = layer_entry(res)
+    cfg = {"workload": wl.name, "T": T, "H": sh.H, "I": sh.I, "E": sh.E, "k": sh.k,
+           "layers": sh.layers, "shared_expert": sh.shared, "cache_slots": wl.cache_slots,
+           "staging_slots": wl.staging_slots,
+           "weights": ("MXFP4 (E2M1 + E8M0/32)" if sh.weights == "mxfp4" else sh.weights),
+           "zipf_s": wl.zipf_s, "overlap": wl.overlap, "cold_start": True,
+           "expert_records_per_layer": a.distinct or sh.E}
+    if wl.resize:
+        cfg["resize"] = {"to_slots": wl.resize[0][1], "before_step": resize_at}
     line = {
         "metric": "MoE-layer decode tokens/s",
         "value": round(res["tokens_per_s"], 2),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": a.steps,
-        "warmup": a.warmup,
+        "steps": K,
+        "warmup": W,
         "ms_per_step": round(res["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "T": T, "H": sh.H, "I": sh.I, "E": sh.E, "k": sh.k,
-                   "layers": sh.layers, "shared_expert": sh.shared,
-                   "cache_slots": wl.cache_slots, "staging_slots": wl.staging_slots,
-                   "weights": ("MXFP4 (E2M1 + E8M0/32)" if sh.weights == "mxfp4" else sh.weights),
-                   "zipf_s": wl.zipf_s,
-                   "overlap": wl.overlap},
+        "config": cfg,
         "roofline": roof,
+        "kernel_us_per_layer": res["kernel_us"],
         "cache": {"hit_rate": round(res["hit_rate"], 4), **{k: res["stats"][k] for k in
-                  ("lookups", "hits", "fills", "bypasses", "evictions")}},
+                  ("lookups", "hits", "fills", "bypasses", "evictions", "bytes_d2d")}},
+        "resize": res["resize"] or None,
         "pcie_h2d_gbs": round(res["h2d_gbs"], 2),
-        "other_T": extra,
     }
-    if graph:
-        line["graph_replay"] = graph
-    if a.weights == "mxfp4" and (a.prefill_steps > 0 or a.dsv4_decode_steps > 0):
-        line.update(run_dsv4(a.prefill_steps, a.dsv4_decode_steps, max(a.dsv4_decode_steps // 4, 1)))
+    if not a.no_cpu_baseline and res["checked"]:
+        log("oracle on the check pairs")
+        base, parity = cpu_baseline(wl, res["checked"], a.cpu_seconds, a.distinct)
+        line["cpu_baseline"] = base
+        line["parity"] = parity
+    if not a.no_context and a.weights == "mxfp4":
+        log("context: 35B-A3B-shaped layer")
+        line["context"] = {"a3b_decode": run_a3b(
+            K if a.steps is not None else DEFAULT_STEPS["a3b_decode"][1],
+            W if a.warmup is not None else DEFAULT_STEPS["a3b_decode"][0],
+            [int(v) for v in a.extra_T.split(",") if v.strip()],
+            [int(v) for v in a.graph_T.split(",") if v.strip()])}
+        if a.prefill_steps > 0 or a.dsv4_decode_steps > 0:
+            log("context: DeepSeek-V4-Flash-shaped stack")
+            line["context"].update(run_dsv4(a.prefill_steps, a.dsv4_decode_steps,
+                                             max(a.dsv4_decode_steps // 4, 1)))
     if a.calibrate_copy_mb > 0:
         calibrate_copy(a.calibrate_copy_mb)
-    if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, T, a.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

@@ -35,6 +35,15 @@ class moe_config(ctypes.Structure):
         "weight_format")]
 
 
+class moe_timing(ctypes.Structure):
+    _fields_ = [("n_decode", ctypes.c_int32), ("n_prefill", ctypes.c_int32),
+                ("decode_ms", ctypes.c_double * 6), ("prefill_ms", ctypes.c_double * 4)]
+
+
+DECODE_KERNELS = ("router", "finalize", "fill", "gateup", "down", "combine")
+PREFILL_STAGES = ("routing", "gateup", "down", "combine")
+
+
 class moe_stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "forward_calls", "lookups", "hits", "fills", "bypasses", "evictions", "bytes_h2d",
@@ -65,8 +74,7 @@ _SIGS = {
     "moe_get_stats": (_I32, [_P, ctypes.POINTER(moe_stats)]),
     "moe_reset_stats": (_I32, [_P]),
     "moe_set_timing": (_I32, [_P, _I32]),
-    "moe_get_timing": (_I32, [_P, _P, _P, _P, _P]),
-    "moe_get_timing_split": (_I32, [_P, _P, _P]),
+    "moe_get_timing": (_I32, [_P, ctypes.POINTER(moe_timing)]),
     "moe_probe_copy": (_I32, [_P, _P, ctypes.c_size_t, _P]),
 }
 
@@ -246,20 +254,13 @@ def moe_set_timing(ctx, enable: bool):
     _check(lib.moe_set_timing(ctx, 1 if enable else 0), "moe_set_timing")
 
 
-def moe_get_timing(ctx):
-    nd, np_ = ctypes.c_int32(), ctypes.c_int32()
-    md, mp = ctypes.c_double(), ctypes.c_double()
-    _check(lib.moe_get_timing(ctx, ctypes.byref(nd), ctypes.byref(md), ctypes.byref(np_),
-                              ctypes.byref(mp)), "moe_get_timing")
-    return dict(n_decode=nd.value, ms_decode=md.value, n_prefill=np_.value, ms_prefill=mp.value)
-
-
-def moe_get_timing_split(ctx):
-    n = (ctypes.c_int32 * 2)()
-    ms = (ctypes.c_double * 6)()
-    _check(lib.moe_get_timing_split(ctx, n, ms), "moe_get_timing_split")
-    return dict(n_decode=n[0], ms_decode=ms[0], ms_decode_gateup=ms[1], ms_decode_down=ms[2],
-                n_prefill=n[1], ms_prefill=ms[3], ms_prefill_gateup=ms[4], ms_prefill_down=ms[5])
+def moe_get_timing(ctx) -> dict:
+    """Records and summed milliseconds per decode kernel and prefill stage."""
+    t = moe_timing()
+    _check(lib.moe_get_timing(ctx, ctypes.byref(t)), "moe_get_timing")
+    return dict(n_decode=t.n_decode, n_prefill=t.n_prefill,
+                decode_ms=dict(zip(DECODE_KERNELS, list(t.decode_ms))),
+                prefill_ms=dict(zip(PREFILL_STAGES, list(t.prefill_ms))))
 
 
 def moe_probe_copy(d_src, d_dst, n_bytes: int, stream=None):

@@ -1,11 +1,13 @@
 // C-ABI entry points of libmoe: validation, memory ownership, cache state,
 // and the launch sequence of the decode forward.
 #include <algorithm>
+#include <cstdio>
 #include <cstring>
 #include <new>
 #include <numeric>
 #include <string>
 #include <thread>
+#include <type_traits>
 #include <vector>
 
 #include "moe_internal.h"
@@ -14,19 +16,24 @@ using namespace moe;
 
 namespace {
 
-thread_local std::string g_err;
+// The last error message of this thread, in a fixed buffer (reporting an
+// error allocates nothing).
+thread_local char g_err[512];
 
-moe_status fail(moe_status code, const std::string& msg) {
-  g_err = msg;
+moe_status fail(moe_status code, const char* msg) {
+  std::snprintf(g_err, sizeof g_err, "%s", msg);
   return code;
 }
+moe_status fail(moe_status code, const std::string& msg) { return fail(code, msg.c_str()); }
 
 #define HIPCHK(expr)                                                        \
   do {                                                                      \
     hipError_t _e = (expr);                                                 \
-    if (_e != hipSuccess)                                                   \
-      return fail(MOE_ERR_HIP, std::string(#expr) + ": " +                  \
-                                   hipGetErrorString(_e));                  \
+    if (_e != hipSuccess) {                                                 \
+      std::snprintf(g_err, sizeof g_err, "%s: %s", #expr,                   \
+                    hipGetErrorString(_e));                                 \
+      return MOE_ERR_HIP;                                                   \
+    }                                                                       \
   } while (0)
 
 #define ALLOC(ptr, bytes)                                                   \
@@ -57,13 +64,13 @@ void destroy_all(Ctx* c) {
   dfree(c->d_router); dfree(c->d_shared); dfree(c->d_slots); dfree(c->d_staging);
   dfree(c->d_key); dfree(c->d_stamp); dfree(c->d_order); dfree(c->d_order_tmp);
   dfree(c->d_hitflag); dfree(c->d_map); dfree(c->d_victim); dfree(c->d_cache);
-  dfree(c->d_logits); dfree(c->d_ids); dfree(c->d_gates);
-  dfree(c->d_counts); dfree(c->d_offsets); dfree(c->d_sorted); dfree(c->d_inv);
-  dfree(c->d_unique); dfree(c->d_slotcode); dfree(c->d_tok); dfree(c->d_items);
-  dfree(c->d_fills); dfree(c->d_meta); dfree(c->d_h); dfree(c->d_yperm);
+  dfree(c->d_scratch);
+  c->ds = DecodeScratch{};
   dfree(c->d_lookup_ids);
   for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
   c->ev_pool.clear();
+  if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
+  c->copy_stream = nullptr;
 }
 
 // Run fn(i) for i in [0, n) on up to `threads` host threads.
@@ -113,6 +120,39 @@ constexpr size_t kMaxTimingPairs = 65536;
 }  // namespace
 
 namespace moe {
+
+size_t decode_scratch_layout(const moe_config& f, int T, uint8_t* base, DecodeScratch* s) {
+  const int H = f.hidden, I = f.inter, E = f.n_experts, k = f.top_k;
+  DecodeScratch d;
+  d.T_cap = T;
+  d.max_unique = std::min(T * k, E);
+  d.max_items = d.max_unique + f.has_shared;
+  d.rows_cap = T * k + T;
+  d.lo_plane = (size_t)d.rows_cap * I;
+  size_t off = 0;
+  auto take = [&](auto*& ptr, size_t bytes) {
+    using P = std::remove_reference_t<decltype(ptr)>;
+    ptr = base ? reinterpret_cast<P>(base + off) : nullptr;
+    off += (bytes + 255) / 256 * 256;
+  };
+  take(d.logits, (size_t)T * E * 4);
+  take(d.ids, (size_t)T * k * 4);
+  take(d.gates, (size_t)T * k * 4);
+  take(d.counts, (size_t)E * 4);
+  take(d.offsets, (size_t)(E + 1) * 4);
+  take(d.sorted, (size_t)T * k * 4);
+  take(d.inv, (size_t)T * k * 4);
+  take(d.unique, (size_t)E * 4);
+  take(d.slotcode, (size_t)E * 4);
+  take(d.tok, (size_t)d.rows_cap * 4);
+  take(d.items, (size_t)d.max_items * sizeof(WorkItem));
+  take(d.fills, (size_t)d.max_unique * sizeof(FillEntry));
+  take(d.meta, sizeof(DevMeta));
+  take(d.h, (size_t)d.rows_cap * I * 2 * 2);  // hi and lo bf16 planes
+  take(d.yperm, (size_t)d.rows_cap * H * 4);
+  if (s) *s = d;
+  return off;
+}
 
 int fillable_slots(const Ctx* c, int layer, bool insert, int* slot0) {
   int first = 0, n = c->C;
@@ -213,10 +253,44 @@ static void repack_expert(const Ctx* c, const uint8_t* qg, const uint8_t* qu, co
 
 }  // namespace moe
 
+namespace {
+
+// The decode forward of one layer on the scratch s (T <= s.T_cap), all on
+// the caller's stream: router -> finalize (top-k, dispatch, cache lookup,
+// work list, fill list) -> copies of this call's misses from the pinned
+// pool (cache fills and bypasses) -> gate/up + SwiGLU -> down -> combine.
+moe_status decode_forward(Ctx* c, const DecodeScratch& s, int layer, const uint16_t* x, int T,
+                          const float* bias, uint16_t* y, float* y32, int32_t* ids,
+                          float* gates, hipStream_t st, bool allow_timing) {
+  const moe_config& f = c->cfg;
+  Ctx::TimingRec tr{};
+  const bool timed = allow_timing && c->timing && c->t_decode.size() < kMaxTimingPairs;
+  if (timed)
+    for (int i = 0; i < 2 * kDecodeStages; i++)
+      if (!(tr.ev[i] = timing_event(c))) return fail(MOE_ERR_HIP, "timing event");
+  auto t0 = [&](int stage) { return timed ? tr.ev[2 * stage] : nullptr; };
+  auto t1 = [&](int stage) { return timed ? tr.ev[2 * stage + 1] : nullptr; };
+  const float* wr = c->d_router + (size_t)layer * f.hidden * f.n_experts;
+  HIPCHK(launch_router(x, T, f.hidden, f.n_experts, wr, bias, s.logits, st, t0(kStRouter),
+                       t1(kStRouter)));
+  HIPCHK(launch_route_finalize(c, s, layer, T, ids, gates, st, t0(kStFinalize),
+                               t1(kStFinalize)));
+  HIPCHK(launch_fill(s.fills, s.meta, std::min(T * f.top_k, f.n_experts), c->rec_bytes, st,
+                     t0(kStFill), t1(kStFill)));
+  HIPCHK(launch_expert_gateup(c, s, x, T, st, t0(kStGateUp), t1(kStGateUp)));
+  HIPCHK(launch_expert_down(c, s, T, st, t0(kStDown), t1(kStDown)));
+  HIPCHK(launch_combine_rows(s.yperm, s.inv, s.gates, T, f.top_k, f.hidden, f.has_shared, y, y32,
+                             st, t0(kStCombine), t1(kStCombine)));
+  if (timed) c->t_decode.push_back(tr);
+  return MOE_OK;
+}
+
+}  // namespace
+
 // =========================================================================
 extern "C" {
 
-const char* moe_last_error(void) { return g_err.c_str(); }
+const char* moe_last_error(void) { return g_err; }
 
 size_t moe_expert_bytes(int32_t hidden, int32_t inter) {
   if (hidden <= 0 || inter <= 0) return 0;
@@ -270,9 +344,6 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   const int Tm = f.max_tokens;
   c->rec_bytes = expert_record_bytes(H, I, f.weight_format);
   c->stride = (c->rec_bytes + 255) / 256 * 256;
-  c->max_unique = std::min(Tm * k, E);
-  c->max_items = c->max_unique + f.has_shared;
-  c->rows_max = Tm * k + Tm;
   c->C = f.cache_slots;
   c->router_set.assign(L, 0);
   c->shared_set.assign(L, 0);
@@ -296,24 +367,20 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   ALLOC(c->d_order_tmp, (size_t)std::max(c->C, 1) * 4);
   ALLOC(c->d_hitflag, (size_t)std::max(c->C, 1));
   ALLOC(c->d_map, (size_t)L * E * 4);
-  ALLOC(c->d_victim, (size_t)c->max_unique * 4);
+  ALLOC(c->d_victim, (size_t)std::min(Tm * k, E) * 4);
   ALLOC(c->d_cache, sizeof(DevCache));
-  ALLOC(c->d_logits, (size_t)Tm * E * 4);
-  ALLOC(c->d_ids, (size_t)Tm * k * 4);
-  ALLOC(c->d_gates, (size_t)Tm * k * 4);
-  ALLOC(c->d_counts, (size_t)E * 4);
-  ALLOC(c->d_offsets, (size_t)(E + 1) * 4);
-  ALLOC(c->d_sorted, (size_t)Tm * k * 4);
-  ALLOC(c->d_inv, (size_t)Tm * k * 4);
-  ALLOC(c->d_unique, (size_t)E * 4);
-  ALLOC(c->d_slotcode, (size_t)E * 4);
-  ALLOC(c->d_tok, (size_t)c->rows_max * 4);
-  ALLOC(c->d_items, (size_t)c->max_items * sizeof(WorkItem));
-  ALLOC(c->d_fills, (size_t)c->max_unique * sizeof(FillEntry));
-  ALLOC(c->d_meta, sizeof(DevMeta));
-  ALLOC(c->d_h, (size_t)c->rows_max * I * 2 * 2);  // hi and lo bf16 planes
-  ALLOC(c->d_yperm, (size_t)c->rows_max * H * 4);
+  ALLOC(c->d_scratch, decode_scratch_layout(f, Tm, nullptr, nullptr));
+  decode_scratch_layout(f, Tm, c->d_scratch, &c->ds);
   ALLOC(c->d_lookup_ids, (size_t)(E + 1) * 4);
+  {
+    // default priority (the caller's streams are expected to use it too)
+    const hipError_t es = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking);
+    if (es != hipSuccess) {
+      destroy_all(c);
+      delete c;
+      return fail(MOE_ERR_HIP, std::string("copy stream: ") + hipGetErrorString(es));
+    }
+  }
 
   std::vector<int32_t> key(std::max(c->C, 1), -1), order(std::max(c->C, 1)), map((size_t)L * E, -1);
   std::iota(order.begin(), order.end(), 0);  // all empty: slot | (0 << kOrderKeyShift)
@@ -322,13 +389,13 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   if (upload(c->d_key, key) != hipSuccess || upload(c->d_order, order) != hipSuccess ||
       upload(c->d_stamp, stamp) != hipSuccess || upload(c->d_map, map) != hipSuccess ||
       hipMemcpy(c->d_cache, zero.data(), sizeof(DevCache), hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy(c->d_meta, zero.data(), sizeof(DevMeta), hipMemcpyHostToDevice) != hipSuccess) {
+      hipMemcpy(c->ds.meta, zero.data(), sizeof(DevMeta), hipMemcpyHostToDevice) != hipSuccess) {
     destroy_all(c);
     delete c;
     return fail(MOE_ERR_HIP, "initialising cache state");
   }
   *out = reinterpret_cast<moe_ctx*>(c);
-  g_err.clear();
+  g_err[0] = 0;
   return MOE_OK;
 }
 
@@ -415,11 +482,10 @@ moe_status moe_set_layer(moe_ctx* ctx, int32_t layer, const float* h_router,
   return MOE_OK;
 }
 
-moe_status moe_layer_forward(moe_ctx* ctx, int32_t layer, const void* d_x, int32_t T,
-                             const float* d_bias, void* d_y, float* d_y32, int32_t* d_ids,
-                             float* d_gates, void* stream) {
-  if (moe_status s = check_ctx(ctx)) return s;
-  Ctx* c = C_(ctx);
+// Checks shared by the two decode entry points (messages without
+// allocation).  Returns MOE_OK or the failure to report.
+static moe_status check_forward(Ctx* c, int32_t layer, const void* d_x, int32_t T,
+                                const void* d_y) {
   const moe_config& f = c->cfg;
   if (layer < 0 || layer >= f.n_layers) return fail(MOE_ERR_INVALID_ARG, "bad layer");
   if (T < 0 || T > f.max_tokens) return fail(MOE_ERR_INVALID_ARG, "T outside [0, max_tokens]");
@@ -430,25 +496,25 @@ moe_status moe_layer_forward(moe_ctx* ctx, int32_t layer, const void* d_x, int32
     return fail(MOE_ERR_STATE, "shared expert of this layer not set");
   const int worst_bypass =
       std::max(0, std::min(T * f.top_k, f.n_experts) - fillable_slots(c, layer, false, nullptr));
-  if (worst_bypass > f.staging_slots)
-    return fail(MOE_ERR_CAPACITY, "staging_slots (" + std::to_string(f.staging_slots) +
-                                      ") below worst-case bypass count " +
-                                      std::to_string(worst_bypass));
-  hipStream_t st = (hipStream_t)stream;
-  const float* wr = c->d_router + (size_t)layer * f.hidden * f.n_experts;
-  HIPCHK(launch_router((const uint16_t*)d_x, T, f.hidden, f.n_experts, wr, d_bias, c->d_logits,
-                       st));
-  HIPCHK(launch_route_finalize(c, layer, T, d_ids, d_gates, st));
-  HIPCHK(launch_fill(c->d_fills, c->d_meta, c->max_unique, c->rec_bytes, st));
-  Ctx::TimingRec tr{nullptr, nullptr, nullptr, nullptr};
-  if (c->timing && c->t_decode.size() < kMaxTimingPairs) {
-    tr = {timing_event(c), timing_event(c), timing_event(c), timing_event(c)};
-    if (!(tr.gu0 && tr.gu1 && tr.dn0 && tr.dn1)) tr = {nullptr, nullptr, nullptr, nullptr};
+  if (worst_bypass > f.staging_slots) {
+    std::snprintf(g_err, sizeof g_err, "staging_slots (%d) below worst-case bypass count %d",
+                  f.staging_slots, worst_bypass);
+    return MOE_ERR_CAPACITY;
   }
-  HIPCHK(launch_expert_gateup(c, (const uint16_t*)d_x, T, st, tr.gu0, tr.gu1));
-  HIPCHK(launch_expert_down(c, T, st, tr.dn0, tr.dn1));
-  if (tr.gu0) c->t_decode.push_back(tr);
-  HIPCHK(launch_combine(c, T, (uint16_t*)d_y, d_y32, st));
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward(moe_ctx* ctx, int32_t layer, const void* d_x, int32_t T,
+                             const float* d_bias, void* d_y, float* d_y32, int32_t* d_ids,
+                             float* d_gates, void* stream) {
+  if (moe_status s = check_ctx(ctx)) return s;
+  Ctx* c = C_(ctx);
+  if (moe_status s = check_forward(c, layer, d_x, T, d_y)) return s;
+  if (T == 0) return MOE_OK;
+  if (moe_status s = decode_forward(c, c->ds, layer, (const uint16_t*)d_x, T, d_bias,
+                                    (uint16_t*)d_y, d_y32, d_ids, d_gates, (hipStream_t)stream,
+                                    true))
+    return s;
   c->host_stats.forward_calls++;
   return MOE_OK;
 }
@@ -482,12 +548,12 @@ moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer, const int32_t* d_exp
   Ctx* c = C_(ctx);
   if (layer < 0 || layer >= c->cfg.n_layers || !d_experts || !d_n || !d_slot)
     return fail(MOE_ERR_INVALID_ARG, "bad layer or NULL pointer");
-  const int worst_bypass = std::max(0, c->max_unique - fillable_slots(c, layer, false, nullptr));
+  const int worst_bypass = std::max(0, c->ds.max_unique - fillable_slots(c, layer, false, nullptr));
   if (worst_bypass > c->cfg.staging_slots)
     return fail(MOE_ERR_CAPACITY, "staging_slots below worst-case bypass count");
   hipStream_t st = (hipStream_t)stream;
-  HIPCHK(launch_cache_lookup(c, layer, d_experts, d_n, c->max_unique, d_slot, false, st));
-  HIPCHK(launch_fill(c->d_fills, c->d_meta, c->max_unique, c->rec_bytes, st));
+  HIPCHK(launch_cache_lookup(c, layer, d_experts, d_n, c->ds.max_unique, d_slot, false, st));
+  HIPCHK(launch_fill(c->ds.fills, c->ds.meta, c->ds.max_unique, c->rec_bytes, st));
   return MOE_OK;
 }
 
@@ -495,7 +561,7 @@ moe_status expert_cache_fill(moe_ctx* ctx, int32_t layer, const int32_t* h_exper
                              int32_t n, void* stream) {
   if (moe_status s = check_ctx(ctx)) return s;
   Ctx* c = C_(ctx);
-  if (layer < 0 || layer >= c->cfg.n_layers || n < 0 || n > c->max_unique ||
+  if (layer < 0 || layer >= c->cfg.n_layers || n < 0 || n > c->ds.max_unique ||
       (n > 0 && !h_experts))
     return fail(MOE_ERR_INVALID_ARG, "bad layer, count or NULL list");
   for (int i = 0; i < n; i++) {
@@ -512,9 +578,9 @@ moe_status expert_cache_fill(moe_ctx* ctx, int32_t layer, const int32_t* h_exper
   buf.push_back(n);
   HIPCHK(hipStreamSynchronize(st));
   HIPCHK(hipMemcpy(c->d_lookup_ids, buf.data(), buf.size() * 4, hipMemcpyHostToDevice));
-  HIPCHK(launch_cache_lookup(c, layer, c->d_lookup_ids, c->d_lookup_ids + n, n, c->d_slotcode, true,
-                             st));
-  HIPCHK(launch_fill(c->d_fills, c->d_meta, n, c->rec_bytes, st));
+  HIPCHK(launch_cache_lookup(c, layer, c->d_lookup_ids, c->d_lookup_ids + n, n, c->ds.slotcode,
+                             true, st));
+  HIPCHK(launch_fill(c->ds.fills, c->ds.meta, n, c->rec_bytes, st));
   HIPCHK(hipStreamSynchronize(st));
   return MOE_OK;
 }
@@ -642,19 +708,20 @@ moe_status moe_inspect_dispatch(moe_ctx* ctx, int32_t* h_T, int32_t* h_counts,
   if (moe_status s = check_ctx(ctx)) return s;
   Ctx* c = C_(ctx);
   HIPCHK(hipDeviceSynchronize());
+  const DecodeScratch& d = c->ds;
   DevMeta m;
-  HIPCHK(hipMemcpy(&m, c->d_meta, sizeof m, hipMemcpyDeviceToHost));
+  HIPCHK(hipMemcpy(&m, d.meta, sizeof m, hipMemcpyDeviceToHost));
   const int E = c->cfg.n_experts, nk = m.T * c->cfg.top_k;
   if (h_T) *h_T = m.T;
   if (h_n_unique) *h_n_unique = m.n_unique;
-  if (h_counts) HIPCHK(hipMemcpy(h_counts, c->d_counts, (size_t)E * 4, hipMemcpyDeviceToHost));
-  if (h_offsets) HIPCHK(hipMemcpy(h_offsets, c->d_offsets, (size_t)(E + 1) * 4, hipMemcpyDeviceToHost));
-  if (h_sorted && nk) HIPCHK(hipMemcpy(h_sorted, c->d_sorted, (size_t)nk * 4, hipMemcpyDeviceToHost));
-  if (h_inv && nk) HIPCHK(hipMemcpy(h_inv, c->d_inv, (size_t)nk * 4, hipMemcpyDeviceToHost));
+  if (h_counts) HIPCHK(hipMemcpy(h_counts, d.counts, (size_t)E * 4, hipMemcpyDeviceToHost));
+  if (h_offsets) HIPCHK(hipMemcpy(h_offsets, d.offsets, (size_t)(E + 1) * 4, hipMemcpyDeviceToHost));
+  if (h_sorted && nk) HIPCHK(hipMemcpy(h_sorted, d.sorted, (size_t)nk * 4, hipMemcpyDeviceToHost));
+  if (h_inv && nk) HIPCHK(hipMemcpy(h_inv, d.inv, (size_t)nk * 4, hipMemcpyDeviceToHost));
   if (h_unique && m.n_unique)
-    HIPCHK(hipMemcpy(h_unique, c->d_unique, (size_t)m.n_unique * 4, hipMemcpyDeviceToHost));
+    HIPCHK(hipMemcpy(h_unique, d.unique, (size_t)m.n_unique * 4, hipMemcpyDeviceToHost));
   if (h_slot && m.n_unique)
-    HIPCHK(hipMemcpy(h_slot, c->d_slotcode, (size_t)m.n_unique * 4, hipMemcpyDeviceToHost));
+    HIPCHK(hipMemcpy(h_slot, d.slotcode, (size_t)m.n_unique * 4, hipMemcpyDeviceToHost));
   return MOE_OK;
 }
 
@@ -708,50 +775,52 @@ moe_status moe_set_timing(moe_ctx* ctx, int32_t enable) {
   return MOE_OK;
 }
 
-static hipError_t sum_timing(const std::vector<Ctx::TimingRec>& v, double* ms3) {
-  double s[3] = {0, 0, 0};
-  for (const auto& r : v) {
-    float a = 0, b = 0;
-    hipError_t e = hipEventElapsedTime(&a, r.gu0, r.gu1);
-    if (e == hipSuccess) e = hipEventElapsedTime(&b, r.dn0, r.dn1);
-    if (e != hipSuccess) return e;
-    s[0] += (double)a + b;
-    s[1] += a;
-    s[2] += b;
-  }
-  for (int i = 0; i < 3; i++) ms3[i] = s[i];
+// Stages that must have finished before a stage can start (-1 ends a
+// list).  A stage's time is its stop minus the latest of its own start and
+// its predecessors' stops, so that a dispatch-recorded start taken before
+// the kernel could run does not count.
+static const int kDecodePreds[kDecodeStages][3] = {
+    {-1, -1, -1}, {kStRouter, -1, -1}, {kStFinalize, -1, -1},
+    {kStFill, -1, -1}, {kStGateUp, -1, -1}, {kStDown, -1, -1}};
+static const int kPrefillPreds[kPrefillStages][3] = {
+    {-1, -1, -1}, {kPfRouting, -1, -1}, {kPfGateUp, -1, -1}, {kPfDown, -1, -1}};
+
+// Sum the stage times of the records into ms[0..stages).
+static hipError_t sum_timing(const std::vector<Ctx::TimingRec>& v, int stages,
+                             const int (*preds)[3], double* ms) {
+  for (int i = 0; i < stages; i++) ms[i] = 0.0;
+  for (const auto& r : v)
+    for (int i = 0; i < stages; i++) {
+      float t = 0;
+      hipError_t e = hipEventElapsedTime(&t, r.ev[2 * i], r.ev[2 * i + 1]);
+      for (int j = 0; j < 3 && e == hipSuccess && preds[i][j] >= 0; j++) {
+        float u = 0;
+        e = hipEventElapsedTime(&u, r.ev[2 * preds[i][j] + 1], r.ev[2 * i + 1]);
+        t = std::min(t, u);
+      }
+      if (e != hipSuccess) return e;
+      ms[i] += (double)std::max(t, 0.0f);
+    }
   return hipSuccess;
 }
 
-static moe_status take_timing(Ctx* c, int32_t* n2, double* ms6) {
+moe_status moe_get_timing(moe_ctx* ctx, moe_timing* out) {
+  if (moe_status s = check_ctx(ctx)) return s;
+  if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+  Ctx* c = C_(ctx);
   HIPCHK(hipDeviceSynchronize());
-  n2[0] = (int32_t)c->t_decode.size();
-  n2[1] = (int32_t)c->t_prefill.size();
-  HIPCHK(sum_timing(c->t_decode, ms6));
-  HIPCHK(sum_timing(c->t_prefill, ms6 + 3));
+  double d[kDecodeStages], p[kPrefillStages];
+  HIPCHK(sum_timing(c->t_decode, kDecodeStages, kDecodePreds, d));
+  HIPCHK(sum_timing(c->t_prefill, kPrefillStages, kPrefillPreds, p));
+  *out = moe_timing{};
+  out->n_decode = (int32_t)c->t_decode.size();
+  out->n_prefill = (int32_t)c->t_prefill.size();
+  for (int i = 0; i < kDecodeStages; i++) out->decode_ms[i] = d[i];
+  for (int i = 0; i < kPrefillStages; i++) out->prefill_ms[i] = p[i];
   c->t_decode.clear();
   c->t_prefill.clear();
   c->ev_next = 0;
   return MOE_OK;
-}
-
-moe_status moe_get_timing(moe_ctx* ctx, int32_t* h_n_decode, double* h_ms_decode,
-                          int32_t* h_n_prefill, double* h_ms_prefill) {
-  if (moe_status s = check_ctx(ctx)) return s;
-  int32_t n[2];
-  double ms[6];
-  if (moe_status s = take_timing(C_(ctx), n, ms)) return s;
-  if (h_n_decode) *h_n_decode = n[0];
-  if (h_n_prefill) *h_n_prefill = n[1];
-  if (h_ms_decode) *h_ms_decode = ms[0];
-  if (h_ms_prefill) *h_ms_prefill = ms[3];
-  return MOE_OK;
-}
-
-moe_status moe_get_timing_split(moe_ctx* ctx, int32_t* h_n, double* h_ms) {
-  if (moe_status s = check_ctx(ctx)) return s;
-  if (!h_n || !h_ms) return fail(MOE_ERR_INVALID_ARG, "NULL output array");
-  return take_timing(C_(ctx), h_n, h_ms);
 }
 
 moe_status moe_probe_copy(const void* d_src, void* d_dst, size_t n_bytes, void* stream) {

@@ -132,16 +132,16 @@ __device__ __forceinline__ void down_epilogue(const f32x4* red, int nw, const Wo
 // registers.
 template <int CPW>
 __global__ __launch_bounds__(1024) void gateup_decode_kernel(
-    const WorkItem* __restrict__ items, const DevMeta* __restrict__ meta,
+    const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items_p,
     const int32_t* __restrict__ tok, const uint16_t* __restrict__ x, uint32_t x_bytes, int H,
     int I, uint16_t* __restrict__ h, size_t lo_plane) {
   const int item = blockIdx.y;
   // Both loads at once (the grid covers the largest possible item count and
   // items[] has that many entries): one memory latency before the weight
-  // loads instead of two.  The exit test reads the whole item (a real item
-  // has cnt >= 1 and a weight pointer) so the compiler cannot sink the item
-  // load below it.
-  const int n_items = meta->n_items;
+  // loads instead of two.  The exit test reads the whole
+  // item (a real item has cnt >= 1 and a weight pointer) so the compiler
+  // cannot sink the item load below it.
+  const int n_items = *n_items_p;
   const WorkItem it = items[item];
   if ((item >= n_items) | (it.cnt < 1) | (it.w == nullptr)) return;
   const int p = blockIdx.x;
@@ -229,16 +229,16 @@ __global__ __launch_bounds__(1024) void gateup_decode_kernel(
 // h planes.
 template <int CPW>
 __global__ __launch_bounds__(1024) void down_decode_kernel(
-    const WorkItem* __restrict__ items, const DevMeta* __restrict__ meta,
+    const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items_p,
     const uint16_t* __restrict__ h, size_t lo_plane, int H, int I, size_t gateup_bytes,
     float* __restrict__ yperm) {
   const int item = blockIdx.y;
   // Both loads at once (the grid covers the largest possible item count and
   // items[] has that many entries): one memory latency before the weight
-  // loads instead of two.  The exit test reads the whole item (a real item
-  // has cnt >= 1 and a weight pointer) so the compiler cannot sink the item
-  // load below it.
-  const int n_items = meta->n_items;
+  // loads instead of two.  The exit test reads the whole
+  // item (a real item has cnt >= 1 and a weight pointer) so the compiler
+  // cannot sink the item load below it.
+  const int n_items = *n_items_p;
   const WorkItem it = items[item];
   if ((item >= n_items) | (it.cnt < 1) | (it.w == nullptr)) return;
   const int q = blockIdx.x;
@@ -364,7 +364,7 @@ struct WBf16 {
 // as above.
 template <int CPW, class W>
 __global__ __launch_bounds__(W::kMaxThreads) void gateup_stream_kernel(
-    const WorkItem* __restrict__ items, const DevMeta* __restrict__ meta,
+    const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items_p,
     const int32_t* __restrict__ tok, const uint16_t* __restrict__ x, uint32_t x_bytes, int H,
     int I, uint16_t* __restrict__ h, size_t lo_plane) {
   constexpr int S = CPW < W::kStep ? CPW : W::kStep;  // chunks per step
@@ -372,10 +372,10 @@ __global__ __launch_bounds__(W::kMaxThreads) void gateup_stream_kernel(
   const int item = blockIdx.y;
   // Both loads at once (the grid covers the largest possible item count and
   // items[] has that many entries): one memory latency before the weight
-  // loads instead of two.  The exit test reads the whole item (a real item
-  // has cnt >= 1 and a weight pointer) so the compiler cannot sink the item
-  // load below it.
-  const int n_items = meta->n_items;
+  // loads instead of two.  The exit test reads the whole
+  // item (a real item has cnt >= 1 and a weight pointer) so the compiler
+  // cannot sink the item load below it.
+  const int n_items = *n_items_p;
   const WorkItem it = items[item];
   if ((item >= n_items) | (it.cnt < 1) | (it.w == nullptr)) return;
   const int p = blockIdx.x;
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(W::kMaxThreads) void gateup_stream_kernel(
 
 template <int CPW, class W>
 __global__ __launch_bounds__(W::kMaxThreads) void down_stream_kernel(
-    const WorkItem* __restrict__ items, const DevMeta* __restrict__ meta,
+    const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items_p,
     const uint16_t* __restrict__ h, size_t lo_plane, int H, int I, size_t gateup_bytes,
     float* __restrict__ yperm) {
   constexpr int S = CPW < W::kStep ? CPW : W::kStep;
@@ -457,10 +457,10 @@ __global__ __launch_bounds__(W::kMaxThreads) void down_stream_kernel(
   const int item = blockIdx.y;
   // Both loads at once (the grid covers the largest possible item count and
   // items[] has that many entries): one memory latency before the weight
-  // loads instead of two.  The exit test reads the whole item (a real item
-  // has cnt >= 1 and a weight pointer) so the compiler cannot sink the item
-  // load below it.
-  const int n_items = meta->n_items;
+  // loads instead of two.  The exit test reads the whole
+  // item (a real item has cnt >= 1 and a weight pointer) so the compiler
+  // cannot sink the item load below it.
+  const int n_items = *n_items_p;
   const WorkItem it = items[item];
   if ((item >= n_items) | (it.cnt < 1) | (it.w == nullptr)) return;
   const int q = blockIdx.x;
@@ -613,14 +613,15 @@ int down_stream_cpw(int KC) {
 
 }  // namespace
 
+// Work-list rows of the launch grid: the most items a call of T tokens has.
 static int items_for(const Ctx* c, int T) {
   return std::min(T * c->cfg.top_k, c->cfg.n_experts) + c->cfg.has_shared;
 }
 
-hipError_t launch_expert_gateup(const Ctx* c, const uint16_t* x, int T, hipStream_t st,
-                                hipEvent_t ev0, hipEvent_t ev1) {
+hipError_t launch_expert_gateup(const Ctx* c, const DecodeScratch& s, const uint16_t* x, int T,
+                                hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   dim3 grid(c->cfg.inter / kAtomRows, items_for(c, T));
-  const size_t lo = (size_t)c->rows_max * c->cfg.inter;
+  const size_t lo = s.lo_plane;
   const int KC = c->cfg.hidden / kAtomK;
   const bool bf16 = c->cfg.weight_format == MOE_WEIGHTS_BF16;
   if (T <= kMaxStreamTokens) {
@@ -628,8 +629,8 @@ hipError_t launch_expert_gateup(const Ctx* c, const uint16_t* x, int T, hipStrea
     const int waves = stream_waves(KC, cpw);
 #define GATEUP_S(N, F)                                                                     \
   MOE_LAUNCH((gateup_stream_kernel<N, F>), grid, waves * 64, waves * 2 * 64 * 16, st, ev0, \
-             ev1, c->d_items, c->d_meta, c->d_tok, x, (uint32_t)T * c->cfg.hidden * 2,      \
-             c->cfg.hidden, c->cfg.inter, c->d_h, lo)
+             ev1, s.items, &s.meta->n_items, s.tok, x, (uint32_t)T * c->cfg.hidden * 2,          \
+             c->cfg.hidden, c->cfg.inter, s.h, lo)
 #define GATEUP_F(N) \
   if (bf16) GATEUP_S(N, WBf16); else GATEUP_S(N, WMxfp4);
     switch (cpw) {
@@ -644,12 +645,12 @@ hipError_t launch_expert_gateup(const Ctx* c, const uint16_t* x, int T, hipStrea
     return hipGetLastError();
   }
   if (bf16) return hipErrorNotSupported;  // bf16 contexts have max_tokens <= 16
-  const Split s = split_k(KC, grid.x * grid.y, 4);
-#define GATEUP(N)                                                                           \
-  MOE_LAUNCH(gateup_decode_kernel<N>, grid, s.waves * 64, s.waves * 2 * 64 * 16, st, ev0, ev1, \
-             c->d_items, c->d_meta, c->d_tok, x, (uint32_t)T * c->cfg.hidden * 2,            \
-             c->cfg.hidden, c->cfg.inter, c->d_h, lo)
-  switch (s.cpw) {
+  const Split sp = split_k(KC, grid.x * grid.y, 4);
+#define GATEUP(N)                                                                             \
+  MOE_LAUNCH(gateup_decode_kernel<N>, grid, sp.waves * 64, sp.waves * 2 * 64 * 16, st, ev0, ev1, \
+             s.items, &s.meta->n_items, s.tok, x, (uint32_t)T * c->cfg.hidden * 2, c->cfg.hidden,     \
+             c->cfg.inter, s.h, lo)
+  switch (sp.cpw) {
     case 1: GATEUP(1); break;
     case 2: GATEUP(2); break;
     case 3: GATEUP(3); break;
@@ -659,10 +660,10 @@ hipError_t launch_expert_gateup(const Ctx* c, const uint16_t* x, int T, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_expert_down(const Ctx* c, int T, hipStream_t st, hipEvent_t ev0,
-                              hipEvent_t ev1) {
+hipError_t launch_expert_down(const Ctx* c, const DecodeScratch& s, int T, hipStream_t st,
+                              hipEvent_t ev0, hipEvent_t ev1) {
   dim3 grid(c->cfg.hidden / (2 * kAtomRows), items_for(c, T));
-  const size_t lo = (size_t)c->rows_max * c->cfg.inter;
+  const size_t lo = s.lo_plane;
   const bool bf16 = c->cfg.weight_format == MOE_WEIGHTS_BF16;
   const size_t gub = gateup_section_bytes(c->cfg.hidden, c->cfg.inter, c->cfg.weight_format);
   const int KC = c->cfg.inter / kAtomK;
@@ -671,7 +672,7 @@ hipError_t launch_expert_down(const Ctx* c, int T, hipStream_t st, hipEvent_t ev
     const int waves = stream_waves(KC, cpw);
 #define DOWN_S(N, F)                                                                         \
   MOE_LAUNCH((down_stream_kernel<N, F>), grid, waves * 64, waves * 2 * 64 * 16, st, ev0, ev1, \
-             c->d_items, c->d_meta, c->d_h, lo, c->cfg.hidden, c->cfg.inter, gub, c->d_yperm)
+             s.items, &s.meta->n_items, s.h, lo, c->cfg.hidden, c->cfg.inter, gub, s.yperm)
 #define DOWN_F(N) \
   if (bf16) DOWN_S(N, WBf16); else DOWN_S(N, WMxfp4);
     switch (cpw) {
@@ -686,11 +687,11 @@ hipError_t launch_expert_down(const Ctx* c, int T, hipStream_t st, hipEvent_t ev
     return hipGetLastError();
   }
   if (bf16) return hipErrorNotSupported;  // bf16 contexts have max_tokens <= 16
-  const Split s = split_k(KC, grid.x * grid.y, 4);
-#define DOWN(N)                                                                           \
-  MOE_LAUNCH(down_decode_kernel<N>, grid, s.waves * 64, s.waves * 2 * 64 * 16, st, ev0, ev1, \
-             c->d_items, c->d_meta, c->d_h, lo, c->cfg.hidden, c->cfg.inter, gub, c->d_yperm)
-  switch (s.cpw) {
+  const Split sp = split_k(KC, grid.x * grid.y, 4);
+#define DOWN(N)                                                                             \
+  MOE_LAUNCH(down_decode_kernel<N>, grid, sp.waves * 64, sp.waves * 2 * 64 * 16, st, ev0, ev1, \
+             s.items, &s.meta->n_items, s.h, lo, c->cfg.hidden, c->cfg.inter, gub, s.yperm)
+  switch (sp.cpw) {
     case 1: DOWN(1); break;
     case 2: DOWN(2); break;
     case 3: DOWN(3); break;
@@ -702,15 +703,11 @@ hipError_t launch_expert_down(const Ctx* c, int T, hipStream_t st, hipEvent_t ev
 
 hipError_t launch_combine_rows(const float* yperm, const int32_t* inv, const float* gates, int T,
                                int k, int H, int has_shared, uint16_t* y, float* y32,
-                               hipStream_t st) {
+                               hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   dim3 grid((H / 4 + 255) / 256, T);
-  combine_kernel<<<grid, 256, 0, st>>>(yperm, inv, gates, T, k, H, has_shared, y, y32);
+  MOE_LAUNCH(combine_kernel, grid, 256, 0, st, ev0, ev1, yperm, inv, gates, T, k, H, has_shared,
+             y, y32);
   return hipGetLastError();
-}
-
-hipError_t launch_combine(const Ctx* c, int T, uint16_t* y, float* y32, hipStream_t st) {
-  return launch_combine_rows(c->d_yperm, c->d_inv, c->d_gates, T, c->cfg.top_k, c->cfg.hidden,
-                             c->cfg.has_shared, y, y32, st);
 }
 
 }  // namespace moe

@@ -58,9 +58,9 @@ constexpr int kFillBlocks = 256;
 }  // namespace
 
 hipError_t launch_fill(const FillEntry* fills, const DevMeta* meta, int max_fill, size_t bytes,
-                       hipStream_t st) {
+                       hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (max_fill <= 0) return hipSuccess;
-  fill_kernel<<<kFillBlocks, 256, 0, st>>>(fills, meta, max_fill, bytes / 16);
+  MOE_LAUNCH(fill_kernel, kFillBlocks, 256, 0, st, ev0, ev1, fills, meta, max_fill, bytes / 16);
   return hipGetLastError();
 }
 

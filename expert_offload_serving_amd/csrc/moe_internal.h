@@ -74,12 +74,42 @@ struct FillEntry {         // one host-pool -> HBM expert copy
 struct DevMeta {
   int32_t T;
   int32_t n_unique;
-  int32_t n_items;
-  int32_t n_fill;
+  int32_t n_items;         // work-list entries: unique experts + shared
+  int32_t n_fill;          // copies issued (cache fills + bypasses)
   int32_t n_hit;
   int32_t n_bypass;
   int32_t pad[2];
 };
+
+// Per-call device arrays of the decode forward, carved out of one buffer
+// (decode_scratch_layout): the context's own, sized at create for
+// max_tokens, or a caller-independent static one.
+struct DecodeScratch {
+  int T_cap = 0;             // tokens the layout was sized for
+  int max_unique = 0;        // min(T_cap * k, E)
+  int max_items = 0;         // max_unique + has_shared
+  int rows_cap = 0;          // T_cap * k + T_cap (shared rows)
+  size_t lo_plane = 0;       // elements from h's hi plane to its lo plane
+  float* logits = nullptr;   // [T_cap][E]
+  int32_t* ids = nullptr;    // [T_cap*k]
+  float* gates = nullptr;    // [T_cap*k]
+  int32_t* counts = nullptr;   // [E]
+  int32_t* offsets = nullptr;  // [E+1]
+  int32_t* sorted = nullptr;   // [T_cap*k]
+  int32_t* inv = nullptr;      // [T_cap*k]
+  int32_t* unique = nullptr;   // [E]
+  int32_t* slotcode = nullptr; // [E]
+  int32_t* tok = nullptr;      // [rows_cap] token of each permuted row
+  WorkItem* items = nullptr;   // [max_items]
+  FillEntry* fills = nullptr;  // [max_unique]
+  DevMeta* meta = nullptr;
+  uint16_t* h = nullptr;       // bf16 [2][rows_cap][I]: hi, lo planes
+  float* yperm = nullptr;      // [rows_cap][H]
+};
+
+// Bytes of a decode scratch for T tokens; with base != NULL the arrays of
+// *s are laid out from base (256-byte aligned pieces).
+size_t decode_scratch_layout(const moe_config& f, int T, uint8_t* base, DecodeScratch* s);
 
 // Cache state and statistics on the device.
 struct DevCache {
@@ -120,9 +150,6 @@ struct Ctx {
   int device = 0;
   size_t rec_bytes = 0;     // 3*H*I*17/32
   size_t stride = 0;        // record stride (256-byte multiple)
-  int max_unique = 0;       // min(T_max*k, E)
-  int max_items = 0;        // max_unique + has_shared
-  int rows_max = 0;         // T_max*k + T_max (shared rows)
 
   // host pool and HBM weights
   uint8_t* pool = nullptr;          // pinned, [L][E] records
@@ -144,39 +171,28 @@ struct Ctx {
   int32_t* d_victim = nullptr;
   DevCache* d_cache = nullptr;
 
-  // decode scratch
-  float* d_logits = nullptr;        // [T_max][E]
-  int32_t* d_ids = nullptr;         // [T_max*k]
-  float* d_gates = nullptr;         // [T_max*k]
-  int32_t* d_counts = nullptr;      // [E]
-  int32_t* d_offsets = nullptr;     // [E+1]
-  int32_t* d_sorted = nullptr;      // [T_max*k]
-  int32_t* d_inv = nullptr;         // [T_max*k]
-  int32_t* d_unique = nullptr;      // [E]
-  int32_t* d_slotcode = nullptr;    // [E]
-  int32_t* d_tok = nullptr;         // [rows_max] token of each permuted row
-  WorkItem* d_items = nullptr;      // [max_items]
-  FillEntry* d_fills = nullptr;     // [max_unique]
-  DevMeta* d_meta = nullptr;
-  uint16_t* d_h = nullptr;          // bf16 [2][rows_max][I]: hi, lo planes
-  float* d_yperm = nullptr;         // [rows_max][H]
+  // decode scratch (one allocation, sized for max_tokens)
+  uint8_t* d_scratch = nullptr;
+  DecodeScratch ds;
   int32_t* d_lookup_ids = nullptr;  // [E] for expert_cache_fill
+
+  // internal copy stream of the prefill layer uploads, joined to the
+  // caller's stream by events
+  hipStream_t copy_stream = nullptr;
 
   // prefill (allocated on first use)
   int Tp_max = 0;
   uint8_t* d_layerbuf[2] = {nullptr, nullptr};
-  hipStream_t copy_stream = nullptr;
   hipEvent_t ev_upload[2] = {nullptr, nullptr};
   hipEvent_t ev_compute[2] = {nullptr, nullptr};
   struct Prefill* pf = nullptr;
 
-  // timing
+  // timing: start and stop events of each stage, recorded by the kernel
+  // dispatches themselves
   bool timing = false;
   std::vector<hipEvent_t> ev_pool;  // reused
-  // start and stop of the gate/up and the down kernel, recorded by the
-  // dispatches themselves
   struct TimingRec {
-    hipEvent_t gu0, gu1, dn0, dn1;
+    hipEvent_t ev[2 * 8];
   };
   std::vector<TimingRec> t_decode, t_prefill;
   size_t ev_next = 0;
@@ -186,41 +202,50 @@ struct Ctx {
 };
 
 // ---------------------------------------------------------------------------
-// Launchers (each enqueues on `st` and returns hipGetLastError()).
+// Launchers (each enqueues on `st` and returns hipGetLastError()).  Every
+// launcher takes optional start and stop events (either may be NULL): when
+// one is given, the kernel is launched with hipExtLaunchKernel, which
+// records them as part of the dispatch, so that their interval is the
+// kernel's own duration.
 // ---------------------------------------------------------------------------
 hipError_t launch_router(const uint16_t* x, int T, int H, int E, const float* w_router_t,
-                         const float* bias, float* logits, hipStream_t st);
-hipError_t launch_route_finalize(Ctx* c, int layer, int T, int32_t* user_ids,
-                                 float* user_gates, hipStream_t st);
+                         const float* bias, float* logits, hipStream_t st,
+                         hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+hipError_t launch_route_finalize(Ctx* c, const DecodeScratch& s, int layer, int T,
+                                 int32_t* user_ids, float* user_gates, hipStream_t st,
+                                 hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_cache_lookup(Ctx* c, int layer, const int32_t* d_experts,
                                const int32_t* d_n, int n_max, int32_t* d_slot, bool insert,
                                hipStream_t st);
 hipError_t launch_fill(const FillEntry* fills, const DevMeta* meta, int max_fill,
-                       size_t bytes, hipStream_t st);
+                       size_t bytes, hipStream_t st, hipEvent_t ev0 = nullptr,
+                       hipEvent_t ev1 = nullptr);
 hipError_t launch_copy_pairs(const FillEntry* pairs, int n, size_t bytes,
                              hipStream_t st);
 hipError_t launch_probe_copy(const void* src, void* dst, size_t n_bytes,
                              hipStream_t st);
-// The expert launchers take optional start and stop events: when given, the
-// kernel is launched with hipExtLaunchKernel, which records them as part of
-// the dispatch, so that their interval is the kernel's own duration.
-hipError_t launch_expert_gateup(const Ctx* c, const uint16_t* x, int T, hipStream_t st,
-                                hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
-hipError_t launch_expert_down(const Ctx* c, int T, hipStream_t st, hipEvent_t ev0 = nullptr,
-                              hipEvent_t ev1 = nullptr);
-hipError_t launch_combine(const Ctx* c, int T, uint16_t* y, float* y32, hipStream_t st);
+hipError_t launch_expert_gateup(const Ctx* c, const DecodeScratch& s, const uint16_t* x, int T,
+                                hipStream_t st, hipEvent_t ev0 = nullptr,
+                                hipEvent_t ev1 = nullptr);
+hipError_t launch_expert_down(const Ctx* c, const DecodeScratch& s, int T, hipStream_t st,
+                              hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_combine_rows(const float* yperm, const int32_t* inv, const float* gates, int T,
                                int k, int H, int has_shared, uint16_t* y, float* y32,
-                               hipStream_t st);
+                               hipStream_t st, hipEvent_t ev0 = nullptr,
+                               hipEvent_t ev1 = nullptr);
 
 // Next event of the context's timing pool (created on demand; NULL on failure).
 hipEvent_t timing_event(Ctx* c);
 
+// Stages timed per decode call and per prefill layer.
+enum DecodeStage { kStRouter, kStFinalize, kStFill, kStGateUp, kStDown, kStCombine, kDecodeStages };
+enum PrefillStage { kPfRouting, kPfGateUp, kPfDown, kPfCombine, kPrefillStages };
+
 // kernel<<<grid, block, shm, st>>>(args...), or with start and stop events
-// recorded by the dispatch itself when ev0 is given.
+// recorded by the dispatch itself when either is given.
 #define MOE_LAUNCH(KERNEL, GRID, BLOCK, SHM, ST, EV0, EV1, ...)                          \
   do {                                                                                  \
-    if (EV0)                                                                            \
+    if ((EV0) || (EV1))                                                                 \
       hipExtLaunchKernelGGL(KERNEL, dim3(GRID), dim3(BLOCK), (uint32_t)(SHM), ST, EV0, EV1, \
                             0u, __VA_ARGS__);                                           \
     else                                                                                \

@@ -876,7 +876,6 @@ hipError_t prefill_alloc(Ctx* c) {
   const size_t layer_bytes = (size_t)E * c->stride;
   for (int b = 0; b < 2; b++)
     if ((e = hipMalloc((void**)&c->d_layerbuf[b], layer_bytes)) != hipSuccess) return e;
-  if ((e = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking)) != hipSuccess) return e;
   for (int b = 0; b < 2; b++) {
     if ((e = hipEventCreateWithFlags(&c->ev_upload[b], hipEventDisableTiming)) != hipSuccess) return e;
     if ((e = hipEventCreateWithFlags(&c->ev_compute[b], hipEventDisableTiming)) != hipSuccess) return e;
@@ -887,7 +886,6 @@ hipError_t prefill_alloc(Ctx* c) {
 }  // namespace
 
 void prefill_free(Ctx* c) {
-  if (c->copy_stream) (void)hipStreamSynchronize(c->copy_stream);
   if (Prefill* p = c->pf) {
     void* ptrs[] = {p->logits, p->ids, p->gates, p->chunk_cnt, p->counts, p->offsets, p->sorted,
                     p->inv, p->tok, p->tiles, p->n_tiles, p->h, p->hlo, p->yperm};
@@ -903,8 +901,6 @@ void prefill_free(Ctx* c) {
     if (c->ev_compute[b]) (void)hipEventDestroy(c->ev_compute[b]);
     c->ev_upload[b] = c->ev_compute[b] = nullptr;
   }
-  if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
-  c->copy_stream = nullptr;
 }
 
 int prefill_layers_run(const Ctx* c) { return c->pf ? c->pf->last_layers : 0; }
@@ -980,8 +976,16 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
     int32_t* inv = p->inv + l * per;
     int32_t* counts = p->counts + (size_t)l * (E + 1);
     int32_t* offsets = p->offsets + (size_t)l * (E + 1);
-    router_prefill_kernel<<<dim3((T + 63) / 64, (E + 63) / 64), 256, 0, st>>>(x, T, H, E, wrt,
-                                                                              bias, p->logits);
+    Ctx::TimingRec tr{};
+    const bool timed = c->timing && c->t_prefill.size() < 65536;
+    if (timed)
+      for (int i = 0; i < 2 * kPrefillStages; i++)
+        if (!(tr.ev[i] = timing_event(c))) return hipErrorOutOfMemory;
+    auto t0 = [&](int stage) { return timed ? tr.ev[2 * stage] : nullptr; };
+    auto t1 = [&](int stage) { return timed ? tr.ev[2 * stage + 1] : nullptr; };
+    // the routing stage runs from the router's start to the dispatch's end
+    MOE_LAUNCH(router_prefill_kernel, dim3((T + 63) / 64, (E + 63) / 64), 256, 0, st,
+               t0(kPfRouting), nullptr, x, T, H, E, wrt, bias, p->logits);
     const TopkArgs ta{E, k, f.renormalize, p->logits, ids, gates, nullptr, nullptr};
     const int nk = (E + 63) / 64, tb = (T + 15) / 16;
     if (nk <= 1) topk_prefill_kernel<1><<<tb, 1024, 0, st>>>(ta, T);
@@ -990,30 +994,27 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
     else if (nk <= 8) topk_prefill_kernel<8><<<tb, 1024, 0, st>>>(ta, T);
     else topk_prefill_kernel<16><<<tb, 1024, 0, st>>>(ta, T);
     dispatch_count_kernel<<<nchunk, 256, 0, st>>>(ids, T, k, E, p->chunk_cnt);
-    dispatch_place_kernel<<<nchunk, 1024, 0, st>>>(ids, T, k, E, f.has_shared, nchunk,
-                                                   p->chunk_cnt, counts, offsets, sorted, inv,
-                                                   p->tok, p->tiles, p->n_tiles);
+    MOE_LAUNCH(dispatch_place_kernel, nchunk, 1024, 0, st, nullptr, t1(kPfRouting), ids, T, k, E,
+               f.has_shared, nchunk, p->chunk_cnt, counts, offsets, sorted, inv, p->tok, p->tiles,
+               p->n_tiles);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     GroupArgs ga{p->tiles, p->n_tiles, counts, offsets, p->tok, c->d_layerbuf[b],
                  c->stride, f.has_shared ? c->d_shared + (size_t)l * c->stride : nullptr, E};
-    Ctx::TimingRec tr{nullptr, nullptr, nullptr, nullptr};
-    if (c->timing && c->t_prefill.size() < 65536) {
-      tr = {timing_event(c), timing_event(c), timing_event(c), timing_event(c)};
-      if (!(tr.gu0 && tr.gu1 && tr.dn0 && tr.dn1)) tr = {nullptr, nullptr, nullptr, nullptr};
-    }
     const int nbn_gu = (2 * I + 511) / 512, nbn_dn = (H + 511) / 512;
     const size_t hhi_bytes = (size_t)p->Tmax * (k + 1) * I * 2;
     const size_t hlo_bytes = prefill_lo_bytes(p->Tmax, k, E, I);
-    MOE_LAUNCH(gateup_prefill_kernel, p->max_tiles * nbn_gu, 64 * kGemmWaves, 0, st, tr.gu0,
-               tr.gu1, ga, x, (uint32_t)T * H * 2, H, I, nbn_gu, p->h, p->hlo);
-    MOE_LAUNCH(down_prefill_kernel, p->max_tiles * nbn_dn, 64 * kGemmWaves, 0, st, tr.dn0,
-               tr.dn1, ga, p->h, (uint32_t)hhi_bytes, p->hlo, (uint32_t)hlo_bytes, H, I,
+    MOE_LAUNCH(gateup_prefill_kernel, p->max_tiles * nbn_gu, 64 * kGemmWaves, 0, st,
+               t0(kPfGateUp), t1(kPfGateUp), ga, x, (uint32_t)T * H * 2, H, I, nbn_gu, p->h,
+               p->hlo);
+    MOE_LAUNCH(down_prefill_kernel, p->max_tiles * nbn_dn, 64 * kGemmWaves, 0, st, t0(kPfDown),
+               t1(kPfDown), ga, p->h, (uint32_t)hhi_bytes, p->hlo, (uint32_t)hlo_bytes, H, I,
                nbn_dn, gateup_section_bytes(H, I), p->yperm);
-    if (tr.gu0) c->t_prefill.push_back(tr);
     if ((e = launch_combine_rows(p->yperm, inv, gates, T, k, H, f.has_shared,
-                                 (uint16_t*)ys[l], y32s ? y32s[l] : nullptr, st)) != hipSuccess)
+                                 (uint16_t*)ys[l], y32s ? y32s[l] : nullptr, st, t0(kPfCombine),
+                                 t1(kPfCombine))) != hipSuccess)
       return e;
+    if (timed) c->t_prefill.push_back(tr);
     if ((e = hipEventRecord(c->ev_compute[b], st)) != hipSuccess) return e;
   }
   return hipGetLastError();

@@ -353,7 +353,7 @@ __global__ __launch_bounds__(kFinalizeThreads) void cache_lookup_kernel(
   for (int u = threadIdx.x; u < n; u += blockDim.x) out_slot[u] = s_slot[u];
 }
 
-LookupArgs make_lookup_args(Ctx* c, int layer, bool insert) {
+LookupArgs make_lookup_args(Ctx* c, int layer, bool insert, FillEntry* fills, DevMeta* meta) {
   LookupArgs la;
   la.layer = layer;
   la.E = c->cfg.n_experts;
@@ -375,26 +375,31 @@ LookupArgs make_lookup_args(Ctx* c, int layer, bool insert) {
   la.slots = c->d_slots;
   la.staging_buf = c->d_staging;
   la.stride = c->stride;
-  la.fills = c->d_fills;
-  la.meta = c->d_meta;
+  la.fills = fills;
+  la.meta = meta;
   return la;
 }
 
 }  // namespace
 
 hipError_t launch_router(const uint16_t* x, int T, int H, int E, const float* wrt,
-                         const float* bias, float* logits, hipStream_t st) {
+                         const float* bias, float* logits, hipStream_t st, hipEvent_t ev0,
+                         hipEvent_t ev1) {
   if (T <= 1)
-    router_kernel<1><<<E, kRouterWaves * 64, 0, st>>>(x, T, H, E, wrt, bias, logits);
+    MOE_LAUNCH(router_kernel<1>, E, kRouterWaves * 64, 0, st, ev0, ev1, x, T, H, E, wrt, bias,
+               logits);
   else if (T <= 4)
-    router_kernel<4><<<E, kRouterWaves * 64, 0, st>>>(x, T, H, E, wrt, bias, logits);
+    MOE_LAUNCH(router_kernel<4>, E, kRouterWaves * 64, 0, st, ev0, ev1, x, T, H, E, wrt, bias,
+               logits);
   else
-    router_kernel<kRouterTG><<<E, kRouterWaves * 64, 0, st>>>(x, T, H, E, wrt, bias, logits);
+    MOE_LAUNCH(router_kernel<kRouterTG>, E, kRouterWaves * 64, 0, st, ev0, ev1, x, T, H, E, wrt,
+               bias, logits);
   return hipGetLastError();
 }
 
-hipError_t launch_route_finalize(Ctx* c, int layer, int T, int32_t* user_ids,
-                                 float* user_gates, hipStream_t st) {
+hipError_t launch_route_finalize(Ctx* c, const DecodeScratch& s, int layer, int T,
+                                 int32_t* user_ids, float* user_gates, hipStream_t st,
+                                 hipEvent_t ev0, hipEvent_t ev1) {
   FinalizeArgs a;
   a.T = T;
   a.H = c->cfg.hidden;
@@ -402,39 +407,39 @@ hipError_t launch_route_finalize(Ctx* c, int layer, int T, int32_t* user_ids,
   a.k = c->cfg.top_k;
   a.renorm = c->cfg.renormalize;
   a.has_shared = c->cfg.has_shared;
-  a.logits = c->d_logits;
-  a.ids = c->d_ids;
-  a.gates = c->d_gates;
+  a.logits = s.logits;
+  a.ids = s.ids;
+  a.gates = s.gates;
   a.user_ids = user_ids;
   a.user_gates = user_gates;
-  a.counts = c->d_counts;
-  a.offsets = c->d_offsets;
-  a.sorted = c->d_sorted;
-  a.inv = c->d_inv;
-  a.unique = c->d_unique;
-  a.slotcode = c->d_slotcode;
-  a.tok = c->d_tok;
-  a.items = c->d_items;
+  a.counts = s.counts;
+  a.offsets = s.offsets;
+  a.sorted = s.sorted;
+  a.inv = s.inv;
+  a.unique = s.unique;
+  a.slotcode = s.slotcode;
+  a.tok = s.tok;
+  a.items = s.items;
   a.shared_w = c->cfg.has_shared ? c->d_shared + (size_t)layer * c->stride : nullptr;
-  a.la = make_lookup_args(c, layer, false);
+  a.la = make_lookup_args(c, layer, false, s.fills, s.meta);
   const int nk = (a.E + 63) / 64;
   if (nk <= 1)
-    route_finalize_kernel<1><<<1, kFinalizeThreads, 0, st>>>(a);
+    MOE_LAUNCH(route_finalize_kernel<1>, 1, kFinalizeThreads, 0, st, ev0, ev1, a);
   else if (nk <= 2)
-    route_finalize_kernel<2><<<1, kFinalizeThreads, 0, st>>>(a);
+    MOE_LAUNCH(route_finalize_kernel<2>, 1, kFinalizeThreads, 0, st, ev0, ev1, a);
   else if (nk <= 4)
-    route_finalize_kernel<4><<<1, kFinalizeThreads, 0, st>>>(a);
+    MOE_LAUNCH(route_finalize_kernel<4>, 1, kFinalizeThreads, 0, st, ev0, ev1, a);
   else if (nk <= 8)
-    route_finalize_kernel<8><<<1, kFinalizeThreads, 0, st>>>(a);
+    MOE_LAUNCH(route_finalize_kernel<8>, 1, kFinalizeThreads, 0, st, ev0, ev1, a);
   else
-    route_finalize_kernel<16><<<1, kFinalizeThreads, 0, st>>>(a);
+    MOE_LAUNCH(route_finalize_kernel<16>, 1, kFinalizeThreads, 0, st, ev0, ev1, a);
   return hipGetLastError();
 }
 
 hipError_t launch_cache_lookup(Ctx* c, int layer, const int32_t* d_experts, const int32_t* d_n,
                                int n_max, int32_t* d_slot, bool insert, hipStream_t st) {
-  cache_lookup_kernel<<<1, kFinalizeThreads, 0, st>>>(make_lookup_args(c, layer, insert),
-                                                      d_experts, d_n, n_max, d_slot);
+  cache_lookup_kernel<<<1, kFinalizeThreads, 0, st>>>(
+      make_lookup_args(c, layer, insert, c->ds.fills, c->ds.meta), d_experts, d_n, n_max, d_slot);
   return hipGetLastError();
 }
 

@@ -179,9 +179,9 @@ class MoEEngine:
         b.moe_set_timing(self.ctx, enable)
 
     def get_timing(self) -> dict:
-        """Summed event times (ms) since the last call, in total and per
-        expert kernel (gate/up, down), for decode calls and prefill layers."""
-        return b.moe_get_timing_split(self.ctx)
+        """Summed kernel times (ms) since the last call, per decode kernel
+        and per prefill stage, with the record counts."""
+        return b.moe_get_timing(self.ctx)
 
     def close(self):
         if self.ctx:

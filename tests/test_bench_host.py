@@ -65,3 +65,27 @@ def test_profile_fields_follow_the_source_hash(tmp_path, monkeypatch):
     assert bench.traffic_from_profile("k", "w") is None
     assert bench.traffic_from_profile("other", "w") is None  # no such summary
     assert bench.mfma_busy_from_profile() is None
+
+
+def test_layer_bytes_adds_router_and_combine():
+    """The layer's bytes are the expert kernels' plus the router (W_r once
+    per call, token rows, bias, logits) and the combine (every fp32 expert
+    row read once, y written in bf16)."""
+    sh = gen.Shape(H=256, I=512, E=8, k=2, shared=True)
+    lookups, calls, pairs, T_total = 7, 3, 12, 6
+    gu, dn = bench.kernel_bytes(sh, lookups, calls, pairs, T_total)
+    rows = pairs + T_total
+    router = calls * sh.H * sh.E * 4 + T_total * (sh.H * 2 + 2 * sh.E * 4)
+    combine = rows * sh.H * 4 + T_total * sh.H * 2
+    assert bench.layer_bytes(sh, lookups, calls, pairs, T_total) == gu + dn + router + combine
+    no_bias = bench.layer_bytes(sh, lookups, calls, pairs, T_total, bias=False)
+    assert no_bias == gu + dn + router + combine - T_total * sh.E * 4
+
+
+def test_check_pairs_lie_in_the_timed_steps():
+    wl = gen.WORKLOADS["glm_decode"]
+    for W, K, n in ((5, 20, 4), (0, 1024, 4), (3, 1, 4), (0, 7, 1)):
+        pairs = bench.check_pairs_of(wl, W, K, n)
+        assert pairs and all(W <= s < W + K and 0 <= l < wl.shape.layers for s, l in pairs)
+        assert (W + K - 1) in {s for s, _ in pairs}
+    assert bench.check_pairs_of(wl, 5, 20, 0) == []

@@ -64,6 +64,7 @@ _SIGS = {
     "moe_set_expert": (_I32, [_P, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "moe_set_layer": (_I32, [_P, _I32, _P, _P, _P, _P, _P]),
     "moe_layer_forward": (_I32, [_P, _I32, _P, _I32, _P, _P, _P, _P, _P, _P]),
+    "moe_layer_forward_noalloc": (_I32, [_P, _I32, _P, _I32, _P, _P, _P, _P, _P, _P]),
     "moe_prefill_forward": (_I32, [_P, _I32, _P, _I32, _P, _P, _P, _P]),
     "expert_cache_lookup": (_I32, [_P, _I32, _P, _P, _P, _P]),
     "expert_cache_fill": (_I32, [_P, _I32, _P, _I32, _P]),
@@ -168,6 +169,13 @@ def moe_layer_forward(ctx, layer, d_x, T, d_bias, d_y, d_y32=None, d_ids=None, d
                       stream=None):
     _check(lib.moe_layer_forward(ctx, layer, _ptr(d_x), T, _ptr(d_bias), _ptr(d_y), _ptr(d_y32),
                                  _ptr(d_ids), _ptr(d_gates), _stream(stream)), "moe_layer_forward")
+
+
+def moe_layer_forward_noalloc(ctx, layer, d_x, T, d_bias, d_y, d_y32=None, d_ids=None,
+                              d_gates=None, stream=None):
+    _check(lib.moe_layer_forward_noalloc(ctx, layer, _ptr(d_x), T, _ptr(d_bias), _ptr(d_y),
+                                         _ptr(d_y32), _ptr(d_ids), _ptr(d_gates),
+                                         _stream(stream)), "moe_layer_forward_noalloc")
 
 
 def moe_prefill_forward(ctx, n_layers, d_xs: Sequence, T, d_biases, d_ys: Sequence,

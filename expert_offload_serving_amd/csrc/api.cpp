@@ -394,6 +394,14 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     delete c;
     return fail(MOE_ERR_HIP, "initialising cache state");
   }
+  {
+    const hipError_t es = static_scratch_address(c->device, &c->static_scratch);
+    if (es != hipSuccess) {
+      destroy_all(c);
+      delete c;
+      return fail(MOE_ERR_HIP, std::string("device scratch address: ") + hipGetErrorString(es));
+    }
+  }
   *out = reinterpret_cast<moe_ctx*>(c);
   g_err[0] = 0;
   return MOE_OK;
@@ -515,6 +523,30 @@ moe_status moe_layer_forward(moe_ctx* ctx, int32_t layer, const void* d_x, int32
                                     (uint16_t*)d_y, d_y32, d_ids, d_gates, (hipStream_t)stream,
                                     true))
     return s;
+  c->host_stats.forward_calls++;
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward_noalloc(moe_ctx* ctx, int32_t layer, const void* d_x, int32_t T,
+                                     const float* d_bias, void* d_y, float* d_y32,
+                                     int32_t* d_ids, float* d_gates, void* stream) {
+  if (moe_status s = check_ctx(ctx)) return s;
+  Ctx* c = C_(ctx);
+  if (moe_status s = check_forward(c, layer, d_x, T, d_y)) return s;
+  if (T == 0) return MOE_OK;
+  const size_t need = decode_scratch_layout(c->cfg, T, nullptr, nullptr);
+  if (need > kStaticScratchBytes) {
+    std::snprintf(g_err, sizeof g_err,
+                  "this call needs %zu bytes of device scratch, the fixed array holds %zu",
+                  need, kStaticScratchBytes);
+    return MOE_ERR_CAPACITY;
+  }
+  DecodeScratch s;
+  decode_scratch_layout(c->cfg, T, c->static_scratch, &s);
+  if (moe_status st = decode_forward(c, s, layer, (const uint16_t*)d_x, T, d_bias,
+                                     (uint16_t*)d_y, d_y32, d_ids, d_gates, (hipStream_t)stream,
+                                     false))
+    return st;
   c->host_stats.forward_calls++;
   return MOE_OK;
 }

@@ -111,6 +111,12 @@ struct DecodeScratch {
 // *s are laid out from base (256-byte aligned pieces).
 size_t decode_scratch_layout(const moe_config& f, int T, uint8_t* base, DecodeScratch* s);
 
+// The fixed device scratch of moe_layer_forward_noalloc: its size, and the
+// device address of `device`'s copy (resolved once per device, with that
+// device current; later calls return the kept address).
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+hipError_t static_scratch_address(int device, uint8_t** out);
+
 // Cache state and statistics on the device.
 struct DevCache {
   uint64_t clock;
@@ -171,9 +177,11 @@ struct Ctx {
   int32_t* d_victim = nullptr;
   DevCache* d_cache = nullptr;
 
-  // decode scratch (one allocation, sized for max_tokens)
+  // decode scratch (one allocation, sized for max_tokens), and the device
+  // address of this device's fixed scratch array (moe_layer_forward_noalloc)
   uint8_t* d_scratch = nullptr;
   DecodeScratch ds;
+  uint8_t* static_scratch = nullptr;
   int32_t* d_lookup_ids = nullptr;  // [E] for expert_cache_fill
 
   // internal copy stream of the prefill layer uploads, joined to the

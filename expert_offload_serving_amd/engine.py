@@ -142,6 +142,14 @@ class MoEEngine:
         b.moe_layer_forward(self.ctx, layer, x, T, bias, y, y32, ids, gates, stream)
         return y
 
+    def forward_noalloc(self, layer: int, x, y, bias=None, ids=None, gates=None, y32=None,
+                        stream=None):
+        """forward() through moe_layer_forward_noalloc: the library's fixed
+        device scratch, no allocation (y must be given)."""
+        T = check_forward(self.H, self.E, self.k, self.max_tokens, x, bias, y, ids, gates, y32)
+        b.moe_layer_forward_noalloc(self.ctx, layer, x, T, bias, y, y32, ids, gates, stream)
+        return y
+
     def prefill(self, xs: Sequence, ys: Sequence, biases: Optional[Sequence] = None,
                 y32s: Optional[Sequence] = None, stream=None):
         T = check_prefill(self.H, self.E, self.L, self.max_prefill_tokens, xs, ys, biases, y32s)

@@ -227,6 +227,27 @@ moe_status moe_layer_forward(moe_ctx* ctx, int32_t layer, const void* d_x,
                              void* stream);
 
 /*
+ * moe_layer_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, checks, arithmetic and cache behaviour; the
+ * per-call device scratch (logits, routing, dispatch, work and fill lists,
+ * h, fp32 expert outputs) lives in a fixed 16 MiB device array of the
+ * library instead of the context's own buffer, and the call allocates
+ * nothing (no hipMalloc, no events; kernel timing is not recorded).  Each
+ * GPU holds one such array for the life of the process, resolved at
+ * moe_create, and every call on that GPU shares it, so calls that overlap
+ * on one GPU (from any context or stream) race; nothing in it needs to
+ * start at zero.  Errors: as moe_layer_forward, and CAPACITY when the call
+ * needs more scratch than the array holds (about 2*T*(k+1)*(H+I) bytes plus
+ * T*E*4; T=32 tokens at H=4096, I=2048, top-6 with a shared expert need
+ * 5.5 MiB).
+ */
+moe_status moe_layer_forward_noalloc(moe_ctx* ctx, int32_t layer, const void* d_x,
+                                     int32_t T, const float* d_bias, void* d_y,
+                                     float* d_y32, int32_t* d_ids, float* d_gates,
+                                     void* stream);
+
+/*
  * Prefill forward of layers 0..n_layers-1 for T tokens each
  * (0 < T <= max_prefill_tokens).  Layer l's experts are uploaded whole from
  * the pinned pool into one of two HBM layer buffers on an internal copy

@@ -199,6 +199,8 @@ def run_decode(wl, T, steps, warmup, seed=0, eng=None, distinct=None, resize_at=
 
     def do_step(s, allow_resize=True):
         if allow_resize and resize_to is not None and s == resize_at:
+            # the resize waits for the queued steps; time only its own work
+            torch.cuda.synchronize()
             t0 = time.perf_counter()
             before = eng.stats()
             eng.cache_resize(resize_to)

@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "moe_internal.h"
+#include "resize_plan.h"
 
 using namespace moe;
 
@@ -61,9 +62,11 @@ void destroy_all(Ctx* c) {
   prefill_free(c);
   if (c->pool) (void)hipHostFree(c->pool);
   c->pool = nullptr;
-  dfree(c->d_router); dfree(c->d_shared); dfree(c->d_slots); dfree(c->d_staging);
-  dfree(c->d_key); dfree(c->d_stamp); dfree(c->d_order); dfree(c->d_order_tmp);
-  dfree(c->d_hitflag); dfree(c->d_map); dfree(c->d_victim); dfree(c->d_cache);
+  dfree(c->d_router); dfree(c->d_shared); dfree(c->d_staging);
+  arena_free(c->arena);
+  c->d_slots = nullptr;
+  dfree(c->d_key); dfree(c->d_stamp); dfree(c->d_order); dfree(c->d_map); dfree(c->d_pairs);
+  dfree(c->d_cache);
   dfree(c->d_scratch);
   c->ds = DecodeScratch{};
   dfree(c->d_lookup_ids);
@@ -340,7 +343,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       return fail(MOE_ERR_HIP, std::string("device query: ") + hipGetErrorString(e0));
     }
   }
-  const int H = f.hidden, I = f.inter, E = f.n_experts, k = f.top_k, L = f.n_layers;
+  const int H = f.hidden, I = f.inter, E = f.n_experts, L = f.n_layers;
   const int Tm = f.max_tokens;
   c->rec_bytes = expert_record_bytes(H, I, f.weight_format);
   c->stride = (c->rec_bytes + 255) / 256 * 256;
@@ -359,15 +362,24 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   }
   ALLOC(c->d_router, (size_t)L * H * E * sizeof(float));
   if (f.has_shared) ALLOC(c->d_shared, (size_t)L * c->stride);
-  ALLOC(c->d_slots, (size_t)c->C * c->stride);
+  c->max_slots = (int)std::min<int64_t>((int64_t)L * E, kMaxCacheSlots);
+  {
+    hipError_t ea = arena_init(c->arena, c->device, (size_t)c->max_slots * c->stride);
+    if (ea == hipSuccess) ea = arena_ensure(c->arena, (size_t)c->C * c->stride);
+    if (ea != hipSuccess) {
+      destroy_all(c);
+      delete c;
+      return fail(ea == hipErrorOutOfMemory ? MOE_ERR_OOM : MOE_ERR_HIP,
+                  std::string("cache slot memory: ") + hipGetErrorString(ea));
+    }
+    c->d_slots = c->arena.base;
+  }
   ALLOC(c->d_staging, (size_t)f.staging_slots * c->stride);
-  ALLOC(c->d_key, (size_t)std::max(c->C, 1) * 4);
-  ALLOC(c->d_stamp, (size_t)std::max(c->C, 1) * 8);
-  ALLOC(c->d_order, (size_t)std::max(c->C, 1) * 4);
-  ALLOC(c->d_order_tmp, (size_t)std::max(c->C, 1) * 4);
-  ALLOC(c->d_hitflag, (size_t)std::max(c->C, 1));
+  ALLOC(c->d_key, (size_t)c->max_slots * 4);
+  ALLOC(c->d_stamp, (size_t)c->max_slots * 8);
+  ALLOC(c->d_order, (size_t)c->max_slots * 4);
   ALLOC(c->d_map, (size_t)L * E * 4);
-  ALLOC(c->d_victim, (size_t)std::min(Tm * k, E) * 4);
+  ALLOC(c->d_pairs, (size_t)c->max_slots * sizeof(FillEntry));
   ALLOC(c->d_cache, sizeof(DevCache));
   ALLOC(c->d_scratch, decode_scratch_layout(f, Tm, nullptr, nullptr));
   decode_scratch_layout(f, Tm, c->d_scratch, &c->ds);
@@ -617,6 +629,21 @@ moe_status expert_cache_fill(moe_ctx* ctx, int32_t layer, const int32_t* h_exper
   return MOE_OK;
 }
 
+// Upload a slot table (and the expert -> slot map it implies) for C2 slots.
+static hipError_t upload_cache_state(Ctx* c, const std::vector<int32_t>& key,
+                                     const std::vector<uint64_t>& stamp,
+                                     const std::vector<int32_t>& order) {
+  const int L = c->cfg.n_layers, E = c->cfg.n_experts;
+  std::vector<int32_t> map((size_t)L * E, -1);
+  for (size_t s = 0; s < key.size(); s++)
+    if (key[s] >= 0) map[key[s]] = (int32_t)s;
+  hipError_t e = upload(c->d_key, key);
+  if (e == hipSuccess) e = upload(c->d_stamp, stamp);
+  if (e == hipSuccess) e = upload(c->d_order, order);
+  if (e == hipSuccess) e = upload(c->d_map, map);
+  return e;
+}
+
 moe_status expert_cache_resize(moe_ctx* ctx, int32_t new_slots, void* stream) {
   if (moe_status s = check_ctx(ctx)) return s;
   Ctx* c = C_(ctx);
@@ -638,79 +665,45 @@ moe_status expert_cache_resize(moe_ctx* ctx, int32_t new_slots, void* stream) {
     HIPCHK(hipMemcpy(stamp.data(), c->d_stamp, (size_t)C * 8, hipMemcpyDeviceToHost));
   }
   HIPCHK(hipMemcpy(&dc, c->d_cache, sizeof dc, hipMemcpyDeviceToHost));
+  const ResizePlan plan = plan_resize(key, stamp, C2, kOrderKeyShift);
 
-  // New state: src_of[d] = old slot copied into new slot d (or -1).
-  std::vector<int32_t> key2(C2, -1), src_of(C2, -1);
-  std::vector<uint64_t> stamp2(C2, 0);
-  uint64_t evicted = 0, moved = 0;
-  if (C2 >= C) {
-    for (int s = 0; s < C; s++)
-      if (key[s] >= 0) { key2[s] = key[s]; stamp2[s] = stamp[s]; src_of[s] = s; }
-  } else {
-    std::vector<int> occ;
-    for (int s = 0; s < C; s++) if (key[s] >= 0) occ.push_back(s);
-    std::sort(occ.begin(), occ.end(), [&](int a, int b) { return stamp[a] < stamp[b]; });
-    std::vector<char> alive(C, 0);
-    size_t drop = occ.size() > (size_t)C2 ? occ.size() - C2 : 0;
-    for (size_t i = drop; i < occ.size(); i++) alive[occ[i]] = 1;
-    evicted = drop;
-    std::vector<int> free_low;
-    for (int s = 0; s < C2; s++) {
-      if (alive[s]) { key2[s] = key[s]; stamp2[s] = stamp[s]; src_of[s] = s; }
-      else free_low.push_back(s);
-    }
-    size_t fi = 0;
-    for (int s = C2; s < C; s++)
-      if (alive[s]) {
-        const int d = free_low[fi++];
-        key2[d] = key[s]; stamp2[d] = stamp[s]; src_of[d] = s;
-        moved++;
-      }
+  // Growing maps memory for the new slots first: on failure nothing changed.
+  if (C2 > C) {
+    const hipError_t e = arena_ensure(c->arena, (size_t)C2 * c->stride);
+    if (e != hipSuccess)
+      return fail(e == hipErrorOutOfMemory ? MOE_ERR_OOM : MOE_ERR_HIP,
+                  std::string("cache slot memory: ") + hipGetErrorString(e));
   }
-  // Move the surviving records into a slot buffer of the new size.
-  uint8_t* slots2 = nullptr;
-  if (C2 && hipMalloc((void**)&slots2, (size_t)C2 * c->stride) != hipSuccess)
-    return fail(MOE_ERR_OOM, "resized slot buffer");
-  std::vector<FillEntry> pairs;
-  for (int d = 0; d < C2; d++)
-    if (src_of[d] >= 0)
-      pairs.push_back({c->d_slots + (size_t)src_of[d] * c->stride, slots2 + (size_t)d * c->stride});
-  if (!pairs.empty()) {
-    FillEntry* dp = nullptr;
-    HIPCHK(hipMalloc((void**)&dp, pairs.size() * sizeof(FillEntry)));
-    HIPCHK(hipMemcpy(dp, pairs.data(), pairs.size() * sizeof(FillEntry), hipMemcpyHostToDevice));
-    HIPCHK(launch_copy_pairs(dp, (int)pairs.size(), c->rec_bytes, st));
-    HIPCHK(hipStreamSynchronize(st));
-    HIPCHK(hipFree(dp));
+  // Shrinking moves the survivors held past the new capacity down (sources
+  // and destinations are disjoint) and only then publishes the new table.
+  // Should that fail part way, the records the old table names may already
+  // be overwritten, so the cache is left empty (always consistent: outputs
+  // never depend on the cache) and the error is returned.
+  auto fail_empty = [&](hipError_t e) {
+    const std::vector<int32_t> k0(C2, -1);
+    const std::vector<uint64_t> s0(C2, 0);
+    (void)upload_cache_state(c, k0, s0, recency_order(k0, s0, kOrderKeyShift));
+    c->C = C2;
+    std::snprintf(g_err, sizeof g_err, "resize: %s (the cache was emptied)", hipGetErrorString(e));
+    return MOE_ERR_HIP;
+  };
+  if (!plan.moves.empty()) {
+    std::vector<FillEntry> pairs;
+    for (const auto& m : plan.moves)
+      pairs.push_back({c->d_slots + (size_t)m.first * c->stride, c->d_slots + (size_t)m.second * c->stride});
+    hipError_t e = hipMemcpy(c->d_pairs, pairs.data(), pairs.size() * sizeof(FillEntry),
+                             hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = launch_copy_pairs(c->d_pairs, (int)pairs.size(), c->rec_bytes, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail_empty(e);
   }
-  dfree(c->d_slots);
-  c->d_slots = slots2;
-  // Recency order: empty slots by index, then occupied by stamp.
-  std::vector<int32_t> order(C2);
-  std::iota(order.begin(), order.end(), 0);
-  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
-    return (key2[a] < 0 ? 0 : stamp2[a]) < (key2[b] < 0 ? 0 : stamp2[b]);
-  });
-  for (auto& o : order) o |= (key2[o] + 1) << kOrderKeyShift;
-  std::vector<int32_t> map((size_t)L * E, -1);
-  for (int s = 0; s < C2; s++) if (key2[s] >= 0) map[key2[s]] = s;
-  dfree(c->d_key); dfree(c->d_stamp); dfree(c->d_order); dfree(c->d_order_tmp); dfree(c->d_hitflag);
-  const size_t n1 = std::max(C2, 1);
-  if (hipMalloc((void**)&c->d_key, n1 * 4) != hipSuccess ||
-      hipMalloc((void**)&c->d_stamp, n1 * 8) != hipSuccess ||
-      hipMalloc((void**)&c->d_order, n1 * 4) != hipSuccess ||
-      hipMalloc((void**)&c->d_order_tmp, n1 * 4) != hipSuccess ||
-      hipMalloc((void**)&c->d_hitflag, n1) != hipSuccess)
-    return fail(MOE_ERR_OOM, "resized cache state");
-  HIPCHK(upload(c->d_key, key2));
-  HIPCHK(upload(c->d_stamp, stamp2));
-  HIPCHK(upload(c->d_order, order));
-  HIPCHK(upload(c->d_map, map));
-  dc.evictions += evicted;
-  HIPCHK(hipMemcpy(c->d_cache, &dc, sizeof dc, hipMemcpyHostToDevice));
+  if (hipError_t e = upload_cache_state(c, plan.key, plan.stamp, plan.order)) return fail_empty(e);
+  dc.evictions += plan.evicted.size();
+  if (hipError_t e = hipMemcpy(c->d_cache, &dc, sizeof dc, hipMemcpyHostToDevice)) return fail_empty(e);
   c->C = C2;
+  if (C2 < C) arena_trim(c->arena, (size_t)C2 * c->stride);
   c->host_stats.resizes++;
-  c->host_stats.bytes_d2d += moved * c->rec_bytes;
+  c->host_stats.bytes_d2d += (uint64_t)plan.moves.size() * c->rec_bytes;
   return MOE_OK;
 }
 

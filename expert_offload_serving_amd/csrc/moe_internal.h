@@ -135,10 +135,7 @@ struct LookupArgs {
   uint64_t* stamp;         // [C]
   int32_t* order;          // [C] packed entries, least recent first (the
                            // sub-array of the slots slot0 .. slot0+C-1)
-  int32_t* order_tmp;      // [C]
   int32_t* map;            // [L*E] slot of each key or -1
-  uint8_t* hitflag;        // [C]
-  int32_t* victim;         // [max unique]
   DevCache* cache;
   const uint8_t* pool;     // pinned host pool (device-mapped)
   uint8_t* slots;          // [C] records
@@ -147,6 +144,28 @@ struct LookupArgs {
   FillEntry* fills;        // [max unique]
   DevMeta* meta;
 };
+
+// ---------------------------------------------------------------------------
+// Cache slot memory: a device address range reserved for the largest
+// capacity, backed by equal chunks (64 MiB .. 1 GiB, chosen per context)
+// mapped from its start as far as the current capacity needs (HIP virtual
+// memory management).
+// ---------------------------------------------------------------------------
+constexpr size_t kSlotChunkMin = (size_t)64 << 20;
+constexpr size_t kSlotChunkMax = (size_t)1 << 30;
+struct SlotArena {
+  uint8_t* base = nullptr;
+  size_t reserved = 0;     // bytes of address range
+  size_t chunk = 0;        // bytes per physical chunk
+  int device = 0;
+  std::vector<hipMemGenericAllocationHandle_t> chunks;  // chunk i backs [i, i+1) * chunk
+};
+hipError_t arena_init(SlotArena& a, int device, size_t max_bytes);
+// Back [0, bytes) with memory; all or nothing (on failure the arena is as before).
+hipError_t arena_ensure(SlotArena& a, size_t bytes);
+// Release the chunks that lie wholly at or past `bytes`.
+void arena_trim(SlotArena& a, size_t bytes);
+void arena_free(SlotArena& a);
 
 // ---------------------------------------------------------------------------
 // Context
@@ -164,17 +183,18 @@ struct Ctx {
   std::vector<uint8_t> router_set;  // per layer
   std::vector<uint8_t> shared_set;
 
-  // cache
+  // cache: C slots of the arena; the state arrays hold max_slots entries so
+  // that a resize never reallocates them
   int C = 0;
-  uint8_t* d_slots = nullptr;       // [C] records
+  int max_slots = 0;                // min(L*E, kMaxCacheSlots)
+  SlotArena arena;
+  uint8_t* d_slots = nullptr;       // arena.base: slot s at d_slots + s*stride
   uint8_t* d_staging = nullptr;     // [S] records
-  int32_t* d_key = nullptr;
-  uint64_t* d_stamp = nullptr;
-  int32_t* d_order = nullptr;
-  int32_t* d_order_tmp = nullptr;
-  uint8_t* d_hitflag = nullptr;
+  int32_t* d_key = nullptr;         // [max_slots]
+  uint64_t* d_stamp = nullptr;      // [max_slots]
+  int32_t* d_order = nullptr;       // [max_slots]
   int32_t* d_map = nullptr;         // [L*E]
-  int32_t* d_victim = nullptr;
+  FillEntry* d_pairs = nullptr;     // [max_slots] resize moves
   DevCache* d_cache = nullptr;
 
   // decode scratch (one allocation, sized for max_tokens), and the device

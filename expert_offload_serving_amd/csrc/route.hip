@@ -366,10 +366,7 @@ LookupArgs make_lookup_args(Ctx* c, int layer, bool insert, FillEntry* fills, De
   la.key = c->d_key;
   la.stamp = c->d_stamp;
   la.order = c->d_order + la.slot0;
-  la.order_tmp = c->d_order_tmp;
   la.map = c->d_map;
-  la.hitflag = c->d_hitflag;
-  la.victim = c->d_victim;
   la.cache = c->d_cache;
   la.pool = c->pool;
   la.slots = c->d_slots;

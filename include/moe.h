@@ -130,7 +130,7 @@ typedef struct moe_stats {
   uint64_t bypasses;        /* keys served from staging, state unchanged     */
   uint64_t evictions;       /* resident keys displaced by fills or resizes   */
   uint64_t bytes_h2d;       /* expert bytes copied from the host pool        */
-  uint64_t bytes_d2d;       /* expert bytes moved by resizes                 */
+  uint64_t bytes_d2d;       /* expert bytes copied by resizes (moved records) */
   uint64_t resizes;         /* expert_cache_resize calls                     */
   uint64_t prefill_layers;  /* layers run by moe_prefill_forward             */
 } moe_stats;
@@ -298,13 +298,21 @@ moe_status expert_cache_fill(moe_ctx* ctx, int32_t layer,
                              void* stream);
 
 /*
- * (sync) Resize the cache to new_slots (0 <= new_slots <= L*E) without
- * touching the host pool.  Growing appends empty slots.  Shrinking evicts
- * occupied slots in ascending recency while more than new_slots are
- * occupied, moves the survivors held in slots >= new_slots (ascending) into
- * the lowest empty slots < new_slots (ascending) keeping their recency,
- * then releases the tail of the slot memory.  Errors: INVALID_ARG,
- * UNSUPPORTED (above 4096 slots, or a policy other than GLOBAL), OOM, HIP.
+ * (sync) Resize the cache to new_slots (0 <= new_slots <= min(L*E, 4096))
+ * without touching the host pool or restarting: the GPU expert-cache budget
+ * changes at run time (aipolix.com FreeToken article, sixth paragraph).
+ * Growing maps memory for the new, empty slots.  Shrinking evicts occupied
+ * slots in ascending recency while more than new_slots are occupied, moves
+ * the survivors held in slots >= new_slots (ascending) into the lowest empty
+ * slots < new_slots (ascending) keeping their recency, and releases the slot
+ * memory past the new capacity.  Only the moved records are copied (at most
+ * new_slots of them; moe_stats.bytes_d2d counts their bytes).  The slots live
+ * in one reserved device address range backed by chunks of 64 MiB to 1 GiB,
+ * so up to one chunk past the last slot stays mapped.  Errors: INVALID_ARG,
+ * UNSUPPORTED (a policy other than GLOBAL), OOM (growing: the state is
+ * unchanged), HIP (when a copy or upload fails after records were moved the
+ * cache is left empty, which is consistent because outputs never depend on
+ * the cache).
  */
 moe_status expert_cache_resize(moe_ctx* ctx, int32_t new_slots, void* stream);
 

@@ -51,11 +51,15 @@ def test_glm_decode_with_resize():
     for s in range(wl.steps):
         if s in resize:
             run.eng.cache_resize(resize[s])
-            run.cache.resize(resize[s])
+            moves, evicted = run.cache.resize(resize[s])
             key, stamp, clock = run.eng.cache_snapshot()
             k_ref, s_ref, c_ref = run.cache.snapshot()
             assert key.tolist() == k_ref and stamp.tolist() == s_ref and clock == c_ref
-            _flush(f"resized to {resize[s]} slots at step {s}")
+            # at most C' records move, and only those are copied
+            assert len(moves) <= resize[s]
+            assert run.eng.stats()["bytes_d2d"] == len(moves) * wl.shape.expert_bytes()
+            _flush(f"resized to {resize[s]} slots at step {s}: {len(evicted)} evicted, "
+                   f"{len(moves)} moved")
         for l in range(wl.shape.layers):
             check = s in (0, 511, 512, wl.steps - 1) and l in (0, 7)
             _, err = run.step(l, s, check_out=check)
@@ -82,14 +86,18 @@ def test_resize_sequences_against_oracle(seed):
                       zipf_s=1.1, overlap=0.5)
     run = H.DecodeRun(wl, m, T=T)
     ref = H.DecodeRun(wl, m, T=T, cache_slots=0)
+    moved = 0
     for s in range(wl.steps):
         if rng.random() < 0.3:
             C2 = int(rng.choice([0, 1, 2, 5, 10, 17, 30, 48]))
             run.eng.cache_resize(C2)
-            run.cache.resize(C2)
+            moves, _ = run.cache.resize(C2)
+            moved += len(moves)
             key, stamp, clock = run.eng.cache_snapshot()
             k_ref, s_ref, c_ref = run.cache.snapshot()
             assert key.tolist() == k_ref and stamp.tolist() == s_ref and clock == c_ref
+            # only the records that change slots are copied
+            assert run.eng.stats()["bytes_d2d"] == moved * sh.expert_bytes()
         l = int(rng.integers(0, sh.layers))
         y, _ = run.step(l, s, check_out=(s % 10 == 0))
         y0, _ = ref.step(l, s, check_state=False)

@@ -99,7 +99,16 @@ enum {
   MOE_WEIGHTS_BF16 = 1
 };
 
-/* Layer-stack shape and capacities, fixed at moe_create. */
+/*
+ * Layer-stack shape and capacities, fixed at moe_create.  The shapes the
+ * pages name: many experts with few active per token (DeepSeek-V4-Flash: 6
+ * of 256) and an optional always-on shared expert (aiforradalom.hu article,
+ * section "A Mixture-of-Experts (MoE) kihívásai és a FreeToken
+ * megoldásai").  H and I must be multiples of 128: the weights are tiled in
+ * 16-row x 128-K atoms (four MX blocks of 32 per lane of a wave, the operand
+ * the MFMA and the one-load-per-lane streaming are built around); every
+ * shape the pages name has such sizes.
+ */
 typedef struct moe_config {
   int32_t hidden;          /* H: multiple of 128, 128..6144                  */
   int32_t inter;           /* I: expert intermediate size, multiple of 128,
@@ -143,9 +152,11 @@ size_t moe_expert_bytes(int32_t hidden, int32_t inter);
 
 /*
  * Create a context on the current HIP device: allocates the pinned host
- * expert pool (n_layers * n_experts expert records), the HBM router
- * matrices, shared experts, cache slots, staging slots and scratch, and
- * the device-resident cache state (all slots empty, clock 0).
+ * expert pool (n_layers * n_experts expert records; the experts live in host
+ * memory and come to the GPU on demand: aiforradalom.hu article, section "A
+ * Mixture-of-Experts (MoE) kihívásai és a FreeToken megoldásai"), the HBM
+ * router matrices, shared experts, cache slots, staging slots and scratch,
+ * and the device-resident cache state (all slots empty, clock 0).
  * Errors: INVALID_ARG (NULL or field out of range), UNSUPPORTED (H or I not
  * a multiple of 128 or above 6144, cache_slots above 4096), OOM, HIP.  *out
  * is set only on success.
@@ -157,12 +168,17 @@ moe_status moe_destroy(moe_ctx* ctx);
 
 /*
  * (sync) Set one layer's router matrix W_r, fp32 [H][E] row-major (E
- * contiguous).  Copied to HBM.  Errors: INVALID_ARG, HIP.
+ * contiguous).  Copied to HBM.  Offloading leaves the router unchanged
+ * (jansverre.net FreeToken article, section "Hva er FreeToken?"), so it is
+ * always resident.  Errors: INVALID_ARG, HIP.
  */
 moe_status moe_set_router(moe_ctx* ctx, int32_t layer, const float* h_router);
 
 /*
- * (sync) Set one expert's MXFP4 weights from the canonical layout:
+ * (sync) Set one expert's weights (MXFP4 for DeepSeek-V4-Flash on the pages:
+ * jansverre.net FreeToken article, section "Hvor raskt kjører modellene?";
+ * the element and scale encodings are OCP MX v1.0's) from the canonical
+ * layout:
  *   h_qg [I][H/2], h_qu [I][H/2], h_qd [H][I/2]: E2M1 codes, rows are output
  *     features, K contiguous, element 2i in the low nibble of byte i;
  *   h_sg [I][H/32], h_su [I][H/32], h_sd [H][I/32]: E8M0 scale bytes, one per
@@ -183,8 +199,10 @@ moe_status moe_set_expert(moe_ctx* ctx, int32_t layer, int32_t expert,
                           const uint8_t* h_su, const uint8_t* h_sd);
 
 /*
- * (sync) Set a whole layer: router plus all E routed experts plus the shared
- * expert.  h_q holds E consecutive records of [qg | qu | qd] (3*H*I/2
+ * (sync) Set a whole layer, loaded once into the host pool (the pages load
+ * the model into host memory and stream experts from there: aiforradalom.hu
+ * article, section "A Mixture-of-Experts (MoE) kihívásai és a FreeToken
+ * megoldásai"): router plus all E routed experts plus the shared expert.  h_q holds E consecutive records of [qg | qu | qd] (3*H*I/2
  * bytes each) and h_s E consecutive records of [sg | su | sd] (3*H*I/32
  * bytes each), each part laid out as in moe_set_expert; h_shared_q /
  * h_shared_s hold one such record, or are NULL when has_shared is 0.  With
@@ -196,7 +214,14 @@ moe_status moe_set_layer(moe_ctx* ctx, int32_t layer, const float* h_router,
                          const uint8_t* h_shared_q, const uint8_t* h_shared_s);
 
 /*
- * Decode forward of one layer for T tokens (0 <= T <= max_tokens):
+ * Decode forward of one layer for T tokens (0 <= T <= max_tokens).  The
+ * pages' decode path: only the experts a token activates are needed, they
+ * are served from one global LRU cache across the MoE layers and fetched
+ * from host memory on a miss (jansverre.net FreeToken article, section
+ * "Hvorfor er båndbredden viktigere enn antall kjerner?"), with no
+ * approximation: the router is unchanged and the experts' partial results
+ * are summed at the end (same article, section "Hva er FreeToken?").
+ * Computed:
  *   logits l = fp32(x W_r + bias) accumulated in fp64; top-k ids ordered by
  *   (logit descending, expert ascending); gates = softmax over the chosen
  *   logits (renormalize = 1) or the full-softmax probabilities of the chosen
@@ -249,7 +274,10 @@ moe_status moe_layer_forward_noalloc(moe_ctx* ctx, int32_t layer, const void* d_
 
 /*
  * Prefill forward of layers 0..n_layers-1 for T tokens each
- * (0 < T <= max_prefill_tokens).  Layer l's experts are uploaded whole from
+ * (0 < T <= max_prefill_tokens): the pages stream the next layer's experts
+ * over PCIe while the GPU computes the current layer (aipolix.com FreeToken
+ * article, fourth paragraph; jansverre.net article, section "Hvorfor er
+ * båndbredden viktigere enn antall kjerner?").  Layer l's experts are uploaded whole from
  * the pinned pool into one of two HBM layer buffers on an internal copy
  * stream; the upload of layer l+1 overlaps the compute of layer l and waits
  * for layer l-1 (the previous reader of that buffer).  Expert FFNs run as
@@ -287,7 +315,10 @@ moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer,
                                int32_t* d_slot, void* stream);
 
 /*
- * Preload experts of one layer: the same rule as a lookup of h_experts
+ * Preload experts of one layer (placing a set beforehand, the placement the
+ * pages compare their LRU against: jansverre.net FreeToken article, section
+ * "Hvorfor er båndbredden viktigere enn antall kjerner?"): the same rule as
+ * a lookup of h_experts
  * (ascending unique, 0 <= n <= min(E, max_tokens*k)), without compute.  It
  * inserts under every policy (it is how the STATIC set is placed).
  * Errors: INVALID_ARG (unsorted, duplicate or out-of-range ids), CAPACITY

@@ -24,3 +24,4 @@ from .router import logits, topk, gates, route  # noqa: F401
 from .dispatch import permutation  # noqa: F401
 from .experts import expert_ffn, moe_layer  # noqa: F401
 from .cache import SlotCache  # noqa: F401
+from .mx import moe_layer_mx, quantize_mxfp8  # noqa: F401

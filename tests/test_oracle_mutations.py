@@ -15,6 +15,7 @@ import oracle
 from oracle import cache as ocache
 from oracle import dispatch as odispatch
 from oracle import experts as oexperts
+from oracle import mx as omx
 from oracle import mxfp4 as omxfp4
 from oracle import router as orouter
 from workload import gen
@@ -23,6 +24,7 @@ from tests import test_bf16_rounding as p_bf16
 from tests import test_oracle_cache as p_cache
 from tests import test_oracle_dispatch as p_dispatch
 from tests import test_oracle_experts as p_experts
+from tests import test_oracle_mx as p_mx
 from tests import test_oracle_mxfp4 as p_mxfp4
 from tests import test_oracle_router as p_router
 
@@ -294,6 +296,53 @@ def m_bf16_ties_away(mp):
     mp.setattr(gen, "f32_to_bf16_bits", away)
 
 
+def m_mx_scale_off_by_one(mp):
+    good = omx.block_exponents
+    mp.setattr(omx, "block_exponents", lambda v: good(v) + 1)
+
+
+def m_mx_truncates(mp):
+    def round_trunc(t):
+        t = np.asarray(t, dtype=np.float64)
+        a = np.abs(t)
+        with np.errstate(divide="ignore"):
+            e = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), -6)
+        step = np.ldexp(1.0, (e - 3).astype(np.int64))
+        return np.copysign(np.minimum(np.floor(a / step) * step, 448.0), t)
+    mp.setattr(omx, "round_e4m3", round_trunc)
+
+
+def m_mx_no_clamp(mp):
+    def round_noclamp(t):
+        t = np.asarray(t, dtype=np.float64)
+        a = np.abs(t)
+        with np.errstate(divide="ignore"):
+            e = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), -6)
+        step = np.ldexp(1.0, (e - 3).astype(np.int64))
+        return np.copysign(np.round(a / step) * step, t)
+    mp.setattr(omx, "round_e4m3", round_noclamp)
+
+
+def m_mx_block_of_16(mp):
+    def quant16(v):
+        v = np.asarray(v, dtype=np.float64)
+        b = v.reshape(v.shape[:-1] + (v.shape[-1] // 16, 16))
+        amax = np.max(np.abs(b), axis=-1)
+        with np.errstate(divide="ignore"):
+            e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, -127)
+        sc = np.repeat(np.ldexp(1.0, e.astype(np.int64)), 16, axis=-1)
+        return omx.round_e4m3(v / sc) * sc
+    mp.setattr(omx, "quantize_mxfp8", quant16)
+
+
+def m_mx_h_not_quantised(mp):
+    def ffn(xq_t, wg, wu, wd):
+        x = np.asarray(xq_t, dtype=np.float64)
+        a, b = wg.astype(np.float64) @ x, wu.astype(np.float64) @ x
+        return wd.astype(np.float64) @ (a / (1.0 + np.exp(-a)) * b)
+    mp.setattr(omx, "expert_ffn_mx", ffn)
+
+
 # --------------------------------------------------------- pins to run
 MXFP4_PINS = [p_mxfp4.test_e2m1_table_matches_spec_fixture,
               p_mxfp4.test_e2m1_table_matches_bitfield_closed_form,
@@ -317,6 +366,10 @@ CACHE_PINS = [p_cache.test_matches_textbook_lru_when_unique_set_fits,
               p_cache.test_bypass_when_unique_set_exceeds_capacity,
               p_cache.test_resize_invariants, p_cache.test_resize_hand_computed_slot_numbering,
               lambda: p_cache.test_resize_brute_force_against_rank_model(4, 3, 3)]
+MX_PINS = [p_mx.test_e4m3_fields, p_mx.test_round_e4m3_is_nearest_with_ties_to_even,
+           p_mx.test_block_scale_rule, p_mx.test_quantize_closed_forms,
+           p_mx.test_mx_layer_equals_plain_layer_on_representable_inputs,
+           p_mx.test_mx_layer_near_plain_layer]
 BF16_PINS = [p_bf16.test_ties_go_to_even, p_bf16.test_special_values_match_torch,
              p_bf16.test_random_values_match_torch]
 
@@ -344,6 +397,11 @@ MUTATIONS = [
     (m_resize_evicts_most_recent, CACHE_PINS),
     (m_lookup_hits_not_pinned, CACHE_PINS),
     (m_lookup_victims_most_recent_first, CACHE_PINS),
+    (m_mx_scale_off_by_one, MX_PINS),
+    (m_mx_truncates, MX_PINS),
+    (m_mx_no_clamp, MX_PINS),
+    (m_mx_block_of_16, MX_PINS),
+    (m_mx_h_not_quantised, MX_PINS),
     (m_bf16_truncates, BF16_PINS),
     (m_bf16_ties_away, BF16_PINS),
 ]
@@ -373,5 +431,6 @@ def test_planted_mistake_is_caught(monkeypatch, mutate, pins):
 def test_pins_pass_again_after_the_mutations():
     """monkeypatch restored every module: the plain oracle passes its pins."""
     assert oracle.router.topk is orouter.topk
-    for pins in (MXFP4_PINS, ROUTER_PINS, DISPATCH_PINS, EXPERT_PINS, CACHE_PINS, BF16_PINS):
+    for pins in (MXFP4_PINS, ROUTER_PINS, DISPATCH_PINS, EXPERT_PINS, CACHE_PINS, MX_PINS,
+                 BF16_PINS):
         assert not _caught(pins)

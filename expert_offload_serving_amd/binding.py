@@ -32,7 +32,7 @@ class moe_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "hidden", "inter", "n_experts", "top_k", "n_layers", "has_shared", "renormalize",
         "max_tokens", "cache_slots", "staging_slots", "max_prefill_tokens", "cache_policy",
-        "weight_format")]
+        "weight_format", "prefill_format")]
 
 
 class moe_timing(ctypes.Structure):
@@ -66,12 +66,14 @@ _SIGS = {
     "moe_layer_forward": (_I32, [_P, _I32, _P, _I32, _P, _P, _P, _P, _P, _P]),
     "moe_layer_forward_noalloc": (_I32, [_P, _I32, _P, _I32, _P, _P, _P, _P, _P, _P]),
     "moe_prefill_forward": (_I32, [_P, _I32, _P, _I32, _P, _P, _P, _P]),
+    "moe_set_prefill_format": (_I32, [_P, _I32]),
     "expert_cache_lookup": (_I32, [_P, _I32, _P, _P, _P, _P]),
     "expert_cache_fill": (_I32, [_P, _I32, _P, _I32, _P]),
     "expert_cache_resize": (_I32, [_P, _I32, _P]),
     "expert_cache_snapshot": (_I32, [_P, _I32, _P, _P, _P, _P]),
     "moe_inspect_dispatch": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_inspect_prefill": (_I32, [_P, _I32, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_inspect_prefill_mx": (_I32, [_P, _P, _P, _P, _P, _P]),
     "moe_get_stats": (_I32, [_P, ctypes.POINTER(moe_stats)]),
     "moe_reset_stats": (_I32, [_P]),
     "moe_set_timing": (_I32, [_P, _I32]),
@@ -186,6 +188,14 @@ def moe_prefill_forward(ctx, n_layers, d_xs: Sequence, T, d_biases, d_ys: Sequen
                                    arr(d_y32s), _stream(stream)), "moe_prefill_forward")
 
 
+# moe_config.prefill_format values, in enum order (MOE_PREFILL_BF16, ...)
+PREFILL_FORMATS = ("bf16", "mxfp8")
+
+
+def moe_set_prefill_format(ctx, fmt: str):
+    _check(lib.moe_set_prefill_format(ctx, PREFILL_FORMATS.index(fmt)), "moe_set_prefill_format")
+
+
 def expert_cache_lookup(ctx, layer, d_experts, d_n, d_slot, stream=None):
     _check(lib.expert_cache_lookup(ctx, layer, _ptr(d_experts), _ptr(d_n), _ptr(d_slot),
                                    _stream(stream)), "expert_cache_lookup")
@@ -246,6 +256,21 @@ def moe_inspect_prefill(ctx, layer: int, E: int, k: int, T_max: int):
     n = T.value
     return dict(T=n, ids=ids[:n * k].reshape(n, k), gates=gates[:n * k].reshape(n, k),
                 counts=counts, offsets=offsets, sorted=sorted_[:n * k], inv=inv[:n * k])
+
+
+def moe_inspect_prefill_mx(ctx, H: int, I: int, k: int, shared: bool, T_max: int):
+    T = ctypes.c_int32()
+    rows_max = T_max * (k + 1)
+    xq = np.zeros(T_max * H, np.uint8)
+    xs = np.zeros(T_max * (H // 32), np.uint8)
+    hq = np.zeros(rows_max * I, np.uint8)
+    hs = np.zeros(rows_max * (I // 32), np.uint8)
+    _check(lib.moe_inspect_prefill_mx(ctx, ctypes.byref(T), _ptr(xq), _ptr(xs), _ptr(hq), _ptr(hs)),
+           "moe_inspect_prefill_mx")
+    n = T.value
+    R = n * k + (n if shared else 0)
+    return dict(T=n, xq=xq[:n * H].reshape(n, H), xs=xs[:n * (H // 32)].reshape(n, H // 32),
+                hq=hq[:R * I].reshape(R, I), hs=hs[:R * (I // 32)].reshape(R, I // 32))
 
 
 def moe_get_stats(ctx) -> dict:

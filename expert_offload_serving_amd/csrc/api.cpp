@@ -309,6 +309,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       f.max_prefill_tokens < 0 || (f.has_shared != 0 && f.has_shared != 1) ||
       f.cache_policy < MOE_CACHE_GLOBAL || f.cache_policy > MOE_CACHE_STATIC ||
       f.weight_format < MOE_WEIGHTS_MXFP4 || f.weight_format > MOE_WEIGHTS_BF16 ||
+      f.prefill_format < MOE_PREFILL_BF16 || f.prefill_format > MOE_PREFILL_MXFP8 ||
       (f.renormalize != 0 && f.renormalize != 1))
     return fail(MOE_ERR_INVALID_ARG, "moe_config field out of range");
   if ((int64_t)f.cache_slots > (int64_t)f.n_layers * f.n_experts)
@@ -320,6 +321,8 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   if (f.weight_format == MOE_WEIGHTS_BF16 && (f.max_tokens > 16 || f.max_prefill_tokens > 0))
     return fail(MOE_ERR_UNSUPPORTED,
                 "bf16 experts run the decode path for at most 16 tokens per call (no prefill)");
+  if (f.prefill_format == MOE_PREFILL_MXFP8 && f.weight_format != MOE_WEIGHTS_MXFP4)
+    return fail(MOE_ERR_UNSUPPORTED, "the MXFP8 prefill mode needs MXFP4 experts");
   if (f.cache_slots > kMaxCacheSlots)
     return fail(MOE_ERR_UNSUPPORTED, "cache_slots above 4096");
   if (f.max_prefill_tokens > (1 << 20))
@@ -348,6 +351,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   c->rec_bytes = expert_record_bytes(H, I, f.weight_format);
   c->stride = (c->rec_bytes + 255) / 256 * 256;
   c->C = f.cache_slots;
+  c->prefill_format = f.prefill_format;
   c->router_set.assign(L, 0);
   c->shared_set.assign(L, 0);
 
@@ -586,6 +590,18 @@ moe_status moe_prefill_forward(moe_ctx* ctx, int32_t n_layers, const void* const
   return MOE_OK;
 }
 
+moe_status moe_set_prefill_format(moe_ctx* ctx, int32_t format) {
+  if (moe_status s = check_ctx(ctx)) return s;
+  Ctx* c = C_(ctx);
+  if (format < MOE_PREFILL_BF16 || format > MOE_PREFILL_MXFP8)
+    return fail(MOE_ERR_INVALID_ARG, "unknown prefill format");
+  if (format == MOE_PREFILL_MXFP8 && c->cfg.weight_format != MOE_WEIGHTS_MXFP4)
+    return fail(MOE_ERR_UNSUPPORTED, "the MXFP8 prefill mode needs MXFP4 experts");
+  HIPCHK(hipDeviceSynchronize());
+  c->prefill_format = format;
+  return MOE_OK;
+}
+
 moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer, const int32_t* d_experts,
                                const int32_t* d_n, int32_t* d_slot, void* stream) {
   if (moe_status s = check_ctx(ctx)) return s;
@@ -760,6 +776,17 @@ moe_status moe_inspect_prefill(moe_ctx* ctx, int32_t layer, int32_t* h_T, int32_
   if (run > 0 && (layer < 0 || layer >= run))
     return fail(MOE_ERR_INVALID_ARG, "layer outside the layers of the last prefill call");
   HIPCHK(prefill_inspect(c, layer, h_T, h_ids, h_gates, h_counts, h_offsets, h_sorted, h_inv));
+  return MOE_OK;
+}
+
+moe_status moe_inspect_prefill_mx(moe_ctx* ctx, int32_t* h_T, uint8_t* h_xq, uint8_t* h_xs,
+                                  uint8_t* h_hq, uint8_t* h_hs) {
+  if (moe_status s = check_ctx(ctx)) return s;
+  if (!h_T) return fail(MOE_ERR_INVALID_ARG, "h_T is NULL");
+  Ctx* c = C_(ctx);
+  if (prefill_last_mx(c) == 0)
+    return fail(MOE_ERR_UNSUPPORTED, "the last prefill call did not run in the MXFP8 mode");
+  HIPCHK(prefill_inspect_mx(c, h_T, h_xq, h_xs, h_hq, h_hs));
   return MOE_OK;
 }
 

@@ -209,6 +209,7 @@ struct Ctx {
   hipStream_t copy_stream = nullptr;
 
   // prefill (allocated on first use)
+  int prefill_format = MOE_PREFILL_BF16;
   int Tp_max = 0;
   uint8_t* d_layerbuf[2] = {nullptr, nullptr};
   hipEvent_t ev_upload[2] = {nullptr, nullptr};
@@ -289,6 +290,10 @@ int fillable_slots(const Ctx* c, int layer, bool insert, int* slot0);
 int prefill_max_tiles(int T, int k, int E);
 size_t prefill_lo_bytes(int T, int k, int E, int I);
 int prefill_layers_run(const Ctx* c);
+// 1 if the last prefill call ran in the MXFP8 mode, 0 if not, -1 if none ran
+int prefill_last_mx(const Ctx* c);
+hipError_t prefill_inspect_mx(Ctx* c, int32_t* T, uint8_t* xq, uint8_t* xs, uint8_t* hq,
+                              uint8_t* hs);
 hipError_t prefill_inspect(Ctx* c, int layer, int32_t* T, int32_t* ids, float* gates,
                            int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* inv);
 hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* x, int T,

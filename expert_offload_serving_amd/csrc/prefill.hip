@@ -18,6 +18,7 @@ struct Prefill {
   int Tmax = 0;
   int last_T = 0;
   int last_layers = 0;
+  int last_mx = 0;             // the last call ran in the MXFP8 mode
   int nchunk_max = 0;
   int max_tiles = 0;
   float* logits = nullptr;     // [Tmax][E]
@@ -31,7 +32,11 @@ struct Prefill {
   int32_t* tok = nullptr;      // [Tmax*k + Tmax]
   int2* tiles = nullptr;       // [max_tiles]: (group, first row)
   int32_t* n_tiles = nullptr;  // [1]
-  uint16_t* h = nullptr;       // bf16 [rows][I]: h rounded to bf16
+  uint16_t* h = nullptr;       // bf16 [rows][I]: h rounded to bf16; in the MXFP8
+                               // mode the same memory holds h's codes
+                               // [rows][I] then its scales [rows][I/32]
+  uint8_t* xq = nullptr;       // MXFP8 mode: x codes [Tmax][H], then scales
+                               // [Tmax][H/32] (allocated on first use)
   uint8_t* hlo = nullptr;      // low-order records of h: [max_tiles][I/128][8][1664]
   float* yperm = nullptr;      // [rows][H]
 };
@@ -837,6 +842,373 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
 #undef DN
 }
 
+// ------------------------------------------------------- native-MX GEMMs
+// The opt-in MXFP8 prefill mode (moe_config.prefill_format): both expert
+// matrices on v_mfma_scale_f32_16x16x128_f8f6f4 with the activations block-
+// quantised to MXFP8 (E4M3 elements, one E8M0 scale per 32 along K; OCP MX
+// scale rule, nearest-even rounding clamped to +-448) and the MXFP4 weight
+// atoms taken as stored: no dequantisation, one MFMA per 16 rows x 16
+// columns x 128 K, half the activation bytes of the bf16 path.
+//
+// Activation stage in LDS (per K chunk of 128): fragment g (tile rows
+// 16g .. 16g+15) is 2 KB laid out as the MFMA operand wants it: lane L's 32
+// codes (row L%16, MX block L/16 of the chunk) as two 16-byte halves at
+// 16L and 1024 + 16L, so each half is one conflict-free 16-byte read per
+// lane.  A buffer-to-LDS load fills one half of one fragment (lane j fetches
+// row 16g + j%16, block j/16, half h of the gathered row).  The 128 rows'
+// scale bytes follow as [row][4 blocks] (one 4-byte load per row).
+constexpr int kMxFrag = 2048;
+constexpr int kMxCodes = 8 * kMxFrag;                    // 16 KB per stage
+constexpr int kMxAStage = kMxCodes + kBM * 4;            // + 512 B of scales
+constexpr int kLdsMx = kStagesA * kMxAStage + kStagesB * kLdsBStage;   // 101 KB
+constexpr int kLdsMxGateUp = kLdsMx > 8 * kEpiWave ? kLdsMx : 8 * kEpiWave;
+static_assert(kLdsMxGateUp <= 160 * 1024, "LDS per CU");
+
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// MXFP8 block quantisation of 32 fp32 values: exponent e = floor(log2 amax)
+// - 8 clamped to [-127, 127] (-127 for an all-zero block); codes of
+// v * 2^-e (exact: a power-of-two scaling that stays finite for fp32 inputs,
+// since e <= 119 there) clamped to +-448 and converted to nearest E4M3 with
+// the hardware convert at scale 1.  Element i goes to byte i of `codes`.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  const uint32_t b = __float_as_uint(amax);
+  const int ex = (int)((b >> 23) & 0xFFu);
+  const int fl = ex ? ex - 127 : -149 + (31 - __builtin_clz(b & 0x7FFFFFu));
+  const int e = fl - 8;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+__device__ __forceinline__ uint32_t mx_quant32(const float (&v)[32], uint32_t (&codes)[8]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 32; t++) amax = fmaxf(amax, fabsf(v[t]));
+  const int e = mx_exponent(amax);
+  const float inv = ldexpf(1.0f, -e);
+#pragma unroll
+  for (int q = 0; q < 8; q++) {
+    float t[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) t[u] = fminf(fmaxf(v[4 * q + u] * inv, -448.0f), 448.0f);
+    s16x2 r = {0, 0};
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, t[0], t[1], 1.0f, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, t[2], t[3], 1.0f, true);
+    codes[q] = __builtin_bit_cast(uint32_t, r);
+  }
+  return (uint32_t)(e + 127);
+}
+
+// x [T][H] bf16 -> codes [T][H] and scale bytes [T][H/32]: one thread per
+// block of 32.
+__global__ __launch_bounds__(256) void quantize_x_mx_kernel(const uint16_t* __restrict__ x,
+                                                            int n_blocks,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+  const int blk = blockIdx.x * blockDim.x + threadIdx.x;
+  if (blk >= n_blocks) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)blk * 32);
+  float v[32];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const u32x4 w = src[q];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      v[8 * q + 2 * u] = __uint_as_float(w[u] << 16);
+      v[8 * q + 2 * u + 1] = __uint_as_float(w[u] & 0xFFFF0000u);
+    }
+  }
+  uint32_t c[8];
+  scales[blk] = (uint8_t)mx_quant32(v, c);
+  u32x4* dst = reinterpret_cast<u32x4*>(codes + (size_t)blk * 32);
+  dst[0] = u32x4{c[0], c[1], c[2], c[3]};
+  dst[1] = u32x4{c[4], c[5], c[6], c[7]};
+}
+
+struct MxTile {
+  const uint8_t* wbase;  // expert section start (gate/up or down)
+  uint32_t wbytes;       // section bytes
+  int KC;                // K chunks
+  int k0;                // first K chunk of the walk
+  int rows;              // valid rows in this tile
+  uint32_t aoff[4];      // A waves: lane's piece of fragments 2w, 2w+1, halves 0, 1 (chunk 0)
+  uint32_t asoff;        // waves 0, 1: lane's row scale word (row 64w + lane, chunk 0)
+  uint32_t woff[8];      // B waves, as GemmTile
+  uint32_t soff[2];
+};
+
+template <int MF>
+__device__ __forceinline__ void gemm_tile_mx(const MxTile& gt, __amdgpu_buffer_rsrc_t ra,
+                                             __amdgpu_buffer_rsrc_t rs, uint8_t* lds,
+                                             f32x4 (&acc)[MF > 0 ? MF : 1][kFragsPerWave]) {
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int mh = w >> 2, nq = w & 3;
+  const bool a_wave = w < 4;
+  const int KC = gt.KC;
+  const __amdgpu_buffer_rsrc_t rw = rsrc(gt.wbase, gt.wbytes);
+  uint8_t* const bstages = lds + kStagesA * kMxAStage;
+  auto chunk = [&](int c) { return c + gt.k0 < KC ? c + gt.k0 : c + gt.k0 - KC; };
+  // A waves: step s into stage s % 2 (fragments 2w, 2w+1 that hold rows;
+  // waves 0 and 1 also the scale words of rows 64w .. 64w+63)
+  auto issue_a = [&](int s) {
+    uint8_t* buf = lds + (s % kStagesA) * kMxAStage;
+    const bool in = s < KC;
+    const uint32_t kc = (uint32_t)chunk(s);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int frag = 2 * w + (i >> 1);
+      if (16 * frag < gt.rows)
+        lds_load16(ra, in ? gt.aoff[i] + kc * kAtomK : kOOB, buf + frag * kMxFrag + (i & 1) * 1024);
+    }
+    if (w < 2 && 64 * w < gt.rows)
+      lds_load4(rs, in ? gt.asoff + kc * 4u : kOOB, buf + kMxCodes + 256 * w);
+  };
+  auto issue_b = [&](int c) {
+    uint8_t* buf = bstages + (c % kStagesB) * kLdsBStage;
+    const int u = w - 4;
+    const bool in = c < KC;
+    const uint32_t k = (uint32_t)chunk(c) * kAtomBytes;
+#pragma unroll
+    for (int t = 0; t < 8; t++)
+      lds_load16(rw, in ? gt.woff[t] + k + 16u * lane : kOOB, buf + (8 * u + t) * kAtomData);
+#pragma unroll
+    for (int hh = 0; hh < 2; hh++)
+      lds_load4(rw, in ? gt.soff[hh] + k : kOOB, buf + kLdsBc + (8 * u + 4 * hh) * 64);
+  };
+  auto compute = [&](int s) {
+    if constexpr (MF == 0) {
+      if (!a_wave) issue_b(s + 1);
+    } else {
+      const uint8_t* abuf = lds + (s % kStagesA) * kMxAStage;
+      const uint8_t* bbuf = bstages + (s % kStagesB) * kLdsBStage;
+      i32x8 a8[MF];
+      int as[MF];
+#pragma unroll
+      for (int i = 0; i < MF; i++) {
+        const int frag = 2 * i + mh;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(abuf + frag * kMxFrag + 16 * lane);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(abuf + frag * kMxFrag + 1024 + 16 * lane);
+        a8[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        as[i] = abuf[kMxCodes + 4 * (16 * frag + (lane & 15)) + (lane >> 4)];
+      }
+#pragma unroll
+      for (int f = 0; f < kFragsPerWave; f++) {
+        const int atom = nq * kFragsPerWave + f;
+        const u32x4 wd = *reinterpret_cast<const u32x4*>(bbuf + atom * kAtomData + 16 * lane);
+        const int sd = bbuf[kLdsBc + atom * 64 + lane];
+        const i32x8 b8 = {(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3], 0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < MF; i++)
+          acc[i][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              a8[i], b8, acc[i][f], 0 /* A: fp8 E4M3 */, 4 /* B: fp4 E2M1 */, 0, as[i], 0, sd);
+        if (f == 1 && !a_wave) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_b(s + 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  };
+  if (a_wave)
+    issue_a(0);
+  else
+    issue_b(0);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int s = 0; s < KC; s++) {
+    wait_vmem_all();
+    lds_barrier();
+    if (a_wave) issue_a(s + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s);
+  }
+  wait_vmem_all();
+}
+
+// A-wave offsets of a tile: row r's codes start at rowbase(r), its scale
+// bytes at srowbase(r) (both for chunk 0).
+//
+// 8-bit A operand of the scaled 16x16x128 MFMA: lane l supplies row l % 16;
+// with g = l / 16 its bytes 0..15 are K = 16g .. 16g+15 and its bytes 16..31
+// K = 64+16g .. 64+16g+15 of the 128-wide chunk (not 32 consecutive K as for
+// the 4- and 6-bit formats).  The scale operand of lane l is still that of
+// row l % 16, K block l / 16, so the scale of a byte comes from another lane
+// than the byte itself.  The low half is loaded into fragment bytes
+// [0, 1024), the high half into [1024, 2048).
+template <class RowBase, class ScaleBase>
+__device__ __forceinline__ void set_mx_loads(MxTile& gt, int lane, RowBase rowbase, ScaleBase srowbase) {
+  const int w = wave_id();
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int r = 16 * (2 * w + (i >> 1)) + (lane & 15);
+    gt.aoff[i] = r < gt.rows ? rowbase(r) + 16u * (uint32_t)(lane >> 4) + 64u * (uint32_t)(i & 1)
+                             : kOOB;
+  }
+  const int rs = 64 * w + lane;
+  gt.asoff = (w < 2 && rs < gt.rows) ? srowbase(rs) : kOOB;
+}
+
+template <int MF>
+__device__ __forceinline__ void gateup_tile_mx(const MxTile& gt, __amdgpu_buffer_rsrc_t ra,
+                                               __amdgpu_buffer_rsrc_t rs, uint8_t* lds,
+                                               uint8_t* __restrict__ hq, uint8_t* __restrict__ hs,
+                                               int I, size_t row0, int p0) {
+  const int npairs = I / kAtomRows;
+  const int lane = threadIdx.x & 63, w = wave_id(), mh = w >> 2;
+  f32x4 acc[MF > 0 ? MF : 1][kFragsPerWave];
+#pragma unroll
+  for (int i = 0; i < (MF > 0 ? MF : 1); i++)
+#pragma unroll
+    for (int f = 0; f < kFragsPerWave; f++) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  gemm_tile_mx<MF>(gt, ra, rs, lds, acc);
+  // h = silu(gate) * up through LDS, then one (row, 32-column block) per
+  // lane quantised to MXFP8 (as in the bf16 path's epilogue)
+  lds_barrier();
+  float* ep = reinterpret_cast<float*>(lds + w * kEpiWave);
+#pragma unroll
+  for (int i = 0; i < MF; i++)
+#pragma unroll
+    for (int q = 0; q < kFragsPerWave / 2; q++)
+#pragma unroll
+      for (int r = 0; r < 4; r++)
+        ep[(i * 16 + 4 * (lane >> 4) + r) * kEpiStride + 16 * q + (lane & 15)] =
+            silu(acc[i][2 * q][r]) * acc[i][2 * q + 1][r];
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave reads its own writes
+  const int row = lane & 15, b = (lane >> 4) & 1;
+  const bool col_ok = p0 + 2 * b < npairs;
+#pragma unroll
+  for (int it = 0; it < (MF + 1) / 2; it++) {
+    const int i = 2 * it + (lane >> 5);
+    const int m = (2 * i + mh) * 16 + row;
+    if (i < MF && col_ok && m < gt.rows) {
+      const float* src = ep + (i * 16 + row) * kEpiStride + 32 * b;
+      float v[32];
+#pragma unroll
+      for (int t = 0; t < 8; t++) {
+        const f32x4 x4 = *reinterpret_cast<const f32x4*>(src + 4 * t);
+        v[4 * t] = x4[0], v[4 * t + 1] = x4[1], v[4 * t + 2] = x4[2], v[4 * t + 3] = x4[3];
+      }
+      uint32_t c[8];
+      const uint32_t sbyte = mx_quant32(v, c);
+      const size_t col = (size_t)16 * p0 + 32 * b;
+      u32x4* dst = reinterpret_cast<u32x4*>(hq + (row0 + m) * I + col);
+      dst[0] = u32x4{c[0], c[1], c[2], c[3]};
+      dst[1] = u32x4{c[4], c[5], c[6], c[7]};
+      hs[(row0 + m) * (I / 32) + col / 32] = (uint8_t)sbyte;
+    }
+  }
+}
+
+template <int MF>
+__device__ __forceinline__ void down_tile_mx(const MxTile& gt, __amdgpu_buffer_rsrc_t ra,
+                                             __amdgpu_buffer_rsrc_t rs, uint8_t* lds,
+                                             float* __restrict__ yperm, int H, size_t row0,
+                                             int rg0, int ngroups) {
+  const int lane = threadIdx.x & 63, mh = wave_id() >> 2;
+  f32x4 acc[MF > 0 ? MF : 1][kFragsPerWave];
+#pragma unroll
+  for (int i = 0; i < (MF > 0 ? MF : 1); i++)
+#pragma unroll
+    for (int f = 0; f < kFragsPerWave; f++) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  gemm_tile_mx<MF>(gt, ra, rs, lds, acc);
+#pragma unroll
+  for (int i = 0; i < MF; i++)
+#pragma unroll
+    for (int f = 0; f < kFragsPerWave; f++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int m = (2 * i + mh) * 16 + 4 * (lane >> 4) + r;
+        if (m < gt.rows && rg0 + f < ngroups)
+          yperm[(row0 + m) * H + (rg0 + f) * 16 + (lane & 15)] = acc[i][f][r];
+      }
+}
+
+// Gate/up + SwiGLU on MXFP8 activations: tiles as gateup_prefill_kernel; A
+// is the quantised token rows (codes [T][H], scales [T][H/32], gathered
+// through the permutation); h leaves as MXFP8 (codes [rows][I], scales
+// [rows][I/32]) for the down GEMM.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void gateup_mx_kernel(
+    GroupArgs g, const uint8_t* xq, uint32_t xq_bytes, const uint8_t* xs, uint32_t xs_bytes, int H,
+    int I, int nbn, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
+  int ti, nb;
+  tile_of_block(nbn, &ti, &nb);
+  if (ti >= *g.n_tiles) return;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsMxGateUp];
+  const int2 td = g.tiles[ti];
+  const int grp = td.x, m0 = td.y;
+  const int cnt = g.counts[grp], pos0 = g.offsets[grp];
+  const int lane = threadIdx.x & 63, w = wave_id(), nq = w & 3;
+  MxTile gt;
+  gt.wbase = grp < g.E ? g.layerbuf + (size_t)grp * g.stride : g.shared_w;
+  gt.KC = H / kAtomK;
+  gt.wbytes = (uint32_t)(2 * I / kAtomRows) * (uint32_t)gt.KC * kAtomBytes;
+  gt.k0 = nb * gt.KC / nbn;
+  gt.rows = min(kBM, cnt - m0);
+  for (int i = 0; i < 4; i++) gt.aoff[i] = kOOB;
+  gt.asoff = kOOB;
+  GemmTile wl;
+  clear_loads(wl);
+  if (w < 4) {
+    const int32_t* tok = g.tok + pos0 + m0;
+    set_mx_loads(gt, lane, [&](int r) { return (uint32_t)tok[r] * (uint32_t)H; },
+                 [&](int r) { return (uint32_t)tok[r] * (uint32_t)(H / 32); });
+  } else {
+    wl.KC = gt.KC;
+    set_weight_loads(wl, nb * 32 + 8 * (w - 4), lane, 2 * I / kAtomRows);
+  }
+  for (int t = 0; t < 8; t++) gt.woff[t] = wl.woff[t];
+  gt.soff[0] = wl.soff[0];
+  gt.soff[1] = wl.soff[1];
+  const __amdgpu_buffer_rsrc_t ra = rsrc(xq, xq_bytes), rs = rsrc(xs, xs_bytes);
+  const size_t row0 = (size_t)(pos0 + m0);
+  const int p0 = nb * 16 + 4 * nq;
+#define GUM(N) gateup_tile_mx<N>(gt, ra, rs, lds, hq, hs, I, row0, p0)
+  MOE_MF_SWITCH(wave_mfrags(gt.rows), GUM)
+#undef GUM
+}
+
+// Down on MXFP8 h: tiles as down_prefill_kernel; A rows are the tile's own
+// permuted rows.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void down_mx_kernel(
+    GroupArgs g, const uint8_t* hq, uint32_t hq_bytes, const uint8_t* hs, uint32_t hs_bytes, int H,
+    int I, int nbn, size_t gateup_bytes, float* __restrict__ yperm) {
+  int ti, nb;
+  tile_of_block(nbn, &ti, &nb);
+  if (ti >= *g.n_tiles) return;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsMx];
+  const int2 td = g.tiles[ti];
+  const int grp = td.x, m0 = td.y;
+  const int cnt = g.counts[grp], pos0 = g.offsets[grp];
+  const int lane = threadIdx.x & 63, w = wave_id(), nq = w & 3;
+  const int ngroups = H / kAtomRows;
+  MxTile gt;
+  gt.wbase = (grp < g.E ? g.layerbuf + (size_t)grp * g.stride : g.shared_w) + gateup_bytes;
+  gt.KC = I / kAtomK;
+  gt.wbytes = (uint32_t)ngroups * (uint32_t)gt.KC * kAtomBytes;
+  gt.k0 = nb * gt.KC / nbn;
+  gt.rows = min(kBM, cnt - m0);
+  for (int i = 0; i < 4; i++) gt.aoff[i] = kOOB;
+  gt.asoff = kOOB;
+  GemmTile wl;
+  clear_loads(wl);
+  if (w < 4) {
+    const uint32_t base = (uint32_t)(pos0 + m0);
+    set_mx_loads(gt, lane, [&](int r) { return (base + (uint32_t)r) * (uint32_t)I; },
+                 [&](int r) { return (base + (uint32_t)r) * (uint32_t)(I / 32); });
+  } else {
+    wl.KC = gt.KC;
+    set_weight_loads(wl, nb * 32 + 8 * (w - 4), lane, ngroups);
+  }
+  for (int t = 0; t < 8; t++) gt.woff[t] = wl.woff[t];
+  gt.soff[0] = wl.soff[0];
+  gt.soff[1] = wl.soff[1];
+  const __amdgpu_buffer_rsrc_t ra = rsrc(hq, hq_bytes), rs = rsrc(hs, hs_bytes);
+  const size_t row0 = (size_t)(pos0 + m0);
+  const int rg0 = nb * 32 + 8 * nq;
+#define DNM(N) down_tile_mx<N>(gt, ra, rs, lds, yperm, H, row0, rg0, ngroups)
+  MOE_MF_SWITCH(wave_mfrags(gt.rows), DNM)
+#undef DNM
+}
+
 #undef MOE_MF_SWITCH
 
 template <class T>
@@ -888,7 +1260,7 @@ hipError_t prefill_alloc(Ctx* c) {
 void prefill_free(Ctx* c) {
   if (Prefill* p = c->pf) {
     void* ptrs[] = {p->logits, p->ids, p->gates, p->chunk_cnt, p->counts, p->offsets, p->sorted,
-                    p->inv, p->tok, p->tiles, p->n_tiles, p->h, p->hlo, p->yperm};
+                    p->inv, p->tok, p->tiles, p->n_tiles, p->h, p->hlo, p->yperm, p->xq};
     for (void* q : ptrs)
       if (q) (void)hipFree(q);
     delete p;
@@ -926,6 +1298,29 @@ hipError_t prefill_inspect(Ctx* c, int layer, int32_t* T, int32_t* ids, float* g
   return e;
 }
 
+int prefill_last_mx(const Ctx* c) { return c->pf && c->pf->last_T ? c->pf->last_mx : -1; }
+
+hipError_t prefill_inspect_mx(Ctx* c, int32_t* T, uint8_t* xq, uint8_t* xs, uint8_t* hq,
+                              uint8_t* hs) {
+  *T = c->pf ? c->pf->last_T : 0;
+  if (!c->pf || !*T || !c->pf->last_mx) return hipSuccess;
+  Prefill* p = c->pf;
+  hipError_t e = hipDeviceSynchronize();
+  const moe_config& f = c->cfg;
+  const int H = f.hidden, I = f.inter, k = f.top_k;
+  const size_t rows = (size_t)*T * k + (f.has_shared ? *T : 0);
+  const size_t rows_cap = (size_t)p->Tmax * (k + 1);
+  const uint8_t* h8 = reinterpret_cast<const uint8_t*>(p->h);
+  auto get = [&](void* dst, const void* src, size_t bytes) {
+    if (e == hipSuccess && dst && bytes) e = hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost);
+  };
+  get(xq, p->xq, (size_t)*T * H);
+  get(xs, p->xq + (size_t)p->Tmax * H, (size_t)*T * (H / 32));
+  get(hq, h8, rows * I);
+  get(hs, h8 + rows_cap * I, rows * (I / 32));
+  return e;
+}
+
 hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
                            const float* const* biases, void* const* ys, float* const* y32s,
                            hipStream_t st) {
@@ -935,10 +1330,17 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
     return e;
   }
   Prefill* p = c->pf;
-  p->last_T = T;
-  p->last_layers = n_layers;
   const moe_config& f = c->cfg;
   const int H = f.hidden, I = f.inter, E = f.n_experts, k = f.top_k;
+  const bool mx = c->prefill_format == MOE_PREFILL_MXFP8;
+  if (mx && !p->xq &&
+      (e = hipMalloc((void**)&p->xq, (size_t)p->Tmax * H + (size_t)p->Tmax * (H / 32))) != hipSuccess) {
+    p->xq = nullptr;
+    return e;
+  }
+  p->last_T = T;
+  p->last_layers = n_layers;
+  p->last_mx = mx;
   const size_t layer_bytes = (size_t)E * c->stride;
   const int nchunk = (T + kChunkTokens - 1) / kChunkTokens;
 
@@ -983,9 +1385,16 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
         if (!(tr.ev[i] = timing_event(c))) return hipErrorOutOfMemory;
     auto t0 = [&](int stage) { return timed ? tr.ev[2 * stage] : nullptr; };
     auto t1 = [&](int stage) { return timed ? tr.ev[2 * stage + 1] : nullptr; };
-    // the routing stage runs from the router's start to the dispatch's end
+    // the routing stage runs from its first kernel's start to the dispatch's
+    // end; in the MXFP8 mode it starts with the quantisation of x
+    uint8_t* const xs = p->xq ? p->xq + (size_t)p->Tmax * H : nullptr;
+    if (mx) {
+      const int nblk = T * (H / 32);
+      MOE_LAUNCH(quantize_x_mx_kernel, (nblk + 255) / 256, 256, 0, st, t0(kPfRouting), nullptr, x,
+                 nblk, p->xq, xs);
+    }
     MOE_LAUNCH(router_prefill_kernel, dim3((T + 63) / 64, (E + 63) / 64), 256, 0, st,
-               t0(kPfRouting), nullptr, x, T, H, E, wrt, bias, p->logits);
+               mx ? nullptr : t0(kPfRouting), nullptr, x, T, H, E, wrt, bias, p->logits);
     const TopkArgs ta{E, k, f.renormalize, p->logits, ids, gates, nullptr, nullptr};
     const int nk = (E + 63) / 64, tb = (T + 15) / 16;
     if (nk <= 1) topk_prefill_kernel<1><<<tb, 1024, 0, st>>>(ta, T);
@@ -1004,12 +1413,24 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
     const int nbn_gu = (2 * I + 511) / 512, nbn_dn = (H + 511) / 512;
     const size_t hhi_bytes = (size_t)p->Tmax * (k + 1) * I * 2;
     const size_t hlo_bytes = prefill_lo_bytes(p->Tmax, k, E, I);
-    MOE_LAUNCH(gateup_prefill_kernel, p->max_tiles * nbn_gu, 64 * kGemmWaves, 0, st,
-               t0(kPfGateUp), t1(kPfGateUp), ga, x, (uint32_t)T * H * 2, H, I, nbn_gu, p->h,
-               p->hlo);
-    MOE_LAUNCH(down_prefill_kernel, p->max_tiles * nbn_dn, 64 * kGemmWaves, 0, st, t0(kPfDown),
-               t1(kPfDown), ga, p->h, (uint32_t)hhi_bytes, p->hlo, (uint32_t)hlo_bytes, H, I,
-               nbn_dn, gateup_section_bytes(H, I), p->yperm);
+    if (mx) {
+      const size_t rows_cap = (size_t)p->Tmax * (k + 1);
+      uint8_t* const hq = reinterpret_cast<uint8_t*>(p->h);
+      uint8_t* const hs = hq + rows_cap * I;
+      MOE_LAUNCH(gateup_mx_kernel, p->max_tiles * nbn_gu, 64 * kGemmWaves, 0, st, t0(kPfGateUp),
+                 t1(kPfGateUp), ga, p->xq, (uint32_t)T * H, xs, (uint32_t)(T * (H / 32)), H, I,
+                 nbn_gu, hq, hs);
+      MOE_LAUNCH(down_mx_kernel, p->max_tiles * nbn_dn, 64 * kGemmWaves, 0, st, t0(kPfDown),
+                 t1(kPfDown), ga, hq, (uint32_t)(rows_cap * I), hs, (uint32_t)(rows_cap * (I / 32)),
+                 H, I, nbn_dn, gateup_section_bytes(H, I), p->yperm);
+    } else {
+      MOE_LAUNCH(gateup_prefill_kernel, p->max_tiles * nbn_gu, 64 * kGemmWaves, 0, st,
+                 t0(kPfGateUp), t1(kPfGateUp), ga, x, (uint32_t)T * H * 2, H, I, nbn_gu, p->h,
+                 p->hlo);
+      MOE_LAUNCH(down_prefill_kernel, p->max_tiles * nbn_dn, 64 * kGemmWaves, 0, st, t0(kPfDown),
+                 t1(kPfDown), ga, p->h, (uint32_t)hhi_bytes, p->hlo, (uint32_t)hlo_bytes, H, I,
+                 nbn_dn, gateup_section_bytes(H, I), p->yperm);
+    }
     if ((e = launch_combine_rows(p->yperm, inv, gates, T, k, H, f.has_shared,
                                  (uint16_t*)ys[l], y32s ? y32s[l] : nullptr, st, t0(kPfCombine),
                                  t1(kPfCombine))) != hipSuccess)

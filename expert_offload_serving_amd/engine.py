@@ -94,7 +94,8 @@ class MoEEngine:
     def __init__(self, H: int, I: int, E: int, k: int, n_layers: int = 1,
                  has_shared: bool = False, renormalize: bool = True, max_tokens: int = 16,
                  cache_slots: int = 0, staging_slots: int = 0, max_prefill_tokens: int = 0,
-                 cache_policy: str = "global", weight_format: str = "mxfp4"):
+                 cache_policy: str = "global", weight_format: str = "mxfp4",
+                 prefill_format: str = "bf16"):
         self.H, self.I, self.E, self.k, self.L = H, I, E, k, n_layers
         self.has_shared = bool(has_shared)
         self.max_tokens = max_tokens
@@ -107,7 +108,9 @@ class MoEEngine:
                                 staging_slots=staging_slots,
                                 max_prefill_tokens=max_prefill_tokens,
                                 cache_policy=b.CACHE_POLICIES.index(cache_policy),
-                                weight_format=b.WEIGHT_FORMATS.index(weight_format))
+                                weight_format=b.WEIGHT_FORMATS.index(weight_format),
+                                prefill_format=b.PREFILL_FORMATS.index(prefill_format))
+        self.prefill_format = prefill_format
 
     # ---------------------------------------------------------------- weights
     def set_router(self, layer: int, w_router: np.ndarray):
@@ -156,6 +159,11 @@ class MoEEngine:
         b.moe_prefill_forward(self.ctx, len(xs), xs, T, biases, ys, y32s, stream)
         return ys
 
+    def set_prefill_format(self, fmt: str):
+        """"bf16" (exact) or "mxfp8" (native-MX, quantised activations)."""
+        b.moe_set_prefill_format(self.ctx, fmt)
+        self.prefill_format = fmt
+
     # ------------------------------------------------------------------ cache
     def cache_lookup(self, layer, d_experts, d_n, d_slot, stream=None):
         b.expert_cache_lookup(self.ctx, layer, d_experts, d_n, d_slot, stream)
@@ -176,6 +184,13 @@ class MoEEngine:
         """Routing (ids, gates) and dispatch (counts, offsets, sorted, inv) of
         one layer of the last prefill call."""
         return b.moe_inspect_prefill(self.ctx, layer, self.E, self.k, self.max_prefill_tokens)
+
+    def inspect_prefill_mx(self):
+        """E4M3 codes and E8M0 scale bytes of x and h of the last layer of the
+        last prefill call (MXFP8 mode only); h rows in that layer's permuted
+        order, the shared expert's rows last."""
+        return b.moe_inspect_prefill_mx(self.ctx, self.H, self.I, self.k, self.has_shared,
+                                        self.max_prefill_tokens)
 
     def stats(self) -> dict:
         return b.moe_get_stats(self.ctx)

@@ -100,6 +100,29 @@ enum {
 };
 
 /*
+ * Arithmetic of the prefill expert GEMMs (moe_config.prefill_format).
+ * BF16 (default): bf16 activations, weights dequantised exactly to bf16,
+ * fp32 accumulation, h carried as bf16 plus an fp6 remainder (about 2^-14 of
+ * each 32-block's largest value): the plain layer to within 4e-3 x rms.
+ * MXFP8 (opt-in, this build's native-MX mode): the activations of both
+ * products (x for gate/up, h for down) are block-quantised to MXFP8 (E4M3
+ * elements, one E8M0 scale 2^e per 32 along K with e = floor(log2 amax) - 8,
+ * elements rounded to nearest even and clamped to +-448: the OCP MX v1.0
+ * rule) and multiplied with the MXFP4 weights as stored on the scaled
+ * FP8 x FP4 matrix instructions.  It computes the layer on those quantised
+ * activations (the router still sees the bf16 x): about 5.5% relative rms
+ * and up to about 0.55 x rms max-abs from the plain layer on N(0,1)
+ * activations (two E4M3 roundings), at half the matrix-instruction cost and
+ * half the activation bytes of the bf16 mode.  The pages run
+ * MXFP4 experts (jansverre.net FreeToken article, section "Hvor raskt
+ * kjører modellene?"); quantised activations are this build's reading.
+ */
+enum {
+  MOE_PREFILL_BF16 = 0,
+  MOE_PREFILL_MXFP8 = 1
+};
+
+/*
  * Layer-stack shape and capacities, fixed at moe_create.  The shapes the
  * pages name: many experts with few active per token (DeepSeek-V4-Flash: 6
  * of 256) and an optional always-on shared expert (aiforradalom.hu article,
@@ -128,6 +151,8 @@ typedef struct moe_config {
                               UNSUPPORTED)                                  */
   int32_t cache_policy;    /* MOE_CACHE_GLOBAL (0), _PER_LAYER or _STATIC  */
   int32_t weight_format;   /* MOE_WEIGHTS_MXFP4 (0) or MOE_WEIGHTS_BF16     */
+  int32_t prefill_format;  /* MOE_PREFILL_BF16 (0) or MOE_PREFILL_MXFP8 (MXFP4
+                              weights only); moe_set_prefill_format changes it */
 } moe_config;
 
 /* Counters since creation or the last moe_reset_stats. */
@@ -296,6 +321,13 @@ moe_status moe_prefill_forward(moe_ctx* ctx, int32_t n_layers,
                                float* const* h_y32, void* stream);
 
 /*
+ * (sync) Switch the arithmetic of later moe_prefill_forward calls
+ * (MOE_PREFILL_BF16 or MOE_PREFILL_MXFP8).  Errors: INVALID_ARG (unknown
+ * format), UNSUPPORTED (MXFP8 with bf16 experts).
+ */
+moe_status moe_set_prefill_format(moe_ctx* ctx, int32_t format);
+
+/*
  * Look up n unique experts (ascending, in [0, E)) of one layer in the cache
  * with the moe_layer_forward rule and fill the misses: the cache step of the
  * decode path on its own, for custom pipelines (one global LRU across
@@ -381,6 +413,24 @@ moe_status moe_inspect_dispatch(moe_ctx* ctx, int32_t* h_T, int32_t* h_counts,
 moe_status moe_inspect_prefill(moe_ctx* ctx, int32_t layer, int32_t* h_T, int32_t* h_ids,
                                float* h_gates, int32_t* h_counts, int32_t* h_offsets,
                                int32_t* h_sorted, int32_t* h_inv);
+
+/*
+ * (sync) Copy the block-quantised operands of the LAST layer of the last
+ * moe_prefill_forward call, when that call ran in the MXFP8 mode: h_xq
+ * uint8 [T][H] (E4M3 codes of x), h_xs uint8 [T][H/32] (their E8M0 scale
+ * bytes, exponent + 127), h_hq uint8 [R][I] (E4M3 codes of h = silu(gate) *
+ * up) and h_hs uint8 [R][I/32] (their scale bytes), R = T*k, plus T with a
+ * shared expert.  Row r < T*k of h belongs to pair sorted[r] of that layer
+ * (moe_inspect_prefill); row T*k + t is token t's shared-expert row.  These
+ * are the quantisation decisions the mode takes (OCP MX rule: the block
+ * exponent floor(log2 amax) - 8, elements rounded to nearest even and
+ * clamped to +-448), exposed so that a caller can check them.  Any array
+ * may be NULL.  *h_T receives T (0 if no prefill ran; nothing else is
+ * written then).  Errors: INVALID_ARG (NULL h_T), UNSUPPORTED (the last
+ * call ran in the bf16 mode), HIP.
+ */
+moe_status moe_inspect_prefill_mx(moe_ctx* ctx, int32_t* h_T, uint8_t* h_xq, uint8_t* h_xs,
+                                  uint8_t* h_hq, uint8_t* h_hs);
 
 /* (sync) Read / clear the counters. */
 moe_status moe_get_stats(moe_ctx* ctx, moe_stats* out);

@@ -47,6 +47,16 @@ def e4m3_value(code: int) -> float:
     return s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
 
 
+def dequant_mxfp8(codes: np.ndarray, scale_bytes: np.ndarray) -> np.ndarray:
+    """Values of MXFP8 data: E4M3 codes [..., n] and E8M0 scale bytes
+    [..., n/32] (exponent + 127), each code's value (e4m3_value) times two to
+    its block's exponent.  fp64."""
+    table = np.array([e4m3_value(c) for c in range(256)])
+    codes = np.asarray(codes, dtype=np.uint8)
+    e = np.asarray(scale_bytes, dtype=np.int64) - 127
+    return table[codes] * np.repeat(np.ldexp(1.0, e), 32, axis=-1)
+
+
 def round_e4m3(t: np.ndarray) -> np.ndarray:
     """t rounded to the nearest E4M3 value (ties to even), clamped to
     +-448.  fp64 in and out; every E4M3 value is exact in fp64."""
@@ -117,3 +127,152 @@ def moe_layer_mx(x: np.ndarray, ids: np.ndarray, g: np.ndarray, get_expert, shar
             acc += expert_ffn_mx(xq[t], *shared)
         y[t] = acc
     return y
+
+
+U32 = 2.0 ** -24   # unit roundoff of fp32
+MFMA_ALIGN = 2.0 ** -10
+
+
+def mfma_dot_err(ax: np.ndarray, aw: np.ndarray) -> np.ndarray:
+    """Error allowance of dot products computed as chained 128-term scaled
+    FP8 x FP4 matrix instructions accumulating in fp32: ax [n][K] and aw [I][K]
+    are the operands' magnitudes; returns [n][I].
+
+    Model (measured, not specified by the pages): one instruction's result
+    lies within 2^-10 of its largest product magnitude from the exact sum of
+    its 128 products (measured on gfx950 over 32768 random outputs whose
+    codes span the whole E4M3 range: at most 2^-11.3, 99.9th percentile
+    2^-11.8 -- the instruction aligns its products to the largest one rather
+    than rounding once in fp32), and each add into the fp32 accumulator
+    rounds once (2 u of the running sum of magnitudes per instruction,
+    taken over the whole sum)."""
+    ax = np.asarray(ax, dtype=np.float64)
+    aw = np.asarray(aw, dtype=np.float64)
+    K = ax.shape[-1]
+    out = np.zeros((ax.shape[0], aw.shape[0]))
+    for c in range(0, K, 128):
+        out += np.max(ax[:, None, c:c + 128] * aw[None, :, c:c + 128], axis=-1)
+    nc = (K + 127) // 128
+    return MFMA_ALIGN * out + 2.0 * U32 * nc * (ax @ aw.T)
+
+
+def mx_h_deviation(h: np.ndarray, dh: np.ndarray) -> np.ndarray:
+    """For each element of h (rows of 32-blocks along the last axis), the
+    largest change of its MXFP8-quantised value that a computation of h
+    within +-dh of the exact value can cause: over every block exponent that
+    the perturbed block amax can take and both ends of the element's
+    interval (the rounding is monotone in the value, so its reachable
+    values lie between those of the ends).  Zero where every value in the
+    interval rounds like h itself under the one reachable exponent."""
+    h = np.asarray(h, dtype=np.float64)
+    dh = np.asarray(dh, dtype=np.float64)
+    nb = h.shape[-1] // 32
+    blk = h.shape[:-1] + (nb, 32)
+    hb, db_ = h.reshape(blk), dh.reshape(blk)
+    qb = quantize_mxfp8(h).reshape(blk)
+    lob, hib = hb - db_, hb + db_
+
+    def expo(a):
+        with np.errstate(divide="ignore"):
+            e = np.floor(np.log2(np.where(a > 0, a, 1.0))) - E4M3_EMAX
+        return np.clip(np.where(a > 0, e, -127), -127, 127).astype(np.int64)
+
+    e_lo = expo(np.max(np.maximum(np.abs(hb) - db_, 0.0), axis=-1))
+    e_hi = expo(np.max(np.abs(hb) + db_, axis=-1))
+    dev = np.zeros(blk)
+    # every exponent from the smallest to the largest reachable amax's; a
+    # block with a narrower range repeats its largest
+    for d in range(int(np.max(e_hi - e_lo)) + 1 if e_lo.size else 0):
+        s = np.ldexp(1.0, np.minimum(e_lo + d, e_hi))[..., None]
+        dev = np.maximum(dev, np.maximum(np.abs(round_e4m3(lob / s) * s - qb),
+                                         np.abs(round_e4m3(hib / s) * s - qb)))
+    return dev.reshape(h.shape)
+
+
+SILU_LIP = 1.1   # bound of |d/da (a * sigmoid(a))| over the reals (max ~1.0998)
+
+
+def expert_h_mx(xq, wg, wu, h_rel: float = 2.0 ** -16, dot_err=mfma_dot_err):
+    """h = silu(W_g xq) * (W_u xq) in fp64 for one row xq [H] or a batch [n][H]
+    of already quantised inputs, with dh, the most a kernel computing gate
+    and up within dot_err of the exact sums and h within h_rel of its
+    magnitude on top can be off: the interval whose quantisation decisions
+    mx_h_deviation spans.  Returns (h, dh), [n][I] (or [I] for one row)."""
+    x = np.asarray(xq, dtype=np.float64)
+    one = x.ndim == 1
+    x = np.atleast_2d(x)
+    wg, wu = np.asarray(wg, dtype=np.float64), np.asarray(wu, dtype=np.float64)
+    ax = np.abs(x)
+    a, b = x @ wg.T, x @ wu.T
+    da, db = dot_err(ax, np.abs(wg)), dot_err(ax, np.abs(wu))
+    with np.errstate(over="ignore"):
+        silu = a / (1.0 + np.exp(-a))
+    h = silu * b
+    # |silu(a') b' - silu(a) b| <= L da (|b| + db) + |silu(a)| db for
+    # |a' - a| <= da, |b' - b| <= db; the evaluation error on top is
+    # relative to the computed value
+    dh0 = SILU_LIP * da * (np.abs(b) + db) + np.abs(silu) * db
+    dh = dh0 + h_rel * (np.abs(h) + dh0)
+    return (h[0], dh[0]) if one else (h, dh)
+
+
+def expert_ffn_mx_bound(xq, wg, wu, wd, h_rel: float, dot_err=mfma_dot_err):
+    """Tokens through one expert in the native-MX mode (as expert_ffn_mx, for
+    one row xq [H] or a batch [n][H] of already quantised inputs) with two
+    allowances for a kernel that computes in fp32: flip, per output element,
+    the most that the quantisation decisions on h can move it when gate and
+    up are computed within dot_err of the exact sums and h = silu(gate) * up
+    is evaluated within h_rel of its magnitude on top (expert_h_mx); arith,
+    the error of the down product itself (dot_err of its operands).
+    dot_err(|x|, |W|) gives the allowance of x @ W.T from the operands'
+    magnitudes.  Returns (y, flip, arith), fp64, shaped like xq."""
+    one = np.ndim(xq) == 1
+    h, dh = expert_h_mx(np.atleast_2d(xq), wg, wu, h_rel=h_rel, dot_err=dot_err)
+    wd = np.asarray(wd, dtype=np.float64)
+    hq = quantize_mxfp8(h)
+    awd = np.abs(wd)
+    y = hq @ wd.T
+    flip = mx_h_deviation(h, dh) @ awd.T
+    arith = dot_err(np.abs(hq), awd)
+    if one:
+        return y[0], flip[0], arith[0]
+    return y, flip, arith
+
+
+def moe_layer_mx_bound(x, ids, g, get_expert, shared=None, tokens=None, h_rel: float = 2.0 ** -16,
+                       dot_err=mfma_dot_err):
+    """moe_layer_mx with the allowances of expert_ffn_mx_bound summed over
+    each token's experts (weighted by |g|), plus the fp32 error of combining
+    them ((k + 2) roundings of the sum of the parts' magnitudes).  A kernel
+    of the native-MX mode that computes in fp32 under the stated arithmetic
+    model gives, for every checked element, |y_kernel - y| <= flip + arith.
+    Tokens are grouped by expert so that each expert's products run as one
+    matrix product.  Returns (y, flip, arith), each [T][H] (rows outside
+    tokens NaN)."""
+    T, k = ids.shape
+    H = x.shape[1]
+    rows = np.arange(T) if tokens is None else np.asarray(list(tokens), dtype=np.int64)
+    xq = quantize_mxfp8(np.asarray(x, dtype=np.float64)[rows])
+    n = len(rows)
+    acc, fl, ar, mag = (np.zeros((n, H)) for _ in range(4))
+    sel = ids[rows]
+    for e in np.unique(sel):
+        r, j = np.nonzero(sel == e)
+        ye, fe, ae = expert_ffn_mx_bound(xq[r], *get_expert(int(e)), h_rel=h_rel, dot_err=dot_err)
+        gj = np.asarray(g, dtype=np.float64)[rows[r], j][:, None]
+        np.add.at(acc, r, gj * ye)
+        np.add.at(fl, r, np.abs(gj) * fe)
+        np.add.at(ar, r, np.abs(gj) * ae)
+        np.add.at(mag, r, np.abs(gj * ye))
+    parts = k
+    if shared is not None:
+        ye, fe, ae = expert_ffn_mx_bound(xq, *shared, h_rel=h_rel, dot_err=dot_err)
+        acc += ye
+        fl += fe
+        ar += ae
+        mag += np.abs(ye)
+        parts += 1
+    y, flip, arith = (np.full((T, H), np.nan) for _ in range(3))
+    y[rows], flip[rows] = acc, fl
+    arith[rows] = ar + (parts + 2) * U32 * mag
+    return y, flip, arith

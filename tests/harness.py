@@ -26,18 +26,36 @@ RTOL_Y_DECODE = 1e-3
 # and still far below the 2e-2 contract, so a mis-scaled or misplaced piece
 # of h fails it.
 RTOL_Y_PREFILL = 4e-3
+# The MXFP8 prefill mode against the oracle of the same mode: x's codes are
+# decided exactly as the oracle decides them (bf16 input, power-of-two
+# scale, nearest-even convert); h's can differ where the GPU's fp32 h and the
+# oracle's fp64 h straddle a rounding boundary or a block's amax a power of
+# two.  oracle.mx.moe_layer_mx_bound gives, per output element, the most those
+# decisions and the kernel's fp32 arithmetic can move it; each element is
+# held to its own allowance plus MX_ATOL_RMS x rms(y) for what that model of
+# the arithmetic leaves out (the combine's bf16-free fp32 adds are in it).
+MX_ATOL_RMS = 1e-5
+# ... and against the plain layer: the stated accuracy of that mode on
+# N(0,1) activations.  Two E4M3 roundings (x and h, about 3.6% rms each) give
+# about 5.5% relative rms and up to 0.55 x rms max-abs on the test shapes
+# (oracle.moe_layer_mx against oracle.moe_layer on the CPU).
+RTOL_Y_MX_PLAIN = 0.8
+RRMS_MX_PLAIN = 0.08
 ATOL_G = 1e-6     # gates
 TOL_SUM = 1e-6    # |sum(g) - 1| with renormalisation
 
 
 def oracle_rows(model: "Model", layer: int, xf: np.ndarray, ids: np.ndarray, g: np.ndarray,
-                tokens, workers: Optional[int] = None) -> np.ndarray:
+                tokens, workers: Optional[int] = None, layer_fn=None) -> np.ndarray:
     """Oracle outputs of the listed token rows of one layer, through
     oracle.moe_layer.  Every expert those rows use is dequantised once, and
     the rows are split over worker threads (numpy releases the GIL in the
     dequantisation and in the products; each thread's BLAS keeps to one
     thread), so that a few hundred rows of a 256-expert layer take seconds
-    instead of many minutes.  Returns [len(tokens)][H] in the order given."""
+    instead of many minutes.  layer_fn: the oracle layer to evaluate
+    (oracle.moe_layer by default; oracle.moe_layer_mx for the MXFP8 prefill
+    mode; oracle.mx.moe_layer_mx_bound, whose (y, flip, arith) come back as
+    a tuple).  Returns [len(tokens)][H] in the order given."""
     import concurrent.futures
     from threadpoolctl import threadpool_limits
     tokens = list(tokens)
@@ -52,15 +70,21 @@ def oracle_rows(model: "Model", layer: int, xf: np.ndarray, ids: np.ndarray, g: 
         shared = mats.pop(-1, None)
         chunks = [tokens[i::workers] for i in range(workers) if tokens[i::workers]]
 
+        fn = layer_fn or oracle.moe_layer
+
         def run(rows):
-            return oracle.moe_layer(xf[rows], ids[rows], g[rows], mats.__getitem__,
-                                    shared=shared)
+            return fn(xf[rows], ids[rows], g[rows], mats.__getitem__, shared=shared)
         outs = list(ex.map(run, chunks))
-    y = {}
-    for rows, out in zip(chunks, outs):
-        for i, t in enumerate(rows):
-            y[t] = out[i]
-    return np.stack([y[t] for t in tokens])
+    multi = isinstance(outs[0], tuple)
+    parts = []
+    for m in range(len(outs[0]) if multi else 1):
+        y = {}
+        for rows, out in zip(chunks, outs):
+            o = out[m] if multi else out
+            for i, t in enumerate(rows):
+                y[t] = o[i]
+        parts.append(np.stack([y[t] for t in tokens]))
+    return tuple(parts) if multi else parts[0]
 
 
 def bf16_dev(bits: np.ndarray, device="cuda"):
@@ -115,13 +139,15 @@ class Model:
 
 
 def make_engine(shape: gen.Shape, max_tokens: int, cache_slots: int, staging_slots: int,
-                max_prefill_tokens: int = 0, cache_policy: str = "global"):
+                max_prefill_tokens: int = 0, cache_policy: str = "global",
+                prefill_format: str = "bf16"):
     from expert_offload_serving_amd import MoEEngine
     return MoEEngine(shape.H, shape.I, shape.E, shape.k, n_layers=shape.layers,
                      has_shared=shape.shared, renormalize=shape.renormalize,
                      max_tokens=max_tokens, cache_slots=cache_slots,
                      staging_slots=staging_slots, max_prefill_tokens=max_prefill_tokens,
-                     cache_policy=cache_policy, weight_format=shape.weights)
+                     cache_policy=cache_policy, weight_format=shape.weights,
+                     prefill_format=prefill_format)
 
 
 def check_rounding(y_bf16, y32, what=""):
@@ -129,6 +155,25 @@ def check_rounding(y_bf16, y32, what=""):
     bits = y_bf16.cpu().numpy().view(np.uint16)
     want = gen.f32_to_bf16_bits(y32.cpu().numpy())
     assert np.array_equal(bits, want), f"{what}: bf16 output is not RNE of the fp32 result"
+
+
+def check_y_mx(y_gpu: np.ndarray, ref, what=""):
+    """Element-wise check of the MXFP8 prefill mode against
+    oracle.mx.moe_layer_mx_bound's (y, flip, arith): |y_gpu - y| <= flip +
+    arith + MX_ATOL_RMS x rms(y).  Returns (max |dy| / rms, max allowance /
+    rms, fraction of elements whose |dy| needs the flip allowance)."""
+    y, flip, arith = (np.asarray(a, dtype=np.float64) for a in ref)
+    rms = float(np.sqrt(np.mean(y ** 2)))
+    dy = np.abs(y_gpu.astype(np.float64) - y)
+    base = arith + MX_ATOL_RMS * rms
+    allow = flip + base
+    assert np.all(np.isfinite(y_gpu)), f"{what}: non-finite output"
+    ratio = dy / allow
+    i = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    assert ratio[i] <= 1.0, (f"{what}: element {tuple(int(v) for v in i)} |dy| = {dy[i]:.4g} > "
+                             f"allowance {allow[i]:.4g} (flip {flip[i]:.3g}, arith {arith[i]:.3g}, "
+                             f"rms {rms:.4g})")
+    return float(dy.max() / rms), float(allow.max() / rms), float(np.mean(dy > base))
 
 
 def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, rows=None, what="", rtol=RTOL_Y):
@@ -222,16 +267,110 @@ def small_shape(**kw) -> gen.Shape:
     return replace(base, **kw)
 
 
+# Share of h codes the MXFP8 mode may take differently from the oracle's own
+# choice (each such decision must still lie inside its allowance).  On
+# gfx950 0.02-0.04% of them differ at the test shapes (the instruction's
+# error flips only elements within about 1e-4 of a rounding boundary); a
+# computation with every instruction at its largest measured error would
+# flip about 1%, and a bf16-rounded h about 3%.
+MX_FLIP_SHARE = 0.005
+
+
+def check_mx_decisions(run: "PrefillRun", tokens=None, what=""):
+    """The MXFP8 mode's quantisation decisions on the last layer of the last
+    prefill call, read back with moe_inspect_prefill_mx:
+
+    - x: every scale byte and every element value equal to the oracle's
+      quantisation of the input (the decision is exact on both sides);
+    - h: every element within its allowance, oracle.mx.mx_h_deviation of the
+      oracle's h and expert_h_mx's interval (fp32 gate/up sums under the
+      measured instruction model), and at most MX_FLIP_SHARE of them off the
+      oracle's own choice;
+    - y: the library's output equal, within the down product's and the
+      combine's own arithmetic allowance, to the down product and combine
+      of the h codes the library chose -- the choices are the witness that
+      y is one of the mode's valid outputs.
+
+    Returns (share of h codes off the oracle's choice, max |y - y_w| / rms)."""
+    import concurrent.futures
+    from threadpoolctl import threadpool_limits
+    from oracle import mx as omx
+    sh = run.shape
+    layer = sh.layers - 1
+    T, k = run.T, sh.k
+    toks = list(range(T)) if tokens is None else sorted(tokens)
+    ins = run.eng.inspect_prefill_mx()
+    assert ins["T"] == T
+    xf = gen.bf16_bits_to_f32(run.xb[layer]).astype(np.float64)
+    xq_ref = omx.quantize_mxfp8(xf)
+    assert np.array_equal(ins["xs"].astype(np.int64) - 127, omx.block_exponents(xf)), \
+        f"{what}: x scale bytes differ"
+    xq_gpu = omx.dequant_mxfp8(ins["xq"], ins["xs"])
+    bad = np.argwhere(xq_gpu != xq_ref)
+    assert len(bad) == 0, f"{what}: x codes differ at {bad[:4].tolist()}"
+    _, (_, ids, g) = run.route(layer)
+    perm = oracle.permutation(ids, sh.E)
+    hq = omx.dequant_mxfp8(ins["hq"], ins["hs"])
+    # (row, token, slot) per expert; slot -1 for the shared expert
+    groups = {}
+    for t in toks:
+        for j in range(k):
+            groups.setdefault(int(ids[t, j]), []).append((int(perm["inv"][t * k + j]), t, j))
+        if sh.shared:
+            groups.setdefault(-1, []).append((T * k + t, t, -1))
+
+    def one(item):
+        e, rows = item
+        wg, wu, wd = oexp.dequant_expert(run.model.expert(layer, e))
+        r = np.array([q[0] for q in rows])
+        tt = np.array([q[1] for q in rows])
+        h, dh = omx.expert_h_mx(xq_ref[tt], wg, wu)
+        dev = omx.mx_h_deviation(h, dh)
+        q = omx.quantize_mxfp8(h)
+        off = np.abs(hq[r] - q)
+        wd = wd.astype(np.float64)
+        ye = hq[r] @ wd.T
+        return (e, rows, int(np.sum(off > dev)), int(np.sum(off > 0)), off.size, ye,
+                omx.mfma_dot_err(np.abs(hq[r]), np.abs(wd)))
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with threadpool_limits(1), concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        res = list(ex.map(one, groups.items()))
+    H = sh.H
+    pos = {t: i for i, t in enumerate(toks)}
+    y_w, allow, mag = (np.zeros((len(toks), H)) for _ in range(3))
+    outside = differ = total = 0
+    for e, rows, n_out, n_diff, n, ye, ae in res:
+        outside += n_out
+        differ += n_diff
+        total += n
+        for i, (_, t, j) in enumerate(rows):
+            gj = 1.0 if j < 0 else float(g[t, j])
+            y_w[pos[t]] += gj * ye[i]
+            allow[pos[t]] += abs(gj) * ae[i] + (0.0 if j < 0 else ATOL_G * np.abs(ye[i]))
+            mag[pos[t]] += np.abs(gj * ye[i])
+    assert outside == 0, f"{what}: {outside} of {total} h decisions outside their allowance"
+    share = differ / max(total, 1)
+    assert share <= MX_FLIP_SHARE, f"{what}: {share:.2%} of h codes off the oracle's choice"
+    allow += (k + 3) * 2.0 ** -24 * mag
+    y = run.y32[layer].cpu().numpy()[toks].astype(np.float64)
+    rms = float(np.sqrt(np.mean(y_w ** 2)))
+    d = np.abs(y - y_w)
+    i = np.unravel_index(int(np.argmax(d / allow)), d.shape)
+    assert d[i] <= allow[i], (f"{what}: y at (token {toks[i[0]]}, col {i[1]}) is {d[i]:.4g} from the "
+                              f"down product of the library's own h codes (allowance {allow[i]:.3g})")
+    return share, float(d.max() / rms)
+
+
 class PrefillRun:
     """Prefill of a layer stack: every layer gets its own seeded x [T][H]."""
 
     def __init__(self, shape: gen.Shape, T: int, seed: int = 0, model: Optional[Model] = None,
-                 bias_sets=None):
+                 bias_sets=None, prefill_format: str = "bf16"):
         import torch
         self.shape, self.T = shape, T
         self.model = model or Model(shape, seed)
         self.eng = make_engine(shape, max_tokens=1, cache_slots=0, staging_slots=shape.k,
-                               max_prefill_tokens=T)
+                               max_prefill_tokens=T, prefill_format=prefill_format)
         self.model.load(self.eng)
         L = shape.layers
         self.xb = [gen.tokens(shape, l, 0, T, self.model.seed) for l in range(L)]

@@ -108,24 +108,36 @@ def test_decode_scale_range(case):
     eng.close()
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp8"])
 @pytest.mark.parametrize("case", list(_cases()))
-def test_prefill_scale_range(case):
+def test_prefill_scale_range(case, fmt):
+    """Both prefill modes; the MXFP8 mode is compared with its own oracle
+    (activations quantised by the stated rule) element by element within that
+    oracle's allowance, so that every weight scale byte is still checked."""
+    import oracle.mx
     gu, dn, shift = _cases()[case]
     T = 96
-    print(f"case: prefill scale range {case} T={T}", flush=True)
+    print(f"case: prefill scale range {case} T={T} {fmt}", flush=True)
     m = ScaledModel(SHAPE, seed=32, gu=gu, dn=dn)
     bias = _bias(SHAPE.E, SHAPE.k, T, 200)
-    run = H.PrefillRun(SHAPE, T, seed=32, model=m, bias_sets=[bias])
+    run = H.PrefillRun(SHAPE, T, seed=32, model=m, bias_sets=[bias], prefill_format=fmt)
     run.xb = [gen.tokens_block_scaled(SHAPE, 0, 0, T, shift, m.seed)]
     run.xs = [H.bf16_dev(run.xb[0])]
     run.run()
     xf, ids_ref, g_ref = run.check_routing(0)
     H.check_rounding(run.ys[0], run.y32[0], f"prefill {case}")
-    y_ref = H.oracle_rows(m, 0, xf, ids_ref, g_ref, list(range(T)))
     got = run.y32[0].cpu().numpy()
-    if dn is None:
-        err = H.check_y(got, y_ref, what=f"prefill {case}", rtol=H.RTOL_Y_PREFILL)
+    if fmt == "mxfp8":
+        ref = H.oracle_rows(m, 0, xf, ids_ref, g_ref, list(range(T)),
+                            layer_fn=oracle.mx.moe_layer_mx_bound)
+        err, _, _ = H.check_y_mx(got, ref, what=f"prefill {case} {fmt}")
+        share, _ = H.check_mx_decisions(run, what=f"prefill {case} {fmt}")
+        print(f"  h codes off the oracle's choice: {share:.3%}", flush=True)
     else:
-        err = _check_columns(got, y_ref, H.RTOL_Y_PREFILL, f"prefill {case}")
+        y_ref = H.oracle_rows(m, 0, xf, ids_ref, g_ref, list(range(T)))
+        if dn is None:
+            err = H.check_y(got, y_ref, what=f"prefill {case} {fmt}", rtol=H.RTOL_Y_PREFILL)
+        else:
+            err = _check_columns(got, y_ref, H.RTOL_Y_PREFILL, f"prefill {case} {fmt}")
     print(f"  max err/rms {err:.3e}", flush=True)
     run.close()

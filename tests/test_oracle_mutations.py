@@ -343,6 +343,55 @@ def m_mx_h_not_quantised(mp):
     mp.setattr(omx, "expert_ffn_mx", ffn)
 
 
+def _mx_deviation_variant(upper_only=False, ref_exponent_only=False):
+    def dev_fn(h, dh):
+        h, dh = np.asarray(h, np.float64), np.asarray(dh, np.float64)
+        q_ref = omx.quantize_mxfp8(h)
+        nb = h.shape[-1] // 32
+        hb, db_, qb = (a.reshape(a.shape[:-1] + (nb, 32)) for a in (h, dh, q_ref))
+        dev = np.zeros_like(hb)
+        e_ref = omx.block_exponents(h)
+        amax_lo = np.max(np.maximum(np.abs(hb) - db_, 0.0), axis=-1)
+        amax_hi = np.max(np.abs(hb) + db_, axis=-1)
+        for idx in np.ndindex(e_ref.shape):
+            if ref_exponent_only:
+                es = [int(e_ref[idx])]
+            else:
+                lo_e = -127 if amax_lo[idx] == 0 else int(np.floor(np.log2(amax_lo[idx]))) - 8
+                es = range(max(lo_e, -127), int(np.floor(np.log2(amax_hi[idx]))) - 8 + 1)
+            for e in es:
+                s = np.ldexp(1.0, e)
+                up = np.abs(omx.round_e4m3((hb[idx] + db_[idx]) / s) * s - qb[idx])
+                dn = np.abs(omx.round_e4m3((hb[idx] - db_[idx]) / s) * s - qb[idx])
+                dev[idx] = np.maximum(dev[idx], up if upper_only else np.maximum(up, dn))
+        return dev.reshape(h.shape)
+    return dev_fn
+
+
+def m_mx_bound_upper_end_only(mp):
+    mp.setattr(omx, "mx_h_deviation", _mx_deviation_variant(upper_only=True))
+
+
+def m_mx_bound_fixed_exponent(mp):
+    mp.setattr(omx, "mx_h_deviation", _mx_deviation_variant(ref_exponent_only=True))
+
+
+def m_mx_bound_drops_up_error(mp):
+    def bound(xq, wg, wu, wd, h_rel, dot_err=omx.mfma_dot_err):
+        x = np.atleast_2d(np.asarray(xq, np.float64))
+        wg, wu, wd = (np.asarray(w, np.float64) for w in (wg, wu, wd))
+        a, b = x @ wg.T, x @ wu.T
+        da = dot_err(np.abs(x), np.abs(wg))
+        silu = a / (1.0 + np.exp(-a))
+        h = silu * b
+        dh = omx.SILU_LIP * da * np.abs(b) + h_rel * np.abs(h)
+        hq = omx.quantize_mxfp8(h)
+        out = (hq @ wd.T, omx.mx_h_deviation(h, dh) @ np.abs(wd).T,
+               dot_err(np.abs(hq), np.abs(wd)))
+        return tuple(o[0] for o in out) if np.ndim(xq) == 1 else out
+    mp.setattr(omx, "expert_ffn_mx_bound", bound)
+
+
 # --------------------------------------------------------- pins to run
 MXFP4_PINS = [p_mxfp4.test_e2m1_table_matches_spec_fixture,
               p_mxfp4.test_e2m1_table_matches_bitfield_closed_form,
@@ -370,6 +419,12 @@ MX_PINS = [p_mx.test_e4m3_fields, p_mx.test_round_e4m3_is_nearest_with_ties_to_e
            p_mx.test_block_scale_rule, p_mx.test_quantize_closed_forms,
            p_mx.test_mx_layer_equals_plain_layer_on_representable_inputs,
            p_mx.test_mx_layer_near_plain_layer]
+MX_BOUND_PINS = [p_mx.test_bound_with_zero_allowance_is_the_mx_layer, p_mx.test_mfma_dot_err_closed_form,
+                 lambda: p_mx.test_bound_covers_every_kernel_inside_the_allowance(0),
+                 p_mx.test_bound_covers_the_up_error_when_the_gate_sum_does_not_cancel,
+                 p_mx.test_h_deviation_brute_force_on_small_blocks,
+                 lambda: p_mx.test_decision_allowance_rejects_sloppy_kernels(256, 256),
+                 p_mx.test_layer_bound_sums_the_experts]
 BF16_PINS = [p_bf16.test_ties_go_to_even, p_bf16.test_special_values_match_torch,
              p_bf16.test_random_values_match_torch]
 
@@ -402,6 +457,9 @@ MUTATIONS = [
     (m_mx_no_clamp, MX_PINS),
     (m_mx_block_of_16, MX_PINS),
     (m_mx_h_not_quantised, MX_PINS),
+    (m_mx_bound_upper_end_only, MX_BOUND_PINS),
+    (m_mx_bound_fixed_exponent, MX_BOUND_PINS),
+    (m_mx_bound_drops_up_error, MX_BOUND_PINS),
     (m_bf16_truncates, BF16_PINS),
     (m_bf16_ties_away, BF16_PINS),
 ]
@@ -432,5 +490,5 @@ def test_pins_pass_again_after_the_mutations():
     """monkeypatch restored every module: the plain oracle passes its pins."""
     assert oracle.router.topk is orouter.topk
     for pins in (MXFP4_PINS, ROUTER_PINS, DISPATCH_PINS, EXPERT_PINS, CACHE_PINS, MX_PINS,
-                 BF16_PINS):
+                 MX_BOUND_PINS, BF16_PINS):
         assert not _caught(pins)

@@ -46,6 +46,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # dense fp8 (an fp8 A operand sets the scaled instruction's rate)
 
 # decode steps of the kernel-timing pass
 TIMING_STEPS = 128
@@ -75,6 +76,11 @@ def parse(argv=None):
                          "HIP graph (e.g. 1,4,16; default: none)")
     ap.add_argument("--prefill-steps", type=int, default=3,
                     help="prefill passes of the DeepSeek-V4-Flash-shaped stack (0: skip)")
+    ap.add_argument("--legs", default="headline,a3b,dsv4",
+                    help="workloads to run: the headline decode line and the two context legs "
+                         "(each runs whole; without the headline only the context is printed)")
+    ap.add_argument("--prefill-formats", default="bf16,mxfp8",
+                    help="prefill modes timed on the DeepSeek-V4-Flash-shaped stack")
     ap.add_argument("--dsv4-decode-steps", type=int, default=256,
                     help="T=1 decode steps of the DeepSeek-V4-Flash-shaped stack (0: skip)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -354,10 +360,60 @@ def decode_summary(r, bound="hbm"):
 
 
 # ------------------------------------------------------------ context legs
-def run_dsv4(prefill_steps, decode_steps, decode_warmup, seed=0):
+def time_prefill(eng, sh, T, xs, ys, steps, fmt, name):
+    """steps timed prefill passes of the whole stack in one mode (after one
+    untimed pass): end-to-end rate and the per-stage kernel times."""
+    import torch
+    eng.set_prefill_format(fmt)
+    eng.prefill(xs, ys)
+    torch.cuda.synchronize()
+    eng.reset_stats()
+    eng.set_timing(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        eng.prefill(xs, ys)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    tm = eng.get_timing()
+    eng.set_timing(False)
+    el = t1 - t0
+    layers = steps * sh.layers
+    # algorithmic flops per layer: 3 matrices of H x I per (token, expert),
+    # k routed experts plus the shared one, 2 flops per multiply-add
+    flops_layer = 2 * 3 * sh.H * sh.I * T * (sh.k + (1 if sh.shared else 0))
+    nl = max(tm["n_prefill"], 1)
+    pm = tm["prefill_ms"]
+    gu_ms, dn_ms = pm["gateup"] / nl, pm["down"] / nl
+    gemm_ms = gu_ms + dn_ms
+    tflops = flops_layer / (gemm_ms * 1e9)
+    peak = MFMA_FP8_PEAK_TFLOPS if fmt == "mxfp8" else MFMA_BF16_PEAK_TFLOPS
+    upload = sh.E * sh.expert_bytes() * layers
+    kn = {"bf16": ("gateup_prefill_kernel", "down_prefill_kernel"),
+          "mxfp8": ("gateup_mx_kernel", "down_mx_kernel")}[fmt]
+    return {
+        "workload": name, "format": fmt, "T": T, "layers": sh.layers, "steps": steps,
+        "tokens_per_s_end_to_end": round(T * steps / el, 1),
+        "ms_per_step": round(1e3 * el / steps, 2),
+        "gemm_ms_per_layer": round(gemm_ms, 4),
+        "stage_us_per_layer": {k: round(1e3 * v / nl, 1) for k, v in pm.items()},
+        "gemm_launches": 2 * tm["n_prefill"],
+        "tokens_per_s_gemm_only": round(T / (gemm_ms * 1e-3) / sh.layers, 1),
+        "flops_per_layer": flops_layer,
+        "mfma_tflops": round(tflops, 1),
+        "mfma_peak_tflops": peak,
+        "mfma_frac": round(tflops / peak, 4),
+        kn[0]: {"avg_us": round(1e3 * gu_ms, 1),
+                "tflops": round(2 * flops_layer / 3 / (gu_ms * 1e9), 1)},
+        kn[1]: {"avg_us": round(1e3 * dn_ms, 1),
+                "tflops": round(flops_layer / 3 / (dn_ms * 1e9), 1)},
+        "pcie_h2d_gbs": round(upload / (el * 1e9), 2)}
+
+
+def run_dsv4(prefill_steps, decode_steps, decode_warmup, seed=0, formats=("bf16", "mxfp8")):
     """The DeepSeek-V4-Flash-shaped stack on one engine: prefill of all
-    layers per step (layer uploads included), then T=1 decode through the
-    global LRU (13.4 MB experts: HBM-bound, not cache-resident)."""
+    layers per step (layer uploads included) in each prefill mode, then T=1
+    decode through the global LRU (13.4 MB experts: HBM-bound, not
+    cache-resident)."""
     import torch
     from workload import gen
     wp, wd = gen.WORKLOADS["dsv4_prefill"], gen.WORKLOADS["dsv4_decode"]
@@ -369,47 +425,18 @@ def run_dsv4(prefill_steps, decode_steps, decode_warmup, seed=0):
     if prefill_steps > 0:
         xs = [bf16_dev(gen.tokens(sh, l, 0, T, seed)) for l in range(sh.layers)]
         ys = [torch.empty((T, sh.H), dtype=torch.int16, device="cuda") for _ in range(sh.layers)]
-        eng.prefill(xs, ys)
-        torch.cuda.synchronize()
-        eng.reset_stats()
-        eng.set_timing(True)
-        t0 = time.perf_counter()
-        for _ in range(prefill_steps):
-            eng.prefill(xs, ys)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        tm = eng.get_timing()
-        eng.set_timing(False)
-        el = t1 - t0
-        layers = prefill_steps * sh.layers
-        # algorithmic flops per layer: 3 matrices of H x I per (token, expert),
-        # k routed experts plus the shared one, 2 flops per multiply-add
-        flops_layer = 2 * 3 * sh.H * sh.I * T * (sh.k + (1 if sh.shared else 0))
-        nl = max(tm["n_prefill"], 1)
-        pm = tm["prefill_ms"]
-        gu_ms, dn_ms = pm["gateup"] / nl, pm["down"] / nl
-        gemm_ms = gu_ms + dn_ms
-        tflops = flops_layer / (gemm_ms * 1e9)
-        upload = sh.E * sh.expert_bytes() * layers
-        out["prefill"] = {
-            "workload": wp.name, "T": T, "layers": sh.layers, "steps": prefill_steps,
-            "tokens_per_s_end_to_end": round(T * prefill_steps / el, 1),
-            "ms_per_step": round(1e3 * el / prefill_steps, 2),
-            "gemm_ms_per_layer": round(gemm_ms, 4),
-            "stage_us_per_layer": {k: round(1e3 * v / nl, 1) for k, v in pm.items()},
-            "gemm_launches": 2 * tm["n_prefill"],
-            "tokens_per_s_gemm_only": round(T / (gemm_ms * 1e-3) / sh.layers, 1),
-            "flops_per_layer": flops_layer,
-            "mfma_tflops": round(tflops, 1),
-            "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
-            "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            # matrix-core busy share by counters (profiles/mfma_busy_*.md)
-            "mfma_busy_counters": mfma_busy_from_profile(),
-            "gateup_prefill_kernel": {"avg_us": round(1e3 * gu_ms, 1),
-                                      "tflops": round(2 * flops_layer / 3 / (gu_ms * 1e9), 1)},
-            "down_prefill_kernel": {"avg_us": round(1e3 * dn_ms, 1),
-                                    "tflops": round(flops_layer / 3 / (dn_ms * 1e9), 1)},
-            "pcie_h2d_gbs": round(upload / (el * 1e9), 2)}
+        for fmt in formats:
+            key = "prefill" if fmt == "bf16" else f"prefill_{fmt}"
+            out[key] = time_prefill(eng, sh, T, xs, ys, prefill_steps, fmt, wp.name)
+            log(f"prefill {fmt}: {out[key]['mfma_tflops']} TFLOP/s "
+                f"({out[key]['mfma_frac']:.3f} of {out[key]['mfma_peak_tflops']})")
+        # matrix-core busy share by counters (profiles/mfma_busy_*.md)
+        if "prefill" in out:
+            out["prefill"]["mfma_busy_counters"] = mfma_busy_from_profile()
+        if "prefill_mxfp8" in out:
+            out["prefill_mxfp8"]["mfma_busy_counters"] = mfma_busy_from_profile(
+                ("gateup_mx_kernel", "down_mx_kernel"))
+        eng.set_prefill_format("bf16")
     if decode_steps > 0:
         r = run_decode(wd, 1, decode_steps, decode_warmup, seed, eng=eng)
         out["dsv4_decode_T1"] = decode_summary(r)
@@ -582,15 +609,15 @@ def profile_fields(name):
     return fields
 
 
-def mfma_busy_from_profile():
+def mfma_busy_from_profile(kernels=("gateup_prefill_kernel", "down_prefill_kernel")):
     """Matrix-core busy share (SQ_VALU_MFMA_BUSY_CYCLES per SIMD over
-    GRBM_GUI_ACTIVE per XCD) of the two prefill GEMMs from the committed
-    counter summary, or None."""
+    GRBM_GUI_ACTIVE per XCD) of prefill GEMMs from the committed counter
+    summary, or None."""
     f = profile_fields("mfma_busy_prefill_dsv4_T4096.md")
     if f is None:
         return None
     try:
-        return {k: float(f["busy_" + k]) for k in ("gateup_prefill_kernel", "down_prefill_kernel")}
+        return {k: float(f["busy_" + k]) for k in kernels}
     except (KeyError, ValueError):
         return None
 
@@ -636,71 +663,77 @@ def main():
         print(json.dumps(policy_study(a.policy_study, min(a.warmup or 16, a.policy_study))),
               flush=True)
         return
+    legs = {v.strip() for v in a.legs.split(",") if v.strip()}
+    line = {}
     wl = gen.WORKLOADS[a.workload]
     if a.weights != "mxfp4":
         wl = replace(wl, name=f"{wl.name}_{a.weights}", shape=replace(wl.shape, weights=a.weights))
     W0, K0 = DEFAULT_STEPS.get(a.workload, (32, 512))
     W = W0 if a.warmup is None else a.warmup
     K = K0 if a.steps is None else a.steps
-    T = a.T or max(wl.Ts)
-    sh = wl.shape
-    resize_at = W + K // 2 if wl.resize else None
-    pairs = check_pairs_of(wl, W, K, 0 if a.no_cpu_baseline else a.check_pairs)
-    log(f"headline {wl.name} T={T}: {W} warm-up + {K} timed steps (loading the expert pool)")
-    res = run_decode(wl, T, K, W, distinct=a.distinct, resize_at=resize_at, check_pairs=pairs)
-    log(f"headline done: {res['tokens_per_s']:.1f} tokens/s")
-    kgu, kdn = decode_kernels(T)
-    roof = roofline_entry(kgu, res["gateup_gbs"], res["gateup_us"], res["gateup_bytes"],
-                          res["launches"])
-    roof["traffic"] = traffic_from_profile(kgu, f"{wl.name}_T{T}")
-    roof["other_kernels"] = [roofline_entry(kdn, res["down_gbs"], res["down_us"],
-                                            res["down_bytes"], res["launches"])]
-    roof["layer"] = layer_entry(res)
-    cfg = {"workload": wl.name, "T": T, "H": sh.H, "I": sh.I, "E": sh.E, "k": sh.k,
-           "layers": sh.layers, "shared_expert": sh.shared, "cache_slots": wl.cache_slots,
-           "staging_slots": wl.staging_slots,
-           "weights": ("MXFP4 (E2M1 + E8M0/32)" if sh.weights == "mxfp4" else sh.weights),
-           "zipf_s": wl.zipf_s, "overlap": wl.overlap, "cold_start": True,
-           "expert_records_per_layer": a.distinct or sh.E}
-    if wl.resize:
-        cfg["resize"] = {"to_slots": wl.resize[0][1], "before_step": resize_at}
-    line = {
-        "metric": "MoE-layer decode tokens/s",
-        "value": round(res["tokens_per_s"], 2),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(res["ms_per_step"], 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": cfg,
-        "roofline": roof,
-        "kernel_us_per_layer": res["kernel_us"],
-        "cache": {"hit_rate": round(res["hit_rate"], 4), **{k: res["stats"][k] for k in
-                  ("lookups", "hits", "fills", "bypasses", "evictions", "bytes_d2d")}},
-        "resize": res["resize"] or None,
-        "pcie_h2d_gbs": round(res["h2d_gbs"], 2),
-    }
-    if not a.no_cpu_baseline and res["checked"]:
-        log("oracle on the check pairs")
-        base, parity = cpu_baseline(wl, res["checked"], a.cpu_seconds, a.distinct)
-        line["cpu_baseline"] = base
-        line["parity"] = parity
+    if "headline" in legs:
+        T = a.T or max(wl.Ts)
+        sh = wl.shape
+        resize_at = W + K // 2 if wl.resize else None
+        pairs = check_pairs_of(wl, W, K, 0 if a.no_cpu_baseline else a.check_pairs)
+        log(f"headline {wl.name} T={T}: {W} warm-up + {K} timed steps (loading the expert pool)")
+        res = run_decode(wl, T, K, W, distinct=a.distinct, resize_at=resize_at, check_pairs=pairs)
+        log(f"headline done: {res['tokens_per_s']:.1f} tokens/s")
+        kgu, kdn = decode_kernels(T)
+        roof = roofline_entry(kgu, res["gateup_gbs"], res["gateup_us"], res["gateup_bytes"],
+                              res["launches"])
+        roof["traffic"] = traffic_from_profile(kgu, f"{wl.name}_T{T}")
+        roof["other_kernels"] = [roofline_entry(kdn, res["down_gbs"], res["down_us"],
+                                                res["down_bytes"], res["launches"])]
+        roof["layer"] = layer_entry(res)
+        cfg = {"workload": wl.name, "T": T, "H": sh.H, "I": sh.I, "E": sh.E, "k": sh.k,
+               "layers": sh.layers, "shared_expert": sh.shared, "cache_slots": wl.cache_slots,
+               "staging_slots": wl.staging_slots,
+               "weights": ("MXFP4 (E2M1 + E8M0/32)" if sh.weights == "mxfp4" else sh.weights),
+               "zipf_s": wl.zipf_s, "overlap": wl.overlap, "cold_start": True,
+               "expert_records_per_layer": a.distinct or sh.E}
+        if wl.resize:
+            cfg["resize"] = {"to_slots": wl.resize[0][1], "before_step": resize_at}
+        line.update({
+            "metric": "MoE-layer decode tokens/s",
+            "value": round(res["tokens_per_s"], 2),
+            "unit": "tokens/s",
+            "n_gpus": 1,
+            "steps": K,
+            "warmup": W,
+            "ms_per_step": round(res["ms_per_step"], 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic",
+            "config": cfg,
+            "roofline": roof,
+            "kernel_us_per_layer": res["kernel_us"],
+            "cache": {"hit_rate": round(res["hit_rate"], 4), **{k: res["stats"][k] for k in
+                      ("lookups", "hits", "fills", "bypasses", "evictions", "bytes_d2d")}},
+            "resize": res["resize"] or None,
+            "pcie_h2d_gbs": round(res["h2d_gbs"], 2),
+        })
+        if not a.no_cpu_baseline and res["checked"]:
+            log("oracle on the check pairs")
+            base, parity = cpu_baseline(wl, res["checked"], a.cpu_seconds, a.distinct)
+            line["cpu_baseline"] = base
+            line["parity"] = parity
     if not a.no_context and a.weights == "mxfp4":
-        log("context: 35B-A3B-shaped layer")
-        line["context"] = {"a3b_decode": run_a3b(
-            K if a.steps is not None else DEFAULT_STEPS["a3b_decode"][1],
-            W if a.warmup is not None else DEFAULT_STEPS["a3b_decode"][0],
-            [int(v) for v in a.extra_T.split(",") if v.strip()],
-            [int(v) for v in a.graph_T.split(",") if v.strip()])}
-        if a.prefill_steps > 0 or a.dsv4_decode_steps > 0:
+        ctx = line.setdefault("context", {})
+        if "a3b" in legs:
+            log("context: 35B-A3B-shaped layer")
+            ctx["a3b_decode"] = run_a3b(
+                K if a.steps is not None else DEFAULT_STEPS["a3b_decode"][1],
+                W if a.warmup is not None else DEFAULT_STEPS["a3b_decode"][0],
+                [int(v) for v in a.extra_T.split(",") if v.strip()],
+                [int(v) for v in a.graph_T.split(",") if v.strip()])
+        if "dsv4" in legs and (a.prefill_steps > 0 or a.dsv4_decode_steps > 0):
             log("context: DeepSeek-V4-Flash-shaped stack")
-            line["context"].update(run_dsv4(a.prefill_steps, a.dsv4_decode_steps,
-                                             max(a.dsv4_decode_steps // 4, 1)))
+            ctx.update(run_dsv4(a.prefill_steps, a.dsv4_decode_steps,
+                                max(a.dsv4_decode_steps // 4, 1),
+                                formats=tuple(f for f in a.prefill_formats.split(",") if f)))
     if a.calibrate_copy_mb > 0:
         calibrate_copy(a.calibrate_copy_mb)
     print(json.dumps(line), flush=True)

@@ -113,7 +113,11 @@ enum {
  * activations (the router still sees the bf16 x): about 5.5% relative rms
  * and up to about 0.55 x rms max-abs from the plain layer on N(0,1)
  * activations (two E4M3 roundings), at half the matrix-instruction cost and
- * half the activation bytes of the bf16 mode.  The pages run
+ * half the activation bytes of the bf16 mode.  h is quantised from the
+ * kernel's fp32 values, so an element within rounding error of an E4M3
+ * midpoint (or a block whose amax is within rounding error of a power of
+ * two) may round either way; moe_inspect_prefill_mx exposes the decisions
+ * taken.  The pages run
  * MXFP4 experts (jansverre.net FreeToken article, section "Hvor raskt
  * kjører modellene?"); quantised activations are this build's reading.
  */

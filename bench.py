@@ -267,17 +267,23 @@ def run_decode(wl, T, steps, warmup, seed=0, eng=None, distinct=None, resize_at=
 
     def gbs(nbytes, t_ms):
         return nbytes / (t_ms * 1e6) if t_ms > 0 else None
+    # a call whose copies ran beside the resident experts' kernels launched
+    # gate/up and down twice: per-launch figures count both launches (as
+    # rocprof's per-dispatch averages do); bytes over time is unchanged
+    nlaunch = max(tm["n_decode"] + tm.get("n_decode_split", 0), 1)
     return dict(T=T, steps=steps, elapsed_s=elapsed, tokens_per_s=T * steps / elapsed,
                 ms_per_step=1e3 * elapsed / steps, stats=st,
                 hit_rate=st["hits"] / max(st["lookups"], 1),
-                launches=tm["n_decode"],
+                launches=nlaunch, split_calls=tm.get("n_decode_split", 0), calls=tm["n_decode"],
                 kernel_us={k: round(1e3 * v / nl, 3) for k, v in ms.items()},
-                gateup_us=1e3 * ms["gateup"] / nl, down_us=1e3 * ms["down"] / nl,
-                gateup_bytes=gb / nl, down_bytes=db / nl, layer_bytes=lb / nl,
+                gateup_us=1e3 * ms["gateup"] / nlaunch, down_us=1e3 * ms["down"] / nlaunch,
+                gateup_bytes=gb / nlaunch, down_bytes=db / nlaunch, layer_bytes=lb / nl,
                 layer_us=1e3 * layer_ms / nl,
                 gateup_gbs=gbs(gb, ms["gateup"]), down_gbs=gbs(db, ms["down"]),
                 layer_gbs=gbs(lb, layer_ms),
-                h2d_gbs=st["bytes_h2d"] / (elapsed * 1e9), resize=resize_info, checked=checked)
+                h2d_gbs=st["bytes_h2d"] / (elapsed * 1e9),
+                fill_gbs=gbs(st2["bytes_h2d"], ms["fill"]),
+                resize=resize_info, checked=checked)
 
 
 def run_decode_graph(wl, T, steps, warmup, seed=0):
@@ -351,6 +357,7 @@ def decode_summary(r, bound="hbm"):
     kgu, kdn = decode_kernels(r["T"])
     return {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 4),
             "hit_rate": round(r["hit_rate"], 4), "h2d_gbs": round(r["h2d_gbs"], 2),
+            "fill_kernel_gbs": None if r["fill_gbs"] is None else round(r["fill_gbs"], 2),
             "kernel_us": r["kernel_us"],
             "roofline": [roofline_entry(kgu, r["gateup_gbs"], r["gateup_us"], r["gateup_bytes"],
                                         r["launches"], bound),
@@ -714,6 +721,8 @@ def main():
                       ("lookups", "hits", "fills", "bypasses", "evictions", "bytes_d2d")}},
             "resize": res["resize"] or None,
             "pcie_h2d_gbs": round(res["h2d_gbs"], 2),
+            "copy_overlap": {"split_calls": res["split_calls"], "timed_calls": res["calls"]},
+            "fill_kernel_gbs": None if res["fill_gbs"] is None else round(res["fill_gbs"], 2),
         })
         if not a.no_cpu_baseline and res["checked"]:
             log("oracle on the check pairs")

@@ -37,6 +37,7 @@ class moe_config(ctypes.Structure):
 
 class moe_timing(ctypes.Structure):
     _fields_ = [("n_decode", ctypes.c_int32), ("n_prefill", ctypes.c_int32),
+                ("n_decode_split", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("decode_ms", ctypes.c_double * 6), ("prefill_ms", ctypes.c_double * 4)]
 
 
@@ -75,6 +76,7 @@ _SIGS = {
     "moe_inspect_prefill": (_I32, [_P, _I32, _P, _P, _P, _P, _P, _P, _P]),
     "moe_inspect_prefill_mx": (_I32, [_P, _P, _P, _P, _P, _P]),
     "moe_get_stats": (_I32, [_P, ctypes.POINTER(moe_stats)]),
+    "moe_set_copy_overlap": (_I32, [_P, _I32]),
     "moe_reset_stats": (_I32, [_P]),
     "moe_set_timing": (_I32, [_P, _I32]),
     "moe_get_timing": (_I32, [_P, ctypes.POINTER(moe_timing)]),
@@ -273,6 +275,10 @@ def moe_inspect_prefill_mx(ctx, H: int, I: int, k: int, shared: bool, T_max: int
                 hq=hq[:R * I].reshape(R, I), hs=hs[:R * (I // 32)].reshape(R, I // 32))
 
 
+def moe_set_copy_overlap(ctx, mode: int):
+    _check(lib.moe_set_copy_overlap(ctx, int(mode)), "moe_set_copy_overlap")
+
+
 def moe_get_stats(ctx) -> dict:
     s = moe_stats()
     _check(lib.moe_get_stats(ctx, ctypes.byref(s)), "moe_get_stats")
@@ -291,7 +297,7 @@ def moe_get_timing(ctx) -> dict:
     """Records and summed milliseconds per decode kernel and prefill stage."""
     t = moe_timing()
     _check(lib.moe_get_timing(ctx, ctypes.byref(t)), "moe_get_timing")
-    return dict(n_decode=t.n_decode, n_prefill=t.n_prefill,
+    return dict(n_decode=t.n_decode, n_prefill=t.n_prefill, n_decode_split=t.n_decode_split,
                 decode_ms=dict(zip(DECODE_KERNELS, list(t.decode_ms))),
                 prefill_ms=dict(zip(PREFILL_STAGES, list(t.prefill_ms))))
 

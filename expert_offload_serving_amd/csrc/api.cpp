@@ -74,6 +74,9 @@ void destroy_all(Ctx* c) {
   c->ev_pool.clear();
   if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
   c->copy_stream = nullptr;
+  if (c->ev_routed) (void)hipEventDestroy(c->ev_routed);
+  if (c->ev_resident) (void)hipEventDestroy(c->ev_resident);
+  c->ev_routed = c->ev_resident = nullptr;
 }
 
 // Run fn(i) for i in [0, n) on up to `threads` host threads.
@@ -266,22 +269,51 @@ moe_status decode_forward(Ctx* c, const DecodeScratch& s, int layer, const uint1
                           const float* bias, uint16_t* y, float* y32, int32_t* ids,
                           float* gates, hipStream_t st, bool allow_timing) {
   const moe_config& f = c->cfg;
+  // The resident experts' kernels run beside the copies of the missed ones
+  // when one expert's copy is long (split_fills); not under stream capture,
+  // where the whole call stays on one stream.
+  bool split = c->split_fills;
+  if (split) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    HIPCHK(hipStreamIsCapturing(st, &cs));
+    split = cs == hipStreamCaptureStatusNone;
+  }
   Ctx::TimingRec tr{};
+  tr.split = split;
   const bool timed = allow_timing && c->timing && c->t_decode.size() < kMaxTimingPairs;
   if (timed)
-    for (int i = 0; i < 2 * kDecodeStages; i++)
+    for (int i = 0; i < 2 * (split ? kDecodeTimed : kDecodeStages); i++)
       if (!(tr.ev[i] = timing_event(c))) return fail(MOE_ERR_HIP, "timing event");
   auto t0 = [&](int stage) { return timed ? tr.ev[2 * stage] : nullptr; };
   auto t1 = [&](int stage) { return timed ? tr.ev[2 * stage + 1] : nullptr; };
   const float* wr = c->d_router + (size_t)layer * f.hidden * f.n_experts;
+  const int max_fill = std::min(T * f.top_k, f.n_experts);
   HIPCHK(launch_router(x, T, f.hidden, f.n_experts, wr, bias, s.logits, st, t0(kStRouter),
                        t1(kStRouter)));
   HIPCHK(launch_route_finalize(c, s, layer, T, ids, gates, st, t0(kStFinalize),
                                t1(kStFinalize)));
-  HIPCHK(launch_fill(s.fills, s.meta, std::min(T * f.top_k, f.n_experts), c->rec_bytes, st,
-                     t0(kStFill), t1(kStFill)));
-  HIPCHK(launch_expert_gateup(c, s, x, T, st, t0(kStGateUp), t1(kStGateUp)));
-  HIPCHK(launch_expert_down(c, s, T, st, t0(kStDown), t1(kStDown)));
+  if (split) {
+    // The fills follow finalize on `stream`, so that their workgroups are
+    // placed first; the resident experts run on the internal stream once
+    // the lists exist (its event wait delays them behind the fill's
+    // dispatch); the copied experts run on `stream` after both.
+    HIPCHK(hipEventRecord(c->ev_routed, st));
+    HIPCHK(launch_fill(s.fills, s.meta, max_fill, c->rec_bytes, true, st, t0(kStFill),
+                       t1(kStFill)));
+    HIPCHK(hipStreamWaitEvent(c->copy_stream, c->ev_routed, 0));
+    HIPCHK(launch_expert_gateup(c, s, x, T, kItemsResident, c->copy_stream, t0(kStGateUp),
+                                t1(kStGateUp)));
+    HIPCHK(launch_expert_down(c, s, T, kItemsResident, c->copy_stream, t0(kStDown), t1(kStDown)));
+    HIPCHK(hipEventRecord(c->ev_resident, c->copy_stream));
+    HIPCHK(hipStreamWaitEvent(st, c->ev_resident, 0));
+    HIPCHK(launch_expert_gateup(c, s, x, T, kItemsCopied, st, t0(kStGateUpB), t1(kStGateUpB)));
+    HIPCHK(launch_expert_down(c, s, T, kItemsCopied, st, t0(kStDownB), t1(kStDownB)));
+  } else {
+    HIPCHK(launch_fill(s.fills, s.meta, max_fill, c->rec_bytes, false, st, t0(kStFill),
+                       t1(kStFill)));
+    HIPCHK(launch_expert_gateup(c, s, x, T, kItemsAll, st, t0(kStGateUp), t1(kStGateUp)));
+    HIPCHK(launch_expert_down(c, s, T, kItemsAll, st, t0(kStDown), t1(kStDown)));
+  }
   HIPCHK(launch_combine_rows(s.yperm, s.inv, s.gates, T, f.top_k, f.hidden, f.has_shared, y, y32,
                              st, t0(kStCombine), t1(kStCombine)));
   if (timed) c->t_decode.push_back(tr);
@@ -390,12 +422,21 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   ALLOC(c->d_lookup_ids, (size_t)(E + 1) * 4);
   {
     // default priority (the caller's streams are expected to use it too)
-    const hipError_t es = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking);
+    hipError_t es = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking);
+    // the decode events order work between two streams of this device only:
+    // no timing, no system-scope release
+    const unsigned ef = hipEventDisableTiming | hipEventDisableSystemFence;
+    if (es == hipSuccess) es = hipEventCreateWithFlags(&c->ev_routed, ef);
+    if (es == hipSuccess) es = hipEventCreateWithFlags(&c->ev_resident, ef);
     if (es != hipSuccess) {
       destroy_all(c);
       delete c;
       return fail(MOE_ERR_HIP, std::string("copy stream: ") + hipGetErrorString(es));
     }
+    // decode copies beside the resident experts' kernels once one expert's
+    // copy (hundreds of microseconds at 4 MiB and more over PCIe) dwarfs the
+    // cost of the extra launches and event waits
+    c->split_fills = c->rec_bytes >= kSplitFillMinBytes;
   }
 
   std::vector<int32_t> key(std::max(c->C, 1), -1), order(std::max(c->C, 1)), map((size_t)L * E, -1);
@@ -613,7 +654,7 @@ moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer, const int32_t* d_exp
     return fail(MOE_ERR_CAPACITY, "staging_slots below worst-case bypass count");
   hipStream_t st = (hipStream_t)stream;
   HIPCHK(launch_cache_lookup(c, layer, d_experts, d_n, c->ds.max_unique, d_slot, false, st));
-  HIPCHK(launch_fill(c->ds.fills, c->ds.meta, c->ds.max_unique, c->rec_bytes, st));
+  HIPCHK(launch_fill(c->ds.fills, c->ds.meta, c->ds.max_unique, c->rec_bytes, false, st));
   return MOE_OK;
 }
 
@@ -640,7 +681,7 @@ moe_status expert_cache_fill(moe_ctx* ctx, int32_t layer, const int32_t* h_exper
   HIPCHK(hipMemcpy(c->d_lookup_ids, buf.data(), buf.size() * 4, hipMemcpyHostToDevice));
   HIPCHK(launch_cache_lookup(c, layer, c->d_lookup_ids, c->d_lookup_ids + n, n, c->ds.slotcode,
                              true, st));
-  HIPCHK(launch_fill(c->ds.fills, c->ds.meta, n, c->rec_bytes, st));
+  HIPCHK(launch_fill(c->ds.fills, c->ds.meta, n, c->rec_bytes, false, st));
   HIPCHK(hipStreamSynchronize(st));
   return MOE_OK;
 }
@@ -790,6 +831,14 @@ moe_status moe_inspect_prefill_mx(moe_ctx* ctx, int32_t* h_T, uint8_t* h_xq, uin
   return MOE_OK;
 }
 
+moe_status moe_set_copy_overlap(moe_ctx* ctx, int32_t mode) {
+  if (moe_status s = check_ctx(ctx)) return s;
+  if (mode < -1 || mode > 1) return fail(MOE_ERR_INVALID_ARG, "mode must be -1, 0 or 1");
+  Ctx* c = C_(ctx);
+  c->split_fills = mode == 1 || (mode == -1 && c->rec_bytes >= kSplitFillMinBytes);
+  return MOE_OK;
+}
+
 moe_status moe_get_stats(moe_ctx* ctx, moe_stats* out) {
   if (moe_status s = check_ctx(ctx)) return s;
   if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
@@ -834,25 +883,43 @@ moe_status moe_set_timing(moe_ctx* ctx, int32_t enable) {
 static const int kDecodePreds[kDecodeStages][3] = {
     {-1, -1, -1}, {kStRouter, -1, -1}, {kStFinalize, -1, -1},
     {kStFill, -1, -1}, {kStGateUp, -1, -1}, {kStDown, -1, -1}};
+// a call whose fills run beside the resident experts' kernels
+static const int kDecodeSplitPreds[kDecodeTimed][3] = {
+    {-1, -1, -1}, {kStRouter, -1, -1}, {kStFinalize, -1, -1},
+    {kStFinalize, -1, -1}, {kStGateUp, -1, -1}, {kStDownB, -1, -1},
+    {kStDown, kStFill, -1}, {kStGateUpB, -1, -1}};
 static const int kPrefillPreds[kPrefillStages][3] = {
     {-1, -1, -1}, {kPfRouting, -1, -1}, {kPfGateUp, -1, -1}, {kPfDown, -1, -1}};
 
-// Sum the stage times of the records into ms[0..stages).
+// Time of stage i of record r: its stop minus the latest of its own start
+// and its predecessors' stops.
+static hipError_t stage_ms(const Ctx::TimingRec& r, int i, const int (*preds)[3], double* ms) {
+  float t = 0;
+  hipError_t e = hipEventElapsedTime(&t, r.ev[2 * i], r.ev[2 * i + 1]);
+  for (int j = 0; j < 3 && e == hipSuccess && preds[i][j] >= 0; j++) {
+    float u = 0;
+    e = hipEventElapsedTime(&u, r.ev[2 * preds[i][j] + 1], r.ev[2 * i + 1]);
+    t = std::min(t, u);
+  }
+  *ms = (double)std::max(t, 0.0f);
+  return e;
+}
+
+// Sum the stage times of the records into ms[0..stages); the second parts
+// of a split decode call's expert kernels count to gate/up and down.
 static hipError_t sum_timing(const std::vector<Ctx::TimingRec>& v, int stages,
-                             const int (*preds)[3], double* ms) {
+                             const int (*preds)[3], double* ms, bool decode) {
   for (int i = 0; i < stages; i++) ms[i] = 0.0;
-  for (const auto& r : v)
-    for (int i = 0; i < stages; i++) {
-      float t = 0;
-      hipError_t e = hipEventElapsedTime(&t, r.ev[2 * i], r.ev[2 * i + 1]);
-      for (int j = 0; j < 3 && e == hipSuccess && preds[i][j] >= 0; j++) {
-        float u = 0;
-        e = hipEventElapsedTime(&u, r.ev[2 * preds[i][j] + 1], r.ev[2 * i + 1]);
-        t = std::min(t, u);
-      }
-      if (e != hipSuccess) return e;
-      ms[i] += (double)std::max(t, 0.0f);
+  for (const auto& r : v) {
+    const bool split = decode && r.split;
+    const int (*pr)[3] = split ? kDecodeSplitPreds : preds;
+    for (int i = 0; i < (split ? (int)kDecodeTimed : stages); i++) {
+      double t = 0;
+      if (hipError_t e = stage_ms(r, i, pr, &t)) return e;
+      const int to = i == kStGateUpB ? kStGateUp : i == kStDownB ? kStDown : i;
+      ms[split ? to : i] += t;
     }
+  }
   return hipSuccess;
 }
 
@@ -862,11 +929,14 @@ moe_status moe_get_timing(moe_ctx* ctx, moe_timing* out) {
   Ctx* c = C_(ctx);
   HIPCHK(hipDeviceSynchronize());
   double d[kDecodeStages], p[kPrefillStages];
-  HIPCHK(sum_timing(c->t_decode, kDecodeStages, kDecodePreds, d));
-  HIPCHK(sum_timing(c->t_prefill, kPrefillStages, kPrefillPreds, p));
+  HIPCHK(sum_timing(c->t_decode, kDecodeStages, kDecodePreds, d, true));
+  HIPCHK(sum_timing(c->t_prefill, kPrefillStages, kPrefillPreds, p, false));
+  int n_split = 0;
+  for (const auto& r : c->t_decode) n_split += r.split ? 1 : 0;
   *out = moe_timing{};
   out->n_decode = (int32_t)c->t_decode.size();
   out->n_prefill = (int32_t)c->t_prefill.size();
+  out->n_decode_split = n_split;
   for (int i = 0; i < kDecodeStages; i++) out->decode_ms[i] = d[i];
   for (int i = 0; i < kPrefillStages; i++) out->prefill_ms[i] = p[i];
   c->t_decode.clear();

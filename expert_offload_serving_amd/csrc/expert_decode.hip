@@ -132,17 +132,20 @@ __device__ __forceinline__ void down_epilogue(const f32x4* red, int nw, const Wo
 // registers.
 template <int CPW>
 __global__ __launch_bounds__(1024) void gateup_decode_kernel(
-    const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items_p,
+    const WorkItem* __restrict__ items, int items_cap, const int32_t* __restrict__ lo_p,
+    const int32_t* __restrict__ hi_p,
     const int32_t* __restrict__ tok, const uint16_t* __restrict__ x, uint32_t x_bytes, int H,
     int I, uint16_t* __restrict__ h, size_t lo_plane) {
-  const int item = blockIdx.y;
-  // Both loads at once (the grid covers the largest possible item count and
-  // items[] has that many entries): one memory latency before the weight
-  // loads instead of two.  The exit test reads the whole
-  // item (a real item has cnt >= 1 and a weight pointer) so the compiler
-  // cannot sink the item load below it.
-  const int n_items = *n_items_p;
-  const WorkItem it = items[item];
+  // the launch covers items [*lo_p, *hi_p) of the work list (items_cap
+  // entries; hi <= items_cap)
+  const int item = *lo_p + blockIdx.y;
+  // The item load is issued with the bound loads (clamped into the array,
+  // so that it needs no bound first): one memory latency before the weight
+  // loads instead of two.  The exit
+  // test reads the whole item (a real item has cnt >= 1 and a weight
+  // pointer) so the compiler cannot sink the item load below it.
+  const int n_items = *hi_p;
+  const WorkItem it = items[item < items_cap ? item : items_cap - 1];
   if ((item >= n_items) | (it.cnt < 1) | (it.w == nullptr)) return;
   const int p = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -229,17 +232,20 @@ __global__ __launch_bounds__(1024) void gateup_decode_kernel(
 // h planes.
 template <int CPW>
 __global__ __launch_bounds__(1024) void down_decode_kernel(
-    const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items_p,
+    const WorkItem* __restrict__ items, int items_cap, const int32_t* __restrict__ lo_p,
+    const int32_t* __restrict__ hi_p,
     const uint16_t* __restrict__ h, size_t lo_plane, int H, int I, size_t gateup_bytes,
     float* __restrict__ yperm) {
-  const int item = blockIdx.y;
-  // Both loads at once (the grid covers the largest possible item count and
-  // items[] has that many entries): one memory latency before the weight
-  // loads instead of two.  The exit test reads the whole
-  // item (a real item has cnt >= 1 and a weight pointer) so the compiler
-  // cannot sink the item load below it.
-  const int n_items = *n_items_p;
-  const WorkItem it = items[item];
+  // the launch covers items [*lo_p, *hi_p) of the work list (items_cap
+  // entries; hi <= items_cap)
+  const int item = *lo_p + blockIdx.y;
+  // The item load is issued with the bound loads (clamped into the array,
+  // so that it needs no bound first): one memory latency before the weight
+  // loads instead of two.  The exit
+  // test reads the whole item (a real item has cnt >= 1 and a weight
+  // pointer) so the compiler cannot sink the item load below it.
+  const int n_items = *hi_p;
+  const WorkItem it = items[item < items_cap ? item : items_cap - 1];
   if ((item >= n_items) | (it.cnt < 1) | (it.w == nullptr)) return;
   const int q = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -364,19 +370,22 @@ struct WBf16 {
 // as above.
 template <int CPW, class W>
 __global__ __launch_bounds__(W::kMaxThreads) void gateup_stream_kernel(
-    const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items_p,
+    const WorkItem* __restrict__ items, int items_cap, const int32_t* __restrict__ lo_p,
+    const int32_t* __restrict__ hi_p,
     const int32_t* __restrict__ tok, const uint16_t* __restrict__ x, uint32_t x_bytes, int H,
     int I, uint16_t* __restrict__ h, size_t lo_plane) {
   constexpr int S = CPW < W::kStep ? CPW : W::kStep;  // chunks per step
   constexpr int NS = CPW / S;           // steps
-  const int item = blockIdx.y;
-  // Both loads at once (the grid covers the largest possible item count and
-  // items[] has that many entries): one memory latency before the weight
-  // loads instead of two.  The exit test reads the whole
-  // item (a real item has cnt >= 1 and a weight pointer) so the compiler
-  // cannot sink the item load below it.
-  const int n_items = *n_items_p;
-  const WorkItem it = items[item];
+  // the launch covers items [*lo_p, *hi_p) of the work list (items_cap
+  // entries; hi <= items_cap)
+  const int item = *lo_p + blockIdx.y;
+  // The item load is issued with the bound loads (clamped into the array,
+  // so that it needs no bound first): one memory latency before the weight
+  // loads instead of two.  The exit
+  // test reads the whole item (a real item has cnt >= 1 and a weight
+  // pointer) so the compiler cannot sink the item load below it.
+  const int n_items = *hi_p;
+  const WorkItem it = items[item < items_cap ? item : items_cap - 1];
   if ((item >= n_items) | (it.cnt < 1) | (it.w == nullptr)) return;
   const int p = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -449,19 +458,22 @@ __global__ __launch_bounds__(W::kMaxThreads) void gateup_stream_kernel(
 
 template <int CPW, class W>
 __global__ __launch_bounds__(W::kMaxThreads) void down_stream_kernel(
-    const WorkItem* __restrict__ items, const int32_t* __restrict__ n_items_p,
+    const WorkItem* __restrict__ items, int items_cap, const int32_t* __restrict__ lo_p,
+    const int32_t* __restrict__ hi_p,
     const uint16_t* __restrict__ h, size_t lo_plane, int H, int I, size_t gateup_bytes,
     float* __restrict__ yperm) {
   constexpr int S = CPW < W::kStep ? CPW : W::kStep;
   constexpr int NS = CPW / S;
-  const int item = blockIdx.y;
-  // Both loads at once (the grid covers the largest possible item count and
-  // items[] has that many entries): one memory latency before the weight
-  // loads instead of two.  The exit test reads the whole
-  // item (a real item has cnt >= 1 and a weight pointer) so the compiler
-  // cannot sink the item load below it.
-  const int n_items = *n_items_p;
-  const WorkItem it = items[item];
+  // the launch covers items [*lo_p, *hi_p) of the work list (items_cap
+  // entries; hi <= items_cap)
+  const int item = *lo_p + blockIdx.y;
+  // The item load is issued with the bound loads (clamped into the array,
+  // so that it needs no bound first): one memory latency before the weight
+  // loads instead of two.  The exit
+  // test reads the whole item (a real item has cnt >= 1 and a weight
+  // pointer) so the compiler cannot sink the item load below it.
+  const int n_items = *hi_p;
+  const WorkItem it = items[item < items_cap ? item : items_cap - 1];
   if ((item >= n_items) | (it.cnt < 1) | (it.w == nullptr)) return;
   const int q = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -613,14 +625,25 @@ int down_stream_cpw(int KC) {
 
 }  // namespace
 
-// Work-list rows of the launch grid: the most items a call of T tokens has.
-static int items_for(const Ctx* c, int T) {
-  return std::min(T * c->cfg.top_k, c->cfg.n_experts) + c->cfg.has_shared;
+// Work-list rows of the launch grid: the most items a call of T tokens has
+// in the given part (every unique expert may be resident, or copied), and
+// the device counters that bound the part.
+static int items_for(const Ctx* c, int T, ItemRange part) {
+  const int u = std::min(T * c->cfg.top_k, c->cfg.n_experts);
+  return part == kItemsCopied ? u : u + c->cfg.has_shared;
+}
+static const int32_t* items_lo(const DecodeScratch& s, ItemRange part) {
+  return part == kItemsCopied ? &s.meta->n_items_a : &s.meta->zero;
+}
+static const int32_t* items_hi(const DecodeScratch& s, ItemRange part) {
+  return part == kItemsResident ? &s.meta->n_items_a : &s.meta->n_items;
 }
 
 hipError_t launch_expert_gateup(const Ctx* c, const DecodeScratch& s, const uint16_t* x, int T,
-                                hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  dim3 grid(c->cfg.inter / kAtomRows, items_for(c, T));
+                                ItemRange part, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  dim3 grid(c->cfg.inter / kAtomRows, items_for(c, T, part));
+  const int32_t* lo_p = items_lo(s, part);
+  const int32_t* hi_p = items_hi(s, part);
   const size_t lo = s.lo_plane;
   const int KC = c->cfg.hidden / kAtomK;
   const bool bf16 = c->cfg.weight_format == MOE_WEIGHTS_BF16;
@@ -629,7 +652,7 @@ hipError_t launch_expert_gateup(const Ctx* c, const DecodeScratch& s, const uint
     const int waves = stream_waves(KC, cpw);
 #define GATEUP_S(N, F)                                                                     \
   MOE_LAUNCH((gateup_stream_kernel<N, F>), grid, waves * 64, waves * 2 * 64 * 16, st, ev0, \
-             ev1, s.items, &s.meta->n_items, s.tok, x, (uint32_t)T * c->cfg.hidden * 2,          \
+             ev1, s.items, s.max_items, lo_p, hi_p, s.tok, x, (uint32_t)T * c->cfg.hidden * 2,          \
              c->cfg.hidden, c->cfg.inter, s.h, lo)
 #define GATEUP_F(N) \
   if (bf16) GATEUP_S(N, WBf16); else GATEUP_S(N, WMxfp4);
@@ -645,10 +668,12 @@ hipError_t launch_expert_gateup(const Ctx* c, const DecodeScratch& s, const uint
     return hipGetLastError();
   }
   if (bf16) return hipErrorNotSupported;  // bf16 contexts have max_tokens <= 16
-  const Split sp = split_k(KC, grid.x * grid.y, 4);
+  // the split of the whole list, whichever part this launch covers, so
+  // that an expert's partial sums meet in the same order resident or copied
+  const Split sp = split_k(KC, grid.x * items_for(c, T, kItemsAll), 4);
 #define GATEUP(N)                                                                             \
   MOE_LAUNCH(gateup_decode_kernel<N>, grid, sp.waves * 64, sp.waves * 2 * 64 * 16, st, ev0, ev1, \
-             s.items, &s.meta->n_items, s.tok, x, (uint32_t)T * c->cfg.hidden * 2, c->cfg.hidden,     \
+             s.items, s.max_items, lo_p, hi_p, s.tok, x, (uint32_t)T * c->cfg.hidden * 2, c->cfg.hidden,     \
              c->cfg.inter, s.h, lo)
   switch (sp.cpw) {
     case 1: GATEUP(1); break;
@@ -660,9 +685,11 @@ hipError_t launch_expert_gateup(const Ctx* c, const DecodeScratch& s, const uint
   return hipGetLastError();
 }
 
-hipError_t launch_expert_down(const Ctx* c, const DecodeScratch& s, int T, hipStream_t st,
-                              hipEvent_t ev0, hipEvent_t ev1) {
-  dim3 grid(c->cfg.hidden / (2 * kAtomRows), items_for(c, T));
+hipError_t launch_expert_down(const Ctx* c, const DecodeScratch& s, int T, ItemRange part,
+                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  dim3 grid(c->cfg.hidden / (2 * kAtomRows), items_for(c, T, part));
+  const int32_t* lo_p = items_lo(s, part);
+  const int32_t* hi_p = items_hi(s, part);
   const size_t lo = s.lo_plane;
   const bool bf16 = c->cfg.weight_format == MOE_WEIGHTS_BF16;
   const size_t gub = gateup_section_bytes(c->cfg.hidden, c->cfg.inter, c->cfg.weight_format);
@@ -672,7 +699,7 @@ hipError_t launch_expert_down(const Ctx* c, const DecodeScratch& s, int T, hipSt
     const int waves = stream_waves(KC, cpw);
 #define DOWN_S(N, F)                                                                         \
   MOE_LAUNCH((down_stream_kernel<N, F>), grid, waves * 64, waves * 2 * 64 * 16, st, ev0, ev1, \
-             s.items, &s.meta->n_items, s.h, lo, c->cfg.hidden, c->cfg.inter, gub, s.yperm)
+             s.items, s.max_items, lo_p, hi_p, s.h, lo, c->cfg.hidden, c->cfg.inter, gub, s.yperm)
 #define DOWN_F(N) \
   if (bf16) DOWN_S(N, WBf16); else DOWN_S(N, WMxfp4);
     switch (cpw) {
@@ -687,10 +714,12 @@ hipError_t launch_expert_down(const Ctx* c, const DecodeScratch& s, int T, hipSt
     return hipGetLastError();
   }
   if (bf16) return hipErrorNotSupported;  // bf16 contexts have max_tokens <= 16
-  const Split sp = split_k(KC, grid.x * grid.y, 4);
+  // the split of the whole list, whichever part this launch covers, so
+  // that an expert's partial sums meet in the same order resident or copied
+  const Split sp = split_k(KC, grid.x * items_for(c, T, kItemsAll), 4);
 #define DOWN(N)                                                                             \
   MOE_LAUNCH(down_decode_kernel<N>, grid, sp.waves * 64, sp.waves * 2 * 64 * 16, st, ev0, ev1, \
-             s.items, &s.meta->n_items, s.h, lo, c->cfg.hidden, c->cfg.inter, gub, s.yperm)
+             s.items, s.max_items, lo_p, hi_p, s.h, lo, c->cfg.hidden, c->cfg.inter, gub, s.yperm)
   switch (sp.cpw) {
     case 1: DOWN(1); break;
     case 2: DOWN(2); break;

@@ -71,6 +71,10 @@ struct FillEntry {         // one host-pool -> HBM expert copy
 };
 
 // Small per-call counters kept on the device.
+// Expert record size from which decode runs its copies on the copy stream
+// beside the resident experts' kernels.
+constexpr size_t kSplitFillMinBytes = size_t(4) << 20;
+
 struct DevMeta {
   int32_t T;
   int32_t n_unique;
@@ -78,7 +82,10 @@ struct DevMeta {
   int32_t n_fill;          // copies issued (cache fills + bypasses)
   int32_t n_hit;
   int32_t n_bypass;
-  int32_t pad[2];
+  int32_t zero;            // 0: the first item of the whole list and of the hit part
+  int32_t n_items_a;       // items[0, n_items_a): resident experts and the shared
+                           // one; items[n_items_a, n_items): experts copied by
+                           // this call (fills and bypasses)
 };
 
 // Per-call device arrays of the decode forward, carved out of one buffer
@@ -204,9 +211,14 @@ struct Ctx {
   uint8_t* static_scratch = nullptr;
   int32_t* d_lookup_ids = nullptr;  // [E] for expert_cache_fill
 
-  // internal copy stream of the prefill layer uploads, joined to the
+  // internal stream of the prefill layer uploads and of the decode kernels
+  // of resident experts that run beside a call's fills, joined to the
   // caller's stream by events
   hipStream_t copy_stream = nullptr;
+  bool split_fills = false;         // decode computes resident experts beside the fills
+                                    // (expert records of kSplitFillMinBytes and more)
+  hipEvent_t ev_routed = nullptr;   // decode: the work and fill lists are written
+  hipEvent_t ev_resident = nullptr; // decode: the resident experts are computed
 
   // prefill (allocated on first use)
   int prefill_format = MOE_PREFILL_BF16;
@@ -222,6 +234,7 @@ struct Ctx {
   std::vector<hipEvent_t> ev_pool;  // reused
   struct TimingRec {
     hipEvent_t ev[2 * 8];
+    bool split = false;  // decode call that ran its expert kernels in two parts
   };
   std::vector<TimingRec> t_decode, t_prefill;
   size_t ev_next = 0;
@@ -246,18 +259,23 @@ hipError_t launch_route_finalize(Ctx* c, const DecodeScratch& s, int layer, int 
 hipError_t launch_cache_lookup(Ctx* c, int layer, const int32_t* d_experts,
                                const int32_t* d_n, int n_max, int32_t* d_slot, bool insert,
                                hipStream_t st);
+// confined: the fill runs beside expert kernels (few workgroups, each
+// holding its CU's LDS so that no expert-kernel workgroup shares the CU)
 hipError_t launch_fill(const FillEntry* fills, const DevMeta* meta, int max_fill,
-                       size_t bytes, hipStream_t st, hipEvent_t ev0 = nullptr,
+                       size_t bytes, bool confined, hipStream_t st, hipEvent_t ev0 = nullptr,
                        hipEvent_t ev1 = nullptr);
 hipError_t launch_copy_pairs(const FillEntry* pairs, int n, size_t bytes,
                              hipStream_t st);
 hipError_t launch_probe_copy(const void* src, void* dst, size_t n_bytes,
                              hipStream_t st);
+// Which part of the work list an expert-kernel launch covers: all items,
+// the resident experts and the shared one, or the experts this call copies.
+enum ItemRange { kItemsAll, kItemsResident, kItemsCopied };
 hipError_t launch_expert_gateup(const Ctx* c, const DecodeScratch& s, const uint16_t* x, int T,
-                                hipStream_t st, hipEvent_t ev0 = nullptr,
+                                ItemRange part, hipStream_t st, hipEvent_t ev0 = nullptr,
                                 hipEvent_t ev1 = nullptr);
-hipError_t launch_expert_down(const Ctx* c, const DecodeScratch& s, int T, hipStream_t st,
-                              hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+hipError_t launch_expert_down(const Ctx* c, const DecodeScratch& s, int T, ItemRange part,
+                              hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_combine_rows(const float* yperm, const int32_t* inv, const float* gates, int T,
                                int k, int H, int has_shared, uint16_t* y, float* y32,
                                hipStream_t st, hipEvent_t ev0 = nullptr,
@@ -266,8 +284,12 @@ hipError_t launch_combine_rows(const float* yperm, const int32_t* inv, const flo
 // Next event of the context's timing pool (created on demand; NULL on failure).
 hipEvent_t timing_event(Ctx* c);
 
-// Stages timed per decode call and per prefill layer.
-enum DecodeStage { kStRouter, kStFinalize, kStFill, kStGateUp, kStDown, kStCombine, kDecodeStages };
+// Stages timed per decode call and per prefill layer.  A decode call whose
+// fills run beside the resident experts' kernels times the second part of
+// gate/up and down as stages of their own (kStGateUpB, kStDownB), summed into
+// gate/up and down when reported.
+enum DecodeStage { kStRouter, kStFinalize, kStFill, kStGateUp, kStDown, kStCombine, kDecodeStages,
+                   kStGateUpB = kDecodeStages, kStDownB, kDecodeTimed };
 enum PrefillStage { kPfRouting, kPfGateUp, kPfDown, kPfCombine, kPrefillStages };
 
 // kernel<<<grid, block, shm, st>>>(args...), or with start and stop events

@@ -310,20 +310,38 @@ __global__ __launch_bounds__(kFinalizeThreads) void route_finalize_kernel(Finali
   // reads of s_ids above before the slot codes overwrite them)
   block_lookup(a.la, ls, s_U, n_unique, s_slot);
 
-  // work list for the expert kernels
-  for (int u = tid; u < n_unique; u += nt) {
-    const int code = s_slot[u];
-    const uint8_t* wptr = code >= 0 ? a.la.slots + (size_t)code * a.la.stride
-                                    : a.la.staging_buf + (size_t)(-1 - code) * a.la.stride;
-    const int e = s_U[u];
-    a.items[u] = WorkItem{wptr, s_offsets[e], s_counts[e]};
-    a.slotcode[u] = code;
+  // Work list for the expert kernels: the experts found resident first,
+  // then the shared expert, then the experts this call copies (fills and
+  // bypasses), each part in ascending expert order.  The expert kernels can
+  // then run the first part while the copies are in flight.  One thread per
+  // unique expert (n_unique <= 1024 = blockDim.x).
+  {
+    const int u = tid;
+    const int code = u < n_unique ? s_slot[u] : 0;
+    const bool resident = u < n_unique && code >= 0 && ls.hit[code];
+    const bool copied = u < n_unique && !resident;
+    int both;
+    const int ranks = block_excl_scan((resident ? 1 : 0) | (copied ? 1 << 16 : 0), ls.tmp, &both);
+    const int n_res = both & 0xFFFF;
+    const int n_a = n_res + a.has_shared;
+    if (u < n_unique) {
+      const uint8_t* wptr = code >= 0 ? a.la.slots + (size_t)code * a.la.stride
+                                      : a.la.staging_buf + (size_t)(-1 - code) * a.la.stride;
+      const int e = s_U[u];
+      const int pos = resident ? (ranks & 0xFFFF) : n_a + (ranks >> 16);
+      a.items[pos] = WorkItem{wptr, s_offsets[e], s_counts[e]};
+      a.slotcode[u] = code;
+    }
+    if (a.has_shared) {
+      for (int t = tid; t < T; t += nt) a.tok[nk + t] = t;
+      if (tid == 0) a.items[n_res] = WorkItem{a.shared_w, nk, T};
+    }
+    if (tid == 0) {
+      a.la.meta->n_items = n_unique + a.has_shared;
+      a.la.meta->n_items_a = n_a;
+      a.la.meta->zero = 0;
+    }
   }
-  if (a.has_shared) {
-    for (int t = tid; t < T; t += nt) a.tok[nk + t] = t;
-    if (tid == 0) a.items[n_unique] = WorkItem{a.shared_w, nk, T};
-  }
-  if (tid == 0) a.la.meta->n_items = n_unique + a.has_shared;
 }
 
 // Standalone lookup for expert_cache_lookup / expert_cache_fill.  The list

@@ -192,6 +192,11 @@ class MoEEngine:
         return b.moe_inspect_prefill_mx(self.ctx, self.H, self.I, self.k, self.has_shared,
                                         self.max_prefill_tokens)
 
+    def set_copy_overlap(self, mode: int):
+        """-1 automatic (records of 4 MiB and more), 0 off, 1 on: whether
+        decode copies run beside the resident experts' kernels."""
+        b.moe_set_copy_overlap(self.ctx, mode)
+
     def stats(self) -> dict:
         return b.moe_get_stats(self.ctx)
 

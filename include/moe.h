@@ -267,6 +267,14 @@ moe_status moe_set_layer(moe_ctx* ctx, int32_t layer, const float* h_router,
  *   bits), expert outputs in fp32;
  *   y[t] = sum_j g[t,j] o[t,j] (+ shared expert output), fp32, rounded to
  *   bf16 (nearest, ties to even).  Nothing is synchronised with the host.
+ * When one expert record is at least 4 MiB (its copy takes hundreds of
+ * microseconds), the resident experts and the shared expert are computed on
+ * the context's internal stream while the copies run on `stream`, and the
+ * copied experts are computed on `stream` once their copies have landed;
+ * the internal stream is joined back into `stream` before them, so work
+ * queued on `stream` afterwards sees the call complete.  Outputs and cache state are
+ * the same either way (not under stream capture, where the call stays on
+ * `stream`).
  * d_x: bf16 [T][H].  d_bias: fp32 [T][E] or NULL.  d_y: bf16 [T][H].
  * d_y32: fp32 [T][H] or NULL; when given it also receives y before the bf16
  * rounding.  d_ids (int32 [T][k]) and d_gates (fp32 [T][k]) receive the
@@ -281,13 +289,25 @@ moe_status moe_layer_forward(moe_ctx* ctx, int32_t layer, const void* d_x,
                              void* stream);
 
 /*
+ * Execution order of moe_layer_forward's copies (an execution knob: outputs
+ * and cache state do not depend on it).  mode -1 (the default): copies run
+ * beside the resident experts' kernels when one expert record is at least
+ * 4 MiB; 0: never (fills, then every expert, all on the caller's stream);
+ * 1: always.  The pages stream experts in while the GPU computes (aipolix.com
+ * FreeToken article, fourth paragraph); this applies it within a decode
+ * layer.  Errors: INVALID_ARG (mode outside -1..1).
+ */
+moe_status moe_set_copy_overlap(moe_ctx* ctx, int32_t mode);
+
+/*
  * moe_layer_forward for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  Same arguments, checks, arithmetic and cache behaviour; the
  * per-call device scratch (logits, routing, dispatch, work and fill lists,
  * h, fp32 expert outputs) lives in a fixed 16 MiB device array of the
  * library instead of the context's own buffer, and the call allocates
- * nothing (no hipMalloc, no events; kernel timing is not recorded).  Each
+ * nothing (no hipMalloc, no event creation; kernel timing is not
+ * recorded).  Each
  * GPU holds one such array for the life of the process, resolved at
  * moe_create, and every call on that GPU shares it, so calls that overlap
  * on one GPU (from any context or stream) race; nothing in it needs to
@@ -449,12 +469,19 @@ moe_status moe_reset_stats(moe_ctx* ctx);
  * number of records and the summed milliseconds per kernel, and clears
  * them.  Decode kernels: router, finalize (top-k, dispatch, cache lookup,
  * work list), fill (copies from the pinned pool), gate/up + SwiGLU, down,
- * combine.  Prefill stages, per layer: routing (router start to dispatch
- * end), gate/up GEMM, down GEMM, combine.
+ * combine.  A call that ran its copies beside the resident experts' kernels
+ * (see moe_layer_forward) launches gate/up and down twice; both launches
+ * count to gate/up and down, and n_decode_split counts such calls.  A
+ * kernel's time is its stop minus the later of its start and the stops of
+ * the kernels it waits for.  Prefill stages, per layer: routing (router
+ * start to dispatch end), gate/up GEMM, down GEMM, combine.
  */
 typedef struct moe_timing {
   int32_t n_decode;        /* moe_layer_forward calls recorded              */
   int32_t n_prefill;       /* prefill layers recorded                        */
+  int32_t n_decode_split;  /* of n_decode, calls with two gate/up and down
+                              launches                                       */
+  int32_t reserved;
   double decode_ms[6];     /* router, finalize, fill, gate/up, down, combine */
   double prefill_ms[4];    /* routing, gate/up GEMM, down GEMM, combine      */
 } moe_timing;

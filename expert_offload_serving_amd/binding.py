@@ -77,6 +77,8 @@ _SIGS = {
     "moe_inspect_prefill_mx": (_I32, [_P, _P, _P, _P, _P, _P]),
     "moe_get_stats": (_I32, [_P, ctypes.POINTER(moe_stats)]),
     "moe_set_copy_overlap": (_I32, [_P, _I32]),
+    "moe_set_debug": (_I32, [_P, _I32]),
+    "expert_cache_reset": (_I32, [_P]),
     "moe_reset_stats": (_I32, [_P]),
     "moe_set_timing": (_I32, [_P, _I32]),
     "moe_get_timing": (_I32, [_P, ctypes.POINTER(moe_timing)]),
@@ -277,6 +279,17 @@ def moe_inspect_prefill_mx(ctx, H: int, I: int, k: int, shared: bool, T_max: int
 
 def moe_set_copy_overlap(ctx, mode: int):
     _check(lib.moe_set_copy_overlap(ctx, int(mode)), "moe_set_copy_overlap")
+
+
+DEBUG_SYNC, DEBUG_FAIL_NEXT_FILL = 1, 2
+
+
+def moe_set_debug(ctx, flags: int):
+    _check(lib.moe_set_debug(ctx, int(flags)), "moe_set_debug")
+
+
+def expert_cache_reset(ctx):
+    _check(lib.expert_cache_reset(ctx), "expert_cache_reset")
 
 
 def moe_get_stats(ctx) -> dict:

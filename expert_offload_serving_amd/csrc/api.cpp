@@ -265,6 +265,39 @@ namespace {
 // the caller's stream: router -> finalize (top-k, dispatch, cache lookup,
 // work list, fill list) -> copies of this call's misses from the pinned
 // pool (cache fills and bypasses) -> gate/up + SwiGLU -> down -> combine.
+// The copies of a decode call or a cache fill.  A copy that fails (or the
+// injected failure of MOE_DEBUG_FAIL_NEXT_FILL) leaves slots that name
+// experts whose bytes did not land: the context then refuses cache work
+// until expert_cache_reset.
+static moe_status issue_fill(Ctx* c, const DecodeScratch& s, int max_fill, bool confined,
+                             hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
+  if (c->debug_flags & MOE_DEBUG_FAIL_NEXT_FILL) {
+    c->debug_flags &= ~MOE_DEBUG_FAIL_NEXT_FILL;
+    c->failed = true;
+    return fail(MOE_ERR_HIP,
+                "fill: injected failure, the copies were not issued (expert_cache_reset "
+                "empties the cache)");
+  }
+  const hipError_t e = launch_fill(s.fills, s.meta, max_fill, c->rec_bytes, confined, st, ev0, ev1);
+  if (e != hipSuccess) {
+    c->failed = true;
+    return fail(MOE_ERR_HIP, std::string("fill: ") + hipGetErrorString(e) +
+                                 " (expert_cache_reset empties the cache)");
+  }
+  return MOE_OK;
+}
+
+// MOE_DEBUG_SYNC: wait for the streams a stage used and check for errors,
+// naming the stage.
+static moe_status debug_sync(Ctx* c, hipStream_t st, bool both, bool capturing, const char* stage) {
+  if (!(c->debug_flags & MOE_DEBUG_SYNC) || capturing) return MOE_OK;
+  hipError_t e = hipStreamSynchronize(st);
+  if (e == hipSuccess && both) e = hipStreamSynchronize(c->copy_stream);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, std::string(stage) + ": " + hipGetErrorString(e));
+  return MOE_OK;
+}
+
 moe_status decode_forward(Ctx* c, const DecodeScratch& s, int layer, const uint16_t* x, int T,
                           const float* bias, uint16_t* y, float* y32, int32_t* ids,
                           float* gates, hipStream_t st, bool allow_timing) {
@@ -272,12 +305,10 @@ moe_status decode_forward(Ctx* c, const DecodeScratch& s, int layer, const uint1
   // The resident experts' kernels run beside the copies of the missed ones
   // when one expert's copy is long (split_fills); not under stream capture,
   // where the whole call stays on one stream.
-  bool split = c->split_fills;
-  if (split) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    HIPCHK(hipStreamIsCapturing(st, &cs));
-    split = cs == hipStreamCaptureStatusNone;
-  }
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  HIPCHK(hipStreamIsCapturing(st, &cs));
+  const bool capturing = cs != hipStreamCaptureStatusNone;
+  const bool split = c->split_fills && !capturing;
   Ctx::TimingRec tr{};
   tr.split = split;
   const bool timed = allow_timing && c->timing && c->t_decode.size() < kMaxTimingPairs;
@@ -286,36 +317,46 @@ moe_status decode_forward(Ctx* c, const DecodeScratch& s, int layer, const uint1
       if (!(tr.ev[i] = timing_event(c))) return fail(MOE_ERR_HIP, "timing event");
   auto t0 = [&](int stage) { return timed ? tr.ev[2 * stage] : nullptr; };
   auto t1 = [&](int stage) { return timed ? tr.ev[2 * stage + 1] : nullptr; };
+  auto done = [&](bool both, const char* stage) { return debug_sync(c, st, both, capturing, stage); };
   const float* wr = c->d_router + (size_t)layer * f.hidden * f.n_experts;
   const int max_fill = std::min(T * f.top_k, f.n_experts);
   HIPCHK(launch_router(x, T, f.hidden, f.n_experts, wr, bias, s.logits, st, t0(kStRouter),
                        t1(kStRouter)));
+  if (moe_status r = done(false, "router")) return r;
   HIPCHK(launch_route_finalize(c, s, layer, T, ids, gates, st, t0(kStFinalize),
                                t1(kStFinalize)));
+  if (moe_status r = done(false, "finalize")) return r;
   if (split) {
     // The fills follow finalize on `stream`, so that their workgroups are
     // placed first; the resident experts run on the internal stream once
     // the lists exist (its event wait delays them behind the fill's
     // dispatch); the copied experts run on `stream` after both.
     HIPCHK(hipEventRecord(c->ev_routed, st));
-    HIPCHK(launch_fill(s.fills, s.meta, max_fill, c->rec_bytes, true, st, t0(kStFill),
-                       t1(kStFill)));
+    if (moe_status r = issue_fill(c, s, max_fill, true, st, t0(kStFill), t1(kStFill))) return r;
+    if (moe_status r = done(false, "fill")) return r;
     HIPCHK(hipStreamWaitEvent(c->copy_stream, c->ev_routed, 0));
     HIPCHK(launch_expert_gateup(c, s, x, T, kItemsResident, c->copy_stream, t0(kStGateUp),
                                 t1(kStGateUp)));
+    if (moe_status r = done(true, "gate/up (resident experts)")) return r;
     HIPCHK(launch_expert_down(c, s, T, kItemsResident, c->copy_stream, t0(kStDown), t1(kStDown)));
+    if (moe_status r = done(true, "down (resident experts)")) return r;
     HIPCHK(hipEventRecord(c->ev_resident, c->copy_stream));
     HIPCHK(hipStreamWaitEvent(st, c->ev_resident, 0));
     HIPCHK(launch_expert_gateup(c, s, x, T, kItemsCopied, st, t0(kStGateUpB), t1(kStGateUpB)));
+    if (moe_status r = done(false, "gate/up (copied experts)")) return r;
     HIPCHK(launch_expert_down(c, s, T, kItemsCopied, st, t0(kStDownB), t1(kStDownB)));
+    if (moe_status r = done(false, "down (copied experts)")) return r;
   } else {
-    HIPCHK(launch_fill(s.fills, s.meta, max_fill, c->rec_bytes, false, st, t0(kStFill),
-                       t1(kStFill)));
+    if (moe_status r = issue_fill(c, s, max_fill, false, st, t0(kStFill), t1(kStFill))) return r;
+    if (moe_status r = done(false, "fill")) return r;
     HIPCHK(launch_expert_gateup(c, s, x, T, kItemsAll, st, t0(kStGateUp), t1(kStGateUp)));
+    if (moe_status r = done(false, "gate/up")) return r;
     HIPCHK(launch_expert_down(c, s, T, kItemsAll, st, t0(kStDown), t1(kStDown)));
+    if (moe_status r = done(false, "down")) return r;
   }
   HIPCHK(launch_combine_rows(s.yperm, s.inv, s.gates, T, f.top_k, f.hidden, f.has_shared, y, y32,
                              st, t0(kStCombine), t1(kStCombine)));
+  if (moe_status r = done(false, "combine")) return r;
   if (timed) c->t_decode.push_back(tr);
   return MOE_OK;
 }
@@ -549,9 +590,13 @@ moe_status moe_set_layer(moe_ctx* ctx, int32_t layer, const float* h_router,
 
 // Checks shared by the two decode entry points (messages without
 // allocation).  Returns MOE_OK or the failure to report.
+static const char kFailedMsg[] =
+    "a copy of an expert failed earlier; expert_cache_reset empties the cache";
+
 static moe_status check_forward(Ctx* c, int32_t layer, const void* d_x, int32_t T,
                                 const void* d_y) {
   const moe_config& f = c->cfg;
+  if (c->failed) return fail(MOE_ERR_STATE, kFailedMsg);
   if (layer < 0 || layer >= f.n_layers) return fail(MOE_ERR_INVALID_ARG, "bad layer");
   if (T < 0 || T > f.max_tokens) return fail(MOE_ERR_INVALID_ARG, "T outside [0, max_tokens]");
   if (T == 0) return MOE_OK;
@@ -647,6 +692,7 @@ moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer, const int32_t* d_exp
                                const int32_t* d_n, int32_t* d_slot, void* stream) {
   if (moe_status s = check_ctx(ctx)) return s;
   Ctx* c = C_(ctx);
+  if (c->failed) return fail(MOE_ERR_STATE, kFailedMsg);
   if (layer < 0 || layer >= c->cfg.n_layers || !d_experts || !d_n || !d_slot)
     return fail(MOE_ERR_INVALID_ARG, "bad layer or NULL pointer");
   const int worst_bypass = std::max(0, c->ds.max_unique - fillable_slots(c, layer, false, nullptr));
@@ -654,14 +700,14 @@ moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer, const int32_t* d_exp
     return fail(MOE_ERR_CAPACITY, "staging_slots below worst-case bypass count");
   hipStream_t st = (hipStream_t)stream;
   HIPCHK(launch_cache_lookup(c, layer, d_experts, d_n, c->ds.max_unique, d_slot, false, st));
-  HIPCHK(launch_fill(c->ds.fills, c->ds.meta, c->ds.max_unique, c->rec_bytes, false, st));
-  return MOE_OK;
+  return issue_fill(c, c->ds, c->ds.max_unique, false, st);
 }
 
 moe_status expert_cache_fill(moe_ctx* ctx, int32_t layer, const int32_t* h_experts,
                              int32_t n, void* stream) {
   if (moe_status s = check_ctx(ctx)) return s;
   Ctx* c = C_(ctx);
+  if (c->failed) return fail(MOE_ERR_STATE, kFailedMsg);
   if (layer < 0 || layer >= c->cfg.n_layers || n < 0 || n > c->ds.max_unique ||
       (n > 0 && !h_experts))
     return fail(MOE_ERR_INVALID_ARG, "bad layer, count or NULL list");
@@ -681,7 +727,7 @@ moe_status expert_cache_fill(moe_ctx* ctx, int32_t layer, const int32_t* h_exper
   HIPCHK(hipMemcpy(c->d_lookup_ids, buf.data(), buf.size() * 4, hipMemcpyHostToDevice));
   HIPCHK(launch_cache_lookup(c, layer, c->d_lookup_ids, c->d_lookup_ids + n, n, c->ds.slotcode,
                              true, st));
-  HIPCHK(launch_fill(c->ds.fills, c->ds.meta, n, c->rec_bytes, false, st));
+  if (moe_status r = issue_fill(c, c->ds, n, false, st)) return r;
   HIPCHK(hipStreamSynchronize(st));
   return MOE_OK;
 }
@@ -705,6 +751,7 @@ moe_status expert_cache_resize(moe_ctx* ctx, int32_t new_slots, void* stream) {
   if (moe_status s = check_ctx(ctx)) return s;
   Ctx* c = C_(ctx);
   const int L = c->cfg.n_layers, E = c->cfg.n_experts;
+  if (c->failed) return fail(MOE_ERR_STATE, kFailedMsg);
   if (new_slots < 0 || (int64_t)new_slots > (int64_t)L * E)
     return fail(MOE_ERR_INVALID_ARG, "new_slots outside [0, n_layers*n_experts]");
   if (new_slots > kMaxCacheSlots) return fail(MOE_ERR_UNSUPPORTED, "cache_slots above 4096");
@@ -761,6 +808,28 @@ moe_status expert_cache_resize(moe_ctx* ctx, int32_t new_slots, void* stream) {
   if (C2 < C) arena_trim(c->arena, (size_t)C2 * c->stride);
   c->host_stats.resizes++;
   c->host_stats.bytes_d2d += (uint64_t)plan.moves.size() * c->rec_bytes;
+  return MOE_OK;
+}
+
+moe_status expert_cache_reset(moe_ctx* ctx) {
+  if (moe_status s = check_ctx(ctx)) return s;
+  Ctx* c = C_(ctx);
+  HIPCHK(hipDeviceSynchronize());
+  const int C = std::max(c->C, 1);
+  std::vector<int32_t> key(C, -1), order(C);
+  std::iota(order.begin(), order.end(), 0);  // all empty: slot | (0 << kOrderKeyShift)
+  std::vector<uint64_t> stamp(C, 0);
+  HIPCHK(upload_cache_state(c, key, stamp, order));
+  HIPCHK(hipDeviceSynchronize());
+  c->failed = false;
+  return MOE_OK;
+}
+
+moe_status moe_set_debug(moe_ctx* ctx, int32_t flags) {
+  if (moe_status s = check_ctx(ctx)) return s;
+  if (flags & ~(MOE_DEBUG_SYNC | MOE_DEBUG_FAIL_NEXT_FILL))
+    return fail(MOE_ERR_INVALID_ARG, "unknown debug flag");
+  C_(ctx)->debug_flags = flags;
   return MOE_OK;
 }
 

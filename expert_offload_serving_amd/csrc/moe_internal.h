@@ -241,6 +241,12 @@ struct Ctx {
 
   // host-side counters not tracked on the device
   moe_stats host_stats{};
+
+  // debug switches (MOE_DEBUG_*), and the state after a failed copy: slots
+  // may name experts whose bytes did not land, so cache work is refused
+  // until expert_cache_reset
+  int debug_flags = 0;
+  bool failed = false;
 };
 
 // ---------------------------------------------------------------------------

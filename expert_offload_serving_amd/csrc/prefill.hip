@@ -1341,6 +1341,9 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
   p->last_T = T;
   p->last_layers = n_layers;
   p->last_mx = mx;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if ((e = hipStreamIsCapturing(st, &cs)) != hipSuccess) return e;
+  const bool debug_sync = (c->debug_flags & MOE_DEBUG_SYNC) && cs == hipStreamCaptureStatusNone;
   const size_t layer_bytes = (size_t)E * c->stride;
   const int nchunk = (T + kChunkTokens - 1) / kChunkTokens;
 
@@ -1437,6 +1440,12 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
       return e;
     if (timed) c->t_prefill.push_back(tr);
     if ((e = hipEventRecord(c->ev_compute[b], st)) != hipSuccess) return e;
+    if (debug_sync) {
+      // MOE_DEBUG_SYNC: the layer's work and the next upload have finished
+      if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
+      if ((e = hipStreamSynchronize(c->copy_stream)) != hipSuccess) return e;
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   return hipGetLastError();
 }

@@ -197,6 +197,16 @@ class MoEEngine:
         decode copies run beside the resident experts' kernels."""
         b.moe_set_copy_overlap(self.ctx, mode)
 
+    def set_debug(self, sync: bool = False, fail_next_fill: bool = False):
+        """Synchronise and check every stage; make the next copy step fail
+        (the context then refuses cache work until cache_reset)."""
+        b.moe_set_debug(self.ctx, (b.DEBUG_SYNC if sync else 0) |
+                        (b.DEBUG_FAIL_NEXT_FILL if fail_next_fill else 0))
+
+    def cache_reset(self):
+        """Empty the expert cache (clock and counters kept)."""
+        b.expert_cache_reset(self.ctx)
+
     def stats(self) -> dict:
         return b.moe_get_stats(self.ctx)
 

@@ -404,6 +404,20 @@ moe_status expert_cache_fill(moe_ctx* ctx, int32_t layer,
 moe_status expert_cache_resize(moe_ctx* ctx, int32_t new_slots, void* stream);
 
 /*
+ * (sync) Empty the expert cache: every slot empty, every (layer, expert)
+ * absent (map, keys, stamps and recency order); the clock and the counters
+ * are kept, the host pool and the slot memory are untouched.  A cold
+ * restart of the cache without recreating the context or reloading the
+ * pool: the way back after a failed copy (see moe_set_debug), and usable at
+ * any time.  The pages list early failure reports of the engine, a prefill
+ * that hung on a cold server's first request and a request left queued
+ * without an error (jansverre.net FreeToken article, section "Hva betyr
+ * dette for en vanlig RTX 4090?"); failing loudly and recovering the cache
+ * in place is this build's answer.  Errors: HIP.
+ */
+moe_status expert_cache_reset(moe_ctx* ctx);
+
+/*
  * (sync) Copy the cache state to the host: *h_slots = C always; when
  * capacity >= C also h_key[C] (layer*E + expert, -1 empty), h_stamp[C]
  * (recency number, 0 empty) and *h_clock.  Errors: INVALID_ARG, CAPACITY
@@ -459,6 +473,32 @@ moe_status moe_inspect_prefill_mx(moe_ctx* ctx, int32_t* h_T, uint8_t* h_xq, uin
 /* (sync) Read / clear the counters. */
 moe_status moe_get_stats(moe_ctx* ctx, moe_stats* out);
 moe_status moe_reset_stats(moe_ctx* ctx);
+
+/*
+ * Debug switches (host-initiated; no GPU fault is involved), so that a
+ * failing step is reported rather than left silent (the failure reports
+ * cited at expert_cache_reset).
+ * MOE_DEBUG_SYNC: every stage of moe_layer_forward (router, finalize, fill,
+ *   gate/up, down, combine; both parts of a split call) and every layer of
+ *   moe_prefill_forward is followed by a synchronisation of the streams it
+ *   used and an error check, so that a failing stage is named in the error
+ *   message; results and cache state are bit-identical to an unsynchronised
+ *   run (not under stream capture, where nothing is synchronised).
+ * MOE_DEBUG_FAIL_NEXT_FILL: the next copy step (of moe_layer_forward,
+ *   expert_cache_lookup or expert_cache_fill) issues no copies and fails
+ *   with MOE_ERR_HIP, as a failed copy would, after the lookup has stamped
+ *   and inserted this call's misses.  The flag clears itself.
+ * After any failed copy, injected or real, slots may name experts whose
+ * bytes did not land: moe_layer_forward, moe_layer_forward_noalloc and the
+ * expert_cache_lookup / fill / resize calls return MOE_ERR_STATE until
+ * expert_cache_reset.  expert_cache_snapshot still reads the state.
+ * Errors: INVALID_ARG (unknown flag).
+ */
+enum {
+  MOE_DEBUG_SYNC = 1,
+  MOE_DEBUG_FAIL_NEXT_FILL = 2
+};
+moe_status moe_set_debug(moe_ctx* ctx, int32_t flags);
 
 /*
  * Kernel timing for measurement.  When enabled, every kernel of

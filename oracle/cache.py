@@ -161,5 +161,17 @@ class SlotCache:
         del self.stamp[new_capacity:]
         return moves, evicted
 
+    def reset(self):
+        """Every slot empty, every key absent; the clock and the counters are
+        kept.  A cold restart of the cache without recreating it or reloading
+        the host pool: the recovery after a failed copy, so that no entry
+        whose bytes may not have landed stays resident.  (This build's rule;
+        the pages report only that a cold server could hang.)  Returns the
+        number of entries dropped."""
+        n = sum(1 for k in self.key if k >= 0)
+        self.key = [-1] * self.capacity
+        self.stamp = [0] * self.capacity
+        return n
+
     def snapshot(self):
         return list(self.key), list(self.stamp), self.clock

@@ -234,3 +234,27 @@ def test_resize_brute_force_against_rank_model(E, C, calls):
             r.order = sorted(range(new_C), key=lambda s: (c.key[s] >= 0, c.stamp[s], s))
             for U in subsets[:: max(1, len(subsets) // 4)]:
                 assert c.lookup(0, list(U))[0] == r.lookup(0, list(U))
+
+
+def test_reset_is_a_fresh_cache_at_the_same_clock():
+    """After reset the state equals a new cache whose clock was advanced to
+    the old clock, and every later lookup sequence behaves the same in both
+    (brute force over short traces of a tiny cache)."""
+    import itertools
+    from oracle import SlotCache
+    E, C = 4, 3
+    traces = list(itertools.product([(0,), (1,), (0, 2), (1, 3), (0, 1, 2, 3)], repeat=3))
+    for pre in traces[:40]:
+        for post in traces[::7]:
+            a = SlotCache(C, E)
+            for u in pre:
+                a.lookup(0, list(u))
+            clock = a.clock
+            n_res = sum(1 for k in a.key if k >= 0)
+            assert a.reset() == n_res
+            b = SlotCache(C, E)
+            b.clock = clock
+            assert a.snapshot() == b.snapshot()
+            for u in post:
+                assert a.lookup(0, list(u)) == b.lookup(0, list(u))
+                assert a.snapshot() == b.snapshot()

@@ -228,6 +228,28 @@ def m_resize_evicts_most_recent(mp):
     mp.setattr(ocache.SlotCache, "resize", resize)
 
 
+def m_reset_keeps_most_recent(mp):
+    def reset(self):
+        keep = max(range(self.capacity), key=lambda s: self.stamp[s])
+        k, st = self.key[keep], self.stamp[keep]
+        n = sum(1 for x in self.key if x >= 0)
+        self.key = [-1] * self.capacity
+        self.stamp = [0] * self.capacity
+        self.key[keep], self.stamp[keep] = k, st
+        return n
+    mp.setattr(ocache.SlotCache, "reset", reset)
+
+
+def m_reset_rewinds_clock(mp):
+    good = ocache.SlotCache.reset
+
+    def reset(self):
+        n = good(self)
+        self.clock = 0
+        return n
+    mp.setattr(ocache.SlotCache, "reset", reset)
+
+
 def m_lookup_hits_not_pinned(mp):
     def lookup(self, layer, experts, insert=None):
         # victims may include slots hit earlier in the same call
@@ -414,7 +436,8 @@ CACHE_PINS = [p_cache.test_matches_textbook_lru_when_unique_set_fits,
               lambda: p_cache.test_brute_force_against_recency_list(3, 1, 2, 5),
               p_cache.test_bypass_when_unique_set_exceeds_capacity,
               p_cache.test_resize_invariants, p_cache.test_resize_hand_computed_slot_numbering,
-              lambda: p_cache.test_resize_brute_force_against_rank_model(4, 3, 3)]
+              lambda: p_cache.test_resize_brute_force_against_rank_model(4, 3, 3),
+              p_cache.test_reset_is_a_fresh_cache_at_the_same_clock]
 MX_PINS = [p_mx.test_e4m3_fields, p_mx.test_round_e4m3_is_nearest_with_ties_to_even,
            p_mx.test_block_scale_rule, p_mx.test_quantize_closed_forms,
            p_mx.test_mx_layer_equals_plain_layer_on_representable_inputs,
@@ -451,6 +474,8 @@ MUTATIONS = [
     (m_resize_highest_free_first, CACHE_PINS),
     (m_resize_evicts_most_recent, CACHE_PINS),
     (m_lookup_hits_not_pinned, CACHE_PINS),
+    (m_reset_keeps_most_recent, CACHE_PINS),
+    (m_reset_rewinds_clock, CACHE_PINS),
     (m_lookup_victims_most_recent_first, CACHE_PINS),
     (m_mx_scale_off_by_one, MX_PINS),
     (m_mx_truncates, MX_PINS),

@@ -30,10 +30,15 @@ def bf16_values(bits: np.ndarray) -> np.ndarray:
 
 
 def dequant_expert(w):
-    """Canonical expert (MXFP4 codes and scales, or bf16 matrices) ->
-    (W_g, W_u, W_d) fp32, exact."""
+    """Canonical expert (MXFP4 codes and scales, bf16 matrices, or NVFP4
+    codes, block scales and matrix scales) -> (W_g, W_u, W_d), exact (fp32
+    for MXFP4 and bf16, fp64 for NVFP4)."""
     if hasattr(w, "wg"):
         return bf16_values(w.wg), bf16_values(w.wu), bf16_values(w.wd)
+    if hasattr(w, "tg"):
+        from . import nvfp4
+        return (nvfp4.dequant(w.qg, w.sg, w.tg), nvfp4.dequant(w.qu, w.su, w.tu),
+                nvfp4.dequant(w.qd, w.sd, w.td))
     return dequant(w.qg, w.sg), dequant(w.qu, w.su), dequant(w.qd, w.sd)
 
 

@@ -17,6 +17,7 @@ from oracle import dispatch as odispatch
 from oracle import experts as oexperts
 from oracle import mx as omx
 from oracle import mxfp4 as omxfp4
+from oracle import nvfp4 as onvfp4
 from oracle import router as orouter
 from workload import gen
 
@@ -26,6 +27,7 @@ from tests import test_oracle_dispatch as p_dispatch
 from tests import test_oracle_experts as p_experts
 from tests import test_oracle_mx as p_mx
 from tests import test_oracle_mxfp4 as p_mxfp4
+from tests import test_oracle_nvfp4 as p_nvfp4
 from tests import test_oracle_router as p_router
 
 
@@ -414,6 +416,24 @@ def m_mx_bound_drops_up_error(mp):
     mp.setattr(omx, "expert_ffn_mx_bound", bound)
 
 
+def m_nv_block_of_32(mp):
+    def dequant(packed, scales, matrix_scale):
+        vals = omxfp4.decode_e2m1(omxfp4.unpack_nibbles(packed)).astype(np.float64)
+        s = np.repeat(onvfp4.e4m3_values(scales)[..., ::2], 32, axis=-1)
+        return vals * s * float(np.float32(matrix_scale))
+    mp.setattr(onvfp4, "dequant", dequant)
+
+
+def m_nv_matrix_scale_ignored(mp):
+    good = onvfp4.dequant
+    mp.setattr(onvfp4, "dequant", lambda p, s, t: good(p, s, 1.0))
+
+
+def m_nv_e4m3_mantissa_dropped(mp):
+    good = onvfp4.e4m3_values
+    mp.setattr(onvfp4, "e4m3_values", lambda c: good(np.asarray(c) & 0xF8))
+
+
 # --------------------------------------------------------- pins to run
 MXFP4_PINS = [p_mxfp4.test_e2m1_table_matches_spec_fixture,
               p_mxfp4.test_e2m1_table_matches_bitfield_closed_form,
@@ -448,6 +468,11 @@ MX_BOUND_PINS = [p_mx.test_bound_with_zero_allowance_is_the_mx_layer, p_mx.test_
                  p_mx.test_h_deviation_brute_force_on_small_blocks,
                  lambda: p_mx.test_decision_allowance_rejects_sloppy_kernels(256, 256),
                  p_mx.test_layer_bound_sums_the_experts]
+NV_PINS = [p_nvfp4.test_e4m3_decoding_matches_torch_float8,
+           p_nvfp4.test_block_of_16_and_matrix_scale,
+           p_nvfp4.test_power_of_two_scales_reduce_to_mxfp4,
+           p_nvfp4.test_mantissa_scales_are_exact_products,
+           p_nvfp4.test_expert_dequant_uses_each_matrix_scale]
 BF16_PINS = [p_bf16.test_ties_go_to_even, p_bf16.test_special_values_match_torch,
              p_bf16.test_random_values_match_torch]
 
@@ -485,6 +510,9 @@ MUTATIONS = [
     (m_mx_bound_upper_end_only, MX_BOUND_PINS),
     (m_mx_bound_fixed_exponent, MX_BOUND_PINS),
     (m_mx_bound_drops_up_error, MX_BOUND_PINS),
+    (m_nv_block_of_32, NV_PINS),
+    (m_nv_matrix_scale_ignored, NV_PINS),
+    (m_nv_e4m3_mantissa_dropped, NV_PINS),
     (m_bf16_truncates, BF16_PINS),
     (m_bf16_ties_away, BF16_PINS),
 ]
@@ -515,5 +543,5 @@ def test_pins_pass_again_after_the_mutations():
     """monkeypatch restored every module: the plain oracle passes its pins."""
     assert oracle.router.topk is orouter.topk
     for pins in (MXFP4_PINS, ROUTER_PINS, DISPATCH_PINS, EXPERT_PINS, CACHE_PINS, MX_PINS,
-                 MX_BOUND_PINS, BF16_PINS):
+                 MX_BOUND_PINS, NV_PINS, BF16_PINS):
         assert not _caught(pins)

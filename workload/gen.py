@@ -40,13 +40,16 @@ class Shape:
     layers: int = 1
     shared: bool = False      # one always-on shared expert per layer
     renormalize: bool = True  # renormalise the top-k gates to sum to 1
-    weights: str = "mxfp4"    # expert format: "mxfp4" or "bf16"
+    weights: str = "mxfp4"    # expert format: "mxfp4", "bf16" or "nvfp4"
 
     def expert_bytes(self) -> int:
-        """Bytes of one expert: 3 matrices, MXFP4 (4 bits + 8 bits per 32)
-        or bf16 (16 bits)."""
+        """Bytes of one expert record in the library: 3 matrices, MXFP4 (4
+        bits + 8 bits per 32), bf16 (16 bits) or NVFP4 (4 bits + 8 bits per
+        16, and a 16-byte trailer holding the three fp32 matrix scales)."""
         if self.weights == "bf16":
             return 3 * self.H * self.I * 2
+        if self.weights == "nvfp4":
+            return 3 * self.H * self.I * 9 // 16 + 16
         return 3 * self.H * self.I * 17 // 32
 
 
@@ -219,10 +222,52 @@ def expert_weights_bf16(shape: Shape, layer: int, expert: int, seed: int = 0,
                              wd=w[2 * n:].reshape(H, I))
 
 
+@dataclass
+class ExpertWeightsNV:
+    """Canonical NVFP4 expert: E2M1 codes qg, qu [I][H/2], qd [H][I/2] (as
+    MXFP4); E4M3 block-scale bytes sg, su [I][H/16], sd [H][I/16]; fp32
+    matrix scales tg, tu, td."""
+    qg: np.ndarray
+    qu: np.ndarray
+    qd: np.ndarray
+    sg: np.ndarray
+    su: np.ndarray
+    sd: np.ndarray
+    tg: np.float32
+    tu: np.float32
+    td: np.float32
+
+
+# E4M3 block-scale codes drawn: exponent fields 3..6 (2^-4 .. 2^-1) with any
+# mantissa, so blocks span 0.0625 .. 0.9375; with matrix scales in [0.25,
+# 0.5) the weights sit near the MXFP4 draws' magnitude (up to 6 * 2^-4)
+NV_SCALE_CODES = np.arange(3 << 3, 7 << 3, dtype=np.uint8)
+
+
+def expert_weights_nvfp4(shape: Shape, layer: int, expert: int, seed: int = 0,
+                         scale_codes: np.ndarray = NV_SCALE_CODES) -> ExpertWeightsNV:
+    """Uniform 4-bit codes, E4M3 block scales uniform over scale_codes, fp32
+    matrix scales uniform in [0.25, 0.5).  ``expert = -1`` draws the shared
+    expert."""
+    H, I = shape.H, shape.I
+    g = _rng(seed, _SHARED if expert < 0 else _EXPERT, layer, max(expert, 0), 4)
+    q = g.integers(0, 256, size=3 * H * I // 2, dtype=np.uint8)
+    sc = g.choice(np.asarray(scale_codes, dtype=np.uint8), size=3 * H * I // 16)
+    t = (0.25 + 0.25 * g.random(3)).astype(np.float32)
+    n2, n16 = H * I // 2, H * I // 16
+    return ExpertWeightsNV(
+        qg=q[:n2].reshape(I, H // 2), qu=q[n2:2 * n2].reshape(I, H // 2),
+        qd=q[2 * n2:].reshape(H, I // 2),
+        sg=sc[:n16].reshape(I, H // 16), su=sc[n16:2 * n16].reshape(I, H // 16),
+        sd=sc[2 * n16:].reshape(H, I // 16), tg=t[0], tu=t[1], td=t[2])
+
+
 def expert_weights_of(shape: Shape, layer: int, expert: int, seed: int = 0):
     """The expert in the shape's weight format."""
     if shape.weights == "bf16":
         return expert_weights_bf16(shape, layer, expert, seed)
+    if shape.weights == "nvfp4":
+        return expert_weights_nvfp4(shape, layer, expert, seed)
     return expert_weights(shape, layer, expert, seed)
 
 

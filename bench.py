@@ -85,7 +85,7 @@ def parse(argv=None):
                     help="T=1 decode steps of the DeepSeek-V4-Flash-shaped stack (0: skip)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="also run one plain copy of this many MiB (counter calibration)")
-    ap.add_argument("--weights", choices=("mxfp4", "bf16"), default="mxfp4",
+    ap.add_argument("--weights", choices=("mxfp4", "bf16", "nvfp4"), default="mxfp4",
                     help="expert format of the headline workload (bf16: decode of up to 16 "
                          "tokens; no context legs)")
     ap.add_argument("--policy-study", type=int, default=0, metavar="STEPS",

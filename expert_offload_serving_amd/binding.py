@@ -143,7 +143,7 @@ def moe_expert_bytes(hidden: int, inter: int) -> int:
 # moe_config.cache_policy values, in enum order (MOE_CACHE_GLOBAL, ...)
 CACHE_POLICIES = ("global", "per_layer", "static")
 # moe_config.weight_format values, in enum order (MOE_WEIGHTS_MXFP4, ...)
-WEIGHT_FORMATS = ("mxfp4", "bf16")
+WEIGHT_FORMATS = ("mxfp4", "bf16", "nvfp4")
 
 
 def moe_create(**fields) -> int:

@@ -1,6 +1,7 @@
 // C-ABI entry points of libmoe: validation, memory ownership, cache state,
 // and the launch sequence of the decode forward.
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -244,11 +245,51 @@ void repack_down_bf16(const uint16_t* wd, int H, int I, uint8_t* out) {
   });
 }
 
+// NVFP4 [N][K] matrix: codes as MXFP4 (lane l: row row0 + l % 16, K block
+// of 32 number 4 c + l / 16); its two E4M3 block scales of 16 from s[r][K/16]
+// at 1024 + 2 l.
+static void write_atom_nv(const uint8_t* q, const uint8_t* s, int K, int row0, int c,
+                          uint8_t* atom) {
+  const int kc = K / 2, sc = K / 16;
+  for (int l = 0; l < 64; l++) {
+    const int r = row0 + (l % 16), blk = c * 4 + l / 16;
+    std::memcpy(atom + l * 16, q + (size_t)r * kc + (size_t)blk * 16, 16);
+    atom[kAtomData + 2 * l] = s[(size_t)r * sc + 2 * blk];
+    atom[kAtomData + 2 * l + 1] = s[(size_t)r * sc + 2 * blk + 1];
+  }
+}
+
+static void repack_nv(const uint8_t* qg, const uint8_t* sg, const uint8_t* qu, const uint8_t* su,
+                      const uint8_t* qd, const uint8_t* sd, int H, int I, uint8_t* rec) {
+  const int KCg = H / kAtomK, KCd = I / kAtomK;
+  const int threads = (size_t)I * H > (1 << 22) ? host_threads() : 1;
+  parallel_for(2 * I / kAtomRows, threads, [&](int rg) {
+    const bool up = rg & 1;
+    for (int c = 0; c < KCg; c++)
+      write_atom_nv(up ? qu : qg, up ? su : sg, H, (rg / 2) * kAtomRows, c,
+                    rec + ((size_t)rg * KCg + c) * kAtomBytesNV);
+  });
+  uint8_t* down = rec + gateup_section_bytes(H, I, MOE_WEIGHTS_NVFP4);
+  parallel_for(H / kAtomRows, threads, [&](int rg) {
+    for (int c = 0; c < KCd; c++)
+      write_atom_nv(qd, sd, I, rg * kAtomRows, c, down + ((size_t)rg * KCd + c) * kAtomBytesNV);
+  });
+  // matrix scales: each scale array ends with its matrix's fp32 scale
+  const size_t ng = (size_t)I * H / 16;
+  float t[4] = {0.f, 0.f, 0.f, 0.f};
+  std::memcpy(&t[0], sg + ng, 4);
+  std::memcpy(&t[1], su + ng, 4);
+  std::memcpy(&t[2], sd + ng, 4);
+  std::memcpy(rec + nv_trailer_offset(H, I), t, sizeof t);
+}
+
 // Repack one expert into `rec` in the context's format.
 static void repack_expert(const Ctx* c, const uint8_t* qg, const uint8_t* qu, const uint8_t* qd,
                           const uint8_t* sg, const uint8_t* su, const uint8_t* sd, uint8_t* rec) {
   const int H = c->cfg.hidden, I = c->cfg.inter, fmt = c->cfg.weight_format;
-  if (fmt == MOE_WEIGHTS_BF16) {
+  if (fmt == MOE_WEIGHTS_NVFP4) {
+    repack_nv(qg, sg, qu, su, qd, sd, H, I, rec);
+  } else if (fmt == MOE_WEIGHTS_BF16) {
     repack_gateup_bf16((const uint16_t*)qg, (const uint16_t*)qu, I, H, rec);
     repack_down_bf16((const uint16_t*)qd, H, I, rec + gateup_section_bytes(H, I, fmt));
   } else {
@@ -381,7 +422,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       f.max_tokens > 64 || f.cache_slots < 0 || f.staging_slots < 0 ||
       f.max_prefill_tokens < 0 || (f.has_shared != 0 && f.has_shared != 1) ||
       f.cache_policy < MOE_CACHE_GLOBAL || f.cache_policy > MOE_CACHE_STATIC ||
-      f.weight_format < MOE_WEIGHTS_MXFP4 || f.weight_format > MOE_WEIGHTS_BF16 ||
+      f.weight_format < MOE_WEIGHTS_MXFP4 || f.weight_format > MOE_WEIGHTS_NVFP4 ||
       f.prefill_format < MOE_PREFILL_BF16 || f.prefill_format > MOE_PREFILL_MXFP8 ||
       (f.renormalize != 0 && f.renormalize != 1))
     return fail(MOE_ERR_INVALID_ARG, "moe_config field out of range");
@@ -391,9 +432,10 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     return fail(MOE_ERR_UNSUPPORTED, "n_layers*n_experts too large");
   if (f.hidden % 128 || f.inter % 128 || f.hidden > kMaxH || f.inter > kMaxH)
     return fail(MOE_ERR_UNSUPPORTED, "hidden and inter must be multiples of 128, at most 6144");
-  if (f.weight_format == MOE_WEIGHTS_BF16 && (f.max_tokens > 16 || f.max_prefill_tokens > 0))
+  if (f.weight_format != MOE_WEIGHTS_MXFP4 && (f.max_tokens > 16 || f.max_prefill_tokens > 0))
     return fail(MOE_ERR_UNSUPPORTED,
-                "bf16 experts run the decode path for at most 16 tokens per call (no prefill)");
+                "bf16 and NVFP4 experts run the decode path for at most 16 tokens per call "
+                "(no prefill)");
   if (f.prefill_format == MOE_PREFILL_MXFP8 && f.weight_format != MOE_WEIGHTS_MXFP4)
     return fail(MOE_ERR_UNSUPPORTED, "the MXFP8 prefill mode needs MXFP4 experts");
   if (f.cache_slots > kMaxCacheSlots)
@@ -538,15 +580,28 @@ moe_status moe_set_expert(moe_ctx* ctx, int32_t layer, int32_t expert,
   if (layer < 0 || layer >= c->cfg.n_layers || expert < -1 || expert >= c->cfg.n_experts)
     return fail(MOE_ERR_INVALID_ARG, "bad layer or expert index");
   const bool bf16 = c->cfg.weight_format == MOE_WEIGHTS_BF16;
+  const bool nv = c->cfg.weight_format == MOE_WEIGHTS_NVFP4;
   if (!qg || !qu || !qd || (!bf16 && (!sg || !su || !sd)))
     return fail(MOE_ERR_INVALID_ARG, "NULL weight pointer");
   if (bf16 && (sg || su || sd))
     return fail(MOE_ERR_INVALID_ARG, "bf16 experts take no scale arrays");
   if (expert == -1 && !c->cfg.has_shared)
     return fail(MOE_ERR_STATE, "context has no shared expert");
-  const size_t ns = (size_t)H * I / 32;
-  if (!bf16 && (!scales_valid(sg, ns) || !scales_valid(su, ns) || !scales_valid(sd, ns)))
-    return fail(MOE_ERR_INVALID_ARG, "E8M0 scale byte 255 (NaN)");
+  if (nv) {
+    const size_t n16 = (size_t)H * I / 16;
+    for (const uint8_t* s : {sg, su, sd}) {
+      for (size_t i = 0; i < n16; i++)
+        if ((s[i] & 0x80) || s[i] == 0x7F)
+          return fail(MOE_ERR_INVALID_ARG, "E4M3 block scale negative or NaN");
+      float t;
+      std::memcpy(&t, s + n16, 4);
+      if (!std::isfinite(t)) return fail(MOE_ERR_INVALID_ARG, "matrix scale not finite");
+    }
+  } else if (!bf16) {
+    const size_t ns = (size_t)H * I / 32;
+    if (!scales_valid(sg, ns) || !scales_valid(su, ns) || !scales_valid(sd, ns))
+      return fail(MOE_ERR_INVALID_ARG, "E8M0 scale byte 255 (NaN)");
+  }
   if (expert >= 0) {
     uint8_t* rec = c->pool + ((size_t)layer * c->cfg.n_experts + expert) * c->stride;
     repack_expert(c, qg, qu, qd, sg, su, sd, rec);
@@ -572,7 +627,9 @@ moe_status moe_set_layer(moe_ctx* ctx, int32_t layer, const float* h_router,
   if (c->cfg.has_shared && (!h_shared_q || (!bf16 && !h_shared_s)))
     return fail(MOE_ERR_INVALID_ARG, "shared expert weights required");
   const size_t H = c->cfg.hidden, I = c->cfg.inter;
-  const size_t q1 = bf16 ? H * I * 2 : H * I / 2, s1 = bf16 ? 0 : H * I / 32;
+  const bool nv = c->cfg.weight_format == MOE_WEIGHTS_NVFP4;
+  const size_t q1 = bf16 ? H * I * 2 : H * I / 2;
+  const size_t s1 = bf16 ? 0 : nv ? H * I / 16 + 4 : H * I / 32;
   auto sp = [&](const uint8_t* base, size_t off) { return base ? base + off : nullptr; };
   if (moe_status s = moe_set_router(ctx, layer, h_router)) return s;
   for (int e = 0; e < c->cfg.n_experts; e++) {

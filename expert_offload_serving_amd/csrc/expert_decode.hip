@@ -28,6 +28,7 @@
 namespace moe {
 namespace {
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -45,6 +46,33 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t q, uint32_t sbyte) {
   r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 1));
   r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 2));
   r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 3));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Value of an E4M3 block-scale byte (non-negative, not NaN: checked on the
+// host) as fp32, from its fields: exponent bits 6..3 (bias 7), mantissa
+// bits 2..0, subnormal m * 2^-9.
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+}
+
+// 8 E2M1 codes times an E4M3 block scale s -> 8 bf16, exactly.  The convert
+// to fp32 applies s's power of two (it reads only the exponent field); s's
+// significand (1 + m/8, or 0 for a zero scale) multiplies in fp32.  Every
+// product has at most 6 significant bits, so it is exact in fp32 and in
+// bf16, and one byte permute packs the top halves of two products.
+__device__ __forceinline__ bf16x8 dequant8_nv(uint32_t q, uint32_t sbyte) {
+  const float s = e4m3_value(sbyte);
+  const float f = s == 0.0f ? 0.0f : __uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
+  auto pair = [f](f32x2 v) {
+    return __builtin_amdgcn_perm(__float_as_uint(v[1] * f), __float_as_uint(v[0] * f), 0x07060302u);
+  };
+  u32x4 r;
+  r[0] = pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, s, 0));
+  r[1] = pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, s, 1));
+  r[2] = pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, s, 2));
+  r[3] = pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, s, 3));
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -333,6 +361,7 @@ struct WMxfp4 {
   static constexpr int kAtom = kAtomBytes;
   static constexpr int kStep = 2;
   static constexpr int kMaxThreads = 1024;
+  static constexpr bool kMatrixScale = false;
   struct Reg {
     u32x4 q;
     uint32_t s;
@@ -349,6 +378,7 @@ struct WBf16 {
   static constexpr int kAtom = kAtomBytesBF16;
   static constexpr int kStep = 1;
   static constexpr int kMaxThreads = 512;
+  static constexpr bool kMatrixScale = false;
   struct Reg {
     u32x4 v[4];
   };
@@ -358,6 +388,28 @@ struct WBf16 {
   }
   __device__ static void load_aux(Reg&, const uint8_t*, int) {}
   __device__ static bf16x8 op(const Reg& r, int j) { return __builtin_bit_cast(bf16x8, r.v[j]); }
+};
+// NVFP4: the MXFP4 code layout; the lane's two E4M3 block scales (K steps 0-1
+// and 2-3 of its 32 elements) in one 16-bit load; the matrix's fp32 scale
+// multiplies the accumulators.
+struct WNvfp4 {
+  static constexpr int kAtom = kAtomBytesNV;
+  static constexpr int kStep = 2;
+  static constexpr int kMaxThreads = 1024;
+  static constexpr bool kMatrixScale = true;
+  struct Reg {
+    u32x4 q;
+    uint32_t s;
+  };
+  __device__ static void load_data(Reg& r, const uint8_t* atom, int lane) {
+    r.q = load_atom_data(atom, lane);
+  }
+  __device__ static void load_aux(Reg& r, const uint8_t* atom, int lane) {
+    r.s = *(__attribute__((address_space(1))) const uint16_t*)(atom + kAtomData + 2 * lane);
+  }
+  __device__ static bf16x8 op(const Reg& r, int j) {
+    return dequant8_nv(r.q[j], (r.s >> (8 * (j >> 1))) & 0xFFu);
+  }
 };
 
 // Streaming variants for calls of at most 16 tokens (one M tile).  A wave
@@ -373,7 +425,7 @@ __global__ __launch_bounds__(W::kMaxThreads) void gateup_stream_kernel(
     const WorkItem* __restrict__ items, int items_cap, const int32_t* __restrict__ lo_p,
     const int32_t* __restrict__ hi_p,
     const int32_t* __restrict__ tok, const uint16_t* __restrict__ x, uint32_t x_bytes, int H,
-    int I, uint16_t* __restrict__ h, size_t lo_plane) {
+    int I, uint16_t* __restrict__ h, size_t lo_plane, size_t ms_off) {
   constexpr int S = CPW < W::kStep ? CPW : W::kStep;  // chunks per step
   constexpr int NS = CPW / S;           // steps
   // the launch covers items [*lo_p, *hi_p) of the work list (items_cap
@@ -395,6 +447,13 @@ __global__ __launch_bounds__(W::kMaxThreads) void gateup_stream_kernel(
   const uint8_t* ubase = gbase + (size_t)KC * W::kAtom;
   extern __shared__ f32x4 red[];  // [waves][2][64], sized by the launch
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, x_bytes);
+  // the gate and up matrices' fp32 scales (at ms_off of the record)
+  float msg = 1.0f, msu = 1.0f;
+  if constexpr (W::kMatrixScale) {
+    const float* ms = reinterpret_cast<const float*>(it.w + ms_off);
+    msg = ms[0];
+    msu = ms[1];
+  }
 
   // The token row first: loads return in order, so a token index loaded
   // after the weights would hold the activation loads back until every
@@ -450,6 +509,10 @@ __global__ __launch_bounds__(W::kMaxThreads) void gateup_stream_kernel(
     // refill the buffer this step consumed
     if (st + 2 < NS) load_step(st + 2, b);
   }
+  if constexpr (W::kMatrixScale) {
+    ag *= msg;
+    au *= msu;
+  }
   red[(2 * w) * 64 + lane] = ag;
   red[(2 * w + 1) * 64 + lane] = au;
   lds_sync();
@@ -461,7 +524,7 @@ __global__ __launch_bounds__(W::kMaxThreads) void down_stream_kernel(
     const WorkItem* __restrict__ items, int items_cap, const int32_t* __restrict__ lo_p,
     const int32_t* __restrict__ hi_p,
     const uint16_t* __restrict__ h, size_t lo_plane, int H, int I, size_t gateup_bytes,
-    float* __restrict__ yperm) {
+    float* __restrict__ yperm, size_t ms_off) {
   constexpr int S = CPW < W::kStep ? CPW : W::kStep;
   constexpr int NS = CPW / S;
   // the launch covers items [*lo_p, *hi_p) of the work list (items_cap
@@ -483,6 +546,9 @@ __global__ __launch_bounds__(W::kMaxThreads) void down_stream_kernel(
   const uint8_t* bbase = abase + (size_t)KC * W::kAtom;
   extern __shared__ f32x4 red[];  // [waves][2][64], sized by the launch
   const uint32_t lo_bytes = (uint32_t)(lo_plane * 2);
+  // the down matrix's fp32 scale (at ms_off of the record)
+  float msd = 1.0f;
+  if constexpr (W::kMatrixScale) msd = reinterpret_cast<const float*>(it.w + ms_off)[2];
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(h, 2 * lo_bytes);
 
   typename W::Reg wa[2][S], wb[2][S];
@@ -540,6 +606,10 @@ __global__ __launch_bounds__(W::kMaxThreads) void down_stream_kernel(
       }
     }
     if (st + 2 < NS) load_step(st + 2, b);
+  }
+  if constexpr (W::kMatrixScale) {
+    acc0 *= msd;
+    acc1 *= msd;
   }
   red[(2 * w) * 64 + lane] = acc0;
   red[(2 * w + 1) * 64 + lane] = acc1;
@@ -647,15 +717,17 @@ hipError_t launch_expert_gateup(const Ctx* c, const DecodeScratch& s, const uint
   const size_t lo = s.lo_plane;
   const int KC = c->cfg.hidden / kAtomK;
   const bool bf16 = c->cfg.weight_format == MOE_WEIGHTS_BF16;
+  const bool nv = c->cfg.weight_format == MOE_WEIGHTS_NVFP4;
+  const size_t ms_off = nv ? nv_trailer_offset(c->cfg.hidden, c->cfg.inter) : 0;
   if (T <= kMaxStreamTokens) {
     const int cpw = bf16 ? bf16_stream_cpw(KC, gateup_stream_cpw(KC)) : gateup_stream_cpw(KC);
     const int waves = stream_waves(KC, cpw);
 #define GATEUP_S(N, F)                                                                     \
   MOE_LAUNCH((gateup_stream_kernel<N, F>), grid, waves * 64, waves * 2 * 64 * 16, st, ev0, \
              ev1, s.items, s.max_items, lo_p, hi_p, s.tok, x, (uint32_t)T * c->cfg.hidden * 2,          \
-             c->cfg.hidden, c->cfg.inter, s.h, lo)
+             c->cfg.hidden, c->cfg.inter, s.h, lo, ms_off)
 #define GATEUP_F(N) \
-  if (bf16) GATEUP_S(N, WBf16); else GATEUP_S(N, WMxfp4);
+  if (bf16) GATEUP_S(N, WBf16); else if (nv) GATEUP_S(N, WNvfp4); else GATEUP_S(N, WMxfp4);
     switch (cpw) {
       case 1: GATEUP_F(1); break;
       case 2: GATEUP_F(2); break;
@@ -667,7 +739,7 @@ hipError_t launch_expert_gateup(const Ctx* c, const DecodeScratch& s, const uint
 #undef GATEUP_S
     return hipGetLastError();
   }
-  if (bf16) return hipErrorNotSupported;  // bf16 contexts have max_tokens <= 16
+  if (bf16 || nv) return hipErrorNotSupported;  // such contexts have max_tokens <= 16
   // the split of the whole list, whichever part this launch covers, so
   // that an expert's partial sums meet in the same order resident or copied
   const Split sp = split_k(KC, grid.x * items_for(c, T, kItemsAll), 4);
@@ -692,6 +764,8 @@ hipError_t launch_expert_down(const Ctx* c, const DecodeScratch& s, int T, ItemR
   const int32_t* hi_p = items_hi(s, part);
   const size_t lo = s.lo_plane;
   const bool bf16 = c->cfg.weight_format == MOE_WEIGHTS_BF16;
+  const bool nv = c->cfg.weight_format == MOE_WEIGHTS_NVFP4;
+  const size_t ms_off = nv ? nv_trailer_offset(c->cfg.hidden, c->cfg.inter) : 0;
   const size_t gub = gateup_section_bytes(c->cfg.hidden, c->cfg.inter, c->cfg.weight_format);
   const int KC = c->cfg.inter / kAtomK;
   if (T <= kMaxStreamTokens) {
@@ -699,9 +773,10 @@ hipError_t launch_expert_down(const Ctx* c, const DecodeScratch& s, int T, ItemR
     const int waves = stream_waves(KC, cpw);
 #define DOWN_S(N, F)                                                                         \
   MOE_LAUNCH((down_stream_kernel<N, F>), grid, waves * 64, waves * 2 * 64 * 16, st, ev0, ev1, \
-             s.items, s.max_items, lo_p, hi_p, s.h, lo, c->cfg.hidden, c->cfg.inter, gub, s.yperm)
+             s.items, s.max_items, lo_p, hi_p, s.h, lo, c->cfg.hidden, c->cfg.inter, gub, s.yperm, \
+             ms_off)
 #define DOWN_F(N) \
-  if (bf16) DOWN_S(N, WBf16); else DOWN_S(N, WMxfp4);
+  if (bf16) DOWN_S(N, WBf16); else if (nv) DOWN_S(N, WNvfp4); else DOWN_S(N, WMxfp4);
     switch (cpw) {
       case 1: DOWN_F(1); break;
       case 2: DOWN_F(2); break;
@@ -713,7 +788,7 @@ hipError_t launch_expert_down(const Ctx* c, const DecodeScratch& s, int T, ItemR
 #undef DOWN_S
     return hipGetLastError();
   }
-  if (bf16) return hipErrorNotSupported;  // bf16 contexts have max_tokens <= 16
+  if (bf16 || nv) return hipErrorNotSupported;  // such contexts have max_tokens <= 16
   // the split of the whole list, whichever part this launch covers, so
   // that an expert's partial sums meet in the same order resident or copied
   const Split sp = split_k(KC, grid.x * items_for(c, T, kItemsAll), 4);

@@ -42,11 +42,23 @@ constexpr int kAtomBytes = 1088;
 // bf16 atom: the same 16 rows x 128 K tile as an MXFP4 atom, lane l's 32
 // values (row l % 16, K block l / 16) as 4 pieces of 8 at 1024 p + 16 l.
 constexpr int kAtomBytesBF16 = 4096;
-inline size_t expert_record_bytes(int H, int I, int fmt = MOE_WEIGHTS_MXFP4) {
-  return fmt == MOE_WEIGHTS_BF16 ? (size_t)3 * H * I * 2 : (size_t)3 * H * I * 17 / 32;
-}
+// NVFP4 atom: the MXFP4 atom's 1024 code bytes, then lane l's two E4M3 block
+// scales (row l % 16, K 32 (l / 16) .. +15 and +16 .. +31) at 1024 + 2 l.
+// An NVFP4 record ends with a 16-byte trailer: the fp32 scales of the gate,
+// up and down matrices, then 4 zero bytes.
+constexpr int kAtomBytesNV = 1152;
+constexpr int kNvTrailerBytes = 16;
 inline size_t gateup_section_bytes(int H, int I, int fmt = MOE_WEIGHTS_MXFP4) {
-  return fmt == MOE_WEIGHTS_BF16 ? (size_t)2 * I * H * 2 : (size_t)2 * I * H * 17 / 32;
+  if (fmt == MOE_WEIGHTS_BF16) return (size_t)2 * I * H * 2;
+  if (fmt == MOE_WEIGHTS_NVFP4) return (size_t)2 * I * H * 9 / 16;
+  return (size_t)2 * I * H * 17 / 32;
+}
+// offset of an NVFP4 record's matrix scales: after the gate/up and down atoms
+inline size_t nv_trailer_offset(int H, int I) { return (size_t)3 * H * I * 9 / 16; }
+inline size_t expert_record_bytes(int H, int I, int fmt = MOE_WEIGHTS_MXFP4) {
+  if (fmt == MOE_WEIGHTS_BF16) return (size_t)3 * H * I * 2;
+  if (fmt == MOE_WEIGHTS_NVFP4) return nv_trailer_offset(H, I) + kNvTrailerBytes;
+  return (size_t)3 * H * I * 17 / 32;
 }
 
 // Host-side repack of one canonical MXFP4 matrix [N][K] into atoms.

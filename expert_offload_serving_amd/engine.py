@@ -118,9 +118,23 @@ class MoEEngine:
         b.moe_set_router(self.ctx, layer, np.ascontiguousarray(w_router, dtype=np.float32))
 
     def set_expert(self, layer: int, expert: int, w):
-        """w has canonical MXFP4 arrays qg, qu, qd, sg, su, sd (uint8), or
-        bf16 matrices wg, wu, wd (uint16 bit patterns) for a bf16 context."""
+        """w has canonical MXFP4 arrays qg, qu, qd, sg, su, sd (uint8); bf16
+        matrices wg, wu, wd (uint16 bit patterns) for a bf16 context; or, for
+        an NVFP4 context, codes qg, qu, qd, E4M3 block scales sg, su, sd
+        (one byte per 16) and fp32 matrix scales tg, tu, td."""
         H, I = self.H, self.I
+        if self.weight_format == "nvfp4":
+            shapes = {"qg": (I, H // 2), "qu": (I, H // 2), "qd": (H, I // 2),
+                      "sg": (I, H // 16), "su": (I, H // 16), "sd": (H, I // 16)}
+            for n, shp in shapes.items():
+                check_host(n, getattr(w, n), shp)
+            q = [np.ascontiguousarray(getattr(w, n), dtype=np.uint8) for n in ("qg", "qu", "qd")]
+            # each scale array is followed by its matrix's fp32 scale
+            sc = [np.concatenate([np.ascontiguousarray(getattr(w, n), dtype=np.uint8).ravel(),
+                                  np.array([getattr(w, t)], dtype="<f4").view(np.uint8)])
+                  for n, t in (("sg", "tg"), ("su", "tu"), ("sd", "td"))]
+            b.moe_set_expert(self.ctx, layer, expert, *q, *sc)
+            return
         if self.weight_format == "bf16":
             shapes = {"wg": (I, H), "wu": (I, H), "wd": (H, I)}
             for n, shp in shapes.items():

@@ -90,13 +90,17 @@ enum {
  * one E8M0 scale per 32 along K, DeepSeek-V4-Flash's format on the pages.
  * BF16: plain bf16 matrices, the format the pages run their 35B-A3B model
  * in (jansverre.net FreeToken article, section "Hvor raskt kjører
- * modellene?").  BF16 experts run the decode path for up to 16 tokens per
- * call: moe_create requires max_tokens <= 16 and max_prefill_tokens = 0
- * with them (else UNSUPPORTED).
+ * modellene?").  NVFP4: E2M1 codes with one E4M3 scale per 16 along K and
+ * one fp32 scale per matrix, the format the pages run the 35B-A3B model in
+ * on a laptop GPU (same section); NVIDIA's definition, which the pages do
+ * not spell out.  BF16 and NVFP4 experts run the decode path for up to 16
+ * tokens per call: moe_create requires max_tokens <= 16 and
+ * max_prefill_tokens = 0 with them (else UNSUPPORTED).
  */
 enum {
   MOE_WEIGHTS_MXFP4 = 0,
-  MOE_WEIGHTS_BF16 = 1
+  MOE_WEIGHTS_BF16 = 1,
+  MOE_WEIGHTS_NVFP4 = 2
 };
 
 /*
@@ -154,7 +158,7 @@ typedef struct moe_config {
                               the prefill h records) below 2 GiB (else
                               UNSUPPORTED)                                  */
   int32_t cache_policy;    /* MOE_CACHE_GLOBAL (0), _PER_LAYER or _STATIC  */
-  int32_t weight_format;   /* MOE_WEIGHTS_MXFP4 (0) or MOE_WEIGHTS_BF16     */
+  int32_t weight_format;   /* MOE_WEIGHTS_MXFP4 (0), _BF16 or _NVFP4       */
   int32_t prefill_format;  /* MOE_PREFILL_BF16 (0) or MOE_PREFILL_MXFP8 (MXFP4
                               weights only); moe_set_prefill_format changes it */
 } moe_config;
@@ -218,9 +222,15 @@ moe_status moe_set_router(moe_ctx* ctx, int32_t layer, const float* h_router);
  * layer's shared expert, held in HBM.  The library repacks into its own
  * MFMA-tiled layout.  With weight_format = MOE_WEIGHTS_BF16 the three
  * matrices are bf16 instead: h_qg and h_qu [I][H], h_qd [H][I] (2 bytes per
- * element, same row order), and h_sg, h_su, h_sd must be NULL.  Errors:
- * INVALID_ARG (NULL, bad index, scale byte 255 which is NaN, scale pointers
- * given with bf16 weights), STATE (expert = -1 without has_shared), HIP.
+ * element, same row order), and h_sg, h_su, h_sd must be NULL.  With
+ * MOE_WEIGHTS_NVFP4 the codes are as for MXFP4 and each scale array holds
+ * its matrix's E4M3 block scales, one byte per 16 consecutive K elements of
+ * a row ([I][H/16] or [H][I/16]), followed by the matrix's fp32 scale (4
+ * bytes, little-endian): an element's value is e2m1 x e4m3 x that scale.
+ * Errors: INVALID_ARG (NULL, bad index, E8M0 scale byte 255 which is NaN;
+ * E4M3 block scale negative or NaN, or a matrix scale not finite; scale
+ * pointers given with bf16 weights), STATE (expert = -1 without
+ * has_shared), HIP.
  */
 moe_status moe_set_expert(moe_ctx* ctx, int32_t layer, int32_t expert,
                           const uint8_t* h_qg, const uint8_t* h_qu,
@@ -236,7 +246,8 @@ moe_status moe_set_expert(moe_ctx* ctx, int32_t layer, int32_t expert,
  * bytes each), each part laid out as in moe_set_expert; h_shared_q /
  * h_shared_s hold one such record, or are NULL when has_shared is 0.  With
  * bf16 weights a record of h_q is [wg | wu | wd] (3*H*I*2 bytes) and h_s
- * and h_shared_s are NULL.
+ * and h_shared_s are NULL.  With NVFP4 weights a record of h_s is the three
+ * scale arrays of moe_set_expert back to back (3*(H*I/16 + 4) bytes).
  */
 moe_status moe_set_layer(moe_ctx* ctx, int32_t layer, const float* h_router,
                          const uint8_t* h_q, const uint8_t* h_s,

@@ -76,9 +76,11 @@ def parse(argv=None):
                          "HIP graph (e.g. 1,4,16; default: none)")
     ap.add_argument("--prefill-steps", type=int, default=3,
                     help="prefill passes of the DeepSeek-V4-Flash-shaped stack (0: skip)")
-    ap.add_argument("--legs", default="headline,a3b,dsv4",
-                    help="workloads to run: the headline decode line and the two context legs "
-                         "(each runs whole; without the headline only the context is printed)")
+    ap.add_argument("--legs", default="headline,a3b,dsv4,formats",
+                    help="workloads to run: the headline decode line and the context legs "
+                         "(35B-A3B decode, DeepSeek-V4-Flash prefill and decode, prefill with "
+                         "bf16 and NVFP4 experts; each runs whole; without the headline only "
+                         "the context is printed)")
     ap.add_argument("--prefill-formats", default="bf16,mxfp8",
                     help="prefill modes timed on the DeepSeek-V4-Flash-shaped stack")
     ap.add_argument("--dsv4-decode-steps", type=int, default=256,
@@ -86,8 +88,7 @@ def parse(argv=None):
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="also run one plain copy of this many MiB (counter calibration)")
     ap.add_argument("--weights", choices=("mxfp4", "bf16", "nvfp4"), default="mxfp4",
-                    help="expert format of the headline workload (bf16: decode of up to 16 "
-                         "tokens; no context legs)")
+                    help="expert format of the headline workload (no context legs)")
     ap.add_argument("--policy-study", type=int, default=0, metavar="STEPS",
                     help="instead of the benchmark line: DeepSeek-V4-Flash-shaped decode under "
                          "each cache placement policy (STEPS timed steps per run)")
@@ -367,9 +368,11 @@ def decode_summary(r, bound="hbm"):
 
 
 # ------------------------------------------------------------ context legs
-def time_prefill(eng, sh, T, xs, ys, steps, fmt, name):
+def time_prefill(eng, sh, T, xs, ys, steps, fmt, name, kernels=None):
     """steps timed prefill passes of the whole stack in one mode (after one
-    untimed pass): end-to-end rate and the per-stage kernel times."""
+    untimed pass): end-to-end rate and the per-stage kernel times.
+    kernels: names of the gate/up and down kernels (default: those of the
+    mode's grouped GEMMs for MXFP4 experts)."""
     import torch
     eng.set_prefill_format(fmt)
     eng.prefill(xs, ys)
@@ -395,8 +398,8 @@ def time_prefill(eng, sh, T, xs, ys, steps, fmt, name):
     tflops = flops_layer / (gemm_ms * 1e9)
     peak = MFMA_FP8_PEAK_TFLOPS if fmt == "mxfp8" else MFMA_BF16_PEAK_TFLOPS
     upload = sh.E * sh.expert_bytes() * layers
-    kn = {"bf16": ("gateup_prefill_kernel", "down_prefill_kernel"),
-          "mxfp8": ("gateup_mx_kernel", "down_mx_kernel")}[fmt]
+    kn = kernels or {"bf16": ("gateup_prefill_kernel", "down_prefill_kernel"),
+                     "mxfp8": ("gateup_mx_kernel", "down_mx_kernel")}[fmt]
     return {
         "workload": name, "format": fmt, "T": T, "layers": sh.layers, "steps": steps,
         "tokens_per_s_end_to_end": round(T * steps / el, 1),
@@ -448,6 +451,32 @@ def run_dsv4(prefill_steps, decode_steps, decode_warmup, seed=0, formats=("bf16"
         r = run_decode(wd, 1, decode_steps, decode_warmup, seed, eng=eng)
         out["dsv4_decode_T1"] = decode_summary(r)
     eng.close()
+    return out
+
+
+def run_prefill_formats(steps, T=4096, layers=2, seed=0, formats=("bf16", "nvfp4")):
+    """Prefill with bf16 and NVFP4 experts on a 35B-A3B-shaped stack (H=2048,
+    I=512, E=256, top-8): the expert-streaming kernels over 128-row work
+    items, bf16 matrix cores (NVFP4 is dequantised to bf16 on the way in).
+    Eight generated records per layer are reused for all 256 experts; the
+    routing is the layer's own, so every expert is uploaded and run."""
+    import torch
+    from dataclasses import replace
+    from workload import gen
+    out = {}
+    for w in formats:
+        sh = replace(gen.WORKLOADS["a3b_decode"].shape, layers=layers, weights=w)
+        eng = make_engine(sh, 1, 0, sh.k, prefill_tokens=T)
+        load_weights(eng, sh, seed, distinct=8)
+        xs = [bf16_dev(gen.tokens(sh, l, 0, T, seed)) for l in range(sh.layers)]
+        ys = [torch.empty((T, sh.H), dtype=torch.int16, device="cuda") for _ in range(sh.layers)]
+        r = time_prefill(eng, sh, T, xs, ys, steps, "bf16", f"a3b_prefill_{w}",
+                         kernels=("gateup_decode_kernel", "down_decode_kernel"))
+        r["weights"] = w
+        out[f"prefill_{w}_experts"] = r
+        log(f"prefill with {w} experts: {r['mfma_tflops']} TFLOP/s ({r['mfma_frac']:.3f} of "
+            f"{r['mfma_peak_tflops']})")
+        eng.close()
     return out
 
 
@@ -743,6 +772,9 @@ def main():
             ctx.update(run_dsv4(a.prefill_steps, a.dsv4_decode_steps,
                                 max(a.dsv4_decode_steps // 4, 1),
                                 formats=tuple(f for f in a.prefill_formats.split(",") if f)))
+        if "formats" in legs and a.prefill_steps > 0:
+            log("context: prefill with bf16 and NVFP4 experts")
+            ctx.update(run_prefill_formats(a.prefill_steps))
     if a.calibrate_copy_mb > 0:
         calibrate_copy(a.calibrate_copy_mb)
     print(json.dumps(line), flush=True)

@@ -153,17 +153,79 @@ __device__ __forceinline__ void down_epilogue(const f32x4* red, int nw, const Wo
   }
 }
 
+// Weight-format policies of the expert kernels: how a lane loads its part of
+// an atom and forms the bf16x8 operand of K step j (4 steps per atom).
+struct WMxfp4 {
+  static constexpr int kAtom = kAtomBytes;
+  static constexpr int kStep = 2;
+  static constexpr int kMaxThreads = 1024;
+  static constexpr bool kMatrixScale = false;
+  struct Reg {
+    u32x4 q;
+    uint32_t s;
+  };
+  __device__ static void load_data(Reg& r, const uint8_t* atom, int lane) {
+    r.q = load_atom_data(atom, lane);
+  }
+  __device__ static void load_aux(Reg& r, const uint8_t* atom, int lane) {
+    r.s = load_scale(atom, lane);
+  }
+  __device__ static bf16x8 op(const Reg& r, int j) { return dequant8(r.q[j], r.s); }
+  __device__ static void hide(Reg& r) { asm volatile("" : "+v"(r.q), "+v"(r.s)); }
+};
+struct WBf16 {
+  static constexpr int kAtom = kAtomBytesBF16;
+  static constexpr int kStep = 1;
+  static constexpr int kMaxThreads = 512;
+  static constexpr bool kMatrixScale = false;
+  struct Reg {
+    u32x4 v[4];
+  };
+  __device__ static void load_data(Reg& r, const uint8_t* atom, int lane) {
+#pragma unroll
+    for (int p = 0; p < 4; p++) r.v[p] = *(gu32x4*)(atom + 1024 * p + lane * 16);
+  }
+  __device__ static void load_aux(Reg&, const uint8_t*, int) {}
+  __device__ static bf16x8 op(const Reg& r, int j) { return __builtin_bit_cast(bf16x8, r.v[j]); }
+  __device__ static void hide(Reg& r) {
+    asm volatile("" : "+v"(r.v[0]), "+v"(r.v[1]), "+v"(r.v[2]), "+v"(r.v[3]));
+  }
+};
+// NVFP4: the MXFP4 code layout; the lane's two E4M3 block scales (K steps 0-1
+// and 2-3 of its 32 elements) in one 16-bit load; the matrix's fp32 scale
+// multiplies the accumulators.
+struct WNvfp4 {
+  static constexpr int kAtom = kAtomBytesNV;
+  static constexpr int kStep = 2;
+  static constexpr int kMaxThreads = 1024;
+  static constexpr bool kMatrixScale = true;
+  struct Reg {
+    u32x4 q;
+    uint32_t s;
+  };
+  __device__ static void load_data(Reg& r, const uint8_t* atom, int lane) {
+    r.q = load_atom_data(atom, lane);
+  }
+  __device__ static void load_aux(Reg& r, const uint8_t* atom, int lane) {
+    r.s = *(__attribute__((address_space(1))) const uint16_t*)(atom + kAtomData + 2 * lane);
+  }
+  __device__ static bf16x8 op(const Reg& r, int j) {
+    return dequant8_nv(r.q[j], (r.s >> (8 * (j >> 1))) & 0xFFu);
+  }
+  __device__ static void hide(Reg& r) { asm volatile("" : "+v"(r.q), "+v"(r.s)); }
+};
+
 // Gate/up + SwiGLU for calls of more than 16 tokens.  Block (pair p, item):
 // 16 gate and 16 up rows of one expert; wave w takes K chunks
 // [w*CPW, w*CPW+CPW), all loaded before its first MFMA.  M tiles of 16
 // tokens are processed one after another with the weights held in
 // registers.
-template <int CPW>
-__global__ __launch_bounds__(1024) void gateup_decode_kernel(
+template <int CPW, class W>
+__global__ __launch_bounds__(W::kMaxThreads) void gateup_decode_kernel(
     const WorkItem* __restrict__ items, int items_cap, const int32_t* __restrict__ lo_p,
     const int32_t* __restrict__ hi_p,
     const int32_t* __restrict__ tok, const uint16_t* __restrict__ x, uint32_t x_bytes, int H,
-    int I, uint16_t* __restrict__ h, size_t lo_plane) {
+    int I, uint16_t* __restrict__ h, size_t lo_plane, size_t ms_off) {
   // the launch covers items [*lo_p, *hi_p) of the work list (items_cap
   // entries; hi <= items_cap)
   const int item = *lo_p + blockIdx.y;
@@ -178,27 +240,33 @@ __global__ __launch_bounds__(1024) void gateup_decode_kernel(
   const int p = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int KC = H / kAtomK;
-  const uint8_t* gbase = it.w + (size_t)(2 * p) * KC * kAtomBytes;
-  const uint8_t* ubase = gbase + (size_t)KC * kAtomBytes;
+  const uint8_t* gbase = it.w + (size_t)(2 * p) * KC * W::kAtom;
+  const uint8_t* ubase = gbase + (size_t)KC * W::kAtom;
   extern __shared__ f32x4 red[];  // [waves][2][64], sized by the launch
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, x_bytes);
+  // the gate and up matrices' fp32 scales (at ms_off of the record)
+  float msg = 1.0f, msu = 1.0f;
+  if constexpr (W::kMatrixScale) {
+    const float* ms = reinterpret_cast<const float*>(it.w + ms_off);
+    msg = ms[0];
+    msu = ms[1];
+  }
 
   // Token row of this lane in the first M tile.
   const int trow = (lane & 15) < it.cnt ? tok[it.pos0 + (lane & 15)] : 0;
   // Weight loads are unconditional: a chunk past K (only when waves do not
   // divide K) reads chunk 0, whose finite values meet zero activations.
   // A guarded load would wait at its branch instead of staying in flight.
-  u32x4 wg[CPW], wu[CPW];
-  uint32_t sg[CPW], su[CPW];
+  typename W::Reg wg[CPW], wu[CPW];
 #pragma unroll
   for (int cc = 0; cc < CPW; cc++) {
     const int c = w * CPW + cc;
-    const uint8_t* ga = gbase + (size_t)(c < KC ? c : 0) * kAtomBytes;
-    const uint8_t* ua = ubase + (size_t)(c < KC ? c : 0) * kAtomBytes;
-    wg[cc] = load_atom_data(ga, lane);
-    wu[cc] = load_atom_data(ua, lane);
-    sg[cc] = load_scale(ga, lane);
-    su[cc] = load_scale(ua, lane);
+    const uint8_t* ga = gbase + (size_t)(c < KC ? c : 0) * W::kAtom;
+    const uint8_t* ua = ubase + (size_t)(c < KC ? c : 0) * W::kAtom;
+    W::load_data(wg[cc], ga, lane);
+    W::load_data(wu[cc], ua, lane);
+    W::load_aux(wg[cc], ga, lane);
+    W::load_aux(wu[cc], ua, lane);
   }
 
   // One M tile of 16 tokens.  The first tile is peeled out of the loop so
@@ -230,16 +298,22 @@ __global__ __launch_bounds__(1024) void gateup_decode_kernel(
         // from loop-invariant motion keeps the (4x larger) dequantised
         // fragments from being hoisted out of the tile loop and held live.
 #pragma unroll
-        for (int q = 0; q < CPW; q++)
-          asm volatile("" : "+v"(wg[q]), "+v"(wu[q]), "+v"(sg[q]), "+v"(su[q]));
+        for (int q = 0; q < CPW; q++) {
+          W::hide(wg[q]);
+          W::hide(wu[q]);
+        }
       }
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[cc & 1][j], dequant8(wg[cc][j], sg[cc]), ag, 0, 0, 0);
-        au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[cc & 1][j], dequant8(wu[cc][j], su[cc]), au, 0, 0, 0);
+        ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[cc & 1][j], W::op(wg[cc], j), ag, 0, 0, 0);
+        au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[cc & 1][j], W::op(wu[cc], j), au, 0, 0, 0);
         // keep each fragment's dequant next to its MFMAs (bounds live registers)
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    if constexpr (W::kMatrixScale) {
+      ag *= msg;
+      au *= msu;
     }
     red[(2 * w) * 64 + lane] = ag;
     red[(2 * w + 1) * 64 + lane] = au;
@@ -258,12 +332,12 @@ __global__ __launch_bounds__(1024) void gateup_decode_kernel(
 // q, item): rows [32q, 32q+32) of H of one expert, as two 16-row groups that
 // share every h fragment; waves split K = I; each weight fragment meets both
 // h planes.
-template <int CPW>
-__global__ __launch_bounds__(1024) void down_decode_kernel(
+template <int CPW, class W>
+__global__ __launch_bounds__(W::kMaxThreads) void down_decode_kernel(
     const WorkItem* __restrict__ items, int items_cap, const int32_t* __restrict__ lo_p,
     const int32_t* __restrict__ hi_p,
     const uint16_t* __restrict__ h, size_t lo_plane, int H, int I, size_t gateup_bytes,
-    float* __restrict__ yperm) {
+    float* __restrict__ yperm, size_t ms_off) {
   // the launch covers items [*lo_p, *hi_p) of the work list (items_cap
   // entries; hi <= items_cap)
   const int item = *lo_p + blockIdx.y;
@@ -278,23 +352,25 @@ __global__ __launch_bounds__(1024) void down_decode_kernel(
   const int q = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int KC = I / kAtomK;
-  const uint8_t* abase = it.w + gateup_bytes + (size_t)(2 * q) * KC * kAtomBytes;
-  const uint8_t* bbase = abase + (size_t)KC * kAtomBytes;
+  const uint8_t* abase = it.w + gateup_bytes + (size_t)(2 * q) * KC * W::kAtom;
+  const uint8_t* bbase = abase + (size_t)KC * W::kAtom;
   extern __shared__ f32x4 red[];  // [waves][2][64], sized by the launch
   const uint32_t lo_bytes = (uint32_t)(lo_plane * 2);
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(h, 2 * lo_bytes);
+  // the down matrix's fp32 scale (at ms_off of the record)
+  float msd = 1.0f;
+  if constexpr (W::kMatrixScale) msd = reinterpret_cast<const float*>(it.w + ms_off)[2];
 
   // Unconditional weight loads, as in the gate/up kernel.
-  u32x4 wa[CPW], wb[CPW];
-  uint32_t sa[CPW], sb[CPW];
+  typename W::Reg wa[CPW], wb[CPW];
 #pragma unroll
   for (int cc = 0; cc < CPW; cc++) {
     const int c = w * CPW + cc;
-    const size_t o = (size_t)(c < KC ? c : 0) * kAtomBytes;
-    wa[cc] = load_atom_data(abase + o, lane);
-    wb[cc] = load_atom_data(bbase + o, lane);
-    sa[cc] = load_scale(abase + o, lane);
-    sb[cc] = load_scale(bbase + o, lane);
+    const size_t o = (size_t)(c < KC ? c : 0) * W::kAtom;
+    W::load_data(wa[cc], abase + o, lane);
+    W::load_data(wb[cc], bbase + o, lane);
+    W::load_aux(wa[cc], abase + o, lane);
+    W::load_aux(wb[cc], bbase + o, lane);
   }
 
   // One M tile of 16 tokens (first tile peeled, as in the gate/up kernel).
@@ -327,18 +403,25 @@ __global__ __launch_bounds__(1024) void down_decode_kernel(
       }
       if (cc == 0) {
 #pragma unroll
-        for (int r = 0; r < CPW; r++) asm volatile("" : "+v"(wa[r]), "+v"(wb[r]), "+v"(sa[r]), "+v"(sb[r]));
+        for (int r = 0; r < CPW; r++) {
+          W::hide(wa[r]);
+          W::hide(wb[r]);
+        }
       }
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        const bf16x8 b0 = dequant8(wa[cc][j], sa[cc]);
+        const bf16x8 b0 = W::op(wa[cc], j);
         acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[cc & 1][j], b0, acc0, 0, 0, 0);
         acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[cc & 1][j], b0, acc0, 0, 0, 0);
-        const bf16x8 b1 = dequant8(wb[cc][j], sb[cc]);
+        const bf16x8 b1 = W::op(wb[cc], j);
         acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[cc & 1][j], b1, acc1, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[cc & 1][j], b1, acc1, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    if constexpr (W::kMatrixScale) {
+      acc0 *= msd;
+      acc1 *= msd;
     }
     red[(2 * w) * 64 + lane] = acc0;
     red[(2 * w + 1) * 64 + lane] = acc1;
@@ -357,61 +440,6 @@ __global__ __launch_bounds__(1024) void down_decode_kernel(
 // pieces used as they are.  kStep: chunks per load step (a bf16 chunk holds
 // four times the bytes); kMaxThreads: workgroup size limit (bf16 keeps 8
 // waves, which leaves its larger operands 256 registers a lane).
-struct WMxfp4 {
-  static constexpr int kAtom = kAtomBytes;
-  static constexpr int kStep = 2;
-  static constexpr int kMaxThreads = 1024;
-  static constexpr bool kMatrixScale = false;
-  struct Reg {
-    u32x4 q;
-    uint32_t s;
-  };
-  __device__ static void load_data(Reg& r, const uint8_t* atom, int lane) {
-    r.q = load_atom_data(atom, lane);
-  }
-  __device__ static void load_aux(Reg& r, const uint8_t* atom, int lane) {
-    r.s = load_scale(atom, lane);
-  }
-  __device__ static bf16x8 op(const Reg& r, int j) { return dequant8(r.q[j], r.s); }
-};
-struct WBf16 {
-  static constexpr int kAtom = kAtomBytesBF16;
-  static constexpr int kStep = 1;
-  static constexpr int kMaxThreads = 512;
-  static constexpr bool kMatrixScale = false;
-  struct Reg {
-    u32x4 v[4];
-  };
-  __device__ static void load_data(Reg& r, const uint8_t* atom, int lane) {
-#pragma unroll
-    for (int p = 0; p < 4; p++) r.v[p] = *(gu32x4*)(atom + 1024 * p + lane * 16);
-  }
-  __device__ static void load_aux(Reg&, const uint8_t*, int) {}
-  __device__ static bf16x8 op(const Reg& r, int j) { return __builtin_bit_cast(bf16x8, r.v[j]); }
-};
-// NVFP4: the MXFP4 code layout; the lane's two E4M3 block scales (K steps 0-1
-// and 2-3 of its 32 elements) in one 16-bit load; the matrix's fp32 scale
-// multiplies the accumulators.
-struct WNvfp4 {
-  static constexpr int kAtom = kAtomBytesNV;
-  static constexpr int kStep = 2;
-  static constexpr int kMaxThreads = 1024;
-  static constexpr bool kMatrixScale = true;
-  struct Reg {
-    u32x4 q;
-    uint32_t s;
-  };
-  __device__ static void load_data(Reg& r, const uint8_t* atom, int lane) {
-    r.q = load_atom_data(atom, lane);
-  }
-  __device__ static void load_aux(Reg& r, const uint8_t* atom, int lane) {
-    r.s = *(__attribute__((address_space(1))) const uint16_t*)(atom + kAtomData + 2 * lane);
-  }
-  __device__ static bf16x8 op(const Reg& r, int j) {
-    return dequant8_nv(r.q[j], (r.s >> (8 * (j >> 1))) & 0xFFu);
-  }
-};
-
 // Streaming variants for calls of at most 16 tokens (one M tile).  A wave
 // covers CPW consecutive K chunks in steps of two chunks with two steps of
 // weight loads in flight (double-buffered registers), so a wave can cover
@@ -702,30 +730,55 @@ static int items_for(const Ctx* c, int T, ItemRange part) {
   const int u = std::min(T * c->cfg.top_k, c->cfg.n_experts);
   return part == kItemsCopied ? u : u + c->cfg.has_shared;
 }
-static const int32_t* items_lo(const DecodeScratch& s, ItemRange part) {
-  return part == kItemsCopied ? &s.meta->n_items_a : &s.meta->zero;
-}
-static const int32_t* items_hi(const DecodeScratch& s, ItemRange part) {
-  return part == kItemsResident ? &s.meta->n_items_a : &s.meta->n_items;
+static ExpertList decode_list(const Ctx* c, const DecodeScratch& s, int T, ItemRange part) {
+  ExpertList L;
+  L.items = s.items;
+  L.items_cap = s.max_items;
+  L.lo_p = part == kItemsCopied ? &s.meta->n_items_a : &s.meta->zero;
+  L.hi_p = part == kItemsResident ? &s.meta->n_items_a : &s.meta->n_items;
+  L.grid_items = items_for(c, T, part);
+  L.split_items = items_for(c, T, kItemsAll);
+  L.tok = s.tok;
+  L.h = s.h;
+  L.lo_plane = s.lo_plane;
+  L.yperm = s.yperm;
+  L.stream = T <= kMaxStreamTokens;
+  return L;
 }
 
-hipError_t launch_expert_gateup(const Ctx* c, const DecodeScratch& s, const uint16_t* x, int T,
-                                ItemRange part, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  dim3 grid(c->cfg.inter / kAtomRows, items_for(c, T, part));
-  const int32_t* lo_p = items_lo(s, part);
-  const int32_t* hi_p = items_hi(s, part);
-  const size_t lo = s.lo_plane;
-  const int KC = c->cfg.hidden / kAtomK;
+// The K split of the kernels for more than 16 rows per item: within the
+// format's workgroup size, for the whole list whichever part a launch
+// covers (so that an expert's partial sums meet in the same order resident
+// or copied).
+static Split list_split(const Ctx* c, const ExpertList& L, int KC, int row_groups) {
+  const int max_waves = c->cfg.weight_format == MOE_WEIGHTS_BF16 ? WBf16::kMaxThreads / 64 : kMaxWaves;
+  int s = 1;
+  while (s < max_waves && s * row_groups * L.split_items < 4096) s *= 2;
+  s = std::max(s, (KC + 3) / 4);
+  s = std::min(s, std::min(max_waves, KC));
+  return {s, (KC + s - 1) / s};
+}
+
+bool list_split_fits(const Ctx* c, int K) {
+  const int max_waves = c->cfg.weight_format == MOE_WEIGHTS_BF16 ? WBf16::kMaxThreads / 64 : kMaxWaves;
+  return K / kAtomK <= 4 * max_waves;
+}
+
+hipError_t launch_gateup_list(const Ctx* c, const ExpertList& L, const uint16_t* x,
+                              uint32_t x_bytes, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  dim3 grid(c->cfg.inter / kAtomRows, L.grid_items);
+  const size_t lo = L.lo_plane;
+  const int H = c->cfg.hidden, I = c->cfg.inter;
+  const int KC = H / kAtomK;
   const bool bf16 = c->cfg.weight_format == MOE_WEIGHTS_BF16;
   const bool nv = c->cfg.weight_format == MOE_WEIGHTS_NVFP4;
-  const size_t ms_off = nv ? nv_trailer_offset(c->cfg.hidden, c->cfg.inter) : 0;
-  if (T <= kMaxStreamTokens) {
+  const size_t ms_off = nv ? nv_trailer_offset(H, I) : 0;
+  if (L.stream) {
     const int cpw = bf16 ? bf16_stream_cpw(KC, gateup_stream_cpw(KC)) : gateup_stream_cpw(KC);
     const int waves = stream_waves(KC, cpw);
 #define GATEUP_S(N, F)                                                                     \
   MOE_LAUNCH((gateup_stream_kernel<N, F>), grid, waves * 64, waves * 2 * 64 * 16, st, ev0, \
-             ev1, s.items, s.max_items, lo_p, hi_p, s.tok, x, (uint32_t)T * c->cfg.hidden * 2,          \
-             c->cfg.hidden, c->cfg.inter, s.h, lo, ms_off)
+             ev1, L.items, L.items_cap, L.lo_p, L.hi_p, L.tok, x, x_bytes, H, I, L.h, lo, ms_off)
 #define GATEUP_F(N) \
   if (bf16) GATEUP_S(N, WBf16); else if (nv) GATEUP_S(N, WNvfp4); else GATEUP_S(N, WMxfp4);
     switch (cpw) {
@@ -739,14 +792,13 @@ hipError_t launch_expert_gateup(const Ctx* c, const DecodeScratch& s, const uint
 #undef GATEUP_S
     return hipGetLastError();
   }
-  if (bf16 || nv) return hipErrorNotSupported;  // such contexts have max_tokens <= 16
-  // the split of the whole list, whichever part this launch covers, so
-  // that an expert's partial sums meet in the same order resident or copied
-  const Split sp = split_k(KC, grid.x * items_for(c, T, kItemsAll), 4);
-#define GATEUP(N)                                                                             \
-  MOE_LAUNCH(gateup_decode_kernel<N>, grid, sp.waves * 64, sp.waves * 2 * 64 * 16, st, ev0, ev1, \
-             s.items, s.max_items, lo_p, hi_p, s.tok, x, (uint32_t)T * c->cfg.hidden * 2, c->cfg.hidden,     \
-             c->cfg.inter, s.h, lo)
+  if (!list_split_fits(c, H)) return hipErrorNotSupported;
+  const Split sp = list_split(c, L, KC, grid.x);
+#define GATEUP_L(N, F)                                                                          \
+  MOE_LAUNCH((gateup_decode_kernel<N, F>), grid, sp.waves * 64, sp.waves * 2 * 64 * 16, st, ev0, \
+             ev1, L.items, L.items_cap, L.lo_p, L.hi_p, L.tok, x, x_bytes, H, I, L.h, lo, ms_off)
+#define GATEUP(N) \
+  if (bf16) GATEUP_L(N, WBf16); else if (nv) GATEUP_L(N, WNvfp4); else GATEUP_L(N, WMxfp4);
   switch (sp.cpw) {
     case 1: GATEUP(1); break;
     case 2: GATEUP(2); break;
@@ -754,27 +806,26 @@ hipError_t launch_expert_gateup(const Ctx* c, const DecodeScratch& s, const uint
     default: GATEUP(4); break;
   }
 #undef GATEUP
+#undef GATEUP_L
   return hipGetLastError();
 }
 
-hipError_t launch_expert_down(const Ctx* c, const DecodeScratch& s, int T, ItemRange part,
-                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  dim3 grid(c->cfg.hidden / (2 * kAtomRows), items_for(c, T, part));
-  const int32_t* lo_p = items_lo(s, part);
-  const int32_t* hi_p = items_hi(s, part);
-  const size_t lo = s.lo_plane;
+hipError_t launch_down_list(const Ctx* c, const ExpertList& L, hipStream_t st, hipEvent_t ev0,
+                            hipEvent_t ev1) {
+  dim3 grid(c->cfg.hidden / (2 * kAtomRows), L.grid_items);
+  const size_t lo = L.lo_plane;
+  const int H = c->cfg.hidden, I = c->cfg.inter;
   const bool bf16 = c->cfg.weight_format == MOE_WEIGHTS_BF16;
   const bool nv = c->cfg.weight_format == MOE_WEIGHTS_NVFP4;
-  const size_t ms_off = nv ? nv_trailer_offset(c->cfg.hidden, c->cfg.inter) : 0;
-  const size_t gub = gateup_section_bytes(c->cfg.hidden, c->cfg.inter, c->cfg.weight_format);
-  const int KC = c->cfg.inter / kAtomK;
-  if (T <= kMaxStreamTokens) {
+  const size_t ms_off = nv ? nv_trailer_offset(H, I) : 0;
+  const size_t gub = gateup_section_bytes(H, I, c->cfg.weight_format);
+  const int KC = I / kAtomK;
+  if (L.stream) {
     const int cpw = bf16 ? bf16_stream_cpw(KC, down_stream_cpw(KC)) : down_stream_cpw(KC);
     const int waves = stream_waves(KC, cpw);
 #define DOWN_S(N, F)                                                                         \
   MOE_LAUNCH((down_stream_kernel<N, F>), grid, waves * 64, waves * 2 * 64 * 16, st, ev0, ev1, \
-             s.items, s.max_items, lo_p, hi_p, s.h, lo, c->cfg.hidden, c->cfg.inter, gub, s.yperm, \
-             ms_off)
+             L.items, L.items_cap, L.lo_p, L.hi_p, L.h, lo, H, I, gub, L.yperm, ms_off)
 #define DOWN_F(N) \
   if (bf16) DOWN_S(N, WBf16); else if (nv) DOWN_S(N, WNvfp4); else DOWN_S(N, WMxfp4);
     switch (cpw) {
@@ -788,13 +839,13 @@ hipError_t launch_expert_down(const Ctx* c, const DecodeScratch& s, int T, ItemR
 #undef DOWN_S
     return hipGetLastError();
   }
-  if (bf16 || nv) return hipErrorNotSupported;  // such contexts have max_tokens <= 16
-  // the split of the whole list, whichever part this launch covers, so
-  // that an expert's partial sums meet in the same order resident or copied
-  const Split sp = split_k(KC, grid.x * items_for(c, T, kItemsAll), 4);
-#define DOWN(N)                                                                             \
-  MOE_LAUNCH(down_decode_kernel<N>, grid, sp.waves * 64, sp.waves * 2 * 64 * 16, st, ev0, ev1, \
-             s.items, s.max_items, lo_p, hi_p, s.h, lo, c->cfg.hidden, c->cfg.inter, gub, s.yperm)
+  if (!list_split_fits(c, I)) return hipErrorNotSupported;
+  const Split sp = list_split(c, L, KC, grid.x);
+#define DOWN_L(N, F)                                                                          \
+  MOE_LAUNCH((down_decode_kernel<N, F>), grid, sp.waves * 64, sp.waves * 2 * 64 * 16, st, ev0, \
+             ev1, L.items, L.items_cap, L.lo_p, L.hi_p, L.h, lo, H, I, gub, L.yperm, ms_off)
+#define DOWN(N) \
+  if (bf16) DOWN_L(N, WBf16); else if (nv) DOWN_L(N, WNvfp4); else DOWN_L(N, WMxfp4);
   switch (sp.cpw) {
     case 1: DOWN(1); break;
     case 2: DOWN(2); break;
@@ -802,7 +853,19 @@ hipError_t launch_expert_down(const Ctx* c, const DecodeScratch& s, int T, ItemR
     default: DOWN(4); break;
   }
 #undef DOWN
+#undef DOWN_L
   return hipGetLastError();
+}
+
+hipError_t launch_expert_gateup(const Ctx* c, const DecodeScratch& s, const uint16_t* x, int T,
+                                ItemRange part, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  return launch_gateup_list(c, decode_list(c, s, T, part), x, (uint32_t)T * c->cfg.hidden * 2, st,
+                            ev0, ev1);
+}
+
+hipError_t launch_expert_down(const Ctx* c, const DecodeScratch& s, int T, ItemRange part,
+                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  return launch_down_list(c, decode_list(c, s, T, part), st, ev0, ev1);
 }
 
 hipError_t launch_combine_rows(const float* yperm, const int32_t* inv, const float* gates, int T,

@@ -286,6 +286,31 @@ hipError_t launch_copy_pairs(const FillEntry* pairs, int n, size_t bytes,
                              hipStream_t st);
 hipError_t launch_probe_copy(const void* src, void* dst, size_t n_bytes,
                              hipStream_t st);
+// What one launch of the expert kernels covers: items [*lo_p, *hi_p) of a
+// work list, the token of each permuted row, h (two bf16 planes, lo_plane
+// elements apart) and the fp32 expert outputs.
+struct ExpertList {
+  const WorkItem* items = nullptr;
+  int items_cap = 0;                // entries of items[]
+  const int32_t* lo_p = nullptr;    // device bounds of the items covered
+  const int32_t* hi_p = nullptr;
+  int grid_items = 0;               // grid rows: the most items the bounds can hold
+  int split_items = 0;              // items the K split is chosen for (the whole list)
+  const int32_t* tok = nullptr;     // permuted row -> token
+  uint16_t* h = nullptr;
+  size_t lo_plane = 0;
+  float* yperm = nullptr;
+  bool stream = false;              // at most 16 rows per item: the streaming kernels
+};
+hipError_t launch_gateup_list(const Ctx* c, const ExpertList& L, const uint16_t* x,
+                              uint32_t x_bytes, hipStream_t st, hipEvent_t ev0 = nullptr,
+                              hipEvent_t ev1 = nullptr);
+hipError_t launch_down_list(const Ctx* c, const ExpertList& L, hipStream_t st,
+                            hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+// whether the kernels for more than 16 rows per item can split a K of this
+// length (bf16 weights take at most 8 waves of 4 chunks)
+bool list_split_fits(const Ctx* c, int K);
+
 // Which part of the work list an expert-kernel launch covers: all items,
 // the resident experts and the shared one, or the experts this call copies.
 enum ItemRange { kItemsAll, kItemsResident, kItemsCopied };

@@ -37,9 +37,24 @@ struct Prefill {
                                // [rows][I] then its scales [rows][I/32]
   uint8_t* xq = nullptr;       // MXFP8 mode: x codes [Tmax][H], then scales
                                // [Tmax][H/32] (allocated on first use)
+  // bf16 and NVFP4 experts: a work list of chunks of at most
+  // kPrefillRowsPerItem rows per expert (h then holds two bf16 planes)
+  WorkItem* items = nullptr;
+  int32_t* bounds = nullptr;   // [2]: first and end item of the list
+  int items_cap = 0;
   uint8_t* hlo = nullptr;      // low-order records of h: [max_tiles][I/128][8][1664]
   float* yperm = nullptr;      // [rows][H]
 };
+
+// Rows per work item when bf16 or NVFP4 experts run prefill through the
+// decode kernels (which hold a weight slice in registers and loop over the
+// item's 16-row tiles): large groups (the shared expert's T rows) are cut
+// into chunks so that the launch has enough workgroups.
+constexpr int kPrefillRowsPerItem = 128;
+int prefill_items_cap(int T, int k, int E) {
+  const int R = kPrefillRowsPerItem;
+  return (T * k + R - 1) / R + E + (T + R - 1) / R + 1;
+}
 
 // Tiles of 128 rows: every group's partial tile plus the whole rows, rounded
 // up to a multiple of 8 (the launch deals tiles to the 8 XCDs).
@@ -1216,6 +1231,44 @@ hipError_t dalloc(T** p, size_t n) {
   return hipMalloc((void**)p, std::max<size_t>(n, 1) * sizeof(T));
 }
 
+// Work list of a layer for the decode kernels: every routed expert's rows
+// in chunks of kPrefillRowsPerItem (experts ascending), then the shared
+// expert's T rows likewise.  One workgroup of 1024 threads, thread e for
+// expert e (E <= 1024).
+__global__ __launch_bounds__(1024) void build_items_kernel(
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, int E, int T, int k,
+    int has_shared, const uint8_t* layer_w, size_t stride, const uint8_t* shared_w,
+    WorkItem* __restrict__ items, int32_t* __restrict__ bounds) {
+  constexpr int R = kPrefillRowsPerItem;
+  __shared__ int scan[1024];
+  const int e = threadIdx.x;
+  const int cnt = e < E ? counts[e] : 0;
+  const int nch = (cnt + R - 1) / R;
+  scan[e] = nch;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {  // inclusive scan
+    const int v = e >= d ? scan[e - d] : 0;
+    __syncthreads();
+    scan[e] += v;
+    __syncthreads();
+  }
+  const int base = scan[e] - nch;
+  for (int c = 0; c < nch; c++) {
+    const int r0 = c * R;
+    items[base + c] = WorkItem{layer_w + (size_t)e * stride, offsets[e] + r0, min(R, cnt - r0)};
+  }
+  const int routed = scan[1023];
+  const int nsh = has_shared ? (T + R - 1) / R : 0;
+  for (int c = e; c < nsh; c += blockDim.x) {
+    const int r0 = c * R;
+    items[routed + c] = WorkItem{shared_w, T * k + r0, min(R, T - r0)};
+  }
+  if (e == 0) {
+    bounds[0] = 0;
+    bounds[1] = routed + nsh;
+  }
+}
+
 hipError_t prefill_alloc(Ctx* c) {
   if (c->pf) return hipSuccess;
   const moe_config& f = c->cfg;
@@ -1241,9 +1294,15 @@ hipError_t prefill_alloc(Ctx* c) {
   PA(tok, rows);
   PA(tiles, (size_t)p->max_tiles);
   PA(n_tiles, 1);
-  PA(h, rows * f.inter);
-  PA(hlo, prefill_lo_bytes(T, k, E, f.inter));
+  const bool streamed = f.weight_format != MOE_WEIGHTS_MXFP4;
+  PA(h, (streamed ? 2 : 1) * rows * f.inter);
+  if (!streamed) PA(hlo, prefill_lo_bytes(T, k, E, f.inter));
   PA(yperm, rows * f.hidden);
+  if (streamed) {
+    p->items_cap = prefill_items_cap(T, k, E);
+    PA(items, (size_t)p->items_cap);
+    PA(bounds, 2);
+  }
 #undef PA
   const size_t layer_bytes = (size_t)E * c->stride;
   for (int b = 0; b < 2; b++)
@@ -1260,7 +1319,8 @@ hipError_t prefill_alloc(Ctx* c) {
 void prefill_free(Ctx* c) {
   if (Prefill* p = c->pf) {
     void* ptrs[] = {p->logits, p->ids, p->gates, p->chunk_cnt, p->counts, p->offsets, p->sorted,
-                    p->inv, p->tok, p->tiles, p->n_tiles, p->h, p->hlo, p->yperm, p->xq};
+                    p->inv, p->tok, p->tiles, p->n_tiles, p->h, p->hlo, p->yperm, p->xq,
+                    p->items, p->bounds};
     for (void* q : ptrs)
       if (q) (void)hipFree(q);
     delete p;
@@ -1416,7 +1476,28 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
     const int nbn_gu = (2 * I + 511) / 512, nbn_dn = (H + 511) / 512;
     const size_t hhi_bytes = (size_t)p->Tmax * (k + 1) * I * 2;
     const size_t hlo_bytes = prefill_lo_bytes(p->Tmax, k, E, I);
-    if (mx) {
+    if (p->items) {
+      // bf16 or NVFP4 experts: the decode kernels over a work list of
+      // 128-row chunks, h as two bf16 planes
+      build_items_kernel<<<1, 1024, 0, st>>>(
+          counts, offsets, E, T, k, f.has_shared, c->d_layerbuf[b], c->stride,
+          f.has_shared ? c->d_shared + (size_t)l * c->stride : nullptr, p->items, p->bounds);
+      ExpertList L;
+      L.items = p->items;
+      L.items_cap = p->items_cap;
+      L.lo_p = p->bounds;
+      L.hi_p = p->bounds + 1;
+      L.grid_items = L.split_items = p->items_cap;
+      L.tok = p->tok;
+      L.h = p->h;
+      L.lo_plane = (size_t)p->Tmax * (k + 1) * I;
+      L.yperm = p->yperm;
+      L.stream = false;
+      if ((e = launch_gateup_list(c, L, x, (uint32_t)T * H * 2, st, t0(kPfGateUp),
+                                  t1(kPfGateUp))) != hipSuccess)
+        return e;
+      if ((e = launch_down_list(c, L, st, t0(kPfDown), t1(kPfDown))) != hipSuccess) return e;
+    } else if (mx) {
       const size_t rows_cap = (size_t)p->Tmax * (k + 1);
       uint8_t* const hq = reinterpret_cast<uint8_t*>(p->h);
       uint8_t* const hs = hq + rows_cap * I;

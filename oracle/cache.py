@@ -22,6 +22,21 @@ lookup(layer, U) for the ascending unique experts U of one call:
      (evicting its key; clock += 1; stamp; a fill of that slot is issued);
      otherwise it bypasses the cache through staging slot b (the b-th
      bypass), encoded -1-b, and the state is unchanged.
+prefetch(layer, U, pinned) for ascending unique experts U (global policy):
+  the same as a lookup except that
+  - a miss may take only empty slots (ascending index) and occupied slots
+    whose stamp <= pinned (ascending stamp), where pinned is the clock
+    before the lookup of the call that issues the prefetch, so that nothing
+    that call uses is displaced while its kernels read it;
+  - a miss with no such slot is skipped: no staging copy, state unchanged.
+  Hits are stamped and the clock advances as in a lookup.  Its counts are
+  kept apart (pf_lookups, pf_hits, pf_fills); its evictions add to
+  evictions.  This build's reading of a cross-layer prefetch of likely
+  misses: the pages carry the layer-ahead upload into prefill (aipolix.com
+  FreeToken article, fourth paragraph) and mention preloading experts that
+  activation patterns mark as likely (world.tibi.club FreeToken article,
+  section "Cum reușește FreeToken să ruleze 753B pe un singur GPU?", third
+  technique) without a rule.
 resize(C'): grow appends empty slots; shrink evicts occupied slots in
   ascending stamp while occupancy > C', then moves every survivor in a slot
   >= C' (ascending) to the lowest empty slot < C' (ascending), keeping key
@@ -56,6 +71,7 @@ class SlotCache:
         self.stamp = [0] * capacity
         self.clock = 0
         self.hits = self.fills = self.bypasses = self.evictions = 0
+        self.pf_lookups = self.pf_hits = self.pf_fills = 0
 
     @property
     def capacity(self):
@@ -123,6 +139,38 @@ class SlotCache:
                 bypass.append((b, layer, e))
                 self.bypasses += 1
         return slots, fills, bypass
+
+    def prefetch(self, layer: int, experts, pinned: int):
+        """Insert-only lookup of a predicted set (see the module docstring).
+        Returns the fills [(slot, layer, expert)] in issue order."""
+        assert self.policy == "global", "prefetch is defined for the global policy only"
+        experts = [int(e) for e in experts]
+        assert experts == sorted(set(experts)), "experts must be ascending unique"
+        keys = [layer * self.E + e for e in experts]
+        misses = []
+        for kk, e in zip(keys, experts):
+            s = self.slot_of(kk)
+            self.pf_lookups += 1
+            if s is None:
+                misses.append((kk, e))
+            else:
+                self.clock += 1
+                self.stamp[s] = self.clock
+                self.pf_hits += 1
+        empty = [s for s in range(self.capacity) if self.key[s] < 0]
+        old = sorted((self.stamp[s], s) for s in range(self.capacity)
+                     if self.key[s] >= 0 and self.stamp[s] <= pinned)
+        victims = empty + [s for _, s in old]
+        fills = []
+        for (kk, e), s in zip(misses, victims):
+            if self.key[s] >= 0:
+                self.evictions += 1
+            self.key[s] = kk
+            self.clock += 1
+            self.stamp[s] = self.clock
+            fills.append((s, layer, e))
+            self.pf_fills += 1
+        return fills
 
     def fill(self, layer: int, experts):
         """Explicit preload: the same rule as a lookup, inserting under every

@@ -258,3 +258,103 @@ def test_reset_is_a_fresh_cache_at_the_same_clock():
             for u in post:
                 assert a.lookup(0, list(u)) == b.lookup(0, list(u))
                 assert a.snapshot() == b.snapshot()
+
+
+# ------------------------------------------------------------------ prefetch
+def test_prefetch_hand_computed():
+    """C=6, E=8, two layers.  Layer 0 takes slots 0-2, layer 1 slots 3-4;
+    the issuing call (layer 0, experts 2 and 3) starts at clock 5, hits slot
+    2 and fills slot 5.  Its prefetch of layer 1's experts 1, 4, 5, 6, 7:
+    expert 1 hits (slot 4, stamp 8); only slots 0, 1, 3 hold stamps <= 5, so
+    4, 5, 6 take them in that (stamp) order and 7 is skipped -- slots 2 and 5,
+    which the issuing call uses, are never victims."""
+    c = SlotCache(6, 8, 2)
+    c.lookup(0, [0, 1, 2])
+    c.lookup(1, [0, 1])
+    pinned = c.clock
+    assert pinned == 5
+    c.lookup(0, [2, 3])
+    fills = c.prefetch(1, [1, 4, 5, 6, 7], pinned)
+    assert fills == [(0, 1, 4), (1, 1, 5), (3, 1, 6)]
+    assert c.key == [12, 13, 2, 14, 9, 3]
+    assert c.stamp == [9, 10, 6, 11, 8, 7]
+    assert c.clock == 11
+    assert (c.pf_lookups, c.pf_hits, c.pf_fills) == (5, 1, 3)
+    assert c.evictions == 3 and (c.hits, c.fills, c.bypasses) == (1, 6, 0)
+    # the prefetched experts are hits for the next layer's lookup
+    slots, f2, byp = c.lookup(1, [4, 6])
+    assert slots == [0, 3] and not f2 and not byp
+
+
+def test_prefetch_into_empty_slots_ascending():
+    c = SlotCache(5, 4, 2)
+    c.lookup(0, [3])                      # slot 0
+    pinned = c.clock
+    c.lookup(0, [1])                      # slot 1
+    assert c.prefetch(1, [0, 2], pinned) == [(2, 1, 0), (3, 1, 2)]
+    assert c.key == [3, 1, 4, 6, -1] and c.stamp == [1, 2, 3, 4, 0]
+
+
+def _prefetch_brute(key, stamp, clock, E, layer, experts, pinned):
+    """Independent statement: hits restamped in ascending expert order;
+    eligible = slots not holding a listed key with (empty or stamp <= pinned),
+    taken in (stamp, index) order by the misses in ascending expert order."""
+    key, stamp = list(key), list(stamp)
+    listed = {layer * E + e for e in experts}
+    for e in experts:
+        kk = layer * E + e
+        if kk in key:
+            clock += 1
+            stamp[key.index(kk)] = clock
+    eligible = sorted((s for s in range(len(key))
+                       if key[s] not in listed and (key[s] < 0 or stamp[s] <= pinned)),
+                      key=lambda s: (stamp[s], s))
+    misses = [e for e in experts if layer * E + e not in key]
+    for e, s in zip(misses, eligible):
+        key[s] = layer * E + e
+        clock += 1
+        stamp[s] = clock
+    return key, stamp, clock
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_prefetch_matches_brute_force(seed):
+    """Random traces of lookups, each followed by a prefetch of a random set
+    of another layer, against the brute-force statement; and the slots the
+    issuing call used keep their keys."""
+    rng = np.random.default_rng(seed)
+    C, E, L = int(rng.integers(1, 12)), int(rng.integers(2, 10)), 3
+    c = SlotCache(C, E, L)
+    for _ in range(30):
+        layer = int(rng.integers(L))
+        U = sorted(set(rng.integers(0, E, int(rng.integers(1, E + 1))).tolist()))
+        pinned = c.clock
+        slots, _, _ = c.lookup(layer, U)
+        used = {s for s in slots if s >= 0}
+        nxt = (layer + 1) % L
+        P = sorted(set(rng.integers(0, E, int(rng.integers(0, E + 1))).tolist()))
+        before = (list(c.key), list(c.stamp), c.clock)
+        want = _prefetch_brute(*before, E, nxt, P, pinned)
+        fills = c.prefetch(nxt, P, pinned)
+        assert (c.key, c.stamp, c.clock) == want
+        assert all(c.key[s] == before[0][s] for s in used)
+        assert len(fills) == sum(1 for kk in {nxt * E + e for e in P}
+                                 if kk in c.key and kk not in before[0])
+
+
+def test_prefetch_with_nothing_pinned_is_a_lookup():
+    """With pinned equal to the current clock (no issuing call) and enough
+    room, a prefetch leaves the state a lookup of the same set leaves."""
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        a, b = SlotCache(8, 6, 2), SlotCache(8, 6, 2)
+        for _ in range(6):
+            layer = int(rng.integers(2))
+            U = sorted(set(rng.integers(0, 6, 3).tolist()))
+            a.lookup(layer, U)
+            b.lookup(layer, U)
+        P = sorted(set(rng.integers(0, 6, 3).tolist()))
+        a.prefetch(1, P, a.clock)
+        _, _, byp = b.lookup(1, P)
+        assert not byp
+        assert (a.key, a.stamp, a.clock) == (b.key, b.stamp, b.clock)

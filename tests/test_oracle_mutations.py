@@ -306,6 +306,53 @@ def m_lookup_victims_most_recent_first(mp):
     mp.setattr(ocache.SlotCache, "lookup", lookup)
 
 
+def m_prefetch_ignores_pinning(mp):
+    good = ocache.SlotCache.prefetch
+
+    def prefetch(self, layer, experts, pinned):
+        return good(self, layer, experts, self.clock)
+    mp.setattr(ocache.SlotCache, "prefetch", prefetch)
+
+
+def m_prefetch_hits_not_stamped(mp):
+    good = ocache.SlotCache.prefetch
+
+    def prefetch(self, layer, experts, pinned):
+        keys = {layer * self.E + int(e) for e in experts}
+        kept = {s: self.stamp[s] for s in range(self.capacity) if self.key[s] in keys}
+        fills = good(self, layer, experts, pinned)
+        for s, st in kept.items():
+            if self.key[s] in keys:
+                self.stamp[s] = st
+        return fills
+    mp.setattr(ocache.SlotCache, "prefetch", prefetch)
+
+
+def m_prefetch_victims_by_index(mp):
+    def prefetch(self, layer, experts, pinned):
+        experts = [int(e) for e in experts]
+        misses = []
+        for e in experts:
+            kk = layer * self.E + e
+            s = self.slot_of(kk)
+            if s is None:
+                misses.append(kk)
+            else:
+                self.clock += 1
+                self.stamp[s] = self.clock
+        victims = [s for s in range(self.capacity)
+                   if self.key[s] < 0 or (self.stamp[s] <= pinned and self.key[s] not in
+                                          {layer * self.E + x for x in experts})]
+        fills = []
+        for kk, s in zip(misses, victims):
+            self.key[s] = kk
+            self.clock += 1
+            self.stamp[s] = self.clock
+            fills.append((s, layer, kk - layer * self.E))
+        return fills
+    mp.setattr(ocache.SlotCache, "prefetch", prefetch)
+
+
 def m_bf16_truncates(mp):
     def trunc(a):
         u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
@@ -457,7 +504,10 @@ CACHE_PINS = [p_cache.test_matches_textbook_lru_when_unique_set_fits,
               p_cache.test_bypass_when_unique_set_exceeds_capacity,
               p_cache.test_resize_invariants, p_cache.test_resize_hand_computed_slot_numbering,
               lambda: p_cache.test_resize_brute_force_against_rank_model(4, 3, 3),
-              p_cache.test_reset_is_a_fresh_cache_at_the_same_clock]
+              p_cache.test_reset_is_a_fresh_cache_at_the_same_clock,
+              p_cache.test_prefetch_hand_computed, p_cache.test_prefetch_into_empty_slots_ascending,
+              lambda: [p_cache.test_prefetch_matches_brute_force(s) for s in range(6)],
+              p_cache.test_prefetch_with_nothing_pinned_is_a_lookup]
 MX_PINS = [p_mx.test_e4m3_fields, p_mx.test_round_e4m3_is_nearest_with_ties_to_even,
            p_mx.test_block_scale_rule, p_mx.test_quantize_closed_forms,
            p_mx.test_mx_layer_equals_plain_layer_on_representable_inputs,
@@ -502,6 +552,9 @@ MUTATIONS = [
     (m_reset_keeps_most_recent, CACHE_PINS),
     (m_reset_rewinds_clock, CACHE_PINS),
     (m_lookup_victims_most_recent_first, CACHE_PINS),
+    (m_prefetch_ignores_pinning, CACHE_PINS),
+    (m_prefetch_hits_not_stamped, CACHE_PINS),
+    (m_prefetch_victims_by_index, CACHE_PINS),
     (m_mx_scale_off_by_one, MX_PINS),
     (m_mx_truncates, MX_PINS),
     (m_mx_no_clamp, MX_PINS),

@@ -48,7 +48,8 @@ PREFILL_STAGES = ("routing", "gateup", "down", "combine")
 class moe_stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "forward_calls", "lookups", "hits", "fills", "bypasses", "evictions", "bytes_h2d",
-        "bytes_d2d", "resizes", "prefill_layers")]
+        "bytes_d2d", "resizes", "prefill_layers", "prefetch_lookups", "prefetch_hits",
+        "prefetch_fills")]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
@@ -77,6 +78,7 @@ _SIGS = {
     "moe_inspect_prefill_mx": (_I32, [_P, _P, _P, _P, _P, _P]),
     "moe_get_stats": (_I32, [_P, ctypes.POINTER(moe_stats)]),
     "moe_set_copy_overlap": (_I32, [_P, _I32]),
+    "moe_set_prefetch": (_I32, [_P, _I32, _P, _I32]),
     "moe_set_debug": (_I32, [_P, _I32]),
     "expert_cache_reset": (_I32, [_P]),
     "moe_reset_stats": (_I32, [_P]),
@@ -279,6 +281,10 @@ def moe_inspect_prefill_mx(ctx, H: int, I: int, k: int, shared: bool, T_max: int
 
 def moe_set_copy_overlap(ctx, mode: int):
     _check(lib.moe_set_copy_overlap(ctx, int(mode)), "moe_set_copy_overlap")
+
+
+def moe_set_prefetch(ctx, layer: int, d_experts, n: int):
+    _check(lib.moe_set_prefetch(ctx, int(layer), d_experts, int(n)), "moe_set_prefetch")
 
 
 DEBUG_SYNC, DEBUG_FAIL_NEXT_FILL = 1, 2

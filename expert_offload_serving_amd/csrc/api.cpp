@@ -78,6 +78,13 @@ void destroy_all(Ctx* c) {
   if (c->ev_routed) (void)hipEventDestroy(c->ev_routed);
   if (c->ev_resident) (void)hipEventDestroy(c->ev_resident);
   c->ev_routed = c->ev_resident = nullptr;
+  if (c->pf_stream) (void)hipStreamDestroy(c->pf_stream);
+  c->pf_stream = nullptr;
+  if (c->ev_filled) (void)hipEventDestroy(c->ev_filled);
+  if (c->ev_pf_done) (void)hipEventDestroy(c->ev_pf_done);
+  c->ev_filled = c->ev_pf_done = nullptr;
+  dfree(c->d_pf_fills);
+  dfree(c->d_pf_meta);
 }
 
 // Run fn(i) for i in [0, n) on up to `threads` host threads.
@@ -310,8 +317,9 @@ namespace {
 // injected failure of MOE_DEBUG_FAIL_NEXT_FILL) leaves slots that name
 // experts whose bytes did not land: the context then refuses cache work
 // until expert_cache_reset.
-static moe_status issue_fill(Ctx* c, const DecodeScratch& s, int max_fill, bool confined,
-                             hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
+static moe_status issue_fill(Ctx* c, const FillEntry* fills, const DevMeta* meta, int max_fill,
+                             bool confined, hipStream_t st, hipEvent_t ev0 = nullptr,
+                             hipEvent_t ev1 = nullptr) {
   if (c->debug_flags & MOE_DEBUG_FAIL_NEXT_FILL) {
     c->debug_flags &= ~MOE_DEBUG_FAIL_NEXT_FILL;
     c->failed = true;
@@ -319,7 +327,7 @@ static moe_status issue_fill(Ctx* c, const DecodeScratch& s, int max_fill, bool 
                 "fill: injected failure, the copies were not issued (expert_cache_reset "
                 "empties the cache)");
   }
-  const hipError_t e = launch_fill(s.fills, s.meta, max_fill, c->rec_bytes, confined, st, ev0, ev1);
+  const hipError_t e = launch_fill(fills, meta, max_fill, c->rec_bytes, confined, st, ev0, ev1);
   if (e != hipSuccess) {
     c->failed = true;
     return fail(MOE_ERR_HIP, std::string("fill: ") + hipGetErrorString(e) +
@@ -343,6 +351,8 @@ moe_status decode_forward(Ctx* c, const DecodeScratch& s, int layer, const uint1
                           const float* bias, uint16_t* y, float* y32, int32_t* ids,
                           float* gates, hipStream_t st, bool allow_timing) {
   const moe_config& f = c->cfg;
+  const Ctx::PrefetchReq pr = c->pf_req;  // consumed by this call
+  c->pf_req = Ctx::PrefetchReq{};
   // The resident experts' kernels run beside the copies of the missed ones
   // when one expert's copy is long (split_fills); not under stream capture,
   // where the whole call stays on one stream.
@@ -367,14 +377,35 @@ moe_status decode_forward(Ctx* c, const DecodeScratch& s, int layer, const uint1
   HIPCHK(launch_route_finalize(c, s, layer, T, ids, gates, st, t0(kStFinalize),
                                t1(kStFinalize)));
   if (moe_status r = done(false, "finalize")) return r;
+  // A prefetch armed by moe_set_prefetch: looked up and copied once this
+  // call's own copies are done, beside its expert kernels (on the prefetch
+  // stream; under capture in order on `stream`), and joined back before the
+  // call ends.
+  bool pf_issued = false;
+  auto prefetch = [&]() -> moe_status {
+    if (pr.n <= 0) return MOE_OK;
+    hipStream_t ps = capturing ? st : c->pf_stream;
+    if (!capturing) {
+      HIPCHK(hipEventRecord(c->ev_filled, st));
+      HIPCHK(hipStreamWaitEvent(ps, c->ev_filled, 0));
+    }
+    HIPCHK(launch_cache_prefetch(c, pr.layer, pr.experts, pr.n, s.meta, ps));
+    if (moe_status r = issue_fill(c, c->d_pf_fills, c->d_pf_meta, pr.n, true, ps)) return r;
+    if (!capturing) {
+      HIPCHK(hipEventRecord(c->ev_pf_done, ps));
+      pf_issued = true;
+    }
+    return debug_sync(c, ps, false, capturing, "prefetch");
+  };
   if (split) {
     // The fills follow finalize on `stream`, so that their workgroups are
     // placed first; the resident experts run on the internal stream once
     // the lists exist (its event wait delays them behind the fill's
     // dispatch); the copied experts run on `stream` after both.
     HIPCHK(hipEventRecord(c->ev_routed, st));
-    if (moe_status r = issue_fill(c, s, max_fill, true, st, t0(kStFill), t1(kStFill))) return r;
+    if (moe_status r = issue_fill(c, s.fills, s.meta, max_fill, true, st, t0(kStFill), t1(kStFill))) return r;
     if (moe_status r = done(false, "fill")) return r;
+    if (moe_status r = prefetch()) return r;
     HIPCHK(hipStreamWaitEvent(c->copy_stream, c->ev_routed, 0));
     HIPCHK(launch_expert_gateup(c, s, x, T, kItemsResident, c->copy_stream, t0(kStGateUp),
                                 t1(kStGateUp)));
@@ -388,8 +419,9 @@ moe_status decode_forward(Ctx* c, const DecodeScratch& s, int layer, const uint1
     HIPCHK(launch_expert_down(c, s, T, kItemsCopied, st, t0(kStDownB), t1(kStDownB)));
     if (moe_status r = done(false, "down (copied experts)")) return r;
   } else {
-    if (moe_status r = issue_fill(c, s, max_fill, false, st, t0(kStFill), t1(kStFill))) return r;
+    if (moe_status r = issue_fill(c, s.fills, s.meta, max_fill, false, st, t0(kStFill), t1(kStFill))) return r;
     if (moe_status r = done(false, "fill")) return r;
+    if (moe_status r = prefetch()) return r;
     HIPCHK(launch_expert_gateup(c, s, x, T, kItemsAll, st, t0(kStGateUp), t1(kStGateUp)));
     if (moe_status r = done(false, "gate/up")) return r;
     HIPCHK(launch_expert_down(c, s, T, kItemsAll, st, t0(kStDown), t1(kStDown)));
@@ -398,6 +430,7 @@ moe_status decode_forward(Ctx* c, const DecodeScratch& s, int layer, const uint1
   HIPCHK(launch_combine_rows(s.yperm, s.inv, s.gates, T, f.top_k, f.hidden, f.has_shared, y, y32,
                              st, t0(kStCombine), t1(kStCombine)));
   if (moe_status r = done(false, "combine")) return r;
+  if (pf_issued) HIPCHK(hipStreamWaitEvent(st, c->ev_pf_done, 0));
   if (timed) c->t_decode.push_back(tr);
   return MOE_OK;
 }
@@ -503,14 +536,19 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   ALLOC(c->d_scratch, decode_scratch_layout(f, Tm, nullptr, nullptr));
   decode_scratch_layout(f, Tm, c->d_scratch, &c->ds);
   ALLOC(c->d_lookup_ids, (size_t)(E + 1) * 4);
+  ALLOC(c->d_pf_fills, (size_t)E * sizeof(FillEntry));
+  ALLOC(c->d_pf_meta, sizeof(DevMeta));
   {
     // default priority (the caller's streams are expected to use it too)
     hipError_t es = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking);
-    // the decode events order work between two streams of this device only:
+    if (es == hipSuccess) es = hipStreamCreateWithFlags(&c->pf_stream, hipStreamNonBlocking);
+    // the decode events order work between streams of this device only:
     // no timing, no system-scope release
     const unsigned ef = hipEventDisableTiming | hipEventDisableSystemFence;
     if (es == hipSuccess) es = hipEventCreateWithFlags(&c->ev_routed, ef);
     if (es == hipSuccess) es = hipEventCreateWithFlags(&c->ev_resident, ef);
+    if (es == hipSuccess) es = hipEventCreateWithFlags(&c->ev_filled, ef);
+    if (es == hipSuccess) es = hipEventCreateWithFlags(&c->ev_pf_done, ef);
     if (es != hipSuccess) {
       destroy_all(c);
       delete c;
@@ -529,7 +567,8 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   if (upload(c->d_key, key) != hipSuccess || upload(c->d_order, order) != hipSuccess ||
       upload(c->d_stamp, stamp) != hipSuccess || upload(c->d_map, map) != hipSuccess ||
       hipMemcpy(c->d_cache, zero.data(), sizeof(DevCache), hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy(c->ds.meta, zero.data(), sizeof(DevMeta), hipMemcpyHostToDevice) != hipSuccess) {
+      hipMemcpy(c->ds.meta, zero.data(), sizeof(DevMeta), hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(c->d_pf_meta, zero.data(), sizeof(DevMeta), hipMemcpyHostToDevice) != hipSuccess) {
     destroy_all(c);
     delete c;
     return fail(MOE_ERR_HIP, "initialising cache state");
@@ -757,7 +796,7 @@ moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer, const int32_t* d_exp
     return fail(MOE_ERR_CAPACITY, "staging_slots below worst-case bypass count");
   hipStream_t st = (hipStream_t)stream;
   HIPCHK(launch_cache_lookup(c, layer, d_experts, d_n, c->ds.max_unique, d_slot, false, st));
-  return issue_fill(c, c->ds, c->ds.max_unique, false, st);
+  return issue_fill(c, c->ds.fills, c->ds.meta, c->ds.max_unique, false, st);
 }
 
 moe_status expert_cache_fill(moe_ctx* ctx, int32_t layer, const int32_t* h_experts,
@@ -784,7 +823,7 @@ moe_status expert_cache_fill(moe_ctx* ctx, int32_t layer, const int32_t* h_exper
   HIPCHK(hipMemcpy(c->d_lookup_ids, buf.data(), buf.size() * 4, hipMemcpyHostToDevice));
   HIPCHK(launch_cache_lookup(c, layer, c->d_lookup_ids, c->d_lookup_ids + n, n, c->ds.slotcode,
                              true, st));
-  if (moe_status r = issue_fill(c, c->ds, n, false, st)) return r;
+  if (moe_status r = issue_fill(c, c->ds.fills, c->ds.meta, n, false, st)) return r;
   HIPCHK(hipStreamSynchronize(st));
   return MOE_OK;
 }
@@ -957,6 +996,20 @@ moe_status moe_inspect_prefill_mx(moe_ctx* ctx, int32_t* h_T, uint8_t* h_xq, uin
   return MOE_OK;
 }
 
+moe_status moe_set_prefetch(moe_ctx* ctx, int32_t layer, const int32_t* d_experts,
+                            int32_t n) {
+  if (moe_status s = check_ctx(ctx)) return s;
+  Ctx* c = C_(ctx);
+  if (c->failed) return fail(MOE_ERR_STATE, kFailedMsg);
+  if (c->cfg.cache_policy != MOE_CACHE_GLOBAL)
+    return fail(MOE_ERR_UNSUPPORTED, "prefetch is supported for the global cache policy only");
+  if (layer < 0 || layer >= c->cfg.n_layers || n < 0 || n > c->cfg.n_experts ||
+      (n > 0 && !d_experts))
+    return fail(MOE_ERR_INVALID_ARG, "bad layer, count or NULL list");
+  c->pf_req = n > 0 ? Ctx::PrefetchReq{layer, d_experts, n} : Ctx::PrefetchReq{};
+  return MOE_OK;
+}
+
 moe_status moe_set_copy_overlap(moe_ctx* ctx, int32_t mode) {
   if (moe_status s = check_ctx(ctx)) return s;
   if (mode < -1 || mode > 1) return fail(MOE_ERR_INVALID_ARG, "mode must be -1, 0 or 1");
@@ -978,7 +1031,10 @@ moe_status moe_get_stats(moe_ctx* ctx, moe_stats* out) {
   out->fills = dc.fills;
   out->bypasses = dc.bypasses;
   out->evictions = dc.evictions;
-  out->bytes_h2d = (dc.fills + dc.bypasses) * c->rec_bytes;
+  out->prefetch_lookups = dc.pf_lookups;
+  out->prefetch_hits = dc.pf_hits;
+  out->prefetch_fills = dc.pf_fills;
+  out->bytes_h2d = (dc.fills + dc.bypasses + dc.pf_fills) * c->rec_bytes;
   return MOE_OK;
 }
 

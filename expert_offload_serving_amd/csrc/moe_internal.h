@@ -140,6 +140,7 @@ hipError_t static_scratch_address(int device, uint8_t** out);
 struct DevCache {
   uint64_t clock;
   uint64_t lookups, hits, fills, bypasses, evictions;
+  uint64_t pf_lookups, pf_hits, pf_fills;  // prefetch lookups (moe_set_prefetch)
 };
 
 // Arguments of the block-wide LRU lookup.
@@ -162,6 +163,10 @@ struct LookupArgs {
   size_t stride;           // bytes between records
   FillEntry* fills;        // [max unique]
   DevMeta* meta;
+  // A prefetch (moe_set_prefetch) when non-null: the meta of the call that
+  // issues it, whose hit and filled slots (the most recent entries of the
+  // recency order) are never victims; misses with no victim are skipped.
+  const DevMeta* pin = nullptr;
 };
 
 // ---------------------------------------------------------------------------
@@ -232,6 +237,22 @@ struct Ctx {
   hipEvent_t ev_routed = nullptr;   // decode: the work and fill lists are written
   hipEvent_t ev_resident = nullptr; // decode: the resident experts are computed
 
+  // cross-layer prefetch: the request armed by moe_set_prefetch (consumed
+  // by the next decode call), the stream its lookup and copies run on beside
+  // that call's expert kernels, its fill list and meta, and the events that
+  // start it after the call's own copies and join it back before the call
+  // ends
+  struct PrefetchReq {
+    int layer = -1;
+    const int32_t* experts = nullptr;
+    int n = 0;
+  } pf_req;
+  hipStream_t pf_stream = nullptr;
+  FillEntry* d_pf_fills = nullptr;  // [E]
+  DevMeta* d_pf_meta = nullptr;
+  hipEvent_t ev_filled = nullptr;
+  hipEvent_t ev_pf_done = nullptr;
+
   // prefill (allocated on first use)
   int prefill_format = MOE_PREFILL_BF16;
   int Tp_max = 0;
@@ -277,6 +298,10 @@ hipError_t launch_route_finalize(Ctx* c, const DecodeScratch& s, int layer, int 
 hipError_t launch_cache_lookup(Ctx* c, int layer, const int32_t* d_experts,
                                const int32_t* d_n, int n_max, int32_t* d_slot, bool insert,
                                hipStream_t st);
+// prefetch lookup of d_experts[0..n) of `layer` into d_pf_fills / d_pf_meta,
+// pinning what the call whose meta is `pin` uses
+hipError_t launch_cache_prefetch(Ctx* c, int layer, const int32_t* d_experts, int n,
+                                 const DevMeta* pin, hipStream_t st);
 // confined: the fill runs beside expert kernels (few workgroups, each
 // holding its CU's LDS so that no expert-kernel workgroup shares the CU)
 hipError_t launch_fill(const FillEntry* fills, const DevMeta* meta, int max_fill,

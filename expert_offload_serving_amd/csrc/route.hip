@@ -141,7 +141,13 @@ __device__ void block_lookup(const LookupArgs& a, LookupShared& ls, const int* s
   const int ranks = block_excl_scan((hit ? 1 : 0) | (miss ? 1 << 16 : 0), ls.tmp, &both);  // barrier: hit[] cleared
   const int hrank = ranks & 0xFFFF, mrank = ranks >> 16;
   const int n_hit = both & 0xFFFF, n_miss = both >> 16;
-  const int n_fill = a.insert ? min(n_miss, C - n_hit) : 0;
+  // A prefetch leaves the issuing call's slots alone: they are the last
+  // n_pin entries of the recency order (that call stamped them last, and
+  // none holds a key of this lookup, which names another layer's experts or
+  // experts that call did not use).
+  const bool pf = a.pin != nullptr;
+  const int n_pin = pf ? a.pin->n_hit + a.pin->n_fill - a.pin->n_bypass : 0;
+  const int n_fill = a.insert ? max(0, min(n_miss, C - n_hit - n_pin)) : 0;
   if (hit) {
     ls.hit[slot] = 1;
     a.stamp[slot] = clock0 + 1 + (uint64_t)hrank;
@@ -187,10 +193,12 @@ __device__ void block_lookup(const LookupArgs& a, LookupShared& ls, const int* s
       ls.order[n_keep + n_hit + mrank] = s | ((key + 1) << kOrderKeyShift);
       a.fills[mrank] = FillEntry{src, a.slots + (size_t)s * a.stride};
       s_slot[u] = s;
-    } else {
+    } else if (!pf) {
       const int b = mrank - n_fill;
       a.fills[mrank] = FillEntry{src, a.staging_buf + (size_t)b * a.stride};
       s_slot[u] = -1 - b;
+    } else {
+      s_slot[u] = INT_MIN;  // prefetch: skipped
     }
   }
   if (u < n && !valid) s_slot[u] = INT_MIN;
@@ -199,14 +207,20 @@ __device__ void block_lookup(const LookupArgs& a, LookupShared& ls, const int* s
   if (tid == 0) {
     DevCache* dc = a.cache;
     dc->clock = clock0 + (uint64_t)n_hit + (uint64_t)n_fill;
-    dc->lookups += (uint64_t)(n_hit + n_miss);
-    dc->hits += (uint64_t)n_hit;
-    dc->fills += (uint64_t)n_fill;
-    dc->bypasses += (uint64_t)(n_miss - n_fill);
+    if (pf) {
+      dc->pf_lookups += (uint64_t)(n_hit + n_miss);
+      dc->pf_hits += (uint64_t)n_hit;
+      dc->pf_fills += (uint64_t)n_fill;
+    } else {
+      dc->lookups += (uint64_t)(n_hit + n_miss);
+      dc->hits += (uint64_t)n_hit;
+      dc->fills += (uint64_t)n_fill;
+      dc->bypasses += (uint64_t)(n_miss - n_fill);
+    }
     dc->evictions += (uint64_t)ls.evict;
-    a.meta->n_fill = n_miss;
+    a.meta->n_fill = pf ? n_fill : n_miss;
     a.meta->n_hit = n_hit;
-    a.meta->n_bypass = n_miss - n_fill;
+    a.meta->n_bypass = pf ? 0 : n_miss - n_fill;
   }
   lds_sync();
 }
@@ -344,11 +358,12 @@ __global__ __launch_bounds__(kFinalizeThreads) void route_finalize_kernel(Finali
   }
 }
 
-// Standalone lookup for expert_cache_lookup / expert_cache_fill.  The list
-// must be ascending and unique: from the first entry that is not above its
-// predecessor on, every entry is passed on as invalid (slot code INT_MIN,
-// no state change), so a duplicate can never claim two slots or two
-// recency positions.
+// Standalone lookup for expert_cache_lookup / expert_cache_fill and the
+// prefetch lookup.  The list must be ascending and unique: from the first
+// entry that is not above its predecessor on, every entry is passed on as
+// invalid (slot code INT_MIN, no state change), so a duplicate can never
+// claim two slots or two recency positions.  d_n: the count on the device,
+// or NULL for n_max entries; out_slot may be NULL.
 __global__ __launch_bounds__(kFinalizeThreads) void cache_lookup_kernel(
     LookupArgs la, const int32_t* experts, const int32_t* d_n, int n_max, int32_t* out_slot) {
   __shared__ int s_U[1024];
@@ -356,7 +371,7 @@ __global__ __launch_bounds__(kFinalizeThreads) void cache_lookup_kernel(
   __shared__ int s_first_bad;
   __shared__ LookupShared ls;
   prefetch_lookup(la, ls);
-  int n = *d_n;
+  int n = d_n ? *d_n : n_max;
   n = n < 0 ? 0 : (n > n_max ? n_max : n);
   if (threadIdx.x == 0) s_first_bad = n;
   for (int u = threadIdx.x; u < n; u += blockDim.x) s_U[u] = experts[u];
@@ -368,7 +383,8 @@ __global__ __launch_bounds__(kFinalizeThreads) void cache_lookup_kernel(
     if (u >= s_first_bad) s_U[u] = -1;
   lds_sync();
   block_lookup(la, ls, s_U, n, s_slot);
-  for (int u = threadIdx.x; u < n; u += blockDim.x) out_slot[u] = s_slot[u];
+  if (out_slot)
+    for (int u = threadIdx.x; u < n; u += blockDim.x) out_slot[u] = s_slot[u];
 }
 
 LookupArgs make_lookup_args(Ctx* c, int layer, bool insert, FillEntry* fills, DevMeta* meta) {
@@ -448,6 +464,14 @@ hipError_t launch_route_finalize(Ctx* c, const DecodeScratch& s, int layer, int 
     MOE_LAUNCH(route_finalize_kernel<8>, 1, kFinalizeThreads, 0, st, ev0, ev1, a);
   else
     MOE_LAUNCH(route_finalize_kernel<16>, 1, kFinalizeThreads, 0, st, ev0, ev1, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_prefetch(Ctx* c, int layer, const int32_t* d_experts, int n,
+                                 const DevMeta* pin, hipStream_t st) {
+  LookupArgs la = make_lookup_args(c, layer, true, c->d_pf_fills, c->d_pf_meta);
+  la.pin = pin;
+  cache_lookup_kernel<<<1, kFinalizeThreads, 0, st>>>(la, d_experts, nullptr, n, nullptr);
   return hipGetLastError();
 }
 

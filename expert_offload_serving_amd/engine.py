@@ -211,6 +211,18 @@ class MoEEngine:
         decode copies run beside the resident experts' kernels."""
         b.moe_set_copy_overlap(self.ctx, mode)
 
+    def set_prefetch(self, layer: int, experts=None):
+        """Arm a prefetch of `layer`'s experts (a device int32 tensor,
+        ascending and unique; None or empty disarms) for the next decode
+        call.  The tensor must stay alive until that call has run."""
+        if experts is None or experts.numel() == 0:
+            b.moe_set_prefetch(self.ctx, layer, None, 0)
+            self._prefetch_list = None
+            return
+        assert experts.is_cuda and str(experts.dtype) == "torch.int32" and experts.is_contiguous()
+        b.moe_set_prefetch(self.ctx, layer, experts.data_ptr(), experts.numel())
+        self._prefetch_list = experts  # kept until replaced
+
     def set_debug(self, sync: bool = False, fail_next_fill: bool = False):
         """Synchronise and check every stage; make the next copy step fail
         (the context then refuses cache work until cache_reset)."""

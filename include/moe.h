@@ -177,6 +177,10 @@ typedef struct moe_stats {
   uint64_t bytes_d2d;       /* expert bytes copied by resizes (moved records) */
   uint64_t resizes;         /* expert_cache_resize calls                     */
   uint64_t prefill_layers;  /* layers run by moe_prefill_forward             */
+  uint64_t prefetch_lookups; /* keys named by prefetches (moe_set_prefetch)  */
+  uint64_t prefetch_hits;   /* of those, keys already resident               */
+  uint64_t prefetch_fills;  /* keys a prefetch inserted (copies; also in
+                               bytes_h2d)                                    */
 } moe_stats;
 
 /* Message for the last error on this thread ("" if none).  Never NULL. */
@@ -311,6 +315,36 @@ moe_status moe_layer_forward(moe_ctx* ctx, int32_t layer, const void* d_x,
  * layer.  Errors: INVALID_ARG (mode outside -1..1).
  */
 moe_status moe_set_copy_overlap(moe_ctx* ctx, int32_t mode);
+
+/*
+ * Cross-layer miss prefetch: arm a request that the next decode call
+ * (moe_layer_forward or moe_layer_forward_noalloc with T >= 1, of any layer)
+ * carries out, typically for the layer after that call's.  The pages carry
+ * the next layer's upload under the current layer's compute in prefill
+ * (aipolix.com FreeToken article, fourth paragraph) and name preloading of
+ * experts that activation patterns make likely as one of the engine's
+ * techniques, without a rule or a predictor (world.tibi.club FreeToken
+ * article, section "Cum reușește FreeToken să ruleze 753B pe un singur
+ * GPU?", third item).  The predictor is the caller's: the request names n
+ * experts of `layer`, d_experts[0..n) (device int32, ascending and unique;
+ * read when the call runs, so a kernel queued before the call may write it;
+ * from the first entry that is not above its predecessor, or out of range,
+ * on, entries are ignored).  Once the call's own copies are done it looks
+ * them up with the lookup rule except that a miss may take only an empty
+ * slot (ascending) or a slot whose stamp is at most the clock before the
+ * call's own lookup (ascending stamp) -- never one the call uses -- and a
+ * miss with no such slot is skipped (no staging copy); hits are stamped and
+ * the clock advances as in a lookup.  The misses it inserts are copied from
+ * the pool beside the call's expert kernels (on an internal stream, joined
+ * back into the call's stream before the call ends; under stream capture in
+ * order on that stream) and are hits for later lookups.  Outputs never
+ * depend on it.  Counted in moe_stats' prefetch_* fields (its evictions in
+ * evictions).  n = 0 disarms.  A request not yet carried out is replaced by
+ * the next moe_set_prefetch.  Errors: INVALID_ARG (layer out of range, n
+ * outside [0, n_experts], NULL list with n > 0), UNSUPPORTED (cache policy
+ * other than GLOBAL), STATE (after a failed copy).
+ */
+moe_status moe_set_prefetch(moe_ctx* ctx, int32_t layer, const int32_t* d_experts, int32_t n);
 
 /*
  * moe_layer_forward for callers that cannot allocate device memory: code

@@ -187,6 +187,18 @@ def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, rows=None, what="", rtol=RTOL_
     return err / rms
 
 
+def valid_prefix(experts, E):
+    """The entries of a lookup list the library acts on: those before the
+    first one that is out of range or not above its predecessor."""
+    out = []
+    for e in experts:
+        e = int(e)
+        if e < 0 or e >= E or (out and e <= out[-1]):
+            break
+        out.append(e)
+    return out
+
+
 class DecodeRun:
     """Runs decode steps of one workload on the GPU and the oracle side by side."""
 
@@ -222,13 +234,23 @@ class DecodeRun:
         bias = gen.bias_from_sets(self.sets[layer][step], sh.E) if self.sets else None
         return xb, bias
 
-    def step(self, layer, step, check_out=False, check_state=True, out_tokens=None):
+    def step(self, layer, step, check_out=False, check_state=True, out_tokens=None,
+             prefetch=None, forward=None):
+        """prefetch: (layer, experts) armed for this call (moe_set_prefetch),
+        mirrored by the oracle cache's prefetch after the call's lookup.
+        forward: the engine method to call (default eng.forward; another
+        entry point's dispatch arrays are not the context's, so then only
+        the cache state is compared)."""
         import torch
         sh = self.wl.shape
         xb, bias = self.inputs(layer, step)
         x = bf16_dev(xb)
         bdev = torch.from_numpy(bias).to(self.dev) if bias is not None else None
-        y = self.eng.forward(layer, x, bias=bdev, ids=self.ids, gates=self.gates, y32=self.y32)
+        if prefetch is not None:
+            self.eng.set_prefetch(prefetch[0], torch.tensor(list(prefetch[1]), dtype=torch.int32,
+                                                            device=self.dev))
+        fwd = forward or self.eng.forward
+        y = fwd(layer, x, bias=bdev, ids=self.ids, gates=self.gates, y32=self.y32)
         xf = gen.bf16_bits_to_f32(xb)
         lg, ids_ref, g_ref = self.model.route(layer, xf, bias)
         ids = self.ids.cpu().numpy()
@@ -238,12 +260,16 @@ class DecodeRun:
         if sh.renormalize:
             assert np.max(np.abs(g.astype(np.float64).sum(1) - 1)) <= TOL_SUM
         perm = oracle.permutation(ids_ref, sh.E)
+        pinned = self.cache.clock
         slots_ref, fills, bypass = self.cache.lookup(layer, perm["unique"])
+        if prefetch is not None:
+            self.cache.prefetch(prefetch[0], valid_prefix(prefetch[1], sh.E), pinned)
         if check_state:
-            d = self.eng.inspect_dispatch()
-            for k in ("counts", "offsets", "sorted", "inv", "unique"):
-                assert np.array_equal(d[k], perm[k]), f"{k} differs at layer {layer} step {step}"
-            assert d["slot"].tolist() == slots_ref, f"slots differ at layer {layer} step {step}"
+            if forward is None:
+                d = self.eng.inspect_dispatch()
+                for k in ("counts", "offsets", "sorted", "inv", "unique"):
+                    assert np.array_equal(d[k], perm[k]), f"{k} differs at layer {layer} step {step}"
+                assert d["slot"].tolist() == slots_ref, f"slots differ at layer {layer} step {step}"
             key, stamp, clock = self.eng.cache_snapshot()
             k_ref, s_ref, c_ref = self.cache.snapshot()
             assert key.tolist() == k_ref and stamp.tolist() == s_ref and clock == c_ref, \

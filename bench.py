@@ -89,6 +89,13 @@ def parse(argv=None):
                     help="also run one plain copy of this many MiB (counter calibration)")
     ap.add_argument("--weights", choices=("mxfp4", "bf16", "nvfp4"), default="mxfp4",
                     help="expert format of the headline workload (no context legs)")
+    ap.add_argument("--prefetch-study", type=int, default=0, metavar="STEPS",
+                    help="instead of the benchmark line: GLM-5.2-shaped decode with each "
+                         "cross-layer prefetch predictor (STEPS timed steps per run)")
+    ap.add_argument("--prefetch-kinds", default="none,exact,half,popular,random",
+                    help="predictors the prefetch study runs")
+    ap.add_argument("--prefetch-slots", default="",
+                    help="cache capacities the prefetch study runs (default: 1228,614)")
     ap.add_argument("--policy-study", type=int, default=0, metavar="STEPS",
                     help="instead of the benchmark line: DeepSeek-V4-Flash-shaped decode under "
                          "each cache placement policy (STEPS timed steps per run)")
@@ -182,7 +189,7 @@ def decode_inputs(wl, T, n, seed=0):
 
 # ------------------------------------------------------------ decode runs
 def run_decode(wl, T, steps, warmup, seed=0, eng=None, distinct=None, resize_at=None,
-               check_pairs=()):
+               check_pairs=(), prefetch_plan=None):
     """Decode throughput: W untimed steps, then K timed steps by wall clock
     (host submission included; a cache resize placed at step `resize_at` is
     inside the timed region).  Then a kernel-timing pass over the same K
@@ -190,7 +197,8 @@ def run_decode(wl, T, steps, warmup, seed=0, eng=None, distinct=None, resize_at=
     as in the timed pass, in which every kernel carries start and stop
     events recorded by its own dispatch.  Then a check pass: the listed
     (step, layer) pairs again with routing and fp32 outputs read back (the
-    outputs do not depend on the cache state)."""
+    outputs do not depend on the cache state).  prefetch_plan: {(step,
+    layer): (layer', device int32 experts)} armed before that call."""
     import torch
 
     sh = wl.shape
@@ -217,6 +225,8 @@ def run_decode(wl, T, steps, warmup, seed=0, eng=None, distinct=None, resize_at=
                                evicted=after["evictions"] - before["evictions"],
                                bytes_d2d=after["bytes_d2d"] - before["bytes_d2d"])
         for l in range(sh.layers):
+            if prefetch_plan is not None and (s, l) in prefetch_plan:
+                eng.set_prefetch(*prefetch_plan[(s, l)])
             eng.forward(l, xs[l][s], bias=None if bs[l] is None else bs[l][s], y=y)
 
     for s in range(warmup):
@@ -304,6 +314,8 @@ def run_decode_graph(wl, T, steps, warmup, seed=0):
 
     def do_step(s):
         for l in range(sh.layers):
+            if prefetch_plan is not None and (s, l) in prefetch_plan:
+                eng.set_prefetch(*prefetch_plan[(s, l)])
             eng.forward(l, xs[l][s], bias=None if bs[l] is None else bs[l][s], y=y)
 
     for s in range(warmup):
@@ -537,6 +549,80 @@ def policy_study(steps, warmup, seed=0):
             "steps": steps, "warmup": warmup, "zipf_s": wl.zipf_s, "overlap": wl.overlap}}
 
 
+def prefetch_plans(wl, T, n, seed=0):
+    """Predicted expert sets of the call after each (step, layer) of a decode
+    trace, as device lists, for the prefetch study.  Computed from the
+    workload generator before any timing:
+      exact   - the next call's drawn sets (its routing under the trace's
+                bias): a perfect predictor, the most a prefetch can give;
+      half    - each of those experts kept with probability 1/2, else
+                replaced by a uniformly drawn other expert;
+      popular - the next layer's most popular experts under the trace's
+                ranking, as many as T * k (activation statistics);
+      random  - as many uniformly drawn experts as the exact set has."""
+    import torch
+    from workload import gen
+    sh = wl.shape
+    sets = [gen.zipf_sets(sh, l, T, n, wl.zipf_s, wl.overlap, seed) for l in range(sh.layers)]
+    rng = np.random.default_rng(seed + 99)
+    m = min(T * sh.k, sh.E)
+    popular = [torch.tensor(sorted(gen.popularity_order(sh, l, seed)[:m].tolist()),
+                            dtype=torch.int32, device="cuda") for l in range(sh.layers)]
+    plans = {k: {} for k in ("exact", "half", "popular", "random")}
+    for st in range(n):
+        for l in range(sh.layers):
+            nl, ns = (l + 1) % sh.layers, st + (1 if l + 1 == sh.layers else 0)
+            if ns >= n:
+                continue
+            true = sorted(set(sets[nl][ns].ravel().tolist()))
+            others = np.setdiff1d(np.arange(sh.E), true)
+            half = [e if rng.random() < 0.5 else int(rng.choice(others)) for e in true]
+            rnd = rng.choice(sh.E, len(true), replace=False).tolist()
+            for k, lst in (("exact", true), ("half", sorted(set(half))), ("random", sorted(rnd))):
+                plans[k][(st, l)] = (nl, torch.tensor(lst, dtype=torch.int32, device="cuda"))
+            plans["popular"][(st, l)] = (nl, popular[nl])
+    return plans
+
+
+def prefetch_study(steps, warmup, seed=0, kinds=("none", "exact", "half", "popular", "random"),
+                   caps=None):
+    """The GLM-5.2-shaped decode (T = 1, 8 layers, 20 MB experts) at two
+    cache capacities (60% and 30% of the experts, no resize inside a run),
+    each run from an empty cache: without prefetch, and with each layer's
+    call prefetching the next call's experts as predicted by prefetch_plans."""
+    from dataclasses import replace
+    from workload import gen
+    wl = replace(gen.WORKLOADS["glm_decode"], resize=())
+    sh = wl.shape
+    T = 1
+    eng = make_engine(sh, T, wl.cache_slots, wl.staging_slots)
+    load_weights(eng, sh, seed, distinct=8)
+    plans = prefetch_plans(wl, T, warmup + steps, seed)
+    rows = []
+    for cap in caps or (wl.cache_slots, wl.cache_slots // 2):
+        for kind in kinds:
+            eng.cache_resize(cap)
+            eng.cache_reset()
+            r = run_decode(replace(wl, cache_slots=cap), T, steps, warmup, seed, eng=eng,
+                           prefetch_plan=None if kind == "none" else plans[kind])
+            st = r["stats"]
+            n = max(st["lookups"], 1)
+            rows.append({"cache_slots": cap, "predictor": kind,
+                         "tokens_per_s": round(r["tokens_per_s"], 1),
+                         "ms_per_step": round(r["ms_per_step"], 3),
+                         "hit_rate": round(st["hits"] / n, 4),
+                         "prefetch_fills_per_call": round(st["prefetch_fills"] /
+                                                          (steps * sh.layers), 3),
+                         "prefetch_hit_rate": round(st["prefetch_hits"] /
+                                                    max(st["prefetch_lookups"], 1), 4),
+                         "h2d_gbs": round(r["h2d_gbs"], 2)})
+            print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    eng.close()
+    return {"prefetch_study": rows, "config": {"workload": wl.name, "T": T, "layers": sh.layers,
+            "E": sh.E, "k": sh.k, "shared_expert": sh.shared, "steps": steps, "warmup": warmup,
+            "zipf_s": wl.zipf_s, "overlap": wl.overlap, "expert_records_per_layer": 8}}
+
+
 # ------------------------------------------------------ oracle on the sample
 def check_pairs_of(wl, warmup, steps, n_pairs):
     """(step, layer) pairs spread over the timed steps and the layers (the
@@ -695,6 +781,12 @@ def main():
     from dataclasses import replace
     from workload import gen
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if a.prefetch_study > 0:
+        print(json.dumps(prefetch_study(
+            a.prefetch_study, min(a.warmup or 16, a.prefetch_study),
+            kinds=tuple(k for k in a.prefetch_kinds.split(",") if k),
+            caps=tuple(int(v) for v in a.prefetch_slots.split(",") if v) or None)), flush=True)
+        return
     if a.policy_study > 0:
         print(json.dumps(policy_study(a.policy_study, min(a.warmup or 16, a.policy_study))),
               flush=True)

@@ -81,10 +81,13 @@ void destroy_all(Ctx* c) {
   if (c->pf_stream) (void)hipStreamDestroy(c->pf_stream);
   c->pf_stream = nullptr;
   if (c->ev_filled) (void)hipEventDestroy(c->ev_filled);
+  if (c->ev_pf_lookup) (void)hipEventDestroy(c->ev_pf_lookup);
   if (c->ev_pf_done) (void)hipEventDestroy(c->ev_pf_done);
-  c->ev_filled = c->ev_pf_done = nullptr;
+  c->ev_filled = c->ev_pf_lookup = c->ev_pf_done = nullptr;
   dfree(c->d_pf_fills);
   dfree(c->d_pf_meta);
+  if (c->pf_flag) (void)hipHostFree(c->pf_flag);
+  c->pf_flag = nullptr;
 }
 
 // Run fn(i) for i in [0, n) on up to `threads` host threads.
@@ -336,6 +339,22 @@ static moe_status issue_fill(Ctx* c, const FillEntry* fills, const DevMeta* meta
   return MOE_OK;
 }
 
+// Wait for all work on the device; a prefetch in flight is then done.
+static hipError_t sync_device(Ctx* c) {
+  const hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) c->pf_inflight = false;
+  return e;
+}
+
+// Make `st` wait for a prefetch still in flight (its cache-state update and
+// its copies) before cache work queued on it next.
+static hipError_t join_prefetch(Ctx* c, hipStream_t st) {
+  if (!c->pf_inflight) return hipSuccess;
+  const hipError_t e = hipStreamWaitEvent(st, c->ev_pf_done, 0);
+  if (e == hipSuccess) c->pf_inflight = false;
+  return e;
+}
+
 // MOE_DEBUG_SYNC: wait for the streams a stage used and check for errors,
 // naming the stage.
 static moe_status debug_sync(Ctx* c, hipStream_t st, bool both, bool capturing, const char* stage) {
@@ -371,17 +390,29 @@ moe_status decode_forward(Ctx* c, const DecodeScratch& s, int layer, const uint1
   auto done = [&](bool both, const char* stage) { return debug_sync(c, st, both, capturing, stage); };
   const float* wr = c->d_router + (size_t)layer * f.hidden * f.n_experts;
   const int max_fill = std::min(T * f.top_k, f.n_experts);
+  // A prefetch issued by the previous call may still be copying: its cache
+  // update must precede this call's lookup, and its copies this call's
+  // copies and expert kernels (the router runs meanwhile).  Under capture
+  // it must be over already (waiting on it cannot be recorded).
+  if (c->pf_inflight && __atomic_load_n(c->pf_flag, __ATOMIC_ACQUIRE) >= c->pf_seq)
+    c->pf_inflight = false;  // its copies are done
+  const bool pf_wait = c->pf_inflight;
+  if (pf_wait && capturing)
+    return fail(MOE_ERR_STATE,
+                "a prefetch issued by an earlier call is still copying; synchronize the device "
+                "before capturing");
   HIPCHK(launch_router(x, T, f.hidden, f.n_experts, wr, bias, s.logits, st, t0(kStRouter),
                        t1(kStRouter)));
   if (moe_status r = done(false, "router")) return r;
+  if (pf_wait && !capturing) HIPCHK(hipStreamWaitEvent(st, c->ev_pf_lookup, 0));
   HIPCHK(launch_route_finalize(c, s, layer, T, ids, gates, st, t0(kStFinalize),
                                t1(kStFinalize)));
   if (moe_status r = done(false, "finalize")) return r;
+  if (pf_wait && !capturing) HIPCHK(join_prefetch(c, st));
   // A prefetch armed by moe_set_prefetch: looked up and copied once this
-  // call's own copies are done, beside its expert kernels (on the prefetch
-  // stream; under capture in order on `stream`), and joined back before the
-  // call ends.
-  bool pf_issued = false;
+  // call's own copies are done, beside its expert kernels and into the next
+  // call (on the prefetch stream; the next cache work waits for it), or
+  // under capture in order on `stream`.
   auto prefetch = [&]() -> moe_status {
     if (pr.n <= 0) return MOE_OK;
     hipStream_t ps = capturing ? st : c->pf_stream;
@@ -390,10 +421,12 @@ moe_status decode_forward(Ctx* c, const DecodeScratch& s, int layer, const uint1
       HIPCHK(hipStreamWaitEvent(ps, c->ev_filled, 0));
     }
     HIPCHK(launch_cache_prefetch(c, pr.layer, pr.experts, pr.n, s.meta, ps));
+    if (!capturing) HIPCHK(hipEventRecord(c->ev_pf_lookup, ps));
     if (moe_status r = issue_fill(c, c->d_pf_fills, c->d_pf_meta, pr.n, true, ps)) return r;
     if (!capturing) {
       HIPCHK(hipEventRecord(c->ev_pf_done, ps));
-      pf_issued = true;
+      HIPCHK(launch_signal(c->pf_flag, ++c->pf_seq, ps));
+      c->pf_inflight = true;
     }
     return debug_sync(c, ps, false, capturing, "prefetch");
   };
@@ -430,7 +463,6 @@ moe_status decode_forward(Ctx* c, const DecodeScratch& s, int layer, const uint1
   HIPCHK(launch_combine_rows(s.yperm, s.inv, s.gates, T, f.top_k, f.hidden, f.has_shared, y, y32,
                              st, t0(kStCombine), t1(kStCombine)));
   if (moe_status r = done(false, "combine")) return r;
-  if (pf_issued) HIPCHK(hipStreamWaitEvent(st, c->ev_pf_done, 0));
   if (timed) c->t_decode.push_back(tr);
   return MOE_OK;
 }
@@ -538,6 +570,13 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   ALLOC(c->d_lookup_ids, (size_t)(E + 1) * 4);
   ALLOC(c->d_pf_fills, (size_t)E * sizeof(FillEntry));
   ALLOC(c->d_pf_meta, sizeof(DevMeta));
+  if (hipHostMalloc((void**)&c->pf_flag, 64, hipHostMallocDefault) != hipSuccess) {
+    c->pf_flag = nullptr;
+    destroy_all(c);
+    delete c;
+    return fail(MOE_ERR_OOM, "pinned prefetch flag");
+  }
+  *c->pf_flag = 0;
   {
     // default priority (the caller's streams are expected to use it too)
     hipError_t es = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking);
@@ -548,6 +587,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     if (es == hipSuccess) es = hipEventCreateWithFlags(&c->ev_routed, ef);
     if (es == hipSuccess) es = hipEventCreateWithFlags(&c->ev_resident, ef);
     if (es == hipSuccess) es = hipEventCreateWithFlags(&c->ev_filled, ef);
+    if (es == hipSuccess) es = hipEventCreateWithFlags(&c->ev_pf_lookup, ef);
     if (es == hipSuccess) es = hipEventCreateWithFlags(&c->ev_pf_done, ef);
     if (es != hipSuccess) {
       destroy_all(c);
@@ -779,7 +819,7 @@ moe_status moe_set_prefill_format(moe_ctx* ctx, int32_t format) {
     return fail(MOE_ERR_INVALID_ARG, "unknown prefill format");
   if (format == MOE_PREFILL_MXFP8 && c->cfg.weight_format != MOE_WEIGHTS_MXFP4)
     return fail(MOE_ERR_UNSUPPORTED, "the MXFP8 prefill mode needs MXFP4 experts");
-  HIPCHK(hipDeviceSynchronize());
+  HIPCHK(sync_device(c));
   c->prefill_format = format;
   return MOE_OK;
 }
@@ -795,6 +835,7 @@ moe_status expert_cache_lookup(moe_ctx* ctx, int32_t layer, const int32_t* d_exp
   if (worst_bypass > c->cfg.staging_slots)
     return fail(MOE_ERR_CAPACITY, "staging_slots below worst-case bypass count");
   hipStream_t st = (hipStream_t)stream;
+  HIPCHK(join_prefetch(c, st));
   HIPCHK(launch_cache_lookup(c, layer, d_experts, d_n, c->ds.max_unique, d_slot, false, st));
   return issue_fill(c, c->ds.fills, c->ds.meta, c->ds.max_unique, false, st);
 }
@@ -819,6 +860,7 @@ moe_status expert_cache_fill(moe_ctx* ctx, int32_t layer, const int32_t* h_exper
   hipStream_t st = (hipStream_t)stream;
   std::vector<int32_t> buf(h_experts, h_experts + n);
   buf.push_back(n);
+  HIPCHK(join_prefetch(c, st));
   HIPCHK(hipStreamSynchronize(st));
   HIPCHK(hipMemcpy(c->d_lookup_ids, buf.data(), buf.size() * 4, hipMemcpyHostToDevice));
   HIPCHK(launch_cache_lookup(c, layer, c->d_lookup_ids, c->d_lookup_ids + n, n, c->ds.slotcode,
@@ -855,7 +897,7 @@ moe_status expert_cache_resize(moe_ctx* ctx, int32_t new_slots, void* stream) {
     return fail(MOE_ERR_UNSUPPORTED, "resize is supported for the global cache policy only");
   hipStream_t st = (hipStream_t)stream;
   HIPCHK(hipStreamSynchronize(st));
-  HIPCHK(hipDeviceSynchronize());
+  HIPCHK(sync_device(c));
   const int C = c->C, C2 = new_slots;
   std::vector<int32_t> key(C);
   std::vector<uint64_t> stamp(C);
@@ -910,13 +952,13 @@ moe_status expert_cache_resize(moe_ctx* ctx, int32_t new_slots, void* stream) {
 moe_status expert_cache_reset(moe_ctx* ctx) {
   if (moe_status s = check_ctx(ctx)) return s;
   Ctx* c = C_(ctx);
-  HIPCHK(hipDeviceSynchronize());
+  HIPCHK(sync_device(c));
   const int C = std::max(c->C, 1);
   std::vector<int32_t> key(C, -1), order(C);
   std::iota(order.begin(), order.end(), 0);  // all empty: slot | (0 << kOrderKeyShift)
   std::vector<uint64_t> stamp(C, 0);
   HIPCHK(upload_cache_state(c, key, stamp, order));
-  HIPCHK(hipDeviceSynchronize());
+  HIPCHK(sync_device(c));
   c->failed = false;
   return MOE_OK;
 }
@@ -938,7 +980,7 @@ moe_status expert_cache_snapshot(moe_ctx* ctx, int32_t capacity, int32_t* h_key,
   if (capacity < c->C) return fail(MOE_ERR_CAPACITY, "snapshot capacity below cache size");
   if ((c->C && (!h_key || !h_stamp)) || !h_clock)
     return fail(MOE_ERR_INVALID_ARG, "NULL snapshot array");
-  HIPCHK(hipDeviceSynchronize());
+  HIPCHK(sync_device(c));
   if (c->C) {
     HIPCHK(hipMemcpy(h_key, c->d_key, (size_t)c->C * 4, hipMemcpyDeviceToHost));
     HIPCHK(hipMemcpy(h_stamp, c->d_stamp, (size_t)c->C * 8, hipMemcpyDeviceToHost));
@@ -954,7 +996,7 @@ moe_status moe_inspect_dispatch(moe_ctx* ctx, int32_t* h_T, int32_t* h_counts,
                                 int32_t* h_unique, int32_t* h_n_unique, int32_t* h_slot) {
   if (moe_status s = check_ctx(ctx)) return s;
   Ctx* c = C_(ctx);
-  HIPCHK(hipDeviceSynchronize());
+  HIPCHK(sync_device(c));
   const DecodeScratch& d = c->ds;
   DevMeta m;
   HIPCHK(hipMemcpy(&m, d.meta, sizeof m, hipMemcpyDeviceToHost));
@@ -1022,7 +1064,7 @@ moe_status moe_get_stats(moe_ctx* ctx, moe_stats* out) {
   if (moe_status s = check_ctx(ctx)) return s;
   if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
   Ctx* c = C_(ctx);
-  HIPCHK(hipDeviceSynchronize());
+  HIPCHK(sync_device(c));
   DevCache dc;
   HIPCHK(hipMemcpy(&dc, c->d_cache, sizeof dc, hipMemcpyDeviceToHost));
   *out = c->host_stats;
@@ -1041,7 +1083,7 @@ moe_status moe_get_stats(moe_ctx* ctx, moe_stats* out) {
 moe_status moe_reset_stats(moe_ctx* ctx) {
   if (moe_status s = check_ctx(ctx)) return s;
   Ctx* c = C_(ctx);
-  HIPCHK(hipDeviceSynchronize());
+  HIPCHK(sync_device(c));
   DevCache dc;
   HIPCHK(hipMemcpy(&dc, c->d_cache, sizeof dc, hipMemcpyDeviceToHost));
   const uint64_t clock = dc.clock;
@@ -1109,7 +1151,7 @@ moe_status moe_get_timing(moe_ctx* ctx, moe_timing* out) {
   if (moe_status s = check_ctx(ctx)) return s;
   if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
   Ctx* c = C_(ctx);
-  HIPCHK(hipDeviceSynchronize());
+  HIPCHK(sync_device(c));
   double d[kDecodeStages], p[kPrefillStages];
   HIPCHK(sum_timing(c->t_decode, kDecodeStages, kDecodePreds, d, true));
   HIPCHK(sum_timing(c->t_prefill, kPrefillStages, kPrefillPreds, p, false));

@@ -89,6 +89,19 @@ hipError_t launch_copy_pairs(const FillEntry* pairs, int n, size_t bytes, hipStr
   return hipGetLastError();
 }
 
+// One thread stores `seq` to a word of pinned host memory with a
+// system-scope release (a vector store), after the work queued before it on
+// the stream: the host reads it to learn that work is done without a HIP
+// call.
+__global__ void signal_kernel(uint64_t* flag, uint64_t seq) {
+  __hip_atomic_store(flag, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+hipError_t launch_signal(uint64_t* host_flag, uint64_t seq, hipStream_t st) {
+  signal_kernel<<<1, 1, 0, st>>>(host_flag, seq);
+  return hipGetLastError();
+}
+
 hipError_t launch_probe_copy(const void* src, void* dst, size_t n_bytes, hipStream_t st) {
   probe_copy_kernel<<<4096, 256, 0, st>>>(reinterpret_cast<const u32x4*>(src),
                                          reinterpret_cast<u32x4*>(dst), n_bytes / 16);

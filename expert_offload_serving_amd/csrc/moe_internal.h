@@ -239,9 +239,8 @@ struct Ctx {
 
   // cross-layer prefetch: the request armed by moe_set_prefetch (consumed
   // by the next decode call), the stream its lookup and copies run on beside
-  // that call's expert kernels, its fill list and meta, and the events that
-  // start it after the call's own copies and join it back before the call
-  // ends
+  // that call's expert kernels and into the next call, its fill list and
+  // meta, and the events that order it against later cache work
   struct PrefetchReq {
     int layer = -1;
     const int32_t* experts = nullptr;
@@ -250,8 +249,13 @@ struct Ctx {
   hipStream_t pf_stream = nullptr;
   FillEntry* d_pf_fills = nullptr;  // [E]
   DevMeta* d_pf_meta = nullptr;
-  hipEvent_t ev_filled = nullptr;
-  hipEvent_t ev_pf_done = nullptr;
+  hipEvent_t ev_filled = nullptr;   // the issuing call's own copies are done
+  hipEvent_t ev_pf_lookup = nullptr;  // the prefetch's cache-state update is done
+  hipEvent_t ev_pf_done = nullptr;  // its copies are done
+  bool pf_inflight = false;         // a prefetch ran on pf_stream that no later
+                                    // cache work has waited for yet
+  uint64_t* pf_flag = nullptr;      // pinned host word: the last prefetch whose
+  uint64_t pf_seq = 0;              // copies are done (the device stores pf_seq)
 
   // prefill (allocated on first use)
   int prefill_format = MOE_PREFILL_BF16;
@@ -309,6 +313,8 @@ hipError_t launch_fill(const FillEntry* fills, const DevMeta* meta, int max_fill
                        hipEvent_t ev1 = nullptr);
 hipError_t launch_copy_pairs(const FillEntry* pairs, int n, size_t bytes,
                              hipStream_t st);
+// store seq to *host_flag (pinned host memory) once the stream gets there
+hipError_t launch_signal(uint64_t* host_flag, uint64_t seq, hipStream_t st);
 hipError_t launch_probe_copy(const void* src, void* dst, size_t n_bytes,
                              hipStream_t st);
 // What one launch of the expert kernels covers: items [*lo_p, *hi_p) of a

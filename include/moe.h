@@ -335,10 +335,13 @@ moe_status moe_set_copy_overlap(moe_ctx* ctx, int32_t mode);
  * call's own lookup (ascending stamp) -- never one the call uses -- and a
  * miss with no such slot is skipped (no staging copy); hits are stamped and
  * the clock advances as in a lookup.  The misses it inserts are copied from
- * the pool beside the call's expert kernels (on an internal stream, joined
- * back into the call's stream before the call ends; under stream capture in
- * order on that stream) and are hits for later lookups.  Outputs never
- * depend on it.  Counted in moe_stats' prefetch_* fields (its evictions in
+ * the pool on an internal stream, beside the call's expert kernels and on
+ * into the next call, and are hits for later lookups: the next decode call
+ * (its routing runs meanwhile), expert_cache_lookup and expert_cache_fill
+ * wait for those copies on their stream, the calls that synchronize the
+ * device do, and a call under stream capture fails with STATE while they
+ * run (synchronize before capturing).  Under capture a request is carried
+ * out in order on the capturing stream.  Outputs never depend on it.  Counted in moe_stats' prefetch_* fields (its evictions in
  * evictions).  n = 0 disarms.  A request not yet carried out is replaced by
  * the next moe_set_prefetch.  Errors: INVALID_ARG (layer out of range, n
  * outside [0, n_experts], NULL list with n > 0), UNSUPPORTED (cache policy

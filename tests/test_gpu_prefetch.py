@@ -216,3 +216,71 @@ def test_prefetch_argument_checks():
         eng.set_prefetch(1, t)
     assert e.value.name == "UNSUPPORTED"
     eng.close()
+
+
+def test_cache_calls_after_a_prefetch_in_flight():
+    """A prefetching call followed at once by expert_cache_fill, a resize
+    and another prefetching call: each waits for the copies still in
+    flight; state checked against the oracle after each."""
+    import torch
+    sh = H.small_shape(E=32, k=4, shared=True, layers=2)
+    T = 4
+    wl = gen.Workload("pf_then", sh, Ts=(T,), steps=6, cache_slots=20,
+                      staging_slots=T * sh.k, zipf_s=1.1, overlap=0.5)
+    print("case: cache calls after a prefetch in flight", flush=True)
+    run = H.DecodeRun(wl, H.Model(sh, seed=74), T=T)
+    run.eng.set_copy_overlap(1)
+
+    def same_state(what):
+        key, stamp, clock = run.eng.cache_snapshot()
+        k_ref, s_ref, c_ref = run.cache.snapshot()
+        assert key.tolist() == k_ref and stamp.tolist() == s_ref and clock == c_ref, what
+
+    run.step(0, 0, prefetch=(1, [0, 5, 9, 13, 21, 30]))
+    run.eng.cache_fill(1, [2, 5, 17])
+    run.cache.fill(1, [2, 5, 17])
+    same_state("fill after a prefetch")
+    run.step(1, 0, prefetch=(0, [1, 2, 3, 4, 5, 6, 7, 8]))
+    run.eng.cache_resize(14)
+    run.cache.resize(14)
+    same_state("resize after a prefetch")
+    for s in range(1, wl.steps):
+        for l in range(sh.layers):
+            run.step(l, s, check_out=(s == wl.steps - 1),
+                     prefetch=((l + 1) % sh.layers, list(range(2 * s, 2 * s + 6))))
+    run.close()
+
+
+def test_capture_after_an_eager_prefetch():
+    """An eager call that prefetches, a synchronisation, then forwards
+    captured on the same context: the capture sees the prefetch finished
+    and records no wait; replays equal the eager outputs."""
+    import torch
+    sh = H.small_shape(E=32, k=4, shared=True, layers=2)
+    T = 4
+    print("case: capture after an eager prefetch", flush=True)
+    m = H.Model(sh, seed=75)
+    eng = H.make_engine(sh, T, cache_slots=12, staging_slots=T * sh.k)
+    m.load(eng)
+    ref_eng = H.make_engine(sh, T, cache_slots=12, staging_slots=T * sh.k)
+    m.load(ref_eng)
+    x = [H.bf16_dev(gen.tokens(sh, l, 0, T, 75)) for l in range(sh.layers)]
+    lst = torch.tensor([3, 8, 20], dtype=torch.int32, device="cuda")
+    for e in (eng, ref_eng):
+        e.set_prefetch(1, lst)
+        e.forward(0, x[0])
+    torch.cuda.synchronize()
+    y = torch.empty((T, sh.H), dtype=torch.int16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        eng.forward(1, x[1], y=y)
+    torch.cuda.synchronize()
+    y_ref = ref_eng.forward(1, x[1])
+    torch.cuda.synchronize()
+    for _ in range(2):
+        y.fill_(0x7FFF)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref)
+    eng.close()
+    ref_eng.close()

@@ -89,6 +89,9 @@ def parse(argv=None):
                     help="also run one plain copy of this many MiB (counter calibration)")
     ap.add_argument("--weights", choices=("mxfp4", "bf16", "nvfp4"), default="mxfp4",
                     help="expert format of the headline workload (no context legs)")
+    ap.add_argument("--copy-overlap", type=int, choices=(-1, 0, 1), default=-1,
+                    help="headline decode: copies beside the resident experts' kernels "
+                         "(-1: the library's choice by record size, 0: never, 1: always)")
     ap.add_argument("--prefetch-study", type=int, default=0, metavar="STEPS",
                     help="instead of the benchmark line: GLM-5.2-shaped decode with each "
                          "cross-layer prefetch predictor (STEPS timed steps per run)")
@@ -189,7 +192,7 @@ def decode_inputs(wl, T, n, seed=0):
 
 # ------------------------------------------------------------ decode runs
 def run_decode(wl, T, steps, warmup, seed=0, eng=None, distinct=None, resize_at=None,
-               check_pairs=(), prefetch_plan=None):
+               check_pairs=(), prefetch_plan=None, copy_overlap=-1):
     """Decode throughput: W untimed steps, then K timed steps by wall clock
     (host submission included; a cache resize placed at step `resize_at` is
     inside the timed region).  Then a kernel-timing pass over the same K
@@ -206,6 +209,7 @@ def run_decode(wl, T, steps, warmup, seed=0, eng=None, distinct=None, resize_at=
     if own:
         eng = make_engine(sh, T, wl.cache_slots, wl.staging_slots)
         load_weights(eng, sh, seed, distinct)
+    eng.set_copy_overlap(copy_overlap)
     n = warmup + steps
     xs, bs, hx, hb = decode_inputs(wl, T, n, seed)
     y = torch.empty((T, sh.H), dtype=torch.int16, device="cuda")
@@ -805,7 +809,8 @@ def main():
         resize_at = W + K // 2 if wl.resize else None
         pairs = check_pairs_of(wl, W, K, 0 if a.no_cpu_baseline else a.check_pairs)
         log(f"headline {wl.name} T={T}: {W} warm-up + {K} timed steps (loading the expert pool)")
-        res = run_decode(wl, T, K, W, distinct=a.distinct, resize_at=resize_at, check_pairs=pairs)
+        res = run_decode(wl, T, K, W, distinct=a.distinct, resize_at=resize_at, check_pairs=pairs,
+                         copy_overlap=a.copy_overlap)
         log(f"headline done: {res['tokens_per_s']:.1f} tokens/s")
         kgu, kdn = decode_kernels(T)
         roof = roofline_entry(kgu, res["gateup_gbs"], res["gateup_us"], res["gateup_bytes"],

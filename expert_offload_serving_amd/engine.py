@@ -215,11 +215,12 @@ class MoEEngine:
         """Arm a prefetch of `layer`'s experts (a device int32 tensor,
         ascending and unique; None or empty disarms) for the next decode
         call.  The tensor must stay alive until that call has run."""
-        if experts is None or experts.numel() == 0:
+        if experts is None or (hasattr(experts, "numel") and experts.numel() == 0):
             b.moe_set_prefetch(self.ctx, layer, None, 0)
             self._prefetch_list = None
             return
-        assert experts.is_cuda and str(experts.dtype) == "torch.int32" and experts.is_contiguous()
+        n = int(experts.shape[0]) if hasattr(experts, "shape") and len(experts.shape) == 1 else -1
+        check_device("experts", experts, ("int32",), (n,))
         b.moe_set_prefetch(self.ctx, layer, experts.data_ptr(), experts.numel())
         self._prefetch_list = experts  # kept until replaced
 

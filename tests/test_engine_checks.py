@@ -87,3 +87,11 @@ def test_host_weight_shapes():
     eg.check_host("w", np.zeros((H, E), np.float32), (H, E))
     with pytest.raises(ValueError, match="shape"):
         eg.check_host("w", np.zeros((E, H), np.float32), (H, E))
+
+
+def test_prefetch_list_checks():
+    """set_prefetch takes a 1-D contiguous int32 CUDA tensor (or nothing)."""
+    stub = type("S", (), {"ctx": None})()
+    for bad, msg in ((_cpu((3,), torch.int32), "CUDA"), (np.arange(3, dtype=np.int32), "torch tensor")):
+        with pytest.raises(ValueError, match=msg):
+            eg.MoEEngine.set_prefetch(stub, 1, bad)

@@ -14,12 +14,18 @@ from tests.test_gpu_nvfp4 import _Model, _as_nvfp4
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("fmt,T", [("bf16", 33), ("bf16", 64), ("nvfp4", 33), ("nvfp4", 64)])
-def test_decode_beyond_16_tokens(fmt, T):
-    sh = replace(H.small_shape(H=1024, I=512, E=64, k=6, shared=True, layers=2), weights=fmt)
-    wl = gen.Workload("wide", sh, Ts=(T,), steps=6, cache_slots=40,
+@pytest.mark.parametrize("fmt,T,kw", [
+    ("bf16", 33, {}), ("bf16", 64, {}), ("nvfp4", 33, {}), ("nvfp4", 64, {}),
+    ("bf16", 17, dict(H=4096, I=256, E=16, k=2)),      # the largest K a bf16 wave split takes
+    ("nvfp4", 64, dict(H=6144, I=256, E=16, k=4)),
+])
+def test_decode_beyond_16_tokens(fmt, T, kw):
+    base = dict(H=1024, I=512, E=64, k=6, shared=True, layers=2)
+    base.update(kw)
+    sh = replace(H.small_shape(**base), weights=fmt)
+    wl = gen.Workload("wide", sh, Ts=(T,), steps=6, cache_slots=min(40, sh.E * sh.layers),
                       staging_slots=min(T * sh.k, sh.E), zipf_s=1.1, overlap=0.5)
-    print(f"case: {fmt} decode T={T}", flush=True)
+    print(f"case: {fmt} decode T={T} {kw}", flush=True)
     m = H.Model(sh, seed=11)
     run = H.DecodeRun(wl, m, T=T, max_tokens=64)
     for s in range(wl.steps):
@@ -56,6 +62,9 @@ def test_nvfp4_beyond_16_tokens_equals_mxfp4():
     ("nvfp4", 300, dict(H=512, I=256, E=32, k=4, shared=True, layers=2)),
     ("bf16", 129, dict(H=384, I=256, E=16, k=2)),
     ("nvfp4", 700, dict(H=256, I=256, E=1024, k=16, shared=True)),
+    ("bf16", 1, dict(H=256, I=128, E=8, k=2, shared=True)),
+    ("nvfp4", 17, dict(H=256, I=128, E=8, k=2, shared=True)),
+    ("bf16", 40, dict(H=4096, I=128, E=4, k=2)),       # the largest K a bf16 wave split takes
 ])
 def test_prefill_other_formats(fmt, T, kw):
     """Every token of every layer: routing and permutation bit-exact,

@@ -438,7 +438,7 @@ def time_prefill(eng, sh, T, xs, ys, steps, fmt, name, kernels=None):
 def run_dsv4(prefill_steps, decode_steps, decode_warmup, seed=0, formats=("bf16", "mxfp8")):
     """The DeepSeek-V4-Flash-shaped stack on one engine: prefill of all
     layers per step (layer uploads included) in each prefill mode, then T=1
-    decode through the global LRU (13.4 MB experts: HBM-bound, not
+    and T=32 decode through the global LRU (13.4 MB experts: HBM-bound, not
     cache-resident)."""
     import torch
     from workload import gen
@@ -466,6 +466,13 @@ def run_dsv4(prefill_steps, decode_steps, decode_warmup, seed=0, formats=("bf16"
     if decode_steps > 0:
         r = run_decode(wd, 1, decode_steps, decode_warmup, seed, eng=eng)
         out["dsv4_decode_T1"] = decode_summary(r)
+        # T = 32 from an emptied cache: about 87 unique experts per layer
+        # against 256 slots over 4 layers, so most lookups miss (PCIe-bound);
+        # the kernels for more than 16 tokens per call
+        eng.cache_reset()
+        n32 = max(decode_steps // 8, 16)
+        r = run_decode(wd, 32, n32, max(n32 // 4, 4), seed, eng=eng)
+        out["dsv4_decode_T32"] = decode_summary(r)
     eng.close()
     return out
 

@@ -857,6 +857,170 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
 #undef DN
 }
 
+// ------------------------------------------------ gate/up on bf16 weights
+// Grouped GEMM tile for bf16 experts: C[128 token rows][128 columns] over K
+// in chunks of 128, on the loads, stages and waits of gemm_tile_mf (A waves
+// 0-3 fetch the token rows, B waves 4-7 the weights, one step ahead).  A
+// tile holds 8 weight atoms of 4 KB (4 pairs of 16 gate and 16 up rows), the
+// stage the same 32 KB of LDS an MXFP4 stage of 32 atoms takes; wave w owns
+// pair w % 4 (atoms 2(w%4), 2(w%4)+1) and the fragments 2i + w/4, and feeds
+// the stored bf16 pieces to the MFMA as they are.  Each wave then holds the
+// gate and up sums of its own pair, so h = silu(g) * u is formed in
+// registers and leaves as two bf16 planes (hi = RNE(h), lo = RNE(h - hi)).
+constexpr int kBwAtoms = 8;                                          // 128 columns
+constexpr int kLdsBwB = kBwAtoms * kAtomBytesBF16;                   // 32 KB per B stage
+constexpr int kLdsBw = kStagesA * kLdsA + kStagesB * kLdsBwB;        // 128 KB
+static_assert(kLdsBw <= 160 * 1024, "LDS per CU");
+
+template <int MF>
+__device__ __forceinline__ void gemm_tile_bw(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
+                                             uint8_t* lds, f32x4 (&acc)[MF > 0 ? MF : 1][2]) {
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int mh = w >> 2, nq = w & 3;
+  const bool a_wave = w < 4;
+  const int KC = gt.KC;
+  const __amdgpu_buffer_rsrc_t rw = rsrc(gt.wbase, gt.wbytes);
+  uint8_t* const bstages = lds + kStagesA * kLdsA;
+  auto chunk = [&](int c) { return c + gt.k0 < KC ? c + gt.k0 : c + gt.k0 - KC; };
+  // A waves: as in gemm_tile_mf (rows past gt.rows are not fetched).
+  auto issue_a = [&](int s) {
+    uint8_t* buf = lds + (s % kStagesA) * kLdsA;
+    const bool in = s < KC;
+    const uint32_t k = (uint32_t)chunk(s) * (kAtomK * 2);
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      if (32 * w + 4 * i < gt.rows)
+        lds_load16(ra, in ? gt.aoff[i] + k : kOOB, buf + (8 * w + i) * 1024);
+  };
+  // B waves: wave 4 + u loads atoms 2u, 2u+1 of the chunk (8 KB).
+  auto issue_b = [&](int c) {
+    uint8_t* buf = bstages + (c % kStagesB) * kLdsBwB;
+    const int u = w - 4;
+    const bool in = c < KC;
+    const uint32_t k = (uint32_t)chunk(c) * kAtomBytesBF16;
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+      const int a = 2 * u + (t >> 2), piece = t & 3;
+      lds_load16(rw, in ? gt.woff[t >> 2] + k + 1024u * piece + 16u * lane : kOOB,
+                 buf + a * kAtomBytesBF16 + piece * 1024);
+    }
+  };
+  auto compute = [&](int s) {
+    if constexpr (MF == 0) {
+      if (!a_wave) issue_b(s + 1);
+    } else {
+      const uint8_t* abuf = lds + (s % kStagesA) * kLdsA;
+      const uint8_t* bbuf = bstages + (s % kStagesB) * kLdsBwB;
+      const int r = lane & 15;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int slot = ((4 * (lane >> 4) + j) ^ r) & 15;
+        bf16x8 a[MF];
+#pragma unroll
+        for (int i = 0; i < MF; i++)
+          a[i] = *reinterpret_cast<const bf16x8*>(abuf + (2 * i + mh) * 4096 + 256 * r + 16 * slot);
+        const bf16x8 bg = *reinterpret_cast<const bf16x8*>(bbuf + (2 * nq) * kAtomBytesBF16 + 1024 * j + 16 * lane);
+        const bf16x8 bu = *reinterpret_cast<const bf16x8*>(bbuf + (2 * nq + 1) * kAtomBytesBF16 + 1024 * j + 16 * lane);
+#pragma unroll
+        for (int i = 0; i < MF; i++) {
+          acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bg, acc[i][0], 0, 0, 0);
+          acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bu, acc[i][1], 0, 0, 0);
+        }
+        if (j == 0 && !a_wave) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_b(s + 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  };
+  if (a_wave)
+    issue_a(0);
+  else
+    issue_b(0);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int s = 0; s < KC; s++) {
+    wait_vmem_all();
+    lds_barrier();
+    if (a_wave) issue_a(s + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s);  // the B waves issue step s+1 inside
+  }
+  // No buffer-to-LDS write may land after the workgroup has ended.
+  wait_vmem_all();
+}
+
+template <int MF>
+__device__ __forceinline__ void gateup_tile_bw(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
+                                               uint8_t* lds, uint16_t* __restrict__ h,
+                                               size_t lo_plane, int I, size_t row0, int pair) {
+  const int lane = threadIdx.x & 63, mh = wave_id() >> 2;
+  f32x4 acc[MF > 0 ? MF : 1][2];
+#pragma unroll
+  for (int i = 0; i < (MF > 0 ? MF : 1); i++) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  gemm_tile_bw<MF>(gt, ra, lds, acc);
+  if (pair >= I / kAtomRows) return;  // columns past I (the last block's)
+#pragma unroll
+  for (int i = 0; i < MF; i++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int m = (2 * i + mh) * 16 + 4 * (lane >> 4) + r;
+      if (m < gt.rows) {
+        const float hv = silu(acc[i][0][r]) * acc[i][1][r];
+        const uint16_t hi = __builtin_bit_cast(uint16_t, (__bf16)hv);
+        const uint16_t lo = __builtin_bit_cast(uint16_t, (__bf16)(hv - __uint_as_float((uint32_t)hi << 16)));
+        const size_t o = (row0 + m) * (size_t)I + (size_t)pair * 16 + (lane & 15);
+        h[o] = hi;
+        h[lo_plane + o] = lo;
+      }
+    }
+}
+
+// Gate/up + SwiGLU on bf16 experts.  N-block nb covers pairs 4nb .. 4nb+3
+// (atoms: row groups 8nb .. 8nb+7, gate and up alternating); h leaves as two
+// bf16 planes, lo_plane elements apart, for the down kernel.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void gateup_prefill_bw_kernel(
+    GroupArgs g, const uint16_t* x, uint32_t x_bytes, int H, int I, int nbn,
+    uint16_t* __restrict__ h, size_t lo_plane) {
+  int ti, nb;
+  tile_of_block(nbn, &ti, &nb);
+  if (ti >= *g.n_tiles) return;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBw];
+  const int2 td = g.tiles[ti];
+  const int grp = td.x, m0 = td.y;
+  const int cnt = g.counts[grp], pos0 = g.offsets[grp];
+  const int lane = threadIdx.x & 63, w = wave_id(), nq = w & 3;
+  const int ngroups = 2 * I / kAtomRows;
+  GemmTile gt;
+  gt.wbase = grp < g.E ? g.layerbuf + (size_t)grp * g.stride : g.shared_w;
+  gt.KC = H / kAtomK;
+  gt.wbytes = (uint32_t)ngroups * (uint32_t)gt.KC * kAtomBytesBF16;
+  gt.k0 = nb * gt.KC / nbn;
+  gt.rows = min(kBM, cnt - m0);
+  clear_loads(gt);
+  if (w < 4) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int r = 32 * w + 4 * i + (lane >> 4);
+      if (r < gt.rows) gt.aoff[i] = (uint32_t)g.tok[pos0 + m0 + r] * (uint32_t)H * 2u + a_piece(r, lane);
+    }
+  } else {
+    // B wave 4 + u: atoms 2u, 2u+1 = row groups 8nb + 2u, +1 (one pair)
+    const uint32_t group_bytes = (uint32_t)gt.KC * kAtomBytesBF16;
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      const int rg = 8 * nb + 2 * (w - 4) + t;
+      gt.woff[t] = (uint32_t)(rg < ngroups ? rg : 0) * group_bytes;
+    }
+  }
+  const __amdgpu_buffer_rsrc_t ra = rsrc(x, x_bytes);
+  const size_t row0 = (size_t)(pos0 + m0);
+  const int pair = 4 * nb + nq;
+#define GUB(N) gateup_tile_bw<N>(gt, ra, lds, h, lo_plane, I, row0, pair)
+  MOE_MF_SWITCH(wave_mfrags(gt.rows), GUB)
+#undef GUB
+}
+
 // ------------------------------------------------------- native-MX GEMMs
 // The opt-in MXFP8 prefill mode (moe_config.prefill_format): both expert
 // matrices on v_mfma_scale_f32_16x16x128_f8f6f4 with the activations block-
@@ -1493,9 +1657,16 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
       L.lo_plane = (size_t)p->Tmax * (k + 1) * I;
       L.yperm = p->yperm;
       L.stream = false;
-      if ((e = launch_gateup_list(c, L, x, (uint32_t)T * H * 2, st, t0(kPfGateUp),
-                                  t1(kPfGateUp))) != hipSuccess)
+      if (f.weight_format == MOE_WEIGHTS_BF16) {
+        // bf16 weights: the grouped GEMM over the dispatch's 128-row tiles
+        const int nbn_bw = 2 * I / (kBwAtoms * kAtomRows);
+        MOE_LAUNCH(gateup_prefill_bw_kernel, p->max_tiles * nbn_bw, 64 * kGemmWaves, 0, st,
+                   t0(kPfGateUp), t1(kPfGateUp), ga, x, (uint32_t)T * H * 2, H, I, nbn_bw, p->h,
+                   L.lo_plane);
+      } else if ((e = launch_gateup_list(c, L, x, (uint32_t)T * H * 2, st, t0(kPfGateUp),
+                                         t1(kPfGateUp))) != hipSuccess) {
         return e;
+      }
       if ((e = launch_down_list(c, L, st, t0(kPfDown), t1(kPfDown))) != hipSuccess) return e;
     } else if (mx) {
       const size_t rows_cap = (size_t)p->Tmax * (k + 1);

@@ -8,6 +8,7 @@
 #include <algorithm>
 
 #include "moe_internal.h"
+#include "nvfp4_dequant.h"
 #include "route_common.h"
 
 namespace moe {
@@ -1021,6 +1022,194 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
 #undef GUB
 }
 
+// ------------------------------------------------- gate/up on NVFP4 weights
+// The MXFP4 grouped GEMM tile (gemm_tile_mf: 128 token rows x 512 columns,
+// 32 atoms per stage) on NVFP4 atoms: 1024 code bytes as MXFP4, then lane
+// l's two E4M3 block scales at 1024 + 2l.  A B stage holds the 32 atoms'
+// codes and then their 128-byte scale blocks (36 KB); a B wave fetches its 8
+// atoms' scales with one 16-byte load per lane (lane l: atom l/8, bytes
+// 16 (l%8)).  The dequant is the exact one of the decode kernels.  Each wave
+// holds gate and up of 4 pairs, so h = silu(t_g g) * (t_u u) (t: the
+// matrix scales) is formed in registers and stored as two bf16 planes.
+constexpr int kLdsNvB = kAtomsPerTile * kAtomData + kAtomsPerTile * 128;    // 36 KB
+constexpr int kLdsNv = kStagesA * kLdsA + kStagesB * kLdsNvB;             // 136 KB
+static_assert(kLdsNv <= 160 * 1024, "LDS per CU");
+
+template <int MF>
+__device__ __forceinline__ void gemm_tile_nv(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
+                                             uint8_t* lds,
+                                             f32x4 (&acc)[MF > 0 ? MF : 1][kFragsPerWave]) {
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int mh = w >> 2, nq = w & 3;
+  const bool a_wave = w < 4;
+  const int KC = gt.KC;
+  const __amdgpu_buffer_rsrc_t rw = rsrc(gt.wbase, gt.wbytes);
+  uint8_t* const bstages = lds + kStagesA * kLdsA;
+  constexpr int kScales = kAtomsPerTile * kAtomData;  // scale blocks within a B stage
+  auto chunk = [&](int c) { return c + gt.k0 < KC ? c + gt.k0 : c + gt.k0 - KC; };
+  auto issue_a = [&](int s) {
+    uint8_t* buf = lds + (s % kStagesA) * kLdsA;
+    const bool in = s < KC;
+    const uint32_t k = (uint32_t)chunk(s) * (kAtomK * 2);
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      if (32 * w + 4 * i < gt.rows)
+        lds_load16(ra, in ? gt.aoff[i] + k : kOOB, buf + (8 * w + i) * 1024);
+  };
+  // B waves: chunk c into stage c % 2 (codes of atoms 8u .. 8u+7, then
+  // their scale blocks).
+  auto issue_b = [&](int c) {
+    uint8_t* buf = bstages + (c % kStagesB) * kLdsNvB;
+    const int u = w - 4;
+    const bool in = c < KC;
+    const uint32_t k = (uint32_t)chunk(c) * kAtomBytesNV;
+#pragma unroll
+    for (int t = 0; t < 8; t++)
+      lds_load16(rw, in ? gt.woff[t] + k + 16u * lane : kOOB, buf + (8 * u + t) * kAtomData);
+    lds_load16(rw, in ? gt.soff[0] + k : kOOB, buf + kScales + 8 * u * 128);
+  };
+  auto compute = [&](int s) {
+    if constexpr (MF == 0) {
+      if (!a_wave) issue_b(s + 1);
+    } else {
+      const uint8_t* abuf = lds + (s % kStagesA) * kLdsA;
+      const uint8_t* bbuf = bstages + (s % kStagesB) * kLdsNvB;
+      u32x4 wd[kFragsPerWave];
+      uint32_t sd[kFragsPerWave];
+#pragma unroll
+      for (int f = 0; f < kFragsPerWave; f++) {
+        const int atom = nq * kFragsPerWave + f;
+        wd[f] = *reinterpret_cast<const u32x4*>(bbuf + atom * kAtomData + 16 * lane);
+        sd[f] = *reinterpret_cast<const uint16_t*>(bbuf + kScales + atom * 128 + 2 * lane);
+      }
+      bf16x8 a[2][MF];
+      auto fetch = [&](int j, int q) {
+        const int r = lane & 15;
+        const int slot = ((4 * (lane >> 4) + j) ^ r) & 15;
+#pragma unroll
+        for (int i = 0; i < MF; i++)
+          a[q][i] = *reinterpret_cast<const bf16x8*>(abuf + (2 * i + mh) * 4096 + 256 * r + 16 * slot);
+      };
+      fetch(0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        if (j + 1 < 4) fetch(j + 1, (j + 1) & 1);
+        const int sh = 8 * (j >> 1);  // steps 0-1: the first block scale, 2-3: the second
+        bf16x8 bb[2];
+        bb[0] = nvfp4::dequant8_nv(wd[0][j], (sd[0] >> sh) & 0xFFu);
+#pragma unroll
+        for (int f = 0; f < kFragsPerWave; f++) {
+          if (f + 1 < kFragsPerWave) bb[(f + 1) & 1] = nvfp4::dequant8_nv(wd[f + 1][j], (sd[f + 1] >> sh) & 0xFFu);
+#pragma unroll
+          for (int i = 0; i < MF; i++)
+            acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j & 1][i], bb[f & 1], acc[i][f], 0, 0, 0);
+        }
+        if (j == 0 && !a_wave) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_b(s + 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  };
+  if (a_wave)
+    issue_a(0);
+  else
+    issue_b(0);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int s = 0; s < KC; s++) {
+    wait_vmem_all();
+    lds_barrier();
+    if (a_wave) issue_a(s + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s);  // the B waves issue step s+1 inside
+  }
+  wait_vmem_all();
+}
+
+template <int MF>
+__device__ __forceinline__ void gateup_tile_nv(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
+                                               uint8_t* lds, uint16_t* __restrict__ h,
+                                               size_t lo_plane, int I, size_t row0, int p0,
+                                               float tg, float tu) {
+  const int lane = threadIdx.x & 63, mh = wave_id() >> 2;
+  f32x4 acc[MF > 0 ? MF : 1][kFragsPerWave];
+#pragma unroll
+  for (int i = 0; i < (MF > 0 ? MF : 1); i++)
+#pragma unroll
+    for (int f = 0; f < kFragsPerWave; f++) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  gemm_tile_nv<MF>(gt, ra, lds, acc);
+#pragma unroll
+  for (int q = 0; q < kFragsPerWave / 2; q++) {
+    const int pair = p0 + q;
+    if (pair >= I / kAtomRows) break;  // columns past I (the last block's)
+#pragma unroll
+    for (int i = 0; i < MF; i++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int m = (2 * i + mh) * 16 + 4 * (lane >> 4) + r;
+        if (m < gt.rows) {
+          const float hv = silu(tg * acc[i][2 * q][r]) * (tu * acc[i][2 * q + 1][r]);
+          const uint16_t hi = __builtin_bit_cast(uint16_t, (__bf16)hv);
+          const uint16_t lo =
+              __builtin_bit_cast(uint16_t, (__bf16)(hv - __uint_as_float((uint32_t)hi << 16)));
+          const size_t o = (row0 + m) * (size_t)I + (size_t)pair * 16 + (lane & 15);
+          h[o] = hi;
+          h[lo_plane + o] = lo;
+        }
+      }
+  }
+}
+
+// Gate/up + SwiGLU on NVFP4 experts: n-block nb and column quarters as in
+// gateup_prefill_kernel; h leaves as two bf16 planes for the down kernel.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void gateup_prefill_nv_kernel(
+    GroupArgs g, const uint16_t* x, uint32_t x_bytes, int H, int I, int nbn, size_t ms_off,
+    uint16_t* __restrict__ h, size_t lo_plane) {
+  int ti, nb;
+  tile_of_block(nbn, &ti, &nb);
+  if (ti >= *g.n_tiles) return;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsNv];
+  const int2 td = g.tiles[ti];
+  const int grp = td.x, m0 = td.y;
+  const int cnt = g.counts[grp], pos0 = g.offsets[grp];
+  const int lane = threadIdx.x & 63, w = wave_id(), nq = w & 3;
+  const int ngroups = 2 * I / kAtomRows;
+  const uint8_t* rec = grp < g.E ? g.layerbuf + (size_t)grp * g.stride : g.shared_w;
+  GemmTile gt;
+  gt.wbase = rec;
+  gt.KC = H / kAtomK;
+  gt.wbytes = (uint32_t)ngroups * (uint32_t)gt.KC * kAtomBytesNV;
+  gt.k0 = nb * gt.KC / nbn;
+  gt.rows = min(kBM, cnt - m0);
+  clear_loads(gt);
+  if (w < 4) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int r = 32 * w + 4 * i + (lane >> 4);
+      if (r < gt.rows) gt.aoff[i] = (uint32_t)g.tok[pos0 + m0 + r] * (uint32_t)H * 2u + a_piece(r, lane);
+    }
+  } else {
+    // atoms 8(w-4) + t of the tile: row groups 32nb + 8(w-4) + t; groups
+    // past the matrix (the last, partial block) read group 0
+    const uint32_t group_bytes = (uint32_t)gt.KC * kAtomBytesNV;
+    const int rg0 = nb * 32 + 8 * (w - 4);
+#pragma unroll
+    for (int t = 0; t < 8; t++)
+      gt.woff[t] = (uint32_t)(rg0 + t < ngroups ? rg0 + t : 0) * group_bytes;
+    const int rs = rg0 + (lane >> 3);
+    gt.soff[0] = (uint32_t)(rs < ngroups ? rs : 0) * group_bytes + kAtomData + 16u * (lane & 7);
+  }
+  const float* ms = reinterpret_cast<const float*>(rec + ms_off);
+  const float tg = ms[0], tu = ms[1];
+  const __amdgpu_buffer_rsrc_t ra = rsrc(x, x_bytes);
+  const size_t row0 = (size_t)(pos0 + m0);
+  const int p0 = nb * 16 + 4 * nq;
+#define GUN(N) gateup_tile_nv<N>(gt, ra, lds, h, lo_plane, I, row0, p0, tg, tu)
+  MOE_MF_SWITCH(wave_mfrags(gt.rows), GUN)
+#undef GUN
+}
+
 // ------------------------------------------------------- native-MX GEMMs
 // The opt-in MXFP8 prefill mode (moe_config.prefill_format): both expert
 // matrices on v_mfma_scale_f32_16x16x128_f8f6f4 with the activations block-
@@ -1663,6 +1852,10 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
         MOE_LAUNCH(gateup_prefill_bw_kernel, p->max_tiles * nbn_bw, 64 * kGemmWaves, 0, st,
                    t0(kPfGateUp), t1(kPfGateUp), ga, x, (uint32_t)T * H * 2, H, I, nbn_bw, p->h,
                    L.lo_plane);
+      } else if (f.weight_format == MOE_WEIGHTS_NVFP4) {
+        MOE_LAUNCH(gateup_prefill_nv_kernel, p->max_tiles * nbn_gu, 64 * kGemmWaves, 0, st,
+                   t0(kPfGateUp), t1(kPfGateUp), ga, x, (uint32_t)T * H * 2, H, I, nbn_gu,
+                   nv_trailer_offset(H, I), p->h, L.lo_plane);
       } else if ((e = launch_gateup_list(c, L, x, (uint32_t)T * H * 2, st, t0(kPfGateUp),
                                          t1(kPfGateUp))) != hipSuccess) {
         return e;

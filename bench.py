@@ -477,21 +477,22 @@ def run_dsv4(prefill_steps, decode_steps, decode_warmup, seed=0, formats=("bf16"
     return out
 
 
-def prefill_streamed_hbm(sh, T, r):
-    """HBM roofline of the streamed prefill kernels: algorithmic bytes per
-    layer (every routed expert's weights once -- at T*k/E rows per expert
-    all are routed -- the token rows once, h written and read as two bf16
-    planes, the fp32 expert outputs) over each kernel's time.  bf16 weights
-    at 128 rows per expert give 128 flops per weight byte, under the 312 a
-    2.5 PFLOP/s / 8 TB/s machine needs: those kernels are bounded by HBM."""
+def prefill_streamed_hbm(sh, T, r, kernels):
+    """HBM roofline of the prefill GEMMs with bf16 or NVFP4 experts:
+    algorithmic bytes per layer (every routed expert's weights once -- at
+    T*k/E rows per expert all are routed -- the token rows once, h written
+    and read as two bf16 planes, the fp32 expert outputs) over each kernel's
+    time.  bf16 weights at 128 rows per expert give 128 flops per weight
+    byte, under the 312 a 2.5 PFLOP/s / 8 TB/s machine needs: at that shape
+    the GEMMs are bounded by HBM, not by the matrix cores."""
     rows = T * sh.k + (T if sh.shared else 0)
     n_exp = sh.E + (1 if sh.shared else 0)
     wbytes = sh.expert_bytes() * n_exp
     gu_w, dn_w = wbytes * 2 / 3, wbytes / 3
     gu = gu_w + T * sh.H * 2 + rows * sh.I * 4
     dn = dn_w + rows * sh.I * 4 + rows * sh.H * 4
-    gu_us = r["gateup_decode_kernel"]["avg_us"]
-    dn_us = r["down_decode_kernel"]["avg_us"]
+    gu_us = r[kernels[0]]["avg_us"]
+    dn_us = r[kernels[1]]["avg_us"]
     f = lambda b, us: round(b / (us * 1e3) / HBM_PEAK_GBS, 4)
     return {"bytes_gateup": round(gu), "bytes_down": round(dn), "peak_gbs": HBM_PEAK_GBS,
             "gateup_frac": f(gu, gu_us), "down_frac": f(dn, dn_us),
@@ -500,10 +501,10 @@ def prefill_streamed_hbm(sh, T, r):
 
 def run_prefill_formats(steps, T=4096, layers=2, seed=0, formats=("bf16", "nvfp4")):
     """Prefill with bf16 and NVFP4 experts on a 35B-A3B-shaped stack (H=2048,
-    I=512, E=256, top-8): the expert-streaming kernels over 128-row work
-    items, bf16 matrix cores (NVFP4 is dequantised to bf16 on the way in).
-    Eight generated records per layer are reused for all 256 experts; the
-    routing is the layer's own, so every expert is uploaded and run."""
+    I=512, E=256, top-8): the grouped bf16 GEMMs of each format (NVFP4 is
+    dequantised to bf16 on its way from LDS to the matrix cores).  Eight
+    generated records per layer are reused for all 256 experts; the routing
+    is the layer's own, so every expert is uploaded and run."""
     import torch
     from dataclasses import replace
     from workload import gen
@@ -514,10 +515,11 @@ def run_prefill_formats(steps, T=4096, layers=2, seed=0, formats=("bf16", "nvfp4
         load_weights(eng, sh, seed, distinct=8)
         xs = [bf16_dev(gen.tokens(sh, l, 0, T, seed)) for l in range(sh.layers)]
         ys = [torch.empty((T, sh.H), dtype=torch.int16, device="cuda") for _ in range(sh.layers)]
-        r = time_prefill(eng, sh, T, xs, ys, steps, "bf16", f"a3b_prefill_{w}",
-                         kernels=("gateup_decode_kernel", "down_decode_kernel"))
+        kn = {"bf16": ("gateup_prefill_bw_kernel", "down_prefill_bw_kernel"),
+              "nvfp4": ("gateup_prefill_nv_kernel", "down_prefill_nv_kernel")}[w]
+        r = time_prefill(eng, sh, T, xs, ys, steps, "bf16", f"a3b_prefill_{w}", kernels=kn)
         r["weights"] = w
-        r["hbm"] = prefill_streamed_hbm(sh, T, r)
+        r["hbm"] = prefill_streamed_hbm(sh, T, r, kn)
         out[f"prefill_{w}_experts"] = r
         log(f"prefill with {w} experts: {r['mfma_tflops']} TFLOP/s ({r['mfma_frac']:.3f} of "
             f"{r['mfma_peak_tflops']})")

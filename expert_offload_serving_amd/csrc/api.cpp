@@ -370,10 +370,10 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     return fail(MOE_ERR_UNSUPPORTED, "n_layers*n_experts too large");
   if (f.hidden % 128 || f.inter % 128 || f.hidden > kMaxH || f.inter > kMaxH)
     return fail(MOE_ERR_UNSUPPORTED, "hidden and inter must be multiples of 128, at most 6144");
-  if (f.weight_format == MOE_WEIGHTS_BF16 && (f.max_tokens > 16 || f.max_prefill_tokens > 0) &&
+  if (f.weight_format == MOE_WEIGHTS_BF16 && f.max_tokens > 16 &&
       (f.hidden > 4096 || f.inter > 4096))
     return fail(MOE_ERR_UNSUPPORTED,
-                "bf16 experts above 16 tokens per call or in prefill need H and I <= 4096");
+                "bf16 experts above 16 tokens per decode call need H and I <= 4096");
   if (f.prefill_format == MOE_PREFILL_MXFP8 && f.weight_format != MOE_WEIGHTS_MXFP4)
     return fail(MOE_ERR_UNSUPPORTED, "the MXFP8 prefill mode needs MXFP4 experts");
   if (f.cache_slots > kMaxCacheSlots)

@@ -655,20 +655,10 @@ __global__ __launch_bounds__(256) void combine_kernel(
   if (y32) *reinterpret_cast<f32x4*>(y32 + (size_t)t * H + col) = acc;
 }
 
-// Waves per workgroup (the split of K) and chunks per wave, for K of KC
-// chunks and `tiles` output tiles: split until the launch has about 4096
-// waves (fills 256 CUs at 16 waves), but never give a wave more than
-// max_cpw chunks (its loads are all issued at once).
+// Waves per workgroup (the split of K) and chunks per wave.
 struct Split {
   int waves, cpw;
 };
-Split split_k(int KC, int tiles, int max_cpw) {
-  int s = 1;
-  while (s < kMaxWaves && s * tiles < 4096) s *= 2;
-  s = std::max(s, (KC + max_cpw - 1) / max_cpw);
-  s = std::min(s, std::min(kMaxWaves, KC));
-  return {s, (KC + s - 1) / s};
-}
 
 // Chunks per wave of the streaming launches (1, 2, 4, 8 or 16), from timings
 // of every variant on the 35B-A3B, DSV4 and GLM decode shapes (K of 16, 32
@@ -735,7 +725,9 @@ static Split list_split(const Ctx* c, const ExpertList& L, int KC, int row_group
   return {s, (KC + s - 1) / s};
 }
 
-bool list_split_fits(const Ctx* c, int K) {
+// Whether the kernels for more than 16 rows per item can split a K of this
+// length (bf16 weights take at most 8 waves of 4 chunks).
+static bool list_split_fits(const Ctx* c, int K) {
   const int max_waves = c->cfg.weight_format == MOE_WEIGHTS_BF16 ? WBf16::kMaxThreads / 64 : kMaxWaves;
   return K / kAtomK <= 4 * max_waves;
 }

@@ -287,9 +287,6 @@ hipError_t launch_gateup_list(const Ctx* c, const ExpertList& L, const uint16_t*
                               hipEvent_t ev1 = nullptr);
 hipError_t launch_down_list(const Ctx* c, const ExpertList& L, hipStream_t st,
                             hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
-// whether the kernels for more than 16 rows per item can split a K of this
-// length (bf16 weights take at most 8 waves of 4 chunks)
-bool list_split_fits(const Ctx* c, int K);
 
 // Which part of the work list an expert-kernel launch covers: all items,
 // the resident experts and the shared one, or the experts this call copies.

@@ -38,24 +38,9 @@ struct Prefill {
                                // [rows][I] then its scales [rows][I/32]
   uint8_t* xq = nullptr;       // MXFP8 mode: x codes [Tmax][H], then scales
                                // [Tmax][H/32] (allocated on first use)
-  // bf16 and NVFP4 experts: a work list of chunks of at most
-  // kPrefillRowsPerItem rows per expert (h then holds two bf16 planes)
-  WorkItem* items = nullptr;
-  int32_t* bounds = nullptr;   // [2]: first and end item of the list
-  int items_cap = 0;
   uint8_t* hlo = nullptr;      // low-order records of h: [max_tiles][I/128][8][1664]
   float* yperm = nullptr;      // [rows][H]
 };
-
-// Rows per work item when bf16 or NVFP4 experts run prefill through the
-// decode kernels (which hold a weight slice in registers and loop over the
-// item's 16-row tiles): large groups (the shared expert's T rows) are cut
-// into chunks so that the launch has enough workgroups.
-constexpr int kPrefillRowsPerItem = 128;
-int prefill_items_cap(int T, int k, int E) {
-  const int R = kPrefillRowsPerItem;
-  return (T * k + R - 1) / R + E + (T + R - 1) / R + 1;
-}
 
 // Tiles of 128 rows: every group's partial tile plus the whole rows, rounded
 // up to a multiple of 8 (the launch deals tiles to the 8 XCDs).
@@ -1210,6 +1195,319 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
 #undef GUN
 }
 
+// --------------------------------------------------- down on NVFP4 weights
+// Down GEMM tile for NVFP4 experts: C[128 rows][128 columns of H] over K = I
+// in chunks of 128, A = h as its two bf16 planes (hi and lo, each swizzled
+// as the A stage of gemm_tile_mf), B = 8 NVFP4 atoms (row groups of H) with
+// their scale blocks.  Every weight fragment meets both planes, so h's
+// 16 significant bits reach the sums, as in the decode kernels.  Wave w owns
+// atoms 2(w%4), 2(w%4)+1 and fragments 2i + w/4.
+constexpr int kNvdAtoms = 8;
+constexpr int kLdsNvdA = 2 * kLdsA;                                     // hi, lo: 64 KB
+constexpr int kLdsNvdB = kNvdAtoms * kAtomData + kNvdAtoms * 128;       // 9 KB
+constexpr int kLdsNvd = kStagesA * kLdsNvdA + kStagesB * kLdsNvdB;      // 146 KB
+static_assert(kLdsNvd <= 160 * 1024, "LDS per CU");
+
+template <int MF>
+__device__ __forceinline__ void gemm_tile_nvd(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
+                                              uint32_t lo_bytes, uint8_t* lds,
+                                              f32x4 (&acc)[MF > 0 ? MF : 1][2]) {
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int mh = w >> 2, nq = w & 3;
+  const bool a_wave = w < 4;
+  const int KC = gt.KC;
+  const __amdgpu_buffer_rsrc_t rw = rsrc(gt.wbase, gt.wbytes);
+  uint8_t* const bstages = lds + kStagesA * kLdsNvdA;
+  constexpr int kScales = kNvdAtoms * kAtomData;
+  auto chunk = [&](int c) { return c + gt.k0 < KC ? c + gt.k0 : c + gt.k0 - KC; };
+  // A waves: rows 32w .. 32w+31 of both planes (16 loads).
+  auto issue_a = [&](int s) {
+    uint8_t* buf = lds + (s % kStagesA) * kLdsNvdA;
+    const bool in = s < KC;
+    const uint32_t k = (uint32_t)chunk(s) * (kAtomK * 2);
+#pragma unroll
+    for (int pl = 0; pl < 2; pl++)
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+        if (32 * w + 4 * i < gt.rows)
+          lds_load16(ra, in ? gt.aoff[i] + k + (pl ? lo_bytes : 0u) : kOOB,
+                     buf + pl * kLdsA + (8 * w + i) * 1024);
+  };
+  // B waves: wave 4 + u loads atoms 2u, 2u+1 (codes) and their two scale
+  // blocks (one 4-byte load a lane: 256 bytes).
+  auto issue_b = [&](int c) {
+    uint8_t* buf = bstages + (c % kStagesB) * kLdsNvdB;
+    const int u = w - 4;
+    const bool in = c < KC;
+    const uint32_t k = (uint32_t)chunk(c) * kAtomBytesNV;
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+      lds_load16(rw, in ? gt.woff[t] + k + 16u * lane : kOOB, buf + (2 * u + t) * kAtomData);
+    lds_load4(rw, in ? gt.soff[0] + k : kOOB, buf + kScales + 2 * u * 128);
+  };
+  auto compute = [&](int s) {
+    if constexpr (MF == 0) {
+      if (!a_wave) issue_b(s + 1);
+    } else {
+      const uint8_t* abuf = lds + (s % kStagesA) * kLdsNvdA;
+      const uint8_t* bbuf = bstages + (s % kStagesB) * kLdsNvdB;
+      u32x4 wd[2];
+      uint32_t sd[2];
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        const int atom = 2 * nq + t;
+        wd[t] = *reinterpret_cast<const u32x4*>(bbuf + atom * kAtomData + 16 * lane);
+        sd[t] = *reinterpret_cast<const uint16_t*>(bbuf + kScales + atom * 128 + 2 * lane);
+      }
+      const int r = lane & 15;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int slot = ((4 * (lane >> 4) + j) ^ r) & 15;
+        const int sh = 8 * (j >> 1);
+        bf16x8 bb[2];
+#pragma unroll
+        for (int t = 0; t < 2; t++) bb[t] = nvfp4::dequant8_nv(wd[t][j], (sd[t] >> sh) & 0xFFu);
+#pragma unroll
+        for (int i = 0; i < MF; i++) {
+          const uint8_t* row = abuf + (2 * i + mh) * 4096 + 256 * r + 16 * slot;
+          const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(row);
+          const bf16x8 alo = *reinterpret_cast<const bf16x8*>(row + kLdsA);
+#pragma unroll
+          for (int t = 0; t < 2; t++) {
+            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bb[t], acc[i][t], 0, 0, 0);
+            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bb[t], acc[i][t], 0, 0, 0);
+          }
+        }
+        if (j == 0 && !a_wave) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_b(s + 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  };
+  if (a_wave)
+    issue_a(0);
+  else
+    issue_b(0);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int s = 0; s < KC; s++) {
+    wait_vmem_all();
+    lds_barrier();
+    if (a_wave) issue_a(s + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s);
+  }
+  wait_vmem_all();
+}
+
+template <int MF>
+__device__ __forceinline__ void down_tile_nvd(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
+                                              uint32_t lo_bytes, uint8_t* lds,
+                                              float* __restrict__ yperm, int H, size_t row0,
+                                              int rg0, float td) {
+  const int lane = threadIdx.x & 63, mh = wave_id() >> 2;
+  f32x4 acc[MF > 0 ? MF : 1][2];
+#pragma unroll
+  for (int i = 0; i < (MF > 0 ? MF : 1); i++) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  gemm_tile_nvd<MF>(gt, ra, lo_bytes, lds, acc);
+#pragma unroll
+  for (int i = 0; i < MF; i++)
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int m = (2 * i + mh) * 16 + 4 * (lane >> 4) + r;
+        if (m < gt.rows)
+          yperm[(row0 + m) * H + (rg0 + t) * 16 + (lane & 15)] = td * acc[i][t][r];
+      }
+}
+
+// Down on NVFP4 experts.  N-block nb covers row groups 8nb .. 8nb+7 of H
+// (128 columns); A is h's two bf16 planes (lo_bytes apart).
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void down_prefill_nv_kernel(
+    GroupArgs g, const uint16_t* h, uint32_t h_bytes, uint32_t lo_bytes, int H, int I, int nbn,
+    size_t gateup_bytes, size_t ms_off, float* __restrict__ yperm) {
+  int ti, nb;
+  tile_of_block(nbn, &ti, &nb);
+  if (ti >= *g.n_tiles) return;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsNvd];
+  const int2 td = g.tiles[ti];
+  const int grp = td.x, m0 = td.y;
+  const int cnt = g.counts[grp], pos0 = g.offsets[grp];
+  const int lane = threadIdx.x & 63, w = wave_id(), nq = w & 3;
+  const int ngroups = H / kAtomRows;  // a multiple of 8: no partial block
+  const uint8_t* rec = grp < g.E ? g.layerbuf + (size_t)grp * g.stride : g.shared_w;
+  GemmTile gt;
+  gt.wbase = rec + gateup_bytes;
+  gt.KC = I / kAtomK;
+  gt.wbytes = (uint32_t)ngroups * (uint32_t)gt.KC * kAtomBytesNV;
+  gt.k0 = nb * gt.KC / nbn;
+  gt.rows = min(kBM, cnt - m0);
+  clear_loads(gt);
+  if (w < 4) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int r = 32 * w + 4 * i + (lane >> 4);
+      if (r < gt.rows) gt.aoff[i] = (uint32_t)(pos0 + m0 + r) * (uint32_t)I * 2u + a_piece(r, lane);
+    }
+  } else {
+    const uint32_t group_bytes = (uint32_t)gt.KC * kAtomBytesNV;
+    const int rgb = 8 * nb + 2 * (w - 4);
+#pragma unroll
+    for (int t = 0; t < 2; t++) gt.woff[t] = (uint32_t)(rgb + t) * group_bytes;
+    // lane l: atom rgb + l/32, bytes 4 (l%32) of its scale block
+    gt.soff[0] = (uint32_t)(rgb + (lane >> 5)) * group_bytes + kAtomData + 4u * (lane & 31);
+  }
+  const float tdn = reinterpret_cast<const float*>(rec + ms_off)[2];
+  const __amdgpu_buffer_rsrc_t ra = rsrc(h, h_bytes);
+  const size_t row0 = (size_t)(pos0 + m0);
+  const int rg0 = 8 * nb + 2 * nq;
+#define DNN(N) down_tile_nvd<N>(gt, ra, lo_bytes, lds, yperm, H, row0, rg0, tdn)
+  MOE_MF_SWITCH(wave_mfrags(gt.rows), DNN)
+#undef DNN
+}
+
+// ----------------------------------------------------- down on bf16 weights
+// As gemm_tile_nvd with bf16 atoms (4 KB): 4 atoms (64 columns of H) per
+// tile, so that two stages of h's two planes (64 KB each) and of the atoms
+// (16 KB each) fill the 160 KB of LDS; wave w owns atom w%4.
+constexpr int kBwdAtoms = 4;
+constexpr int kLdsBwdB = kBwdAtoms * kAtomBytesBF16;                    // 16 KB
+constexpr int kLdsBwd = kStagesA * kLdsNvdA + kStagesB * kLdsBwdB;      // 160 KB
+static_assert(kLdsBwd <= 160 * 1024, "LDS per CU");
+
+template <int MF>
+__device__ __forceinline__ void gemm_tile_bwd(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
+                                              uint32_t lo_bytes, uint8_t* lds,
+                                              f32x4 (&acc)[MF > 0 ? MF : 1]) {
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int mh = w >> 2, nq = w & 3;
+  const bool a_wave = w < 4;
+  const int KC = gt.KC;
+  const __amdgpu_buffer_rsrc_t rw = rsrc(gt.wbase, gt.wbytes);
+  uint8_t* const bstages = lds + kStagesA * kLdsNvdA;
+  auto chunk = [&](int c) { return c + gt.k0 < KC ? c + gt.k0 : c + gt.k0 - KC; };
+  auto issue_a = [&](int s) {
+    uint8_t* buf = lds + (s % kStagesA) * kLdsNvdA;
+    const bool in = s < KC;
+    const uint32_t k = (uint32_t)chunk(s) * (kAtomK * 2);
+#pragma unroll
+    for (int pl = 0; pl < 2; pl++)
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+        if (32 * w + 4 * i < gt.rows)
+          lds_load16(ra, in ? gt.aoff[i] + k + (pl ? lo_bytes : 0u) : kOOB,
+                     buf + pl * kLdsA + (8 * w + i) * 1024);
+  };
+  // B waves: wave 4 + u loads atom u (four 1 KB pieces).
+  auto issue_b = [&](int c) {
+    uint8_t* buf = bstages + (c % kStagesB) * kLdsBwdB;
+    const int u = w - 4;
+    const bool in = c < KC;
+    const uint32_t k = (uint32_t)chunk(c) * kAtomBytesBF16;
+#pragma unroll
+    for (int piece = 0; piece < 4; piece++)
+      lds_load16(rw, in ? gt.woff[0] + k + 1024u * piece + 16u * lane : kOOB,
+                 buf + u * kAtomBytesBF16 + piece * 1024);
+  };
+  auto compute = [&](int s) {
+    if constexpr (MF == 0) {
+      if (!a_wave) issue_b(s + 1);
+    } else {
+      const uint8_t* abuf = lds + (s % kStagesA) * kLdsNvdA;
+      const uint8_t* bbuf = bstages + (s % kStagesB) * kLdsBwdB;
+      const int r = lane & 15;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int slot = ((4 * (lane >> 4) + j) ^ r) & 15;
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(bbuf + nq * kAtomBytesBF16 + 1024 * j + 16 * lane);
+#pragma unroll
+        for (int i = 0; i < MF; i++) {
+          const uint8_t* row = abuf + (2 * i + mh) * 4096 + 256 * r + 16 * slot;
+          const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(row);
+          const bf16x8 alo = *reinterpret_cast<const bf16x8*>(row + kLdsA);
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, acc[i], 0, 0, 0);
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, acc[i], 0, 0, 0);
+        }
+        if (j == 0 && !a_wave) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_b(s + 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  };
+  if (a_wave)
+    issue_a(0);
+  else
+    issue_b(0);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int s = 0; s < KC; s++) {
+    wait_vmem_all();
+    lds_barrier();
+    if (a_wave) issue_a(s + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s);
+  }
+  wait_vmem_all();
+}
+
+template <int MF>
+__device__ __forceinline__ void down_tile_bwd(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
+                                              uint32_t lo_bytes, uint8_t* lds,
+                                              float* __restrict__ yperm, int H, size_t row0,
+                                              int rg) {
+  const int lane = threadIdx.x & 63, mh = wave_id() >> 2;
+  f32x4 acc[MF > 0 ? MF : 1];
+#pragma unroll
+  for (int i = 0; i < (MF > 0 ? MF : 1); i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  gemm_tile_bwd<MF>(gt, ra, lo_bytes, lds, acc);
+#pragma unroll
+  for (int i = 0; i < MF; i++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int m = (2 * i + mh) * 16 + 4 * (lane >> 4) + r;
+      if (m < gt.rows) yperm[(row0 + m) * H + rg * 16 + (lane & 15)] = acc[i][r];
+    }
+}
+
+// Down on bf16 experts.  N-block nb covers row groups 4nb .. 4nb+3 of H.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void down_prefill_bw_kernel(
+    GroupArgs g, const uint16_t* h, uint32_t h_bytes, uint32_t lo_bytes, int H, int I, int nbn,
+    size_t gateup_bytes, float* __restrict__ yperm) {
+  int ti, nb;
+  tile_of_block(nbn, &ti, &nb);
+  if (ti >= *g.n_tiles) return;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBwd];
+  const int2 td = g.tiles[ti];
+  const int grp = td.x, m0 = td.y;
+  const int cnt = g.counts[grp], pos0 = g.offsets[grp];
+  const int lane = threadIdx.x & 63, w = wave_id(), nq = w & 3;
+  const int ngroups = H / kAtomRows;
+  GemmTile gt;
+  gt.wbase = (grp < g.E ? g.layerbuf + (size_t)grp * g.stride : g.shared_w) + gateup_bytes;
+  gt.KC = I / kAtomK;
+  gt.wbytes = (uint32_t)ngroups * (uint32_t)gt.KC * kAtomBytesBF16;
+  gt.k0 = nb * gt.KC / nbn;
+  gt.rows = min(kBM, cnt - m0);
+  clear_loads(gt);
+  if (w < 4) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int r = 32 * w + 4 * i + (lane >> 4);
+      if (r < gt.rows) gt.aoff[i] = (uint32_t)(pos0 + m0 + r) * (uint32_t)I * 2u + a_piece(r, lane);
+    }
+  } else {
+    gt.woff[0] = (uint32_t)(4 * nb + (w - 4)) * (uint32_t)gt.KC * kAtomBytesBF16;
+  }
+  const __amdgpu_buffer_rsrc_t ra = rsrc(h, h_bytes);
+  const size_t row0 = (size_t)(pos0 + m0);
+#define DNB(N) down_tile_bwd<N>(gt, ra, lo_bytes, lds, yperm, H, row0, 4 * nb + nq)
+  MOE_MF_SWITCH(wave_mfrags(gt.rows), DNB)
+#undef DNB
+}
+
 // ------------------------------------------------------- native-MX GEMMs
 // The opt-in MXFP8 prefill mode (moe_config.prefill_format): both expert
 // matrices on v_mfma_scale_f32_16x16x128_f8f6f4 with the activations block-
@@ -1584,44 +1882,6 @@ hipError_t dalloc(T** p, size_t n) {
   return hipMalloc((void**)p, std::max<size_t>(n, 1) * sizeof(T));
 }
 
-// Work list of a layer for the decode kernels: every routed expert's rows
-// in chunks of kPrefillRowsPerItem (experts ascending), then the shared
-// expert's T rows likewise.  One workgroup of 1024 threads, thread e for
-// expert e (E <= 1024).
-__global__ __launch_bounds__(1024) void build_items_kernel(
-    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, int E, int T, int k,
-    int has_shared, const uint8_t* layer_w, size_t stride, const uint8_t* shared_w,
-    WorkItem* __restrict__ items, int32_t* __restrict__ bounds) {
-  constexpr int R = kPrefillRowsPerItem;
-  __shared__ int scan[1024];
-  const int e = threadIdx.x;
-  const int cnt = e < E ? counts[e] : 0;
-  const int nch = (cnt + R - 1) / R;
-  scan[e] = nch;
-  __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {  // inclusive scan
-    const int v = e >= d ? scan[e - d] : 0;
-    __syncthreads();
-    scan[e] += v;
-    __syncthreads();
-  }
-  const int base = scan[e] - nch;
-  for (int c = 0; c < nch; c++) {
-    const int r0 = c * R;
-    items[base + c] = WorkItem{layer_w + (size_t)e * stride, offsets[e] + r0, min(R, cnt - r0)};
-  }
-  const int routed = scan[1023];
-  const int nsh = has_shared ? (T + R - 1) / R : 0;
-  for (int c = e; c < nsh; c += blockDim.x) {
-    const int r0 = c * R;
-    items[routed + c] = WorkItem{shared_w, T * k + r0, min(R, T - r0)};
-  }
-  if (e == 0) {
-    bounds[0] = 0;
-    bounds[1] = routed + nsh;
-  }
-}
-
 hipError_t prefill_alloc(Ctx* c) {
   if (c->pf) return hipSuccess;
   const moe_config& f = c->cfg;
@@ -1647,15 +1907,12 @@ hipError_t prefill_alloc(Ctx* c) {
   PA(tok, rows);
   PA(tiles, (size_t)p->max_tiles);
   PA(n_tiles, 1);
-  const bool streamed = f.weight_format != MOE_WEIGHTS_MXFP4;
-  PA(h, (streamed ? 2 : 1) * rows * f.inter);
-  if (!streamed) PA(hlo, prefill_lo_bytes(T, k, E, f.inter));
+  // bf16 and NVFP4 experts carry h as two bf16 planes; MXFP4 ones as a
+  // bf16 plane and the low-order records
+  const bool two_planes = f.weight_format != MOE_WEIGHTS_MXFP4;
+  PA(h, (two_planes ? 2 : 1) * rows * f.inter);
+  if (!two_planes) PA(hlo, prefill_lo_bytes(T, k, E, f.inter));
   PA(yperm, rows * f.hidden);
-  if (streamed) {
-    p->items_cap = prefill_items_cap(T, k, E);
-    PA(items, (size_t)p->items_cap);
-    PA(bounds, 2);
-  }
 #undef PA
   const size_t layer_bytes = (size_t)E * c->stride;
   for (int b = 0; b < 2; b++)
@@ -1672,8 +1929,7 @@ hipError_t prefill_alloc(Ctx* c) {
 void prefill_free(Ctx* c) {
   if (Prefill* p = c->pf) {
     void* ptrs[] = {p->logits, p->ids, p->gates, p->chunk_cnt, p->counts, p->offsets, p->sorted,
-                    p->inv, p->tok, p->tiles, p->n_tiles, p->h, p->hlo, p->yperm, p->xq,
-                    p->items, p->bounds};
+                    p->inv, p->tok, p->tiles, p->n_tiles, p->h, p->hlo, p->yperm, p->xq};
     for (void* q : ptrs)
       if (q) (void)hipFree(q);
     delete p;
@@ -1829,38 +2085,29 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
     const int nbn_gu = (2 * I + 511) / 512, nbn_dn = (H + 511) / 512;
     const size_t hhi_bytes = (size_t)p->Tmax * (k + 1) * I * 2;
     const size_t hlo_bytes = prefill_lo_bytes(p->Tmax, k, E, I);
-    if (p->items) {
-      // bf16 or NVFP4 experts: the decode kernels over a work list of
-      // 128-row chunks, h as two bf16 planes
-      build_items_kernel<<<1, 1024, 0, st>>>(
-          counts, offsets, E, T, k, f.has_shared, c->d_layerbuf[b], c->stride,
-          f.has_shared ? c->d_shared + (size_t)l * c->stride : nullptr, p->items, p->bounds);
-      ExpertList L;
-      L.items = p->items;
-      L.items_cap = p->items_cap;
-      L.lo_p = p->bounds;
-      L.hi_p = p->bounds + 1;
-      L.grid_items = L.split_items = p->items_cap;
-      L.tok = p->tok;
-      L.h = p->h;
-      L.lo_plane = (size_t)p->Tmax * (k + 1) * I;
-      L.yperm = p->yperm;
-      L.stream = false;
+    if (f.weight_format != MOE_WEIGHTS_MXFP4) {
+      // bf16 or NVFP4 experts: grouped GEMMs over the same tiles, h between
+      // them as two bf16 planes (hi, then lo lo_plane elements on)
+      const size_t lo_plane = (size_t)p->Tmax * (k + 1) * I;
+      const uint32_t lo_bytes = (uint32_t)(lo_plane * 2);
       if (f.weight_format == MOE_WEIGHTS_BF16) {
-        // bf16 weights: the grouped GEMM over the dispatch's 128-row tiles
-        const int nbn_bw = 2 * I / (kBwAtoms * kAtomRows);
-        MOE_LAUNCH(gateup_prefill_bw_kernel, p->max_tiles * nbn_bw, 64 * kGemmWaves, 0, st,
-                   t0(kPfGateUp), t1(kPfGateUp), ga, x, (uint32_t)T * H * 2, H, I, nbn_bw, p->h,
-                   L.lo_plane);
-      } else if (f.weight_format == MOE_WEIGHTS_NVFP4) {
+        const int nbn_g = 2 * I / (kBwAtoms * kAtomRows), nbn_d = H / (kBwdAtoms * kAtomRows);
+        MOE_LAUNCH(gateup_prefill_bw_kernel, p->max_tiles * nbn_g, 64 * kGemmWaves, 0, st,
+                   t0(kPfGateUp), t1(kPfGateUp), ga, x, (uint32_t)T * H * 2, H, I, nbn_g, p->h,
+                   lo_plane);
+        MOE_LAUNCH(down_prefill_bw_kernel, p->max_tiles * nbn_d, 64 * kGemmWaves, 0, st,
+                   t0(kPfDown), t1(kPfDown), ga, p->h, 2 * lo_bytes, lo_bytes, H, I, nbn_d,
+                   gateup_section_bytes(H, I, MOE_WEIGHTS_BF16), p->yperm);
+      } else {
+        const int nbn_d = H / (kNvdAtoms * kAtomRows);
         MOE_LAUNCH(gateup_prefill_nv_kernel, p->max_tiles * nbn_gu, 64 * kGemmWaves, 0, st,
                    t0(kPfGateUp), t1(kPfGateUp), ga, x, (uint32_t)T * H * 2, H, I, nbn_gu,
-                   nv_trailer_offset(H, I), p->h, L.lo_plane);
-      } else if ((e = launch_gateup_list(c, L, x, (uint32_t)T * H * 2, st, t0(kPfGateUp),
-                                         t1(kPfGateUp))) != hipSuccess) {
-        return e;
+                   nv_trailer_offset(H, I), p->h, lo_plane);
+        MOE_LAUNCH(down_prefill_nv_kernel, p->max_tiles * nbn_d, 64 * kGemmWaves, 0, st,
+                   t0(kPfDown), t1(kPfDown), ga, p->h, 2 * lo_bytes, lo_bytes, H, I, nbn_d,
+                   gateup_section_bytes(H, I, MOE_WEIGHTS_NVFP4), nv_trailer_offset(H, I),
+                   p->yperm);
       }
-      if ((e = launch_down_list(c, L, st, t0(kPfDown), t1(kPfDown))) != hipSuccess) return e;
     } else if (mx) {
       const size_t rows_cap = (size_t)p->Tmax * (k + 1);
       uint8_t* const hq = reinterpret_cast<uint8_t*>(p->h);

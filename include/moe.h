@@ -93,11 +93,11 @@ enum {
  * modellene?").  NVFP4: E2M1 codes with one E4M3 scale per 16 along K and
  * one fp32 scale per matrix, the format the pages run the 35B-A3B model in
  * on a laptop GPU (same section); NVIDIA's definition, which the pages do
- * not spell out.  BF16 and NVFP4 experts run decode and prefill through the
- * expert-streaming kernels (prefill: each expert's rows in chunks of 128,
- * h carried as two bf16 planes; the grouped GEMMs and the MXFP8 prefill mode
- * are MXFP4 only).  BF16 experts above 16 tokens per call or in prefill
- * need H and I <= 4096 (else UNSUPPORTED).
+ * not spell out.  Decode runs every format through the expert-streaming
+ * kernels; prefill runs grouped GEMMs in every format, carrying h between
+ * them as two bf16 planes for BF16 and NVFP4 experts (the MXFP8 prefill
+ * mode is MXFP4 only).  BF16 experts above 16 tokens per decode call need
+ * H and I <= 4096 (else UNSUPPORTED).
  */
 enum {
   MOE_WEIGHTS_MXFP4 = 0,

@@ -92,13 +92,12 @@ def test_bf16_limits():
     from expert_offload_serving_amd import binding
     sh = H.small_shape(weights="bf16")
     big = H.small_shape(H=6144, I=256, weights="bf16")
-    # above 16 tokens per call or in prefill, bf16 experts need H, I <= 4096
-    for kw in (dict(max_tokens=17), dict(max_tokens=4, max_prefill_tokens=64)):
-        with pytest.raises(binding.MoEError) as ei:
-            H.make_engine(big, kw["max_tokens"], 8, 8, max_prefill_tokens=kw.get("max_prefill_tokens", 0))
-        assert ei.value.status == -6  # UNSUPPORTED
-        H.make_engine(sh, kw["max_tokens"], 8, 64,
-                      max_prefill_tokens=kw.get("max_prefill_tokens", 0)).close()
+    # above 16 tokens per decode call, bf16 experts need H, I <= 4096
+    with pytest.raises(binding.MoEError) as ei:
+        H.make_engine(big, 17, 8, 8)
+    assert ei.value.status == -6  # UNSUPPORTED
+    H.make_engine(sh, 17, 8, 64).close()
+    H.make_engine(big, 4, 8, 8, max_prefill_tokens=64).close()   # prefill: any size
     eng = H.make_engine(sh, 4, 8, 8)
     w4 = gen.expert_weights(H.small_shape(), 0, 0)
     w = gen.expert_weights_bf16(sh, 0, 0)

@@ -1,7 +1,7 @@
-"""bf16 and NVFP4 experts beyond 16 tokens per decode call and in prefill
-(GPU): the expert-streaming kernels for more than 16 rows per item, fed by
-the decode work list or by a prefill work list of 128-row chunks, against
-the oracle; NVFP4 bit-identical to MXFP4 on equal values on those kernels."""
+"""bf16 and NVFP4 experts beyond 16 tokens per decode call (the kernels for
+more than 16 rows per item) and in prefill (grouped GEMMs with h as two
+bf16 planes), against the oracle; NVFP4 bit-identical to MXFP4 on equal
+values on the decode kernels."""
 from dataclasses import replace
 
 import numpy as np
@@ -64,7 +64,9 @@ def test_nvfp4_beyond_16_tokens_equals_mxfp4():
     ("nvfp4", 700, dict(H=256, I=256, E=1024, k=16, shared=True)),
     ("bf16", 1, dict(H=256, I=128, E=8, k=2, shared=True)),
     ("nvfp4", 17, dict(H=256, I=128, E=8, k=2, shared=True)),
-    ("bf16", 40, dict(H=4096, I=128, E=4, k=2)),       # the largest K a bf16 wave split takes
+    ("bf16", 40, dict(H=4096, I=128, E=4, k=2)),
+    ("bf16", 70, dict(H=6144, I=256, E=4, k=2, shared=True)),   # the largest H
+    ("nvfp4", 70, dict(H=6144, I=384, E=4, k=2, shared=True)),
 ])
 def test_prefill_other_formats(fmt, T, kw):
     """Every token of every layer: routing and permutation bit-exact,

@@ -430,6 +430,14 @@ __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, uint32_t vof
 
 // Wait until none of this wave's vector-memory instructions is outstanding.
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most the last N vector-memory instructions of this wave are
+// outstanding (loads complete in issue order): with weights three stages
+// deep, a B wave's N loads of the next step.
+template <int N>
+__device__ __forceinline__ void wait_vmem_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 __device__ __forceinline__ int wave_id() {
@@ -855,8 +863,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
 // registers and leaves as two bf16 planes (hi = RNE(h), lo = RNE(h - hi)).
 constexpr int kBwAtoms = 8;                                          // 128 columns
 constexpr int kLdsBwB = kBwAtoms * kAtomBytesBF16;                   // 32 KB per B stage
-constexpr int kLdsBw = kStagesA * kLdsA + kStagesB * kLdsBwB;        // 128 KB
+constexpr int kStagesBw = 3;                                         // weights two steps ahead
+constexpr int kBwLoads = 8;                                          // per B wave and step
+constexpr int kLdsBw = kStagesA * kLdsA + kStagesBw * kLdsBwB;       // 160 KB
 static_assert(kLdsBw <= 160 * 1024, "LDS per CU");
+
 
 template <int MF>
 __device__ __forceinline__ void gemm_tile_bw(const GemmTile& gt, __amdgpu_buffer_rsrc_t ra,
@@ -878,9 +889,10 @@ __device__ __forceinline__ void gemm_tile_bw(const GemmTile& gt, __amdgpu_buffer
       if (32 * w + 4 * i < gt.rows)
         lds_load16(ra, in ? gt.aoff[i] + k : kOOB, buf + (8 * w + i) * 1024);
   };
-  // B waves: wave 4 + u loads atoms 2u, 2u+1 of the chunk (8 KB).
+  // B waves: wave 4 + u loads atoms 2u, 2u+1 of the chunk (8 KB), always
+  // kBwLoads instructions (chunks past the end go to the out-of-range offset).
   auto issue_b = [&](int c) {
-    uint8_t* buf = bstages + (c % kStagesB) * kLdsBwB;
+    uint8_t* buf = bstages + (c % kStagesBw) * kLdsBwB;
     const int u = w - 4;
     const bool in = c < KC;
     const uint32_t k = (uint32_t)chunk(c) * kAtomBytesBF16;
@@ -893,10 +905,10 @@ __device__ __forceinline__ void gemm_tile_bw(const GemmTile& gt, __amdgpu_buffer
   };
   auto compute = [&](int s) {
     if constexpr (MF == 0) {
-      if (!a_wave) issue_b(s + 1);
+      if (!a_wave) issue_b(s + 2);
     } else {
       const uint8_t* abuf = lds + (s % kStagesA) * kLdsA;
-      const uint8_t* bbuf = bstages + (s % kStagesB) * kLdsBwB;
+      const uint8_t* bbuf = bstages + (s % kStagesBw) * kLdsBwB;
       const int r = lane & 15;
 #pragma unroll
       for (int j = 0; j < 4; j++) {
@@ -914,23 +926,32 @@ __device__ __forceinline__ void gemm_tile_bw(const GemmTile& gt, __amdgpu_buffer
         }
         if (j == 0 && !a_wave) {
           __builtin_amdgcn_sched_barrier(0);
-          issue_b(s + 1);
+          issue_b(s + 2);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
   };
-  if (a_wave)
+  // The weights stream from HBM, the token rows mostly from L2: the B waves
+  // keep two steps of weights in flight (three stages), the A waves one.
+  // Step s writes B stage (s+2) % 3, which step s-1 read: every wave has
+  // passed step s's barrier, so none reads it any more.
+  if (a_wave) {
     issue_a(0);
-  else
+  } else {
     issue_b(0);
+    issue_b(1);
+  }
   __builtin_amdgcn_sched_barrier(0);
   for (int s = 0; s < KC; s++) {
-    wait_vmem_all();
+    if (a_wave)
+      wait_vmem_all();
+    else
+      wait_vmem_keep<kBwLoads>();  // step s has landed; step s+1 may still be in flight
     lds_barrier();
     if (a_wave) issue_a(s + 1);
     __builtin_amdgcn_sched_barrier(0);
-    compute(s);  // the B waves issue step s+1 inside
+    compute(s);  // the B waves issue step s+2 inside
   }
   // No buffer-to-LDS write may land after the workgroup has ended.
   wait_vmem_all();
@@ -1526,7 +1547,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
 constexpr int kMxFrag = 2048;
 constexpr int kMxCodes = 8 * kMxFrag;                    // 16 KB per stage
 constexpr int kMxAStage = kMxCodes + kBM * 4;            // + 512 B of scales
-constexpr int kLdsMx = kStagesA * kMxAStage + kStagesB * kLdsBStage;   // 101 KB
+constexpr int kStagesMxB = 3;                             // weights two steps ahead
+constexpr int kMxBLoads = 10;                             // per B wave and step
+constexpr int kLdsMx = kStagesA * kMxAStage + kStagesMxB * kLdsBStage;   // 135 KB
 constexpr int kLdsMxGateUp = kLdsMx > 8 * kEpiWave ? kLdsMx : 8 * kEpiWave;
 static_assert(kLdsMxGateUp <= 160 * 1024, "LDS per CU");
 
@@ -1628,8 +1651,10 @@ __device__ __forceinline__ void gemm_tile_mx(const MxTile& gt, __amdgpu_buffer_r
     if (w < 2 && 64 * w < gt.rows)
       lds_load4(rs, in ? gt.asoff + kc * 4u : kOOB, buf + kMxCodes + 256 * w);
   };
+  // B waves: always kMxBLoads instructions (chunks past the end go to the
+  // out-of-range offset).
   auto issue_b = [&](int c) {
-    uint8_t* buf = bstages + (c % kStagesB) * kLdsBStage;
+    uint8_t* buf = bstages + (c % kStagesMxB) * kLdsBStage;
     const int u = w - 4;
     const bool in = c < KC;
     const uint32_t k = (uint32_t)chunk(c) * kAtomBytes;
@@ -1642,10 +1667,10 @@ __device__ __forceinline__ void gemm_tile_mx(const MxTile& gt, __amdgpu_buffer_r
   };
   auto compute = [&](int s) {
     if constexpr (MF == 0) {
-      if (!a_wave) issue_b(s + 1);
+      if (!a_wave) issue_b(s + 2);
     } else {
       const uint8_t* abuf = lds + (s % kStagesA) * kMxAStage;
-      const uint8_t* bbuf = bstages + (s % kStagesB) * kLdsBStage;
+      const uint8_t* bbuf = bstages + (s % kStagesMxB) * kLdsBStage;
       i32x8 a8[MF];
       int as[MF];
 #pragma unroll
@@ -1669,23 +1694,30 @@ __device__ __forceinline__ void gemm_tile_mx(const MxTile& gt, __amdgpu_buffer_r
               a8[i], b8, acc[i][f], 0 /* A: fp8 E4M3 */, 4 /* B: fp4 E2M1 */, 0, as[i], 0, sd);
         if (f == 1 && !a_wave) {
           __builtin_amdgcn_sched_barrier(0);
-          issue_b(s + 1);
+          issue_b(s + 2);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
   };
-  if (a_wave)
+  // Weights three stages deep, as in gemm_tile_bw; the A waves' load count
+  // depends on the tile's rows, so they keep one step in flight.
+  if (a_wave) {
     issue_a(0);
-  else
+  } else {
     issue_b(0);
+    issue_b(1);
+  }
   __builtin_amdgcn_sched_barrier(0);
   for (int s = 0; s < KC; s++) {
-    wait_vmem_all();
+    if (a_wave)
+      wait_vmem_all();
+    else
+      wait_vmem_keep<kMxBLoads>();
     lds_barrier();
     if (a_wave) issue_a(s + 1);
     __builtin_amdgcn_sched_barrier(0);
-    compute(s);
+    compute(s);  // the B waves issue step s+2 inside
   }
   wait_vmem_all();
 }

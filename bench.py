@@ -233,8 +233,22 @@ def run_decode(wl, T, steps, warmup, seed=0, eng=None, distinct=None, resize_at=
                 eng.set_prefetch(*prefetch_plan[(s, l)])
             eng.forward(l, xs[l][s], bias=None if bs[l] is None else bs[l][s], y=y)
 
+    # the first step from the cold cache: its first call (every expert a
+    # miss, first launches included) and the whole step, each timed alone
+    torch.cuda.synchronize()
+    cold = {}
     for s in range(warmup):
-        do_step(s)
+        if s == 0 and own and prefetch_plan is None:
+            t0 = time.perf_counter()
+            eng.forward(0, xs[0][0], bias=None if bs[0] is None else bs[0][0], y=y)
+            torch.cuda.synchronize()
+            cold["first_call_ms"] = round(1e3 * (time.perf_counter() - t0), 3)
+            for l in range(1, sh.layers):
+                eng.forward(l, xs[l][0], bias=None if bs[l] is None else bs[l][0], y=y)
+            torch.cuda.synchronize()
+            cold["first_step_ms"] = round(1e3 * (time.perf_counter() - t0), 3)
+        else:
+            do_step(s)
     torch.cuda.synchronize()
     eng.reset_stats()
     torch.cuda.synchronize()
@@ -298,7 +312,7 @@ def run_decode(wl, T, steps, warmup, seed=0, eng=None, distinct=None, resize_at=
                 layer_gbs=gbs(lb, layer_ms),
                 h2d_gbs=st["bytes_h2d"] / (elapsed * 1e9),
                 fill_gbs=gbs(st2["bytes_h2d"], ms["fill"]),
-                resize=resize_info, checked=checked)
+                resize=resize_info, checked=checked, cold=cold)
 
 
 def run_decode_graph(wl, T, steps, warmup, seed=0):
@@ -790,6 +804,38 @@ def traffic_from_profile(kernel, workload):
         return None
 
 
+def probe_bandwidth(mb=1024, reps=3):
+    """Reference rates for the two links the path moves bytes over: a pinned
+    host buffer copied to the device by the DMA engines (hipMemcpyAsync via
+    torch; the fill kernel's PCIe rate is set against it), and the library's
+    device-to-device copy kernel (bytes read plus bytes written per second).
+    Best of `reps` copies of `mb` MiB each, timed with HIP events."""
+    import torch
+    from expert_offload_serving_amd import binding
+    n = mb << 20
+    host = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    dev = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(dev)
+
+    def best(fn):
+        t = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            t.append(e0.elapsed_time(e1))
+        return min(t)
+    h2d_ms = best(lambda: dev.copy_(host, non_blocking=True))
+    d2d_ms = best(lambda: binding.moe_probe_copy(dev.data_ptr(), dst.data_ptr(), n))
+    del host, dev, dst
+    return {"pcie_h2d_peak_gbs": round(n / (h2d_ms * 1e6), 2),
+            "copy_kernel_gbs": round(2 * n / (d2d_ms * 1e6), 1), "mib": mb,
+            "how": "best of 3: pinned host -> device DMA copy; library copy kernel "
+                   "device -> device, read + write bytes"}
+
+
 def calibrate_copy(mb):
     """One plain device-to-device copy of `mb` MiB through the library's copy
     kernel, for scaling traffic counters to bytes."""
@@ -878,6 +924,7 @@ def main():
                       ("lookups", "hits", "fills", "bypasses", "evictions", "bytes_d2d")}},
             "resize": res["resize"] or None,
             "pcie_h2d_gbs": round(res["h2d_gbs"], 2),
+            "cold_start": res["cold"] or None,
             "copy_overlap": {"split_calls": res["split_calls"], "timed_calls": res["calls"]},
             "fill_kernel_gbs": None if res["fill_gbs"] is None else round(res["fill_gbs"], 2),
         })
@@ -886,6 +933,7 @@ def main():
             base, parity = cpu_baseline(wl, res["checked"], a.cpu_seconds, a.distinct)
             line["cpu_baseline"] = base
             line["parity"] = parity
+        line["probes"] = probe_bandwidth()
     if not a.no_context and a.weights == "mxfp4":
         ctx = line.setdefault("context", {})
         if "a3b" in legs:

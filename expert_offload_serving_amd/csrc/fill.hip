@@ -28,6 +28,29 @@ __device__ __forceinline__ void copy_record(const u32x4* __restrict__ src, u32x4
   for (; i < units; i += stride) dst[i] = src[i];
 }
 
+// Device-to-device copy of `units` 16-byte units (resize moves, the copy
+// probe): a workgroup takes contiguous chunks of 8 x 256 units (32 KB), each
+// thread 8 units of a chunk in flight; loads and stores are nontemporal, since
+// neither side is read again soon.
+constexpr int kD2dThreads = 256, kD2dDepth = 8;
+__device__ __forceinline__ void copy_d2d(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                         size_t units) {
+  constexpr size_t kChunk = (size_t)kD2dThreads * kD2dDepth;
+  const size_t n_chunks = units / kChunk;
+  for (size_t c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+    const size_t base = c * kChunk + threadIdx.x;
+    u32x4 v[kD2dDepth];
+#pragma unroll
+    for (int i = 0; i < kD2dDepth; i++) v[i] = __builtin_nontemporal_load(src + base + i * kD2dThreads);
+#pragma unroll
+    for (int i = 0; i < kD2dDepth; i++) __builtin_nontemporal_store(v[i], dst + base + i * kD2dThreads);
+  }
+  // the tail (fewer than a chunk's units), one unit per thread of the grid
+  for (size_t i = n_chunks * kChunk + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < units;
+       i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
 // A confined fill (one that runs beside expert kernels) has workgroups that
 // each take (nearly) a whole CU's LDS, so that no expert-kernel workgroup
 // (all of them use LDS) is placed beside them: a workgroup sharing a CU with
@@ -50,16 +73,16 @@ __global__ __launch_bounds__(1024) void fill_kernel(const FillEntry* __restrict_
     copy_record(reinterpret_cast<const u32x4*>(fills[r].src), reinterpret_cast<u32x4*>(fills[r].dst),
                 units);
 }
-__global__ __launch_bounds__(256) void copy_pairs_kernel(const FillEntry* __restrict__ pairs, int n,
-                                                         size_t units) {
+__global__ __launch_bounds__(kD2dThreads) void copy_pairs_kernel(const FillEntry* __restrict__ pairs,
+                                                                  int n, size_t units) {
   for (int r = 0; r < n; r++)
-    copy_record(reinterpret_cast<const u32x4*>(pairs[r].src), reinterpret_cast<u32x4*>(pairs[r].dst),
-                units);
+    copy_d2d(reinterpret_cast<const u32x4*>(pairs[r].src), reinterpret_cast<u32x4*>(pairs[r].dst),
+             units);
 }
 
-__global__ __launch_bounds__(256) void probe_copy_kernel(const u32x4* __restrict__ src,
-                                                         u32x4* __restrict__ dst, size_t units) {
-  copy_record(src, dst, units);
+__global__ __launch_bounds__(kD2dThreads) void probe_copy_kernel(const u32x4* __restrict__ src,
+                                                                  u32x4* __restrict__ dst, size_t units) {
+  copy_d2d(src, dst, units);
 }
 
 constexpr int kCopyBlocks = 1024;
@@ -85,7 +108,7 @@ hipError_t launch_fill(const FillEntry* fills, const DevMeta* meta, int max_fill
 }
 hipError_t launch_copy_pairs(const FillEntry* pairs, int n, size_t bytes, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  copy_pairs_kernel<<<kCopyBlocks, 256, 0, st>>>(pairs, n, bytes / 16);
+  copy_pairs_kernel<<<kCopyBlocks, kD2dThreads, 0, st>>>(pairs, n, bytes / 16);
   return hipGetLastError();
 }
 
@@ -103,7 +126,7 @@ hipError_t launch_signal(uint64_t* host_flag, uint64_t seq, hipStream_t st) {
 }
 
 hipError_t launch_probe_copy(const void* src, void* dst, size_t n_bytes, hipStream_t st) {
-  probe_copy_kernel<<<4096, 256, 0, st>>>(reinterpret_cast<const u32x4*>(src),
+  probe_copy_kernel<<<kCopyBlocks, kD2dThreads, 0, st>>>(reinterpret_cast<const u32x4*>(src),
                                          reinterpret_cast<u32x4*>(dst), n_bytes / 16);
   return hipGetLastError();
 }

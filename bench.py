@@ -468,6 +468,10 @@ def run_dsv4(prefill_steps, decode_steps, decode_warmup, seed=0, formats=("bf16"
         for fmt in formats:
             key = "prefill" if fmt == "bf16" else f"prefill_{fmt}"
             out[key] = time_prefill(eng, sh, T, xs, ys, prefill_steps, fmt, wp.name)
+            kn = {"bf16": ("gateup_prefill_kernel", "down_prefill_kernel"),
+                  "mxfp8": ("gateup_mx_kernel", "down_mx_kernel")}[fmt]
+            xb, hb = (2.0, 2.0 + 13 / 16) if fmt == "bf16" else (1 + 1 / 32, 1 + 1 / 32)
+            out[key]["hbm"] = prefill_streamed_hbm(sh, T, out[key], kn, xb, hb)
             log(f"prefill {fmt}: {out[key]['mfma_tflops']} TFLOP/s "
                 f"({out[key]['mfma_frac']:.3f} of {out[key]['mfma_peak_tflops']})")
         # matrix-core busy share by counters (profiles/mfma_busy_*.md)
@@ -491,26 +495,32 @@ def run_dsv4(prefill_steps, decode_steps, decode_warmup, seed=0, formats=("bf16"
     return out
 
 
-def prefill_streamed_hbm(sh, T, r, kernels):
-    """HBM roofline of the prefill GEMMs with bf16 or NVFP4 experts:
-    algorithmic bytes per layer (every routed expert's weights once -- at
-    T*k/E rows per expert all are routed -- the token rows once, h written
-    and read as two bf16 planes, the fp32 expert outputs) over each kernel's
-    time.  bf16 weights at 128 rows per expert give 128 flops per weight
-    byte, under the 312 a 2.5 PFLOP/s / 8 TB/s machine needs: at that shape
-    the GEMMs are bounded by HBM, not by the matrix cores."""
+def prefill_streamed_hbm(sh, T, r, kernels, x_bytes=2.0, h_bytes=4.0):
+    """HBM roofline of a pair of prefill GEMMs: algorithmic bytes per layer
+    over each kernel's time.  The bytes: every expert's weights once (at
+    T*k/E rows per expert all are routed; the shared expert's weights, which
+    each of its T/128 tiles reads, count once), the token rows once, h written
+    by gate/up and read by down, the fp32 expert outputs.  x_bytes and h_bytes
+    are the bytes per element of x and h as the GEMMs move them: bf16 x with
+    h as two bf16 planes (bf16 and NVFP4 experts: 2, 4), bf16 x with h as a
+    bf16 plane plus its fp6 remainder records (2, 2 + 13/16), MXFP8 x and h
+    (1 + 1/32 each).  flops_per_weight_byte against the matrix cores' ridge
+    (peak flops over 8 TB/s: 312 for bf16, 625 for fp8) says which bound
+    applies: below it the GEMMs are bounded by HBM."""
     rows = T * sh.k + (T if sh.shared else 0)
     n_exp = sh.E + (1 if sh.shared else 0)
     wbytes = sh.expert_bytes() * n_exp
     gu_w, dn_w = wbytes * 2 / 3, wbytes / 3
-    gu = gu_w + T * sh.H * 2 + rows * sh.I * 4
-    dn = dn_w + rows * sh.I * 4 + rows * sh.H * 4
+    gu = gu_w + T * sh.H * x_bytes + rows * sh.I * h_bytes
+    dn = dn_w + rows * sh.I * h_bytes + rows * sh.H * 4
     gu_us = r[kernels[0]]["avg_us"]
     dn_us = r[kernels[1]]["avg_us"]
     f = lambda b, us: round(b / (us * 1e3) / HBM_PEAK_GBS, 4)
     return {"bytes_gateup": round(gu), "bytes_down": round(dn), "peak_gbs": HBM_PEAK_GBS,
             "gateup_frac": f(gu, gu_us), "down_frac": f(dn, dn_us),
-            "flops_per_weight_byte": round(r["flops_per_layer"] / wbytes, 1)}
+            "layer_frac": f(gu + dn, gu_us + dn_us),
+            "flops_per_weight_byte": round(r["flops_per_layer"] / wbytes, 1),
+            "ridge_flops_per_byte": round(r["mfma_peak_tflops"] * 1e12 / (HBM_PEAK_GBS * 1e9), 1)}
 
 
 def run_prefill_formats(steps, T=4096, layers=2, seed=0, formats=("bf16", "nvfp4")):

@@ -22,6 +22,7 @@ struct Prefill {
   int last_mx = 0;             // the last call ran in the MXFP8 mode
   int nchunk_max = 0;
   int max_tiles = 0;
+  int resident_wgs = 8;        // GEMM workgroups resident at once: one per CU, a multiple of 8
   float* logits = nullptr;     // [Tmax][E]
   int32_t* ids = nullptr;      // [L][Tmax*k]
   float* gates = nullptr;      // [L][Tmax*k]
@@ -310,10 +311,13 @@ __global__ __launch_bounds__(1024) void dispatch_place_kernel(
 // Tile t of the tile list and n-block nb, with the workgroups of one tile
 // kept on one XCD (workgroup ids are dealt round-robin over the 8 XCDs), so
 // that the tile's gathered token rows stay in that XCD's L2.
-__device__ __forceinline__ void tile_of_block(int nbn, int* ti, int* nb) {
-  const int L = blockIdx.x, xcd = L & 7, j = L >> 3;
+__device__ __forceinline__ void tile_of_index(int L, int nbn, int* ti, int* nb) {
+  const int xcd = L & 7, j = L >> 3;
   *ti = (j / nbn) * 8 + xcd;
   *nb = j % nbn;
+}
+__device__ __forceinline__ void tile_of_block(int nbn, int* ti, int* nb) {
+  tile_of_index(blockIdx.x, nbn, ti, nb);
 }
 
 // Grouped GEMM tile: C[128 token rows][512 columns] over K in chunks of 128,
@@ -1625,8 +1629,15 @@ struct MxTile {
   uint32_t soff[2];
 };
 
+// Chaining (a workgroup that runs several tiles in turn): nx is the next
+// tile of the same workgroup when `chain` (the same K; KC >= 2), and its
+// steps 0 and 1 are issued by this tile's last steps in place of the loads
+// past the end, so they land while this tile's epilogue runs; `pre` says that
+// this tile's own first steps were issued that way.  sa and sb are the A and
+// B stages of this tile's step 0: the stage rings run on across tiles.
 template <int MF>
-__device__ __forceinline__ void gemm_tile_mx(const MxTile& gt, __amdgpu_buffer_rsrc_t ra,
+__device__ __forceinline__ void gemm_tile_mx(const MxTile& gt, const MxTile& nx, bool chain,
+                                             bool pre, int sa, int sb, __amdgpu_buffer_rsrc_t ra,
                                              __amdgpu_buffer_rsrc_t rs, uint8_t* lds,
                                              f32x4 (&acc)[MF > 0 ? MF : 1][kFragsPerWave]) {
   const int lane = threadIdx.x & 63, w = wave_id();
@@ -1635,42 +1646,48 @@ __device__ __forceinline__ void gemm_tile_mx(const MxTile& gt, __amdgpu_buffer_r
   const int KC = gt.KC;
   const __amdgpu_buffer_rsrc_t rw = rsrc(gt.wbase, gt.wbytes);
   uint8_t* const bstages = lds + kStagesA * kMxAStage;
-  auto chunk = [&](int c) { return c + gt.k0 < KC ? c + gt.k0 : c + gt.k0 - KC; };
-  // A waves: step s into stage s % 2 (fragments 2w, 2w+1 that hold rows;
-  // waves 0 and 1 also the scale words of rows 64w .. 64w+63)
+  auto chunk_of = [&](const MxTile& t, int c) { return c + t.k0 < KC ? c + t.k0 : c + t.k0 - KC; };
+  // A waves: step s into stage (sa + s) % 2 (fragments 2w, 2w+1 that hold
+  // rows; waves 0 and 1 also the scale words of rows 64w .. 64w+63); step KC
+  // is the next tile's step 0 when chained.
   auto issue_a = [&](int s) {
-    uint8_t* buf = lds + (s % kStagesA) * kMxAStage;
-    const bool in = s < KC;
-    const uint32_t kc = (uint32_t)chunk(s);
+    uint8_t* buf = lds + ((sa + s) % kStagesA) * kMxAStage;
+    const bool nxt = s >= KC && chain;
+    const MxTile& t = nxt ? nx : gt;
+    const bool in = s < KC || nxt;
+    const uint32_t kc = (uint32_t)chunk_of(t, nxt ? s - KC : s);
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int frag = 2 * w + (i >> 1);
-      if (16 * frag < gt.rows)
-        lds_load16(ra, in ? gt.aoff[i] + kc * kAtomK : kOOB, buf + frag * kMxFrag + (i & 1) * 1024);
+      if (16 * frag < t.rows)
+        lds_load16(ra, in ? t.aoff[i] + kc * kAtomK : kOOB, buf + frag * kMxFrag + (i & 1) * 1024);
     }
-    if (w < 2 && 64 * w < gt.rows)
-      lds_load4(rs, in ? gt.asoff + kc * 4u : kOOB, buf + kMxCodes + 256 * w);
+    if (w < 2 && 64 * w < t.rows)
+      lds_load4(rs, in ? t.asoff + kc * 4u : kOOB, buf + kMxCodes + 256 * w);
   };
   // B waves: always kMxBLoads instructions (chunks past the end go to the
-  // out-of-range offset).
+  // out-of-range offset, or, chained, are the next tile's chunks 0 and 1).
   auto issue_b = [&](int c) {
-    uint8_t* buf = bstages + (c % kStagesMxB) * kLdsBStage;
+    uint8_t* buf = bstages + ((sb + c) % kStagesMxB) * kLdsBStage;
     const int u = w - 4;
-    const bool in = c < KC;
-    const uint32_t k = (uint32_t)chunk(c) * kAtomBytes;
+    const bool nxt = c >= KC && chain;
+    const MxTile& t = nxt ? nx : gt;
+    const __amdgpu_buffer_rsrc_t rb = nxt ? rsrc(nx.wbase, nx.wbytes) : rw;
+    const bool in = c < KC || nxt;
+    const uint32_t k = (uint32_t)chunk_of(t, nxt ? c - KC : c) * kAtomBytes;
 #pragma unroll
-    for (int t = 0; t < 8; t++)
-      lds_load16(rw, in ? gt.woff[t] + k + 16u * lane : kOOB, buf + (8 * u + t) * kAtomData);
+    for (int q = 0; q < 8; q++)
+      lds_load16(rb, in ? t.woff[q] + k + 16u * lane : kOOB, buf + (8 * u + q) * kAtomData);
 #pragma unroll
     for (int hh = 0; hh < 2; hh++)
-      lds_load4(rw, in ? gt.soff[hh] + k : kOOB, buf + kLdsBc + (8 * u + 4 * hh) * 64);
+      lds_load4(rb, in ? t.soff[hh] + k : kOOB, buf + kLdsBc + (8 * u + 4 * hh) * 64);
   };
   auto compute = [&](int s) {
     if constexpr (MF == 0) {
       if (!a_wave) issue_b(s + 2);
     } else {
-      const uint8_t* abuf = lds + (s % kStagesA) * kMxAStage;
-      const uint8_t* bbuf = bstages + (s % kStagesMxB) * kLdsBStage;
+      const uint8_t* abuf = lds + ((sa + s) % kStagesA) * kMxAStage;
+      const uint8_t* bbuf = bstages + ((sb + s) % kStagesMxB) * kLdsBStage;
       i32x8 a8[MF];
       int as[MF];
 #pragma unroll
@@ -1701,16 +1718,20 @@ __device__ __forceinline__ void gemm_tile_mx(const MxTile& gt, __amdgpu_buffer_r
     }
   };
   // Weights three stages deep, as in gemm_tile_bw; the A waves' load count
-  // depends on the tile's rows, so they keep one step in flight.
-  if (a_wave) {
-    issue_a(0);
-  } else {
-    issue_b(0);
-    issue_b(1);
+  // depends on the tile's rows, so they keep one step in flight.  A chained
+  // tile's first wait is a full one: the previous tile's epilogue stores are
+  // counted too.
+  if (!pre) {
+    if (a_wave) {
+      issue_a(0);
+    } else {
+      issue_b(0);
+      issue_b(1);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   for (int s = 0; s < KC; s++) {
-    if (a_wave)
+    if (a_wave || (pre && s == 0))
       wait_vmem_all();
     else
       wait_vmem_keep<kMxBLoads>();
@@ -1719,7 +1740,9 @@ __device__ __forceinline__ void gemm_tile_mx(const MxTile& gt, __amdgpu_buffer_r
     __builtin_amdgcn_sched_barrier(0);
     compute(s);  // the B waves issue step s+2 inside
   }
-  wait_vmem_all();
+  // No buffer-to-LDS write may land after the workgroup has ended; the next
+  // tile's first loads stay in flight through the epilogue.
+  if (!chain) wait_vmem_all();
 }
 
 // A-wave offsets of a tile: row r's codes start at rowbase(r), its scale
@@ -1757,7 +1780,7 @@ __device__ __forceinline__ void gateup_tile_mx(const MxTile& gt, __amdgpu_buffer
   for (int i = 0; i < (MF > 0 ? MF : 1); i++)
 #pragma unroll
     for (int f = 0; f < kFragsPerWave; f++) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gemm_tile_mx<MF>(gt, ra, rs, lds, acc);
+  gemm_tile_mx<MF>(gt, gt, false, false, 0, 0, ra, rs, lds, acc);
   // h = silu(gate) * up through LDS, then one (row, 32-column block) per
   // lane quantised to MXFP8 (as in the bf16 path's epilogue)
   lds_barrier();
@@ -1797,7 +1820,8 @@ __device__ __forceinline__ void gateup_tile_mx(const MxTile& gt, __amdgpu_buffer
 }
 
 template <int MF>
-__device__ __forceinline__ void down_tile_mx(const MxTile& gt, __amdgpu_buffer_rsrc_t ra,
+__device__ __forceinline__ void down_tile_mx(const MxTile& gt, const MxTile& nx, bool chain,
+                                             bool pre, int sa, int sb, __amdgpu_buffer_rsrc_t ra,
                                              __amdgpu_buffer_rsrc_t rs, uint8_t* lds,
                                              float* __restrict__ yperm, int H, size_t row0,
                                              int rg0, int ngroups) {
@@ -1807,7 +1831,7 @@ __device__ __forceinline__ void down_tile_mx(const MxTile& gt, __amdgpu_buffer_r
   for (int i = 0; i < (MF > 0 ? MF : 1); i++)
 #pragma unroll
     for (int f = 0; f < kFragsPerWave; f++) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gemm_tile_mx<MF>(gt, ra, rs, lds, acc);
+  gemm_tile_mx<MF>(gt, nx, chain, pre, sa, sb, ra, rs, lds, acc);
 #pragma unroll
   for (int i = 0; i < MF; i++)
 #pragma unroll
@@ -1865,20 +1889,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void g
 }
 
 // Down on MXFP8 h: tiles as down_prefill_kernel; A rows are the tile's own
-// permuted rows.
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void down_mx_kernel(
-    GroupArgs g, const uint8_t* hq, uint32_t hq_bytes, const uint8_t* hs, uint32_t hs_bytes, int H,
-    int I, int nbn, size_t gateup_bytes, float* __restrict__ yperm) {
+// permuted rows.  A workgroup runs work items blockIdx.x, + gridDim.x, ...
+// (grid: one workgroup per CU, a multiple of 8, so every item keeps the XCD
+// that tile_of_index gives it) and chains them: the next item's first two
+// steps load while this one's epilogue stores its outputs.
+struct DownMxItem {
+  MxTile t;
+  size_t row0;
+  int rg0;
+};
+
+__device__ __forceinline__ bool down_mx_item(const GroupArgs& g, int L, int nbn, int H, int I,
+                                             size_t gateup_bytes, DownMxItem& it) {
   int ti, nb;
-  tile_of_block(nbn, &ti, &nb);
-  if (ti >= *g.n_tiles) return;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsMx];
+  tile_of_index(L, nbn, &ti, &nb);
+  if (ti >= *g.n_tiles) return false;
   const int2 td = g.tiles[ti];
   const int grp = td.x, m0 = td.y;
   const int cnt = g.counts[grp], pos0 = g.offsets[grp];
   const int lane = threadIdx.x & 63, w = wave_id(), nq = w & 3;
   const int ngroups = H / kAtomRows;
-  MxTile gt;
+  MxTile& gt = it.t;
   gt.wbase = (grp < g.E ? g.layerbuf + (size_t)grp * g.stride : g.shared_w) + gateup_bytes;
   gt.KC = I / kAtomK;
   gt.wbytes = (uint32_t)ngroups * (uint32_t)gt.KC * kAtomBytes;
@@ -1899,12 +1930,40 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void d
   for (int t = 0; t < 8; t++) gt.woff[t] = wl.woff[t];
   gt.soff[0] = wl.soff[0];
   gt.soff[1] = wl.soff[1];
+  it.row0 = (size_t)(pos0 + m0);
+  it.rg0 = nb * 32 + 8 * nq;
+  return true;
+}
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void down_mx_kernel(
+    GroupArgs g, const uint8_t* hq, uint32_t hq_bytes, const uint8_t* hs, uint32_t hs_bytes, int H,
+    int I, int nbn, size_t gateup_bytes, float* __restrict__ yperm) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsMx];
+  const int ngroups = H / kAtomRows;
+  const int KC = I / kAtomK;
   const __amdgpu_buffer_rsrc_t ra = rsrc(hq, hq_bytes), rs = rsrc(hs, hs_bytes);
-  const size_t row0 = (size_t)(pos0 + m0);
-  const int rg0 = nb * 32 + 8 * nq;
-#define DNM(N) down_tile_mx<N>(gt, ra, rs, lds, yperm, H, row0, rg0, ngroups)
-  MOE_MF_SWITCH(wave_mfrags(gt.rows), DNM)
+  DownMxItem cur, nxt;
+  int L = blockIdx.x;
+  if (!down_mx_item(g, L, nbn, H, I, gateup_bytes, cur)) return;
+  bool pre = false;
+  int sa = 0, sb = 0;
+  for (;;) {
+    // every wave reads the same item list, so the loop is uniform
+    const bool more = down_mx_item(g, L + (int)gridDim.x, nbn, H, I, gateup_bytes, nxt);
+    const bool chain = more && KC >= 2;
+#define DNM(N) \
+  down_tile_mx<N>(cur.t, nxt.t, chain, pre, sa, sb, ra, rs, lds, yperm, H, cur.row0, cur.rg0, ngroups)
+    MOE_MF_SWITCH(wave_mfrags(cur.t.rows), DNM)
 #undef DNM
+    if (!more) break;
+    // the rings run on; an unchained item issues its own first steps into
+    // stages no wave reads any more (they held steps KC-2 and KC-3)
+    sa = (sa + KC) % kStagesA;
+    sb = (sb + KC) % kStagesMxB;
+    pre = chain;
+    cur = nxt;
+    L += (int)gridDim.x;
+  }
 }
 
 #undef MOE_MF_SWITCH
@@ -1925,6 +1984,11 @@ hipError_t prefill_alloc(Ctx* c) {
   p->max_tiles = prefill_max_tiles(T, k, E);
   const size_t rows = (size_t)T * k + T;
   hipError_t e;
+  int n_cu = 0;
+  if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, c->device)) !=
+      hipSuccess)
+    return e;
+  p->resident_wgs = std::max(8, n_cu / 8 * 8);
 #define PA(ptr, n) \
   if ((e = dalloc(&p->ptr, (n))) != hipSuccess) return e
   const size_t L = f.n_layers;
@@ -2147,7 +2211,11 @@ hipError_t prefill_forward(Ctx* c, int n_layers, const void* const* xs, int T,
       MOE_LAUNCH(gateup_mx_kernel, p->max_tiles * nbn_gu, 64 * kGemmWaves, 0, st, t0(kPfGateUp),
                  t1(kPfGateUp), ga, p->xq, (uint32_t)T * H, xs, (uint32_t)(T * (H / 32)), H, I,
                  nbn_gu, hq, hs);
-      MOE_LAUNCH(down_mx_kernel, p->max_tiles * nbn_dn, 64 * kGemmWaves, 0, st, t0(kPfDown),
+      // one workgroup per CU, each running its items in turn; both bounds are
+      // multiples of 8, so each workgroup's items stay on its XCD and come
+      // in ascending tile order (its loop ends at the first one past n_tiles)
+      MOE_LAUNCH(down_mx_kernel, std::min(p->max_tiles * nbn_dn, p->resident_wgs),
+                 64 * kGemmWaves, 0, st, t0(kPfDown),
                  t1(kPfDown), ga, hq, (uint32_t)(rows_cap * I), hs, (uint32_t)(rows_cap * (I / 32)),
                  H, I, nbn_dn, gateup_section_bytes(H, I), p->yperm);
     } else {

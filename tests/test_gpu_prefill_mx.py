@@ -43,7 +43,10 @@ def _check_layer_mx(run, layer, tokens, plain=True):
                                   (64, dict(E=64, k=8, shared=True, renormalize=False)),
                                   (1000, dict(H=384, I=256, E=40, k=6)),
                                   (200, dict(H=640, I=384, E=12, k=3, shared=True)),
-                                  (700, dict(H=256, I=256, E=1024, k=16, shared=True))])
+                                  (700, dict(H=256, I=256, E=1024, k=16, shared=True)),
+                                  # one K chunk (I = 128) and more work items than
+                                  # workgroups: items run in turn without chaining
+                                  (600, dict(H=256, I=128, E=512, k=8))])
 def test_mx_prefill_small_all_tokens(T, kw):
     sh = H.small_shape(**kw)
     print(f"case: mx prefill T={T} {kw}", flush=True)

@@ -3,8 +3,10 @@
 // computes: aipolix.com FreeToken article, fourth paragraph; jansverre.net
 // FreeToken article, section "Hvorfor er båndbredden viktigere enn antall
 // kjerner?"), an fp64 router GEMM on MFMA, multi-workgroup top-k and
-// counting-sort dispatch, and the expert FFN as grouped bf16 MFMA GEMMs over
-// every expert with fused MXFP4 dequantisation.
+// counting-sort dispatch, and the expert FFN as grouped MFMA GEMMs over every
+// expert: bf16 MFMAs on MXFP4 weights dequantised in registers (the default),
+// on bf16 weights as stored and on NVFP4 weights dequantised exactly, or the
+// opt-in MXFP8 mode on the scaled fp8 x fp4 MFMA.
 #include <algorithm>
 
 #include "moe_internal.h"

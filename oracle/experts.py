@@ -47,7 +47,10 @@ def expert_ffn(x_t: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray):
     x = np.asarray(x_t, dtype=np.float64)
     a = wg.astype(np.float64) @ x
     b = wu.astype(np.float64) @ x
-    h = a / (1.0 + np.exp(-a)) * b
+    # exp(-a) overflows to inf for a below about -709; a / inf is then -0,
+    # which is silu's limit there, so the overflow is expected and silenced
+    with np.errstate(over="ignore"):
+        h = a / (1.0 + np.exp(-a)) * b
     return wd.astype(np.float64) @ h
 
 

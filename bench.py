@@ -216,7 +216,12 @@ def run_decode(wl, T, steps, warmup, seed=0, eng=None, distinct=None, resize_at=
     resize_to = wl.resize[0][1] if wl.resize else None
     resize_info = {}
 
-    def do_step(s, allow_resize=True):
+    # the first step from the cold cache, by events recorded on the stream
+    # (no synchronisation inside a timed region): its first call (every
+    # expert a miss, first launches included) and the whole step
+    cold_ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if own else None
+
+    def do_step(s, allow_resize=True, mark=False):
         if allow_resize and resize_to is not None and s == resize_at:
             # the resize waits for the queued steps; time only its own work
             torch.cuda.synchronize()
@@ -228,35 +233,32 @@ def run_decode(wl, T, steps, warmup, seed=0, eng=None, distinct=None, resize_at=
                                wall_ms=round(1e3 * (time.perf_counter() - t0), 3),
                                evicted=after["evictions"] - before["evictions"],
                                bytes_d2d=after["bytes_d2d"] - before["bytes_d2d"])
+        mark = mark and cold_ev is not None
         for l in range(sh.layers):
             if prefetch_plan is not None and (s, l) in prefetch_plan:
                 eng.set_prefetch(*prefetch_plan[(s, l)])
+            if mark and l == 0:
+                cold_ev[0].record()
             eng.forward(l, xs[l][s], bias=None if bs[l] is None else bs[l][s], y=y)
+            if mark and l == 0:
+                cold_ev[1].record()
+        if mark:
+            cold_ev[2].record()
 
-    # the first step from the cold cache: its first call (every expert a
-    # miss, first launches included) and the whole step, each timed alone
-    torch.cuda.synchronize()
-    cold = {}
     for s in range(warmup):
-        if s == 0 and own and prefetch_plan is None:
-            t0 = time.perf_counter()
-            eng.forward(0, xs[0][0], bias=None if bs[0] is None else bs[0][0], y=y)
-            torch.cuda.synchronize()
-            cold["first_call_ms"] = round(1e3 * (time.perf_counter() - t0), 3)
-            for l in range(1, sh.layers):
-                eng.forward(l, xs[l][0], bias=None if bs[l] is None else bs[l][0], y=y)
-            torch.cuda.synchronize()
-            cold["first_step_ms"] = round(1e3 * (time.perf_counter() - t0), 3)
-        else:
-            do_step(s)
+        do_step(s, mark=s == 0)
     torch.cuda.synchronize()
     eng.reset_stats()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(warmup, warmup + steps):
-        do_step(s)
+        do_step(s, mark=s == 0)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    cold = {}
+    if cold_ev is not None and warmup + steps > 0:
+        cold = {"first_call_ms": round(cold_ev[0].elapsed_time(cold_ev[1]), 3),
+                "first_step_ms": round(cold_ev[0].elapsed_time(cold_ev[2]), 3)}
     st = eng.stats()
     elapsed = t1 - t0
     # kernel-timing pass over the first timed steps, at most TIMING_STEPS of

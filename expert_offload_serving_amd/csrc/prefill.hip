@@ -434,12 +434,16 @@ __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, uint32_t vof
                : "memory");
 }
 
-// The same loads with the nontemporal hint, for weights the MXFP8 GEMMs
-// stream once: without it they are allocated in L2 and the Infinity Cache
-// for nothing.  Measured at DSV4 T = 4096, per layer: gate/up 567 -> 553 us,
-// down 372 -> 357 us; the combine after them takes 121 instead of 103 us
-// (its reads of the fp32 outputs now meet their write-backs).  The bf16
-// mode's GEMMs, bound by the matrix cores, run the same either way.
+// The same loads with the nontemporal hint, for the weights of the GEMMs
+// that HBM bounds (the MXFP8 mode's, and those on bf16 and NVFP4 experts),
+// which stream them once: without it they are allocated in L2 and the
+// Infinity Cache for nothing.  Measured per layer: MXFP8 mode at the DSV4
+// shape, T = 4096, gate/up 567 -> 553 us and down 372 -> 357 us (the
+// combine after them 103 -> 121 us: its reads of the fp32 outputs now meet
+// their write-backs); bf16 experts at the 35B-A3B shape gate/up 352 -> 328
+// us, down 403 -> 393 us, combine 58 -> 45 us; NVFP4 experts gate/up 409 ->
+// 392 us, down 265 -> 260 us.  The default mode's GEMMs on MXFP4 weights,
+// bound by the matrix cores, run the same either way and keep normal loads.
 __device__ __forceinline__ void lds_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voffset, void* lds) {
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voffset), "s"(r),
                "{m0}"((uint32_t)(uintptr_t)(lds_void*)lds)
@@ -922,7 +926,7 @@ __device__ __forceinline__ void gemm_tile_bw(const GemmTile& gt, __amdgpu_buffer
 #pragma unroll
     for (int t = 0; t < 8; t++) {
       const int a = 2 * u + (t >> 2), piece = t & 3;
-      lds_load16(rw, in ? gt.woff[t >> 2] + k + 1024u * piece + 16u * lane : kOOB,
+      lds_load16_nt(rw, in ? gt.woff[t >> 2] + k + 1024u * piece + 16u * lane : kOOB,
                  buf + a * kAtomBytesBF16 + piece * 1024);
     }
   };
@@ -1094,8 +1098,8 @@ __device__ __forceinline__ void gemm_tile_nv(const GemmTile& gt, __amdgpu_buffer
     const uint32_t k = (uint32_t)chunk(c) * kAtomBytesNV;
 #pragma unroll
     for (int t = 0; t < 8; t++)
-      lds_load16(rw, in ? gt.woff[t] + k + 16u * lane : kOOB, buf + (8 * u + t) * kAtomData);
-    lds_load16(rw, in ? gt.soff[0] + k : kOOB, buf + kScales + 8 * u * 128);
+      lds_load16_nt(rw, in ? gt.woff[t] + k + 16u * lane : kOOB, buf + (8 * u + t) * kAtomData);
+    lds_load16_nt(rw, in ? gt.soff[0] + k : kOOB, buf + kScales + 8 * u * 128);
   };
   auto compute = [&](int s) {
     if constexpr (MF == 0) {
@@ -1286,8 +1290,8 @@ __device__ __forceinline__ void gemm_tile_nvd(const GemmTile& gt, __amdgpu_buffe
     const uint32_t k = (uint32_t)chunk(c) * kAtomBytesNV;
 #pragma unroll
     for (int t = 0; t < 2; t++)
-      lds_load16(rw, in ? gt.woff[t] + k + 16u * lane : kOOB, buf + (2 * u + t) * kAtomData);
-    lds_load4(rw, in ? gt.soff[0] + k : kOOB, buf + kScales + 2 * u * 128);
+      lds_load16_nt(rw, in ? gt.woff[t] + k + 16u * lane : kOOB, buf + (2 * u + t) * kAtomData);
+    lds_load4_nt(rw, in ? gt.soff[0] + k : kOOB, buf + kScales + 2 * u * 128);
   };
   auto compute = [&](int s) {
     if constexpr (MF == 0) {
@@ -1452,7 +1456,7 @@ __device__ __forceinline__ void gemm_tile_bwd(const GemmTile& gt, __amdgpu_buffe
     const uint32_t k = (uint32_t)chunk(c) * kAtomBytesBF16;
 #pragma unroll
     for (int piece = 0; piece < 4; piece++)
-      lds_load16(rw, in ? gt.woff[0] + k + 1024u * piece + 16u * lane : kOOB,
+      lds_load16_nt(rw, in ? gt.woff[0] + k + 1024u * piece + 16u * lane : kOOB,
                  buf + u * kAtomBytesBF16 + piece * 1024);
   };
   auto compute = [&](int s) {
